@@ -1,0 +1,243 @@
+"""Benchmark of the windowed atom-attention block on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+A step is one call of the whole block (pack, [token projection], prep,
+slot attention, post, [pool]) on one batch of synthetic input of the named
+workload. Inputs are resident in HBM before the timed region; to keep the
+256 MB Infinity Cache from serving them, the step cycles through enough
+copies of the inputs that they do not fit in it. The timed region is exactly
+K steps between two device synchronisations. Per-kernel durations come from
+HIP events the library records around each launch on the stream it launches
+on (profiling mode of libatomattn), over the same timed region.
+
+Prints ONE JSON line: metric entries/s (B*A*H*K per second), plus
+atoms/s, the roofline of the dominant kernel and the fp64 oracle's rate on
+the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense matrix peaks
+
+
+def kernel_work(w):
+    """Algorithmic work per launch of each kernel: ('hbm', bytes) for the
+    bandwidth-bound slot attention, ('mfma', flops) for the projections."""
+    d = w.dims
+    B, A, T, K, C, S, H, D, V, M, U = (d[k] for k in "B A T K C S H D V M U".split())
+    HD = H * D
+    e = 2 if w.dtype.itemsize == 2 else 4
+    N, E = B * A, B * A * K
+    af3 = w.style == "af3"
+    slot_bytes = (3 * N * HD * e + 8 * E + E + N + (E * V * e if af3 else 0)
+                  + E * H * e + N * HD * e)
+    if af3:
+        prep = N * 2 * (4 * S * C + 4 * C * HD)
+        post = N * 2 * (HD * C + S * C + 2 * S * C + 2 * C * M + M * C + S * C)
+    else:
+        prep = N * 2 * (2 * S * C + 4 * C * HD)
+        post = N * 2 * (HD * C + S * C + 2 * S * C + 2 * C * M + M * C + S * C)
+    work = {"slot_attention": ("hbm", slot_bytes), "prep": ("mfma", prep),
+            "post": ("mfma", post)}
+    if w.stage == "encoder":
+        work["pool"] = ("mfma", N * 2 * C * U)
+    else:
+        work["token_proj"] = ("mfma", B * T * 2 * U * C)
+    return work
+
+
+def _source_sha(kernel):
+    files = {"slot_attention": "slot.hip", "prep": "prep.hip", "post": "post.hip",
+             "pool": "post.hip", "token_proj": "prep.hip", "pack": "pack.hip"}
+    h = hashlib.sha256()
+    for f in (files.get(kernel, ""), "common.hpp"):
+        p = os.path.join(ROOT, "windowed_atom_attention_amd", "csrc", f)
+        if f and os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current source of this kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get("%s@%s" % (kernel, workload))
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != _source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(name, seconds=12.0):
+    """The fp64 oracle, as it stands, on the host cores: repeated whole-block
+    runs of the same workload (sampled atoms for workloads too large to run
+    whole within the budget)."""
+    import numpy as np
+    import torch
+    import oracle
+    from windowed_atom_attention_amd.workloads import make_workload
+
+    w = make_workload(name)
+    d = w.dims
+    entries_per_atom = d["H"] * d["K"]
+    nthreads = oracle.threads(0)
+    # one probe run on a bounded sample decides how much fits the budget
+    sel = None
+    if d["B"] * d["A"] > 8192:
+        g = np.random.default_rng(0)
+        sel = np.zeros((d["B"], d["A"]), bool)
+        for b in range(d["B"]):
+            start = int(g.integers(0, d["A"] - 1024))
+            sel[b, start:start + 1024] = True
+        sel = torch.from_numpy(sel)
+    t0 = time.perf_counter()
+    r = oracle.block(**w.kwargs(), select=sel)
+    dt = time.perf_counter() - t0
+    atoms = int(r["done_atom"].sum()) if sel is not None else d["B"] * d["A"]
+    reps = max(1, min(50, int(seconds / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.block(**w.kwargs(), select=sel)
+    dt = (time.perf_counter() - t0) / reps
+    sample = ("%d whole-block run(s) of workload %s" % (reps, name) if sel is None else
+              "%d run(s) of workload %s restricted to %d atoms (1024 consecutive query "
+              "atoms per batch, their keys and tokens)" % (reps, name, atoms))
+    return {"value": atoms * entries_per_atom / dt, "unit": "entries/s",
+            "cores": nthreads, "kind": "oracle", "sample": sample,
+            "atoms_per_s": atoms / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="1",
+                    help="workload: 0, 1, 2, 3, 4a, 4b (default 1)")
+    ap.add_argument("--cache-bytes", type=float, default=768e6,
+                    help="input copies are added until they exceed this")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from windowed_atom_attention_amd import (profile_enable, profile_read,
+                                             windowed_atom_attention, workspace_bytes)
+    from windowed_atom_attention_amd.workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    w = make_workload(args.config)
+    d = w.dims
+    g = w.to(dev)
+    in_bytes = sum(t.numel() * t.element_size() for grp in
+                   (g.activations, g.masks, g.structure) for t in grp.values())
+    copies = max(1, math.ceil(args.cache_bytes / max(in_bytes, 1)))
+    sets = [g]
+    for _ in range(copies - 1):
+        sets.append(dataclasses.replace(
+            g, activations={k: v.clone() for k, v in g.activations.items()},
+            masks={k: v.clone() for k, v in g.masks.items()},
+            structure={k: v.clone() for k, v in g.structure.items()}))
+    ws = torch.empty(workspace_bytes(d, w.style, w.stage, w.dtype), dtype=torch.uint8, device=dev)
+    out = None
+
+    def step(i):
+        nonlocal out
+        s = sets[i % len(sets)]
+        out = windowed_atom_attention(**s.kwargs(), workspace=ws, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    profile_enable(True)
+    profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = profile_read()
+    profile_enable(False)
+
+    elapsed = t1 - t0
+    ms_step = elapsed * 1e3 / args.steps
+    entries = w.entries
+    value = entries * args.steps / elapsed
+    dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    work = kernel_work(w)
+    per_kernel = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in kt.items()}
+    dom = max((k for k in per_kernel if k in work), key=lambda k: per_kernel[k]["avg_us"])
+    bound, amount = work[dom]
+    avg_s = per_kernel[dom]["avg_us"] * 1e-6
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": amount / avg_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": amount / avg_s / 1e12,
+                "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = _traffic(dom, args.config)
+    roof["kernel"] = dom
+    roof["work_per_launch"] = amount
+    for k, v in per_kernel.items():
+        if k in work:
+            b, a = work[k]
+            if b == "hbm":
+                v["GB_per_s"] = a / (v["avg_us"] * 1e-6) / 1e9
+                v["frac_hbm"] = v["GB_per_s"] / HBM_PEAK_GBS
+            else:
+                v["TFLOP_per_s"] = a / (v["avg_us"] * 1e-6) / 1e12
+                v["frac_mfma"] = v["TFLOP_per_s"] / MFMA_PEAK_TFLOPS[dtype]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.config)
+
+    names = {"0": "tiny AF3 encoder fp32", "1": "AF3 encoder fp32",
+             "2": "ESMFold2 encoder bf16 radius 48", "3": "AF3 decoder bf16",
+             "4a": "large mixed AF3 encoder bf16", "4b": "large mixed ESMFold2 encoder bf16 radius 64"}
+    line = {
+        "metric": "atom-slot attention entries/sec (B*A*H*K) per block, 1xMI355X",
+        "value": value, "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": "%s (config %s): B=%d A=%d T=%d K=%d C=%d S=%d H=%d D=%d "
+                               "V=%d M=%d U=%d, %s, radius %d" % (
+                                   names[args.config], args.config, d["B"], d["A"], d["T"],
+                                   d["K"], d["C"], d["S"], d["H"], d["D"], d["V"], d["M"],
+                                   d["U"], w.stage, w.radius),
+                   "style": w.style, "stage": w.stage, "entries_per_step": entries,
+                   "atoms_per_step": w.atoms, "input_copies": copies},
+        "atoms_per_s": w.atoms * args.steps / elapsed,
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+* small instances of every workload recipe (a few tiles plus a ragged tail),
+  all outputs element by element;
+* the full-size workloads in the launch configuration the benchmark times,
+  on sampled atoms/tokens the oracle computes one by one, plus properties
+  that hold at any size;
+* masks bit-exact; the slot-attention step alone on seeded Q/K/V;
+* invariants on the GPU path itself (junk payloads, radius, batches,
+  determinism), the subnormal sigmoid tail and the pooling precondition
+  status word.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import RTOL, assert_close, compare_block, exact_zero_checks, np64, run_gpu
+from windowed_atom_attention_amd import masks as gpu_masks
+from windowed_atom_attention_amd import slot_attention as gpu_slot_attention
+from windowed_atom_attention_amd import windowed_atom_attention
+from windowed_atom_attention_amd.workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    ("0", {}),
+    ("1", dict(A=300)),
+    ("2", dict(A=300)),
+    ("3", dict(B=2, A=400)),
+    ("4a", dict(A=500)),
+    ("4b", dict(A=500)),
+    # the other style/stage/dtype combinations on the same recipes
+    ("0", dict(stage="decoder")),
+    ("0", dict(style="esmfold2")),
+    ("0", dict(style="esmfold2", stage="decoder", dtype=torch.bfloat16)),
+    ("1", dict(A=200, dtype=torch.bfloat16)),
+    ("2", dict(A=200, dtype=torch.float32, stage="decoder")),
+    ("3", dict(B=2, A=300, dtype=torch.float32, style="esmfold2")),
+    ("4a", dict(A=333, stage="decoder", radius=20)),
+]
+
+
+def _id(case):
+    name, kw = case
+    return name + "-" + "-".join("%s=%s" % (k, str(v).replace("torch.", "")) for k, v in kw.items())
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+def test_block_small_matches_oracle(case):
+    name, kw = case
+    w = make_workload(name, **kw)
+    print("case", _id(case), w.dims, flush=True)
+    gpu = run_gpu(w)
+    ref = oracle.block(**w.kwargs(), intermediates=True)
+    exact_zero_checks(w, gpu, ref["usable"], ref["allowed"])
+    compare_block(w, gpu, ref)
+
+
+@pytest.mark.parametrize("name", ["0", "2", "4a", "4b"])
+def test_masks_bit_exact(name):
+    w = make_workload(name, A=None if name == "0" else 700)
+    g = w.to("cuda")
+    us, al = gpu_masks(g.masks, g.structure, w.dims["T"], w.radius)
+    ref = oracle.block(**w.kwargs(), intermediates=True)
+    assert np.array_equal(us.cpu().numpy(), ref["usable"].astype(bool))
+    assert np.array_equal(al.cpu().numpy(), ref["allowed"].astype(bool))
+
+
+@pytest.mark.parametrize("style", ["af3", "esmfold2"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_slot_attention_step(style, dtype):
+    w = make_workload("4a" if style == "af3" else "4b", A=600, dtype=dtype)
+    ref_masks = oracle.block(**w.kwargs(), intermediates=True)
+    B, A = w.dims["B"], w.dims["A"]
+    HD = w.dims["H"] * w.dims["D"]
+    gen = torch.Generator().manual_seed(17)
+    q, k, v = (torch.randn((B, A, HD), generator=gen).to(dtype) for _ in range(3))
+    usable = torch.from_numpy(ref_masks["usable"]).bool()
+    kw = dict(eps=w.eps, style=style, radius=w.radius)
+    pair = pair_scale = w_pair = None
+    if style == "af3":
+        pair = w.activations["pair"]
+        pair_scale = w.parameters["pair_scale"]
+        w_pair = w.parameters["w_pair"]
+    ref = oracle.slot_attention(q, k, v, usable, w.structure["key_index"],
+                                w.masks["window_mask"], heads=w.dims["H"],
+                                pair=pair, pair_scale=pair_scale, w_pair=w_pair, **kw)
+    cu = lambda t: None if t is None else t.cuda()
+    att, o = gpu_slot_attention(cu(q), cu(k), cu(v), cu(usable), cu(w.structure["key_index"]),
+                                cu(w.masks["window_mask"]), heads=w.dims["H"],
+                                pair=cu(pair), pair_scale=cu(pair_scale), w_pair=cu(w_pair), **kw)
+    rtol = RTOL[dtype]
+    al = ref["allowed"].astype(bool)
+    attn = np64(att)
+    assert np.all(attn[np.broadcast_to(~al[:, None], attn.shape)] == 0.0)
+    assert_close("attention", attn, ref["attention"], rtol)
+    assert_close("o", np64(o), ref["o"], rtol)
+
+
+# ------------------------------------------------------- full size, sampled
+
+FULL = ["1", "2", "3", "4a", "4b"]
+
+
+def _sample_rows(w, n=48, seed=0):
+    B, A = w.dims["B"], w.dims["A"]
+    g = np.random.default_rng(seed)
+    sel = np.zeros((B, A), bool)
+    for b in range(B):
+        # first/last atoms, tile and block boundaries, and random atoms
+        fixed = [0, 1, 15, 16, 31, 32, A // 2, A - 33, A - 32, A - 17, A - 16, A - 1]
+        sel[b, [a for a in fixed if 0 <= a < A]] = True
+        sel[b, g.integers(0, A, n // B)] = True
+    return sel
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_block_full_size_sampled(name):
+    w = make_workload(name)
+    print("full", name, w.dims, flush=True)
+    gpu = run_gpu(w)
+    sel = _sample_rows(w)
+    ref = oracle.block(**w.kwargs(), select=torch.from_numpy(sel), intermediates=False)
+    rows = ref["done_atom"].astype(bool)
+    toks = ref["done_token"].astype(bool) if w.stage == "encoder" else None
+    assert rows[sel].all()
+    compare_block(w, gpu, ref, rows=rows, tokens=toks)
+    # properties at full size: finite outputs, attention rows sum to 1 or 0
+    for k, v in gpu.items():
+        assert torch.isfinite(v.float()).all(), k
+    rs = gpu["attention"].float().sum(-1)
+    tol = 1e-4 if w.dtype == torch.float32 else 3e-2
+    assert bool(((rs - 1).abs() < tol).logical_or(rs == 0).all())
+    g = w.to("cuda")
+    us, al = gpu_masks(g.masks, g.structure, w.dims["T"], w.radius)
+    empty = ~al.any(-1)  # rows without allowed slots: exactly zero
+    assert bool((rs.transpose(0, 1)[:, empty] == 0).all())
+    assert bool((gpu["hidden"][~us] == 0).all())
+
+
+# --------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("name,kw", [("0", {}), ("4a", dict(A=400)),
+                                     ("4b", dict(A=400)), ("3", dict(B=2, A=300))])
+def test_junk_payloads_do_not_leak_bitwise(name, kw):
+    w = make_workload(name, **kw)
+    r1 = run_gpu(w)
+    ref = oracle.block(**w.kwargs(), intermediates=True)
+    us = torch.from_numpy(ref["usable"]).bool()
+    al = torch.from_numpy(ref["allowed"]).bool()
+    w2 = make_workload(name, **kw)
+    for k in ("atom", "condition"):
+        w2.activations[k][~us] = 0.0
+    if "pair" in w2.activations:
+        w2.activations["pair"][~al] = 0.0
+    if "token" in w2.activations:
+        tv = w2.masks["token_valid"]
+        w2.activations["token"][~tv] = 0.0
+    r2 = run_gpu(w2)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+@pytest.mark.parametrize("name", ["0", "4b"])
+def test_radius_minus_one_equals_unlimited_bitwise(name):
+    w = make_workload(name, A=None if name == "0" else 300)
+    w.radius = -1
+    r1 = run_gpu(w)
+    w.radius = w.dims["A"] - 1
+    r2 = run_gpu(w)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_batches_do_not_mix_bitwise():
+    w = make_workload("3", B=3, A=256, dtype=torch.float32)
+    r1 = run_gpu(w)
+    w2 = make_workload("3", B=3, A=256, dtype=torch.float32)
+    g = torch.Generator().manual_seed(5)
+    for v in w2.activations.values():
+        v[1] = torch.randn(v[1].shape, generator=g).to(v.dtype)
+    r2 = run_gpu(w2)
+    for k in r1:  # batch is axis 0 of every output
+        assert torch.equal(r1[k][0], r2[k][0]), k
+        assert torch.equal(r1[k][2], r2[k][2]), k
+        assert not torch.equal(r1[k][1], r2[k][1]), k
+
+
+@pytest.mark.parametrize("name", ["1", "4a"])
+def test_deterministic_bitwise(name):
+    w = make_workload(name, A=1000)
+    r1 = run_gpu(w)
+    r2 = run_gpu(w)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_all_missing_windows_and_unusable_everything():
+    w = make_workload("1", A=200)
+    w.masks["window_mask"][:] = False
+    gpu = run_gpu(w)
+    ref = oracle.block(**w.kwargs(), intermediates=True)
+    assert bool((gpu["attention"] == 0).all())
+    compare_block(w, gpu, ref)
+    w = make_workload("1", A=200)
+    w.masks["valid"][:] = False
+    gpu = run_gpu(w)
+    for k, v in gpu.items():
+        assert bool((v == 0).all()), k
+
+
+def test_sigmoid_subnormal_tail_fp32():
+    """AF3 attention gate sigmoid(-95) = 5.5e-42 is a subnormal fp32 value;
+    with a zero entry state and zero transition output it is visible in
+    hidden and must not be flushed."""
+    w = make_workload("0", A=40)
+    p = w.parameters
+    p["w_residual_gate"].zero_()
+    p["b_residual_gate"][0] = -95.0
+    p["w_ff_out"].zero_()
+    w.activations["atom"][0, 5] = 0.0
+    assert bool(w.masks["valid"][0, 5])
+    gpu = run_gpu(w)
+    ref = oracle.block(**w.kwargs())
+    h = np64(gpu["hidden"])[0, 5]
+    r = ref["hidden"][0, 5]
+    big = np.abs(r) > 1e-43
+    assert big.any()
+    assert np.all(h[big] != 0.0)
+    np.testing.assert_allclose(h[big], r[big], rtol=2e-2)
+
+
+def test_status_word_reports_unsorted_tokens():
+    w = make_workload("1", A=256)
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    g = w.to("cuda")
+    windowed_atom_attention(**g.kwargs(), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    a2t = w.structure["atom_to_token"].clone()
+    a2t[0, 100:112] = 1  # a token reappearing after later ones
+    w.structure["atom_to_token"] = a2t
+    g = w.to("cuda")
+    out = windowed_atom_attention(**g.kwargs(), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    # the other outputs are unaffected by the precondition
+    ref = oracle.block(**w.kwargs())
+    assert_close("hidden", np64(out["hidden"]), ref["hidden"], RTOL[w.dtype])
+
+
+def test_strided_inputs_are_not_mutated():
+    w = make_workload("0")
+    g = w.to("cuda")
+    # a non-contiguous atom tensor with the same values
+    big = torch.zeros((1, 64, 64), device="cuda")
+    big[..., ::2] = g.activations["atom"]
+    g.activations["atom"] = big[..., ::2]
+    before = {k: v.clone() for k, v in g.activations.items()}
+    out = windowed_atom_attention(**g.kwargs())
+    torch.cuda.synchronize()
+    for k, v in g.activations.items():
+        assert torch.equal(v.nan_to_num(), before[k].nan_to_num()), k
+    ref = oracle.block(**w.kwargs())
+    assert_close("hidden", np64(out["hidden"]), ref["hidden"], RTOL[w.dtype])

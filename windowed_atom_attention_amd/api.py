@@ -1,0 +1,335 @@
+"""Python entry points over libatomattn.so.
+
+``windowed_atom_attention`` mirrors the signature on the page
+"windowed_atom_attention -- Local atom attention, encoder pooling and
+decoder skip/readout": four dicts plus eps, style, stage and radius, and a
+dict result with ``hidden``, ``attention`` and exactly one of
+``position_update`` (decoder) / ``token_output`` (encoder).
+
+This layer only marshals arguments: it checks names, shapes and dtypes,
+makes non-contiguous inputs contiguous (copies, never in place), allocates
+outputs and the workspace with torch, and passes device pointers plus the
+current HIP stream to the C ABI. Every step of the block runs in the HIP
+kernels; there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import _native as N
+
+_FLOAT_DTYPES = {torch.float32: N.F32, torch.bfloat16: N.BF16}
+_STYLES = {"af3": N.AF3, "esmfold2": N.ESMFOLD2}
+_STAGES = {"encoder": N.ENCODER, "decoder": N.DECODER}
+
+_ACT_BY_STYLE = {"af3": ("atom", "condition", "pair"),
+                 "esmfold2": ("atom", "condition", "rope_cos", "rope_sin")}
+_PARAMS_COMMON = ("w_q", "w_k", "w_v", "w_value_gate", "w_attention_out",
+                  "w_ff_gate", "w_ff_up", "w_ff_out")
+_PARAMS_STYLE = {"af3": ("cond_scale", "w_scale", "b_scale", "w_shift",
+                         "w_residual_gate", "b_residual_gate", "b_q",
+                         "pair_scale", "w_pair"),
+                 "esmfold2": ("w_mod",)}
+
+
+def _dev_ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _prep(t: torch.Tensor, dtype=None) -> torch.Tensor:
+    """Contiguous, 16-byte aligned view or copy (never modifies `t`)."""
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("expected dtype %s, got %s" % (dtype, t.dtype))
+    if not t.is_contiguous():
+        t = t.contiguous()
+    if t.data_ptr() % 16 != 0:
+        t = t.clone()
+    return t
+
+
+def _mask(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.bool:
+        raise TypeError("masks must be torch.bool, got %s" % t.dtype)
+    return _prep(t).view(torch.uint8)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def dims_from(activations, parameters, masks, structure, style, stage) -> Dict[str, int]:
+    """B,A,T,K,C,S,H,D,V,M,U read off the supplied shapes (checked)."""
+    B, A, C = activations["atom"].shape
+    S = activations["condition"].shape[-1]
+    T = masks["token_valid"].shape[-1]
+    K = structure["key_index"].shape[-1]
+    HD = parameters["w_q"].shape[-1]
+    M = parameters["w_ff_gate"].shape[-1]
+    if style == "af3":
+        H = parameters["w_pair"].shape[-1]
+        V = activations["pair"].shape[-1]
+    else:
+        D_ = activations["rope_cos"].shape[-1]
+        if D_ == 0 or HD % D_ != 0:
+            raise ValueError("rope width %d does not divide H*D=%d" % (D_, HD))
+        H = HD // D_
+        V = 1
+    if HD % H != 0:
+        raise ValueError("H=%d does not divide H*D=%d" % (H, HD))
+    D = HD // H
+    U = parameters["w_pool"].shape[-1] if stage == "encoder" else activations["token"].shape[-1]
+    d = dict(B=B, A=A, T=T, K=K, C=C, S=S, H=H, D=D, V=V, M=M, U=U)
+    expect = {
+        ("activations", "condition"): (B, A, S),
+        ("masks", "valid"): (B, A), ("masks", "token_valid"): (B, T),
+        ("masks", "window_mask"): (B, A, K),
+        ("structure", "atom_to_token"): (B, A), ("structure", "key_index"): (B, A, K),
+        ("parameters", "w_q"): (C, HD), ("parameters", "w_k"): (C, HD),
+        ("parameters", "w_v"): (C, HD), ("parameters", "w_value_gate"): (C, HD),
+        ("parameters", "w_attention_out"): (HD, C),
+        ("parameters", "w_ff_gate"): (C, M), ("parameters", "w_ff_up"): (C, M),
+        ("parameters", "w_ff_out"): (M, C),
+    }
+    if style == "af3":
+        expect.update({("activations", "pair"): (B, A, K, V),
+                       ("parameters", "cond_scale"): (3, S),
+                       ("parameters", "w_scale"): (3, S, C),
+                       ("parameters", "b_scale"): (3, C),
+                       ("parameters", "w_shift"): (3, S, C),
+                       ("parameters", "w_residual_gate"): (2, S, C),
+                       ("parameters", "b_residual_gate"): (2, C),
+                       ("parameters", "b_q"): (HD,),
+                       ("parameters", "pair_scale"): (V,),
+                       ("parameters", "w_pair"): (V, H)})
+    else:
+        expect.update({("activations", "rope_cos"): (B, A, D),
+                       ("activations", "rope_sin"): (B, A, D),
+                       ("parameters", "w_mod"): (S, 6, C)})
+    if stage == "encoder":
+        expect[("parameters", "w_pool")] = (C, U)
+    else:
+        expect.update({("activations", "token"): (B, T, U),
+                       ("parameters", "w_token"): (U, C),
+                       ("parameters", "readout_scale"): (C,),
+                       ("parameters", "w_readout"): (C, 3)})
+        if style == "esmfold2":
+            expect[("parameters", "readout_bias")] = (C,)
+    groups = dict(activations=activations, parameters=parameters, masks=masks,
+                  structure=structure)
+    for (g, name), shape in expect.items():
+        if name not in groups[g]:
+            raise KeyError("%s is missing %r" % (g, name))
+        got = tuple(groups[g][name].shape)
+        if got != tuple(shape):
+            raise ValueError("%s[%r] has shape %s, expected %s" % (g, name, got, tuple(shape)))
+    return d
+
+
+def workspace_bytes(dims: Dict[str, int], style: str, stage: str, dtype: torch.dtype) -> int:
+    nd = N.Dims(**{k: int(v) for k, v in dims.items()})
+    out = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_workspace_bytes(ctypes.byref(nd), _STYLES[style],
+                                              _STAGES[stage], _FLOAT_DTYPES[dtype],
+                                              ctypes.byref(out)),
+            "atom_attn_workspace_bytes")
+    return int(out.value)
+
+
+def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
+                            structure: dict, eps: float = 1e-05,
+                            style: str = "af3", stage: str = "decoder",
+                            radius: int = -1, *, workspace: Optional[torch.Tensor] = None,
+                            status: Optional[torch.Tensor] = None,
+                            out: Optional[Dict[str, torch.Tensor]] = None
+                            ) -> Dict[str, torch.Tensor]:
+    """One windowed atom-attention block on the GPU.
+
+    Returns {"hidden" [B,A,C], "attention" [B,H,A,K]} plus "token_output"
+    [B,T,U] (encoder) or "position_update" [B,A,3] (decoder), in the input
+    float dtype (float32 or bfloat16). `workspace` (uint8, at least
+    workspace_bytes(...) bytes), `status` (int32 [1]) and preallocated
+    `out` tensors are optional; the call is asynchronous on the current
+    stream."""
+    if style not in _STYLES:
+        raise ValueError("style must be 'af3' or 'esmfold2', got %r" % (style,))
+    if stage not in _STAGES:
+        raise ValueError("stage must be 'encoder' or 'decoder', got %r" % (stage,))
+    if isinstance(radius, bool) or int(radius) != radius or radius < -1:
+        raise ValueError("radius must be an integer >= -1")
+    d = dims_from(activations, parameters, masks, structure, style, stage)
+    atom = activations["atom"]
+    dtype = atom.dtype
+    if dtype not in _FLOAT_DTYPES:
+        raise TypeError("float tensors must be float32 or bfloat16, got %s" % dtype)
+    dev = atom.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device, got %s" % dev)
+
+    keep = []
+
+    def f(t):
+        if t is None:
+            return None
+        if t.device != dev:
+            raise ValueError("all tensors must share one device")
+        t = _prep(t, dtype)
+        keep.append(t)
+        return t
+
+    def ix(t):
+        if t.dtype != torch.int64:
+            raise TypeError("indices must be int64, got %s" % t.dtype)
+        if t.device != dev:
+            raise ValueError("all tensors must share one device")
+        t = _prep(t)
+        keep.append(t)
+        return t
+
+    def mk(t):
+        if t.device != dev:
+            raise ValueError("all tensors must share one device")
+        t = _mask(t)
+        keep.append(t)
+        return t
+
+    acts = {k: f(activations.get(k)) for k in _ACT_BY_STYLE[style]}
+    if stage == "decoder":
+        acts["token"] = f(activations["token"])
+    names = list(_PARAMS_COMMON) + list(_PARAMS_STYLE[style])
+    names += ["w_pool"] if stage == "encoder" else ["w_token", "readout_scale", "w_readout"]
+    if stage == "decoder" and style == "esmfold2":
+        names.append("readout_bias")
+    pars = {k: f(parameters[k]) for k in names}
+
+    nin = N.Inputs(
+        atom=_dev_ptr(acts.get("atom")), condition=_dev_ptr(acts.get("condition")),
+        pair=_dev_ptr(acts.get("pair")), token=_dev_ptr(acts.get("token")),
+        rope_cos=_dev_ptr(acts.get("rope_cos")), rope_sin=_dev_ptr(acts.get("rope_sin")),
+        valid=_dev_ptr(mk(masks["valid"])),
+        token_valid=_dev_ptr(mk(masks["token_valid"])),
+        window_mask=_dev_ptr(mk(masks["window_mask"])),
+        atom_to_token=_dev_ptr(ix(structure["atom_to_token"])),
+        key_index=_dev_ptr(ix(structure["key_index"])))
+    npar = N.Params(**{k: _dev_ptr(v) for k, v in pars.items()})
+
+    B, A, T, K, C, H, U = (d[k] for k in "B A T K C H U".split())
+    res = dict(out) if out is not None else {}
+
+    def o(name, shape):
+        t = res.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            res[name] = t
+        elif tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError("out[%r] must be a contiguous %s tensor of shape %s" % (name, dtype, shape))
+        return t
+
+    nout = N.Outputs(hidden=_dev_ptr(o("hidden", (B, A, C))),
+                     attention=_dev_ptr(o("attention", (B, H, A, K))))
+    if stage == "encoder":
+        nout.token_output = _dev_ptr(o("token_output", (B, T, U)))
+    else:
+        nout.position_update = _dev_ptr(o("position_update", (B, A, 3)))
+    if status is not None:
+        if status.dtype != torch.int32 or status.numel() < 1 or status.device != dev:
+            raise ValueError("status must be an int32 device tensor with >= 1 element")
+        nout.status = status.data_ptr()
+
+    need = workspace_bytes(d, style, stage, dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise ValueError("workspace needs %d bytes on %s" % (need, dev))
+    nd = N.Dims(**{k: int(v) for k, v in d.items()})
+    fn = N.lib().atom_attn_encoder if stage == "encoder" else N.lib().atom_attn_decoder
+    with torch.cuda.device(dev):
+        rc = fn(ctypes.byref(nd), _STYLES[style], _FLOAT_DTYPES[dtype],
+                ctypes.byref(nin), ctypes.byref(npar), float(eps), int(radius),
+                ctypes.byref(nout), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    N.check(rc, "atom_attn_%s" % stage)
+    # Copies made above are freed when `keep` goes away; torch's allocator
+    # hands their memory only to later work on this same stream, which runs
+    # after the kernels, so no synchronisation is needed.
+    del keep
+    names_out = ["hidden", "attention", "token_output" if stage == "encoder" else "position_update"]
+    return {k: res[k] for k in names_out}
+
+
+def masks(masks: dict, structure: dict, T: int, radius: int = -1):
+    """usable [B,A] and allowed [B,A,K] (torch.bool) computed on the GPU."""
+    valid = _mask(masks["valid"])
+    tv = _mask(masks["token_valid"])
+    wm = _mask(masks["window_mask"])
+    a2t = _prep(structure["atom_to_token"], torch.int64)
+    ki = _prep(structure["key_index"], torch.int64)
+    B, A, K = ki.shape
+    dev = ki.device
+    usable = torch.empty((B, A), dtype=torch.uint8, device=dev)
+    allowed = torch.empty((B, A, K), dtype=torch.uint8, device=dev)
+    nd = N.Dims(B=B, A=A, T=int(T), K=K, C=1, S=1, H=1, D=1, V=1, M=1, U=1)
+    nin = N.Inputs(valid=valid.data_ptr(), token_valid=tv.data_ptr(),
+                   window_mask=wm.data_ptr(), atom_to_token=a2t.data_ptr(),
+                   key_index=ki.data_ptr())
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_masks(ctypes.byref(nd), ctypes.byref(nin), int(radius),
+                                     usable.data_ptr(), allowed.data_ptr(),
+                                     _stream_handle(dev))
+    N.check(rc, "atom_attn_masks")
+    torch.cuda.current_stream(dev).synchronize()
+    return usable.bool(), allowed.bool()
+
+
+def slot_attention(q, k, v, usable, key_index, window_mask, heads: int,
+                   eps: float = 1e-5, style: str = "af3", radius: int = -1,
+                   pair=None, pair_scale=None, w_pair=None):
+    """The slot-attention step alone on supplied q/k/v rows [B,A,H*D].
+    Returns attention [B,H,A,K] and o [B,A,H*D]."""
+    dtype = q.dtype
+    q, k, v = (_prep(x, dtype) for x in (q, k, v))
+    B, A, HD = q.shape
+    K = key_index.shape[-1]
+    H = int(heads)
+    D = HD // H
+    us = _prep(usable.to(torch.uint8))
+    ki = _prep(key_index, torch.int64)
+    wm = _mask(window_mask)
+    V = 1
+    ptrs = [None, None, None]
+    keep = []
+    if style == "af3":
+        pair, pair_scale, w_pair = (_prep(x, dtype) for x in (pair, pair_scale, w_pair))
+        keep += [pair, pair_scale, w_pair]
+        V = pair.shape[-1]
+        ptrs = [pair.data_ptr(), pair_scale.data_ptr(), w_pair.data_ptr()]
+    dev = q.device
+    att = torch.empty((B, H, A, K), dtype=dtype, device=dev)
+    o = torch.empty((B, A, HD), dtype=dtype, device=dev)
+    nd = N.Dims(B=B, A=A, T=1, K=K, C=1, S=1, H=H, D=D, V=V, M=1, U=1)
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_slot_attention(
+            ctypes.byref(nd), _STYLES[style], _FLOAT_DTYPES[dtype], float(eps),
+            int(radius), us.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            ki.data_ptr(), wm.data_ptr(), ptrs[0], ptrs[1], ptrs[2],
+            att.data_ptr(), o.data_ptr(), _stream_handle(dev))
+    N.check(rc, "atom_attn_slot_attention")
+    torch.cuda.current_stream(dev).synchronize()
+    return att, o
+
+
+def profile_enable(on: bool = True) -> None:
+    N.check(N.lib().atom_attn_profile_enable(1 if on else 0), "atom_attn_profile_enable")
+
+
+def profile_read(max_kernels: int = 16) -> Dict[str, tuple]:
+    """{kernel name: (total milliseconds, launches)} since the last read."""
+    names = (ctypes.c_char_p * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int64 * max_kernels)()
+    n = N.lib().atom_attn_profile_read(names, ms, cnt, max_kernels)
+    if n < 0:
+        N.check(n, "atom_attn_profile_read")
+    return {names[i].decode(): (ms[i], int(cnt[i])) for i in range(n)}

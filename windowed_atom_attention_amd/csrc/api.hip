@@ -1,0 +1,502 @@
+// api.hip -- the C ABI of libatomattn.so (declared in include/atom_attn.h):
+// argument checks, workspace layout, weight packing jobs and the launch
+// sequence of one block call. Host code only; every step of the block runs
+// in the kernels of pack/prep/slot/post.hip.
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/atom_attn.h"
+#include "kernels.hpp"
+
+using namespace waa;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+// ------------------------------------------------------------ profiler
+
+struct ProfRec {
+    int kernel;
+    hipEvent_t start, stop;
+};
+struct Profiler {
+    bool on = false;
+    std::vector<ProfRec> recs;
+    std::vector<hipEvent_t> pool;
+    const char *names[16] = {"pack", "token_proj", "prep", "slot_attention",
+                             "post", "pool", "masks"};
+    int nnames = 7;
+};
+Profiler g_prof;
+
+hipEvent_t prof_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+enum { KN_PACK = 0, KN_TOKEN = 1, KN_PREP = 2, KN_SLOT = 3, KN_POST = 4, KN_POOL = 5, KN_MASKS = 6 };
+
+// Run one launcher, bracketed by events when profiling is on.
+template <typename F> int timed(int kernel, hipStream_t s, F launch) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (g_prof.on) {
+        e0 = prof_event();
+        e1 = prof_event();
+        if (e0 && e1)
+            (void)hipEventRecord(e0, s);
+    }
+    hipError_t err = launch();
+    if (g_prof.on && e0 && e1) {
+        (void)hipEventRecord(e1, s);
+        g_prof.recs.push_back({kernel, e0, e1});
+    }
+    return err == hipSuccess ? ATOM_ATTN_OK : ATOM_ATTN_ELAUNCH;
+}
+
+// ------------------------------------------------------------ checks
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_valid(const atom_attn_dims *d) {
+    return d && d->B >= 1 && d->A >= 1 && d->T >= 1 && d->K >= 1 && d->C >= 1 &&
+           d->S >= 1 && d->H >= 1 && d->D >= 1 && d->V >= 1 && d->M >= 1 &&
+           d->U >= 1;
+}
+
+// eps must be finite and stay > 0 once represented in the input dtype.
+bool eps_valid(double eps, int dtype) {
+    if (!(eps > 0.0) || !std::isfinite(eps))
+        return false;
+    const float f = (float)eps;
+    if (!(f > 0.0f) || !std::isfinite(f))
+        return false;
+    if (dtype == ATOM_ATTN_BF16) {
+        uint32_t u;
+        std::memcpy(&u, &f, 4);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        if ((u >> 16) == 0)
+            return false;
+    }
+    return true;
+}
+
+bool mult32_le(int64_t x, int64_t cap) { return x % 32 == 0 && x <= cap; }
+
+// The kernels' supported set; returns ATOM_ATTN_OK or EUNSUPPORTED.
+int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
+    const int64_t HD = d->H * d->D;
+    if (!mult32_le(d->C, 512) || !mult32_le(d->S, 512) || !mult32_le(HD, 512) ||
+        !mult32_le(d->M, 512) || !mult32_le(d->U, 512))
+        return ATOM_ATTN_EUNSUPPORTED;
+    if (d->D % 16 != 0 || d->D > 128 || d->K > 512)
+        return ATOM_ATTN_EUNSUPPORTED;
+    if (style == ATOM_ATTN_AF3 && (d->V % 8 != 0 || d->V > 64))
+        return ATOM_ATTN_EUNSUPPORTED;
+    if (d->B * d->A > (int64_t)1 << 30 || d->B * d->T > (int64_t)1 << 30 ||
+        d->B * d->A * d->K > ((int64_t)1 << 31) - 1 ||
+        d->B * d->H * d->A * d->K > ((int64_t)1 << 31) - 1)
+        return ATOM_ATTN_EUNSUPPORTED;
+    const Dims dd{(int)d->B, (int)d->A, (int)d->T, (int)d->K, (int)d->C, (int)d->S,
+                  (int)d->H, (int)d->D, (int)d->V, (int)d->M, (int)d->U};
+    if (prep_lds_bytes(dd, dtype, style) > kMaxLds ||
+        post_lds_bytes(dd, dtype, style) > kMaxLds ||
+        !slot_supported(dd, dtype, style))
+        return ATOM_ATTN_EUNSUPPORTED;
+    if (stage == ATOM_ATTN_ENCODER && pool_lds_bytes(dd, dtype) > kMaxLds)
+        return ATOM_ATTN_EUNSUPPORTED;
+    if (stage == ATOM_ATTN_DECODER && token_proj_lds_bytes(dd, dtype) > kMaxLds)
+        return ATOM_ATTN_EUNSUPPORTED;
+    return ATOM_ATTN_OK;
+}
+
+// ------------------------------------------------------------ workspace
+
+struct Layout {
+    size_t packed, q, k, v, g, o, usable, tokproj, total;
+    int64_t pack_units;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Packed weight matrices of one call, in the order they are laid out.
+struct Mat {
+    int64_t *off;
+    const void *src;
+    int64_t ld;
+    int kd, n;
+};
+
+void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
+               const atom_attn_params *par, PackedOffsets *off,
+               std::vector<Mat> *mats) {
+    const int C = (int)d->C, S = (int)d->S, HD = (int)(d->H * d->D), M = (int)d->M,
+              U = (int)d->U;
+    auto at = [&](const void *base, int64_t elems) -> const void * {
+        return base ? (const char *)base + elems * esz : nullptr;
+    };
+    for (int j = 0; j < 3; ++j) off->w_scale[j] = off->w_shift[j] = -1;
+    for (int j = 0; j < 2; ++j) off->w_rg[j] = -1;
+    for (int j = 0; j < 6; ++j) off->w_mod[j] = -1;
+    off->w_q = off->w_k = off->w_v = off->w_vg = off->w_ao = -1;
+    off->ff_gate = off->ff_up = off->ff_out = off->w_pool = off->w_token = -1;
+    if (style == ATOM_ATTN_AF3) {
+        for (int j = 0; j < 3; ++j) {
+            mats->push_back({&off->w_scale[j], at(par ? par->w_scale : nullptr, (int64_t)j * S * C), C, S, C});
+            mats->push_back({&off->w_shift[j], at(par ? par->w_shift : nullptr, (int64_t)j * S * C), C, S, C});
+        }
+        for (int j = 0; j < 2; ++j)
+            mats->push_back({&off->w_rg[j], at(par ? par->w_residual_gate : nullptr, (int64_t)j * S * C), C, S, C});
+    } else {
+        for (int j = 0; j < 6; ++j)
+            mats->push_back({&off->w_mod[j], at(par ? par->w_mod : nullptr, (int64_t)j * C), 6 * C, S, C});
+    }
+    mats->push_back({&off->w_q, par ? par->w_q : nullptr, HD, C, HD});
+    mats->push_back({&off->w_k, par ? par->w_k : nullptr, HD, C, HD});
+    mats->push_back({&off->w_v, par ? par->w_v : nullptr, HD, C, HD});
+    mats->push_back({&off->w_vg, par ? par->w_value_gate : nullptr, HD, C, HD});
+    mats->push_back({&off->w_ao, par ? par->w_attention_out : nullptr, C, HD, C});
+    mats->push_back({&off->ff_gate, par ? par->w_ff_gate : nullptr, M, C, M});
+    mats->push_back({&off->ff_up, par ? par->w_ff_up : nullptr, M, C, M});
+    mats->push_back({&off->ff_out, par ? par->w_ff_out : nullptr, C, M, C});
+    if (stage == ATOM_ATTN_ENCODER)
+        mats->push_back({&off->w_pool, par ? par->w_pool : nullptr, U, C, U});
+    else
+        mats->push_back({&off->w_token, par ? par->w_token : nullptr, C, U, C});
+    int64_t o = 0;
+    for (auto &m : *mats) {
+        *m.off = o;
+        o += packed_units(m.kd, m.n, esz);
+    }
+}
+
+Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
+    const int esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
+    PackedOffsets off;
+    std::vector<Mat> mats;
+    list_mats(d, style, stage, esz, nullptr, &off, &mats);
+    int64_t units = 0;
+    for (auto &m : mats)
+        units += packed_units(m.kd, m.n, esz);
+    Layout L;
+    const size_t N = (size_t)(d->B * d->A);
+    const size_t rowb = (size_t)(d->H * d->D) * esz;
+    size_t o = 0;
+    L.pack_units = units;
+    L.packed = o; o = up256(o + (size_t)units * 16);
+    L.q = o; o = up256(o + N * rowb);
+    L.k = o; o = up256(o + N * rowb);
+    L.v = o; o = up256(o + N * rowb);
+    L.g = o; o = up256(o + N * rowb);
+    L.o = o; o = up256(o + N * rowb);
+    L.usable = o; o = up256(o + N);
+    L.tokproj = o;
+    if (stage == ATOM_ATTN_DECODER)
+        o = up256(o + (size_t)(d->B * d->T * d->C) * 4);
+    L.total = o;
+    return L;
+}
+
+int check_common(const atom_attn_dims *d, int style, int stage, int dtype) {
+    if (!dims_valid(d))
+        return ATOM_ATTN_EINVAL;
+    if (style != ATOM_ATTN_AF3 && style != ATOM_ATTN_ESMFOLD2)
+        return ATOM_ATTN_EINVAL;
+    if (stage != ATOM_ATTN_ENCODER && stage != ATOM_ATTN_DECODER)
+        return ATOM_ATTN_EINVAL;
+    if (dtype != ATOM_ATTN_F32 && dtype != ATOM_ATTN_BF16)
+        return ATOM_ATTN_EINVAL;
+    if (style == ATOM_ATTN_ESMFOLD2 && d->D % 2 != 0)
+        return ATOM_ATTN_EODD_HEAD;
+    return ATOM_ATTN_OK;
+}
+
+int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
+              const atom_attn_inputs *in, const atom_attn_params *par,
+              double eps, int64_t radius, atom_attn_outputs *out,
+              void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_common(d, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!in || !par || !out || !eps_valid(eps, dtype) || radius < -1)
+        return ATOM_ATTN_EINVAL;
+    const bool af3 = style == ATOM_ATTN_AF3, enc = stage == ATOM_ATTN_ENCODER;
+    // pointers each style/stage needs
+    const void *need_f[] = {in->atom, in->condition, par->w_q, par->w_k, par->w_v,
+                            par->w_value_gate, par->w_attention_out, par->w_ff_gate,
+                            par->w_ff_up, par->w_ff_out, out->hidden, out->attention};
+    for (const void *p : need_f)
+        if (!p || !aligned16(p))
+            return ATOM_ATTN_EINVAL;
+    if (!in->valid || !in->token_valid || !in->window_mask || !in->atom_to_token ||
+        !in->key_index)
+        return ATOM_ATTN_EINVAL;
+    if (af3) {
+        const void *nf[] = {in->pair, par->cond_scale, par->w_scale, par->b_scale,
+                            par->w_shift, par->w_residual_gate, par->b_residual_gate,
+                            par->b_q, par->pair_scale, par->w_pair};
+        for (const void *p : nf)
+            if (!p || !aligned16(p))
+                return ATOM_ATTN_EINVAL;
+    } else {
+        const void *nf[] = {in->rope_cos, in->rope_sin, par->w_mod};
+        for (const void *p : nf)
+            if (!p || !aligned16(p))
+                return ATOM_ATTN_EINVAL;
+    }
+    if (enc) {
+        if (!par->w_pool || !out->token_output || !aligned16(par->w_pool) ||
+            !aligned16(out->token_output))
+            return ATOM_ATTN_EINVAL;
+    } else {
+        const void *nf[] = {in->token, par->w_token, par->readout_scale, par->w_readout,
+                            out->position_update};
+        for (const void *p : nf)
+            if (!p || !aligned16(p))
+                return ATOM_ATTN_EINVAL;
+        if (!af3 && !par->readout_bias)
+            return ATOM_ATTN_EINVAL;
+    }
+    rc = shape_supported(d, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    const Layout L = layout_of(d, style, stage, dtype);
+    if (!workspace || !aligned16(workspace) || ws_bytes < L.total)
+        return ATOM_ATTN_EWORKSPACE;
+
+    const int esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
+    const int dt = dtype == ATOM_ATTN_BF16 ? 1 : 0;
+    const int st = af3 ? STYLE_AF3 : STYLE_ESM;
+    const int sg = enc ? STAGE_ENCODER : STAGE_DECODER;
+    char *ws = (char *)workspace;
+    hipStream_t s = (hipStream_t)stream;
+
+    PackedOffsets off;
+    std::vector<Mat> mats;
+    list_mats(d, style, stage, esz, par, &off, &mats);
+    PackArgs pa;
+    std::memset(&pa, 0, sizeof(pa));
+    pa.njobs = (int)mats.size();
+    for (size_t i = 0; i < mats.size(); ++i)
+        pa.job[i] = PackJob{mats[i].src, mats[i].ld, mats[i].kd, mats[i].n, *mats[i].off};
+    pa.total = L.pack_units;
+    pa.out = (uint4 *)(ws + L.packed);
+
+    BlockArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.d = Dims{(int)d->B, (int)d->A, (int)d->T, (int)d->K, (int)d->C, (int)d->S,
+               (int)d->H, (int)d->D, (int)d->V, (int)d->M, (int)d->U};
+    a.eps = (float)eps;
+    a.radius = radius;
+    a.atom = in->atom; a.condition = in->condition; a.pair = in->pair;
+    a.token = in->token; a.rope_cos = in->rope_cos; a.rope_sin = in->rope_sin;
+    a.valid = in->valid; a.token_valid = in->token_valid; a.window_mask = in->window_mask;
+    a.atom_to_token = in->atom_to_token; a.key_index = in->key_index;
+    a.cond_scale = par->cond_scale; a.b_scale = par->b_scale;
+    a.b_rg = par->b_residual_gate; a.b_q = par->b_q;
+    a.readout_scale = par->readout_scale; a.readout_bias = par->readout_bias;
+    a.w_readout = par->w_readout;
+    a.pk = (const uint4 *)(ws + L.packed);
+    a.off = off;
+    a.q = ws + L.q; a.k = ws + L.k; a.v = ws + L.v; a.g = ws + L.g; a.o = ws + L.o;
+    a.usable = (uint8_t *)(ws + L.usable);
+    a.tokproj = enc ? nullptr : (float *)(ws + L.tokproj);
+    a.hidden = out->hidden; a.attention = out->attention;
+    a.token_output = out->token_output; a.position_update = out->position_update;
+    a.status = out->status;
+
+    SlotArgs sa;
+    sa.B = a.d.B; sa.A = a.d.A; sa.K = a.d.K; sa.H = a.d.H; sa.D = a.d.D; sa.V = a.d.V;
+    sa.eps = a.eps;
+    sa.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d->D));
+    sa.radius = radius;
+    sa.usable = a.usable; sa.window_mask = in->window_mask; sa.key_index = in->key_index;
+    sa.q = a.q; sa.k = a.k; sa.v = a.v;
+    sa.pair = in->pair; sa.pair_scale = par->pair_scale; sa.w_pair = par->w_pair;
+    sa.attention = out->attention; sa.o = a.o;
+
+    if ((rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)
+        return rc;
+    if (!enc && (rc = timed(KN_TOKEN, s, [&] { return launch_token_proj(a, dt, s); })) != ATOM_ATTN_OK)
+        return rc;
+    if ((rc = timed(KN_PREP, s, [&] { return launch_prep(a, dt, st, sg, s); })) != ATOM_ATTN_OK)
+        return rc;
+    if ((rc = timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); })) != ATOM_ATTN_OK)
+        return rc;
+    if ((rc = timed(KN_POST, s, [&] { return launch_post(a, dt, st, sg, s); })) != ATOM_ATTN_OK)
+        return rc;
+    if (enc && (rc = timed(KN_POOL, s, [&] { return launch_pool(a, dt, s); })) != ATOM_ATTN_OK)
+        return rc;
+    return ATOM_ATTN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int atom_attn_version(void) { return kAbiVersion; }
+
+const char *atom_attn_error_string(int code) {
+    switch (code) {
+    case ATOM_ATTN_OK:
+        return "ok";
+    case ATOM_ATTN_EINVAL:
+        return "invalid argument (enum, dim < 1, missing or misaligned pointer, "
+               "eps not finite and > 0 in the dtype, radius < -1)";
+    case ATOM_ATTN_EODD_HEAD:
+        return "ESMFold2 style needs an even head width D";
+    case ATOM_ATTN_EWORKSPACE:
+        return "workspace missing, misaligned or smaller than atom_attn_workspace_bytes()";
+    case ATOM_ATTN_ELAUNCH:
+        return "the HIP runtime refused a kernel launch";
+    case ATOM_ATTN_EUNSUPPORTED:
+        return "shape outside the supported set (C, S, H*D, M, U multiples of 32 "
+               "and <= 512; D a multiple of 16 and <= 128; K <= 512; AF3 V a "
+               "multiple of 8 and <= 64)";
+    default:
+        return "unknown status";
+    }
+}
+
+int atom_attn_workspace_bytes(const atom_attn_dims *dims, int style, int stage,
+                              int dtype, size_t *bytes) {
+    int rc = check_common(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!bytes)
+        return ATOM_ATTN_EINVAL;
+    rc = shape_supported(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    *bytes = layout_of(dims, style, stage, dtype).total;
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_encoder(const atom_attn_dims *dims, int style, int dtype,
+                      const atom_attn_inputs *in, const atom_attn_params *par,
+                      double eps, int64_t radius, atom_attn_outputs *out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    return run_block(dims, style, ATOM_ATTN_ENCODER, dtype, in, par, eps, radius,
+                     out, workspace, workspace_bytes, stream);
+}
+
+int atom_attn_decoder(const atom_attn_dims *dims, int style, int dtype,
+                      const atom_attn_inputs *in, const atom_attn_params *par,
+                      double eps, int64_t radius, atom_attn_outputs *out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    return run_block(dims, style, ATOM_ATTN_DECODER, dtype, in, par, eps, radius,
+                     out, workspace, workspace_bytes, stream);
+}
+
+int atom_attn_masks(const atom_attn_dims *dims, const atom_attn_inputs *in,
+                    int64_t radius, uint8_t *usable, uint8_t *allowed,
+                    void *stream) {
+    if (!dims || dims->B < 1 || dims->A < 1 || dims->T < 1 || dims->K < 1 || !in ||
+        radius < -1 || !in->valid || !in->token_valid || !in->window_mask ||
+        !in->atom_to_token || !in->key_index || (!usable && !allowed))
+        return ATOM_ATTN_EINVAL;
+    if (dims->B * dims->A * dims->K > ((int64_t)1 << 40))
+        return ATOM_ATTN_EUNSUPPORTED;
+    const Dims d{(int)dims->B, (int)dims->A, (int)dims->T, (int)dims->K, 1, 1, 1, 1, 1, 1, 1};
+    hipStream_t s = (hipStream_t)stream;
+    return timed(KN_MASKS, s, [&] {
+        return launch_masks(d, in->valid, in->token_valid, in->window_mask,
+                            in->atom_to_token, in->key_index, radius, usable,
+                            allowed, s);
+    });
+}
+
+int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
+                             double eps, int64_t radius, const uint8_t *usable,
+                             const void *q, const void *k, const void *v,
+                             const int64_t *key_index,
+                             const uint8_t *window_mask, const void *pair,
+                             const void *pair_scale, const void *w_pair,
+                             void *attention, void *o, void *stream) {
+    if (!dims || dims->B < 1 || dims->A < 1 || dims->K < 1 || dims->H < 1 ||
+        dims->D < 1 || (style == ATOM_ATTN_AF3 && dims->V < 1))
+        return ATOM_ATTN_EINVAL;
+    if (style != ATOM_ATTN_AF3 && style != ATOM_ATTN_ESMFOLD2)
+        return ATOM_ATTN_EINVAL;
+    if (dtype != ATOM_ATTN_F32 && dtype != ATOM_ATTN_BF16)
+        return ATOM_ATTN_EINVAL;
+    if (!eps_valid(eps, dtype) || radius < -1)
+        return ATOM_ATTN_EINVAL;
+    if (!usable || !key_index || !window_mask)
+        return ATOM_ATTN_EINVAL;
+    const void *need[] = {q, k, v, attention, o};
+    for (const void *p : need)
+        if (!p || !aligned16(p))
+            return ATOM_ATTN_EINVAL;
+    if (style == ATOM_ATTN_AF3 && (!pair || !pair_scale || !w_pair || !aligned16(pair)))
+        return ATOM_ATTN_EINVAL;
+    if (style == ATOM_ATTN_ESMFOLD2 && dims->D % 2 != 0)
+        return ATOM_ATTN_EODD_HEAD;
+    const int64_t HD = dims->H * dims->D;
+    if (HD % 32 != 0 || HD > 512)
+        return ATOM_ATTN_EUNSUPPORTED;
+    const Dims d{(int)dims->B, (int)dims->A, 1, (int)dims->K, 32, 32, (int)dims->H,
+                 (int)dims->D, style == ATOM_ATTN_AF3 ? (int)dims->V : 8, 32, 32};
+    const int dt = dtype == ATOM_ATTN_BF16 ? 1 : 0;
+    const int st = style == ATOM_ATTN_AF3 ? STYLE_AF3 : STYLE_ESM;
+    if (!slot_supported(d, dt, st) || dims->B * dims->A > ((int64_t)1 << 30) ||
+        dims->B * dims->H * dims->A * dims->K > ((int64_t)1 << 31) - 1)
+        return ATOM_ATTN_EUNSUPPORTED;
+    SlotArgs sa;
+    sa.B = d.B; sa.A = d.A; sa.K = d.K; sa.H = d.H; sa.D = d.D; sa.V = d.V;
+    sa.eps = (float)eps;
+    sa.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d.D));
+    sa.radius = radius;
+    sa.usable = usable; sa.window_mask = window_mask; sa.key_index = key_index;
+    sa.q = q; sa.k = k; sa.v = v;
+    sa.pair = pair; sa.pair_scale = pair_scale; sa.w_pair = w_pair;
+    sa.attention = attention; sa.o = o;
+    hipStream_t s = (hipStream_t)stream;
+    return timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); });
+}
+
+int atom_attn_profile_enable(int on) {
+    g_prof.on = on != 0;
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_profile_read(const char **names, double *total_ms, int64_t *launches,
+                           int max) {
+    double tot[16] = {0};
+    int64_t cnt[16] = {0};
+    for (auto &r : g_prof.recs) {
+        if (hipEventSynchronize(r.stop) != hipSuccess)
+            return ATOM_ATTN_ELAUNCH;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+            return ATOM_ATTN_ELAUNCH;
+        tot[r.kernel] += ms;
+        cnt[r.kernel] += 1;
+        g_prof.pool.push_back(r.start);
+        g_prof.pool.push_back(r.stop);
+    }
+    g_prof.recs.clear();
+    int w = 0;
+    for (int i = 0; i < g_prof.nnames && w < max; ++i) {
+        if (cnt[i] == 0)
+            continue;
+        if (names)
+            names[w] = g_prof.names[i];
+        if (total_ms)
+            total_ms[w] = tot[i];
+        if (launches)
+            launches[w] = cnt[i];
+        ++w;
+    }
+    return w;
+}
+
+} // extern "C"

@@ -1,0 +1,183 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libatomattn.
+//
+// Storage types: float (fp32) or bf16_t (bfloat16 bits). All arithmetic is
+// fp32. Matrix products run on the CDNA4 matrix cores (MFMA) with 16-byte
+// per-lane operand chunks:
+//   * 32x32 output tiles (projections): v_mfma_f32_32x32x16_bf16 for bf16,
+//     four v_mfma_f32_32x32x2_f32 for fp32;
+//   * 16x16 output tiles (slot attention): v_mfma_f32_16x16x32_bf16, or four
+//     v_mfma_f32_16x16x4_f32.
+// The k order inside a chunk is a free choice (a matrix product sums over k
+// in any order), so each lane always supplies 16 contiguous bytes of its
+// row (A operand) or column (B operand): lane half h (32x32) or lane
+// quarter g (16x16) supplies k = chunk_base + h*HALF + e (resp. g*QUARTER+e).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace waa {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16_t x) {
+    return __uint_as_float(((uint32_t)x) << 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// Logistic function in two branches so that a very negative argument gives
+// exp(z)/(1+exp(z)) -- down to the subnormal range -- instead of 1/inf.
+// expf/division are the IEEE library versions (no fast-math, no FTZ).
+__device__ __forceinline__ float sigmoid_f(float z) {
+    if (z >= 0.0f)
+        return 1.0f / (1.0f + expf(-z));
+    float e = expf(z);
+    return e / (1.0f + e);
+}
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
+
+// ---------------------------------------------------------- reductions
+// Butterfly reductions over aligned lane groups of width W (power of 2).
+
+template <int W> __device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1)
+        v += __shfl_xor(v, m, W);
+    return v;
+}
+template <int W> __device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1)
+        v = fmaxf(v, __shfl_xor(v, m, W));
+    return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        v = min(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        v = max(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// -------------------------------------------------------- MFMA wrappers
+
+template <typename T> struct Mma32;
+template <> struct Mma32<bf16_t> {
+    static constexpr int KC = 16;  // k values per 16-byte chunk
+    static constexpr int HALF = 8; // k values per lane half
+    __device__ static __forceinline__ void mma(f32x16_t &acc, uint4 a, uint4 b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+            acc, 0, 0, 0);
+    }
+};
+template <> struct Mma32<float> {
+    static constexpr int KC = 8;
+    static constexpr int HALF = 4;
+    __device__ static __forceinline__ void mma(f32x16_t &acc, uint4 a, uint4 b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    }
+};
+
+template <typename T> struct Mma16;
+template <> struct Mma16<bf16_t> {
+    static constexpr int KC = 32;
+    static constexpr int QUARTER = 8;
+    __device__ static __forceinline__ void mma(f32x4_t &acc, uint4 a, uint4 b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+            acc, 0, 0, 0);
+    }
+};
+template <> struct Mma16<float> {
+    static constexpr int KC = 16;
+    static constexpr int QUARTER = 4;
+    __device__ static __forceinline__ void mma(f32x4_t &acc, uint4 a, uint4 b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    }
+};
+
+// Output element v of a 32x32 accumulator in this lane: (row, col).
+__device__ __forceinline__ int acc32_row(int v, int lane) {
+    return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+}
+__device__ __forceinline__ int acc32_col(int lane) { return lane & 31; }
+// Output element v of a 16x16 accumulator in this lane.
+__device__ __forceinline__ int acc16_row(int v, int lane) { return (lane >> 4) * 4 + v; }
+__device__ __forceinline__ int acc16_col(int lane) { return lane & 15; }
+
+// Padding (in elements) that makes a row pitch 16 bytes longer than the
+// data, so that the 32 rows of an operand tile start in different LDS banks.
+template <typename T> constexpr int pad16() { return 16 / (int)sizeof(T); }
+
+// acc += A[32 x Kd] * B[Kd x 32-column block].
+// A: LDS tile, row-major, pitch lda elements (16-byte aligned rows).
+// B: packed weight block (see pack.hip): chunk kc of this column block at
+//    Bp[kc*64 + lane], 16 bytes per lane.
+template <typename T>
+__device__ __forceinline__ void gemm32(f32x16_t &acc, const T *A, int lda,
+                                       int nkc, const uint4 *__restrict__ Bp) {
+    const int lane = threadIdx.x & 63;
+    const T *arow = A + (lane & 31) * lda + (lane >> 5) * Mma32<T>::HALF;
+#pragma unroll 4
+    for (int kc = 0; kc < nkc; ++kc) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * Mma32<T>::KC);
+        const uint4 b = Bp[kc * 64 + lane];
+        Mma32<T>::mma(acc, a, b);
+    }
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+    f32x16_t z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        z[i] = 0.0f;
+    return z;
+}
+__device__ __forceinline__ f32x4_t zero4() {
+    f32x4_t z;
+    z[0] = z[1] = z[2] = z[3] = 0.0f;
+    return z;
+}
+
+// Map the hardware dispatch order (round-robin over the 8 XCDs of MI355X)
+// to a logical block index such that consecutive logical blocks run on the
+// same XCD and share its L2. Bijective on [0, nblk).
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+    const int X = 8;
+    const int full = (nblk / X) * X;
+    if (bid >= full)
+        return bid;
+    return (bid % X) * (full / X) + bid / X;
+}
+
+} // namespace waa

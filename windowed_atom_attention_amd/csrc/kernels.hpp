@@ -1,0 +1,105 @@
+// kernels.hpp -- argument blocks and host launchers of the libatomattn
+// kernels (internal to the library; the public ABI is include/atom_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace waa {
+
+enum { STYLE_AF3 = 0, STYLE_ESM = 1 };
+enum { STAGE_ENCODER = 0, STAGE_DECODER = 1 };
+
+struct Dims {
+    int B, A, T, K, C, S, H, D, V, M, U;
+};
+
+// Offsets, in 16-byte units, of each packed weight matrix inside the packed
+// area of the workspace (-1 = absent).
+struct PackedOffsets {
+    int64_t w_scale[3], w_shift[3], w_rg[2], w_mod[6];
+    int64_t w_q, w_k, w_v, w_vg, w_ao, ff_gate, ff_up, ff_out, w_pool, w_token;
+};
+
+// Everything the projection, post and pool kernels read or write.
+struct BlockArgs {
+    Dims d;
+    float eps;
+    int64_t radius;
+    // inputs
+    const void *atom, *condition, *pair, *token, *rope_cos, *rope_sin;
+    const uint8_t *valid, *token_valid, *window_mask;
+    const int64_t *atom_to_token, *key_index;
+    // vector parameters (read directly, storage dtype)
+    const void *cond_scale, *b_scale, *b_rg, *b_q, *readout_scale,
+        *readout_bias, *w_readout;
+    // packed matrices
+    const uint4 *pk;
+    PackedOffsets off;
+    // workspace
+    void *q, *k, *v, *g, *o;
+    uint8_t *usable;
+    float *tokproj;
+    // outputs
+    void *hidden, *attention, *token_output, *position_update;
+    int32_t *status;
+};
+
+// The slot-attention kernel's arguments.
+struct SlotArgs {
+    int B, A, K, H, D, V;
+    float eps, inv_sqrt_d;
+    int64_t radius;
+    const uint8_t *usable, *window_mask;
+    const int64_t *key_index;
+    const void *q, *k, *v, *pair, *pair_scale, *w_pair;
+    void *attention, *o;
+};
+
+// One matrix to pack: src[r*ld + c] for r < kd, c < n (storage dtype).
+struct PackJob {
+    const void *src;
+    int64_t ld;
+    int32_t kd, n;
+    int64_t dst; // offset in 16-byte units
+};
+constexpr int kMaxPackJobs = 32;
+struct PackArgs {
+    PackJob job[kMaxPackJobs];
+    int njobs;
+    int64_t total; // 16-byte units over all jobs
+    uint4 *out;
+};
+
+// 16-byte units a packed [kd x n] matrix takes (kd, n multiples of 32).
+inline int64_t packed_units(int kd, int n, int dtype_bytes) {
+    return (int64_t)kd * n * dtype_bytes / 16;
+}
+
+// Host launchers; dtype 0 = fp32, 1 = bf16.
+hipError_t launch_pack(const PackArgs &a, int dtype, hipStream_t s);
+hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s);
+hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
+                       hipStream_t s);
+hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
+                       hipStream_t s);
+hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s);
+hipError_t launch_slot(const SlotArgs &a, int dtype, int style, hipStream_t s);
+hipError_t launch_masks(const Dims &d, const uint8_t *valid,
+                        const uint8_t *token_valid, const uint8_t *window_mask,
+                        const int64_t *atom_to_token, const int64_t *key_index,
+                        int64_t radius, uint8_t *usable, uint8_t *allowed,
+                        hipStream_t s);
+
+// LDS bytes each kernel needs for these sizes (host-side shape checks).
+size_t prep_lds_bytes(const Dims &d, int dtype, int style);
+size_t post_lds_bytes(const Dims &d, int dtype, int style);
+size_t pool_lds_bytes(const Dims &d, int dtype);
+size_t token_proj_lds_bytes(const Dims &d, int dtype);
+size_t slot_lds_bytes(const Dims &d, int dtype, int style);
+int slot_supported(const Dims &d, int dtype, int style);
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+} // namespace waa

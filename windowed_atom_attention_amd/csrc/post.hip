@@ -1,0 +1,540 @@
+// post.hip -- everything after the slot attention, one 32-atom tile per
+// workgroup ("windowed_atom_attention", Required behavior):
+//   u  = (o * G) flattened head-major @ w_attention_out   (no bias)
+//   x1 = x0 + g_att * u        (AF3 g_att = sigmoid(c@w_rg[0] + b_rg[0]) on
+//                               the raw condition; ESMFold2 g_att = m2, raw)
+//   z  = A_2(x1) (AF3) or RMS(x1)*(1 + m4) + m3 (ESMFold2)  -- on the NEW x
+//   t  = (SiLU(z @ w_ff_gate) * (z @ w_ff_up)) @ w_ff_out
+//   x2 = x1 + g_tr * t, hidden = select(usable, x2, 0)
+//   decoder: position_update = select(usable,
+//              (LN(hidden)*readout_scale [+ readout_bias]) @ w_readout, 0)
+// The entry state x0 and the conditioning are recomputed from the inputs
+// (two small GEMMs cost far less than storing and re-reading four C-wide
+// vectors per atom). All matrix products are MFMA 32x32 tiles; each dual
+// GEMM's epilogue applies the elementwise step in registers.
+//
+// pool: encoder mean-pool, atomics-free. A tile owns every token whose
+// first usable atom lies in it; it walks its atoms in index order and, for
+// the last open token, continues into the following atoms until that
+// token's atoms end. Requires usable atoms sorted by atom_to_token within a
+// batch; a violation sets the status word.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace waa {
+
+template <typename T>
+__device__ __forceinline__ void load16_f2(const T *src, float *out) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(src);
+    if constexpr (sizeof(T) == 4) {
+        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
+struct PostLayout {
+    int xp, cp, ldS, ldC, ldHD, ldM;
+    size_t o_cs, o_st, o_us, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
+};
+
+__host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+__host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int style) {
+    PostLayout L;
+    L.xp = d.C + 4;
+    L.cp = d.S + 4;
+    L.ldS = d.S + 16 / esz;
+    L.ldC = d.C + 16 / esz;
+    L.ldHD = d.H * d.D + 16 / esz;
+    L.ldM = d.M + 16 / esz;
+    size_t o = 32 * (size_t)L.xp * 4;
+    L.o_cs = o;
+    if (style == STYLE_AF3)
+        o += 32 * (size_t)L.cp * 4;
+    L.o_st = o; o += 32 * 4 * 4;
+    L.o_us = o; o += 32;
+    L.o_opC = o; o = al16(o + 32 * (size_t)L.ldS * esz);
+    L.o_opC2 = o;
+    if (style == STYLE_AF3)
+        o = al16(o + 32 * (size_t)L.ldS * esz);
+    L.o_opU = o; o = al16(o + 32 * (size_t)L.ldHD * esz);
+    L.o_opZ = o; o = al16(o + 32 * (size_t)L.ldC * esz);
+    L.o_opH = o; o = al16(o + 32 * (size_t)L.ldM * esz);
+    L.total = o;
+    return L;
+}
+
+size_t post_lds_bytes(const Dims &d, int dtype, int style) {
+    return post_layout(d, dtype ? 2 : 4, style).total;
+}
+
+template <typename T, int STYLE, int STAGE>
+__global__ __launch_bounds__(256) void k_post(BlockArgs p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Dims d = p.d;
+    const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D, M = d.M;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = tid >> 3, sub = tid & 7;
+    const int n0 = blockIdx.x * 32;
+    const int n = n0 + row;
+    const bool inb = n < N;
+    constexpr int E = 16 / sizeof(T);
+    const PostLayout L = post_layout(d, sizeof(T), STYLE);
+    float *xs = reinterpret_cast<float *>(smem);
+    float *cs = reinterpret_cast<float *>(smem + L.o_cs);
+    float *st = reinterpret_cast<float *>(smem + L.o_st);
+    uint8_t *us = smem + L.o_us;
+    T *opC = reinterpret_cast<T *>(smem + L.o_opC);
+    T *opC2 = reinterpret_cast<T *>(smem + L.o_opC2);
+    T *opU = reinterpret_cast<T *>(smem + L.o_opU);
+    T *opZ = reinterpret_cast<T *>(smem + L.o_opZ);
+    T *opH = reinterpret_cast<T *>(smem + L.o_opH);
+
+    const bool u = inb && p.usable[n];
+    const int b = inb ? n / d.A : 0;
+    if (sub == 0)
+        us[row] = u;
+    {
+        // entry state, as the prep kernel builds it
+        const T *ar = reinterpret_cast<const T *>(p.atom) + (int64_t)n * C;
+        int64_t tk = 0;
+        if (STAGE == STAGE_DECODER && u)
+            tk = p.atom_to_token[n];
+        const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
+        for (int vi = sub; vi < C / E; vi += 8) {
+            float xv[E];
+            if (u) {
+                load16_f2<T>(ar + vi * E, xv);
+                if (STAGE == STAGE_DECODER) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        xv[e] += tp[vi * E + e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    xv[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                xs[row * L.xp + vi * E + e] = xv[e];
+        }
+        // condition: raw (AF3 gates) or SiLU (ESMFold2 modulation)
+        const T *cr = reinterpret_cast<const T *>(p.condition) + (int64_t)n * S;
+        for (int vi = sub; vi < S / E; vi += 8) {
+            float cv[E];
+            if (u) {
+                load16_f2<T>(cr + vi * E, cv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    cv[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (STYLE == STYLE_AF3) {
+                    cs[row * L.cp + vi * E + e] = cv[e];
+                    opC[row * L.ldS + vi * E + e] = from_f<T>(cv[e]);
+                } else {
+                    opC[row * L.ldS + vi * E + e] = from_f<T>(silu_f(cv[e]));
+                }
+            }
+        }
+        // value-gated attention output (o * G), rounded to the storage type
+        const T *orow = reinterpret_cast<const T *>(p.o) + (int64_t)n * HD;
+        const T *grow = reinterpret_cast<const T *>(p.g) + (int64_t)n * HD;
+        for (int vi = sub; vi < HD / E; vi += 8) {
+            float ov[E], gv[E];
+            if (inb) {
+                load16_f2<T>(orow + vi * E, ov);
+                load16_f2<T>(grow + vi * E, gv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    ov[e] = gv[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                opU[row * L.ldHD + vi * E + e] = from_f<T>(ov[e] * gv[e]);
+        }
+    }
+    __syncthreads();
+
+    const int nkS = S / Mma32<T>::KC, nkC = C / Mma32<T>::KC;
+    const int nkHD = HD / Mma32<T>::KC, nkM = M / Mma32<T>::KC;
+
+    if (STYLE == STYLE_AF3) {
+        // c_2 = LN(c) * cond_scale[2]
+        const float *cr = cs + row * L.cp;
+        float s = 0.0f;
+        for (int c = sub; c < S; c += 8)
+            s += cr[c];
+        const float mc = group_sum<8>(s) / (float)S;
+        float q = 0.0f;
+        for (int c = sub; c < S; c += 8) {
+            const float t = cr[c] - mc;
+            q += t * t;
+        }
+        const float rc = 1.0f / sqrtf(group_sum<8>(q) / (float)S + p.eps);
+        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
+        for (int c = sub; c < S; c += 8)
+            opC2[row * L.ldS + c] = from_f<T>((cr[c] - mc) * rc * to_f(cscale[2 * S + c]));
+    }
+
+    // x1 = x0 + g_att * (o*G) @ w_attention_out
+    {
+        const T *brg = reinterpret_cast<const T *>(p.b_rg);
+        const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
+        for (int nb = wave; nb < C / 32; nb += 4) {
+            f32x16_t a1 = zero16(), a2 = zero16();
+            gemm32<T>(a1, opU, L.ldHD, nkHD, p.pk + p.off.w_ao + (int64_t)nb * nkHD * 64);
+            gemm32<T>(a2, opC, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
+            const int c = nb * 32 + acc32_col(lane);
+            const float bias = STYLE == STYLE_AF3 ? to_f(brg[c]) : 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = acc32_row(v, lane);
+                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(a2[v] + bias) : a2[v];
+                xs[r * L.xp + c] += gate * a1[v];
+            }
+        }
+    }
+    __syncthreads();
+    // statistics of the NEW state for the transition norm
+    {
+        const float *xr = xs + row * L.xp;
+        if (STYLE == STYLE_AF3) {
+            float s = 0.0f;
+            for (int c = sub; c < C; c += 8)
+                s += xr[c];
+            const float mean = group_sum<8>(s) / (float)C;
+            float q = 0.0f;
+            for (int c = sub; c < C; c += 8) {
+                const float t = xr[c] - mean;
+                q += t * t;
+            }
+            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            if (sub == 0) {
+                st[row * 4 + 0] = mean;
+                st[row * 4 + 1] = rstd;
+            }
+        } else {
+            float q = 0.0f;
+            for (int c = sub; c < C; c += 8)
+                q += xr[c] * xr[c];
+            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            if (sub == 0) {
+                st[row * 4 + 0] = 0.0f;
+                st[row * 4 + 1] = rstd;
+            }
+        }
+    }
+    __syncthreads();
+    // z = transition-normalised x1
+    {
+        const T *bsc = reinterpret_cast<const T *>(p.b_scale);
+        for (int nb = wave; nb < C / 32; nb += 4) {
+            f32x16_t a1 = zero16(), a2 = zero16();
+            if (STYLE == STYLE_AF3) {
+                gemm32<T>(a1, opC2, L.ldS, nkS, p.pk + p.off.w_scale[2] + (int64_t)nb * nkS * 64);
+                gemm32<T>(a2, opC2, L.ldS, nkS, p.pk + p.off.w_shift[2] + (int64_t)nb * nkS * 64);
+            } else {
+                gemm32<T>(a1, opC, L.ldS, nkS, p.pk + p.off.w_mod[3] + (int64_t)nb * nkS * 64);
+                gemm32<T>(a2, opC, L.ldS, nkS, p.pk + p.off.w_mod[4] + (int64_t)nb * nkS * 64);
+            }
+            const int c = nb * 32 + acc32_col(lane);
+            const float bias = STYLE == STYLE_AF3 ? to_f(bsc[2 * C + c]) : 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = acc32_row(v, lane);
+                const float xn = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
+                float z;
+                if (STYLE == STYLE_AF3)
+                    z = xn * sigmoid_f(a1[v] + bias) + a2[v];
+                else
+                    z = xn * (1.0f + a2[v]) + a1[v];
+                opZ[r * L.ldC + c] = from_f<T>(z);
+            }
+        }
+    }
+    __syncthreads();
+    // h = SiLU(z @ w_ff_gate) * (z @ w_ff_up)
+    for (int nb = wave; nb < M / 32; nb += 4) {
+        f32x16_t a1 = zero16(), a2 = zero16();
+        gemm32<T>(a1, opZ, L.ldC, nkC, p.pk + p.off.ff_gate + (int64_t)nb * nkC * 64);
+        gemm32<T>(a2, opZ, L.ldC, nkC, p.pk + p.off.ff_up + (int64_t)nb * nkC * 64);
+        const int c = nb * 32 + acc32_col(lane);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = acc32_row(v, lane);
+            opH[r * L.ldM + c] = from_f<T>(silu_f(a1[v]) * a2[v]);
+        }
+    }
+    __syncthreads();
+    // x2 = x1 + g_tr * h @ w_ff_out; hidden = select(usable, x2, 0)
+    {
+        T *hid = reinterpret_cast<T *>(p.hidden);
+        const T *brg = reinterpret_cast<const T *>(p.b_rg);
+        const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[1] : p.off.w_mod[5];
+        for (int nb = wave; nb < C / 32; nb += 4) {
+            f32x16_t a1 = zero16(), a2 = zero16();
+            gemm32<T>(a1, opH, L.ldM, nkM, p.pk + p.off.ff_out + (int64_t)nb * nkM * 64);
+            gemm32<T>(a2, opC, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
+            const int c = nb * 32 + acc32_col(lane);
+            const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = acc32_row(v, lane);
+                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(a2[v] + bias) : a2[v];
+                const float x2 = xs[r * L.xp + c] + gate * a1[v];
+                const float h = us[r] ? x2 : 0.0f;
+                xs[r * L.xp + c] = h;
+                const int nn = n0 + r;
+                if (nn < N)
+                    hid[(int64_t)nn * C + c] = from_f<T>(h);
+            }
+        }
+    }
+    if (STAGE == STAGE_DECODER) {
+        __syncthreads();
+        const float *xr = xs + row * L.xp;
+        float s = 0.0f;
+        for (int c = sub; c < C; c += 8)
+            s += xr[c];
+        const float mean = group_sum<8>(s) / (float)C;
+        float q = 0.0f;
+        for (int c = sub; c < C; c += 8) {
+            const float t = xr[c] - mean;
+            q += t * t;
+        }
+        const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+        const T *rs = reinterpret_cast<const T *>(p.readout_scale);
+        const T *rb = reinterpret_cast<const T *>(p.readout_bias);
+        const T *wr = reinterpret_cast<const T *>(p.w_readout);
+        float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f;
+        for (int c = sub; c < C; c += 8) {
+            float z = (xr[c] - mean) * rstd * to_f(rs[c]);
+            if (STYLE == STYLE_ESM)
+                z += to_f(rb[c]);
+            acc0 += z * to_f(wr[c * 3 + 0]);
+            acc1 += z * to_f(wr[c * 3 + 1]);
+            acc2 += z * to_f(wr[c * 3 + 2]);
+        }
+        acc0 = group_sum<8>(acc0);
+        acc1 = group_sum<8>(acc1);
+        acc2 = group_sum<8>(acc2);
+        if (sub == 0 && inb) {
+            T *pu = reinterpret_cast<T *>(p.position_update) + (int64_t)n * 3;
+            const bool ok = us[row];
+            pu[0] = from_f<T>(ok ? acc0 : 0.0f);
+            pu[1] = from_f<T>(ok ? acc1 : 0.0f);
+            pu[2] = from_f<T>(ok ? acc2 : 0.0f);
+        }
+    }
+}
+
+hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
+                       hipStream_t s) {
+    const int N = a.d.B * a.d.A;
+    const int grid = (N + 31) / 32;
+    const size_t lds = post_lds_bytes(a.d, dtype, style);
+    const void *fn = nullptr;
+#define WAA_PICK(T, ST, SG) fn = (const void *)k_post<T, ST, SG>
+    if (dtype == 0) {
+        if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(float, 0, 0); else WAA_PICK(float, 0, 1); }
+        else { if (stage == STAGE_ENCODER) WAA_PICK(float, 1, 0); else WAA_PICK(float, 1, 1); }
+    } else {
+        if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(bf16_t, 0, 0); else WAA_PICK(bf16_t, 0, 1); }
+        else { if (stage == STAGE_ENCODER) WAA_PICK(bf16_t, 1, 0); else WAA_PICK(bf16_t, 1, 1); }
+    }
+#undef WAA_PICK
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    void *args[] = {(void *)&a};
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
+    if (e != hipSuccess)
+        return e;
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------- pool
+
+struct PoolLayout {
+    int ldC, pp;
+    size_t o_ps, o_tok, o_us, total;
+};
+
+__host__ __device__ inline PoolLayout pool_layout(const Dims &d, int esz) {
+    PoolLayout L;
+    L.ldC = d.C + 16 / esz;
+    L.pp = d.U + 4;
+    size_t o = al16(32 * (size_t)L.ldC * esz);
+    L.o_ps = o; o += 32 * (size_t)L.pp * 4;
+    L.o_tok = o; o += 32 * 4;
+    L.o_us = o; o += 32;
+    L.total = al16(o);
+    return L;
+}
+
+size_t pool_lds_bytes(const Dims &d, int dtype) {
+    return pool_layout(d, dtype ? 2 : 4).total;
+}
+
+constexpr int kPoolMaxCols = 4; // U <= 1024
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_pool(BlockArgs p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_prev;
+    const Dims d = p.d;
+    const int A = d.A, C = d.C, U = d.U;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = tid >> 3, sub = tid & 7;
+    const int ntile = (A + 31) / 32;
+    const int b = blockIdx.x / ntile;
+    const int a0 = (blockIdx.x % ntile) * 32;
+    const PoolLayout L = pool_layout(d, sizeof(T));
+    T *opA = reinterpret_cast<T *>(smem);
+    float *ps = reinterpret_cast<float *>(smem + L.o_ps);
+    int *tok = reinterpret_cast<int *>(smem + L.o_tok);
+    uint8_t *us = smem + L.o_us;
+    const int64_t base = (int64_t)b * A;
+
+    // token of the last usable atom before this tile (-1 if none)
+    if (wave == 0) {
+        int prev = -1;
+        for (int hi = a0 - 1; hi >= 0; hi -= 64) {
+            const int a = hi - lane;
+            const bool uu = a >= 0 && p.usable[base + a];
+            const unsigned long long m = __ballot(uu);
+            if (m) {
+                const int l = __ffsll((long long)m) - 1; // lowest lane = largest a
+                prev = (int)p.atom_to_token[base + hi - l];
+                break;
+            }
+        }
+        if (lane == 0)
+            s_prev = prev;
+    }
+
+    const int nkc = C / Mma32<T>::KC;
+    T *tout = reinterpret_cast<T *>(p.token_output);
+    float acc[kPoolMaxCols];
+#pragma unroll
+    for (int i = 0; i < kPoolMaxCols; ++i)
+        acc[i] = 0.0f;
+    int cur = -1, cnt = 0;
+    bool owned = false, first = true, done = false, bad = false;
+
+    auto flush = [&]() {
+        if (cur >= 0 && owned) {
+            const float inv = 1.0f / (float)cnt;
+            T *dst = tout + ((int64_t)b * d.T + cur) * U;
+#pragma unroll
+            for (int i = 0; i < kPoolMaxCols; ++i) {
+                const int col = tid + 256 * i;
+                if (col < U)
+                    dst[col] = from_f<T>(acc[i] * inv);
+            }
+        }
+    };
+
+    for (int chunk = 0; !done; ++chunk) {
+        const int cb = a0 + chunk * 32;
+        if (cb >= A) {
+            flush();
+            break;
+        }
+        __syncthreads();
+        {
+            const int a = cb + row;
+            const bool ok = a < A;
+            if (sub == 0) {
+                us[row] = ok ? p.usable[base + a] : 0;
+                tok[row] = ok ? (int)p.atom_to_token[base + a] : -1;
+            }
+            const T *src = reinterpret_cast<const T *>(p.hidden) + (base + a) * C;
+            constexpr int E = 16 / sizeof(T);
+            for (int vi = sub; vi < C / E; vi += 8) {
+                uint4 val = make_uint4(0, 0, 0, 0);
+                if (ok)
+                    val = *reinterpret_cast<const uint4 *>(src + vi * E);
+                *reinterpret_cast<uint4 *>(opA + row * L.ldC + vi * E) = val;
+            }
+        }
+        __syncthreads();
+        for (int nb = wave; nb < U / 32; nb += 4) {
+            f32x16_t a1 = zero16();
+            gemm32<T>(a1, opA, L.ldC, nkc, p.pk + p.off.w_pool + (int64_t)nb * nkc * 64);
+            const int c = nb * 32 + acc32_col(lane);
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                ps[acc32_row(v, lane) * L.pp + c] = fmaxf(a1[v], 0.0f);
+        }
+        __syncthreads();
+        const int prev_tok = s_prev;
+        for (int r = 0; r < 32; ++r) {
+            const int a = cb + r;
+            if (a >= A)
+                break;
+            if (!us[r])
+                continue;
+            const int t = tok[r];
+            if (t != cur) {
+                flush();
+                if (a >= a0 + 32) {
+                    done = true;
+                    cur = -1;
+                    break;
+                }
+                if ((cur >= 0 && t < cur) || (cur < 0 && first && prev_tok >= 0 && t < prev_tok))
+                    bad = true;
+                owned = !(first && t == prev_tok);
+                first = false;
+                cur = t;
+                cnt = 0;
+#pragma unroll
+                for (int i = 0; i < kPoolMaxCols; ++i)
+                    acc[i] = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < kPoolMaxCols; ++i) {
+                const int col = tid + 256 * i;
+                if (col < U)
+                    acc[i] += ps[r * L.pp + col];
+            }
+            ++cnt;
+        }
+        if (!done) {
+            if (cb + 32 >= A) {
+                flush();
+                done = true;
+            } else if (cur < 0 || !owned) {
+                done = true;
+            }
+        }
+    }
+    if (bad && tid == 0 && p.status != nullptr)
+        p.status[0] = 1;
+}
+
+hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s) {
+    const int ntile = (a.d.A + 31) / 32;
+    const int grid = a.d.B * ntile;
+    const size_t lds = pool_lds_bytes(a.d, dtype);
+    const void *fn = dtype == 0 ? (const void *)k_pool<float> : (const void *)k_pool<bf16_t>;
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    void *args[] = {(void *)&a};
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
+    if (e != hipSuccess)
+        return e;
+    return hipGetLastError();
+}
+
+} // namespace waa

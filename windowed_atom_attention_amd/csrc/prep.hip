@@ -1,0 +1,477 @@
+// prep.hip -- entry state, conditioning and Q/K/V/gate projections.
+//
+// k_token_proj (decoder): tokproj[B*T, C] = select(token_valid, token, 0)
+//   @ w_token, fp32, one 32-token tile per workgroup.
+// k_prep: one 32-atom tile per workgroup (4 waves). Steps, as in
+//   "windowed_atom_attention" (Required behavior):
+//   usability; sanitised entry state x0 (decoder: + gathered token
+//   projection) and condition c; AF3: q_in = A_0(x0), kv_in = A_1(x0) with
+//   A_j(z) = LN(z)*sigmoid(cj@w_scale[j]+b_scale[j]) + cj@w_shift[j],
+//   cj = LN(c)*cond_scale[j]; ESMFold2: in = RMS(x0)*(1+m1)+m0 with
+//   m = SiLU(c)@w_mod; then Q (+b_q for AF3), K, V and G = sigmoid(q_in @
+//   w_value_gate); ESMFold2 also RMS-normalises Q and K per head and
+//   applies the half-split rotary before they are stored, so the slot
+//   kernel gathers pre-rotated keys.
+//   Matrix products run on MFMA (32x32 tiles, A operand from LDS, packed
+//   weights from L2); norms and epilogues are fp32 VALU work on the tile.
+//   The kernel also zero-fills token_output (encoder) and the status word,
+//   so that the pool kernel only writes non-empty tokens.
+// k_masks: the usable/allowed masks alone.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace waa {
+
+// Copy one row of n elements (n*sizeof(T) a multiple of 16 bytes) from
+// global memory into an LDS operand row, or zero it; 8 threads per row.
+template <typename T>
+__device__ __forceinline__ void copy_row(T *dst, const T *src, int n, bool ok,
+                                         int sub) {
+    constexpr int E = 16 / sizeof(T);
+    const int nv = n / E;
+    for (int vi = sub; vi < nv; vi += 8) {
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (ok)
+            val = *reinterpret_cast<const uint4 *>(src + vi * E);
+        *reinterpret_cast<uint4 *>(dst + vi * E) = val;
+    }
+}
+
+// Load 16 bytes of T at src as fp32 values.
+template <typename T>
+__device__ __forceinline__ void load16_f(const T *src, float *out) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(src);
+    if constexpr (sizeof(T) == 4) {
+        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
+// --------------------------------------------------------------- K0
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_token_proj(BlockArgs p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Dims d = p.d;
+    const int rows = d.B * d.T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = tid >> 3, sub = tid & 7;
+    const int r0 = blockIdx.x * 32;
+    const int ldU = d.U + pad16<T>();
+    T *opA = reinterpret_cast<T *>(smem);
+    {
+        const int r = r0 + row;
+        const bool ok = r < rows && p.token_valid[r];
+        copy_row<T>(opA + row * ldU, reinterpret_cast<const T *>(p.token) + (int64_t)r * d.U,
+                    d.U, ok, sub);
+    }
+    __syncthreads();
+    const int nkc = d.U / Mma32<T>::KC;
+    for (int nb = wave; nb < d.C / 32; nb += 4) {
+        f32x16_t acc = zero16();
+        gemm32<T>(acc, opA, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64);
+        const int c = nb * 32 + acc32_col(lane);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = r0 + acc32_row(v, lane);
+            if (r < rows)
+                p.tokproj[(int64_t)r * d.C + c] = acc[v];
+        }
+    }
+}
+
+size_t token_proj_lds_bytes(const Dims &d, int dtype) {
+    const size_t e = dtype ? 2 : 4;
+    return 32 * (d.U * e + 16);
+}
+
+hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
+    const int rows = a.d.B * a.d.T;
+    const int grid = (rows + 31) / 32;
+    const size_t lds = token_proj_lds_bytes(a.d, dtype);
+    if (dtype == 0) {
+        (void)hipFuncSetAttribute((const void *)k_token_proj<float>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL(k_token_proj<float>, dim3(grid), dim3(256), lds, s, a);
+    } else {
+        (void)hipFuncSetAttribute((const void *)k_token_proj<bf16_t>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL(k_token_proj<bf16_t>, dim3(grid), dim3(256), lds, s, a);
+    }
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------- K1
+
+struct PrepLayout {
+    int xp, cp, hp, ldS, ldC;
+    size_t o_cs, o_st, o_us, o_opA, o_opQ, o_opK, o_hb, total;
+};
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+__host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int style) {
+    PrepLayout L;
+    L.xp = d.C + 4;
+    L.cp = d.S + 4;
+    L.hp = d.H * d.D + 4;
+    L.ldS = d.S + 16 / esz;
+    L.ldC = d.C + 16 / esz;
+    size_t o = 32 * L.xp * 4;
+    L.o_cs = o; o += 32 * L.cp * 4;
+    L.o_st = o; o += 32 * 4 * 4;
+    L.o_us = o; o += 32;
+    L.o_opA = o; o = align16(o + 32 * (size_t)L.ldS * esz);
+    L.o_opQ = o; o = align16(o + 32 * (size_t)L.ldC * esz);
+    L.o_opK = o;
+    if (style == STYLE_AF3)
+        o = align16(o + 32 * (size_t)L.ldC * esz);
+    L.o_hb = o;
+    if (style == STYLE_ESM)
+        o = align16(o + 32 * (size_t)L.hp * 4);
+    L.total = o;
+    return L;
+}
+
+size_t prep_lds_bytes(const Dims &d, int dtype, int style) {
+    return prep_layout(d, dtype ? 2 : 4, style).total;
+}
+
+// Per-head RMS normalisation and half-split rotary of the 32 x H*D tile in
+// hb (fp32), stored to dst (storage dtype). One thread per (row, head).
+template <typename T>
+__device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
+                                int n0, T *dst) {
+    const Dims d = p.d;
+    const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2;
+    const T *cosb = reinterpret_cast<const T *>(p.rope_cos);
+    const T *sinb = reinterpret_cast<const T *>(p.rope_sin);
+    for (int pi = threadIdx.x; pi < 32 * d.H; pi += 256) {
+        const int r = pi / d.H, h = pi % d.H;
+        const int n = n0 + r;
+        if (n >= N)
+            continue;
+        const float *x = hb + r * hp + h * D;
+        float ms = 0.0f;
+        for (int e = 0; e < D; ++e)
+            ms += x[e] * x[e];
+        const float rs = 1.0f / sqrtf(ms / (float)D + p.eps);
+        T *out = dst + (int64_t)n * HD + h * D;
+        const T *cs = cosb + (int64_t)n * D;
+        const T *sn = sinb + (int64_t)n * D;
+        for (int e = 0; e < D; ++e) {
+            const float y = x[e] * rs;
+            const float rot = e < half ? -x[e + half] * rs : x[e - half] * rs;
+            out[e] = from_f<T>(y * to_f(cs[e]) + rot * to_f(sn[e]));
+        }
+    }
+}
+
+template <typename T, int STYLE, int STAGE>
+__global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Dims d = p.d;
+    const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = tid >> 3, sub = tid & 7;
+    const int n0 = blockIdx.x * 32;
+    const int n = n0 + row;
+    const bool inb = n < N;
+    constexpr int E = 16 / sizeof(T);
+
+    if (STAGE == STAGE_ENCODER) {
+        T *to = reinterpret_cast<T *>(p.token_output);
+        const int64_t total = (int64_t)d.B * d.T * d.U;
+        for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < total;
+             i += (int64_t)gridDim.x * 256)
+            to[i] = from_f<T>(0.0f);
+    }
+    if (p.status != nullptr && blockIdx.x == 0 && tid == 0)
+        p.status[0] = 0;
+
+    const PrepLayout L = prep_layout(d, sizeof(T), STYLE);
+    float *xs = reinterpret_cast<float *>(smem);
+    float *cs = reinterpret_cast<float *>(smem + L.o_cs);
+    float *st = reinterpret_cast<float *>(smem + L.o_st);
+    uint8_t *us = smem + L.o_us;
+    T *opA = reinterpret_cast<T *>(smem + L.o_opA);
+    T *opQ = reinterpret_cast<T *>(smem + L.o_opQ);
+    T *opK = reinterpret_cast<T *>(smem + L.o_opK);
+    float *hb = reinterpret_cast<float *>(smem + L.o_hb);
+
+    // usability of this row's atom
+    const int b = inb ? n / d.A : 0;
+    int64_t tk = 0;
+    bool u = false;
+    if (inb) {
+        tk = p.atom_to_token[n];
+        u = p.valid[n] && tk >= 0 && tk < d.T && p.token_valid[(int64_t)b * d.T + tk];
+    }
+    if (sub == 0) {
+        us[row] = u;
+        if (inb)
+            p.usable[n] = u;
+    }
+    // sanitised entry state and condition (selected, never multiplied)
+    {
+        const T *ar = reinterpret_cast<const T *>(p.atom) + (int64_t)n * C;
+        const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
+        for (int vi = sub; vi < C / E; vi += 8) {
+            float xv[E];
+            if (u) {
+                load16_f<T>(ar + vi * E, xv);
+                if (STAGE == STAGE_DECODER) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        xv[e] += tp[vi * E + e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    xv[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                xs[row * L.xp + vi * E + e] = xv[e];
+        }
+        const T *cr = reinterpret_cast<const T *>(p.condition) + (int64_t)n * S;
+        for (int vi = sub; vi < S / E; vi += 8) {
+            float cv[E];
+            if (u) {
+                load16_f<T>(cr + vi * E, cv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    cv[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                cs[row * L.cp + vi * E + e] = cv[e];
+        }
+    }
+    __syncthreads();
+
+    // row statistics of x0 (and of c for AF3)
+    {
+        const float *xr = xs + row * L.xp;
+        if (STYLE == STYLE_AF3) {
+            float s = 0.0f;
+            for (int c = sub; c < C; c += 8)
+                s += xr[c];
+            const float mean = group_sum<8>(s) / (float)C;
+            float q = 0.0f;
+            for (int c = sub; c < C; c += 8) {
+                const float t = xr[c] - mean;
+                q += t * t;
+            }
+            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            const float *cr = cs + row * L.cp;
+            float s2 = 0.0f;
+            for (int c = sub; c < S; c += 8)
+                s2 += cr[c];
+            const float mc = group_sum<8>(s2) / (float)S;
+            float q2 = 0.0f;
+            for (int c = sub; c < S; c += 8) {
+                const float t = cr[c] - mc;
+                q2 += t * t;
+            }
+            const float rc = 1.0f / sqrtf(group_sum<8>(q2) / (float)S + p.eps);
+            if (sub == 0) {
+                st[row * 4 + 0] = mean; st[row * 4 + 1] = rstd;
+                st[row * 4 + 2] = mc;   st[row * 4 + 3] = rc;
+            }
+        } else {
+            float q = 0.0f;
+            for (int c = sub; c < C; c += 8)
+                q += xr[c] * xr[c];
+            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            if (sub == 0) {
+                st[row * 4 + 0] = 0.0f;
+                st[row * 4 + 1] = rstd;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int nkS = S / Mma32<T>::KC, nkC = C / Mma32<T>::KC;
+    if (STYLE == STYLE_AF3) {
+        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
+        const T *bscale = reinterpret_cast<const T *>(p.b_scale);
+        for (int j = 0; j < 2; ++j) {
+            {
+                const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
+                for (int c = sub; c < S; c += 8)
+                    opA[row * L.ldS + c] = from_f<T>((cs[row * L.cp + c] - mc) * rc *
+                                                     to_f(cscale[j * S + c]));
+            }
+            __syncthreads();
+            T *dst = j == 0 ? opQ : opK;
+            for (int nb = wave; nb < C / 32; nb += 4) {
+                f32x16_t a1 = zero16(), a2 = zero16();
+                gemm32<T>(a1, opA, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64);
+                gemm32<T>(a2, opA, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
+                const int c = nb * 32 + acc32_col(lane);
+                const float bs = to_f(bscale[j * C + c]);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = acc32_row(v, lane);
+                    const float ln = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
+                    dst[r * L.ldC + c] = from_f<T>(ln * sigmoid_f(a1[v] + bs) + a2[v]);
+                }
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int c = sub; c < S; c += 8)
+            opA[row * L.ldS + c] = from_f<T>(silu_f(cs[row * L.cp + c]));
+        __syncthreads();
+        for (int nb = wave; nb < C / 32; nb += 4) {
+            f32x16_t a1 = zero16(), a2 = zero16();
+            gemm32<T>(a1, opA, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64);
+            gemm32<T>(a2, opA, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
+            const int c = nb * 32 + acc32_col(lane);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = acc32_row(v, lane);
+                const float rm = xs[r * L.xp + c] * st[r * 4 + 1];
+                opQ[r * L.ldC + c] = from_f<T>(rm * (1.0f + a2[v]) + a1[v]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // Q/K/V/G projections
+    T *qo = reinterpret_cast<T *>(p.q);
+    T *ko = reinterpret_cast<T *>(p.k);
+    T *vo = reinterpret_cast<T *>(p.v);
+    T *go = reinterpret_cast<T *>(p.g);
+    if (STYLE == STYLE_AF3) {
+        const T *bq = reinterpret_cast<const T *>(p.b_q);
+        for (int nb = wave; nb < HD / 32; nb += 4) {
+            f32x16_t a1 = zero16(), a2 = zero16();
+            gemm32<T>(a1, opQ, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64);
+            gemm32<T>(a2, opQ, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
+            const int c = nb * 32 + acc32_col(lane);
+            const float bias = to_f(bq[c]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int nn = n0 + acc32_row(v, lane);
+                if (nn < N) {
+                    qo[(int64_t)nn * HD + c] = from_f<T>(a1[v] + bias);
+                    go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(a2[v]));
+                }
+            }
+            f32x16_t a3 = zero16(), a4 = zero16();
+            gemm32<T>(a3, opK, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64);
+            gemm32<T>(a4, opK, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int nn = n0 + acc32_row(v, lane);
+                if (nn < N) {
+                    ko[(int64_t)nn * HD + c] = from_f<T>(a3[v]);
+                    vo[(int64_t)nn * HD + c] = from_f<T>(a4[v]);
+                }
+            }
+        }
+    } else {
+        for (int pass = 0; pass < 2; ++pass) {
+            const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
+            const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
+            for (int nb = wave; nb < HD / 32; nb += 4) {
+                f32x16_t a1 = zero16(), a2 = zero16();
+                gemm32<T>(a1, opQ, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64);
+                gemm32<T>(a2, opQ, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
+                const int c = nb * 32 + acc32_col(lane);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = acc32_row(v, lane);
+                    hb[r * L.hp + c] = a1[v];
+                    const int nn = n0 + r;
+                    if (nn < N) {
+                        if (pass == 0)
+                            go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(a2[v]));
+                        else
+                            vo[(int64_t)nn * HD + c] = from_f<T>(a2[v]);
+                    }
+                }
+            }
+            __syncthreads();
+            head_rms_rotary<T>(p, hb, L.hp, n0, pass == 0 ? qo : ko);
+            __syncthreads();
+        }
+    }
+}
+
+hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
+                       hipStream_t s) {
+    const int N = a.d.B * a.d.A;
+    const int grid = (N + 31) / 32;
+    const size_t lds = prep_lds_bytes(a.d, dtype, style);
+    const void *fn = nullptr;
+#define WAA_PICK(T, ST, SG) fn = (const void *)k_prep<T, ST, SG>
+    if (dtype == 0) {
+        if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(float, 0, 0); else WAA_PICK(float, 0, 1); }
+        else { if (stage == STAGE_ENCODER) WAA_PICK(float, 1, 0); else WAA_PICK(float, 1, 1); }
+    } else {
+        if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(bf16_t, 0, 0); else WAA_PICK(bf16_t, 0, 1); }
+        else { if (stage == STAGE_ENCODER) WAA_PICK(bf16_t, 1, 0); else WAA_PICK(bf16_t, 1, 1); }
+    }
+#undef WAA_PICK
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    void *args[] = {(void *)&a};
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
+    if (e != hipSuccess)
+        return e;
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------- masks
+
+__global__ __launch_bounds__(256) void k_masks(Dims d, const uint8_t *valid,
+                                               const uint8_t *token_valid,
+                                               const uint8_t *window_mask,
+                                               const int64_t *a2t,
+                                               const int64_t *key_index,
+                                               int64_t radius, uint8_t *usable,
+                                               uint8_t *allowed) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t N = (int64_t)d.B * d.A;
+    auto usable_of = [&](int64_t m) -> bool {
+        const int64_t t = a2t[m];
+        return valid[m] && t >= 0 && t < d.T && token_valid[(m / d.A) * d.T + t];
+    };
+    if (i < N && usable)
+        usable[i] = usable_of(i);
+    if (i < N * d.K && allowed) {
+        const int64_t n = i / d.K;
+        const int64_t a = n % d.A, b = n / d.A;
+        const int64_t j = key_index[i];
+        bool ok = usable_of(n) && j >= 0 && j < d.A && window_mask[i] &&
+                  usable_of(b * d.A + j);
+        if (ok && radius >= 0)
+            ok = (j > a ? j - a : a - j) <= radius;
+        allowed[i] = ok;
+    }
+}
+
+hipError_t launch_masks(const Dims &d, const uint8_t *valid,
+                        const uint8_t *token_valid, const uint8_t *window_mask,
+                        const int64_t *atom_to_token, const int64_t *key_index,
+                        int64_t radius, uint8_t *usable, uint8_t *allowed,
+                        hipStream_t s) {
+    const int64_t work = (int64_t)d.B * d.A * d.K;
+    const int64_t grid = (work + 255) / 256;
+    hipLaunchKernelGGL(k_masks, dim3((unsigned)grid), dim3(256), 0, s, d, valid,
+                       token_valid, window_mask, atom_to_token, key_index,
+                       radius, usable, allowed);
+    return hipGetLastError();
+}
+
+} // namespace waa
