@@ -64,7 +64,8 @@ enum { ATOM_ATTN_ENCODER = 0, ATOM_ATTN_DECODER = 1 };
  * width, V pair width (AF3; ignored for ESMFold2), M transition width,
  * U token width (encoder output width, decoder input width).
  * Supported set of the kernels: C, S, H*D, M, U multiples of 32 and at most
- * 512; D a multiple of 16 and at most 128; K <= 512; V <= 64. */
+ * 512; D a multiple of 16 and at most 128; K <= 512; AF3 V a multiple of 8
+ * and at most 64. 16-byte aligned float pointers and workspace. */
 typedef struct {
     int64_t B, A, T, K, C, S, H, D, V, M, U;
 } atom_attn_dims;
@@ -148,7 +149,9 @@ int atom_attn_masks(const atom_attn_dims *dims, const atom_attn_inputs *in,
 
 /* The slot-attention step alone, on caller-supplied per-atom rows q, k, v
  * [B,A,H*D] (head-major; for ESMFold2 already RMS-normalised and rotated)
- * and usable [B,A]: logits q.k/sqrt(D) (+ AF3 pair bias
+ * and usable [B,A]. q and k are fp32 whatever `dtype` is (the block keeps
+ * the logit operands in fp32); v, pair, pair_scale, w_pair, attention and
+ * o use `dtype`. logits q.k/sqrt(D) (+ AF3 pair bias
  * (LN(pair) * pair_scale) @ w_pair), softmax over the allowed slots with
  * exact-zero empty rows, attention [B,H,A,K] and o [B,A,H*D] = sum of
  * weights times v rows. Same kernel as the full block. Uses dims B, A, K,

@@ -286,10 +286,12 @@ def masks(masks: dict, structure: dict, T: int, radius: int = -1):
 def slot_attention(q, k, v, usable, key_index, window_mask, heads: int,
                    eps: float = 1e-5, style: str = "af3", radius: int = -1,
                    pair=None, pair_scale=None, w_pair=None):
-    """The slot-attention step alone on supplied q/k/v rows [B,A,H*D].
-    Returns attention [B,H,A,K] and o [B,A,H*D]."""
-    dtype = q.dtype
-    q, k, v = (_prep(x, dtype) for x in (q, k, v))
+    """The slot-attention step alone on supplied q/k/v rows [B,A,H*D]
+    (q and k are taken in fp32, v sets the dtype). Returns attention
+    [B,H,A,K] and o [B,A,H*D] in v's dtype."""
+    dtype = v.dtype
+    v = _prep(v, dtype)
+    q, k = (_prep(x.float()) for x in (q, k))
     B, A, HD = q.shape
     K = key_index.shape[-1]
     H = int(heads)

@@ -189,11 +189,12 @@ Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
     Layout L;
     const size_t N = (size_t)(d->B * d->A);
     const size_t rowb = (size_t)(d->H * d->D) * esz;
+    const size_t row32 = (size_t)(d->H * d->D) * 4; // Q and K are fp32
     size_t o = 0;
     L.pack_units = units;
     L.packed = o; o = up256(o + (size_t)units * 16);
-    L.q = o; o = up256(o + N * rowb);
-    L.k = o; o = up256(o + N * rowb);
+    L.q = o; o = up256(o + N * row32);
+    L.k = o; o = up256(o + N * row32);
     L.v = o; o = up256(o + N * rowb);
     L.g = o; o = up256(o + N * rowb);
     L.o = o; o = up256(o + N * rowb);

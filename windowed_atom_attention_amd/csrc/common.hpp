@@ -156,6 +156,39 @@ __device__ __forceinline__ void gemm32(f32x16_t &acc, const T *A, int lda,
     }
 }
 
+// Same product with the A operand given as an unevaluated sum hi + lo of
+// two tiles in the storage type ("split" operand): for bf16 this keeps ~16
+// mantissa bits of an fp32 activation at twice the MFMA work; B (the
+// weights) is exact in its storage type. Alo == nullptr means no lo part.
+template <typename T>
+__device__ __forceinline__ void gemm32s(f32x16_t &acc, const T *Ahi, const T *Alo,
+                                        int lda, int nkc, const uint4 *__restrict__ Bp) {
+    if (Alo == nullptr) {
+        gemm32<T>(acc, Ahi, lda, nkc, Bp);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int off = (lane & 31) * lda + (lane >> 5) * Mma32<T>::HALF;
+#pragma unroll 2
+    for (int kc = 0; kc < nkc; ++kc) {
+        const uint4 b = Bp[kc * 64 + lane];
+        const uint4 ah = *reinterpret_cast<const uint4 *>(Ahi + off + kc * Mma32<T>::KC);
+        const uint4 al = *reinterpret_cast<const uint4 *>(Alo + off + kc * Mma32<T>::KC);
+        Mma32<T>::mma(acc, ah, b);
+        Mma32<T>::mma(acc, al, b);
+    }
+}
+
+// Store x into a split operand pair: hi = x rounded to T, lo = the rest
+// rounded to T (for fp32 storage lo is not used).
+template <typename T>
+__device__ __forceinline__ void put_split(T *hi, T *lo, int idx, float x) {
+    const T h = from_f<T>(x);
+    hi[idx] = h;
+    if (lo != nullptr)
+        lo[idx] = from_f<T>(x - to_f(h));
+}
+
 __device__ __forceinline__ f32x16_t zero16() {
     f32x16_t z;
 #pragma unroll

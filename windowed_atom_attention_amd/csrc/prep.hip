@@ -11,7 +11,9 @@
 //   m = SiLU(c)@w_mod; then Q (+b_q for AF3), K, V and G = sigmoid(q_in @
 //   w_value_gate); ESMFold2 also RMS-normalises Q and K per head and
 //   applies the half-split rotary before they are stored, so the slot
-//   kernel gathers pre-rotated keys.
+//   kernel gathers pre-rotated keys. Q and K are stored in fp32 (they set
+//   the softmax logits), V and G in the storage dtype; for bf16 storage the
+//   computed MFMA operands are split into bf16 hi + lo parts.
 //   Matrix products run on MFMA (32x32 tiles, A operand from LDS, packed
 //   weights from L2); norms and epilogues are fp32 VALU work on the tile.
 //   The kernel also zero-fills token_output (encoder) and the status word,
@@ -110,29 +112,39 @@ hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
 
 // --------------------------------------------------------------- K1
 
+// LDS of one 32-atom tile. Operand tiles that hold computed fp32 values
+// (c_j or SiLU(c), q_in, kv_in) are split into hi + lo parts for bf16 so
+// that the logits path keeps ~16 mantissa bits; fp32 tiles are single.
 struct PrepLayout {
     int xp, cp, hp, ldS, ldC;
-    size_t o_cs, o_st, o_us, o_opA, o_opQ, o_opK, o_hb, total;
+    size_t o_cs, o_st, o_us, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 __host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int style) {
     PrepLayout L;
+    const bool split = esz == 2;
     L.xp = d.C + 4;
     L.cp = d.S + 4;
     L.hp = d.H * d.D + 4;
     L.ldS = d.S + 16 / esz;
     L.ldC = d.C + 16 / esz;
+    const size_t tS = align16(32 * (size_t)L.ldS * esz), tC = align16(32 * (size_t)L.ldC * esz);
     size_t o = 32 * L.xp * 4;
     L.o_cs = o; o += 32 * L.cp * 4;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
-    L.o_opA = o; o = align16(o + 32 * (size_t)L.ldS * esz);
-    L.o_opQ = o; o = align16(o + 32 * (size_t)L.ldC * esz);
-    L.o_opK = o;
-    if (style == STYLE_AF3)
-        o = align16(o + 32 * (size_t)L.ldC * esz);
+    L.o_opA = o; o += tS;
+    L.o_opAl = o; if (split) o += tS;
+    L.o_opQ = o; o += tC;
+    L.o_opQl = o; if (split) o += tC;
+    L.o_opK = o; L.o_opKl = o;
+    if (style == STYLE_AF3) {
+        o += tC;
+        L.o_opKl = o;
+        if (split) o += tC;
+    }
     L.o_hb = o;
     if (style == STYLE_ESM)
         o = align16(o + 32 * (size_t)L.hp * 4);
@@ -145,10 +157,10 @@ size_t prep_lds_bytes(const Dims &d, int dtype, int style) {
 }
 
 // Per-head RMS normalisation and half-split rotary of the 32 x H*D tile in
-// hb (fp32), stored to dst (storage dtype). One thread per (row, head).
+// hb (fp32), stored to dst (fp32). One thread per (row, head).
 template <typename T>
 __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
-                                int n0, T *dst) {
+                                int n0, float *dst) {
     const Dims d = p.d;
     const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2;
     const T *cosb = reinterpret_cast<const T *>(p.rope_cos);
@@ -163,13 +175,13 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
         for (int e = 0; e < D; ++e)
             ms += x[e] * x[e];
         const float rs = 1.0f / sqrtf(ms / (float)D + p.eps);
-        T *out = dst + (int64_t)n * HD + h * D;
+        float *out = dst + (int64_t)n * HD + h * D;
         const T *cs = cosb + (int64_t)n * D;
         const T *sn = sinb + (int64_t)n * D;
         for (int e = 0; e < D; ++e) {
             const float y = x[e] * rs;
             const float rot = e < half ? -x[e + half] * rs : x[e - half] * rs;
-            out[e] = from_f<T>(y * to_f(cs[e]) + rot * to_f(sn[e]));
+            out[e] = y * to_f(cs[e]) + rot * to_f(sn[e]);
         }
     }
 }
@@ -185,6 +197,7 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
     const int n = n0 + row;
     const bool inb = n < N;
     constexpr int E = 16 / sizeof(T);
+    constexpr bool SPLIT = sizeof(T) == 2;
 
     if (STAGE == STAGE_ENCODER) {
         T *to = reinterpret_cast<T *>(p.token_output);
@@ -202,8 +215,11 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
     T *opA = reinterpret_cast<T *>(smem + L.o_opA);
+    T *opAl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opAl) : nullptr;
     T *opQ = reinterpret_cast<T *>(smem + L.o_opQ);
+    T *opQl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opQl) : nullptr;
     T *opK = reinterpret_cast<T *>(smem + L.o_opK);
+    T *opKl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opKl) : nullptr;
     float *hb = reinterpret_cast<float *>(smem + L.o_hb);
 
     // usability of this row's atom
@@ -222,12 +238,12 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
     // sanitised entry state and condition (selected, never multiplied)
     {
         const T *ar = reinterpret_cast<const T *>(p.atom) + (int64_t)n * C;
-        const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
         for (int vi = sub; vi < C / E; vi += 8) {
             float xv[E];
             if (u) {
                 load16_f<T>(ar + vi * E, xv);
                 if (STAGE == STAGE_DECODER) {
+                    const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
 #pragma unroll
                     for (int e = 0; e < E; ++e)
                         xv[e] += tp[vi * E + e];
@@ -308,74 +324,76 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
             {
                 const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
                 for (int c = sub; c < S; c += 8)
-                    opA[row * L.ldS + c] = from_f<T>((cs[row * L.cp + c] - mc) * rc *
-                                                     to_f(cscale[j * S + c]));
+                    put_split<T>(opA, opAl, row * L.ldS + c,
+                                 (cs[row * L.cp + c] - mc) * rc * to_f(cscale[j * S + c]));
             }
             __syncthreads();
             T *dst = j == 0 ? opQ : opK;
+            T *dstl = j == 0 ? opQl : opKl;
             for (int nb = wave; nb < C / 32; nb += 4) {
                 f32x16_t a1 = zero16(), a2 = zero16();
-                gemm32<T>(a1, opA, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64);
-                gemm32<T>(a2, opA, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
+                gemm32s<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64);
+                gemm32s<T>(a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
                 const int c = nb * 32 + acc32_col(lane);
                 const float bs = to_f(bscale[j * C + c]);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = acc32_row(v, lane);
                     const float ln = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
-                    dst[r * L.ldC + c] = from_f<T>(ln * sigmoid_f(a1[v] + bs) + a2[v]);
+                    put_split<T>(dst, dstl, r * L.ldC + c, ln * sigmoid_f(a1[v] + bs) + a2[v]);
                 }
             }
             __syncthreads();
         }
     } else {
         for (int c = sub; c < S; c += 8)
-            opA[row * L.ldS + c] = from_f<T>(silu_f(cs[row * L.cp + c]));
+            put_split<T>(opA, opAl, row * L.ldS + c, silu_f(cs[row * L.cp + c]));
         __syncthreads();
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm32<T>(a1, opA, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64);
-            gemm32<T>(a2, opA, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
+            gemm32s<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64);
+            gemm32s<T>(a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
             const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = acc32_row(v, lane);
                 const float rm = xs[r * L.xp + c] * st[r * 4 + 1];
-                opQ[r * L.ldC + c] = from_f<T>(rm * (1.0f + a2[v]) + a1[v]);
+                put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + a2[v]) + a1[v]);
             }
         }
         __syncthreads();
     }
 
-    // Q/K/V/G projections
-    T *qo = reinterpret_cast<T *>(p.q);
-    T *ko = reinterpret_cast<T *>(p.k);
+    // Q/K/V/G projections. Q and K (the logit operands) are stored in fp32,
+    // V and G in the storage dtype.
+    float *qo = reinterpret_cast<float *>(p.q);
+    float *ko = reinterpret_cast<float *>(p.k);
     T *vo = reinterpret_cast<T *>(p.v);
     T *go = reinterpret_cast<T *>(p.g);
     if (STYLE == STYLE_AF3) {
         const T *bq = reinterpret_cast<const T *>(p.b_q);
         for (int nb = wave; nb < HD / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm32<T>(a1, opQ, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64);
-            gemm32<T>(a2, opQ, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
+            gemm32s<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64);
+            gemm32s<T>(a2, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
             const int c = nb * 32 + acc32_col(lane);
             const float bias = to_f(bq[c]);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int nn = n0 + acc32_row(v, lane);
                 if (nn < N) {
-                    qo[(int64_t)nn * HD + c] = from_f<T>(a1[v] + bias);
+                    qo[(int64_t)nn * HD + c] = a1[v] + bias;
                     go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(a2[v]));
                 }
             }
             f32x16_t a3 = zero16(), a4 = zero16();
-            gemm32<T>(a3, opK, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64);
-            gemm32<T>(a4, opK, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
+            gemm32s<T>(a3, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64);
+            gemm32s<T>(a4, opK, opKl, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int nn = n0 + acc32_row(v, lane);
                 if (nn < N) {
-                    ko[(int64_t)nn * HD + c] = from_f<T>(a3[v]);
+                    ko[(int64_t)nn * HD + c] = a3[v];
                     vo[(int64_t)nn * HD + c] = from_f<T>(a4[v]);
                 }
             }
@@ -386,8 +404,8 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
             for (int nb = wave; nb < HD / 32; nb += 4) {
                 f32x16_t a1 = zero16(), a2 = zero16();
-                gemm32<T>(a1, opQ, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64);
-                gemm32<T>(a2, opQ, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
+                gemm32s<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64);
+                gemm32s<T>(a2, opQ, opQl, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
                 const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {

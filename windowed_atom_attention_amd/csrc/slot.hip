@@ -13,7 +13,8 @@
 // How: the 16 queries of a block see a narrow band of key ids (the supplied
 // windows are local), so the workgroup stages the K and V rows of that band
 // [jlo, jhi] for one head in LDS (coalesced row loads, up to 128 rows per
-// chunk), computes the dense 16 x rows score tile Q K^T on MFMA, reads each
+// chunk), computes the dense 16 x rows score tile Q K^T on MFMA (fp32
+// operands: Q and K are kept in fp32 because they set the logits), reads each
 // slot's logit out of that tile by its key id, does the softmax in
 // registers (16 lanes per query), scatters the weights into a dense
 // 16 x rows probability tile (repeated ids add up) and gets o = P V on MFMA.
@@ -33,7 +34,7 @@ constexpr int kQB = 16;     // queries per workgroup
 constexpr int kRMAX = 128;  // key rows per staged chunk
 
 struct SlotLayout {
-    int dk, dkp, vtp, sp;
+    int dkS, dkSp, dk, dkp, vtp, sp;
     size_t o_rel, o_beta, o_wpr, o_kst, o_vst, o_s, o_p, total;
 };
 
@@ -42,7 +43,9 @@ __host__ __device__ inline size_t sal16(size_t x) { return (x + 15) & ~(size_t)1
 __host__ __device__ inline SlotLayout slot_layout(int K, int H, int D, int V,
                                                   int esz, int style) {
     SlotLayout L;
-    const int kc = esz == 2 ? 32 : 16; // MFMA k per chunk
+    const int kc = esz == 2 ? 32 : 16; // MFMA k per chunk of the P V product
+    L.dkS = (D + 15) / 16 * 16;          // fp32 score product: 16 per chunk
+    L.dkSp = L.dkS + 4;
     L.dk = (D + kc - 1) / kc * kc;
     L.dkp = L.dk + 16 / esz;
     L.vtp = kRMAX + 8; // bf16 transposed V pitch
@@ -55,7 +58,7 @@ __host__ __device__ inline SlotLayout slot_layout(int K, int H, int D, int V,
     L.o_wpr = o;
     if (style == STYLE_AF3)
         o = sal16(o + (size_t)V * H * 4);
-    L.o_kst = o; o = sal16(o + (size_t)kRMAX * L.dkp * esz);
+    L.o_kst = o; o = sal16(o + (size_t)kRMAX * L.dkSp * 4);
     L.o_vst = o;
     if (esz == 2)
         o = sal16(o + (size_t)L.dk * L.vtp * esz);
@@ -167,12 +170,12 @@ __global__ __launch_bounds__(256) void k_slot(SlotArgs p) {
     int *rel_s = reinterpret_cast<int *>(smem + L.o_rel);
     float *beta = reinterpret_cast<float *>(smem + L.o_beta);
     float *wpr = reinterpret_cast<float *>(smem + L.o_wpr);
-    T *kst = reinterpret_cast<T *>(smem + L.o_kst);
+    float *kst = reinterpret_cast<float *>(smem + L.o_kst);
     T *vst = reinterpret_cast<T *>(smem + L.o_vst);
     float *sbuf = reinterpret_cast<float *>(smem + L.o_s);
     float *pbuf = reinterpret_cast<float *>(smem + L.o_p);
-    const T *qg = reinterpret_cast<const T *>(p.q);
-    const T *kg = reinterpret_cast<const T *>(p.k);
+    const float *qg = reinterpret_cast<const float *>(p.q); // fp32 logit operands
+    const float *kg = reinterpret_cast<const float *>(p.k);
     const T *vg = reinterpret_cast<const T *>(p.v);
     T *att = reinterpret_cast<T *>(p.attention);
     T *og = reinterpret_cast<T *>(p.o);
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(256) void k_slot(SlotArgs p) {
 
     const int span = jhi - jlo + 1;
     const int nch = (span + kRMAX - 1) / kRMAX;
-    const int nkq = L.dk / KC;
+    const int nkq = L.dkS / 16;
     const int g = lane >> 4, l16 = lane & 15;
     const float scale = p.inv_sqrt_d;
 
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(256) void k_slot(SlotArgs p) {
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) {
                 qf[kc] = make_uint4(0, 0, 0, 0);
-                const int d0 = kc * KC + g * QU;
+                const int d0 = kc * 16 + g * 4;
                 if (kc < nkq && aq < A && d0 < D)
                     qf[kc] = *reinterpret_cast<const uint4 *>(qg + (bA + aq) * HD + h * D + d0);
             }
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(256) void k_slot(SlotArgs p) {
             const int c0 = jlo + c * kRMAX;
             const int rows = min(kRMAX, jhi + 1 - c0);
             const int rpad = (rows + 31) / 32 * 32;
-            stage_rows<T>(kst, L.dkp, kg, bA + c0, HD, h * D, D, L.dk, rows, rpad);
+            stage_rows<float>(kst, L.dkSp, kg, bA + c0, HD, h * D, D, L.dkS, rows, rpad);
             if (nch == 1) {
                 if constexpr (sizeof(T) == 2)
                     stage_rows_t(reinterpret_cast<bf16_t *>(vst), L.vtp,
@@ -336,11 +339,11 @@ __global__ __launch_bounds__(256) void k_slot(SlotArgs p) {
             __syncthreads();
             for (int cb = wave; cb < rpad / 16; cb += 4) {
                 f32x4_t acc = zero4();
-                const T *krow = kst + (cb * 16 + l16) * L.dkp + g * QU;
+                const float *krow = kst + (cb * 16 + l16) * L.dkSp + g * 4;
 #pragma unroll
                 for (int kc = 0; kc < 8; ++kc)
                     if (kc < nkq)
-                        Mma16<T>::mma(acc, qf[kc], *reinterpret_cast<const uint4 *>(krow + kc * KC));
+                        Mma16<float>::mma(acc, qf[kc], *reinterpret_cast<const uint4 *>(krow + kc * 16));
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     sbuf[acc16_row(v, lane) * L.sp + cb * 16 + acc16_col(lane)] = acc[v];
