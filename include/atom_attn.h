@@ -64,8 +64,9 @@ enum { ATOM_ATTN_ENCODER = 0, ATOM_ATTN_DECODER = 1 };
  * width, V pair width (AF3; ignored for ESMFold2), M transition width,
  * U token width (encoder output width, decoder input width).
  * Supported set of the kernels: C, S, H*D, M, U multiples of 32 and at most
- * 512; D a multiple of 16 and at most 128; K <= 512; AF3 V a multiple of 8
- * and at most 64. 16-byte aligned float pointers and workspace. */
+ * 512; D one of 16, 32, 64, 128; K <= 256; AF3: V a multiple of 8
+ * with V*sizeof(dtype) <= 64 bytes, H <= 8, and H <= 4 when K > 128.
+ * Float pointers and the workspace must be 16-byte aligned. */
 typedef struct {
     int64_t B, A, T, K, C, S, H, D, V, M, U;
 } atom_attn_dims;
@@ -151,18 +152,23 @@ int atom_attn_masks(const atom_attn_dims *dims, const atom_attn_inputs *in,
  * [B,A,H*D] (head-major; for ESMFold2 already RMS-normalised and rotated)
  * and usable [B,A]. q and k are fp32 whatever `dtype` is (the block keeps
  * the logit operands in fp32); v, pair, pair_scale, w_pair, attention and
- * o use `dtype`. logits q.k/sqrt(D) (+ AF3 pair bias
- * (LN(pair) * pair_scale) @ w_pair), softmax over the allowed slots with
- * exact-zero empty rows, attention [B,H,A,K] and o [B,A,H*D] = sum of
- * weights times v rows. Same kernel as the full block. Uses dims B, A, K,
- * H, D, V. eps is used by the pair LayerNorm. */
+ * o use `dtype`. Computes logits q.k/sqrt(D) (+ AF3 pair bias
+ * (LN(pair) * pair_scale) @ w_pair), the softmax over the allowed slots
+ * with exact-zero empty rows, attention [B,H,A,K] and o [B,A,H*D] = sum of
+ * weights times v rows -- with the same kernel as the full block, after a
+ * copy of v into the transposed layout that kernel reads (in `workspace`,
+ * atom_attn_slot_workspace_bytes() bytes). Uses dims B, A, K, H, D, V; eps
+ * is used by the pair LayerNorm. */
+int atom_attn_slot_workspace_bytes(const atom_attn_dims *dims, int dtype,
+                                   size_t *bytes);
 int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
                              double eps, int64_t radius, const uint8_t *usable,
                              const void *q, const void *k, const void *v,
                              const int64_t *key_index,
                              const uint8_t *window_mask, const void *pair,
                              const void *pair_scale, const void *w_pair,
-                             void *attention, void *o, void *stream);
+                             void *attention, void *o, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *atom_attn_error_string(int code);

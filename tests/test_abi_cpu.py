@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.EXPORTS)
-    assert lib.atom_attn_version() == 1
+    assert lib.atom_attn_version() == 2
 
 
 def test_error_strings():
@@ -61,6 +61,9 @@ def test_workspace_query_status_codes():
     assert _ws(_dims(H=4, D=7), style=N.ESMFOLD2)[0] == N.EODD_HEAD
     assert _ws(_dims(C=48))[0] == N.EUNSUPPORTED
     assert _ws(_dims(K=1000))[0] == N.EUNSUPPORTED
+    assert _ws(_dims(K=300))[0] == N.EUNSUPPORTED
+    assert _ws(_dims(V=32))[0] == N.EUNSUPPORTED            # fp32 pair row > 64 B
+    assert _ws(_dims(V=32), dtype=N.BF16)[0] == N.OK
     assert _ws(_dims(V=3))[0] == N.EUNSUPPORTED
     assert _ws(_dims(V=3), style=N.ESMFOLD2)[0] == N.OK  # V unused there
     # decoder adds the fp32 token projection
@@ -91,7 +94,7 @@ def test_block_rejects_bad_arguments_before_any_launch():
     assert lib.atom_attn_masks(ctypes.byref(nd), None, -1, None, None, None) == N.EINVAL
     assert lib.atom_attn_slot_attention(ctypes.byref(nd), N.AF3, N.F32, 1e-5, -1,
                                         None, None, None, None, None, None, None,
-                                        None, None, None, None, None) == N.EINVAL
+                                        None, None, None, None, None, 0, None) == N.EINVAL
 
 
 def test_python_binding_argument_checks():

@@ -39,6 +39,10 @@ SMALL = [
     ("2", dict(A=200, dtype=torch.float32, stage="decoder")),
     ("3", dict(B=2, A=300, dtype=torch.float32, style="esmfold2")),
     ("4a", dict(A=333, stage="decoder", radius=20)),
+    # random key ids over hundreds of atoms: key bands wider than one chunk
+    ("0", dict(A=600)),
+    ("0", dict(A=450, K=40, style="esmfold2", dtype=torch.bfloat16)),
+    ("0", dict(A=300, K=200, dtype=torch.bfloat16, stage="decoder")),
 ]
 
 

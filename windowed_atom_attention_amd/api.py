@@ -311,12 +311,18 @@ def slot_attention(q, k, v, usable, key_index, window_mask, heads: int,
     att = torch.empty((B, H, A, K), dtype=dtype, device=dev)
     o = torch.empty((B, A, HD), dtype=dtype, device=dev)
     nd = N.Dims(B=B, A=A, T=1, K=K, C=1, S=1, H=H, D=D, V=V, M=1, U=1)
+    need = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_slot_workspace_bytes(ctypes.byref(nd), _FLOAT_DTYPES[dtype],
+                                                   ctypes.byref(need)),
+            "atom_attn_slot_workspace_bytes")
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         rc = N.lib().atom_attn_slot_attention(
             ctypes.byref(nd), _STYLES[style], _FLOAT_DTYPES[dtype], float(eps),
             int(radius), us.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
             ki.data_ptr(), wm.data_ptr(), ptrs[0], ptrs[1], ptrs[2],
-            att.data_ptr(), o.data_ptr(), _stream_handle(dev))
+            att.data_ptr(), o.data_ptr(), ws.data_ptr(), int(need.value),
+            _stream_handle(dev))
     N.check(rc, "atom_attn_slot_attention")
     torch.cuda.current_stream(dev).synchronize()
     return att, o

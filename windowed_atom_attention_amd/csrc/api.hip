@@ -13,7 +13,7 @@ using namespace waa;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 // ------------------------------------------------------------ profiler
 
@@ -97,9 +97,7 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
     if (!mult32_le(d->C, 512) || !mult32_le(d->S, 512) || !mult32_le(HD, 512) ||
         !mult32_le(d->M, 512) || !mult32_le(d->U, 512))
         return ATOM_ATTN_EUNSUPPORTED;
-    if (d->D % 16 != 0 || d->D > 128 || d->K > 512)
-        return ATOM_ATTN_EUNSUPPORTED;
-    if (style == ATOM_ATTN_AF3 && (d->V % 8 != 0 || d->V > 64))
+    if ((d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) || d->K > 256)
         return ATOM_ATTN_EUNSUPPORTED;
     if (d->B * d->A > (int64_t)1 << 30 || d->B * d->T > (int64_t)1 << 30 ||
         d->B * d->A * d->K > ((int64_t)1 << 31) - 1 ||
@@ -195,7 +193,8 @@ Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
     L.packed = o; o = up256(o + (size_t)units * 16);
     L.q = o; o = up256(o + N * row32);
     L.k = o; o = up256(o + N * row32);
-    L.v = o; o = up256(o + N * rowb);
+    // V transposed per batch: [B][H*D][vt_pitch(A)]
+    L.v = o; o = up256(o + (size_t)(d->B * d->H * d->D) * vt_pitch((int)d->A) * esz);
     L.g = o; o = up256(o + N * rowb);
     L.o = o; o = up256(o + N * rowb);
     L.usable = o; o = up256(o + N);
@@ -360,8 +359,9 @@ const char *atom_attn_error_string(int code) {
         return "the HIP runtime refused a kernel launch";
     case ATOM_ATTN_EUNSUPPORTED:
         return "shape outside the supported set (C, S, H*D, M, U multiples of 32 "
-               "and <= 512; D a multiple of 16 and <= 128; K <= 512; AF3 V a "
-               "multiple of 8 and <= 64)";
+               "and <= 512; D one of 16, 32, 64, 128; K <= 256; AF3: V a "
+               "multiple of 8 with V*sizeof(dtype) <= 64, H <= 8, and H <= 4 "
+               "when K > 128)";
     default:
         return "unknown status";
     }
@@ -415,13 +415,24 @@ int atom_attn_masks(const atom_attn_dims *dims, const atom_attn_inputs *in,
     });
 }
 
+int atom_attn_slot_workspace_bytes(const atom_attn_dims *dims, int dtype,
+                                   size_t *bytes) {
+    if (!dims || dims->B < 1 || dims->A < 1 || dims->H < 1 || dims->D < 1 || !bytes ||
+        (dtype != ATOM_ATTN_F32 && dtype != ATOM_ATTN_BF16))
+        return ATOM_ATTN_EINVAL;
+    const size_t esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
+    *bytes = up256((size_t)(dims->B * dims->H * dims->D) * vt_pitch((int)dims->A) * esz);
+    return ATOM_ATTN_OK;
+}
+
 int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
                              double eps, int64_t radius, const uint8_t *usable,
                              const void *q, const void *k, const void *v,
                              const int64_t *key_index,
                              const uint8_t *window_mask, const void *pair,
                              const void *pair_scale, const void *w_pair,
-                             void *attention, void *o, void *stream) {
+                             void *attention, void *o, void *workspace,
+                             size_t workspace_bytes, void *stream) {
     if (!dims || dims->B < 1 || dims->A < 1 || dims->K < 1 || dims->H < 1 ||
         dims->D < 1 || (style == ATOM_ATTN_AF3 && dims->V < 1))
         return ATOM_ATTN_EINVAL;
@@ -451,16 +462,22 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
     if (!slot_supported(d, dt, st) || dims->B * dims->A > ((int64_t)1 << 30) ||
         dims->B * dims->H * dims->A * dims->K > ((int64_t)1 << 31) - 1)
         return ATOM_ATTN_EUNSUPPORTED;
+    size_t need_ws = 0;
+    atom_attn_slot_workspace_bytes(dims, dtype, &need_ws);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need_ws)
+        return ATOM_ATTN_EWORKSPACE;
     SlotArgs sa;
     sa.B = d.B; sa.A = d.A; sa.K = d.K; sa.H = d.H; sa.D = d.D; sa.V = d.V;
     sa.eps = (float)eps;
     sa.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d.D));
     sa.radius = radius;
     sa.usable = usable; sa.window_mask = window_mask; sa.key_index = key_index;
-    sa.q = q; sa.k = k; sa.v = v;
+    sa.q = q; sa.k = k; sa.v = workspace;
     sa.pair = pair; sa.pair_scale = pair_scale; sa.w_pair = w_pair;
     sa.attention = attention; sa.o = o;
     hipStream_t s = (hipStream_t)stream;
+    if (launch_vt(v, workspace, d.B, d.A, (int)HD, dt, s) != hipSuccess)
+        return ATOM_ATTN_ELAUNCH;
     return timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); });
 }
 

@@ -69,6 +69,32 @@ template <int W> __device__ __forceinline__ float group_max(float v) {
         v = fmaxf(v, __shfl_xor(v, m, W));
     return v;
 }
+// Reductions over aligned groups of 16 lanes with DPP lane permutations
+// (pure VALU, no LDS traffic): swap neighbours, swap pairs, mirror within
+// 8, mirror within 16 -- after the four steps every lane holds the result.
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+    switch (ctrl) {
+    case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    }
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_f(v, 0xB1);
+    v += dpp_f(v, 0x4E);
+    v += dpp_f(v, 0x141);
+    v += dpp_f(v, 0x140);
+    return v;
+}
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, dpp_f(v, 0xB1));
+    v = fmaxf(v, dpp_f(v, 0x4E));
+    v = fmaxf(v, dpp_f(v, 0x141));
+    v = fmaxf(v, dpp_f(v, 0x140));
+    return v;
+}
+
 __device__ __forceinline__ int wave_min_i(int v) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1)

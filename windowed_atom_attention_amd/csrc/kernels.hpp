@@ -15,6 +15,11 @@ struct Dims {
     int B, A, T, K, C, S, H, D, V, M, U;
 };
 
+// V is stored transposed per batch, [B][H*D][vt_pitch(A)], so that the slot
+// kernel's P V product reads 8 (bf16) or 4 (fp32) consecutive key rows of one
+// channel as one 16-byte vector.
+__host__ __device__ inline int vt_pitch(int A) { return (A + 7) & ~7; }
+
 // Offsets, in 16-byte units, of each packed weight matrix inside the packed
 // area of the workspace (-1 = absent).
 struct PackedOffsets {
@@ -48,7 +53,7 @@ struct BlockArgs {
 
 // The slot-attention kernel's arguments.
 struct SlotArgs {
-    int B, A, K, H, D, V;
+    int B, A, K, H, D, V;  // v is transposed: [B][H*D][vt_pitch(A)]
     float eps, inv_sqrt_d;
     int64_t radius;
     const uint8_t *usable, *window_mask;
@@ -86,6 +91,8 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
                        hipStream_t s);
 hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s);
 hipError_t launch_slot(const SlotArgs &a, int dtype, int style, hipStream_t s);
+hipError_t launch_vt(const void *v, void *vt, int B, int A, int HD, int dtype,
+                     hipStream_t s);
 hipError_t launch_masks(const Dims &d, const uint8_t *valid,
                         const uint8_t *token_valid, const uint8_t *window_mask,
                         const int64_t *atom_to_token, const int64_t *key_index,

@@ -117,7 +117,7 @@ hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
 // that the logits path keeps ~16 mantissa bits; fp32 tiles are single.
 struct PrepLayout {
     int xp, cp, hp, ldS, ldC;
-    size_t o_cs, o_st, o_us, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
+    size_t o_cs, o_st, o_us, o_rb, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -135,6 +135,7 @@ __host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int st
     L.o_cs = o; o += 32 * L.cp * 4;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
+    L.o_rb = o; o += 64 * 4; // per row: atom index within its batch, then batch
     L.o_opA = o; o += tS;
     L.o_opAl = o; if (split) o += tS;
     L.o_opQ = o; o += tC;
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
     float *cs = reinterpret_cast<float *>(smem + L.o_cs);
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
+    int *rb = reinterpret_cast<int *>(smem + L.o_rb);
     T *opA = reinterpret_cast<T *>(smem + L.o_opA);
     T *opAl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opAl) : nullptr;
     T *opQ = reinterpret_cast<T *>(smem + L.o_opQ);
@@ -232,6 +234,8 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
     }
     if (sub == 0) {
         us[row] = u;
+        rb[row] = inb ? n - b * d.A : 0; // atom index within its batch
+        rb[32 + row] = b;
         if (inb)
             p.usable[n] = u;
     }
@@ -370,6 +374,11 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
     float *ko = reinterpret_cast<float *>(p.k);
     T *vo = reinterpret_cast<T *>(p.v);
     T *go = reinterpret_cast<T *>(p.g);
+    const int vtp = vt_pitch(d.A);
+    // transposed V position of (atom row r of this tile, channel c)
+    auto vt_at = [&](int r, int c) -> int64_t {
+        return ((int64_t)rb[32 + r] * HD + c) * vtp + rb[r];
+    };
     if (STYLE == STYLE_AF3) {
         const T *bq = reinterpret_cast<const T *>(p.b_q);
         for (int nb = wave; nb < HD / 32; nb += 4) {
@@ -394,7 +403,7 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
                 const int nn = n0 + acc32_row(v, lane);
                 if (nn < N) {
                     ko[(int64_t)nn * HD + c] = a3[v];
-                    vo[(int64_t)nn * HD + c] = from_f<T>(a4[v]);
+                    vo[vt_at(acc32_row(v, lane), c)] = from_f<T>(a4[v]);
                 }
             }
         }
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
                         if (pass == 0)
                             go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(a2[v]));
                         else
-                            vo[(int64_t)nn * HD + c] = from_f<T>(a2[v]);
+                            vo[vt_at(r, c)] = from_f<T>(a2[v]);
                     }
                 }
             }
