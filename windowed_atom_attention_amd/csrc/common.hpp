@@ -205,6 +205,47 @@ __device__ __forceinline__ void gemm32s(f32x16_t &acc, const T *Ahi, const T *Al
     }
 }
 
+// Two products at once, acc1 += A1 @ B1 and acc2 += A2 @ B2, over nk1 and
+// nk2 16-byte k-chunks (nk2 = 0 for a single product). A tiles come from LDS
+// (optionally split into hi + lo parts, see gemm32s), B from the packed
+// weights in L2. The B chunks of both products are fetched eight at a time
+// before any of them is used, so a batch costs one L2 round trip instead of
+// one per chunk.
+template <typename T>
+__device__ __forceinline__ void gemm_dual(f32x16_t &acc1, const T *A1, const T *A1lo,
+                                          int lda1, int nk1, const uint4 *__restrict__ B1,
+                                          f32x16_t &acc2, const T *A2, const T *A2lo,
+                                          int lda2, int nk2, const uint4 *__restrict__ B2) {
+    constexpr int KC = Mma32<T>::KC;
+    const int lane = threadIdx.x & 63;
+    const int o1 = (lane & 31) * lda1 + (lane >> 5) * Mma32<T>::HALF;
+    const int o2 = (lane & 31) * lda2 + (lane >> 5) * Mma32<T>::HALF;
+    const int nk = nk1 > nk2 ? nk1 : nk2;
+    for (int kb = 0; kb < nk; kb += 8) {
+        uint4 b1[8], b2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (kb + j < nk1)
+                b1[j] = B1[(kb + j) * 64 + lane];
+            if (kb + j < nk2)
+                b2[j] = B2[(kb + j) * 64 + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (kb + j < nk1) {
+                Mma32<T>::mma(acc1, *reinterpret_cast<const uint4 *>(A1 + o1 + (kb + j) * KC), b1[j]);
+                if (A1lo != nullptr)
+                    Mma32<T>::mma(acc1, *reinterpret_cast<const uint4 *>(A1lo + o1 + (kb + j) * KC), b1[j]);
+            }
+            if (kb + j < nk2) {
+                Mma32<T>::mma(acc2, *reinterpret_cast<const uint4 *>(A2 + o2 + (kb + j) * KC), b2[j]);
+                if (A2lo != nullptr)
+                    Mma32<T>::mma(acc2, *reinterpret_cast<const uint4 *>(A2lo + o2 + (kb + j) * KC), b2[j]);
+            }
+        }
+    }
+}
+
 // Store x into a split operand pair: hi = x rounded to T, lo = the rest
 // rounded to T (for fp32 storage lo is not used).
 template <typename T>

@@ -40,33 +40,34 @@ __device__ __forceinline__ void load16_f2(const T *src, float *out) {
 }
 
 struct PostLayout {
-    int xp, cp, ldS, ldC, ldHD, ldM;
-    size_t o_cs, o_st, o_us, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
+    int xp, ldS, ldC, ldHD, ldH;
+    size_t o_st, o_us, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
 };
+
+// Transition width handled per pass: h is staged kMC columns at a time.
+constexpr int kMC = 128;
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 __host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int style) {
     PostLayout L;
     L.xp = d.C + 4;
-    L.cp = d.S + 4;
     L.ldS = d.S + 16 / esz;
     L.ldC = d.C + 16 / esz;
     L.ldHD = d.H * d.D + 16 / esz;
-    L.ldM = d.M + 16 / esz;
+    L.ldH = (d.M < kMC ? d.M : kMC) + 16 / esz;
     size_t o = 32 * (size_t)L.xp * 4;
-    L.o_cs = o;
-    if (style == STYLE_AF3)
-        o += 32 * (size_t)L.cp * 4;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
     L.o_opC = o; o = al16(o + 32 * (size_t)L.ldS * esz);
-    L.o_opC2 = o;
-    if (style == STYLE_AF3)
-        o = al16(o + 32 * (size_t)L.ldS * esz);
-    L.o_opU = o; o = al16(o + 32 * (size_t)L.ldHD * esz);
+    // one tile holds, in turn, o*G (until x1), LN(c)*cond_scale[2] (AF3,
+    // until z) and a chunk of h (transition)
+    int w = L.ldHD > L.ldH ? L.ldHD : L.ldH;
+    if (style == STYLE_AF3 && L.ldS > w)
+        w = L.ldS;
+    L.o_opU = L.o_opC2 = L.o_opH = o;
+    o = al16(o + 32 * (size_t)w * esz);
     L.o_opZ = o; o = al16(o + 32 * (size_t)L.ldC * esz);
-    L.o_opH = o; o = al16(o + 32 * (size_t)L.ldM * esz);
     L.total = o;
     return L;
 }
@@ -76,7 +77,7 @@ size_t post_lds_bytes(const Dims &d, int dtype, int style) {
 }
 
 template <typename T, int STYLE, int STAGE>
-__global__ __launch_bounds__(256) void k_post(BlockArgs p) {
+__global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D, M = d.M;
@@ -88,7 +89,6 @@ __global__ __launch_bounds__(256) void k_post(BlockArgs p) {
     constexpr int E = 16 / sizeof(T);
     const PostLayout L = post_layout(d, sizeof(T), STYLE);
     float *xs = reinterpret_cast<float *>(smem);
-    float *cs = reinterpret_cast<float *>(smem + L.o_cs);
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
     T *opC = reinterpret_cast<T *>(smem + L.o_opC);
@@ -138,14 +138,9 @@ __global__ __launch_bounds__(256) void k_post(BlockArgs p) {
                     cv[e] = 0.0f;
             }
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (STYLE == STYLE_AF3) {
-                    cs[row * L.cp + vi * E + e] = cv[e];
-                    opC[row * L.ldS + vi * E + e] = from_f<T>(cv[e]);
-                } else {
-                    opC[row * L.ldS + vi * E + e] = from_f<T>(silu_f(cv[e]));
-                }
-            }
+            for (int e = 0; e < E; ++e)
+                opC[row * L.ldS + vi * E + e] =
+                    STYLE == STYLE_AF3 ? from_f<T>(cv[e]) : from_f<T>(silu_f(cv[e]));
         }
         // value-gated attention output (o * G), rounded to the storage type
         const T *orow = reinterpret_cast<const T *>(p.o) + (int64_t)n * HD;
@@ -170,32 +165,14 @@ __global__ __launch_bounds__(256) void k_post(BlockArgs p) {
     const int nkS = S / Mma32<T>::KC, nkC = C / Mma32<T>::KC;
     const int nkHD = HD / Mma32<T>::KC, nkM = M / Mma32<T>::KC;
 
-    if (STYLE == STYLE_AF3) {
-        // c_2 = LN(c) * cond_scale[2]
-        const float *cr = cs + row * L.cp;
-        float s = 0.0f;
-        for (int c = sub; c < S; c += 8)
-            s += cr[c];
-        const float mc = group_sum<8>(s) / (float)S;
-        float q = 0.0f;
-        for (int c = sub; c < S; c += 8) {
-            const float t = cr[c] - mc;
-            q += t * t;
-        }
-        const float rc = 1.0f / sqrtf(group_sum<8>(q) / (float)S + p.eps);
-        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
-        for (int c = sub; c < S; c += 8)
-            opC2[row * L.ldS + c] = from_f<T>((cr[c] - mc) * rc * to_f(cscale[2 * S + c]));
-    }
-
     // x1 = x0 + g_att * (o*G) @ w_attention_out
     {
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm32<T>(a1, opU, L.ldHD, nkHD, p.pk + p.off.w_ao + (int64_t)nb * nkHD * 64);
-            gemm32<T>(a2, opC, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
+            gemm_dual<T>(a1, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao + (int64_t)nb * nkHD * 64,
+                         a2, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
             const int c = nb * 32 + acc32_col(lane);
             const float bias = STYLE == STYLE_AF3 ? to_f(brg[c]) : 0.0f;
 #pragma unroll
@@ -207,6 +184,25 @@ __global__ __launch_bounds__(256) void k_post(BlockArgs p) {
         }
     }
     __syncthreads();
+    if (STYLE == STYLE_AF3) {
+        // c_2 = LN(c) * cond_scale[2] (opC holds the raw condition exactly),
+        // into the tile o*G occupied
+        const T *cr = opC + row * L.ldS;
+        float s = 0.0f;
+        for (int c = sub; c < S; c += 8)
+            s += to_f(cr[c]);
+        const float mc = group_sum<8>(s) / (float)S;
+        float q = 0.0f;
+        for (int c = sub; c < S; c += 8) {
+            const float t = to_f(cr[c]) - mc;
+            q += t * t;
+        }
+        const float rc = 1.0f / sqrtf(group_sum<8>(q) / (float)S + p.eps);
+        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
+        for (int c = sub; c < S; c += 8)
+            opC2[row * L.ldS + c] = from_f<T>((to_f(cr[c]) - mc) * rc * to_f(cscale[2 * S + c]));
+    }
+
     // statistics of the NEW state for the transition norm
     {
         const float *xr = xs + row * L.xp;
@@ -243,11 +239,11 @@ __global__ __launch_bounds__(256) void k_post(BlockArgs p) {
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
             if (STYLE == STYLE_AF3) {
-                gemm32<T>(a1, opC2, L.ldS, nkS, p.pk + p.off.w_scale[2] + (int64_t)nb * nkS * 64);
-                gemm32<T>(a2, opC2, L.ldS, nkS, p.pk + p.off.w_shift[2] + (int64_t)nb * nkS * 64);
+                gemm_dual<T>(a1, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_scale[2] + (int64_t)nb * nkS * 64,
+                             a2, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_shift[2] + (int64_t)nb * nkS * 64);
             } else {
-                gemm32<T>(a1, opC, L.ldS, nkS, p.pk + p.off.w_mod[3] + (int64_t)nb * nkS * 64);
-                gemm32<T>(a2, opC, L.ldS, nkS, p.pk + p.off.w_mod[4] + (int64_t)nb * nkS * 64);
+                gemm_dual<T>(a1, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[3] + (int64_t)nb * nkS * 64,
+                             a2, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[4] + (int64_t)nb * nkS * 64);
             }
             const int c = nb * 32 + acc32_col(lane);
             const float bias = STYLE == STYLE_AF3 ? to_f(bsc[2 * C + c]) : 0.0f;
@@ -265,40 +261,61 @@ __global__ __launch_bounds__(256) void k_post(BlockArgs p) {
         }
     }
     __syncthreads();
-    // h = SiLU(z @ w_ff_gate) * (z @ w_ff_up)
-    for (int nb = wave; nb < M / 32; nb += 4) {
-        f32x16_t a1 = zero16(), a2 = zero16();
-        gemm32<T>(a1, opZ, L.ldC, nkC, p.pk + p.off.ff_gate + (int64_t)nb * nkC * 64);
-        gemm32<T>(a2, opZ, L.ldC, nkC, p.pk + p.off.ff_up + (int64_t)nb * nkC * 64);
-        const int c = nb * 32 + acc32_col(lane);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = acc32_row(v, lane);
-            opH[r * L.ldM + c] = from_f<T>(silu_f(a1[v]) * a2[v]);
-        }
-    }
-    __syncthreads();
-    // x2 = x1 + g_tr * h @ w_ff_out; hidden = select(usable, x2, 0)
+    // x2 = x1 + g_tr * (h @ w_ff_out), h = SiLU(z @ w_ff_gate) * (z @ w_ff_up),
+    // with h staged kMC columns at a time. Output columns go in groups of
+    // 128 (one 32-column block per wave), so each wave carries one block of
+    // h @ w_ff_out in registers across the passes; with C > 128 and M > kMC
+    // the h chunks are recomputed per group. hidden = select(usable, x2, 0).
     {
+        constexpr int KC = Mma32<T>::KC;
         T *hid = reinterpret_cast<T *>(p.hidden);
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[1] : p.off.w_mod[5];
-        for (int nb = wave; nb < C / 32; nb += 4) {
-            f32x16_t a1 = zero16(), a2 = zero16();
-            gemm32<T>(a1, opH, L.ldM, nkM, p.pk + p.off.ff_out + (int64_t)nb * nkM * 64);
-            gemm32<T>(a2, opC, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
-            const int c = nb * 32 + acc32_col(lane);
-            const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
+        const bool single = M <= kMC;
+        for (int cg = 0; cg < C / 32; cg += 4) {
+            const int nb = cg + wave;
+            const bool own = nb < C / 32;
+            f32x16_t acc = zero16();
+            for (int m0 = 0; m0 < M; m0 += kMC) {
+                const int mc = M - m0 < kMC ? M - m0 : kMC;
+                if (cg == 0 || !single) {
+                    if (m0 > 0 || cg > 0)
+                        __syncthreads(); // the previous chunk of h has been consumed
+                    for (int hb = wave; hb < mc / 32; hb += 4) {
+                        const int64_t wb = (int64_t)(m0 / 32 + hb) * nkC * 64;
+                        f32x16_t a1 = zero16(), a2 = zero16();
+                        gemm_dual<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + wb,
+                                     a2, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_up + wb);
+                        const int c = hb * 32 + acc32_col(lane);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = acc32_row(v, lane);
-                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(a2[v] + bias) : a2[v];
-                const float x2 = xs[r * L.xp + c] + gate * a1[v];
-                const float h = us[r] ? x2 : 0.0f;
-                xs[r * L.xp + c] = h;
-                const int nn = n0 + r;
-                if (nn < N)
-                    hid[(int64_t)nn * C + c] = from_f<T>(h);
+                        for (int v = 0; v < 16; ++v)
+                            opH[acc32_row(v, lane) * L.ldH + c] = from_f<T>(silu_f(a1[v]) * a2[v]);
+                    }
+                    __syncthreads();
+                }
+                if (!own)
+                    continue;
+                const bool last = m0 + kMC >= M;
+                f32x16_t ga = zero16();
+                gemm_dual<T>(acc, opH, nullptr, L.ldH, mc / KC,
+                             p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64,
+                             ga, opC, nullptr, L.ldS, last ? nkS : 0,
+                             p.pk + offg + (int64_t)nb * nkS * 64);
+                if (last) {
+                    const int c = nb * 32 + acc32_col(lane);
+                    const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int r = acc32_row(v, lane);
+                        const float gate = STYLE == STYLE_AF3 ? sigmoid_f(ga[v] + bias) : ga[v];
+                        const float x2 = xs[r * L.xp + c] + gate * acc[v];
+                        const float h = us[r] ? x2 : 0.0f;
+                        xs[r * L.xp + c] = h;
+                        const int nn = n0 + r;
+                        if (nn < N)
+                            hid[(int64_t)nn * C + c] = from_f<T>(h);
+                    }
+                }
             }
         }
     }
@@ -471,7 +488,9 @@ __global__ __launch_bounds__(256) void k_pool(BlockArgs p) {
         __syncthreads();
         for (int nb = wave; nb < U / 32; nb += 4) {
             f32x16_t a1 = zero16();
-            gemm32<T>(a1, opA, L.ldC, nkc, p.pk + p.off.w_pool + (int64_t)nb * nkc * 64);
+            f32x16_t unused = zero16();
+            gemm_dual<T>(a1, opA, nullptr, L.ldC, nkc, p.pk + p.off.w_pool + (int64_t)nb * nkc * 64,
+                         unused, opA, nullptr, L.ldC, 0, nullptr);
             const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
             for (int v = 0; v < 16; ++v)

@@ -78,7 +78,9 @@ __global__ __launch_bounds__(256) void k_token_proj(BlockArgs p) {
     const int nkc = d.U / Mma32<T>::KC;
     for (int nb = wave; nb < d.C / 32; nb += 4) {
         f32x16_t acc = zero16();
-        gemm32<T>(acc, opA, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64);
+        f32x16_t unused = zero16();
+        gemm_dual<T>(acc, opA, nullptr, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64,
+                     unused, opA, nullptr, ldU, 0, nullptr);
         const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -116,8 +118,8 @@ hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
 // (c_j or SiLU(c), q_in, kv_in) are split into hi + lo parts for bf16 so
 // that the logits path keeps ~16 mantissa bits; fp32 tiles are single.
 struct PrepLayout {
-    int xp, cp, hp, ldS, ldC;
-    size_t o_cs, o_st, o_us, o_rb, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
+    int xp, hp, ldS, ldC;
+    size_t o_st, o_us, o_rb, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -126,13 +128,11 @@ __host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int st
     PrepLayout L;
     const bool split = esz == 2;
     L.xp = d.C + 4;
-    L.cp = d.S + 4;
     L.hp = d.H * d.D + 4;
     L.ldS = d.S + 16 / esz;
     L.ldC = d.C + 16 / esz;
     const size_t tS = align16(32 * (size_t)L.ldS * esz), tC = align16(32 * (size_t)L.ldC * esz);
     size_t o = 32 * L.xp * 4;
-    L.o_cs = o; o += 32 * L.cp * 4;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
     L.o_rb = o; o += 64 * 4; // per row: atom index within its batch, then batch
@@ -188,7 +188,7 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
 }
 
 template <typename T, int STYLE, int STAGE>
-__global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
+__global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D;
@@ -212,7 +212,6 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
 
     const PrepLayout L = prep_layout(d, sizeof(T), STYLE);
     float *xs = reinterpret_cast<float *>(smem);
-    float *cs = reinterpret_cast<float *>(smem + L.o_cs);
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
     int *rb = reinterpret_cast<int *>(smem + L.o_rb);
@@ -261,22 +260,11 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
             for (int e = 0; e < E; ++e)
                 xs[row * L.xp + vi * E + e] = xv[e];
         }
-        const T *cr = reinterpret_cast<const T *>(p.condition) + (int64_t)n * S;
-        for (int vi = sub; vi < S / E; vi += 8) {
-            float cv[E];
-            if (u) {
-                load16_f<T>(cr + vi * E, cv);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    cv[e] = 0.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                cs[row * L.cp + vi * E + e] = cv[e];
-        }
     }
     __syncthreads();
+    // the sanitised condition row (zero for unusable atoms), read on demand
+    const T *crow = reinterpret_cast<const T *>(p.condition) + (int64_t)n * S;
+    auto cond = [&](int c) -> float { return u ? to_f(crow[c]) : 0.0f; };
 
     // row statistics of x0 (and of c for AF3)
     {
@@ -292,14 +280,13 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
                 q += t * t;
             }
             const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
-            const float *cr = cs + row * L.cp;
             float s2 = 0.0f;
             for (int c = sub; c < S; c += 8)
-                s2 += cr[c];
+                s2 += cond(c);
             const float mc = group_sum<8>(s2) / (float)S;
             float q2 = 0.0f;
             for (int c = sub; c < S; c += 8) {
-                const float t = cr[c] - mc;
+                const float t = cond(c) - mc;
                 q2 += t * t;
             }
             const float rc = 1.0f / sqrtf(group_sum<8>(q2) / (float)S + p.eps);
@@ -329,15 +316,15 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
                 const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
                 for (int c = sub; c < S; c += 8)
                     put_split<T>(opA, opAl, row * L.ldS + c,
-                                 (cs[row * L.cp + c] - mc) * rc * to_f(cscale[j * S + c]));
+                                 (cond(c) - mc) * rc * to_f(cscale[j * S + c]));
             }
             __syncthreads();
             T *dst = j == 0 ? opQ : opK;
             T *dstl = j == 0 ? opQl : opKl;
             for (int nb = wave; nb < C / 32; nb += 4) {
                 f32x16_t a1 = zero16(), a2 = zero16();
-                gemm32s<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64);
-                gemm32s<T>(a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
+                gemm_dual<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64,
+                             a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
                 const int c = nb * 32 + acc32_col(lane);
                 const float bs = to_f(bscale[j * C + c]);
 #pragma unroll
@@ -351,12 +338,12 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
         }
     } else {
         for (int c = sub; c < S; c += 8)
-            put_split<T>(opA, opAl, row * L.ldS + c, silu_f(cs[row * L.cp + c]));
+            put_split<T>(opA, opAl, row * L.ldS + c, silu_f(cond(c)));
         __syncthreads();
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm32s<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64);
-            gemm32s<T>(a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
+            gemm_dual<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64,
+                         a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
             const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -383,8 +370,8 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
         const T *bq = reinterpret_cast<const T *>(p.b_q);
         for (int nb = wave; nb < HD / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm32s<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64);
-            gemm32s<T>(a2, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
+            gemm_dual<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64,
+                         a2, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
             const int c = nb * 32 + acc32_col(lane);
             const float bias = to_f(bq[c]);
 #pragma unroll
@@ -396,8 +383,8 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
                 }
             }
             f32x16_t a3 = zero16(), a4 = zero16();
-            gemm32s<T>(a3, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64);
-            gemm32s<T>(a4, opK, opKl, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
+            gemm_dual<T>(a3, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64,
+                         a4, opK, opKl, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int nn = n0 + acc32_row(v, lane);
@@ -413,8 +400,8 @@ __global__ __launch_bounds__(256) void k_prep(BlockArgs p) {
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
             for (int nb = wave; nb < HD / 32; nb += 4) {
                 f32x16_t a1 = zero16(), a2 = zero16();
-                gemm32s<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64);
-                gemm32s<T>(a2, opQ, opQl, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
+                gemm_dual<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64,
+                             a2, opQ, opQl, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
                 const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
