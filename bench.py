@@ -62,7 +62,8 @@ def kernel_work(w):
 
 def _source_sha(kernel):
     files = {"slot_attention": "slot.hip", "prep": "prep.hip", "post": "post.hip",
-             "pool": "post.hip", "token_proj": "prep.hip", "pack": "pack.hip"}
+             "pool": "post.hip", "token_proj": "prep.hip", "pack": "pack.hip",
+             "vt": "slot.hip", "masks": "prep.hip"}
     h = hashlib.sha256()
     for f in (files.get(kernel, ""), "common.hpp"):
         p = os.path.join(ROOT, "windowed_atom_attention_amd", "csrc", f)
@@ -84,6 +85,94 @@ def _traffic(kernel, workload):
     if not rec or rec.get("source_sha") != _source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+# Kernel symbols of libatomattn, as they appear in a rocprofv3 trace, and the
+# names the library's own profiler gives them.
+KERNEL_SYMBOLS = {"k_slot": "slot_attention", "k_prep": "prep", "k_post": "post",
+                  "k_pool": "pool", "k_pack": "pack", "k_token_proj": "token_proj",
+                  "k_vt": "vt", "k_masks": "masks"}
+
+
+def kernel_of(symbol):
+    """Library kernel name of a trace symbol (demangled or mangled), else None."""
+    import re
+    m = re.search(r"k_(slot|prep|post|pool|pack|token_proj|vt|masks)(?![a-z_])", symbol)
+    return KERNEL_SYMBOLS["k_" + m.group(1)] if m else None
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(reps=5):
+    """A plain elementwise copy (y = -x, fp32) of COPY_PROBE_BYTES read and
+    the same written, the calibration kernel for the HBM byte counters."""
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    x = torch.ones(n, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": "neg", "bytes_read": COPY_PROBE_BYTES,
+                      "bytes_written": COPY_PROBE_BYTES, "launches": reps}))
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no counter_collection.csv under %s" % directory)
+    return rows
+
+
+def _per_dispatch(rows, counter, select):
+    """Mean over dispatches of `counter` (summed over its dimensions within
+    a dispatch) for the rows whose kernel name `select` maps to a key."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = select(r.get("Kernel_Name", ""))
+        if key is None:
+            continue
+        did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per.setdefault(key, {}).setdefault(did, 0.0)
+        per[key][did] += float(r["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """profiles/traffic.json entries from four rocprofv3 --pmc runs: FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch) over a bench run of `workload` and over
+    the copy probe. Each counter is scaled by known bytes / what it reads for
+    the copy probe."""
+    neg = lambda name: "neg" if "neg" in name else None
+    cf, _ = _per_dispatch(_counter_rows(copy_fetch_dir), "FETCH_SIZE", neg)["neg"]
+    cw, _ = _per_dispatch(_counter_rows(copy_write_dir), "WRITE_SIZE", neg)["neg"]
+    f_read = COPY_PROBE_BYTES / (cf * 1024.0)
+    f_write = COPY_PROBE_BYTES / (cw * 1024.0)
+    fetch = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE", kernel_of)
+    write = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE", kernel_of)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    for k in sorted(set(fetch) & set(write)):
+        rd = fetch[k][0] * 1024.0 * f_read
+        wr = write[k][0] * 1024.0 * f_write
+        db["%s@%s" % (k, workload)] = {
+            "bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+            "fetch_kib_raw": fetch[k][0], "write_kib_raw": write[k][0],
+            "dispatches": [fetch[k][1], write[k][1]],
+            "copy_scale": {"fetch": f_read, "write": f_write},
+            "source_sha": _source_sha(k)}
+    with open(path, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+    print(json.dumps({k: v["bytes_per_launch"] for k, v in db.items()}))
 
 
 def cpu_baseline(name, seconds=12.0):
@@ -135,12 +224,25 @@ def main():
     ap.add_argument("--cache-bytes", type=float, default=768e6,
                     help="input copies are added until they exceed this")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only the counter-calibration copy kernel")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic.json entries for --config from "
+                         "rocprofv3 --pmc output directories (no GPU work)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.config, *args.traffic_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
     from windowed_atom_attention_amd import (profile_enable, profile_read,
