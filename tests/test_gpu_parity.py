@@ -43,6 +43,13 @@ SMALL = [
     ("0", dict(A=600)),
     ("0", dict(A=450, K=40, style="esmfold2", dtype=torch.bfloat16)),
     ("0", dict(A=300, K=200, dtype=torch.bfloat16, stage="decoder")),
+    # every pair-row width the slot kernel specialises on (AF3 bf16: 8, 16,
+    # 24, 32 channels; fp32: 8, 16), and wider heads
+    ("0", dict(A=200, V=24, K=64, dtype=torch.bfloat16)),
+    ("0", dict(A=200, V=32, dtype=torch.bfloat16, K=40)),
+    ("0", dict(A=150, V=16, H=4, D=64)),
+    ("0", dict(A=150, H=2, D=128, V=16, dtype=torch.bfloat16, stage="decoder")),
+    ("0", dict(A=200, K=48, style="esmfold2", H=8, D=16)),
 ]
 
 

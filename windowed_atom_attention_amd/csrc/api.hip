@@ -38,7 +38,9 @@ hipEvent_t prof_event() {
         return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess)
+    // timing-only events: no system-scope fence (no cache writeback and
+    // invalidate between the kernels they bracket)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
         return nullptr;
     return e;
 }

@@ -34,23 +34,27 @@ __device__ __forceinline__ float to_f(bf16_t x) {
 
 template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even (NaN stays NaN): the gfx950
+// conversion instruction (v_cvt_pk_bf16_f32).
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+    return __builtin_bit_cast(bf16_t, (__bf16)x);
+}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 values -> two bf16 packed in one word (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Logistic function in two branches so that a very negative argument gives
-// exp(z)/(1+exp(z)) -- down to the subnormal range -- instead of 1/inf.
-// expf/division are the IEEE library versions (no fast-math, no FTZ).
+// Logistic function from e = exp(-|z|) in (0, 1]: 1/(1+e) for z >= 0 and
+// e/(1+e) below, so a very negative argument keeps its tiny (down to
+// subnormal) value instead of 1 - 1. exp2f keeps subnormal results (the
+// compiler range-scales them); the reciprocal is the hardware one (1 ulp).
 __device__ __forceinline__ float sigmoid_f(float z) {
-    if (z >= 0.0f)
-        return 1.0f / (1.0f + expf(-z));
-    float e = expf(z);
-    return e / (1.0f + e);
+    const float e = exp2f(-fabsf(z) * 1.4426950408889634f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
+    return z >= 0.0f ? r : e * r;
 }
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 

@@ -60,6 +60,10 @@ struct SlotArgs {
     const int64_t *key_index;
     const void *q, *k, *v, *pair, *pair_scale, *w_pair;
     void *attention, *o;
+    // key_index / window_mask rows may be read as 16-byte vectors: K is a
+    // multiple of the slots per thread and both bases are 16-byte aligned
+    // (set by the launcher)
+    int vec_rows;
 };
 
 // One matrix to pack: src[r*ld + c] for r < kd, c < n (storage dtype).

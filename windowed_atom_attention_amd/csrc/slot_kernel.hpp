@@ -1,0 +1,608 @@
+// slot_kernel.hpp -- masked slot attention, one block of 16 query atoms per
+// workgroup (4 waves, 16 threads per query). Included by the translation
+// units that instantiate it (slot_af3_f32.hip, slot_af3_bf16.hip,
+// slot_esm.hip); the launcher lives in slot.hip.
+//
+// What it computes ("windowed_atom_attention", Required behavior; the AF3
+// and ESMFold2 encoder pages): a slot (a, k) with key id j is allowed iff
+// 0 <= j < A, atoms a and j are usable, window_mask[a, k], and |j - a| <=
+// radius when radius >= 0. Logits are Q[a].K[j]/sqrt(D) plus, for AF3, the
+// per-head pair bias (LN(pair[a, k]) * pair_scale) @ w_pair. A softmax over
+// the allowed slots of the row (every slot its own term, repeats included)
+// gives attention[b, h, a, k]; a row without allowed slots is exactly zero.
+// o[a, h] = sum_k w_k V[j_k, h].
+//
+// How:
+//  * Each thread owns SPL consecutive slots of one query. It loads their key
+//    ids and window bits (16-byte vectors where rows allow), gathers the key
+//    usability of the slots that can be allowed and, for a usable query,
+//    the pair rows of all its slots. The pair bias of every slot and head is
+//    formed in registers from one pass over the row: with d = x - x[0]
+//    (shifted data keeps the variance well conditioned),
+//      LN(x) . w_h = rstd * (sum_v d_v w_vh - mean(d) * sum_v w_vh),
+//      rstd = 1 / sqrt(mean(d^2) - mean(d)^2 + eps).
+//    Bias values of slots that are not allowed are never used, so a NaN
+//    payload in such a row never reaches an output.
+//  * The 16 queries of a block see a narrow band [jlo, jhi] of key ids (the
+//    supplied windows are local). Each wave takes one head: it computes the
+//    dense 16 x band score tile Q K^T on MFMA with both operands read from
+//    L2 straight into registers (Q and K are fp32: they set the logits) and
+//    leaves it in LDS. Every thread reads its slots' logits out of the tiles
+//    by key id and does the softmax in registers. The same LDS then holds
+//    the dense 16 x band probability tiles: zeroed, filled with each slot's
+//    weight by key id (a repeated id in a row adds up), and multiplied by V
+//    on MFMA per head, V read from the transposed copy the prep kernel
+//    writes so that a lane's operand is 16 contiguous bytes.
+//  * A band wider than 128 rows is processed in chunks (any key_index is
+//    correct; the windowed layouts need a single chunk).
+#pragma once
+
+#include <climits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace waa {
+
+constexpr int kQB = 16;     // queries per workgroup
+constexpr int kRMAX = 128;  // key rows per chunk of the band
+constexpr int kHG = 4;      // heads per pass (one per wave)
+
+struct SlotLayout {
+    int sp;
+    size_t o_wpr, o_wsum, o_t, o_tag, total;
+};
+
+__host__ __device__ inline size_t sal16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// LDS: AF3 pair weights pair_scale * w_pair as [V][4] (heads padded to 4)
+// and their column sums; the score / probability tiles [4][16][sp] fp32;
+// the writer tag of each probability cell [16][128].
+__host__ __device__ inline SlotLayout slot_layout(int H, int V, int style) {
+    (void)H;
+    SlotLayout L;
+    L.sp = kRMAX + 4;
+    size_t o = 0;
+    L.o_wpr = o;
+    L.o_wsum = o;
+    if (style == STYLE_AF3) {
+        o = sal16(o + (size_t)V * kHG * 4);
+        L.o_wsum = o;
+        o = sal16(o + kHG * 4);
+    }
+    L.o_t = o; o = sal16(o + (size_t)kHG * kQB * L.sp * 4);
+    L.o_tag = o; o = sal16(o + (size_t)kQB * kRMAX * 4);
+    L.total = o;
+    return L;
+}
+
+__host__ __device__ inline int slot_spl(int K) { return K <= 16 ? 1 : (K <= 128 ? 8 : 16); }
+
+template <typename T>
+__device__ __forceinline__ void unpack16(uint4 v, float *out) {
+    if constexpr (sizeof(T) == 4) {
+        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
+// P operand (probabilities, fp32 in LDS) as a 16-byte chunk of T.
+template <typename T>
+__device__ __forceinline__ uint4 p_chunk(const float *src);
+template <> __device__ __forceinline__ uint4 p_chunk<float>(const float *src) {
+    return *reinterpret_cast<const uint4 *>(src);
+}
+template <> __device__ __forceinline__ uint4 p_chunk<bf16_t>(const float *src) {
+    const float4 lo = *reinterpret_cast<const float4 *>(src);
+    const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+    return make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                      pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+}
+
+// 16 bytes of the transposed V row `src` starting at key row r (of A rows):
+// one vector load when all its rows exist, else row by row with zeros past
+// the batch's last atom (the pitch padding is never read).
+template <typename T>
+__device__ __forceinline__ uint4 vt_chunk(const T *src, int r, int A) {
+    constexpr int E = 16 / sizeof(T);
+    if (r + E <= A)
+        return *reinterpret_cast<const uint4 *>(src + r);
+    T tmp[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        tmp[e] = r + e < A ? src[r + e] : (T)0;
+    uint4 v;
+    __builtin_memcpy(&v, tmp, 16);
+    return v;
+}
+
+// NV: 16-byte vectors per AF3 pair row (V = NV * 16 / sizeof(T)); 1 for
+// ESMFold2, which has no pair input.
+template <typename T, int STYLE, int SPL, int DK, int NV>
+__global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_lo, s_hi;
+    constexpr int KC = Mma16<T>::KC, QU = Mma16<T>::QUARTER;
+    constexpr int E = 16 / sizeof(T);
+    constexpr int VV = NV * E;                       // AF3 pair channels
+    constexpr int NKQ = DK / 16;                     // fp32 k chunks of Q.K
+    constexpr int NDB = DK / 16;                     // 16-wide output blocks of o
+    constexpr int CBG = DK <= 32 ? 4 : (DK == 64 ? 2 : 1); // score blocks per load batch
+    const int A = p.A, K = p.K, H = p.H, HD = H * DK;
+    const int nqb = (A + kQB - 1) / kQB;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = wg / nqb, a0 = (wg % nqb) * kQB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = tid >> 4, j16 = tid & 15;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int a = a0 + q;
+    const bool qin = a < A;
+    const int64_t bA = (int64_t)b * A;
+    const int64_t nrow = bA + (qin ? a : 0);
+    const int k0 = j16 * SPL;
+    const SlotLayout L = slot_layout(H, VV, STYLE);
+    float *wpr = reinterpret_cast<float *>(smem + L.o_wpr);
+    float *wsum = reinterpret_cast<float *>(smem + L.o_wsum);
+    float *tile = reinterpret_cast<float *>(smem + L.o_t);
+    const float *qg = reinterpret_cast<const float *>(p.q); // fp32 logit operands
+    const float *kg = reinterpret_cast<const float *>(p.k);
+    const T *vtg = reinterpret_cast<const T *>(p.v);        // [B][HD][vt_pitch(A)]
+    const int vtp = vt_pitch(A);
+    T *att = reinterpret_cast<T *>(p.attention);
+    T *og = reinterpret_cast<T *>(p.o);
+
+    // ---- key ids and window bits of this thread's slots
+    const bool full = qin && k0 + SPL <= K; // every slot of the thread exists
+    int64_t kid[SPL];
+    bool wmv[SPL];
+    if (SPL >= 8 && p.vec_rows && full) {
+        const int64_t off = nrow * K + k0;
+#pragma unroll
+        for (int i = 0; i + 2 <= SPL; i += 2) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(p.key_index + off + i);
+            kid[i] = (int64_t)(((uint64_t)v.y << 32) | v.x);
+            kid[i + 1] = (int64_t)(((uint64_t)v.w << 32) | v.z);
+        }
+        uint32_t wb[SPL / 4 > 0 ? SPL / 4 : 1] = {};
+        if constexpr (SPL == 8) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(p.window_mask + off);
+            wb[0] = w.x;
+            wb[1] = w.y;
+        } else if constexpr (SPL == 16) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(p.window_mask + off);
+            wb[0] = w.x; wb[1] = w.y; wb[2] = w.z; wb[3] = w.w;
+        }
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            wmv[i] = ((wb[i / 4] >> (8 * (i % 4))) & 0xffu) != 0;
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            const int k = k0 + i;
+            kid[i] = -1;
+            wmv[i] = false;
+            if (qin && k < K) {
+                kid[i] = p.key_index[nrow * K + k];
+                wmv[i] = p.window_mask[nrow * K + k] != 0;
+            }
+        }
+    }
+    const bool qok = qin && p.usable[nrow];
+    if (tid == 0) {
+        s_lo = INT_MAX;
+        s_hi = -1;
+    }
+    if (STYLE == STYLE_AF3) {
+        const T *ps = reinterpret_cast<const T *>(p.pair_scale);
+        const T *wp = reinterpret_cast<const T *>(p.w_pair);
+        for (int i = tid; i < VV * kHG; i += 256) {
+            const int v = i / kHG, h = i % kHG;
+            wpr[i] = h < H ? to_f(ps[v]) * to_f(wp[v * H + h]) : 0.0f;
+        }
+        if (tid < kHG) {
+            float s = 0.0f;
+            for (int v = 0; v < VV; ++v)
+                s += tid < H ? to_f(ps[v]) * to_f(wp[v * H + tid]) : 0.0f;
+            wsum[tid] = s;
+        }
+    }
+    bool cand[SPL];
+    uint8_t uj[SPL];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int64_t j = kid[i];
+        const int64_t dist = j > a ? j - a : a - j;
+        cand[i] = qok && wmv[i] && j >= 0 && j < A && (p.radius < 0 || dist <= p.radius);
+        uj[i] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+        if (cand[i])
+            uj[i] = p.usable[bA + kid[i]];
+
+    // ---- AF3 pair bias per slot and head (H <= 4), in registers
+    float beta[SPL][kHG];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int h = 0; h < kHG; ++h)
+            beta[i][h] = 0.0f;
+    __syncthreads(); // wpr, wsum, s_lo/s_hi initialised
+    const int nsl = full ? SPL : K - k0; // slots of this thread that exist
+    if (STYLE == STYLE_AF3 && qok && nsl > 0) {
+        const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + k0) * VV;
+        const float4 *w4p = reinterpret_cast<const float4 *>(wpr);
+        const float4 ws = *reinterpret_cast<const float4 *>(wsum);
+        constexpr float kInvV = 1.0f / (float)VV;
+        // slots per group: their rows are in flight together and one
+        // broadcast weight read serves them all
+        constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : 2);
+#pragma unroll
+        for (int g0 = 0; g0 < SPL; g0 += GS) {
+            uint4 pb[GS][NV];
+            // rows past the end of a ragged key list re-read the last row
+            // (unconditional loads; their bias is never used)
+#pragma unroll
+            for (int ii = 0; ii < GS; ++ii) {
+                const T *src = prow + min(g0 + ii, nsl - 1) * VV;
+#pragma unroll
+                for (int pt = 0; pt < NV; ++pt)
+                    pb[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
+            }
+            float x0[GS], sd[GS], sq[GS], bb[GS][kHG];
+#pragma unroll
+            for (int ii = 0; ii < GS; ++ii) {
+                float t[E];
+                unpack16<T>(pb[ii][0], t);
+                x0[ii] = t[0];
+                sd[ii] = sq[ii] = 0.0f;
+#pragma unroll
+                for (int h = 0; h < kHG; ++h)
+                    bb[ii][h] = 0.0f;
+            }
+#pragma unroll
+            for (int pt = 0; pt < NV; ++pt) {
+                float xv[GS][E];
+#pragma unroll
+                for (int ii = 0; ii < GS; ++ii)
+                    unpack16<T>(pb[ii][pt], xv[ii]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float4 w4 = w4p[pt * E + e]; // one broadcast read, all heads
+#pragma unroll
+                    for (int ii = 0; ii < GS; ++ii) {
+                        const float dv = xv[ii][e] - x0[ii];
+                        sd[ii] += dv;
+                        sq[ii] = fmaf(dv, dv, sq[ii]);
+                        bb[ii][0] = fmaf(dv, w4.x, bb[ii][0]);
+                        bb[ii][1] = fmaf(dv, w4.y, bb[ii][1]);
+                        bb[ii][2] = fmaf(dv, w4.z, bb[ii][2]);
+                        bb[ii][3] = fmaf(dv, w4.w, bb[ii][3]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < GS; ++ii) {
+                const float md = sd[ii] * kInvV;
+                const float var = fmaxf(fmaf(sq[ii], kInvV, -md * md), 0.0f);
+                const float rstd = rsqrtf(var + p.eps);
+                beta[g0 + ii][0] = (bb[ii][0] - md * ws.x) * rstd;
+                beta[g0 + ii][1] = (bb[ii][1] - md * ws.y) * rstd;
+                beta[g0 + ii][2] = (bb[ii][2] - md * ws.z) * rstd;
+                beta[g0 + ii][3] = (bb[ii][3] - md * ws.w) * rstd;
+            }
+            // keep the next group's loads from being hoisted above this
+            // group's arithmetic (registers: one group in flight)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    int rel[SPL];
+    int lo = INT_MAX, hi = -1;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        rel[i] = (cand[i] && uj[i]) ? (int)kid[i] : -1;
+        if (rel[i] >= 0) {
+            lo = min(lo, rel[i]);
+            hi = max(hi, rel[i]);
+        }
+    }
+    lo = wave_min_i(lo);
+    hi = wave_max_i(hi);
+    if (lane == 0) {
+        atomicMin(&s_lo, lo);
+        atomicMax(&s_hi, hi);
+    }
+    __syncthreads();
+    const int jhi = s_hi;
+
+    // whole-vector attention stores when rows and slot groups are 16-byte
+    // multiples (attention rows then start 16-byte aligned)
+    constexpr bool kVecAtt = (SPL * (int)sizeof(T)) % 16 == 0;
+    const bool vec_att = kVecAtt && (K % SPL) == 0 && ((uintptr_t)att & 15) == 0;
+    auto store_att = [&](int h, const float *w) {
+        if (!qin || k0 >= K) // K % SPL == 0 on the vector path: k0 < K means k0 + SPL <= K
+            return;
+        T *arow = att + (((int64_t)b * H + h) * A + a) * K;
+        if (kVecAtt && vec_att) {
+#pragma unroll
+            for (int i = 0; i + E <= SPL; i += E) {
+                uint4 v4;
+                if constexpr (sizeof(T) == 2) {
+                    v4 = make_uint4(pack_bf16x2(w[i], w[i + 1]), pack_bf16x2(w[i + 2], w[i + 3]),
+                                    pack_bf16x2(w[i + 4], w[i + 5]), pack_bf16x2(w[i + 6], w[i + 7]));
+                } else {
+                    v4 = make_uint4(__float_as_uint(w[i]), __float_as_uint(w[i + 1]),
+                                    __float_as_uint(w[i + 2]), __float_as_uint(w[i + 3]));
+                }
+                *reinterpret_cast<uint4 *>(arow + k0 + i) = v4;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < SPL; ++i)
+                if (k0 + i < K)
+                    arow[k0 + i] = from_f<T>(w[i]);
+        }
+    };
+
+    if (jhi < 0) {
+        // no allowed slot anywhere in the block: all-zero rows
+        float zw[SPL];
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            zw[i] = 0.0f;
+        for (int h = 0; h < H; ++h)
+            store_att(h, zw);
+        if (qin)
+            for (int c = j16; c < HD; c += 16)
+                og[nrow * HD + c] = from_f<T>(0.0f);
+        return;
+    }
+
+    const int jal = s_lo & ~7; // band start, aligned for the transposed V rows
+    const int span = jhi + 1 - jal;
+    const int nch = (span + kRMAX - 1) / kRMAX;
+    const float scale = p.inv_sqrt_d;
+    float *twave = tile + wave * kQB * L.sp; // this wave's head tile
+    // Unique writer of each probability cell (query, key row): every
+    // allowed slot writes its slot index into the tag tile and the one
+    // whose index survives writes the cell with a plain store; the others
+    // (repeated key ids in a row) add their weights with LDS atomics after
+    // a barrier. A wide band (several chunks) adds every weight atomically.
+    int *tag = reinterpret_cast<int *>(smem + L.o_tag);
+    bool win[SPL];
+    int lose_any = 0;
+    if (nch == 1) {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            if (rel[i] >= 0)
+                tag[q * kRMAX + rel[i] - jal] = k0 + i;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            win[i] = rel[i] >= 0 && tag[q * kRMAX + rel[i] - jal] == k0 + i;
+            lose_any |= (rel[i] >= 0 && !win[i]) ? 1 : 0;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            win[i] = false;
+        lose_any = 1;
+    }
+    lose_any = __syncthreads_or(lose_any);
+
+    for (int hg = 0; hg < H; hg += kHG) {
+        const int hw = hg + wave; // this wave's head in the S and P V products
+        const bool hv = hw < H;
+        // Q fragments (A operand of S): query row l16, fp32
+        uint4 qf[NKQ];
+        {
+            const int aq = a0 + l16;
+#pragma unroll
+            for (int kc = 0; kc < NKQ; ++kc) {
+                qf[kc] = make_uint4(0, 0, 0, 0);
+                if (hv && aq < A)
+                    qf[kc] = *reinterpret_cast<const uint4 *>(qg + (bA + aq) * HD + hw * DK + kc * 16 + g * 4);
+            }
+        }
+        // lg: the pair bias until a slot's logit is added to it (each slot
+        // lies in exactly one chunk), then the logit, then the weight
+        float (&lg)[SPL][kHG] = beta;
+        if (hg > 0) { // only ESMFold2 has more than 4 heads, and no pair bias
+#pragma unroll
+            for (int i = 0; i < SPL; ++i)
+#pragma unroll
+                for (int hh = 0; hh < kHG; ++hh)
+                    lg[i][hh] = 0.0f;
+        }
+
+        for (int c = 0; c < nch; ++c) {
+            const int c0 = jal + c * kRMAX;
+            const int rows = min(kRMAX, jhi + 1 - c0);
+            const int ncb = (rows + 15) / 16;
+            if (hv) {
+                for (int cb0 = 0; cb0 < ncb; cb0 += CBG) {
+                    f32x4_t acc[CBG];
+                    uint4 kb[CBG][NKQ];
+#pragma unroll
+                    for (int t = 0; t < CBG; ++t) {
+                        acc[t] = zero4();
+                        const int r = (cb0 + t) * 16 + l16;
+#pragma unroll
+                        for (int kc = 0; kc < NKQ; ++kc) {
+                            kb[t][kc] = make_uint4(0, 0, 0, 0);
+                            if (r < rows)
+                                kb[t][kc] = *reinterpret_cast<const uint4 *>(
+                                    kg + (bA + c0 + r) * HD + hw * DK + kc * 16 + g * 4);
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < CBG; ++t)
+#pragma unroll
+                        for (int kc = 0; kc < NKQ; ++kc)
+                            Mma16<float>::mma(acc[t], qf[kc], kb[t][kc]);
+#pragma unroll
+                    for (int t = 0; t < CBG; ++t)
+                        if (cb0 + t < ncb)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                twave[acc16_row(v, lane) * L.sp + (cb0 + t) * 16 + acc16_col(lane)] = acc[t][v];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int hh = 0; hh < kHG; ++hh) {
+                if (hg + hh >= H)
+                    break;
+                const float *sh = tile + (hh * kQB + q) * L.sp;
+#pragma unroll
+                for (int i = 0; i < SPL; ++i) {
+                    const int r = rel[i] - c0;
+                    if (rel[i] >= 0 && r >= 0 && r < rows)
+                        lg[i][hh] = fmaf(sh[r], scale, lg[i][hh]);
+                }
+            }
+            __syncthreads(); // score tiles read; the next chunk or P may reuse them
+        }
+        // the tiles become the (zeroed) probability tiles
+        for (int i = tid; i < kHG * kQB * L.sp / 4; i += 256)
+            reinterpret_cast<float4 *>(tile)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+        // masked softmax per head over the row: 16 lanes per query
+#pragma unroll
+        for (int hh = 0; hh < kHG; ++hh) {
+            if (hg + hh >= H)
+                break;
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i)
+                if (rel[i] >= 0)
+                    m = fmaxf(m, lg[i][hh]);
+            m = max16(m);
+            float w[SPL];
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+                w[i] = rel[i] >= 0 ? __expf(lg[i][hh] - m) : 0.0f;
+                sum += w[i];
+            }
+            sum = sum16(sum);
+            const float inv = sum > 0.0f ? __builtin_amdgcn_rcpf(sum) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+                w[i] *= inv;
+                lg[i][hh] = w[i];
+            }
+            store_att(hg + hh, w);
+        }
+        __syncthreads(); // probability tiles zero
+
+        // o = P V per head; P scattered by key id (repeats add up)
+        f32x4_t oacc[NDB];
+#pragma unroll
+        for (int t = 0; t < NDB; ++t)
+            oacc[t] = zero4();
+        for (int c = 0; c < nch; ++c) {
+            const int c0 = jal + c * kRMAX;
+            const int rows = min(kRMAX, jhi + 1 - c0);
+            const int rpad = (rows + 31) / 32 * 32;
+#pragma unroll
+            for (int hh = 0; hh < kHG; ++hh) {
+                if (hg + hh >= H)
+                    break;
+                float *ph = tile + (hh * kQB + q) * L.sp;
+#pragma unroll
+                for (int i = 0; i < SPL; ++i) {
+                    const int r = rel[i] - c0;
+                    if (win[i])
+                        ph[r] = lg[i][hh];
+                }
+            }
+            if (lose_any) {
+                __syncthreads();
+#pragma unroll
+                for (int hh = 0; hh < kHG; ++hh) {
+                    if (hg + hh >= H)
+                        break;
+                    float *ph = tile + (hh * kQB + q) * L.sp;
+#pragma unroll
+                    for (int i = 0; i < SPL; ++i) {
+                        const int r = rel[i] - c0;
+                        if (rel[i] >= 0 && !win[i] && r >= 0 && r < rows)
+                            atomicAdd(&ph[r], lg[i][hh]);
+                    }
+                }
+            }
+            __syncthreads();
+            if (hv) {
+                const float *prow = twave + l16 * L.sp + g * QU;
+                const T *vrow = vtg + ((int64_t)b * HD + hw * DK) * vtp;
+                for (int kc = 0; kc < rpad / KC; ++kc) {
+                    const uint4 av = p_chunk<T>(prow + kc * KC);
+                    const int r = c0 + kc * KC + g * QU;
+#pragma unroll
+                    for (int t = 0; t < NDB; ++t) {
+                        const uint4 bv = vt_chunk<T>(vrow + (int64_t)(t * 16 + l16) * vtp, r, A);
+                        Mma16<T>::mma(oacc[t], av, bv);
+                    }
+                }
+                // leave this wave's P tile zero for the next chunk / head group
+                for (int i = lane; i < kQB * L.sp / 4; i += 64)
+                    reinterpret_cast<float4 *>(twave)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            __syncthreads();
+        }
+        if (hv) {
+#pragma unroll
+            for (int t = 0; t < NDB; ++t) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int aq = a0 + acc16_row(v, lane);
+                    if (aq < A)
+                        og[(bA + aq) * HD + hw * DK + t * 16 + acc16_col(lane)] = from_f<T>(oacc[t][v]);
+                }
+            }
+        }
+    }
+}
+
+// Kernel of one style/dtype family for the given slots-per-thread, head
+// width and pair vectors per row (defined in the instantiating units).
+const void *pick_slot_af3_f32(int spl, int D, int nv);
+const void *pick_slot_af3_bf16(int spl, int D, int nv);
+const void *pick_slot_esm(int dtype, int spl, int D);
+
+template <typename T, int STYLE, int NV>
+const void *pick_slot_sd(int spl, int D) {
+    switch (spl) {
+    case 1:
+        switch (D) {
+        case 16: return (const void *)k_slot<T, STYLE, 1, 16, NV>;
+        case 32: return (const void *)k_slot<T, STYLE, 1, 32, NV>;
+        case 64: return (const void *)k_slot<T, STYLE, 1, 64, NV>;
+        default: return (const void *)k_slot<T, STYLE, 1, 128, NV>;
+        }
+    case 8:
+        switch (D) {
+        case 16: return (const void *)k_slot<T, STYLE, 8, 16, NV>;
+        case 32: return (const void *)k_slot<T, STYLE, 8, 32, NV>;
+        case 64: return (const void *)k_slot<T, STYLE, 8, 64, NV>;
+        default: return (const void *)k_slot<T, STYLE, 8, 128, NV>;
+        }
+    default:
+        switch (D) {
+        case 16: return (const void *)k_slot<T, STYLE, 16, 16, NV>;
+        case 32: return (const void *)k_slot<T, STYLE, 16, 32, NV>;
+        case 64: return (const void *)k_slot<T, STYLE, 16, 64, NV>;
+        default: return (const void *)k_slot<T, STYLE, 16, 128, NV>;
+        }
+    }
+}
+
+} // namespace waa

@@ -154,10 +154,16 @@ def make_workload(name: str, seed: Optional[int] = None, A: Optional[int] = None
                   B: Optional[int] = None, T: Optional[int] = None,
                   K: Optional[int] = None, dtype: Optional[torch.dtype] = None,
                   style: Optional[str] = None, stage: Optional[str] = None,
-                  radius: Optional[int] = None, eps: float = 1e-5) -> Workload:
+                  radius: Optional[int] = None, eps: float = 1e-5,
+                  **widths: int) -> Workload:
     """Draw the named workload (optionally resized: A/B/T/K overrides keep the
-    recipe, so a small instance spans a few tiles and a ragged tail)."""
+    recipe, so a small instance spans a few tiles and a ragged tail; `widths`
+    may override C, S, V, H, D, M, U)."""
     r = dict(CONFIGS[name])
+    for k, v in widths.items():
+        if k not in ("C", "S", "V", "H", "D", "M", "U"):
+            raise TypeError("unknown width %r" % k)
+        r[k] = int(v)
     if A is not None:
         r["A"] = A
         if T is None:
