@@ -169,73 +169,38 @@ __device__ __forceinline__ int acc16_col(int lane) { return lane & 15; }
 // data, so that the 32 rows of an operand tile start in different LDS banks.
 template <typename T> constexpr int pad16() { return 16 / (int)sizeof(T); }
 
-// acc += A[32 x Kd] * B[Kd x 32-column block].
-// A: LDS tile, row-major, pitch lda elements (16-byte aligned rows).
-// B: packed weight block (see pack.hip): chunk kc of this column block at
-//    Bp[kc*64 + lane], 16 bytes per lane.
-template <typename T>
-__device__ __forceinline__ void gemm32(f32x16_t &acc, const T *A, int lda,
-                                       int nkc, const uint4 *__restrict__ Bp) {
-    const int lane = threadIdx.x & 63;
-    const T *arow = A + (lane & 31) * lda + (lane >> 5) * Mma32<T>::HALF;
-#pragma unroll 4
-    for (int kc = 0; kc < nkc; ++kc) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * Mma32<T>::KC);
-        const uint4 b = Bp[kc * 64 + lane];
-        Mma32<T>::mma(acc, a, b);
-    }
-}
-
-// Same product with the A operand given as an unevaluated sum hi + lo of
-// two tiles in the storage type ("split" operand): for bf16 this keeps ~16
-// mantissa bits of an fp32 activation at twice the MFMA work; B (the
-// weights) is exact in its storage type. Alo == nullptr means no lo part.
-template <typename T>
-__device__ __forceinline__ void gemm32s(f32x16_t &acc, const T *Ahi, const T *Alo,
-                                        int lda, int nkc, const uint4 *__restrict__ Bp) {
-    if (Alo == nullptr) {
-        gemm32<T>(acc, Ahi, lda, nkc, Bp);
-        return;
-    }
-    const int lane = threadIdx.x & 63;
-    const int off = (lane & 31) * lda + (lane >> 5) * Mma32<T>::HALF;
-#pragma unroll 2
-    for (int kc = 0; kc < nkc; ++kc) {
-        const uint4 b = Bp[kc * 64 + lane];
-        const uint4 ah = *reinterpret_cast<const uint4 *>(Ahi + off + kc * Mma32<T>::KC);
-        const uint4 al = *reinterpret_cast<const uint4 *>(Alo + off + kc * Mma32<T>::KC);
-        Mma32<T>::mma(acc, ah, b);
-        Mma32<T>::mma(acc, al, b);
-    }
-}
-
 // Two products at once, acc1 += A1 @ B1 and acc2 += A2 @ B2, over nk1 and
-// nk2 16-byte k-chunks (nk2 = 0 for a single product). A tiles come from LDS
-// (optionally split into hi + lo parts, see gemm32s), B from the packed
-// weights in L2. The B chunks of both products are fetched eight at a time
-// before any of them is used, so a batch costs one L2 round trip instead of
-// one per chunk.
+// nk2 16-byte k-chunks (nk2 = 0 for a single product).
+// A: LDS tiles, row-major, pitch lda elements (16-byte aligned rows),
+//    optionally given as an unevaluated sum hi + lo of two tiles in the
+//    storage type ("split" operand: for bf16 it keeps ~16 mantissa bits of
+//    an fp32 activation at twice the MFMA work); Alo == nullptr means none.
+// B: packed weight blocks (see pack.hip): chunk kc of the column block at
+//    B[kc*64 + lane], 16 bytes per lane, read from L2.
+// The B chunks are software-pipelined in batches of four per product: the
+// next batch is in flight while the MFMAs of the current one run.
 template <typename T>
 __device__ __forceinline__ void gemm_dual(f32x16_t &acc1, const T *A1, const T *A1lo,
                                           int lda1, int nk1, const uint4 *__restrict__ B1,
                                           f32x16_t &acc2, const T *A2, const T *A2lo,
                                           int lda2, int nk2, const uint4 *__restrict__ B2) {
-    constexpr int KC = Mma32<T>::KC;
+    constexpr int KC = Mma32<T>::KC, NB = 4;
     const int lane = threadIdx.x & 63;
     const int o1 = (lane & 31) * lda1 + (lane >> 5) * Mma32<T>::HALF;
     const int o2 = (lane & 31) * lda2 + (lane >> 5) * Mma32<T>::HALF;
     const int nk = nk1 > nk2 ? nk1 : nk2;
-    for (int kb = 0; kb < nk; kb += 8) {
-        uint4 b1[8], b2[8];
+    auto fetch = [&](uint4 (&b1)[NB], uint4 (&b2)[NB], int kb) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NB; ++j) {
             if (kb + j < nk1)
                 b1[j] = B1[(kb + j) * 64 + lane];
             if (kb + j < nk2)
                 b2[j] = B2[(kb + j) * 64 + lane];
         }
+    };
+    auto compute = [&](const uint4 (&b1)[NB], const uint4 (&b2)[NB], int kb) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NB; ++j) {
             if (kb + j < nk1) {
                 Mma32<T>::mma(acc1, *reinterpret_cast<const uint4 *>(A1 + o1 + (kb + j) * KC), b1[j]);
                 if (A1lo != nullptr)
@@ -247,6 +212,18 @@ __device__ __forceinline__ void gemm_dual(f32x16_t &acc1, const T *A1, const T *
                     Mma32<T>::mma(acc2, *reinterpret_cast<const uint4 *>(A2lo + o2 + (kb + j) * KC), b2[j]);
             }
         }
+    };
+    uint4 ba1[NB], ba2[NB], bb1[NB], bb2[NB];
+    fetch(ba1, ba2, 0);
+    for (int kb = 0; kb < nk; kb += 2 * NB) {
+        if (kb + NB < nk)
+            fetch(bb1, bb2, kb + NB);
+        compute(ba1, ba2, kb);
+        if (kb + NB >= nk)
+            break;
+        if (kb + 2 * NB < nk)
+            fetch(ba1, ba2, kb + 2 * NB);
+        compute(bb1, bb2, kb + NB);
     }
 }
 
