@@ -7,9 +7,10 @@ slot attention, post, [pool]) on one batch of synthetic input of the named
 workload. Inputs are resident in HBM before the timed region; to keep the
 256 MB Infinity Cache from serving them, the step cycles through enough
 copies of the inputs that they do not fit in it. The timed region is exactly
-K steps between two device synchronisations. Per-kernel durations come from
-HIP events the library records around each launch on the stream it launches
-on (profiling mode of libatomattn), over the same timed region.
+K steps between two device synchronisations and gives the throughput. A
+second timed region of the same K steps runs with the library's profiling
+mode on: HIP events recorded around each launch on the stream it launches
+on give every kernel's average duration (the roofline figures).
 
 Prints ONE JSON line: metric entries/s (B*A*H*K per second), plus
 atoms/s, the roofline of the dominant kernel and the fp64 oracle's rate on
@@ -224,6 +225,8 @@ def main():
     ap.add_argument("--cache-bytes", type=float, default=768e6,
                     help="input copies are added until they exceed this")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of HIP graphs that capture one step each")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the counter-calibration copy kernel")
     ap.add_argument("--traffic-summary", nargs=4,
@@ -265,26 +268,51 @@ def main():
     ws = torch.empty(workspace_bytes(d, w.style, w.stage, w.dtype), dtype=torch.uint8, device=dev)
     out = None
 
-    def step(i):
+    def eager(i):
         nonlocal out
         s = sets[i % len(sets)]
         out = windowed_atom_attention(**s.kwargs(), workspace=ws, out=out)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    profile_enable(True)
-    profile_read()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kt = profile_read()
-    profile_enable(False)
+    graphs = []
 
-    elapsed = t1 - t0
+    def step(i, instrumented=False):
+        if graphs and not instrumented:
+            graphs[i % len(graphs)].replay()
+        else:
+            eager(i)
+
+    def timed(instrumented):
+        if instrumented:
+            profile_enable(True)
+            profile_read()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, instrumented)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kt = profile_read() if instrumented else None
+        profile_enable(False)
+        return t1 - t0, kt
+
+    for i in range(args.warmup):
+        eager(i)
+    if args.graph:
+        # one captured step per input copy (the library makes no allocation,
+        # host synchronisation or memset inside a call)
+        torch.cuda.synchronize()
+        for s in sets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                windowed_atom_attention(**s.kwargs(), workspace=ws, out=out)
+            graphs.append(gr)
+        for i in range(len(graphs)):
+            step(i)
+    # the throughput comes from an uninstrumented timed region; the kernel
+    # durations from HIP events around every launch in a second timed region
+    # of the same steps (the events add a little time between kernels)
+    elapsed, _ = timed(False)
+    elapsed_ev, kt = timed(True)
     ms_step = elapsed * 1e3 / args.steps
     entries = w.entries
     value = entries * args.steps / elapsed
@@ -324,7 +352,8 @@ def main():
     line = {
         "metric": "atom-slot attention entries/sec (B*A*H*K) per block, 1xMI355X",
         "value": value, "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": ms_step,
+        "ms_per_step_instrumented": elapsed_ev * 1e3 / args.steps, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": "%s (config %s): B=%d A=%d T=%d K=%d C=%d S=%d H=%d D=%d "
                                "V=%d M=%d U=%d, %s, radius %d" % (

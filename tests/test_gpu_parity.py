@@ -19,7 +19,7 @@ import oracle
 from _parity import RTOL, assert_close, compare_block, exact_zero_checks, np64, run_gpu
 from windowed_atom_attention_amd import masks as gpu_masks
 from windowed_atom_attention_amd import slot_attention as gpu_slot_attention
-from windowed_atom_attention_amd import windowed_atom_attention
+from windowed_atom_attention_amd import windowed_atom_attention, workspace_bytes
 from windowed_atom_attention_amd.workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -276,3 +276,29 @@ def test_strided_inputs_are_not_mutated():
         assert torch.equal(v.nan_to_num(), before[k].nan_to_num()), k
     ref = oracle.block(**w.kwargs())
     assert_close("hidden", np64(out["hidden"]), ref["hidden"], RTOL[w.dtype])
+
+
+def test_graph_capture_replays_match_eager():
+    """One block call captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, rewrites the outputs bit for bit as
+    the eager call did (window slots without repeated key ids, whose weights
+    would be summed in a run-dependent order)."""
+    w = make_workload("1", A=700)
+    g = w.to("cuda")
+    ws = torch.empty(workspace_bytes(w.dims, w.style, w.stage, w.dtype),
+                     dtype=torch.uint8, device="cuda")
+    out = windowed_atom_attention(**g.kwargs(), workspace=ws)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        windowed_atom_attention(**g.kwargs(), workspace=ws, out=out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for v in out.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), k

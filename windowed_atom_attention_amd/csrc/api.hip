@@ -4,6 +4,8 @@
 // in the kernels of pack/prep/slot/post.hip.
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/atom_attn.h"
@@ -30,6 +32,22 @@ struct Profiler {
     int nnames = 7;
 };
 Profiler g_prof;
+
+} // namespace
+
+namespace waa {
+void allow_lds(const void *fn, size_t bytes) {
+    static std::mutex mu;
+    static std::unordered_map<const void *, size_t> limit;
+    std::lock_guard<std::mutex> lock(mu);
+    size_t &cur = limit[fn];
+    if (bytes > cur &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess)
+        cur = bytes;
+}
+} // namespace waa
+
+namespace {
 
 hipEvent_t prof_event() {
     if (!g_prof.pool.empty()) {

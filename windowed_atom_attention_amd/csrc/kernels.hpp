@@ -113,4 +113,8 @@ int slot_supported(const Dims &d, int dtype, int style);
 
 constexpr size_t kMaxLds = 160 * 1024;
 
+// Raise a kernel's dynamic-LDS limit to `bytes` if it is lower (the runtime
+// call is made only when a launch needs more than any launch before).
+void allow_lds(const void *fn, size_t bytes);
+
 } // namespace waa

@@ -372,7 +372,7 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
         else { if (stage == STAGE_ENCODER) WAA_PICK(bf16_t, 1, 0); else WAA_PICK(bf16_t, 1, 1); }
     }
 #undef WAA_PICK
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    allow_lds(fn, lds);
     void *args[] = {(void *)&a};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
     if (e != hipSuccess)
@@ -548,7 +548,7 @@ hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s) {
     const int grid = a.d.B * ntile;
     const size_t lds = pool_lds_bytes(a.d, dtype);
     const void *fn = dtype == 0 ? (const void *)k_pool<float> : (const void *)k_pool<bf16_t>;
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    allow_lds(fn, lds);
     void *args[] = {(void *)&a};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
     if (e != hipSuccess)

@@ -101,12 +101,10 @@ hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
     const int grid = (rows + 31) / 32;
     const size_t lds = token_proj_lds_bytes(a.d, dtype);
     if (dtype == 0) {
-        (void)hipFuncSetAttribute((const void *)k_token_proj<float>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        allow_lds((const void *)k_token_proj<float>, lds);
         hipLaunchKernelGGL(k_token_proj<float>, dim3(grid), dim3(256), lds, s, a);
     } else {
-        (void)hipFuncSetAttribute((const void *)k_token_proj<bf16_t>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        allow_lds((const void *)k_token_proj<bf16_t>, lds);
         hipLaunchKernelGGL(k_token_proj<bf16_t>, dim3(grid), dim3(256), lds, s, a);
     }
     return hipGetLastError();
@@ -438,7 +436,7 @@ hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
         else { if (stage == STAGE_ENCODER) WAA_PICK(bf16_t, 1, 0); else WAA_PICK(bf16_t, 1, 1); }
     }
 #undef WAA_PICK
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    allow_lds(fn, lds);
     void *args[] = {(void *)&a};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
     if (e != hipSuccess)

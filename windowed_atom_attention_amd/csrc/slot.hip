@@ -35,7 +35,7 @@ hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) 
     }
     if (fn == nullptr)
         return hipErrorInvalidValue;
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    allow_lds(fn, lds);
     const int grid = a.B * ((a.A + kQB - 1) / kQB);
     void *args[] = {(void *)&a};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
