@@ -55,7 +55,12 @@ def kernel_work(w):
     work = {"slot_attention": ("hbm", slot_bytes), "prep": ("mfma", prep),
             "post": ("mfma", post)}
     if w.stage == "encoder":
-        work["pool"] = ("mfma", N * 2 * C * U)
+        # the pooled projection runs inside post; the pool kernel only joins
+        # tokens that cross 32-row tiles (reads the tile records, writes at
+        # most two token rows per tile)
+        work["post"] = ("mfma", post + N * 2 * C * U)
+        ntile = (N + 31) // 32
+        work["pool"] = ("hbm", ntile * (2 * U * 4 + 32) + ntile * 2 * U * e)
     else:
         work["token_proj"] = ("mfma", B * T * 2 * U * C)
     return work

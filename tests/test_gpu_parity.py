@@ -302,3 +302,38 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for k in ref:
             assert torch.equal(out[k], ref[k]), k
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pooling_tokens_across_tiles(dtype):
+    """Token layouts the tile-local pooling has to join: a token of 100
+    atoms spanning four 32-atom tiles, with a whole tile of unusable atoms
+    inside it; a token ending exactly at a tile boundary; one-atom tokens;
+    a batch boundary inside a tile (B=2, A=150); empty tokens."""
+    w = make_workload("1", B=2, A=150, dtype=dtype)
+    B, A, T = w.dims["B"], w.dims["A"], w.dims["T"]
+    a2t = torch.zeros((B, A), dtype=torch.int64)
+    for b in range(B):
+        pos, t = 0, 0
+        for size in [100, 28, 1, 1, 5] + [3] * 10:
+            if pos >= A or t >= T:
+                break
+            a2t[b, pos:pos + size] = t
+            pos += size
+            t += 2 if size == 1 else 1  # odd ids after one-atom tokens stay empty
+        a2t[b, pos:] = min(t, T - 1)
+    w.structure["atom_to_token"] = a2t
+    valid = w.masks["valid"].clone()
+    valid[0, 40:75] = False  # an unusable tile inside the long token
+    w.masks["valid"] = valid
+    tv = w.masks["token_valid"].clone()
+    tv[:] = True
+    w.masks["token_valid"] = tv
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    g = w.to("cuda")
+    out = windowed_atom_attention(**g.kwargs(), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = oracle.block(**w.kwargs(), intermediates=True)
+    assert_close("token_output", np64(out["token_output"]), ref["token_output"], RTOL[dtype])
+    exact_zero_checks(w, {k: v for k, v in out.items()}, ref["usable"], ref["allowed"])

@@ -129,7 +129,8 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
         post_lds_bytes(dd, dtype, style) > kMaxLds ||
         !slot_supported(dd, dtype, style))
         return ATOM_ATTN_EUNSUPPORTED;
-    if (stage == ATOM_ATTN_ENCODER && pool_lds_bytes(dd, dtype) > kMaxLds)
+    // pooling keys (batch * T + token) are int32
+    if (stage == ATOM_ATTN_ENCODER && d->B * d->T >= ((int64_t)1 << 31))
         return ATOM_ATTN_EUNSUPPORTED;
     if (stage == ATOM_ATTN_DECODER && token_proj_lds_bytes(dd, dtype) > kMaxLds)
         return ATOM_ATTN_EUNSUPPORTED;
@@ -139,7 +140,7 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
 // ------------------------------------------------------------ workspace
 
 struct Layout {
-    size_t packed, q, k, v, g, o, usable, tokproj, total;
+    size_t packed, q, k, v, g, o, usable, tokproj, pool_sum, pool_int, total;
     int64_t pack_units;
 };
 
@@ -221,6 +222,14 @@ Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
     L.tokproj = o;
     if (stage == ATOM_ATTN_DECODER)
         o = up256(o + (size_t)(d->B * d->T * d->C) * 4);
+    const size_t ntile = (N + 31) / 32;
+    L.pool_sum = o;
+    L.pool_int = o;
+    if (stage == ATOM_ATTN_ENCODER) {
+        o = up256(o + ntile * 2 * (size_t)d->U * 4);
+        L.pool_int = o;
+        o = up256(o + ntile * 8 * 4);
+    }
     L.total = o;
     return L;
 }
@@ -329,6 +338,8 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.q = ws + L.q; a.k = ws + L.k; a.v = ws + L.v; a.g = ws + L.g; a.o = ws + L.o;
     a.usable = (uint8_t *)(ws + L.usable);
     a.tokproj = enc ? nullptr : (float *)(ws + L.tokproj);
+    a.pool_sum = enc ? (float *)(ws + L.pool_sum) : nullptr;
+    a.pool_int = enc ? (int *)(ws + L.pool_int) : nullptr;
     a.hidden = out->hidden; a.attention = out->attention;
     a.token_output = out->token_output; a.position_update = out->position_update;
     a.status = out->status;

@@ -46,6 +46,11 @@ struct BlockArgs {
     void *q, *k, *v, *g, *o;
     uint8_t *usable;
     float *tokproj;
+    // encoder pooling records, one per 32-row tile: first / last segment
+    // sums [tile][2][U] and [tile][8] ints (segments, first key, first
+    // count, last key, last count)
+    float *pool_sum;
+    int *pool_int;
     // outputs
     void *hidden, *attention, *token_output, *position_update;
     int32_t *status;
@@ -106,7 +111,6 @@ hipError_t launch_masks(const Dims &d, const uint8_t *valid,
 // LDS bytes each kernel needs for these sizes (host-side shape checks).
 size_t prep_lds_bytes(const Dims &d, int dtype, int style);
 size_t post_lds_bytes(const Dims &d, int dtype, int style);
-size_t pool_lds_bytes(const Dims &d, int dtype);
 size_t token_proj_lds_bytes(const Dims &d, int dtype);
 size_t slot_lds_bytes(const Dims &d, int dtype, int style);
 int slot_supported(const Dims &d, int dtype, int style);

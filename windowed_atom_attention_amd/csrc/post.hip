@@ -41,7 +41,7 @@ __device__ __forceinline__ void load16_f2(const T *src, float *out) {
 
 struct PostLayout {
     int xp, ldS, ldC, ldHD, ldH;
-    size_t o_st, o_us, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
+    size_t o_st, o_us, o_key, o_seg, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
 };
 
 // Transition width handled per pass: h is staged kMC columns at a time.
@@ -59,6 +59,8 @@ __host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int st
     size_t o = 32 * (size_t)L.xp * 4;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
+    L.o_key = o; o += 32 * 4;      // (batch, token) key of each row, -1 if unusable
+    L.o_seg = o; o += 4 * 33 * 4;  // segment of each row; segment keys, counts; count
     L.o_opC = o; o = al16(o + 32 * (size_t)L.ldS * esz);
     // one tile holds, in turn, o*G (until x1), LN(c)*cond_scale[2] (AF3,
     // until z) and a chunk of h (transition)
@@ -99,8 +101,12 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
 
     const bool u = inb && p.usable[n];
     const int b = inb ? n / d.A : 0;
-    if (sub == 0)
+    int *rkey = reinterpret_cast<int *>(smem + L.o_key);
+    if (sub == 0) {
         us[row] = u;
+        if (STAGE == STAGE_ENCODER)
+            rkey[row] = u ? b * d.T + (int)p.atom_to_token[n] : -1;
+    }
     {
         // entry state, as the prep kernel builds it
         const T *ar = reinterpret_cast<const T *>(p.atom) + (int64_t)n * C;
@@ -319,6 +325,93 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
             }
         }
     }
+    if (STAGE == STAGE_ENCODER) {
+        // ---- pooling: ReLU(hidden @ w_pool) of this tile's rows, summed per
+        // segment of consecutive usable rows with one (batch, token) key.
+        // Segments inside the tile are complete tokens (keys are sorted) and
+        // their means are written here; the first and the last segment may
+        // continue in neighbouring tiles and go to this tile's record for
+        // the pooling fix-up kernel.
+        __syncthreads(); // hidden rows complete in xs
+        for (int vi = sub; vi < C / E; vi += 8) {
+            T tmp[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                tmp[e] = from_f<T>(xs[row * L.xp + vi * E + e]);
+            uint4 v4;
+            __builtin_memcpy(&v4, tmp, 16);
+            *reinterpret_cast<uint4 *>(opZ + row * L.ldC + vi * E) = v4;
+        }
+        int *segid = reinterpret_cast<int *>(smem + L.o_seg);
+        int *skey = segid + 32, *scnt = segid + 64, *snum = segid + 96;
+        if (wave == 0) {
+            const int k = lane < 32 ? rkey[lane] : -1;
+            const uint64_t um = __ballot(k >= 0);
+            const uint64_t below = um & ((1ull << lane) - 1ull);
+            const int prev = below ? 63 - __clzll((long long)below) : -1;
+            const int pk = prev >= 0 ? rkey[prev] : -1;
+            const bool start = k >= 0 && (prev < 0 || pk != k);
+            const uint64_t sm = __ballot(start);
+            const int sidx = __popcll(sm & ((2ull << lane) - 1ull)) - 1;
+            if (lane < 32)
+                segid[lane] = k >= 0 ? sidx : -1;
+            if (start) {
+                const uint64_t above = sm & ~((2ull << lane) - 1ull);
+                const int nxt = above ? __ffsll((long long)above) - 1 : 32;
+                const uint64_t span = ((nxt >= 64 ? 0ull : (1ull << nxt)) - 1ull) & ~((1ull << lane) - 1ull);
+                skey[sidx] = k;
+                scnt[sidx] = __popcll(um & span);
+            }
+            // keys must not decrease along the usable rows (sorted tokens)
+            const bool bad = k >= 0 && prev >= 0 && pk > k;
+            if (__ballot(bad) != 0ull && lane == 0 && p.status != nullptr)
+                p.status[0] = 1;
+            if (lane == 0)
+                snum[0] = __popcll(sm);
+        }
+        __syncthreads();
+        const int nseg = snum[0];
+        const int tile = blockIdx.x;
+        float *rsum = p.pool_sum + (int64_t)tile * 2 * d.U;
+        if (tid == 0) {
+            int *ri = p.pool_int + (int64_t)tile * 8;
+            ri[0] = nseg;
+            ri[1] = nseg > 0 ? skey[0] : -1;
+            ri[2] = nseg > 0 ? scnt[0] : 0;
+            ri[3] = nseg > 1 ? skey[nseg - 1] : -1;
+            ri[4] = nseg > 1 ? scnt[nseg - 1] : 0;
+        }
+        if (nseg > 0) {
+            T *tout = reinterpret_cast<T *>(p.token_output);
+            for (int nb = wave; nb < d.U / 32; nb += 4) {
+                f32x16_t a1 = zero16(), unused = zero16();
+                gemm_dual<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb * nkC * 64,
+                             unused, opZ, nullptr, L.ldC, 0, nullptr);
+                int sv[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    sv[v] = segid[acc32_row(v, lane)];
+                    a1[v] = fmaxf(a1[v], 0.0f);
+                }
+                const int col = nb * 32 + acc32_col(lane);
+                for (int s = 0; s < nseg; ++s) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        part += sv[v] == s ? a1[v] : 0.0f;
+                    part += __shfl_xor(part, 32);
+                    if (lane < 32) {
+                        if (s == 0)
+                            rsum[col] = part;
+                        else if (s == nseg - 1)
+                            rsum[d.U + col] = part;
+                        else
+                            tout[(int64_t)skey[s] * d.U + col] = from_f<T>(part / (float)scnt[s]);
+                    }
+                }
+            }
+        }
+    }
     if (STAGE == STAGE_DECODER) {
         __syncthreads();
         const float *xr = xs + row * L.xp;
@@ -380,179 +473,84 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
     return hipGetLastError();
 }
 
-// --------------------------------------------------------------- pool
+// --------------------------------------------------------------- pool fix-up
 
-struct PoolLayout {
-    int ldC, pp;
-    size_t o_ps, o_tok, o_us, total;
-};
-
-__host__ __device__ inline PoolLayout pool_layout(const Dims &d, int esz) {
-    PoolLayout L;
-    L.ldC = d.C + 16 / esz;
-    L.pp = d.U + 4;
-    size_t o = al16(32 * (size_t)L.ldC * esz);
-    L.o_ps = o; o += 32 * (size_t)L.pp * 4;
-    L.o_tok = o; o += 32 * 4;
-    L.o_us = o; o += 32;
-    L.total = al16(o);
-    return L;
-}
-
-size_t pool_lds_bytes(const Dims &d, int dtype) {
-    return pool_layout(d, dtype ? 2 : 4).total;
-}
-
-constexpr int kPoolMaxCols = 4; // U <= 1024
-
+// Tokens whose atoms cross tile boundaries: every tile's record holds the
+// sums and counts of its first and last segment (post kernel). A tile owns
+// its last segment (when it has two or more) and its first segment unless
+// that continues the last segment of the previous non-empty tile; the owner
+// adds the first-segment sums of the following tiles while they continue the
+// token (a single-segment tile passes it on), in tile order, and writes the
+// mean. Keys that decrease across tiles set the status word.
 template <typename T>
-__global__ __launch_bounds__(256) void k_pool(BlockArgs p) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_prev;
-    const Dims d = p.d;
-    const int A = d.A, C = d.C, U = d.U;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = tid >> 3, sub = tid & 7;
-    const int ntile = (A + 31) / 32;
-    const int b = blockIdx.x / ntile;
-    const int a0 = (blockIdx.x % ntile) * 32;
-    const PoolLayout L = pool_layout(d, sizeof(T));
-    T *opA = reinterpret_cast<T *>(smem);
-    float *ps = reinterpret_cast<float *>(smem + L.o_ps);
-    int *tok = reinterpret_cast<int *>(smem + L.o_tok);
-    uint8_t *us = smem + L.o_us;
-    const int64_t base = (int64_t)b * A;
-
-    // token of the last usable atom before this tile (-1 if none)
-    if (wave == 0) {
-        int prev = -1;
-        for (int hi = a0 - 1; hi >= 0; hi -= 64) {
-            const int a = hi - lane;
-            const bool uu = a >= 0 && p.usable[base + a];
-            const unsigned long long m = __ballot(uu);
-            if (m) {
-                const int l = __ffsll((long long)m) - 1; // lowest lane = largest a
-                prev = (int)p.atom_to_token[base + hi - l];
-                break;
-            }
-        }
-        if (lane == 0)
-            s_prev = prev;
-    }
-
-    const int nkc = C / Mma32<T>::KC;
-    T *tout = reinterpret_cast<T *>(p.token_output);
-    float acc[kPoolMaxCols];
-#pragma unroll
-    for (int i = 0; i < kPoolMaxCols; ++i)
-        acc[i] = 0.0f;
-    int cur = -1, cnt = 0;
-    bool owned = false, first = true, done = false, bad = false;
-
-    auto flush = [&]() {
-        if (cur >= 0 && owned) {
-            const float inv = 1.0f / (float)cnt;
-            T *dst = tout + ((int64_t)b * d.T + cur) * U;
-#pragma unroll
-            for (int i = 0; i < kPoolMaxCols; ++i) {
-                const int col = tid + 256 * i;
-                if (col < U)
-                    dst[col] = from_f<T>(acc[i] * inv);
-            }
-        }
-    };
-
-    for (int chunk = 0; !done; ++chunk) {
-        const int cb = a0 + chunk * 32;
-        if (cb >= A) {
-            flush();
-            break;
-        }
-        __syncthreads();
-        {
-            const int a = cb + row;
-            const bool ok = a < A;
-            if (sub == 0) {
-                us[row] = ok ? p.usable[base + a] : 0;
-                tok[row] = ok ? (int)p.atom_to_token[base + a] : -1;
-            }
-            const T *src = reinterpret_cast<const T *>(p.hidden) + (base + a) * C;
-            constexpr int E = 16 / sizeof(T);
-            for (int vi = sub; vi < C / E; vi += 8) {
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (ok)
-                    val = *reinterpret_cast<const uint4 *>(src + vi * E);
-                *reinterpret_cast<uint4 *>(opA + row * L.ldC + vi * E) = val;
-            }
-        }
-        __syncthreads();
-        for (int nb = wave; nb < U / 32; nb += 4) {
-            f32x16_t a1 = zero16();
-            f32x16_t unused = zero16();
-            gemm_dual<T>(a1, opA, nullptr, L.ldC, nkc, p.pk + p.off.w_pool + (int64_t)nb * nkc * 64,
-                         unused, opA, nullptr, L.ldC, 0, nullptr);
-            const int c = nb * 32 + acc32_col(lane);
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                ps[acc32_row(v, lane) * L.pp + c] = fmaxf(a1[v], 0.0f);
-        }
-        __syncthreads();
-        const int prev_tok = s_prev;
-        for (int r = 0; r < 32; ++r) {
-            const int a = cb + r;
-            if (a >= A)
-                break;
-            if (!us[r])
-                continue;
-            const int t = tok[r];
-            if (t != cur) {
-                flush();
-                if (a >= a0 + 32) {
-                    done = true;
-                    cur = -1;
-                    break;
-                }
-                if ((cur >= 0 && t < cur) || (cur < 0 && first && prev_tok >= 0 && t < prev_tok))
-                    bad = true;
-                owned = !(first && t == prev_tok);
-                first = false;
-                cur = t;
-                cnt = 0;
-#pragma unroll
-                for (int i = 0; i < kPoolMaxCols; ++i)
-                    acc[i] = 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < kPoolMaxCols; ++i) {
-                const int col = tid + 256 * i;
-                if (col < U)
-                    acc[i] += ps[r * L.pp + col];
-            }
-            ++cnt;
-        }
-        if (!done) {
-            if (cb + 32 >= A) {
-                flush();
-                done = true;
-            } else if (cur < 0 || !owned) {
-                done = true;
-            }
-        }
-    }
-    if (bad && tid == 0 && p.status != nullptr)
+__global__ __launch_bounds__(256) void k_pool_fix(BlockArgs p) {
+    const int t = blockIdx.x, ntile = gridDim.x, U = p.d.U, tid = threadIdx.x;
+    const int *ri = p.pool_int;
+    const float *rs = p.pool_sum;
+    const int nseg = ri[t * 8];
+    if (nseg == 0)
+        return;
+    int u = t - 1;
+    while (u >= 0 && ri[u * 8] == 0)
+        --u;
+    const int prev_last = u < 0 ? -1 : (ri[u * 8] == 1 ? ri[u * 8 + 1] : ri[u * 8 + 3]);
+    const int fkey = ri[t * 8 + 1];
+    if (prev_last > fkey && tid == 0 && p.status != nullptr)
         p.status[0] = 1;
+    T *tout = reinterpret_cast<T *>(p.token_output);
+    for (int which = 0; which < 2; ++which) {
+        int key, cnt;
+        bool may_continue;
+        if (which == 0) {
+            if (prev_last == fkey)
+                continue;
+            key = fkey;
+            cnt = ri[t * 8 + 2];
+            may_continue = nseg == 1;
+        } else {
+            if (nseg < 2)
+                continue;
+            key = ri[t * 8 + 3];
+            cnt = ri[t * 8 + 4];
+            may_continue = true;
+        }
+        float acc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int col = tid + 256 * i;
+            acc[i] = col < U ? rs[((int64_t)t * 2 + which) * U + col] : 0.0f;
+        }
+        for (int v = t + 1; may_continue && v < ntile; ++v) {
+            const int ns = ri[v * 8];
+            if (ns == 0)
+                continue;
+            if (ri[v * 8 + 1] != key)
+                break;
+            cnt += ri[v * 8 + 2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int col = tid + 256 * i;
+                if (col < U)
+                    acc[i] += rs[(int64_t)v * 2 * U + col];
+            }
+            may_continue = ns == 1;
+        }
+        const float inv = 1.0f / (float)cnt;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int col = tid + 256 * i;
+            if (col < U)
+                tout[(int64_t)key * U + col] = from_f<T>(acc[i] * inv);
+        }
+    }
 }
 
 hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s) {
-    const int ntile = (a.d.A + 31) / 32;
-    const int grid = a.d.B * ntile;
-    const size_t lds = pool_lds_bytes(a.d, dtype);
-    const void *fn = dtype == 0 ? (const void *)k_pool<float> : (const void *)k_pool<bf16_t>;
-    allow_lds(fn, lds);
-    void *args[] = {(void *)&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
-    if (e != hipSuccess)
-        return e;
+    const int grid = (a.d.B * a.d.A + 31) / 32;
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_pool_fix<float>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_pool_fix<bf16_t>, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
