@@ -169,62 +169,88 @@ __device__ __forceinline__ int acc16_col(int lane) { return lane & 15; }
 // data, so that the 32 rows of an operand tile start in different LDS banks.
 template <typename T> constexpr int pad16() { return 16 / (int)sizeof(T); }
 
-// Two products at once, acc1 += A1 @ B1 and acc2 += A2 @ B2, over nk1 and
-// nk2 16-byte k-chunks (nk2 = 0 for a single product).
-// A: LDS tiles, row-major, pitch lda elements (16-byte aligned rows),
-//    optionally given as an unevaluated sum hi + lo of two tiles in the
-//    storage type ("split" operand: for bf16 it keeps ~16 mantissa bits of
-//    an fp32 activation at twice the MFMA work); Alo == nullptr means none.
+// Matrix products acc1 += A1 @ B1 (and, with DUAL, acc2 += A2 @ B2) over
+// nk1 (nk2) 16-byte k-chunks, nk >= 1.
+// A: LDS tiles, row-major, pitch lda elements (16-byte aligned rows); with
+//    SPLIT each is an unevaluated sum hi + lo of two tiles in the storage
+//    type (for bf16 it keeps ~16 mantissa bits of an fp32 activation at
+//    twice the MFMA work).
 // B: packed weight blocks (see pack.hip): chunk kc of the column block at
 //    B[kc*64 + lane], 16 bytes per lane, read from L2.
-// The B chunks are software-pipelined in batches of four per product: the
-// next batch is in flight while the MFMAs of the current one run.
-template <typename T>
-__device__ __forceinline__ void gemm_dual(f32x16_t &acc1, const T *A1, const T *A1lo,
+// Software pipeline: kPipe B chunks per product are in flight; each chunk is
+// consumed and its register refilled with the chunk kPipe ahead. Every load
+// is unconditional (indices clamp to the last chunk, so the tail re-reads
+// it), which lets the compiler wait for exactly the chunk it needs instead
+// of draining all loads; the A chunks of a group are read from LDS together.
+constexpr int kPipe = 4;
+template <typename T, bool DUAL, bool SPLIT>
+__device__ __forceinline__ void gemm_pipe(f32x16_t &acc1, const T *A1, const T *A1lo,
                                           int lda1, int nk1, const uint4 *__restrict__ B1,
                                           f32x16_t &acc2, const T *A2, const T *A2lo,
                                           int lda2, int nk2, const uint4 *__restrict__ B2) {
-    constexpr int KC = Mma32<T>::KC, NB = 4;
+    constexpr int KC = Mma32<T>::KC, P = kPipe;
     const int lane = threadIdx.x & 63;
     const int o1 = (lane & 31) * lda1 + (lane >> 5) * Mma32<T>::HALF;
-    const int o2 = (lane & 31) * lda2 + (lane >> 5) * Mma32<T>::HALF;
-    const int nk = nk1 > nk2 ? nk1 : nk2;
-    auto fetch = [&](uint4 (&b1)[NB], uint4 (&b2)[NB], int kb) {
+    const int o2 = DUAL ? (lane & 31) * lda2 + (lane >> 5) * Mma32<T>::HALF : 0;
+    const int nk = DUAL ? (nk1 > nk2 ? nk1 : nk2) : nk1;
+    const int l1 = nk1 - 1, l2 = DUAL ? nk2 - 1 : 0;
+    uint4 b1[P], b2[P];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            if (kb + j < nk1)
-                b1[j] = B1[(kb + j) * 64 + lane];
-            if (kb + j < nk2)
-                b2[j] = B2[(kb + j) * 64 + lane];
-        }
-    };
-    auto compute = [&](const uint4 (&b1)[NB], const uint4 (&b2)[NB], int kb) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            if (kb + j < nk1) {
-                Mma32<T>::mma(acc1, *reinterpret_cast<const uint4 *>(A1 + o1 + (kb + j) * KC), b1[j]);
-                if (A1lo != nullptr)
-                    Mma32<T>::mma(acc1, *reinterpret_cast<const uint4 *>(A1lo + o1 + (kb + j) * KC), b1[j]);
-            }
-            if (kb + j < nk2) {
-                Mma32<T>::mma(acc2, *reinterpret_cast<const uint4 *>(A2 + o2 + (kb + j) * KC), b2[j]);
-                if (A2lo != nullptr)
-                    Mma32<T>::mma(acc2, *reinterpret_cast<const uint4 *>(A2lo + o2 + (kb + j) * KC), b2[j]);
-            }
-        }
-    };
-    uint4 ba1[NB], ba2[NB], bb1[NB], bb2[NB];
-    fetch(ba1, ba2, 0);
-    for (int kb = 0; kb < nk; kb += 2 * NB) {
-        if (kb + NB < nk)
-            fetch(bb1, bb2, kb + NB);
-        compute(ba1, ba2, kb);
-        if (kb + NB >= nk)
-            break;
-        if (kb + 2 * NB < nk)
-            fetch(ba1, ba2, kb + 2 * NB);
-        compute(bb1, bb2, kb + NB);
+    for (int j = 0; j < P; ++j) {
+        b1[j] = B1[(j < l1 ? j : l1) * 64 + lane];
+        if (DUAL)
+            b2[j] = B2[(j < l2 ? j : l2) * 64 + lane];
     }
+    for (int kb = 0; kb < nk; kb += P) {
+        uint4 x1[P], x1l[P], x2[P], x2l[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int k1 = kb + j < l1 ? kb + j : l1;
+            x1[j] = *reinterpret_cast<const uint4 *>(A1 + o1 + k1 * KC);
+            if (SPLIT)
+                x1l[j] = *reinterpret_cast<const uint4 *>(A1lo + o1 + k1 * KC);
+            if (DUAL) {
+                const int k2 = kb + j < l2 ? kb + j : l2;
+                x2[j] = *reinterpret_cast<const uint4 *>(A2 + o2 + k2 * KC);
+                if (SPLIT)
+                    x2l[j] = *reinterpret_cast<const uint4 *>(A2lo + o2 + k2 * KC);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int k = kb + j;
+            if (k < nk1) {
+                Mma32<T>::mma(acc1, x1[j], b1[j]);
+                if (SPLIT)
+                    Mma32<T>::mma(acc1, x1l[j], b1[j]);
+            }
+            if (DUAL && k < nk2) {
+                Mma32<T>::mma(acc2, x2[j], b2[j]);
+                if (SPLIT)
+                    Mma32<T>::mma(acc2, x2l[j], b2[j]);
+            }
+            const int n1 = k + P < l1 ? k + P : l1;
+            b1[j] = B1[n1 * 64 + lane];
+            if (DUAL) {
+                const int n2 = k + P < l2 ? k + P : l2;
+                b2[j] = B2[n2 * 64 + lane];
+            }
+        }
+    }
+}
+
+template <typename T, bool SPLIT = false>
+__device__ __forceinline__ void gemm2(f32x16_t &acc1, const T *A1, const T *A1lo, int lda1,
+                                      int nk1, const uint4 *__restrict__ B1, f32x16_t &acc2,
+                                      const T *A2, const T *A2lo, int lda2, int nk2,
+                                      const uint4 *__restrict__ B2) {
+    gemm_pipe<T, true, SPLIT>(acc1, A1, A1lo, lda1, nk1, B1, acc2, A2, A2lo, lda2, nk2, B2);
+}
+
+template <typename T, bool SPLIT = false>
+__device__ __forceinline__ void gemm1(f32x16_t &acc, const T *A, const T *Alo, int lda, int nk,
+                                      const uint4 *__restrict__ B) {
+    gemm_pipe<T, false, SPLIT>(acc, A, Alo, lda, nk, B, acc, A, Alo, lda, 0, B);
 }
 
 // Store x into a split operand pair: hi = x rounded to T, lo = the rest

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm_dual<T>(a1, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao + (int64_t)nb * nkHD * 64,
+            gemm2<T>(a1, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao + (int64_t)nb * nkHD * 64,
                          a2, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
             const int c = nb * 32 + acc32_col(lane);
             const float bias = STYLE == STYLE_AF3 ? to_f(brg[c]) : 0.0f;
@@ -245,10 +245,10 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
             if (STYLE == STYLE_AF3) {
-                gemm_dual<T>(a1, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_scale[2] + (int64_t)nb * nkS * 64,
+                gemm2<T>(a1, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_scale[2] + (int64_t)nb * nkS * 64,
                              a2, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_shift[2] + (int64_t)nb * nkS * 64);
             } else {
-                gemm_dual<T>(a1, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[3] + (int64_t)nb * nkS * 64,
+                gemm2<T>(a1, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[3] + (int64_t)nb * nkS * 64,
                              a2, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[4] + (int64_t)nb * nkS * 64);
             }
             const int c = nb * 32 + acc32_col(lane);
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                     for (int hb = wave; hb < mc / 32; hb += 4) {
                         const int64_t wb = (int64_t)(m0 / 32 + hb) * nkC * 64;
                         f32x16_t a1 = zero16(), a2 = zero16();
-                        gemm_dual<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + wb,
+                        gemm2<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + wb,
                                      a2, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_up + wb);
                         const int c = hb * 32 + acc32_col(lane);
 #pragma unroll
@@ -303,10 +303,12 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                     continue;
                 const bool last = m0 + kMC >= M;
                 f32x16_t ga = zero16();
-                gemm_dual<T>(acc, opH, nullptr, L.ldH, mc / KC,
-                             p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64,
-                             ga, opC, nullptr, L.ldS, last ? nkS : 0,
-                             p.pk + offg + (int64_t)nb * nkS * 64);
+                const uint4 *wo = p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64;
+                if (last)
+                    gemm2<T>(acc, opH, nullptr, L.ldH, mc / KC, wo,
+                             ga, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
+                else
+                    gemm1<T>(acc, opH, nullptr, L.ldH, mc / KC, wo);
                 if (last) {
                     const int c = nb * 32 + acc32_col(lane);
                     const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
@@ -384,9 +386,8 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         if (nseg > 0) {
             T *tout = reinterpret_cast<T *>(p.token_output);
             for (int nb = wave; nb < d.U / 32; nb += 4) {
-                f32x16_t a1 = zero16(), unused = zero16();
-                gemm_dual<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb * nkC * 64,
-                             unused, opZ, nullptr, L.ldC, 0, nullptr);
+                f32x16_t a1 = zero16();
+                gemm1<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb * nkC * 64);
                 int sv[16];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {

@@ -78,9 +78,7 @@ __global__ __launch_bounds__(256) void k_token_proj(BlockArgs p) {
     const int nkc = d.U / Mma32<T>::KC;
     for (int nb = wave; nb < d.C / 32; nb += 4) {
         f32x16_t acc = zero16();
-        f32x16_t unused = zero16();
-        gemm_dual<T>(acc, opA, nullptr, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64,
-                     unused, opA, nullptr, ldU, 0, nullptr);
+        gemm1<T>(acc, opA, nullptr, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64);
         const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -321,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
             T *dstl = j == 0 ? opQl : opKl;
             for (int nb = wave; nb < C / 32; nb += 4) {
                 f32x16_t a1 = zero16(), a2 = zero16();
-                gemm_dual<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64,
+                gemm2<T, SPLIT>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64,
                              a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
                 const int c = nb * 32 + acc32_col(lane);
                 const float bs = to_f(bscale[j * C + c]);
@@ -340,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
         __syncthreads();
         for (int nb = wave; nb < C / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm_dual<T>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64,
+            gemm2<T, SPLIT>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64,
                          a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
             const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
@@ -368,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
         const T *bq = reinterpret_cast<const T *>(p.b_q);
         for (int nb = wave; nb < HD / 32; nb += 4) {
             f32x16_t a1 = zero16(), a2 = zero16();
-            gemm_dual<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64,
+            gemm2<T, SPLIT>(a1, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64,
                          a2, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
             const int c = nb * 32 + acc32_col(lane);
             const float bias = to_f(bq[c]);
@@ -381,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
                 }
             }
             f32x16_t a3 = zero16(), a4 = zero16();
-            gemm_dual<T>(a3, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64,
+            gemm2<T, SPLIT>(a3, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64,
                          a4, opK, opKl, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -398,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
             for (int nb = wave; nb < HD / 32; nb += 4) {
                 f32x16_t a1 = zero16(), a2 = zero16();
-                gemm_dual<T>(a1, opQ, opQl, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64,
+                gemm2<T, SPLIT>(a1, opQ, opQl, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64,
                              a2, opQ, opQl, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
                 const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
