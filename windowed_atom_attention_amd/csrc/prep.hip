@@ -154,31 +154,41 @@ size_t prep_lds_bytes(const Dims &d, int dtype, int style) {
 }
 
 // Per-head RMS normalisation and half-split rotary of the 32 x H*D tile in
-// hb (fp32), stored to dst (fp32). One thread per (row, head).
+// hb (fp32), stored to dst (fp32). Eight threads per row; for each head a
+// thread takes D/16 coordinate pairs (e, e + D/2), so the rotation needs no
+// other thread and the sum of squares one 8-lane reduction:
+//   y = x * rsqrt(mean(x^2) + eps),
+//   out[e] = y[e] cos[e] - y[e+D/2] sin[e],
+//   out[e+D/2] = y[e+D/2] cos[e+D/2] + y[e] sin[e+D/2].
 template <typename T>
 __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
                                 int n0, float *dst) {
     const Dims d = p.d;
-    const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2;
-    const T *cosb = reinterpret_cast<const T *>(p.rope_cos);
-    const T *sinb = reinterpret_cast<const T *>(p.rope_sin);
-    for (int pi = threadIdx.x; pi < 32 * d.H; pi += 256) {
-        const int r = pi / d.H, h = pi % d.H;
-        const int n = n0 + r;
-        if (n >= N)
+    const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2, m = half / 8;
+    const int row = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const int n = n0 + row;
+    const bool ok = n < N;
+    const T *cs = reinterpret_cast<const T *>(p.rope_cos) + (int64_t)(ok ? n : 0) * D;
+    const T *sn = reinterpret_cast<const T *>(p.rope_sin) + (int64_t)(ok ? n : 0) * D;
+    const float invD = 1.0f / (float)D;
+    for (int h = 0; h < d.H; ++h) {
+        const float *x = hb + row * hp + h * D;
+        float ss = 0.0f;
+        for (int i = 0; i < m; ++i) {
+            const int e = sub * m + i;
+            ss = fmaf(x[e], x[e], ss);
+            ss = fmaf(x[e + half], x[e + half], ss);
+        }
+        ss = group_sum<8>(ss);
+        const float rs = rsqrtf(ss * invD + p.eps);
+        if (!ok)
             continue;
-        const float *x = hb + r * hp + h * D;
-        float ms = 0.0f;
-        for (int e = 0; e < D; ++e)
-            ms += x[e] * x[e];
-        const float rs = 1.0f / sqrtf(ms / (float)D + p.eps);
         float *out = dst + (int64_t)n * HD + h * D;
-        const T *cs = cosb + (int64_t)n * D;
-        const T *sn = sinb + (int64_t)n * D;
-        for (int e = 0; e < D; ++e) {
-            const float y = x[e] * rs;
-            const float rot = e < half ? -x[e + half] * rs : x[e - half] * rs;
-            out[e] = y * to_f(cs[e]) + rot * to_f(sn[e]);
+        for (int i = 0; i < m; ++i) {
+            const int e = sub * m + i;
+            const float y1 = x[e] * rs, y2 = x[e + half] * rs;
+            out[e] = y1 * to_f(cs[e]) - y2 * to_f(sn[e]);
+            out[e + half] = y2 * to_f(cs[e + half]) + y1 * to_f(sn[e + half]);
         }
     }
 }
