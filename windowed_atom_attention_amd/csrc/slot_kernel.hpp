@@ -158,8 +158,29 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     T *att = reinterpret_cast<T *>(p.attention);
     T *og = reinterpret_cast<T *>(p.o);
 
-    // ---- key ids and window bits of this thread's slots
+    // ---- AF3 pair rows of this thread's slots, in groups of GS slots: the
+    // first group is in flight from the start, each later group while the
+    // previous one is reduced. Rows past the end of a ragged key list
+    // re-read the last row; rows of unusable queries are loaded but unused.
     const bool full = qin && k0 + SPL <= K; // every slot of the thread exists
+    const int nsl = !qin ? 0 : (full ? SPL : (K > k0 ? K - k0 : 0));
+    constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : (NV * (int)sizeof(T) <= 8 ? 2 : 1));
+    constexpr int NG = SPL / GS;
+    uint4 pbuf[2][GS][NV];
+    const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + k0) * VV;
+    auto load_group = [&](uint4 (&dst)[GS][NV], int g0) {
+#pragma unroll
+        for (int ii = 0; ii < GS; ++ii) {
+            const T *src = prow + min(g0 + ii, nsl - 1) * VV;
+#pragma unroll
+            for (int pt = 0; pt < NV; ++pt)
+                dst[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
+        }
+    };
+    if (STYLE == STYLE_AF3 && nsl > 0)
+        load_group(pbuf[0], 0);
+
+    // ---- key ids and window bits of this thread's slots
     int64_t kid[SPL];
     bool wmv[SPL];
     if (SPL >= 8 && p.vec_rows && full) {
@@ -235,27 +256,18 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
         for (int h = 0; h < kHG; ++h)
             beta[i][h] = 0.0f;
     __syncthreads(); // wpr, wsum, s_lo/s_hi initialised
-    const int nsl = full ? SPL : K - k0; // slots of this thread that exist
-    if (STYLE == STYLE_AF3 && qok && nsl > 0) {
-        const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + k0) * VV;
+    if (STYLE == STYLE_AF3 && nsl > 0) {
         const float4 *w4p = reinterpret_cast<const float4 *>(wpr);
         const float4 ws = *reinterpret_cast<const float4 *>(wsum);
         constexpr float kInvV = 1.0f / (float)VV;
-        // slots per group: their rows are in flight together and one
-        // broadcast weight read serves them all
-        constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : 2);
 #pragma unroll
-        for (int g0 = 0; g0 < SPL; g0 += GS) {
-            uint4 pb[GS][NV];
-            // rows past the end of a ragged key list re-read the last row
-            // (unconditional loads; their bias is never used)
-#pragma unroll
-            for (int ii = 0; ii < GS; ++ii) {
-                const T *src = prow + min(g0 + ii, nsl - 1) * VV;
-#pragma unroll
-                for (int pt = 0; pt < NV; ++pt)
-                    pb[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
-            }
+        for (int gi = 0; gi < NG; ++gi) {
+            if (gi + 1 < NG)
+                load_group(pbuf[(gi + 1) & 1], (gi + 1) * GS);
+            if (!qok)
+                continue;
+            const uint4 (&pb)[GS][NV] = pbuf[gi & 1];
+            const int g0 = gi * GS;
             float x0[GS], sd[GS], sq[GS], bb[GS][kHG];
 #pragma unroll
             for (int ii = 0; ii < GS; ++ii) {
@@ -298,9 +310,6 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                 beta[g0 + ii][2] = (bb[ii][2] - md * ws.z) * rstd;
                 beta[g0 + ii][3] = (bb[ii][3] - md * ws.w) * rstd;
             }
-            // keep the next group's loads from being hoisted above this
-            // group's arithmetic (registers: one group in flight)
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
     int rel[SPL];
@@ -375,27 +384,20 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     // whose index survives writes the cell with a plain store; the others
     // (repeated key ids in a row) add their weights with LDS atomics after
     // a barrier. A wide band (several chunks) adds every weight atomically.
+    // The tags are written here and read after the first barrier of the
+    // score phase.
     int *tag = reinterpret_cast<int *>(smem + L.o_tag);
     bool win[SPL];
-    int lose_any = 0;
+    int lose_any = 1;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+        win[i] = false;
     if (nch == 1) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
             if (rel[i] >= 0)
                 tag[q * kRMAX + rel[i] - jal] = k0 + i;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-            win[i] = rel[i] >= 0 && tag[q * kRMAX + rel[i] - jal] == k0 + i;
-            lose_any |= (rel[i] >= 0 && !win[i]) ? 1 : 0;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < SPL; ++i)
-            win[i] = false;
-        lose_any = 1;
     }
-    lose_any = __syncthreads_or(lose_any);
 
     for (int hg = 0; hg < H; hg += kHG) {
         const int hw = hg + wave; // this wave's head in the S and P V products
@@ -455,7 +457,15 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                                 twave[acc16_row(v, lane) * L.sp + (cb0 + t) * 16 + acc16_col(lane)] = acc[t][v];
                 }
             }
-            __syncthreads();
+            __syncthreads(); // score tiles (and the tags) written
+            if (hg == 0 && c == 0 && nch == 1) {
+                lose_any = 0;
+#pragma unroll
+                for (int i = 0; i < SPL; ++i) {
+                    win[i] = rel[i] >= 0 && tag[q * kRMAX + rel[i] - jal] == k0 + i;
+                    lose_any |= (rel[i] >= 0 && !win[i]) ? 1 : 0;
+                }
+            }
 #pragma unroll
             for (int hh = 0; hh < kHG; ++hh) {
                 if (hg + hh >= H)
@@ -468,7 +478,11 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                         lg[i][hh] = fmaf(sh[r], scale, lg[i][hh]);
                 }
             }
-            __syncthreads(); // score tiles read; the next chunk or P may reuse them
+            // score tiles read; the next chunk or P may reuse them
+            if (hg == 0 && c == nch - 1)
+                lose_any = __syncthreads_or(lose_any);
+            else
+                __syncthreads();
         }
         // the tiles become the (zeroed) probability tiles
         for (int i = tid; i < kHG * kQB * L.sp / 4; i += 256)
