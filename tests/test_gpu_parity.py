@@ -50,6 +50,10 @@ SMALL = [
     ("0", dict(A=150, V=16, H=4, D=64)),
     ("0", dict(A=150, H=2, D=128, V=16, dtype=torch.bfloat16, stage="decoder")),
     ("0", dict(A=200, K=48, style="esmfold2", H=8, D=16)),
+    # more 32-atom tiles than compute units: the projection kernels' 4-wave
+    # form (small grids take the 8-wave form that splits k over wave pairs)
+    ("0", dict(B=30, A=300)),
+    ("0", dict(B=30, A=300, style="esmfold2", stage="decoder", dtype=torch.bfloat16)),
 ]
 
 

@@ -2,6 +2,7 @@
 // argument checks, workspace layout, weight packing jobs and the launch
 // sequence of one block call. Host code only; every step of the block runs
 // in the kernels of pack/prep/slot/post.hip.
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -36,6 +37,20 @@ Profiler g_prof;
 } // namespace
 
 namespace waa {
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 void allow_lds(const void *fn, size_t bytes) {
     static std::mutex mu;
     static std::unordered_map<const void *, size_t> limit;

@@ -47,6 +47,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// 16 bytes of storage-type values -> 16/sizeof(T) floats.
+template <typename T>
+__device__ __forceinline__ void unpack16(uint4 v, float *out) {
+    if constexpr (sizeof(T) == 4) {
+        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
 // Logistic function from e = exp(-|z|) in (0, 1]: 1/(1+e) for z >= 0 and
 // e/(1+e) below, so a very negative argument keeps its tiny (down to
 // subnormal) value instead of 1 - 1. exp2f keeps subnormal results (the
@@ -83,6 +99,13 @@ __device__ __forceinline__ float dpp_f(float v, int ctrl) {
     case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
     default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
     }
+}
+// Sum over aligned groups of 8 lanes (the first three steps of sum16).
+__device__ __forceinline__ float sum8(float v) {
+    v += dpp_f(v, 0xB1);
+    v += dpp_f(v, 0x4E);
+    v += dpp_f(v, 0x141);
+    return v;
 }
 __device__ __forceinline__ float sum16(float v) {
     v += dpp_f(v, 0xB1);
@@ -285,6 +308,27 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
     if (bid >= full)
         return bid;
     return (bid % X) * (full / X) + bid / X;
+}
+
+// One GEMM stage of a 32-row tile (one wave per 32-column output block):
+// for every block nb < nblocks, x1 = A1 @ B1[nb] (and x2 = A2 @ B2[nb]),
+// then epi(nb, v, x1[v], x2[v]) for accumulator elements v of the lane
+// (row acc32_row(v, lane), column nb*32 + acc32_col(lane)). B1[nb] starts
+// at B1 + nb * bs1 (16-byte units).
+template <typename T, bool DUAL, bool SPLIT, typename Epi>
+__device__ __forceinline__ void gemm_stage(int nblocks, const T *A1, const T *A1lo, int lda1,
+                                           int nk1, const uint4 *B1, int64_t bs1,
+                                           const T *A2, const T *A2lo, int lda2, int nk2,
+                                           const uint4 *B2, int64_t bs2, Epi &&epi) {
+    const int wave = threadIdx.x >> 6;
+    for (int nb = wave; nb < nblocks; nb += 4) {
+        f32x16_t a1 = zero16(), a2 = zero16();
+        gemm_pipe<T, DUAL, SPLIT>(a1, A1, A1lo, lda1, nk1, B1 + nb * bs1,
+                                  a2, A2, A2lo, lda2, nk2, DUAL ? B2 + nb * bs2 : B1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            epi(nb, v, a1[v], DUAL ? a2[v] : 0.0f);
+    }
 }
 
 } // namespace waa

@@ -121,4 +121,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 // call is made only when a launch needs more than any launch before).
 void allow_lds(const void *fn, size_t bytes);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 } // namespace waa

@@ -23,22 +23,6 @@
 
 namespace waa {
 
-template <typename T>
-__device__ __forceinline__ void load16_f2(const T *src, float *out) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(src);
-    if constexpr (sizeof(T) == 4) {
-        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
-        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
-    } else {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(w[i] << 16);
-            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-}
-
 struct PostLayout {
     int xp, ldS, ldC, ldHD, ldH;
     size_t o_st, o_us, o_key, o_seg, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
@@ -62,12 +46,12 @@ __host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int st
     L.o_key = o; o += 32 * 4;      // (batch, token) key of each row, -1 if unusable
     L.o_seg = o; o += 4 * 33 * 4;  // segment of each row; segment keys, counts; count
     L.o_opC = o; o = al16(o + 32 * (size_t)L.ldS * esz);
-    // one tile holds, in turn, o*G (until x1), LN(c)*cond_scale[2] (AF3,
-    // until z) and a chunk of h (transition)
-    int w = L.ldHD > L.ldH ? L.ldHD : L.ldH;
-    if (style == STYLE_AF3 && L.ldS > w)
-        w = L.ldS;
-    L.o_opU = L.o_opC2 = L.o_opH = o;
+    L.o_opC2 = o; // LN(c) * cond_scale[2] (AF3)
+    if (style == STYLE_AF3)
+        o = al16(o + 32 * (size_t)L.ldS * esz);
+    // one tile holds, in turn, o*G (until x1) and a chunk of h (transition)
+    const int w = L.ldHD > L.ldH ? L.ldHD : L.ldH;
+    L.o_opU = L.o_opH = o;
     o = al16(o + 32 * (size_t)w * esz);
     L.o_opZ = o; o = al16(o + 32 * (size_t)L.ldC * esz);
     L.total = o;
@@ -78,13 +62,15 @@ size_t post_lds_bytes(const Dims &d, int dtype, int style) {
     return post_layout(d, dtype ? 2 : 4, style).total;
 }
 
+// 256 threads: four waves, TPR = 8 threads per tile row.
 template <typename T, int STYLE, int STAGE>
 __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NT = 256, TPR = NT / 32;
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D, M = d.M;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = tid >> 3, sub = tid & 7;
+    const int row = tid / TPR, sub = tid % TPR;
     const int n0 = blockIdx.x * 32;
     const int n = n0 + row;
     const bool inb = n < N;
@@ -108,62 +94,110 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
             rkey[row] = u ? b * d.T + (int)p.atom_to_token[n] : -1;
     }
     {
-        // entry state, as the prep kernel builds it
-        const T *ar = reinterpret_cast<const T *>(p.atom) + (int64_t)n * C;
+        // entry state (as the prep kernel builds it), condition (raw for the
+        // AF3 gates, SiLU for the ESMFold2 modulation) and o*G rounded to
+        // the storage type; every load of a round is issued before the
+        // rows are converted into LDS
+        // rows past the end read row 0 (loads are unconditional; the values
+        // of unusable or missing rows are replaced by zeros after the load)
+        const int64_t nc = inb ? n : 0;
+        const T *ar = reinterpret_cast<const T *>(p.atom) + nc * C;
+        const T *cr = reinterpret_cast<const T *>(p.condition) + nc * S;
+        const T *orow = reinterpret_cast<const T *>(p.o) + nc * HD;
+        const T *grow = reinterpret_cast<const T *>(p.g) + nc * HD;
         int64_t tk = 0;
         if (STAGE == STAGE_DECODER && u)
             tk = p.atom_to_token[n];
         const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
-        for (int vi = sub; vi < C / E; vi += 8) {
-            float xv[E];
-            if (u) {
-                load16_f2<T>(ar + vi * E, xv);
-                if (STAGE == STAGE_DECODER) {
+        const int nvC = C / E, nvS = S / E, nvH = HD / E;
+        const int nvmax = nvC > nvS ? (nvC > nvH ? nvC : nvH) : (nvS > nvH ? nvS : nvH);
+        constexpr int RV = 4; // vectors per array and thread in one round
+        float csum = 0.0f;
+        for (int base = sub; base < nvmax; base += RV * TPR) {
+            uint4 va[RV], vc[RV], vo[RV], vg[RV];
+            float vt[RV][E]; // decoder: the gathered token projection
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                const int vi = base + j * TPR;
+                va[j] = *reinterpret_cast<const uint4 *>(ar + min(vi, nvC - 1) * E);
+                vc[j] = *reinterpret_cast<const uint4 *>(cr + min(vi, nvS - 1) * E);
+                vo[j] = *reinterpret_cast<const uint4 *>(orow + min(vi, nvH - 1) * E);
+                vg[j] = *reinterpret_cast<const uint4 *>(grow + min(vi, nvH - 1) * E);
+                const uint4 z = make_uint4(0, 0, 0, 0);
+                if (!u) {
+                    va[j] = z;
+                    vc[j] = z;
+                }
+                if (!inb)
+                    vo[j] = vg[j] = z;
+                if constexpr (STAGE == STAGE_DECODER) {
+#pragma unroll
+                    for (int t = 0; t < E / 4; ++t) {
+                        float4 f = *reinterpret_cast<const float4 *>(tp + min(vi, nvC - 1) * E + 4 * t);
+                        if (!u)
+                            f = make_float4(0.f, 0.f, 0.f, 0.f);
+                        vt[j][4 * t + 0] = f.x; vt[j][4 * t + 1] = f.y;
+                        vt[j][4 * t + 2] = f.z; vt[j][4 * t + 3] = f.w;
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                const int vi = base + j * TPR;
+                if (vi < nvC) {
+                    float xv[E];
+                    unpack16<T>(va[j], xv);
+                    if constexpr (STAGE == STAGE_DECODER) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            xv[e] += vt[j][e];
+                    }
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        xv[e] += tp[vi * E + e];
+                        xs[row * L.xp + vi * E + e] = xv[e];
                 }
-            } else {
+                if (vi < nvS) {
+                    float cv[E];
+                    unpack16<T>(vc[j], cv);
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    xv[e] = 0.0f;
+                    for (int e = 0; e < E; ++e) {
+                        opC[row * L.ldS + vi * E + e] =
+                            STYLE == STYLE_AF3 ? from_f<T>(cv[e]) : from_f<T>(silu_f(cv[e]));
+                        csum += cv[e];
+                    }
+                }
+                if (vi < nvH) {
+                    float ov[E], gv[E];
+                    unpack16<T>(vo[j], ov);
+                    unpack16<T>(vg[j], gv);
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        opU[row * L.ldHD + vi * E + e] = from_f<T>(ov[e] * gv[e]);
+                }
             }
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                xs[row * L.xp + vi * E + e] = xv[e];
         }
-        // condition: raw (AF3 gates) or SiLU (ESMFold2 modulation)
-        const T *cr = reinterpret_cast<const T *>(p.condition) + (int64_t)n * S;
-        for (int vi = sub; vi < S / E; vi += 8) {
-            float cv[E];
-            if (u) {
-                load16_f2<T>(cr + vi * E, cv);
-            } else {
+        if (STYLE == STYLE_AF3) {
+            // c_2 = LN(c) * cond_scale[2], each thread on its own entries of
+            // opC (written above by the same thread: no barrier needed)
+            const float mc = sum8(csum) / (float)S;
+            float q = 0.0f;
+            for (int vi = sub; vi < nvS; vi += TPR)
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    cv[e] = 0.0f;
+                for (int e = 0; e < E; ++e) {
+                    const float t = to_f(opC[row * L.ldS + vi * E + e]) - mc;
+                    q += t * t;
+                }
+            const float rc = 1.0f / sqrtf(sum8(q) / (float)S + p.eps);
+            const T *cscale = reinterpret_cast<const T *>(p.cond_scale) + 2 * S;
+            for (int vi = sub; vi < nvS; vi += TPR) {
+                float sc[E];
+                unpack16<T>(*reinterpret_cast<const uint4 *>(cscale + vi * E), sc);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int c = vi * E + e;
+                    opC2[row * L.ldS + c] = from_f<T>((to_f(opC[row * L.ldS + c]) - mc) * rc * sc[e]);
+                }
             }
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                opC[row * L.ldS + vi * E + e] =
-                    STYLE == STYLE_AF3 ? from_f<T>(cv[e]) : from_f<T>(silu_f(cv[e]));
-        }
-        // value-gated attention output (o * G), rounded to the storage type
-        const T *orow = reinterpret_cast<const T *>(p.o) + (int64_t)n * HD;
-        const T *grow = reinterpret_cast<const T *>(p.g) + (int64_t)n * HD;
-        for (int vi = sub; vi < HD / E; vi += 8) {
-            float ov[E], gv[E];
-            if (inb) {
-                load16_f2<T>(orow + vi * E, ov);
-                load16_f2<T>(grow + vi * E, gv);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    ov[e] = gv[e] = 0.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                opU[row * L.ldHD + vi * E + e] = from_f<T>(ov[e] * gv[e]);
         }
     }
     __syncthreads();
@@ -175,63 +209,40 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     {
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
-        for (int nb = wave; nb < C / 32; nb += 4) {
-            f32x16_t a1 = zero16(), a2 = zero16();
-            gemm2<T>(a1, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao + (int64_t)nb * nkHD * 64,
-                         a2, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
-            const int c = nb * 32 + acc32_col(lane);
-            const float bias = STYLE == STYLE_AF3 ? to_f(brg[c]) : 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
+        gemm_stage<T, true, false>(
+            C / 32, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao, (int64_t)nkHD * 64,
+            opC, nullptr, L.ldS, nkS, p.pk + offg, (int64_t)nkS * 64,
+            [&](int nb, int v, float x1, float x2) {
+                const int c = nb * 32 + acc32_col(lane);
                 const int r = acc32_row(v, lane);
-                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(a2[v] + bias) : a2[v];
-                xs[r * L.xp + c] += gate * a1[v];
-            }
-        }
+                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(x2 + to_f(brg[c])) : x2;
+                xs[r * L.xp + c] += gate * x1;
+            });
     }
     __syncthreads();
-    if (STYLE == STYLE_AF3) {
-        // c_2 = LN(c) * cond_scale[2] (opC holds the raw condition exactly),
-        // into the tile o*G occupied
-        const T *cr = opC + row * L.ldS;
-        float s = 0.0f;
-        for (int c = sub; c < S; c += 8)
-            s += to_f(cr[c]);
-        const float mc = group_sum<8>(s) / (float)S;
-        float q = 0.0f;
-        for (int c = sub; c < S; c += 8) {
-            const float t = to_f(cr[c]) - mc;
-            q += t * t;
-        }
-        const float rc = 1.0f / sqrtf(group_sum<8>(q) / (float)S + p.eps);
-        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
-        for (int c = sub; c < S; c += 8)
-            opC2[row * L.ldS + c] = from_f<T>((to_f(cr[c]) - mc) * rc * to_f(cscale[2 * S + c]));
-    }
-
     // statistics of the NEW state for the transition norm
     {
         const float *xr = xs + row * L.xp;
         if (STYLE == STYLE_AF3) {
             float s = 0.0f;
-            for (int c = sub; c < C; c += 8)
+            for (int c = sub; c < C; c += TPR)
                 s += xr[c];
-            const float mean = group_sum<8>(s) / (float)C;
+            const float mean = sum8(s) / (float)C;
             float q = 0.0f;
-            for (int c = sub; c < C; c += 8) {
+            for (int c = sub; c < C; c += TPR) {
                 const float t = xr[c] - mean;
                 q += t * t;
             }
-            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = mean;
                 st[row * 4 + 1] = rstd;
             }
         } else {
             float q = 0.0f;
-            for (int c = sub; c < C; c += 8)
+            for (int c = sub; c < C; c += TPR)
                 q += xr[c] * xr[c];
-            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
                 st[row * 4 + 1] = rstd;
@@ -242,34 +253,28 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     // z = transition-normalised x1
     {
         const T *bsc = reinterpret_cast<const T *>(p.b_scale);
-        for (int nb = wave; nb < C / 32; nb += 4) {
-            f32x16_t a1 = zero16(), a2 = zero16();
-            if (STYLE == STYLE_AF3) {
-                gemm2<T>(a1, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_scale[2] + (int64_t)nb * nkS * 64,
-                             a2, opC2, nullptr, L.ldS, nkS, p.pk + p.off.w_shift[2] + (int64_t)nb * nkS * 64);
-            } else {
-                gemm2<T>(a1, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[3] + (int64_t)nb * nkS * 64,
-                             a2, opC, nullptr, L.ldS, nkS, p.pk + p.off.w_mod[4] + (int64_t)nb * nkS * 64);
-            }
-            const int c = nb * 32 + acc32_col(lane);
-            const float bias = STYLE == STYLE_AF3 ? to_f(bsc[2 * C + c]) : 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
+        const T *opz = STYLE == STYLE_AF3 ? opC2 : opC;
+        const int64_t o1 = STYLE == STYLE_AF3 ? p.off.w_scale[2] : p.off.w_mod[3];
+        const int64_t o2 = STYLE == STYLE_AF3 ? p.off.w_shift[2] : p.off.w_mod[4];
+        gemm_stage<T, true, false>(
+            C / 32, opz, nullptr, L.ldS, nkS, p.pk + o1, (int64_t)nkS * 64,
+            opz, nullptr, L.ldS, nkS, p.pk + o2, (int64_t)nkS * 64,
+            [&](int nb, int v, float x1, float x2) {
+                const int c = nb * 32 + acc32_col(lane);
                 const int r = acc32_row(v, lane);
                 const float xn = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
                 float z;
                 if (STYLE == STYLE_AF3)
-                    z = xn * sigmoid_f(a1[v] + bias) + a2[v];
+                    z = xn * sigmoid_f(x1 + to_f(bsc[2 * C + c])) + x2;
                 else
-                    z = xn * (1.0f + a2[v]) + a1[v];
+                    z = xn * (1.0f + x2) + x1;
                 opZ[r * L.ldC + c] = from_f<T>(z);
-            }
-        }
+            });
     }
     __syncthreads();
     // x2 = x1 + g_tr * (h @ w_ff_out), h = SiLU(z @ w_ff_gate) * (z @ w_ff_up),
     // with h staged kMC columns at a time. Output columns go in groups of
-    // 128 (one 32-column block per wave), so each wave carries one block of
+    // 128 (one 32-column block per wave), so each wave carries its block of
     // h @ w_ff_out in registers across the passes; with C > 128 and M > kMC
     // the h chunks are recomputed per group. hidden = select(usable, x2, 0).
     {
@@ -281,48 +286,44 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         for (int cg = 0; cg < C / 32; cg += 4) {
             const int nb = cg + wave;
             const bool own = nb < C / 32;
-            f32x16_t acc = zero16();
+            f32x16_t acc = zero16(), ga = zero16();
             for (int m0 = 0; m0 < M; m0 += kMC) {
                 const int mc = M - m0 < kMC ? M - m0 : kMC;
                 if (cg == 0 || !single) {
                     if (m0 > 0 || cg > 0)
                         __syncthreads(); // the previous chunk of h has been consumed
-                    for (int hb = wave; hb < mc / 32; hb += 4) {
-                        const int64_t wb = (int64_t)(m0 / 32 + hb) * nkC * 64;
-                        f32x16_t a1 = zero16(), a2 = zero16();
-                        gemm2<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + wb,
-                                     a2, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_up + wb);
-                        const int c = hb * 32 + acc32_col(lane);
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            opH[acc32_row(v, lane) * L.ldH + c] = from_f<T>(silu_f(a1[v]) * a2[v]);
-                    }
+                    gemm_stage<T, true, false>(
+                        mc / 32, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + (int64_t)(m0 / 32) * nkC * 64,
+                        (int64_t)nkC * 64, opZ, nullptr, L.ldC, nkC,
+                        p.pk + p.off.ff_up + (int64_t)(m0 / 32) * nkC * 64, (int64_t)nkC * 64,
+                        [&](int hb, int v, float x1, float x2) {
+                            opH[acc32_row(v, lane) * L.ldH + hb * 32 + acc32_col(lane)] =
+                                from_f<T>(silu_f(x1) * x2);
+                        });
                     __syncthreads();
                 }
                 if (!own)
                     continue;
-                const bool last = m0 + kMC >= M;
-                f32x16_t ga = zero16();
                 const uint4 *wo = p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64;
-                if (last)
+                if (m0 + kMC >= M)
                     gemm2<T>(acc, opH, nullptr, L.ldH, mc / KC, wo,
                              ga, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
                 else
                     gemm1<T>(acc, opH, nullptr, L.ldH, mc / KC, wo);
-                if (last) {
-                    const int c = nb * 32 + acc32_col(lane);
-                    const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
+            }
+            if (own) {
+                const int c = nb * 32 + acc32_col(lane);
+                const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = acc32_row(v, lane);
-                        const float gate = STYLE == STYLE_AF3 ? sigmoid_f(ga[v] + bias) : ga[v];
-                        const float x2 = xs[r * L.xp + c] + gate * acc[v];
-                        const float h = us[r] ? x2 : 0.0f;
-                        xs[r * L.xp + c] = h;
-                        const int nn = n0 + r;
-                        if (nn < N)
-                            hid[(int64_t)nn * C + c] = from_f<T>(h);
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const int r = acc32_row(v, lane);
+                    const float gate = STYLE == STYLE_AF3 ? sigmoid_f(ga[v] + bias) : ga[v];
+                    const float x2 = xs[r * L.xp + c] + gate * acc[v];
+                    const float h = us[r] ? x2 : 0.0f;
+                    xs[r * L.xp + c] = h;
+                    const int nn = n0 + r;
+                    if (nn < N)
+                        hid[(int64_t)nn * C + c] = from_f<T>(h);
                 }
             }
         }
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         // continue in neighbouring tiles and go to this tile's record for
         // the pooling fix-up kernel.
         __syncthreads(); // hidden rows complete in xs
-        for (int vi = sub; vi < C / E; vi += 8) {
+        for (int vi = sub; vi < C / E; vi += TPR) {
             T tmp[E];
 #pragma unroll
             for (int e = 0; e < E; ++e)
@@ -417,20 +418,20 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         __syncthreads();
         const float *xr = xs + row * L.xp;
         float s = 0.0f;
-        for (int c = sub; c < C; c += 8)
+        for (int c = sub; c < C; c += TPR)
             s += xr[c];
-        const float mean = group_sum<8>(s) / (float)C;
+        const float mean = sum8(s) / (float)C;
         float q = 0.0f;
-        for (int c = sub; c < C; c += 8) {
+        for (int c = sub; c < C; c += TPR) {
             const float t = xr[c] - mean;
             q += t * t;
         }
-        const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+        const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
         const T *rs = reinterpret_cast<const T *>(p.readout_scale);
         const T *rb = reinterpret_cast<const T *>(p.readout_bias);
         const T *wr = reinterpret_cast<const T *>(p.w_readout);
         float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f;
-        for (int c = sub; c < C; c += 8) {
+        for (int c = sub; c < C; c += TPR) {
             float z = (xr[c] - mean) * rstd * to_f(rs[c]);
             if (STYLE == STYLE_ESM)
                 z += to_f(rb[c]);
@@ -438,9 +439,9 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
             acc1 += z * to_f(wr[c * 3 + 1]);
             acc2 += z * to_f(wr[c * 3 + 2]);
         }
-        acc0 = group_sum<8>(acc0);
-        acc1 = group_sum<8>(acc1);
-        acc2 = group_sum<8>(acc2);
+        acc0 = sum8(acc0);
+        acc1 = sum8(acc1);
+        acc2 = sum8(acc2);
         if (sub == 0 && inb) {
             T *pu = reinterpret_cast<T *>(p.position_update) + (int64_t)n * 3;
             const bool ok = us[row];

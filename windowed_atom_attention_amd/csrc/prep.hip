@@ -39,23 +39,6 @@ __device__ __forceinline__ void copy_row(T *dst, const T *src, int n, bool ok,
     }
 }
 
-// Load 16 bytes of T at src as fp32 values.
-template <typename T>
-__device__ __forceinline__ void load16_f(const T *src, float *out) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(src);
-    if constexpr (sizeof(T) == 4) {
-        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
-        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
-    } else {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(w[i] << 16);
-            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-}
-
 // --------------------------------------------------------------- K0
 
 template <typename T>
@@ -115,7 +98,7 @@ hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
 // that the logits path keeps ~16 mantissa bits; fp32 tiles are single.
 struct PrepLayout {
     int xp, hp, ldS, ldC;
-    size_t o_st, o_us, o_rb, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
+    size_t o_st, o_us, o_rb, o_cr, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -132,6 +115,7 @@ __host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int st
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
     L.o_rb = o; o += 64 * 4; // per row: atom index within its batch, then batch
+    L.o_cr = o; o += tS;      // the sanitised condition, storage type
     L.o_opA = o; o += tS;
     L.o_opAl = o; if (split) o += tS;
     L.o_opQ = o; o += tC;
@@ -154,18 +138,19 @@ size_t prep_lds_bytes(const Dims &d, int dtype, int style) {
 }
 
 // Per-head RMS normalisation and half-split rotary of the 32 x H*D tile in
-// hb (fp32), stored to dst (fp32). Eight threads per row; for each head a
-// thread takes D/16 coordinate pairs (e, e + D/2), so the rotation needs no
-// other thread and the sum of squares one 8-lane reduction:
+// hb (fp32), stored to dst (fp32). TPR threads per row; for each head a
+// thread takes consecutive coordinate pairs (e, e + D/2), so the rotation
+// needs no other thread and the sum of squares one TPR-lane reduction:
 //   y = x * rsqrt(mean(x^2) + eps),
 //   out[e] = y[e] cos[e] - y[e+D/2] sin[e],
 //   out[e+D/2] = y[e+D/2] cos[e+D/2] + y[e] sin[e+D/2].
-template <typename T>
+template <typename T, int TPR>
 __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
                                 int n0, float *dst) {
     const Dims d = p.d;
-    const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2, m = half / 8;
-    const int row = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2;
+    const int pp = (half + TPR - 1) / TPR; // pairs per thread
+    const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
     const int n = n0 + row;
     const bool ok = n < N;
     const T *cs = reinterpret_cast<const T *>(p.rope_cos) + (int64_t)(ok ? n : 0) * D;
@@ -174,18 +159,22 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
     for (int h = 0; h < d.H; ++h) {
         const float *x = hb + row * hp + h * D;
         float ss = 0.0f;
-        for (int i = 0; i < m; ++i) {
-            const int e = sub * m + i;
-            ss = fmaf(x[e], x[e], ss);
-            ss = fmaf(x[e + half], x[e + half], ss);
+        for (int i = 0; i < pp; ++i) {
+            const int e = sub * pp + i;
+            if (e < half) {
+                ss = fmaf(x[e], x[e], ss);
+                ss = fmaf(x[e + half], x[e + half], ss);
+            }
         }
-        ss = group_sum<8>(ss);
+        ss = sum8(ss);
         const float rs = rsqrtf(ss * invD + p.eps);
         if (!ok)
             continue;
         float *out = dst + (int64_t)n * HD + h * D;
-        for (int i = 0; i < m; ++i) {
-            const int e = sub * m + i;
+        for (int i = 0; i < pp; ++i) {
+            const int e = sub * pp + i;
+            if (e >= half)
+                break;
             const float y1 = x[e] * rs, y2 = x[e + half] * rs;
             out[e] = y1 * to_f(cs[e]) - y2 * to_f(sn[e]);
             out[e + half] = y2 * to_f(cs[e + half]) + y1 * to_f(sn[e + half]);
@@ -193,13 +182,15 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
     }
 }
 
+// 256 threads: four waves, TPR = 8 threads per tile row.
 template <typename T, int STYLE, int STAGE>
 __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NT = 256, TPR = NT / 32;
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = tid >> 3, sub = tid & 7;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int row = tid / TPR, sub = tid % TPR;
     const int n0 = blockIdx.x * 32;
     const int n = n0 + row;
     const bool inb = n < N;
@@ -209,8 +200,8 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     if (STAGE == STAGE_ENCODER) {
         T *to = reinterpret_cast<T *>(p.token_output);
         const int64_t total = (int64_t)d.B * d.T * d.U;
-        for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < total;
-             i += (int64_t)gridDim.x * 256)
+        for (int64_t i = (int64_t)blockIdx.x * NT + tid; i < total;
+             i += (int64_t)gridDim.x * NT)
             to[i] = from_f<T>(0.0f);
     }
     if (p.status != nullptr && blockIdx.x == 0 && tid == 0)
@@ -221,6 +212,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
     int *rb = reinterpret_cast<int *>(smem + L.o_rb);
+    T *crs = reinterpret_cast<T *>(smem + L.o_cr);
     T *opA = reinterpret_cast<T *>(smem + L.o_opA);
     T *opAl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opAl) : nullptr;
     T *opQ = reinterpret_cast<T *>(smem + L.o_opQ);
@@ -229,7 +221,21 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     T *opKl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opKl) : nullptr;
     float *hb = reinterpret_cast<float *>(smem + L.o_hb);
 
-    // usability of this row's atom
+    // Row loads first (unconditional, rows past the end read row 0; values
+    // of unusable atoms are replaced by zeros: selected, never multiplied),
+    // while the usability of the row is resolved.
+    const int64_t nc = inb ? n : 0;
+    const T *ar = reinterpret_cast<const T *>(p.atom) + nc * C;
+    const T *cr = reinterpret_cast<const T *>(p.condition) + nc * S;
+    const int nvC = C / E, nvS = S / E, nvmax = nvC > nvS ? nvC : nvS;
+    constexpr int RV = 4; // vectors per array and thread in one round
+    uint4 va[RV], vc[RV];
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        const int vi = sub + j * TPR;
+        va[j] = *reinterpret_cast<const uint4 *>(ar + min(vi, nvC - 1) * E);
+        vc[j] = *reinterpret_cast<const uint4 *>(cr + min(vi, nvS - 1) * E);
+    }
     const int b = inb ? n / d.A : 0;
     int64_t tk = 0;
     bool u = false;
@@ -244,67 +250,73 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
         if (inb)
             p.usable[n] = u;
     }
-    // sanitised entry state and condition (selected, never multiplied)
-    {
-        const T *ar = reinterpret_cast<const T *>(p.atom) + (int64_t)n * C;
-        for (int vi = sub; vi < C / E; vi += 8) {
-            float xv[E];
-            if (u) {
-                load16_f<T>(ar + vi * E, xv);
+    const float *tp = p.tokproj + ((int64_t)b * d.T + (u ? tk : 0)) * C;
+    for (int base = sub; base < nvmax; base += RV * TPR) {
+        if (base != sub) { // later rounds (C or S above 4 * TPR vectors)
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                const int vi = base + j * TPR;
+                va[j] = *reinterpret_cast<const uint4 *>(ar + min(vi, nvC - 1) * E);
+                vc[j] = *reinterpret_cast<const uint4 *>(cr + min(vi, nvS - 1) * E);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            const int vi = base + j * TPR;
+            if (vi < nvC) {
+                float xv[E];
+                unpack16<T>(va[j], xv);
                 if (STAGE == STAGE_DECODER) {
-                    const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
 #pragma unroll
                     for (int e = 0; e < E; ++e)
                         xv[e] += tp[vi * E + e];
                 }
-            } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    xv[e] = 0.0f;
+                    xs[row * L.xp + vi * E + e] = u ? xv[e] : 0.0f;
             }
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                xs[row * L.xp + vi * E + e] = xv[e];
+            if (vi < nvS)
+                *reinterpret_cast<uint4 *>(crs + row * L.ldS + vi * E) =
+                    u ? vc[j] : make_uint4(0, 0, 0, 0);
         }
     }
     __syncthreads();
-    // the sanitised condition row (zero for unusable atoms), read on demand
-    const T *crow = reinterpret_cast<const T *>(p.condition) + (int64_t)n * S;
-    auto cond = [&](int c) -> float { return u ? to_f(crow[c]) : 0.0f; };
+    // the sanitised condition row (zero for unusable atoms)
+    auto cond = [&](int c) -> float { return to_f(crs[row * L.ldS + c]); };
 
     // row statistics of x0 (and of c for AF3)
     {
         const float *xr = xs + row * L.xp;
         if (STYLE == STYLE_AF3) {
             float s = 0.0f;
-            for (int c = sub; c < C; c += 8)
+            for (int c = sub; c < C; c += TPR)
                 s += xr[c];
-            const float mean = group_sum<8>(s) / (float)C;
+            const float mean = sum8(s) / (float)C;
             float q = 0.0f;
-            for (int c = sub; c < C; c += 8) {
+            for (int c = sub; c < C; c += TPR) {
                 const float t = xr[c] - mean;
                 q += t * t;
             }
-            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
             float s2 = 0.0f;
-            for (int c = sub; c < S; c += 8)
+            for (int c = sub; c < S; c += TPR)
                 s2 += cond(c);
-            const float mc = group_sum<8>(s2) / (float)S;
+            const float mc = sum8(s2) / (float)S;
             float q2 = 0.0f;
-            for (int c = sub; c < S; c += 8) {
+            for (int c = sub; c < S; c += TPR) {
                 const float t = cond(c) - mc;
                 q2 += t * t;
             }
-            const float rc = 1.0f / sqrtf(group_sum<8>(q2) / (float)S + p.eps);
+            const float rc = 1.0f / sqrtf(sum8(q2) / (float)S + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = mean; st[row * 4 + 1] = rstd;
                 st[row * 4 + 2] = mc;   st[row * 4 + 3] = rc;
             }
         } else {
             float q = 0.0f;
-            for (int c = sub; c < C; c += 8)
+            for (int c = sub; c < C; c += TPR)
                 q += xr[c] * xr[c];
-            const float rstd = 1.0f / sqrtf(group_sum<8>(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
                 st[row * 4 + 1] = rstd;
@@ -320,44 +332,38 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
         for (int j = 0; j < 2; ++j) {
             {
                 const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
-                for (int c = sub; c < S; c += 8)
+                for (int c = sub; c < S; c += TPR)
                     put_split<T>(opA, opAl, row * L.ldS + c,
                                  (cond(c) - mc) * rc * to_f(cscale[j * S + c]));
             }
             __syncthreads();
             T *dst = j == 0 ? opQ : opK;
             T *dstl = j == 0 ? opQl : opKl;
-            for (int nb = wave; nb < C / 32; nb += 4) {
-                f32x16_t a1 = zero16(), a2 = zero16();
-                gemm2<T, SPLIT>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j] + (int64_t)nb * nkS * 64,
-                             a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j] + (int64_t)nb * nkS * 64);
-                const int c = nb * 32 + acc32_col(lane);
-                const float bs = to_f(bscale[j * C + c]);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
+            gemm_stage<T, true, SPLIT>(
+                C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
+                opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j], (int64_t)nkS * 64,
+                [&](int nb, int v, float x1, float x2) {
+                    const int c = nb * 32 + acc32_col(lane);
                     const int r = acc32_row(v, lane);
                     const float ln = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
-                    put_split<T>(dst, dstl, r * L.ldC + c, ln * sigmoid_f(a1[v] + bs) + a2[v]);
-                }
-            }
+                    put_split<T>(dst, dstl, r * L.ldC + c,
+                                 ln * sigmoid_f(x1 + to_f(bscale[j * C + c])) + x2);
+                });
             __syncthreads();
         }
     } else {
-        for (int c = sub; c < S; c += 8)
+        for (int c = sub; c < S; c += TPR)
             put_split<T>(opA, opAl, row * L.ldS + c, silu_f(cond(c)));
         __syncthreads();
-        for (int nb = wave; nb < C / 32; nb += 4) {
-            f32x16_t a1 = zero16(), a2 = zero16();
-            gemm2<T, SPLIT>(a1, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0] + (int64_t)nb * nkS * 64,
-                         a2, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1] + (int64_t)nb * nkS * 64);
-            const int c = nb * 32 + acc32_col(lane);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
+        gemm_stage<T, true, SPLIT>(
+            C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0], (int64_t)nkS * 64,
+            opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1], (int64_t)nkS * 64,
+            [&](int nb, int v, float x1, float x2) {
+                const int c = nb * 32 + acc32_col(lane);
                 const int r = acc32_row(v, lane);
                 const float rm = xs[r * L.xp + c] * st[r * 4 + 1];
-                put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + a2[v]) + a1[v]);
-            }
-        }
+                put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + x2) + x1);
+            });
         __syncthreads();
     }
 
@@ -374,56 +380,49 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     };
     if (STYLE == STYLE_AF3) {
         const T *bq = reinterpret_cast<const T *>(p.b_q);
-        for (int nb = wave; nb < HD / 32; nb += 4) {
-            f32x16_t a1 = zero16(), a2 = zero16();
-            gemm2<T, SPLIT>(a1, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q + (int64_t)nb * nkC * 64,
-                         a2, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg + (int64_t)nb * nkC * 64);
-            const int c = nb * 32 + acc32_col(lane);
-            const float bias = to_f(bq[c]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
+        gemm_stage<T, true, SPLIT>(
+            HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q, (int64_t)nkC * 64,
+            opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg, (int64_t)nkC * 64,
+            [&](int nb, int v, float x1, float x2) {
+                const int c = nb * 32 + acc32_col(lane);
                 const int nn = n0 + acc32_row(v, lane);
                 if (nn < N) {
-                    qo[(int64_t)nn * HD + c] = a1[v] + bias;
-                    go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(a2[v]));
+                    qo[(int64_t)nn * HD + c] = x1 + to_f(bq[c]);
+                    go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(x2));
                 }
-            }
-            f32x16_t a3 = zero16(), a4 = zero16();
-            gemm2<T, SPLIT>(a3, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k + (int64_t)nb * nkC * 64,
-                         a4, opK, opKl, L.ldC, nkC, p.pk + p.off.w_v + (int64_t)nb * nkC * 64);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int nn = n0 + acc32_row(v, lane);
-                if (nn < N) {
-                    ko[(int64_t)nn * HD + c] = a3[v];
-                    vo[vt_at(acc32_row(v, lane), c)] = from_f<T>(a4[v]);
+            });
+        gemm_stage<T, true, SPLIT>(
+            HD / 32, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
+            opK, opKl, L.ldC, nkC, p.pk + p.off.w_v, (int64_t)nkC * 64,
+            [&](int nb, int v, float x1, float x2) {
+                const int c = nb * 32 + acc32_col(lane);
+                const int r = acc32_row(v, lane);
+                if (n0 + r < N) {
+                    ko[(int64_t)(n0 + r) * HD + c] = x1;
+                    vo[vt_at(r, c)] = from_f<T>(x2);
                 }
-            }
-        }
+            });
     } else {
         for (int pass = 0; pass < 2; ++pass) {
             const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
-            for (int nb = wave; nb < HD / 32; nb += 4) {
-                f32x16_t a1 = zero16(), a2 = zero16();
-                gemm2<T, SPLIT>(a1, opQ, opQl, L.ldC, nkC, p.pk + off1 + (int64_t)nb * nkC * 64,
-                             a2, opQ, opQl, L.ldC, nkC, p.pk + off2 + (int64_t)nb * nkC * 64);
-                const int c = nb * 32 + acc32_col(lane);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
+            gemm_stage<T, true, SPLIT>(
+                HD / 32, opQ, opQl, L.ldC, nkC, p.pk + off1, (int64_t)nkC * 64,
+                opQ, opQl, L.ldC, nkC, p.pk + off2, (int64_t)nkC * 64,
+                [&](int nb, int v, float x1, float x2) {
+                    const int c = nb * 32 + acc32_col(lane);
                     const int r = acc32_row(v, lane);
-                    hb[r * L.hp + c] = a1[v];
+                    hb[r * L.hp + c] = x1;
                     const int nn = n0 + r;
                     if (nn < N) {
                         if (pass == 0)
-                            go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(a2[v]));
+                            go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(x2));
                         else
-                            vo[vt_at(r, c)] = from_f<T>(a2[v]);
+                            vo[vt_at(r, c)] = from_f<T>(x2);
                     }
-                }
-            }
+                });
             __syncthreads();
-            head_rms_rotary<T>(p, hb, L.hp, n0, pass == 0 ? qo : ko);
+            head_rms_rotary<T, TPR>(p, hb, L.hp, n0, pass == 0 ? qo : ko);
             __syncthreads();
         }
     }

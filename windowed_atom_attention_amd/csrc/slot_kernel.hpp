@@ -78,21 +78,6 @@ __host__ __device__ inline SlotLayout slot_layout(int H, int V, int style) {
 
 __host__ __device__ inline int slot_spl(int K) { return K <= 16 ? 1 : (K <= 128 ? 8 : 16); }
 
-template <typename T>
-__device__ __forceinline__ void unpack16(uint4 v, float *out) {
-    if constexpr (sizeof(T) == 4) {
-        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
-        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
-    } else {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(w[i] << 16);
-            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-}
-
 // P operand (probabilities, fp32 in LDS) as a 16-byte chunk of T.
 template <typename T>
 __device__ __forceinline__ uint4 p_chunk(const float *src);
