@@ -96,14 +96,14 @@ def _traffic(kernel, workload):
 # Kernel symbols of libatomattn, as they appear in a rocprofv3 trace, and the
 # names the library's own profiler gives them.
 KERNEL_SYMBOLS = {"k_slot": "slot_attention", "k_prep": "prep", "k_post": "post",
-                  "k_pool": "pool", "k_pack": "pack", "k_token_proj": "token_proj",
+                  "k_pool_fix": "pool", "k_pack": "pack", "k_token_proj": "token_proj",
                   "k_vt": "vt", "k_masks": "masks"}
 
 
 def kernel_of(symbol):
     """Library kernel name of a trace symbol (demangled or mangled), else None."""
     import re
-    m = re.search(r"k_(slot|prep|post|pool|pack|token_proj|vt|masks)(?![a-z_])", symbol)
+    m = re.search(r"k_(slot|prep|post|pool_fix|pack|token_proj|vt|masks)(?![a-z_])", symbol)
     return KERNEL_SYMBOLS["k_" + m.group(1)] if m else None
 
 

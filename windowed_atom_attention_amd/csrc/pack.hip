@@ -12,10 +12,16 @@ namespace waa {
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // the job of the workgroup's first unit (uniform: scalar reads of the
+    // argument block), then of this thread's unit (a job spans at least 128
+    // units, so at most a step or two further)
+    const int64_t u0 = (int64_t)blockIdx.x * 256;
+    int j = 0;
+    while (j + 1 < a.njobs && u0 >= a.job[j + 1].dst)
+        ++j;
+    const int64_t u = u0 + threadIdx.x;
     if (u >= a.total)
         return;
-    int j = 0;
     while (j + 1 < a.njobs && u >= a.job[j + 1].dst)
         ++j;
     const PackJob &jb = a.job[j];
