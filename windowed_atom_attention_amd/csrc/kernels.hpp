@@ -51,6 +51,9 @@ struct BlockArgs {
     // count, last key, last count)
     float *pool_sum;
     int *pool_int;
+    // post kernel: stream the whole transition width in one pass (set by
+    // its launcher)
+    int post_wide;
     // outputs
     void *hidden, *attention, *token_output, *position_update;
     int32_t *status;

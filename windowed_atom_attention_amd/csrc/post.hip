@@ -28,18 +28,23 @@ struct PostLayout {
     size_t o_st, o_us, o_key, o_seg, o_opC, o_opC2, o_opU, o_opZ, o_opH, total;
 };
 
-// Transition width handled per pass: h is staged kMC columns at a time.
+// Transition width handled per pass (h is staged that many columns at a
+// time): 128, or all of M when the grid has at most one tile per CU and LDS
+// allows (then LDS does not limit occupancy).
 constexpr int kMC = 128;
+__host__ __device__ inline int post_pass_width(const Dims &d, int wide) {
+    return wide ? d.M : (d.M < kMC ? d.M : kMC);
+}
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-__host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int style) {
+__host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int style, int wide) {
     PostLayout L;
     L.xp = d.C + 4;
     L.ldS = d.S + 16 / esz;
     L.ldC = d.C + 16 / esz;
     L.ldHD = d.H * d.D + 16 / esz;
-    L.ldH = (d.M < kMC ? d.M : kMC) + 16 / esz;
+    L.ldH = post_pass_width(d, wide) + 16 / esz;
     size_t o = 32 * (size_t)L.xp * 4;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
@@ -59,7 +64,7 @@ __host__ __device__ inline PostLayout post_layout(const Dims &d, int esz, int st
 }
 
 size_t post_lds_bytes(const Dims &d, int dtype, int style) {
-    return post_layout(d, dtype ? 2 : 4, style).total;
+    return post_layout(d, dtype ? 2 : 4, style, 0).total;
 }
 
 // 256 threads: four waves, TPR = 8 threads per tile row.
@@ -75,7 +80,8 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     const int n = n0 + row;
     const bool inb = n < N;
     constexpr int E = 16 / sizeof(T);
-    const PostLayout L = post_layout(d, sizeof(T), STYLE);
+    const PostLayout L = post_layout(d, sizeof(T), STYLE, p.post_wide);
+    const int MCW = post_pass_width(d, p.post_wide);
     float *xs = reinterpret_cast<float *>(smem);
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
@@ -273,22 +279,22 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     }
     __syncthreads();
     // x2 = x1 + g_tr * (h @ w_ff_out), h = SiLU(z @ w_ff_gate) * (z @ w_ff_up),
-    // with h staged kMC columns at a time. Output columns go in groups of
+    // with h staged MCW columns at a time. Output columns go in groups of
     // 128 (one 32-column block per wave), so each wave carries its block of
-    // h @ w_ff_out in registers across the passes; with C > 128 and M > kMC
+    // h @ w_ff_out in registers across the passes; with C > 128 and M > MCW
     // the h chunks are recomputed per group. hidden = select(usable, x2, 0).
     {
         constexpr int KC = Mma32<T>::KC;
         T *hid = reinterpret_cast<T *>(p.hidden);
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[1] : p.off.w_mod[5];
-        const bool single = M <= kMC;
+        const bool single = M <= MCW;
         for (int cg = 0; cg < C / 32; cg += 4) {
             const int nb = cg + wave;
             const bool own = nb < C / 32;
             f32x16_t acc = zero16(), ga = zero16();
-            for (int m0 = 0; m0 < M; m0 += kMC) {
-                const int mc = M - m0 < kMC ? M - m0 : kMC;
+            for (int m0 = 0; m0 < M; m0 += MCW) {
+                const int mc = M - m0 < MCW ? M - m0 : MCW;
                 if (cg == 0 || !single) {
                     if (m0 > 0 || cg > 0)
                         __syncthreads(); // the previous chunk of h has been consumed
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                 if (!own)
                     continue;
                 const uint4 *wo = p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64;
-                if (m0 + kMC >= M)
+                if (m0 + MCW >= M)
                     gemm2<T>(acc, opH, nullptr, L.ldH, mc / KC, wo,
                              ga, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
                 else
@@ -386,21 +392,22 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         }
         if (nseg > 0) {
             T *tout = reinterpret_cast<T *>(p.token_output);
-            for (int nb = wave; nb < d.U / 32; nb += 4) {
-                f32x16_t a1 = zero16();
-                gemm1<T>(a1, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb * nkC * 64);
-                int sv[16];
+            int sv[16]; // segment of each accumulator row of the lane
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    sv[v] = segid[acc32_row(v, lane)];
-                    a1[v] = fmaxf(a1[v], 0.0f);
-                }
+            for (int v = 0; v < 16; ++v)
+                sv[v] = segid[acc32_row(v, lane)];
+            // segment sums of one ReLU'd 32-column block: the lane's 16 rows,
+            // then its partner lane's (lane ^ 32) other 16 rows
+            auto pool_block = [&](f32x16_t &acc, int nb) {
                 const int col = nb * 32 + acc32_col(lane);
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[v] = fmaxf(acc[v], 0.0f);
                 for (int s = 0; s < nseg; ++s) {
                     float part = 0.0f;
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        part += sv[v] == s ? a1[v] : 0.0f;
+                        part += sv[v] == s ? acc[v] : 0.0f;
                     part += __shfl_xor(part, 32);
                     if (lane < 32) {
                         if (s == 0)
@@ -410,6 +417,22 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                         else
                             tout[(int64_t)skey[s] * d.U + col] = from_f<T>(part / (float)scnt[s]);
                     }
+                }
+            };
+            // two column blocks per GEMM call where the wave has two left
+            const int nbU = d.U / 32;
+            for (int nb0 = wave; nb0 < nbU; nb0 += 8) {
+                const int nb1 = nb0 + 4;
+                f32x16_t a1 = zero16(), a2 = zero16();
+                const uint4 *w0 = p.pk + p.off.w_pool + (int64_t)nb0 * nkC * 64;
+                if (nb1 < nbU) {
+                    gemm2<T>(a1, opZ, nullptr, L.ldC, nkC, w0,
+                             a2, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb1 * nkC * 64);
+                    pool_block(a1, nb0);
+                    pool_block(a2, nb1);
+                } else {
+                    gemm1<T>(a1, opZ, nullptr, L.ldC, nkC, w0);
+                    pool_block(a1, nb0);
                 }
             }
         }
@@ -456,7 +479,10 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
                        hipStream_t s) {
     const int N = a.d.B * a.d.A;
     const int grid = (N + 31) / 32;
-    const size_t lds = post_lds_bytes(a.d, dtype, style);
+    BlockArgs b = a;
+    const int esz = dtype ? 2 : 4;
+    b.post_wide = grid <= device_cus() && post_layout(a.d, esz, style, 1).total <= kMaxLds;
+    const size_t lds = post_layout(a.d, esz, style, b.post_wide).total;
     const void *fn = nullptr;
 #define WAA_PICK(T, ST, SG) fn = (const void *)k_post<T, ST, SG>
     if (dtype == 0) {
@@ -468,7 +494,7 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
     }
 #undef WAA_PICK
     allow_lds(fn, lds);
-    void *args[] = {(void *)&a};
+    void *args[] = {(void *)&b};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
     if (e != hipSuccess)
         return e;
