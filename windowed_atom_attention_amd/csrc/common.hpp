@@ -200,18 +200,19 @@ template <typename T> constexpr int pad16() { return 16 / (int)sizeof(T); }
 //    twice the MFMA work).
 // B: packed weight blocks (see pack.hip): chunk kc of the column block at
 //    B[kc*64 + lane], 16 bytes per lane, read from L2.
-// Software pipeline: kPipe B chunks per product are in flight; each chunk is
-// consumed and its register refilled with the chunk kPipe ahead. Every load
+// Software pipeline: P B chunks per product are in flight; each chunk is
+// consumed and its register refilled with the chunk P ahead. Every load
 // is unconditional (indices clamp to the last chunk, so the tail re-reads
 // it), which lets the compiler wait for exactly the chunk it needs instead
 // of draining all loads; the A chunks of a group are read from LDS together.
-constexpr int kPipe = 4;
-template <typename T, bool DUAL, bool SPLIT>
+// P: pipeline depth in 16-byte chunks per product (4 by default; 2 saves
+// registers where that lets more workgroups fit a CU).
+template <typename T, bool DUAL, bool SPLIT, int P = 4>
 __device__ __forceinline__ void gemm_pipe(f32x16_t &acc1, const T *A1, const T *A1lo,
                                           int lda1, int nk1, const uint4 *__restrict__ B1,
                                           f32x16_t &acc2, const T *A2, const T *A2lo,
                                           int lda2, int nk2, const uint4 *__restrict__ B2) {
-    constexpr int KC = Mma32<T>::KC, P = kPipe;
+    constexpr int KC = Mma32<T>::KC;
     const int lane = threadIdx.x & 63;
     const int o1 = (lane & 31) * lda1 + (lane >> 5) * Mma32<T>::HALF;
     const int o2 = DUAL ? (lane & 31) * lda2 + (lane >> 5) * Mma32<T>::HALF : 0;
@@ -262,18 +263,18 @@ __device__ __forceinline__ void gemm_pipe(f32x16_t &acc1, const T *A1, const T *
     }
 }
 
-template <typename T, bool SPLIT = false>
+template <typename T, bool SPLIT = false, int P = 4>
 __device__ __forceinline__ void gemm2(f32x16_t &acc1, const T *A1, const T *A1lo, int lda1,
                                       int nk1, const uint4 *__restrict__ B1, f32x16_t &acc2,
                                       const T *A2, const T *A2lo, int lda2, int nk2,
                                       const uint4 *__restrict__ B2) {
-    gemm_pipe<T, true, SPLIT>(acc1, A1, A1lo, lda1, nk1, B1, acc2, A2, A2lo, lda2, nk2, B2);
+    gemm_pipe<T, true, SPLIT, P>(acc1, A1, A1lo, lda1, nk1, B1, acc2, A2, A2lo, lda2, nk2, B2);
 }
 
-template <typename T, bool SPLIT = false>
+template <typename T, bool SPLIT = false, int P = 4>
 __device__ __forceinline__ void gemm1(f32x16_t &acc, const T *A, const T *Alo, int lda, int nk,
                                       const uint4 *__restrict__ B) {
-    gemm_pipe<T, false, SPLIT>(acc, A, Alo, lda, nk, B, acc, A, Alo, lda, 0, B);
+    gemm_pipe<T, false, SPLIT, P>(acc, A, Alo, lda, nk, B, acc, A, Alo, lda, 0, B);
 }
 
 // Store x into a split operand pair: hi = x rounded to T, lo = the rest
@@ -315,7 +316,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // then epi(nb, v, x1[v], x2[v]) for accumulator elements v of the lane
 // (row acc32_row(v, lane), column nb*32 + acc32_col(lane)). B1[nb] starts
 // at B1 + nb * bs1 (16-byte units).
-template <typename T, bool DUAL, bool SPLIT, typename Epi>
+template <typename T, bool DUAL, bool SPLIT, int P = 4, typename Epi>
 __device__ __forceinline__ void gemm_stage(int nblocks, const T *A1, const T *A1lo, int lda1,
                                            int nk1, const uint4 *B1, int64_t bs1,
                                            const T *A2, const T *A2lo, int lda2, int nk2,
@@ -323,7 +324,7 @@ __device__ __forceinline__ void gemm_stage(int nblocks, const T *A1, const T *A1
     const int wave = threadIdx.x >> 6;
     for (int nb = wave; nb < nblocks; nb += 4) {
         f32x16_t a1 = zero16(), a2 = zero16();
-        gemm_pipe<T, DUAL, SPLIT>(a1, A1, A1lo, lda1, nk1, B1 + nb * bs1,
+        gemm_pipe<T, DUAL, SPLIT, P>(a1, A1, A1lo, lda1, nk1, B1 + nb * bs1,
                                   a2, A2, A2lo, lda2, nk2, DUAL ? B2 + nb * bs2 : B1);
 #pragma unroll
         for (int v = 0; v < 16; ++v)

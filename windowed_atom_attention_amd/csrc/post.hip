@@ -69,9 +69,12 @@ size_t post_lds_bytes(const Dims &d, int dtype, int style) {
 
 // 256 threads: four waves, TPR = 8 threads per tile row.
 template <typename T, int STYLE, int STAGE>
-__global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NT = 256, TPR = NT / 32;
+    // GEMM pipeline depth: 2 for bf16 keeps the kernel at three
+    // workgroups per CU
+    constexpr int PP = sizeof(T) == 2 ? 2 : 4;
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D, M = d.M;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
         const int nvC = C / E, nvS = S / E, nvH = HD / E;
         const int nvmax = nvC > nvS ? (nvC > nvH ? nvC : nvH) : (nvS > nvH ? nvS : nvH);
-        constexpr int RV = 4; // vectors per array and thread in one round
+        constexpr int RV = sizeof(T) == 2 ? 2 : 4; // vectors per array and thread in one round
         float csum = 0.0f;
         for (int base = sub; base < nvmax; base += RV * TPR) {
             uint4 va[RV], vc[RV], vo[RV], vg[RV];
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
     {
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
-        gemm_stage<T, true, false>(
+        gemm_stage<T, true, false, PP>(
             C / 32, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao, (int64_t)nkHD * 64,
             opC, nullptr, L.ldS, nkS, p.pk + offg, (int64_t)nkS * 64,
             [&](int nb, int v, float x1, float x2) {
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
         const T *opz = STYLE == STYLE_AF3 ? opC2 : opC;
         const int64_t o1 = STYLE == STYLE_AF3 ? p.off.w_scale[2] : p.off.w_mod[3];
         const int64_t o2 = STYLE == STYLE_AF3 ? p.off.w_shift[2] : p.off.w_mod[4];
-        gemm_stage<T, true, false>(
+        gemm_stage<T, true, false, PP>(
             C / 32, opz, nullptr, L.ldS, nkS, p.pk + o1, (int64_t)nkS * 64,
             opz, nullptr, L.ldS, nkS, p.pk + o2, (int64_t)nkS * 64,
             [&](int nb, int v, float x1, float x2) {
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                 if (cg == 0 || !single) {
                     if (m0 > 0 || cg > 0)
                         __syncthreads(); // the previous chunk of h has been consumed
-                    gemm_stage<T, true, false>(
+                    gemm_stage<T, true, false, PP>(
                         mc / 32, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + (int64_t)(m0 / 32) * nkC * 64,
                         (int64_t)nkC * 64, opZ, nullptr, L.ldC, nkC,
                         p.pk + p.off.ff_up + (int64_t)(m0 / 32) * nkC * 64, (int64_t)nkC * 64,
@@ -312,10 +315,10 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                     continue;
                 const uint4 *wo = p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64;
                 if (m0 + MCW >= M)
-                    gemm2<T>(acc, opH, nullptr, L.ldH, mc / KC, wo,
+                    gemm2<T, false, PP>(acc, opH, nullptr, L.ldH, mc / KC, wo,
                              ga, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
                 else
-                    gemm1<T>(acc, opH, nullptr, L.ldH, mc / KC, wo);
+                    gemm1<T, false, PP>(acc, opH, nullptr, L.ldH, mc / KC, wo);
             }
             if (own) {
                 const int c = nb * 32 + acc32_col(lane);
@@ -426,12 +429,12 @@ __global__ __launch_bounds__(256, 2) void k_post(BlockArgs p) {
                 f32x16_t a1 = zero16(), a2 = zero16();
                 const uint4 *w0 = p.pk + p.off.w_pool + (int64_t)nb0 * nkC * 64;
                 if (nb1 < nbU) {
-                    gemm2<T>(a1, opZ, nullptr, L.ldC, nkC, w0,
+                    gemm2<T, false, PP>(a1, opZ, nullptr, L.ldC, nkC, w0,
                              a2, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb1 * nkC * 64);
                     pool_block(a1, nb0);
                     pool_block(a2, nb1);
                 } else {
-                    gemm1<T>(a1, opZ, nullptr, L.ldC, nkC, w0);
+                    gemm1<T, false, PP>(a1, opZ, nullptr, L.ldC, nkC, w0);
                     pool_block(a1, nb0);
                 }
             }
