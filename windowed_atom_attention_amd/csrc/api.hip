@@ -140,7 +140,7 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
         return ATOM_ATTN_EUNSUPPORTED;
     const Dims dd{(int)d->B, (int)d->A, (int)d->T, (int)d->K, (int)d->C, (int)d->S,
                   (int)d->H, (int)d->D, (int)d->V, (int)d->M, (int)d->U};
-    if (prep_lds_bytes(dd, dtype, style) > kMaxLds ||
+    if (prep_lds_bytes(dd, dtype, style, stage) > kMaxLds ||
         post_lds_bytes(dd, dtype, style) > kMaxLds ||
         !slot_supported(dd, dtype, style))
         return ATOM_ATTN_EUNSUPPORTED;

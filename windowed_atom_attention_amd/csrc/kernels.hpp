@@ -112,7 +112,7 @@ hipError_t launch_masks(const Dims &d, const uint8_t *valid,
                         hipStream_t s);
 
 // LDS bytes each kernel needs for these sizes (host-side shape checks).
-size_t prep_lds_bytes(const Dims &d, int dtype, int style);
+size_t prep_lds_bytes(const Dims &d, int dtype, int style, int stage);
 size_t post_lds_bytes(const Dims &d, int dtype, int style);
 size_t token_proj_lds_bytes(const Dims &d, int dtype);
 size_t slot_lds_bytes(const Dims &d, int dtype, int style);

@@ -97,44 +97,53 @@ hipError_t launch_token_proj(const BlockArgs &a, int dtype, hipStream_t s) {
 // (c_j or SiLU(c), q_in, kv_in) are split into hi + lo parts for bf16 so
 // that the logits path keeps ~16 mantissa bits; fp32 tiles are single.
 struct PrepLayout {
-    int xp, hp, ldS, ldC;
-    size_t o_st, o_us, o_rb, o_cr, o_opA, o_opAl, o_opQ, o_opQl, o_opK, o_opKl, o_hb, total;
+    int hp, ldS, ldC;
+    size_t o_xh, o_xl, o_st, o_us, o_rb, o_cr, o_opA, o_opAl, o_hb, o_opQ, o_opQl, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-__host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int style) {
+// LDS of one 32-row tile:
+//  x0 in the storage type (exact for an encoder: x0 is the atom row; a bf16
+//  decoder keeps the rest of the fp32 sum atom + token projection in a
+//  second tile); row statistics, usability, atom/batch index per row; the
+//  raw condition (AF3: LN(c) * cond_scale[j] is built twice); the A operand
+//  tile (hi + lo in bf16), which ESMFold2 reuses as the fp32 staging tile
+//  of its Q/K projections; the Q/K/V/G input tile (hi + lo in bf16).
+__host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int style, int stage) {
     PrepLayout L;
     const bool split = esz == 2;
-    L.xp = d.C + 4;
     L.hp = d.H * d.D + 4;
     L.ldS = d.S + 16 / esz;
     L.ldC = d.C + 16 / esz;
     const size_t tS = align16(32 * (size_t)L.ldS * esz), tC = align16(32 * (size_t)L.ldC * esz);
-    size_t o = 32 * L.xp * 4;
+    size_t o = 0;
+    L.o_xh = o; o += tC;
+    L.o_xl = o;
+    if (split && stage == STAGE_DECODER)
+        o += tC;
     L.o_st = o; o += 32 * 4 * 4;
     L.o_us = o; o += 32;
     L.o_rb = o; o += 64 * 4; // per row: atom index within its batch, then batch
-    L.o_cr = o; o += tS;      // the sanitised condition, storage type
-    L.o_opA = o; o += tS;
-    L.o_opAl = o; if (split) o += tS;
+    L.o_cr = o;
+    if (style == STYLE_AF3)
+        o += tS;
+    L.o_opA = L.o_hb = o;
+    L.o_opAl = o + tS;
+    size_t ra = (split ? 2 : 1) * tS;
+    if (style == STYLE_ESM && 32 * (size_t)L.hp * 4 > ra)
+        ra = 32 * (size_t)L.hp * 4;
+    o = align16(o + ra);
     L.o_opQ = o; o += tC;
-    L.o_opQl = o; if (split) o += tC;
-    L.o_opK = o; L.o_opKl = o;
-    if (style == STYLE_AF3) {
+    L.o_opQl = o;
+    if (split)
         o += tC;
-        L.o_opKl = o;
-        if (split) o += tC;
-    }
-    L.o_hb = o;
-    if (style == STYLE_ESM)
-        o = align16(o + 32 * (size_t)L.hp * 4);
     L.total = o;
     return L;
 }
 
-size_t prep_lds_bytes(const Dims &d, int dtype, int style) {
-    return prep_layout(d, dtype ? 2 : 4, style).total;
+size_t prep_lds_bytes(const Dims &d, int dtype, int style, int stage) {
+    return prep_layout(d, dtype ? 2 : 4, style, stage).total;
 }
 
 // Per-head RMS normalisation and half-split rotary of the 32 x H*D tile in
@@ -182,11 +191,20 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
     }
 }
 
+// Workgroups per CU the LDS layout allows: three for bf16 except the AF3
+// decoder (whose x0 needs a hi + lo pair), two otherwise.
+template <typename T, int STYLE, int STAGE>
+constexpr int prep_wgs() {
+    return sizeof(T) == 2 && !(STYLE == STYLE_AF3 && STAGE == STAGE_DECODER) ? 3 : 2;
+}
+
 // 256 threads: four waves, TPR = 8 threads per tile row.
 template <typename T, int STYLE, int STAGE>
-__global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
+__global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NT = 256, TPR = NT / 32;
+    // GEMM pipeline depth: 2 where three workgroups share a CU (registers)
+    constexpr int PP = (prep_wgs<T, STYLE, STAGE>() == 3) ? 2 : 4;
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -196,6 +214,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     const bool inb = n < N;
     constexpr int E = 16 / sizeof(T);
     constexpr bool SPLIT = sizeof(T) == 2;
+    constexpr bool XLO = SPLIT && STAGE == STAGE_DECODER; // x0 kept as hi + lo
 
     if (STAGE == STAGE_ENCODER) {
         T *to = reinterpret_cast<T *>(p.token_output);
@@ -207,19 +226,25 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     if (p.status != nullptr && blockIdx.x == 0 && tid == 0)
         p.status[0] = 0;
 
-    const PrepLayout L = prep_layout(d, sizeof(T), STYLE);
-    float *xs = reinterpret_cast<float *>(smem);
+    const PrepLayout L = prep_layout(d, sizeof(T), STYLE, STAGE);
+    T *xh = reinterpret_cast<T *>(smem + L.o_xh);
+    T *xl = XLO ? reinterpret_cast<T *>(smem + L.o_xl) : nullptr;
     float *st = reinterpret_cast<float *>(smem + L.o_st);
     uint8_t *us = smem + L.o_us;
     int *rb = reinterpret_cast<int *>(smem + L.o_rb);
     T *crs = reinterpret_cast<T *>(smem + L.o_cr);
     T *opA = reinterpret_cast<T *>(smem + L.o_opA);
     T *opAl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opAl) : nullptr;
+    float *hb = reinterpret_cast<float *>(smem + L.o_hb);
     T *opQ = reinterpret_cast<T *>(smem + L.o_opQ);
     T *opQl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opQl) : nullptr;
-    T *opK = reinterpret_cast<T *>(smem + L.o_opK);
-    T *opKl = SPLIT ? reinterpret_cast<T *>(smem + L.o_opKl) : nullptr;
-    float *hb = reinterpret_cast<float *>(smem + L.o_hb);
+    // x0 of tile element (r, c)
+    auto x0 = [&](int r, int c) -> float {
+        float v = to_f(xh[r * L.ldC + c]);
+        if (XLO)
+            v += to_f(xl[r * L.ldC + c]);
+        return v;
+    };
 
     // Row loads first (unconditional, rows past the end read row 0; values
     // of unusable atoms are replaced by zeros: selected, never multiplied),
@@ -228,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
     const T *ar = reinterpret_cast<const T *>(p.atom) + nc * C;
     const T *cr = reinterpret_cast<const T *>(p.condition) + nc * S;
     const int nvC = C / E, nvS = S / E, nvmax = nvC > nvS ? nvC : nvS;
-    constexpr int RV = 4; // vectors per array and thread in one round
+    constexpr int RV = sizeof(T) == 2 ? 2 : 4; // vectors per array and thread in one round
     uint4 va[RV], vc[RV];
 #pragma unroll
     for (int j = 0; j < RV; ++j) {
@@ -251,8 +276,9 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
             p.usable[n] = u;
     }
     const float *tp = p.tokproj + ((int64_t)b * d.T + (u ? tk : 0)) * C;
+    float xsum = 0.0f, csum = 0.0f;
     for (int base = sub; base < nvmax; base += RV * TPR) {
-        if (base != sub) { // later rounds (C or S above 4 * TPR vectors)
+        if (base != sub) { // later rounds (wide C or S)
 #pragma unroll
             for (int j = 0; j < RV; ++j) {
                 const int vi = base + j * TPR;
@@ -272,41 +298,51 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
                         xv[e] += tp[vi * E + e];
                 }
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    xs[row * L.xp + vi * E + e] = u ? xv[e] : 0.0f;
+                for (int e = 0; e < E; ++e) {
+                    const float x = u ? xv[e] : 0.0f;
+                    if (XLO)
+                        put_split<T>(xh, xl, row * L.ldC + vi * E + e, x);
+                    else
+                        xh[row * L.ldC + vi * E + e] = from_f<T>(x); // exact
+                    xsum += x;
+                }
             }
-            if (vi < nvS)
-                *reinterpret_cast<uint4 *>(crs + row * L.ldS + vi * E) =
-                    u ? vc[j] : make_uint4(0, 0, 0, 0);
+            if (vi < nvS) {
+                const uint4 cvv = u ? vc[j] : make_uint4(0, 0, 0, 0);
+                float cv[E];
+                unpack16<T>(cvv, cv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    csum += cv[e];
+                    if (STYLE == STYLE_ESM) // A operand of the modulation: SiLU(c)
+                        put_split<T>(opA, opAl, row * L.ldS + vi * E + e, silu_f(cv[e]));
+                }
+                if (STYLE == STYLE_AF3)
+                    *reinterpret_cast<uint4 *>(crs + row * L.ldS + vi * E) = cvv;
+            }
         }
     }
-    __syncthreads();
-    // the sanitised condition row (zero for unusable atoms)
-    auto cond = [&](int c) -> float { return to_f(crs[row * L.ldS + c]); };
-
-    // row statistics of x0 (and of c for AF3)
+    // row statistics of x0 (and of c for AF3), each thread over its own
+    // entries of the tiles (written above by the same thread)
     {
-        const float *xr = xs + row * L.xp;
         if (STYLE == STYLE_AF3) {
-            float s = 0.0f;
-            for (int c = sub; c < C; c += TPR)
-                s += xr[c];
-            const float mean = sum8(s) / (float)C;
+            const float mean = sum8(xsum) / (float)C;
             float q = 0.0f;
-            for (int c = sub; c < C; c += TPR) {
-                const float t = xr[c] - mean;
-                q += t * t;
-            }
+            for (int vi = sub; vi < nvC; vi += TPR)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float t = x0(row, vi * E + e) - mean;
+                    q += t * t;
+                }
             const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
-            float s2 = 0.0f;
-            for (int c = sub; c < S; c += TPR)
-                s2 += cond(c);
-            const float mc = sum8(s2) / (float)S;
+            const float mc = sum8(csum) / (float)S;
             float q2 = 0.0f;
-            for (int c = sub; c < S; c += TPR) {
-                const float t = cond(c) - mc;
-                q2 += t * t;
-            }
+            for (int vi = sub; vi < nvS; vi += TPR)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float t = to_f(crs[row * L.ldS + vi * E + e]) - mc;
+                    q2 += t * t;
+                }
             const float rc = 1.0f / sqrtf(sum8(q2) / (float)S + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = mean; st[row * 4 + 1] = rstd;
@@ -314,8 +350,12 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
             }
         } else {
             float q = 0.0f;
-            for (int c = sub; c < C; c += TPR)
-                q += xr[c] * xr[c];
+            for (int vi = sub; vi < nvC; vi += TPR)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float t = x0(row, vi * E + e);
+                    q += t * t;
+                }
             const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
@@ -323,50 +363,8 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
             }
         }
     }
-    __syncthreads();
 
     const int nkS = S / Mma32<T>::KC, nkC = C / Mma32<T>::KC;
-    if (STYLE == STYLE_AF3) {
-        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
-        const T *bscale = reinterpret_cast<const T *>(p.b_scale);
-        for (int j = 0; j < 2; ++j) {
-            {
-                const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
-                for (int c = sub; c < S; c += TPR)
-                    put_split<T>(opA, opAl, row * L.ldS + c,
-                                 (cond(c) - mc) * rc * to_f(cscale[j * S + c]));
-            }
-            __syncthreads();
-            T *dst = j == 0 ? opQ : opK;
-            T *dstl = j == 0 ? opQl : opKl;
-            gemm_stage<T, true, SPLIT>(
-                C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
-                opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j], (int64_t)nkS * 64,
-                [&](int nb, int v, float x1, float x2) {
-                    const int c = nb * 32 + acc32_col(lane);
-                    const int r = acc32_row(v, lane);
-                    const float ln = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
-                    put_split<T>(dst, dstl, r * L.ldC + c,
-                                 ln * sigmoid_f(x1 + to_f(bscale[j * C + c])) + x2);
-                });
-            __syncthreads();
-        }
-    } else {
-        for (int c = sub; c < S; c += TPR)
-            put_split<T>(opA, opAl, row * L.ldS + c, silu_f(cond(c)));
-        __syncthreads();
-        gemm_stage<T, true, SPLIT>(
-            C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0], (int64_t)nkS * 64,
-            opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1], (int64_t)nkS * 64,
-            [&](int nb, int v, float x1, float x2) {
-                const int c = nb * 32 + acc32_col(lane);
-                const int r = acc32_row(v, lane);
-                const float rm = xs[r * L.xp + c] * st[r * 4 + 1];
-                put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + x2) + x1);
-            });
-        __syncthreads();
-    }
-
     // Q/K/V/G projections. Q and K (the logit operands) are stored in fp32,
     // V and G in the storage dtype.
     float *qo = reinterpret_cast<float *>(p.q);
@@ -379,8 +377,37 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
         return ((int64_t)rb[32 + r] * HD + c) * vtp + rb[r];
     };
     if (STYLE == STYLE_AF3) {
+        // A_j(x0) = LN(x0) * sigmoid(a_j @ w_scale[j] + b_scale[j]) + a_j @ w_shift[j]
+        // with a_j = LN(c) * cond_scale[j]; A_0 feeds Q and G, A_1 K and V.
+        // Order: a_0 | A_0 | Q, G and a_1 | A_1 | K, V (one operand tile for
+        // both A_j).
+        const T *cscale = reinterpret_cast<const T *>(p.cond_scale);
+        const T *bscale = reinterpret_cast<const T *>(p.b_scale);
         const T *bq = reinterpret_cast<const T *>(p.b_q);
-        gemm_stage<T, true, SPLIT>(
+        auto build_a = [&](int j) {
+            const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
+            for (int c = sub; c < S; c += TPR)
+                put_split<T>(opA, opAl, row * L.ldS + c,
+                             (to_f(crs[row * L.ldS + c]) - mc) * rc * to_f(cscale[j * S + c]));
+        };
+        auto adaln = [&](int j) {
+            gemm_stage<T, true, SPLIT, PP>(
+                C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
+                opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j], (int64_t)nkS * 64,
+                [&](int nb, int v, float x1, float x2) {
+                    const int c = nb * 32 + acc32_col(lane);
+                    const int r = acc32_row(v, lane);
+                    const float ln = (x0(r, c) - st[r * 4 + 0]) * st[r * 4 + 1];
+                    put_split<T>(opQ, opQl, r * L.ldC + c,
+                                 ln * sigmoid_f(x1 + to_f(bscale[j * C + c])) + x2);
+                });
+        };
+        __syncthreads(); // statistics of every row
+        build_a(0);
+        __syncthreads();
+        adaln(0);
+        __syncthreads();
+        gemm_stage<T, true, SPLIT, PP>(
             HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg, (int64_t)nkC * 64,
             [&](int nb, int v, float x1, float x2) {
@@ -391,9 +418,13 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
                     go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(x2));
                 }
             });
-        gemm_stage<T, true, SPLIT>(
-            HD / 32, opK, opKl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
-            opK, opKl, L.ldC, nkC, p.pk + p.off.w_v, (int64_t)nkC * 64,
+        build_a(1); // the A tile is free once A_0 is formed
+        __syncthreads();
+        adaln(1);
+        __syncthreads();
+        gemm_stage<T, true, SPLIT, PP>(
+            HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
+            opQ, opQl, L.ldC, nkC, p.pk + p.off.w_v, (int64_t)nkC * 64,
             [&](int nb, int v, float x1, float x2) {
                 const int c = nb * 32 + acc32_col(lane);
                 const int r = acc32_row(v, lane);
@@ -403,10 +434,22 @@ __global__ __launch_bounds__(256, 2) void k_prep(BlockArgs p) {
                 }
             });
     } else {
+        // in = RMS(x0) * (1 + m1) + m0, m = SiLU(c) @ w_mod[0..1]
+        __syncthreads(); // statistics and SiLU(c) of every row
+        gemm_stage<T, true, SPLIT, PP>(
+            C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0], (int64_t)nkS * 64,
+            opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1], (int64_t)nkS * 64,
+            [&](int nb, int v, float x1, float x2) {
+                const int c = nb * 32 + acc32_col(lane);
+                const int r = acc32_row(v, lane);
+                const float rm = x0(r, c) * st[r * 4 + 1];
+                put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + x2) + x1);
+            });
+        __syncthreads(); // the A tile becomes the projection staging tile hb
         for (int pass = 0; pass < 2; ++pass) {
             const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
-            gemm_stage<T, true, SPLIT>(
+            gemm_stage<T, true, SPLIT, PP>(
                 HD / 32, opQ, opQl, L.ldC, nkC, p.pk + off1, (int64_t)nkC * 64,
                 opQ, opQl, L.ldC, nkC, p.pk + off2, (int64_t)nkC * 64,
                 [&](int nb, int v, float x1, float x2) {
@@ -432,7 +475,7 @@ hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
                        hipStream_t s) {
     const int N = a.d.B * a.d.A;
     const int grid = (N + 31) / 32;
-    const size_t lds = prep_lds_bytes(a.d, dtype, style);
+    const size_t lds = prep_lds_bytes(a.d, dtype, style, stage);
     const void *fn = nullptr;
 #define WAA_PICK(T, ST, SG) fn = (const void *)k_prep<T, ST, SG>
     if (dtype == 0) {
