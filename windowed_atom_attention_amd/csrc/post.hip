@@ -288,7 +288,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
     // the h chunks are recomputed per group. hidden = select(usable, x2, 0).
     {
         constexpr int KC = Mma32<T>::KC;
-        T *hid = reinterpret_cast<T *>(p.hidden);
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[1] : p.off.w_mod[5];
         const bool single = M <= MCW;
@@ -328,13 +327,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
                     const int r = acc32_row(v, lane);
                     const float gate = STYLE == STYLE_AF3 ? sigmoid_f(ga[v] + bias) : ga[v];
                     const float x2 = xs[r * L.xp + c] + gate * acc[v];
-                    const float h = us[r] ? x2 : 0.0f;
-                    xs[r * L.xp + c] = h;
-                    const int nn = n0 + r;
-                    if (nn < N)
-                        hid[(int64_t)nn * C + c] = from_f<T>(h);
+                    xs[r * L.xp + c] = us[r] ? x2 : 0.0f;
                 }
             }
+        }
+    }
+    // hidden rows are complete in xs: each thread stores 16-byte pieces of
+    // its row (and, for the encoder, the same values as the pooling operand)
+    __syncthreads();
+    {
+        T *hrow = reinterpret_cast<T *>(p.hidden) + (int64_t)(inb ? n : 0) * C;
+        for (int vi = sub; vi < C / E; vi += TPR) {
+            T tmp[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                tmp[e] = from_f<T>(xs[row * L.xp + vi * E + e]);
+            uint4 v4;
+            __builtin_memcpy(&v4, tmp, 16);
+            if (inb)
+                *reinterpret_cast<uint4 *>(hrow + vi * E) = v4;
+            if (STAGE == STAGE_ENCODER)
+                *reinterpret_cast<uint4 *>(opZ + row * L.ldC + vi * E) = v4;
         }
     }
     if (STAGE == STAGE_ENCODER) {
@@ -344,16 +357,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
         // their means are written here; the first and the last segment may
         // continue in neighbouring tiles and go to this tile's record for
         // the pooling fix-up kernel.
-        __syncthreads(); // hidden rows complete in xs
-        for (int vi = sub; vi < C / E; vi += TPR) {
-            T tmp[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                tmp[e] = from_f<T>(xs[row * L.xp + vi * E + e]);
-            uint4 v4;
-            __builtin_memcpy(&v4, tmp, 16);
-            *reinterpret_cast<uint4 *>(opZ + row * L.ldC + vi * E) = v4;
-        }
         int *segid = reinterpret_cast<int *>(smem + L.o_seg);
         int *skey = segid + 32, *scnt = segid + 64, *snum = segid + 96;
         if (wave == 0) {
@@ -441,7 +444,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
         }
     }
     if (STAGE == STAGE_DECODER) {
-        __syncthreads();
         const float *xr = xs + row * L.xp;
         float s = 0.0f;
         for (int c = sub; c < C; c += TPR)
