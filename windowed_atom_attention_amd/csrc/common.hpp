@@ -300,6 +300,16 @@ __device__ __forceinline__ f32x4_t zero4() {
     return z;
 }
 
+// Zero the padding columns A .. vt_pitch(A)-1 of the transposed V rows
+// ([B][HD][pitch]); row i goes to workgroup i % nwg.
+template <typename T>
+__device__ __forceinline__ void zero_vt_pad(T *vt, int B, int HD, int A, int wg, int nwg) {
+    const int pitch = vt_pitch(A), w = pitch - A;
+    for (int64_t i = wg; i < (int64_t)B * HD; i += nwg)
+        for (int e = threadIdx.x; e < w; e += blockDim.x)
+            vt[i * pitch + A + e] = (T)0;
+}
+
 // Map the hardware dispatch order (round-robin over the 8 XCDs of MI355X)
 // to a logical block index such that consecutive logical blocks run on the
 // same XCD and share its L2. Bijective on [0, nblk).

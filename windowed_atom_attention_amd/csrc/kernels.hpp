@@ -17,8 +17,10 @@ struct Dims {
 
 // V is stored transposed per batch, [B][H*D][vt_pitch(A)], so that the slot
 // kernel's P V product reads 8 (bf16) or 4 (fp32) consecutive key rows of one
-// channel as one 16-byte vector.
-__host__ __device__ inline int vt_pitch(int A) { return (A + 7) & ~7; }
+// channel as one 16-byte vector. Columns A .. pitch-1 hold zeros (written by
+// the kernel that writes V): a 32-row P V chunk of a band that ends at the
+// batch's last atom then reads whole vectors, zeros past the end.
+__host__ __device__ inline int vt_pitch(int A) { return ((A + 7) & ~7) + 32; }
 
 // Offsets, in 16-byte units, of each packed weight matrix inside the packed
 // area of the workspace (-1 = absent).

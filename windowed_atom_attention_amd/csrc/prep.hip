@@ -225,6 +225,7 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
     }
     if (p.status != nullptr && blockIdx.x == 0 && tid == 0)
         p.status[0] = 0;
+    zero_vt_pad<T>(reinterpret_cast<T *>(p.v), d.B, HD, d.A, blockIdx.x, gridDim.x);
 
     const PrepLayout L = prep_layout(d, sizeof(T), STYLE, STAGE);
     T *xh = reinterpret_cast<T *>(smem + L.o_xh);

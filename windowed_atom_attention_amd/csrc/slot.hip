@@ -44,8 +44,8 @@ hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) 
     return hipGetLastError();
 }
 
-// Transposed copy of v ([B][A][HD] -> [B][HD][vt_pitch(A)]), for the
-// standalone slot-attention entry point.
+// Transposed copy of v ([B][A][HD] -> [B][HD][vt_pitch(A)], zero padding
+// included), for the standalone slot-attention entry point.
 template <typename T>
 __global__ __launch_bounds__(256) void k_vt(const T *v, T *vt, int B, int A, int HD,
                                             int pitch) {
@@ -57,6 +57,9 @@ __global__ __launch_bounds__(256) void k_vt(const T *v, T *vt, int B, int A, int
     const int64_t r = i - b * per;
     const int aa = (int)(r / HD), c = (int)(r - (int64_t)aa * HD);
     vt[(b * HD + c) * pitch + aa] = v[i];
+    if (i < (int64_t)B * HD) // row i of the transposed copy: its zero padding
+        for (int e = A; e < pitch; ++e)
+            vt[i * pitch + e] = (T)0;
 }
 
 hipError_t launch_vt(const void *v, void *vt, int B, int A, int HD, int dtype,

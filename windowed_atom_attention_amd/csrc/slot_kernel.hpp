@@ -91,23 +91,6 @@ template <> __device__ __forceinline__ uint4 p_chunk<bf16_t>(const float *src) {
                       pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
 }
 
-// 16 bytes of the transposed V row `src` starting at key row r (of A rows):
-// one vector load when all its rows exist, else row by row with zeros past
-// the batch's last atom (the pitch padding is never read).
-template <typename T>
-__device__ __forceinline__ uint4 vt_chunk(const T *src, int r, int A) {
-    constexpr int E = 16 / sizeof(T);
-    if (r + E <= A)
-        return *reinterpret_cast<const uint4 *>(src + r);
-    T tmp[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        tmp[e] = r + e < A ? src[r + e] : (T)0;
-    uint4 v;
-    __builtin_memcpy(&v, tmp, 16);
-    return v;
-}
-
 // NV: 16-byte vectors per AF3 pair row (V = NV * 16 / sizeof(T)); 1 for
 // ESMFold2, which has no pair input.
 template <typename T, int STYLE, int SPL, int DK, int NV>
@@ -119,6 +102,8 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     constexpr int VV = NV * E;                       // AF3 pair channels
     constexpr int NKQ = DK / 16;                     // fp32 k chunks of Q.K
     constexpr int NDB = DK / 16;                     // 16-wide output blocks of o
+    constexpr int NVC = kRMAX / KC;                  // P V k chunks of a full band chunk
+    constexpr int VG = NVC < 8 / NDB ? NVC : (8 / NDB > 0 ? 8 / NDB : 1); // V chunks per load batch (<= 8 vectors)
     constexpr int CBG = DK <= 32 ? 4 : (DK == 64 ? 2 : 1); // score blocks per load batch
     const int A = p.A, K = p.K, H = p.H, HD = H * DK;
     const int nqb = (A + kQB - 1) / kQB;
@@ -384,6 +369,23 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                 tag[q * kRMAX + rel[i] - jal] = k0 + i;
     }
 
+    // V operands (B of P V) of the band chunk starting at key row c0, k
+    // chunks kc0 .. kc0+VG-1 of its nkc, for head hw: chunk kc, output block
+    // t holds rows c0 + kc*KC + g*QU .. +E-1 of channel hw*DK + t*16 + l16.
+    // Chunks past the last re-read it; rows past the batch's last atom are
+    // the zero padding of the transposed rows (at most 31 past A). All VG
+    // chunks are in flight together.
+    auto load_v = [&](uint4 (&dst)[VG][NDB], int c0, int kc0, int nkc, int hw) {
+        const int hc = min(hw, H - 1);
+        const T *vrow = vtg + ((int64_t)b * HD + hc * DK) * vtp;
+#pragma unroll
+        for (int j = 0; j < VG; ++j) {
+            const int r = c0 + min(kc0 + j, nkc - 1) * KC + g * QU;
+#pragma unroll
+            for (int t = 0; t < NDB; ++t)
+                dst[j][t] = *reinterpret_cast<const uint4 *>(vrow + (int64_t)(t * 16 + l16) * vtp + r);
+        }
+    };
     for (int hg = 0; hg < H; hg += kHG) {
         const int hw = hg + wave; // this wave's head in the S and P V products
         const bool hv = hw < H;
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
         for (int c = 0; c < nch; ++c) {
             const int c0 = jal + c * kRMAX;
             const int rows = min(kRMAX, jhi + 1 - c0);
-            const int rpad = (rows + 31) / 32 * 32;
+            const int nkc = (rows + 31) / 32 * 32 / KC;
 #pragma unroll
             for (int hh = 0; hh < kHG; ++hh) {
                 if (hg + hh >= H)
@@ -541,14 +543,17 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
             __syncthreads();
             if (hv) {
                 const float *prow = twave + l16 * L.sp + g * QU;
-                const T *vrow = vtg + ((int64_t)b * HD + hw * DK) * vtp;
-                for (int kc = 0; kc < rpad / KC; ++kc) {
-                    const uint4 av = p_chunk<T>(prow + kc * KC);
-                    const int r = c0 + kc * KC + g * QU;
+                for (int kc0 = 0; kc0 < nkc; kc0 += VG) {
+                    uint4 vb[VG][NDB];
+                    load_v(vb, c0, kc0, nkc, hw);
 #pragma unroll
-                    for (int t = 0; t < NDB; ++t) {
-                        const uint4 bv = vt_chunk<T>(vrow + (int64_t)(t * 16 + l16) * vtp, r, A);
-                        Mma16<T>::mma(oacc[t], av, bv);
+                    for (int j = 0; j < VG; ++j) {
+                        if (kc0 + j < nkc) {
+                            const uint4 av = p_chunk<T>(prow + (kc0 + j) * KC);
+#pragma unroll
+                            for (int t = 0; t < NDB; ++t)
+                                Mma16<T>::mma(oacc[t], av, vb[j][t]);
+                        }
                     }
                 }
                 // leave this wave's P tile zero for the next chunk / head group
