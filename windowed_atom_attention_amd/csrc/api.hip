@@ -155,7 +155,7 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
 // ------------------------------------------------------------ workspace
 
 struct Layout {
-    size_t packed, q, k, v, g, o, usable, tokproj, pool_sum, pool_int, total;
+    size_t packed, q, k, v, g, o, usable, tokproj, pool_sum, pool_int, pbias, total;
     int64_t pack_units;
 };
 
@@ -245,6 +245,11 @@ Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
         L.pool_int = o;
         o = up256(o + ntile * 8 * 4);
     }
+    // AF3 pair bias of every slot, [N*K][4] fp32 (used when the projection
+    // kernel computes it)
+    L.pbias = o;
+    if (style == ATOM_ATTN_AF3)
+        o = up256(o + N * (size_t)d->K * 16);
     L.total = o;
     return L;
 }
@@ -358,8 +363,11 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.hidden = out->hidden; a.attention = out->attention;
     a.token_output = out->token_output; a.position_update = out->position_update;
     a.status = out->status;
+    a.pair_scale = par->pair_scale; a.w_pair = par->w_pair;
+    a.pbias = af3 && prep_hosts_pair_bias(a.d, dt, st, sg) ? (float *)(ws + L.pbias) : nullptr;
 
     SlotArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
     sa.B = a.d.B; sa.A = a.d.A; sa.K = a.d.K; sa.H = a.d.H; sa.D = a.d.D; sa.V = a.d.V;
     sa.eps = a.eps;
     sa.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d->D));
@@ -367,6 +375,7 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.usable = a.usable; sa.window_mask = in->window_mask; sa.key_index = in->key_index;
     sa.q = a.q; sa.k = a.k; sa.v = a.v;
     sa.pair = in->pair; sa.pair_scale = par->pair_scale; sa.w_pair = par->w_pair;
+    sa.pbias = a.pbias;
     sa.attention = out->attention; sa.o = a.o;
 
     if ((rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)
@@ -513,6 +522,7 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
     if (!workspace || !aligned16(workspace) || workspace_bytes < need_ws)
         return ATOM_ATTN_EWORKSPACE;
     SlotArgs sa;
+    std::memset(&sa, 0, sizeof(sa)); // pbias null: the pair bias comes from the pair rows
     sa.B = d.B; sa.A = d.A; sa.K = d.K; sa.H = d.H; sa.D = d.D; sa.V = d.V;
     sa.eps = (float)eps;
     sa.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d.D));

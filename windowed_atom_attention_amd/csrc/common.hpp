@@ -300,6 +300,94 @@ __device__ __forceinline__ f32x4_t zero4() {
     return z;
 }
 
+// ------------------------------------------------------- AF3 pair bias
+// ("windowed_atom_attention", Required behavior, AF3 encoder page): the
+// bias of head h for a slot with pair row x (V channels) is
+// LN(x) . (pair_scale * w_pair[:, h]). With d = x - x[0] (shifted data
+// keeps the one-pass variance well conditioned):
+//   LN(x) . w_h = rstd * (sum_v d_v w_vh - mean(d) * sum_v w_vh),
+//   rstd = 1 / sqrt(mean(d^2) - mean(d)^2 + eps).
+
+// LDS weights: w4[v] = pair_scale[v] * w_pair[v][0..3] (heads past H are
+// zero), and partial column sums wpart[2][4] (lanes of one head reduced
+// per wave; V <= 32). Every thread of the (>= 128-thread) block calls it.
+template <typename T>
+__device__ __forceinline__ void pair_weights(const T *ps, const T *wp, int V, int H, float *w4,
+                                             float *wpart) {
+    const int i = threadIdx.x;
+    float w = 0.0f;
+    if (i < V * 4) {
+        const int v = i / 4, h = i % 4;
+        w = h < H ? to_f(ps[v]) * to_f(wp[v * H + h]) : 0.0f;
+        w4[i] = w;
+    }
+    if (i < 128) { // waves 0 and 1 (whole waves): sum over the lanes of head i % 4
+        w += __shfl_xor(w, 4);
+        w += __shfl_xor(w, 8);
+        w += __shfl_xor(w, 16);
+        w += __shfl_xor(w, 32);
+        if ((i & 63) < 4)
+            wpart[(i >> 6) * 4 + (i & 3)] = w;
+    }
+}
+// Column sums of the weights (after a barrier that follows pair_weights).
+__device__ __forceinline__ float4 pair_wsum(const float *wpart) {
+    const float4 a = reinterpret_cast<const float4 *>(wpart)[0];
+    const float4 b = reinterpret_cast<const float4 *>(wpart)[1];
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Bias of heads 0..3 for G slots whose pair rows (NV 16-byte vectors each)
+// are in registers; w4p from pair_weights, ws from pair_wsum.
+template <typename T, int NV, int G>
+__device__ __forceinline__ void pair_bias_rows(const uint4 (&rows)[G][NV], const float4 *w4p,
+                                               float4 ws, float eps, float (&out)[G][4]) {
+    constexpr int E = 16 / sizeof(T);
+    constexpr float kInvV = 1.0f / (float)(NV * E);
+    float x0[G], sd[G], sq[G], bb[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float t[E];
+        unpack16<T>(rows[g][0], t);
+        x0[g] = t[0];
+        sd[g] = sq[g] = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            bb[g][h] = 0.0f;
+    }
+#pragma unroll
+    for (int pt = 0; pt < NV; ++pt) {
+        float xv[G][E];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            unpack16<T>(rows[g][pt], xv[g]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float4 w4 = w4p[pt * E + e]; // one broadcast read, all heads
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float dv = xv[g][e] - x0[g];
+                sd[g] += dv;
+                sq[g] = fmaf(dv, dv, sq[g]);
+                bb[g][0] = fmaf(dv, w4.x, bb[g][0]);
+                bb[g][1] = fmaf(dv, w4.y, bb[g][1]);
+                bb[g][2] = fmaf(dv, w4.z, bb[g][2]);
+                bb[g][3] = fmaf(dv, w4.w, bb[g][3]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float md = sd[g] * kInvV;
+        const float var = fmaxf(fmaf(sq[g], kInvV, -md * md), 0.0f);
+        const float rstd = rsqrtf(var + eps);
+        out[g][0] = (bb[g][0] - md * ws.x) * rstd;
+        out[g][1] = (bb[g][1] - md * ws.y) * rstd;
+        out[g][2] = (bb[g][2] - md * ws.z) * rstd;
+        out[g][3] = (bb[g][3] - md * ws.w) * rstd;
+    }
+}
+
 // Zero the padding columns A .. vt_pitch(A)-1 of the transposed V rows
 // ([B][HD][pitch]); row i goes to workgroup i % nwg.
 template <typename T>

@@ -56,6 +56,12 @@ struct BlockArgs {
     // post kernel: stream the whole transition width in one pass (set by
     // its launcher)
     int post_wide;
+    // AF3 pair bias computed by extra workgroups of the projection kernel
+    // (when its tiles leave most of the GPU idle): pbias[slot][4] fp32, the
+    // bias of heads 0..3 of every slot (b, a, k); null when the slot kernel
+    // computes it from the pair rows itself
+    const void *pair_scale, *w_pair;
+    float *pbias;
     // outputs
     void *hidden, *attention, *token_output, *position_update;
     int32_t *status;
@@ -69,6 +75,9 @@ struct SlotArgs {
     const uint8_t *usable, *window_mask;
     const int64_t *key_index;
     const void *q, *k, *v, *pair, *pair_scale, *w_pair;
+    // AF3: the pair bias of every slot, [B*A*K][4] fp32, when precomputed
+    // (then pair, pair_scale and w_pair are not read); null otherwise
+    const float *pbias;
     void *attention, *o;
     // key_index / window_mask rows may be read as 16-byte vectors: K is a
     // multiple of the slots per thread and both bases are 16-byte aligned
@@ -95,6 +104,12 @@ struct PackArgs {
 inline int64_t packed_units(int kd, int n, int dtype_bytes) {
     return (int64_t)kd * n * dtype_bytes / 16;
 }
+
+// Whether the projection kernel also computes the AF3 pair bias (fp32, or
+// bf16 pair rows of at most 16 channels): when its tiles leave a quarter of
+// the compute units or more idle, extra workgroups (one per idle unit)
+// compute the bias there and the slot kernel's pair-row phase disappears.
+bool prep_hosts_pair_bias(const Dims &d, int dtype, int style, int stage);
 
 // Host launchers; dtype 0 = fp32, 1 = bf16.
 hipError_t launch_pack(const PackArgs &a, int dtype, hipStream_t s);

@@ -198,7 +198,63 @@ constexpr int prep_wgs() {
     return sizeof(T) == 2 && !(STYLE == STYLE_AF3 && STAGE == STAGE_DECODER) ? 3 : 2;
 }
 
-// 256 threads: four waves, TPR = 8 threads per tile row.
+// Pair-bias workgroup (AF3, extra workgroups of k_prep placed on compute
+// units its tiles leave idle): the bias of heads 0..3 of every slot of
+// [B*A*K], one pair row of NV 16-byte vectors per slot. Workgroup w of
+// nw takes chunks w, w + nw, ... of 256*RB consecutive slots (RB rows per
+// thread in flight at once, at most LIM vectors: a register budget). Slot
+// kernels that read pbias skip the pair rows.
+template <typename T, int NV, int LIM>
+__device__ __forceinline__ void pair_bias_wg(const BlockArgs &p, int w, int nw, unsigned char *smem) {
+    constexpr int E = 16 / sizeof(T), VV = NV * E;
+    constexpr int RB0 = LIM / NV < 8 ? LIM / NV : 8;
+    constexpr int CG = RB0 < 4 ? RB0 : 4;       // slots per reduction (temporaries)
+    constexpr int RB = RB0 / CG * CG;           // slots per thread and chunk, a multiple of CG
+    float *w4 = reinterpret_cast<float *>(smem);
+    float *wpart = w4 + VV * 4;
+    pair_weights<T>(reinterpret_cast<const T *>(p.pair_scale),
+                    reinterpret_cast<const T *>(p.w_pair), VV, p.d.H, w4, wpart);
+    __syncthreads();
+    const float4 wsum = pair_wsum(wpart);
+    const int64_t total = (int64_t)p.d.B * p.d.A * p.d.K;
+    const int64_t nchunk = (total + 256 * RB - 1) / (256 * RB);
+    const T *pair = reinterpret_cast<const T *>(p.pair);
+    float4 *out = reinterpret_cast<float4 *>(p.pbias);
+    for (int64_t c = w; c < nchunk; c += nw) {
+        const int64_t s0 = c * 256 * RB + threadIdx.x;
+        uint4 rows[RB][NV];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int64_t sl = min(s0 + (int64_t)i * 256, total - 1);
+#pragma unroll
+            for (int pt = 0; pt < NV; ++pt)
+                rows[i][pt] = *reinterpret_cast<const uint4 *>(pair + sl * VV + pt * E);
+        }
+#pragma unroll
+        for (int j = 0; j < RB; j += CG) {
+            // the weight reads stay inside each group (hoisting all of them
+            // out of the loops would hold V float4 registers throughout)
+            __asm__ volatile("" ::: "memory");
+            uint4 grp[CG][NV];
+#pragma unroll
+            for (int i = 0; i < CG; ++i)
+#pragma unroll
+                for (int pt = 0; pt < NV; ++pt)
+                    grp[i][pt] = rows[j + i][pt];
+            float bb[CG][4];
+            pair_bias_rows<T, NV, CG>(grp, reinterpret_cast<const float4 *>(w4), wsum, p.eps, bb);
+#pragma unroll
+            for (int i = 0; i < CG; ++i) {
+                const int64_t sl = s0 + (int64_t)(j + i) * 256;
+                if (sl < total)
+                    out[sl] = make_float4(bb[i][0], bb[i][1], bb[i][2], bb[i][3]);
+            }
+        }
+    }
+}
+
+// 256 threads: four waves, TPR = 8 threads per tile row. Workgroups past
+// the tiles (AF3, pbias set) compute the pair bias.
 template <typename T, int STYLE, int STAGE>
 __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -215,17 +271,37 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
     constexpr int E = 16 / sizeof(T);
     constexpr bool SPLIT = sizeof(T) == 2;
     constexpr bool XLO = SPLIT && STAGE == STAGE_DECODER; // x0 kept as hi + lo
+    const int ntile = (N + 31) / 32;
+    if (STYLE == STYLE_AF3 && (int)blockIdx.x >= ntile) {
+        const int w = blockIdx.x - ntile, nw = gridDim.x - ntile;
+        // pair rows of up to 32 bytes (bf16) or 64 bytes (fp32); wider
+        // bf16 rows keep the bias in the slot kernel (registers)
+        constexpr int LIM = prep_wgs<T, STYLE, STAGE>() == 3 ? 16 : 32;
+        const int nv = d.V * (int)sizeof(T) / 16;
+        if constexpr (sizeof(T) == 2) {
+            if (nv == 1)
+                pair_bias_wg<T, 1, LIM>(p, w, nw, smem);
+            else
+                pair_bias_wg<T, 2, LIM>(p, w, nw, smem);
+        } else {
+            if (nv == 2)
+                pair_bias_wg<T, 2, LIM>(p, w, nw, smem);
+            else
+                pair_bias_wg<T, 4, LIM>(p, w, nw, smem);
+        }
+        return;
+    }
 
     if (STAGE == STAGE_ENCODER) {
         T *to = reinterpret_cast<T *>(p.token_output);
         const int64_t total = (int64_t)d.B * d.T * d.U;
         for (int64_t i = (int64_t)blockIdx.x * NT + tid; i < total;
-             i += (int64_t)gridDim.x * NT)
+             i += (int64_t)ntile * NT)
             to[i] = from_f<T>(0.0f);
     }
     if (p.status != nullptr && blockIdx.x == 0 && tid == 0)
         p.status[0] = 0;
-    zero_vt_pad<T>(reinterpret_cast<T *>(p.v), d.B, HD, d.A, blockIdx.x, gridDim.x);
+    zero_vt_pad<T>(reinterpret_cast<T *>(p.v), d.B, HD, d.A, blockIdx.x, ntile);
 
     const PrepLayout L = prep_layout(d, sizeof(T), STYLE, STAGE);
     T *xh = reinterpret_cast<T *>(smem + L.o_xh);
@@ -472,10 +548,23 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
     }
 }
 
+// Pair-bias workgroups: one per compute unit the tiles leave idle.
+static int pair_bias_wgs(const Dims &d) {
+    const int64_t ntile = ((int64_t)d.B * d.A + 31) / 32;
+    return ntile < device_cus() ? device_cus() - (int)ntile : 0;
+}
+
+bool prep_hosts_pair_bias(const Dims &d, int dtype, int style, int stage) {
+    (void)stage;
+    if (style != STYLE_AF3 || (dtype == 1 && d.V > 16))
+        return false;
+    return pair_bias_wgs(d) * 4 >= device_cus(); // a quarter of the GPU or more is idle
+}
+
 hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
                        hipStream_t s) {
     const int N = a.d.B * a.d.A;
-    const int grid = (N + 31) / 32;
+    const int grid = (N + 31) / 32 + (a.pbias != nullptr ? pair_bias_wgs(a.d) : 0);
     const size_t lds = prep_lds_bytes(a.d, dtype, style, stage);
     const void *fn = nullptr;
 #define WAA_PICK(T, ST, SG) fn = (const void *)k_prep<T, ST, SG>

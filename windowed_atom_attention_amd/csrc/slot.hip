@@ -27,7 +27,9 @@ hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) 
     const Dims d{a.B, a.A, 1, a.K, 32, 32, a.H, a.D, a.V, 32, 32};
     const size_t lds = slot_lds_bytes(d, dtype, style);
     const void *fn;
-    if (style == STYLE_AF3) {
+    if (style == STYLE_AF3 && a.pbias != nullptr) {
+        fn = pick_slot_af3_pre(dtype, spl, a.D);
+    } else if (style == STYLE_AF3) {
         const int nv = a.V * (dtype ? 2 : 4) / 16;
         fn = dtype == 0 ? pick_slot_af3_f32(spl, a.D, nv) : pick_slot_af3_bf16(spl, a.D, nv);
     } else {

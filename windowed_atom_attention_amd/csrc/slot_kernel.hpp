@@ -50,26 +50,22 @@ constexpr int kHG = 4;      // heads per pass (one per wave)
 
 struct SlotLayout {
     int sp;
-    size_t o_wpr, o_wsum, o_t, o_tag, total;
+    size_t o_wpr, o_t, o_tag, total;
 };
 
 __host__ __device__ inline size_t sal16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 // LDS: AF3 pair weights pair_scale * w_pair as [V][4] (heads padded to 4)
-// and their column sums; the score / probability tiles [4][16][sp] fp32;
-// the writer tag of each probability cell [16][128].
+// and two partial column sums [2][4]; the score / probability tiles
+// [4][16][sp] fp32; the writer tag of each probability cell [16][128].
 __host__ __device__ inline SlotLayout slot_layout(int H, int V, int style) {
     (void)H;
     SlotLayout L;
     L.sp = kRMAX + 4;
     size_t o = 0;
     L.o_wpr = o;
-    L.o_wsum = o;
-    if (style == STYLE_AF3) {
-        o = sal16(o + (size_t)V * kHG * 4);
-        L.o_wsum = o;
-        o = sal16(o + kHG * 4);
-    }
+    if (style == STYLE_AF3)
+        o = sal16(o + (size_t)(V + 2) * kHG * 4);
     L.o_t = o; o = sal16(o + (size_t)kHG * kQB * L.sp * 4);
     L.o_tag = o; o = sal16(o + (size_t)kQB * kRMAX * 4);
     L.total = o;
@@ -91,14 +87,18 @@ template <> __device__ __forceinline__ uint4 p_chunk<bf16_t>(const float *src) {
                       pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
 }
 
-// NV: 16-byte vectors per AF3 pair row (V = NV * 16 / sizeof(T)); 1 for
-// ESMFold2, which has no pair input.
+// NV: 16-byte vectors per AF3 pair row (V = NV * 16 / sizeof(T)), or 0
+// when the AF3 pair bias comes precomputed (p.pbias); 1 for ESMFold2, which
+// has no pair input.
 template <typename T, int STYLE, int SPL, int DK, int NV>
 __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_lo, s_hi;
     constexpr int KC = Mma16<T>::KC, QU = Mma16<T>::QUARTER;
     constexpr int E = 16 / sizeof(T);
+    constexpr bool PRE = STYLE == STYLE_AF3 && NV == 0;  // pair bias read from p.pbias
+    constexpr bool FUSED = STYLE == STYLE_AF3 && NV > 0; // pair bias from the pair rows
+    constexpr int NVB = NV > 0 ? NV : 1;
     constexpr int VV = NV * E;                       // AF3 pair channels
     constexpr int NKQ = DK / 16;                     // fp32 k chunks of Q.K
     constexpr int NDB = DK / 16;                     // 16-wide output blocks of o
@@ -119,7 +119,6 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     const int k0 = j16 * SPL;
     const SlotLayout L = slot_layout(H, VV, STYLE);
     float *wpr = reinterpret_cast<float *>(smem + L.o_wpr);
-    float *wsum = reinterpret_cast<float *>(smem + L.o_wsum);
     float *tile = reinterpret_cast<float *>(smem + L.o_t);
     const float *qg = reinterpret_cast<const float *>(p.q); // fp32 logit operands
     const float *kg = reinterpret_cast<const float *>(p.k);
@@ -136,9 +135,9 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     const int nsl = !qin ? 0 : (full ? SPL : (K > k0 ? K - k0 : 0));
     constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : (NV * (int)sizeof(T) <= 8 ? 2 : 1));
     constexpr int NG = SPL / GS;
-    uint4 pbuf[2][GS][NV];
+    uint4 pbuf[2][GS][NVB];
     const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + k0) * VV;
-    auto load_group = [&](uint4 (&dst)[GS][NV], int g0) {
+    auto load_group = [&](uint4 (&dst)[GS][NVB], int g0) {
 #pragma unroll
         for (int ii = 0; ii < GS; ++ii) {
             const T *src = prow + min(g0 + ii, nsl - 1) * VV;
@@ -147,8 +146,17 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                 dst[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
         }
     };
-    if (STYLE == STYLE_AF3 && nsl > 0)
+    if (FUSED && nsl > 0)
         load_group(pbuf[0], 0);
+    // precomputed pair bias of the thread's slots (slots past a ragged end
+    // re-read the last one)
+    float4 pbv[PRE ? SPL : 1];
+    if (PRE && nsl > 0) {
+        const float4 *pbr = reinterpret_cast<const float4 *>(p.pbias) + nrow * K + k0;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            pbv[i] = pbr[min(i, nsl - 1)];
+    }
 
     // ---- key ids and window bits of this thread's slots
     int64_t kid[SPL];
@@ -190,20 +198,9 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
         s_lo = INT_MAX;
         s_hi = -1;
     }
-    if (STYLE == STYLE_AF3) {
-        const T *ps = reinterpret_cast<const T *>(p.pair_scale);
-        const T *wp = reinterpret_cast<const T *>(p.w_pair);
-        for (int i = tid; i < VV * kHG; i += 256) {
-            const int v = i / kHG, h = i % kHG;
-            wpr[i] = h < H ? to_f(ps[v]) * to_f(wp[v * H + h]) : 0.0f;
-        }
-        if (tid < kHG) {
-            float s = 0.0f;
-            for (int v = 0; v < VV; ++v)
-                s += tid < H ? to_f(ps[v]) * to_f(wp[v * H + tid]) : 0.0f;
-            wsum[tid] = s;
-        }
-    }
+    if (FUSED)
+        pair_weights<T>(reinterpret_cast<const T *>(p.pair_scale),
+                        reinterpret_cast<const T *>(p.w_pair), VV, H, wpr, wpr + VV * 4);
     bool cand[SPL];
     uint8_t uj[SPL];
 #pragma unroll
@@ -225,61 +222,32 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
 #pragma unroll
         for (int h = 0; h < kHG; ++h)
             beta[i][h] = 0.0f;
-    __syncthreads(); // wpr, wsum, s_lo/s_hi initialised
-    if (STYLE == STYLE_AF3 && nsl > 0) {
+    __syncthreads(); // wpr, s_lo/s_hi initialised
+    if (FUSED && nsl > 0) {
         const float4 *w4p = reinterpret_cast<const float4 *>(wpr);
-        const float4 ws = *reinterpret_cast<const float4 *>(wsum);
-        constexpr float kInvV = 1.0f / (float)VV;
+        const float4 ws = pair_wsum(wpr + VV * 4);
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             if (gi + 1 < NG)
                 load_group(pbuf[(gi + 1) & 1], (gi + 1) * GS);
             if (!qok)
                 continue;
-            const uint4 (&pb)[GS][NV] = pbuf[gi & 1];
-            const int g0 = gi * GS;
-            float x0[GS], sd[GS], sq[GS], bb[GS][kHG];
+            float bb[GS][4];
+            pair_bias_rows<T, NVB, GS>(pbuf[gi & 1], w4p, ws, p.eps, bb);
 #pragma unroll
-            for (int ii = 0; ii < GS; ++ii) {
-                float t[E];
-                unpack16<T>(pb[ii][0], t);
-                x0[ii] = t[0];
-                sd[ii] = sq[ii] = 0.0f;
+            for (int ii = 0; ii < GS; ++ii)
 #pragma unroll
                 for (int h = 0; h < kHG; ++h)
-                    bb[ii][h] = 0.0f;
-            }
+                    beta[gi * GS + ii][h] = bb[ii][h];
+        }
+    }
+    if (PRE && nsl > 0) {
 #pragma unroll
-            for (int pt = 0; pt < NV; ++pt) {
-                float xv[GS][E];
-#pragma unroll
-                for (int ii = 0; ii < GS; ++ii)
-                    unpack16<T>(pb[ii][pt], xv[ii]);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float4 w4 = w4p[pt * E + e]; // one broadcast read, all heads
-#pragma unroll
-                    for (int ii = 0; ii < GS; ++ii) {
-                        const float dv = xv[ii][e] - x0[ii];
-                        sd[ii] += dv;
-                        sq[ii] = fmaf(dv, dv, sq[ii]);
-                        bb[ii][0] = fmaf(dv, w4.x, bb[ii][0]);
-                        bb[ii][1] = fmaf(dv, w4.y, bb[ii][1]);
-                        bb[ii][2] = fmaf(dv, w4.z, bb[ii][2]);
-                        bb[ii][3] = fmaf(dv, w4.w, bb[ii][3]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int ii = 0; ii < GS; ++ii) {
-                const float md = sd[ii] * kInvV;
-                const float var = fmaxf(fmaf(sq[ii], kInvV, -md * md), 0.0f);
-                const float rstd = rsqrtf(var + p.eps);
-                beta[g0 + ii][0] = (bb[ii][0] - md * ws.x) * rstd;
-                beta[g0 + ii][1] = (bb[ii][1] - md * ws.y) * rstd;
-                beta[g0 + ii][2] = (bb[ii][2] - md * ws.z) * rstd;
-                beta[g0 + ii][3] = (bb[ii][3] - md * ws.w) * rstd;
-            }
+        for (int i = 0; i < SPL; ++i) {
+            beta[i][0] = pbv[i].x;
+            beta[i][1] = pbv[i].y;
+            beta[i][2] = pbv[i].z;
+            beta[i][3] = pbv[i].w;
         }
     }
     int rel[SPL];
@@ -581,6 +549,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
 const void *pick_slot_af3_f32(int spl, int D, int nv);
 const void *pick_slot_af3_bf16(int spl, int D, int nv);
 const void *pick_slot_esm(int dtype, int spl, int D);
+const void *pick_slot_af3_pre(int dtype, int spl, int D);
 
 template <typename T, int STYLE, int NV>
 const void *pick_slot_sd(int spl, int D) {
