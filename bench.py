@@ -35,16 +35,20 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense matrix peaks
 
 
-def kernel_work(w):
+def kernel_work(w, split=False):
     """Algorithmic work per launch of each kernel: ('hbm', bytes) for the
-    bandwidth-bound slot attention, ('mfma', flops) for the projections."""
+    bandwidth-bound slot attention, ('mfma', flops) for the projections.
+    With the AF3 pair bias split off (`split`: the projection kernel's extra
+    workgroups stream the pair rows and write 16 bytes of bias per slot),
+    the slot kernel reads that bias instead of the pair rows."""
     d = w.dims
     B, A, T, K, C, S, H, D, V, M, U = (d[k] for k in "B A T K C S H D V M U".split())
     HD = H * D
     e = 2 if w.dtype.itemsize == 2 else 4
     N, E = B * A, B * A * K
     af3 = w.style == "af3"
-    slot_bytes = (3 * N * HD * e + 8 * E + E + N + (E * V * e if af3 else 0)
+    pair = (E * 16 if split else E * V * e) if af3 else 0
+    slot_bytes = (3 * N * HD * e + 8 * E + E + N + pair
                   + E * H * e + N * HD * e)
     if af3:
         prep = N * 2 * (4 * S * C + 4 * C * HD)
@@ -67,13 +71,13 @@ def kernel_work(w):
 
 
 def _source_sha(kernel):
-    files = {"slot_attention": "slot.hip", "prep": "prep.hip", "post": "post.hip",
-             "pool": "post.hip", "token_proj": "prep.hip", "pack": "pack.hip",
-             "vt": "slot.hip", "masks": "prep.hip"}
+    files = {"slot_attention": ["slot.hip", "slot_kernel.hpp"], "prep": ["prep.hip"],
+             "post": ["post.hip"], "pool": ["post.hip"], "token_proj": ["prep.hip"],
+             "pack": ["pack.hip"], "vt": ["slot.hip"], "masks": ["prep.hip"]}
     h = hashlib.sha256()
-    for f in (files.get(kernel, ""), "common.hpp"):
+    for f in files.get(kernel, []) + ["common.hpp", "kernels.hpp"]:
         p = os.path.join(ROOT, "windowed_atom_attention_amd", "csrc", f)
-        if f and os.path.exists(p):
+        if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -253,7 +257,7 @@ def main():
         return
 
     import torch
-    from windowed_atom_attention_amd import (profile_enable, profile_read,
+    from windowed_atom_attention_amd import (pair_bias_split, profile_enable, profile_read,
                                              windowed_atom_attention, workspace_bytes)
     from windowed_atom_attention_amd.workloads import make_workload
 
@@ -322,7 +326,7 @@ def main():
     entries = w.entries
     value = entries * args.steps / elapsed
     dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
-    work = kernel_work(w)
+    work = kernel_work(w, pair_bias_split(w.dims, w.style, w.stage, w.dtype))
     per_kernel = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in kt.items()}
     dom = max((k for k in per_kernel if k in work), key=lambda k: per_kernel[k]["avg_us"])
     bound, amount = work[dom]

@@ -170,6 +170,17 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
                              void *attention, void *o, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* Where a block call with these sizes computes the AF3 pair bias on the
+ * current device (host-only, no GPU work; the compute-unit count of the
+ * current device decides): *split = 1 when extra workgroups of the
+ * projection kernel compute it on compute units its 32-atom tiles leave
+ * idle and the slot kernel reads it back (16 bytes per slot, in the
+ * workspace); 0 when the slot kernel computes it from the pair rows
+ * (always 0 for ESMFold2, which has no pair input). The results are the
+ * same either way. Status codes as atom_attn_workspace_bytes. */
+int atom_attn_pair_bias_split(const atom_attn_dims *dims, int style, int stage,
+                              int dtype, int *split);
+
 /* Static description of a status code (never NULL). */
 const char *atom_attn_error_string(int code);
 

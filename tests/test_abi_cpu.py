@@ -28,7 +28,21 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.EXPORTS)
-    assert lib.atom_attn_version() == 2
+    assert lib.atom_attn_version() == 3
+
+
+def test_pair_bias_split_query():
+    # without a GPU the library assumes 256 compute units (MI355X)
+    from windowed_atom_attention_amd import pair_bias_split
+    w1 = make_workload("1")     # 144 tiles: 112 idle units host the bias
+    assert pair_bias_split(w1.dims, "af3", "encoder", torch.float32)
+    w4 = make_workload("4a", A=24576)  # 768 tiles: every unit busy
+    assert not pair_bias_split(w4.dims, "af3", "encoder", torch.bfloat16)
+    assert not pair_bias_split(make_workload("4b", A=256).dims, "esmfold2", "encoder",
+                               torch.bfloat16)
+    d = _dims(V=32)             # bf16 rows wider than 16 channels stay fused
+    assert not pair_bias_split(d, "af3", "encoder", torch.bfloat16)
+    assert pair_bias_split(_dims(), "af3", "encoder", torch.bfloat16)
 
 
 def test_error_strings():

@@ -3,8 +3,8 @@ Instinct MI355X (gfx950): hand-written HIP kernels behind a C-ABI library
 (libatomattn.so, declared in include/atom_attn.h) with a thin ctypes
 binding. Importing the package does not load the library; the first call
 does, and fails loudly if it has not been built."""
-from .api import (masks, profile_enable, profile_read, slot_attention,
-                  windowed_atom_attention, workspace_bytes)
+from .api import (masks, pair_bias_split, profile_enable, profile_read,
+                  slot_attention, windowed_atom_attention, workspace_bytes)
 
 __all__ = ["windowed_atom_attention", "masks", "slot_attention",
-           "workspace_bytes", "profile_enable", "profile_read"]
+           "workspace_bytes", "pair_bias_split", "profile_enable", "profile_read"]

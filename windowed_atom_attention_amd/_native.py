@@ -46,7 +46,7 @@ class Outputs(ctypes.Structure):
 
 EXPORTS = ("atom_attn_workspace_bytes", "atom_attn_encoder",
            "atom_attn_decoder", "atom_attn_masks", "atom_attn_slot_attention",
-           "atom_attn_slot_workspace_bytes",
+           "atom_attn_slot_workspace_bytes", "atom_attn_pair_bias_split",
            "atom_attn_error_string", "atom_attn_version",
            "atom_attn_profile_enable", "atom_attn_profile_read")
 
@@ -82,6 +82,7 @@ def lib():
                                                _vp, _vp, _vp, _vp, _vp, _vp,
                                                _vp, _vp, _vp, _vp, _vp, szt, _vp]
         L.atom_attn_slot_workspace_bytes.argtypes = [P(Dims), i32, P(szt)]
+        L.atom_attn_pair_bias_split.argtypes = [P(Dims), i32, i32, i32, P(i32)]
         L.atom_attn_error_string.argtypes = [i32]
         L.atom_attn_error_string.restype = ctypes.c_char_p
         L.atom_attn_version.argtypes = []
@@ -90,7 +91,7 @@ def lib():
         for name in ("atom_attn_workspace_bytes", "atom_attn_encoder",
                      "atom_attn_decoder", "atom_attn_masks",
                      "atom_attn_slot_attention", "atom_attn_slot_workspace_bytes",
-                     "atom_attn_version",
+                     "atom_attn_pair_bias_split", "atom_attn_version",
                      "atom_attn_profile_enable", "atom_attn_profile_read"):
             getattr(L, name).restype = i32
         _lib = L

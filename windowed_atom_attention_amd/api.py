@@ -138,6 +138,19 @@ def workspace_bytes(dims: Dict[str, int], style: str, stage: str, dtype: torch.d
     return int(out.value)
 
 
+def pair_bias_split(dims: Dict[str, int], style: str, stage: str, dtype: torch.dtype) -> bool:
+    """True when a block call with these sizes computes the AF3 pair bias in
+    extra workgroups of the projection kernel (on compute units its tiles
+    leave idle on the current device) rather than inside the slot kernel."""
+    nd = N.Dims(**{k: int(v) for k, v in dims.items()})
+    out = ctypes.c_int(0)
+    N.check(N.lib().atom_attn_pair_bias_split(ctypes.byref(nd), _STYLES[style],
+                                              _STAGES[stage], _FLOAT_DTYPES[dtype],
+                                              ctypes.byref(out)),
+            "atom_attn_pair_bias_split")
+    return bool(out.value)
+
+
 def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
                             structure: dict, eps: float = 1e-05,
                             style: str = "af3", stage: str = "decoder",

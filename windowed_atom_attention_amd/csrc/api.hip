@@ -16,7 +16,7 @@ using namespace waa;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 // ------------------------------------------------------------ profiler
 
@@ -433,6 +433,25 @@ int atom_attn_workspace_bytes(const atom_attn_dims *dims, int style, int stage,
     if (rc != ATOM_ATTN_OK)
         return rc;
     *bytes = layout_of(dims, style, stage, dtype).total;
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_pair_bias_split(const atom_attn_dims *dims, int style, int stage,
+                              int dtype, int *split) {
+    int rc = check_common(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!split)
+        return ATOM_ATTN_EINVAL;
+    rc = shape_supported(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    const Dims d{(int)dims->B, (int)dims->A, (int)dims->T, (int)dims->K, (int)dims->C,
+                 (int)dims->S, (int)dims->H, (int)dims->D, (int)dims->V, (int)dims->M,
+                 (int)dims->U};
+    *split = style == ATOM_ATTN_AF3 &&
+             prep_hosts_pair_bias(d, dtype == ATOM_ATTN_BF16 ? 1 : 0, STYLE_AF3,
+                                  stage == ATOM_ATTN_ENCODER ? STAGE_ENCODER : STAGE_DECODER);
     return ATOM_ATTN_OK;
 }
 
