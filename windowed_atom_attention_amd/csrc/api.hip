@@ -167,6 +167,7 @@ struct Mat {
     const void *src;
     int64_t ld;
     int kd, n;
+    bool post; // read by the post kernel (else by the projection kernels)
 };
 
 void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
@@ -184,27 +185,27 @@ void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
     off->ff_gate = off->ff_up = off->ff_out = off->w_pool = off->w_token = -1;
     if (style == ATOM_ATTN_AF3) {
         for (int j = 0; j < 3; ++j) {
-            mats->push_back({&off->w_scale[j], at(par ? par->w_scale : nullptr, (int64_t)j * S * C), C, S, C});
-            mats->push_back({&off->w_shift[j], at(par ? par->w_shift : nullptr, (int64_t)j * S * C), C, S, C});
+            mats->push_back({&off->w_scale[j], at(par ? par->w_scale : nullptr, (int64_t)j * S * C), C, S, C, j == 2});
+            mats->push_back({&off->w_shift[j], at(par ? par->w_shift : nullptr, (int64_t)j * S * C), C, S, C, j == 2});
         }
         for (int j = 0; j < 2; ++j)
-            mats->push_back({&off->w_rg[j], at(par ? par->w_residual_gate : nullptr, (int64_t)j * S * C), C, S, C});
+            mats->push_back({&off->w_rg[j], at(par ? par->w_residual_gate : nullptr, (int64_t)j * S * C), C, S, C, true});
     } else {
         for (int j = 0; j < 6; ++j)
-            mats->push_back({&off->w_mod[j], at(par ? par->w_mod : nullptr, (int64_t)j * C), 6 * C, S, C});
+            mats->push_back({&off->w_mod[j], at(par ? par->w_mod : nullptr, (int64_t)j * C), 6 * C, S, C, j >= 2});
     }
-    mats->push_back({&off->w_q, par ? par->w_q : nullptr, HD, C, HD});
-    mats->push_back({&off->w_k, par ? par->w_k : nullptr, HD, C, HD});
-    mats->push_back({&off->w_v, par ? par->w_v : nullptr, HD, C, HD});
-    mats->push_back({&off->w_vg, par ? par->w_value_gate : nullptr, HD, C, HD});
-    mats->push_back({&off->w_ao, par ? par->w_attention_out : nullptr, C, HD, C});
-    mats->push_back({&off->ff_gate, par ? par->w_ff_gate : nullptr, M, C, M});
-    mats->push_back({&off->ff_up, par ? par->w_ff_up : nullptr, M, C, M});
-    mats->push_back({&off->ff_out, par ? par->w_ff_out : nullptr, C, M, C});
+    mats->push_back({&off->w_q, par ? par->w_q : nullptr, HD, C, HD, false});
+    mats->push_back({&off->w_k, par ? par->w_k : nullptr, HD, C, HD, false});
+    mats->push_back({&off->w_v, par ? par->w_v : nullptr, HD, C, HD, false});
+    mats->push_back({&off->w_vg, par ? par->w_value_gate : nullptr, HD, C, HD, false});
+    mats->push_back({&off->w_ao, par ? par->w_attention_out : nullptr, C, HD, C, true});
+    mats->push_back({&off->ff_gate, par ? par->w_ff_gate : nullptr, M, C, M, true});
+    mats->push_back({&off->ff_up, par ? par->w_ff_up : nullptr, M, C, M, true});
+    mats->push_back({&off->ff_out, par ? par->w_ff_out : nullptr, C, M, C, true});
     if (stage == ATOM_ATTN_ENCODER)
-        mats->push_back({&off->w_pool, par ? par->w_pool : nullptr, U, C, U});
+        mats->push_back({&off->w_pool, par ? par->w_pool : nullptr, U, C, U, true});
     else
-        mats->push_back({&off->w_token, par ? par->w_token : nullptr, C, U, C});
+        mats->push_back({&off->w_token, par ? par->w_token : nullptr, C, U, C, false});
     int64_t o = 0;
     for (auto &m : *mats) {
         *m.off = o;
@@ -331,11 +332,16 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     PackedOffsets off;
     std::vector<Mat> mats;
     list_mats(d, style, stage, esz, par, &off, &mats);
+    // post with eight waves (32x16 strips) when its grid has at most one
+    // tile per CU; its matrices are then packed in the strip layout
+    const int64_t ntile = (d->B * d->A + 31) / 32;
+    const bool post8 = ntile <= device_cus();
     PackArgs pa;
     std::memset(&pa, 0, sizeof(pa));
     pa.njobs = (int)mats.size();
     for (size_t i = 0; i < mats.size(); ++i)
-        pa.job[i] = PackJob{mats[i].src, mats[i].ld, mats[i].kd, mats[i].n, *mats[i].off};
+        pa.job[i] = PackJob{mats[i].src, mats[i].ld, mats[i].kd, mats[i].n, *mats[i].off,
+                            post8 && mats[i].post ? 1 : 0};
     pa.total = L.pack_units;
     pa.out = (uint4 *)(ws + L.packed);
 
@@ -364,6 +370,7 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.token_output = out->token_output; a.position_update = out->position_update;
     a.status = out->status;
     a.pair_scale = par->pair_scale; a.w_pair = par->w_pair;
+    a.post_nw8 = post8 ? 1 : 0;
     a.pbias = af3 && prep_hosts_pair_bias(a.d, dt, st, sg) ? (float *)(ws + L.pbias) : nullptr;
 
     SlotArgs sa;

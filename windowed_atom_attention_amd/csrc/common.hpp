@@ -409,24 +409,152 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
     return (bid % X) * (full / X) + bid / X;
 }
 
-// One GEMM stage of a 32-row tile (one wave per 32-column output block):
-// for every block nb < nblocks, x1 = A1 @ B1[nb] (and x2 = A2 @ B2[nb]),
-// then epi(nb, v, x1[v], x2[v]) for accumulator elements v of the lane
-// (row acc32_row(v, lane), column nb*32 + acc32_col(lane)). B1[nb] starts
-// at B1 + nb * bs1 (16-byte units).
-template <typename T, bool DUAL, bool SPLIT, int P = 4, typename Epi>
+// 32 x 16 output strips of a 32-row tile (8-wave workgroups): the same
+// product as gemm_pipe on 16x16 MFMA tiles, c[0] for rows 0-15 and c[1] for
+// rows 16-31, both fed by one B chunk. B: packed strips (pack.hip, strip
+// layout): chunk kc at B[kc*64 + lane], lane quarter g = lane/16 holding
+// k = kc*KC + g*QUARTER + e of column lane%16. nk in 16-byte k-chunks of
+// Mma16<T>::KC.
+template <typename T, bool DUAL, bool SPLIT, int P = 4>
+__device__ __forceinline__ void gemm_pipe16(f32x4_t (&c1)[2], const T *A1, const T *A1lo,
+                                            int lda1, int nk1, const uint4 *__restrict__ B1,
+                                            f32x4_t (&c2)[2], const T *A2, const T *A2lo,
+                                            int lda2, int nk2, const uint4 *__restrict__ B2) {
+    constexpr int KC = Mma16<T>::KC, QU = Mma16<T>::QUARTER;
+    const int lane = threadIdx.x & 63;
+    const int o1 = (lane & 15) * lda1 + (lane >> 4) * QU, h1 = 16 * lda1;
+    const int o2 = DUAL ? (lane & 15) * lda2 + (lane >> 4) * QU : 0, h2 = DUAL ? 16 * lda2 : 0;
+    const int nk = DUAL ? (nk1 > nk2 ? nk1 : nk2) : nk1;
+    const int l1 = nk1 - 1, l2 = DUAL ? nk2 - 1 : 0;
+    uint4 b1[P], b2[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        b1[j] = B1[(j < l1 ? j : l1) * 64 + lane];
+        if (DUAL)
+            b2[j] = B2[(j < l2 ? j : l2) * 64 + lane];
+    }
+    for (int kb = 0; kb < nk; kb += P) {
+        uint4 x1[P][2], x1l[P][2], x2[P][2], x2l[P][2];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int k1 = kb + j < l1 ? kb + j : l1;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                x1[j][t] = *reinterpret_cast<const uint4 *>(A1 + o1 + t * h1 + k1 * KC);
+                if (SPLIT)
+                    x1l[j][t] = *reinterpret_cast<const uint4 *>(A1lo + o1 + t * h1 + k1 * KC);
+            }
+            if (DUAL) {
+                const int k2 = kb + j < l2 ? kb + j : l2;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    x2[j][t] = *reinterpret_cast<const uint4 *>(A2 + o2 + t * h2 + k2 * KC);
+                    if (SPLIT)
+                        x2l[j][t] = *reinterpret_cast<const uint4 *>(A2lo + o2 + t * h2 + k2 * KC);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int k = kb + j;
+            if (k < nk1) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    Mma16<T>::mma(c1[t], x1[j][t], b1[j]);
+                    if (SPLIT)
+                        Mma16<T>::mma(c1[t], x1l[j][t], b1[j]);
+                }
+            }
+            if (DUAL && k < nk2) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    Mma16<T>::mma(c2[t], x2[j][t], b2[j]);
+                    if (SPLIT)
+                        Mma16<T>::mma(c2[t], x2l[j][t], b2[j]);
+                }
+            }
+            const int n1 = k + P < l1 ? k + P : l1;
+            b1[j] = B1[n1 * 64 + lane];
+            if (DUAL) {
+                const int n2 = k + P < l2 ? k + P : l2;
+                b2[j] = B2[n2 * 64 + lane];
+            }
+        }
+    }
+}
+
+// Output layouts of the GEMM stages of a 32-row tile, as policies:
+//  Blk32<T>: 32x32 blocks (4-wave workgroups), 16 accumulator elements a
+//            lane, packed weights in the block layout;
+//  Blk16<T>: 32x16 strips (8-wave workgroups), 8 elements a lane, packed
+//            weights in the strip layout.
+// BW: output columns per block; NW: waves per workgroup; KC: k values per
+// 16-byte chunk; row(i, lane) / col(lane): the tile row and block column of
+// accumulator element i; colsum: the sum over the lanes that hold one
+// column (whose owner lanes are col_owner).
+template <typename T> struct Blk32 {
+    static constexpr int BW = 32, NW = 4, NE = 16, KC = Mma32<T>::KC;
+    struct Acc {
+        f32x16_t a;
+    };
+    __device__ static __forceinline__ Acc zero() { return Acc{zero16()}; }
+    __device__ static __forceinline__ float at(const Acc &x, int i) { return x.a[i]; }
+    __device__ static __forceinline__ void put(Acc &x, int i, float v) { x.a[i] = v; }
+    __device__ static __forceinline__ int row(int i, int lane) { return acc32_row(i, lane); }
+    __device__ static __forceinline__ int col(int lane) { return lane & 31; }
+    __device__ static __forceinline__ float colsum(float x) { return x + __shfl_xor(x, 32); }
+    __device__ static __forceinline__ bool col_owner(int lane) { return lane < 32; }
+    template <bool DUAL, bool SPLIT, int P>
+    __device__ static __forceinline__ void pipe(Acc &c1, const T *A1, const T *A1lo, int lda1,
+                                                int nk1, const uint4 *B1, Acc &c2, const T *A2,
+                                                const T *A2lo, int lda2, int nk2, const uint4 *B2) {
+        gemm_pipe<T, DUAL, SPLIT, P>(c1.a, A1, A1lo, lda1, nk1, B1, c2.a, A2, A2lo, lda2, nk2, B2);
+    }
+};
+template <typename T> struct Blk16 {
+    static constexpr int BW = 16, NW = 8, NE = 8, KC = Mma16<T>::KC;
+    struct Acc {
+        f32x4_t t[2];
+    };
+    __device__ static __forceinline__ Acc zero() { return Acc{{zero4(), zero4()}}; }
+    __device__ static __forceinline__ float at(const Acc &x, int i) { return x.t[i >> 2][i & 3]; }
+    __device__ static __forceinline__ void put(Acc &x, int i, float v) { x.t[i >> 2][i & 3] = v; }
+    __device__ static __forceinline__ int row(int i, int lane) {
+        return (i >> 2) * 16 + (lane >> 4) * 4 + (i & 3);
+    }
+    __device__ static __forceinline__ int col(int lane) { return lane & 15; }
+    __device__ static __forceinline__ float colsum(float x) {
+        x += __shfl_xor(x, 16);
+        return x + __shfl_xor(x, 32);
+    }
+    __device__ static __forceinline__ bool col_owner(int lane) { return lane < 16; }
+    template <bool DUAL, bool SPLIT, int P>
+    __device__ static __forceinline__ void pipe(Acc &c1, const T *A1, const T *A1lo, int lda1,
+                                                int nk1, const uint4 *B1, Acc &c2, const T *A2,
+                                                const T *A2lo, int lda2, int nk2, const uint4 *B2) {
+        gemm_pipe16<T, DUAL, SPLIT, P>(c1.t, A1, A1lo, lda1, nk1, B1, c2.t, A2, A2lo, lda2, nk2, B2);
+    }
+};
+
+// One GEMM stage of a 32-row tile in layout L (one wave per output block,
+// blocks nb = wave, wave + NW, ...): for every block nb < nblocks,
+// x1 = A1 @ B1[nb] (and x2 = A2 @ B2[nb]), then epi(r, c, x1, x2) for each
+// accumulator element of the lane (tile row r, stage column c). B1[nb]
+// starts at B1 + nb * bs1 (16-byte units); nk in chunks of L::KC.
+template <typename L, typename T, bool DUAL, bool SPLIT, int P = 4, typename Epi>
 __device__ __forceinline__ void gemm_stage(int nblocks, const T *A1, const T *A1lo, int lda1,
                                            int nk1, const uint4 *B1, int64_t bs1,
                                            const T *A2, const T *A2lo, int lda2, int nk2,
                                            const uint4 *B2, int64_t bs2, Epi &&epi) {
-    const int wave = threadIdx.x >> 6;
-    for (int nb = wave; nb < nblocks; nb += 4) {
-        f32x16_t a1 = zero16(), a2 = zero16();
-        gemm_pipe<T, DUAL, SPLIT, P>(a1, A1, A1lo, lda1, nk1, B1 + nb * bs1,
-                                  a2, A2, A2lo, lda2, nk2, DUAL ? B2 + nb * bs2 : B1);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int nb = wave; nb < nblocks; nb += L::NW) {
+        typename L::Acc a1 = L::zero(), a2 = L::zero();
+        L::template pipe<DUAL, SPLIT, P>(a1, A1, A1lo, lda1, nk1, B1 + nb * bs1,
+                                         a2, A2, A2lo, lda2, nk2, DUAL ? B2 + nb * bs2 : B1);
+        const int c0 = nb * L::BW + L::col(lane);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            epi(nb, v, a1[v], DUAL ? a2[v] : 0.0f);
+        for (int i = 0; i < L::NE; ++i)
+            epi(L::row(i, lane), c0, L::at(a1, i), DUAL ? L::at(a2, i) : 0.0f);
     }
 }
 

@@ -54,8 +54,9 @@ struct BlockArgs {
     float *pool_sum;
     int *pool_int;
     // post kernel: stream the whole transition width in one pass (set by
-    // its launcher)
-    int post_wide;
+    // its launcher); eight waves with 32x16 output strips (its matrices are
+    // then packed in the strip layout)
+    int post_wide, post_nw8;
     // AF3 pair bias computed by extra workgroups of the projection kernel
     // (when its tiles leave most of the GPU idle): pbias[slot][4] fp32, the
     // bias of heads 0..3 of every slot (b, a, k); null when the slot kernel
@@ -91,6 +92,7 @@ struct PackJob {
     int64_t ld;
     int32_t kd, n;
     int64_t dst; // offset in 16-byte units
+    int32_t strip; // 1: 16-column strip layout (8-wave kernels), 0: 32-column blocks
 };
 constexpr int kMaxPackJobs = 32;
 struct PackArgs {

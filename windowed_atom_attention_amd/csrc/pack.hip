@@ -1,10 +1,13 @@
 // pack.hip -- rearranges weight matrices into MFMA B-operand chunk order.
 //
 // A [kd x n] matrix (stored [in][out], row pitch ld) becomes, for each
-// 32-column block nb and each k-chunk kc, 64 lanes x 16 bytes: lane
-// (h = lane/32, c = lane%32) holds W[kc*KC + h*HALF + e][nb*32 + c] for
-// e < 16/sizeof(T) (KC/HALF as in Mma32<T>). A wave then fetches one chunk
-// with a single fully coalesced 1 KB load. Layout: [nb][kc][lane].
+// output block nb and each k-chunk kc, 64 lanes x 16 bytes, e < 16/sizeof(T):
+//  * block layout (32x32 MFMA, 32 columns): lane (h = lane/32, c = lane%32)
+//    holds W[kc*KC + h*HALF + e][nb*32 + c] (KC/HALF as in Mma32<T>);
+//  * strip layout (16x16 MFMA, 16 columns): lane (g = lane/16, c = lane%16)
+//    holds W[kc*KC + g*QUARTER + e][nb*16 + c] (KC/QUARTER as in Mma16<T>).
+// A wave then fetches one chunk with a single fully coalesced 1 KB load.
+// Layout: [nb][kc][lane].
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,12 +31,14 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
     const int64_t local = u - jb.dst;
     const int lane = (int)(local & 63);
     const int64_t rest = local >> 6;
-    const int nkc = jb.kd / Mma32<T>::KC;
+    const int KC = jb.strip ? Mma16<T>::KC : Mma32<T>::KC;
+    const int nkc = jb.kd / KC;
     const int kc = (int)(rest % nkc);
     const int nb = (int)(rest / nkc);
     const T *src = reinterpret_cast<const T *>(jb.src);
-    const int col = nb * 32 + (lane & 31);
-    const int row0 = kc * Mma32<T>::KC + (lane >> 5) * Mma32<T>::HALF;
+    const int col = jb.strip ? nb * 16 + (lane & 15) : nb * 32 + (lane & 31);
+    const int row0 = kc * KC + (jb.strip ? (lane >> 4) * Mma16<T>::QUARTER
+                                         : (lane >> 5) * Mma32<T>::HALF);
     constexpr int E = 16 / sizeof(T);
     T vals[E];
 #pragma unroll

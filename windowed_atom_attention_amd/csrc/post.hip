@@ -10,14 +10,19 @@
 //              (LN(hidden)*readout_scale [+ readout_bias]) @ w_readout, 0)
 // The entry state x0 and the conditioning are recomputed from the inputs
 // (two small GEMMs cost far less than storing and re-reading four C-wide
-// vectors per atom). All matrix products are MFMA 32x32 tiles; each dual
-// GEMM's epilogue applies the elementwise step in registers.
+// vectors per atom). All matrix products run on MFMA: 32x32 blocks with
+// four waves, or, for grids of at most one tile per CU, 32x16 strips with
+// eight waves (two per SIMD, so one wave's epilogue runs under the other's
+// MFMAs); each dual GEMM's epilogue applies the elementwise step in
+// registers.
 //
 // pool: encoder mean-pool, atomics-free. A tile owns every token whose
 // first usable atom lies in it; it walks its atoms in index order and, for
 // the last open token, continues into the following atoms until that
 // token's atoms end. Requires usable atoms sorted by atom_to_token within a
 // batch; a violation sets the status word.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -67,11 +72,21 @@ size_t post_lds_bytes(const Dims &d, int dtype, int style) {
     return post_layout(d, dtype ? 2 : 4, style, 0).total;
 }
 
-// 256 threads: four waves, TPR = 8 threads per tile row.
-template <typename T, int STYLE, int STAGE>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs p) {
+// Row sum over the TPR threads of a tile row (aligned lane groups of 8 or 16).
+template <int TPR> __device__ __forceinline__ float row_sum(float x) {
+    return TPR == 16 ? sum16(x) : sum8(x);
+}
+
+// NW waves (4: 32x32 output blocks, several workgroups per CU; 8: 32x16
+// strips, two waves per SIMD for grids of at most one tile per CU), TPR =
+// 64*NW/32 threads per tile row.
+template <typename T, int STYLE, int STAGE, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) void k_post(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int NT = 256, TPR = NT / 32;
+    constexpr int NT = 64 * NW, TPR = NT / 32;
+    using G = typename std::conditional<NW == 8, Blk16<T>, Blk32<T>>::type;
+    using Acc = typename G::Acc;
+    constexpr int BW = G::BW;
     // GEMM pipeline depth: 2 for bf16 keeps the kernel at three
     // workgroups per CU
     constexpr int PP = sizeof(T) == 2 ? 2 : 4;
@@ -188,7 +203,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
         if (STYLE == STYLE_AF3) {
             // c_2 = LN(c) * cond_scale[2], each thread on its own entries of
             // opC (written above by the same thread: no barrier needed)
-            const float mc = sum8(csum) / (float)S;
+            const float mc = row_sum<TPR>(csum) / (float)S;
             float q = 0.0f;
             for (int vi = sub; vi < nvS; vi += TPR)
 #pragma unroll
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
                     const float t = to_f(opC[row * L.ldS + vi * E + e]) - mc;
                     q += t * t;
                 }
-            const float rc = 1.0f / sqrtf(sum8(q) / (float)S + p.eps);
+            const float rc = 1.0f / sqrtf(row_sum<TPR>(q) / (float)S + p.eps);
             const T *cscale = reinterpret_cast<const T *>(p.cond_scale) + 2 * S;
             for (int vi = sub; vi < nvS; vi += TPR) {
                 float sc[E];
@@ -211,19 +226,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
     }
     __syncthreads();
 
-    const int nkS = S / Mma32<T>::KC, nkC = C / Mma32<T>::KC;
-    const int nkHD = HD / Mma32<T>::KC, nkM = M / Mma32<T>::KC;
+    const int nkS = S / G::KC, nkC = C / G::KC;
+    const int nkHD = HD / G::KC, nkM = M / G::KC;
 
     // x1 = x0 + g_att * (o*G) @ w_attention_out
     {
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
-        gemm_stage<T, true, false, PP>(
-            C / 32, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao, (int64_t)nkHD * 64,
+        gemm_stage<G, T, true, false, PP>(
+            C / BW, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao, (int64_t)nkHD * 64,
             opC, nullptr, L.ldS, nkS, p.pk + offg, (int64_t)nkS * 64,
-            [&](int nb, int v, float x1, float x2) {
-                const int c = nb * 32 + acc32_col(lane);
-                const int r = acc32_row(v, lane);
+            [&](int r, int c, float x1, float x2) {
                 const float gate = STYLE == STYLE_AF3 ? sigmoid_f(x2 + to_f(brg[c])) : x2;
                 xs[r * L.xp + c] += gate * x1;
             });
@@ -236,13 +249,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
             float s = 0.0f;
             for (int c = sub; c < C; c += TPR)
                 s += xr[c];
-            const float mean = sum8(s) / (float)C;
+            const float mean = row_sum<TPR>(s) / (float)C;
             float q = 0.0f;
             for (int c = sub; c < C; c += TPR) {
                 const float t = xr[c] - mean;
                 q += t * t;
             }
-            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = mean;
                 st[row * 4 + 1] = rstd;
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
             float q = 0.0f;
             for (int c = sub; c < C; c += TPR)
                 q += xr[c] * xr[c];
-            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
                 st[row * 4 + 1] = rstd;
@@ -265,12 +278,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
         const T *opz = STYLE == STYLE_AF3 ? opC2 : opC;
         const int64_t o1 = STYLE == STYLE_AF3 ? p.off.w_scale[2] : p.off.w_mod[3];
         const int64_t o2 = STYLE == STYLE_AF3 ? p.off.w_shift[2] : p.off.w_mod[4];
-        gemm_stage<T, true, false, PP>(
-            C / 32, opz, nullptr, L.ldS, nkS, p.pk + o1, (int64_t)nkS * 64,
+        gemm_stage<G, T, true, false, PP>(
+            C / BW, opz, nullptr, L.ldS, nkS, p.pk + o1, (int64_t)nkS * 64,
             opz, nullptr, L.ldS, nkS, p.pk + o2, (int64_t)nkS * 64,
-            [&](int nb, int v, float x1, float x2) {
-                const int c = nb * 32 + acc32_col(lane);
-                const int r = acc32_row(v, lane);
+            [&](int r, int c, float x1, float x2) {
                 const float xn = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
                 float z;
                 if (STYLE == STYLE_AF3)
@@ -283,30 +294,30 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
     __syncthreads();
     // x2 = x1 + g_tr * (h @ w_ff_out), h = SiLU(z @ w_ff_gate) * (z @ w_ff_up),
     // with h staged MCW columns at a time. Output columns go in groups of
-    // 128 (one 32-column block per wave), so each wave carries its block of
-    // h @ w_ff_out in registers across the passes; with C > 128 and M > MCW
-    // the h chunks are recomputed per group. hidden = select(usable, x2, 0).
+    // NW blocks (one per wave), so each wave carries its block of
+    // h @ w_ff_out in registers across the passes; with more than one group
+    // and M > MCW the h chunks are recomputed per group.
+    // hidden = select(usable, x2, 0).
     {
-        constexpr int KC = Mma32<T>::KC;
+        constexpr int KC = G::KC;
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[1] : p.off.w_mod[5];
         const bool single = M <= MCW;
-        for (int cg = 0; cg < C / 32; cg += 4) {
+        for (int cg = 0; cg < C / BW; cg += NW) {
             const int nb = cg + wave;
-            const bool own = nb < C / 32;
-            f32x16_t acc = zero16(), ga = zero16();
+            const bool own = nb < C / BW;
+            Acc acc = G::zero(), ga = G::zero();
             for (int m0 = 0; m0 < M; m0 += MCW) {
                 const int mc = M - m0 < MCW ? M - m0 : MCW;
                 if (cg == 0 || !single) {
                     if (m0 > 0 || cg > 0)
                         __syncthreads(); // the previous chunk of h has been consumed
-                    gemm_stage<T, true, false, PP>(
-                        mc / 32, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + (int64_t)(m0 / 32) * nkC * 64,
+                    gemm_stage<G, T, true, false, PP>(
+                        mc / BW, opZ, nullptr, L.ldC, nkC, p.pk + p.off.ff_gate + (int64_t)(m0 / BW) * nkC * 64,
                         (int64_t)nkC * 64, opZ, nullptr, L.ldC, nkC,
-                        p.pk + p.off.ff_up + (int64_t)(m0 / 32) * nkC * 64, (int64_t)nkC * 64,
-                        [&](int hb, int v, float x1, float x2) {
-                            opH[acc32_row(v, lane) * L.ldH + hb * 32 + acc32_col(lane)] =
-                                from_f<T>(silu_f(x1) * x2);
+                        p.pk + p.off.ff_up + (int64_t)(m0 / BW) * nkC * 64, (int64_t)nkC * 64,
+                        [&](int r, int c, float x1, float x2) {
+                            opH[r * L.ldH + c] = from_f<T>(silu_f(x1) * x2);
                         });
                     __syncthreads();
                 }
@@ -314,19 +325,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
                     continue;
                 const uint4 *wo = p.pk + p.off.ff_out + ((int64_t)nb * nkM + m0 / KC) * 64;
                 if (m0 + MCW >= M)
-                    gemm2<T, false, PP>(acc, opH, nullptr, L.ldH, mc / KC, wo,
-                             ga, opC, nullptr, L.ldS, nkS, p.pk + offg + (int64_t)nb * nkS * 64);
+                    G::template pipe<true, false, PP>(acc, opH, nullptr, L.ldH, mc / KC, wo,
+                                                      ga, opC, nullptr, L.ldS, nkS,
+                                                      p.pk + offg + (int64_t)nb * nkS * 64);
                 else
-                    gemm1<T, false, PP>(acc, opH, nullptr, L.ldH, mc / KC, wo);
+                    G::template pipe<false, false, PP>(acc, opH, nullptr, L.ldH, mc / KC, wo,
+                                                       acc, opH, nullptr, L.ldH, 0, wo);
             }
             if (own) {
-                const int c = nb * 32 + acc32_col(lane);
+                const int c = nb * BW + G::col(lane);
                 const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = acc32_row(v, lane);
-                    const float gate = STYLE == STYLE_AF3 ? sigmoid_f(ga[v] + bias) : ga[v];
-                    const float x2 = xs[r * L.xp + c] + gate * acc[v];
+                for (int i = 0; i < G::NE; ++i) {
+                    const int r = G::row(i, lane);
+                    const float gv = G::at(ga, i);
+                    const float gate = STYLE == STYLE_AF3 ? sigmoid_f(gv + bias) : gv;
+                    const float x2 = xs[r * L.xp + c] + gate * G::at(acc, i);
                     xs[r * L.xp + c] = us[r] ? x2 : 0.0f;
                 }
             }
@@ -398,24 +412,24 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
         }
         if (nseg > 0) {
             T *tout = reinterpret_cast<T *>(p.token_output);
-            int sv[16]; // segment of each accumulator row of the lane
+            int sv[G::NE]; // segment of each accumulator row of the lane
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                sv[v] = segid[acc32_row(v, lane)];
-            // segment sums of one ReLU'd 32-column block: the lane's 16 rows,
-            // then its partner lane's (lane ^ 32) other 16 rows
-            auto pool_block = [&](f32x16_t &acc, int nb) {
-                const int col = nb * 32 + acc32_col(lane);
+            for (int i = 0; i < G::NE; ++i)
+                sv[i] = segid[G::row(i, lane)];
+            // segment sums of one ReLU'd column block: the lane's rows, then
+            // the other lanes of its column (colsum)
+            auto pool_block = [&](Acc &acc, int nb) {
+                const int col = nb * BW + G::col(lane);
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[v] = fmaxf(acc[v], 0.0f);
+                for (int i = 0; i < G::NE; ++i)
+                    G::put(acc, i, fmaxf(G::at(acc, i), 0.0f));
                 for (int s = 0; s < nseg; ++s) {
                     float part = 0.0f;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        part += sv[v] == s ? acc[v] : 0.0f;
-                    part += __shfl_xor(part, 32);
-                    if (lane < 32) {
+                    for (int i = 0; i < G::NE; ++i)
+                        part += sv[i] == s ? G::at(acc, i) : 0.0f;
+                    part = G::colsum(part);
+                    if (G::col_owner(lane)) {
                         if (s == 0)
                             rsum[col] = part;
                         else if (s == nseg - 1)
@@ -426,18 +440,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
                 }
             };
             // two column blocks per GEMM call where the wave has two left
-            const int nbU = d.U / 32;
-            for (int nb0 = wave; nb0 < nbU; nb0 += 8) {
-                const int nb1 = nb0 + 4;
-                f32x16_t a1 = zero16(), a2 = zero16();
+            const int nbU = d.U / BW;
+            for (int nb0 = wave; nb0 < nbU; nb0 += 2 * NW) {
+                const int nb1 = nb0 + NW;
+                Acc a1 = G::zero(), a2 = G::zero();
                 const uint4 *w0 = p.pk + p.off.w_pool + (int64_t)nb0 * nkC * 64;
                 if (nb1 < nbU) {
-                    gemm2<T, false, PP>(a1, opZ, nullptr, L.ldC, nkC, w0,
-                             a2, opZ, nullptr, L.ldC, nkC, p.pk + p.off.w_pool + (int64_t)nb1 * nkC * 64);
+                    G::template pipe<true, false, PP>(a1, opZ, nullptr, L.ldC, nkC, w0,
+                                                      a2, opZ, nullptr, L.ldC, nkC,
+                                                      p.pk + p.off.w_pool + (int64_t)nb1 * nkC * 64);
                     pool_block(a1, nb0);
                     pool_block(a2, nb1);
                 } else {
-                    gemm1<T, false, PP>(a1, opZ, nullptr, L.ldC, nkC, w0);
+                    G::template pipe<false, false, PP>(a1, opZ, nullptr, L.ldC, nkC, w0,
+                                                       a1, opZ, nullptr, L.ldC, 0, w0);
                     pool_block(a1, nb0);
                 }
             }
@@ -448,13 +464,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
         float s = 0.0f;
         for (int c = sub; c < C; c += TPR)
             s += xr[c];
-        const float mean = sum8(s) / (float)C;
+        const float mean = row_sum<TPR>(s) / (float)C;
         float q = 0.0f;
         for (int c = sub; c < C; c += TPR) {
             const float t = xr[c] - mean;
             q += t * t;
         }
-        const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
+        const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
         const T *rs = reinterpret_cast<const T *>(p.readout_scale);
         const T *rb = reinterpret_cast<const T *>(p.readout_bias);
         const T *wr = reinterpret_cast<const T *>(p.w_readout);
@@ -467,9 +483,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void k_post(BlockArgs 
             acc1 += z * to_f(wr[c * 3 + 1]);
             acc2 += z * to_f(wr[c * 3 + 2]);
         }
-        acc0 = sum8(acc0);
-        acc1 = sum8(acc1);
-        acc2 = sum8(acc2);
+        acc0 = row_sum<TPR>(acc0);
+        acc1 = row_sum<TPR>(acc1);
+        acc2 = row_sum<TPR>(acc2);
         if (sub == 0 && inb) {
             T *pu = reinterpret_cast<T *>(p.position_update) + (int64_t)n * 3;
             const bool ok = us[row];
@@ -489,7 +505,7 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
     b.post_wide = grid <= device_cus() && post_layout(a.d, esz, style, 1).total <= kMaxLds;
     const size_t lds = post_layout(a.d, esz, style, b.post_wide).total;
     const void *fn = nullptr;
-#define WAA_PICK(T, ST, SG) fn = (const void *)k_post<T, ST, SG>
+#define WAA_PICK(T, ST, SG) fn = a.post_nw8 ? (const void *)k_post<T, ST, SG, 8> : (const void *)k_post<T, ST, SG, 4>
     if (dtype == 0) {
         if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(float, 0, 0); else WAA_PICK(float, 0, 1); }
         else { if (stage == STAGE_ENCODER) WAA_PICK(float, 1, 0); else WAA_PICK(float, 1, 1); }
@@ -500,7 +516,7 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
 #undef WAA_PICK
     allow_lds(fn, lds);
     void *args[] = {(void *)&b};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(a.post_nw8 ? 512 : 256), args, lds, s);
     if (e != hipSuccess)
         return e;
     return hipGetLastError();

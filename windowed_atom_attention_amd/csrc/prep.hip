@@ -468,12 +468,10 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
                              (to_f(crs[row * L.ldS + c]) - mc) * rc * to_f(cscale[j * S + c]));
         };
         auto adaln = [&](int j) {
-            gemm_stage<T, true, SPLIT, PP>(
+            gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
                 C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
                 opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j], (int64_t)nkS * 64,
-                [&](int nb, int v, float x1, float x2) {
-                    const int c = nb * 32 + acc32_col(lane);
-                    const int r = acc32_row(v, lane);
+                [&](int r, int c, float x1, float x2) {
                     const float ln = (x0(r, c) - st[r * 4 + 0]) * st[r * 4 + 1];
                     put_split<T>(opQ, opQl, r * L.ldC + c,
                                  ln * sigmoid_f(x1 + to_f(bscale[j * C + c])) + x2);
@@ -484,12 +482,11 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         __syncthreads();
         adaln(0);
         __syncthreads();
-        gemm_stage<T, true, SPLIT, PP>(
+        gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
             HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg, (int64_t)nkC * 64,
-            [&](int nb, int v, float x1, float x2) {
-                const int c = nb * 32 + acc32_col(lane);
-                const int nn = n0 + acc32_row(v, lane);
+            [&](int r, int c, float x1, float x2) {
+                const int nn = n0 + r;
                 if (nn < N) {
                     qo[(int64_t)nn * HD + c] = x1 + to_f(bq[c]);
                     go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(x2));
@@ -499,12 +496,10 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         __syncthreads();
         adaln(1);
         __syncthreads();
-        gemm_stage<T, true, SPLIT, PP>(
+        gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
             HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_v, (int64_t)nkC * 64,
-            [&](int nb, int v, float x1, float x2) {
-                const int c = nb * 32 + acc32_col(lane);
-                const int r = acc32_row(v, lane);
+            [&](int r, int c, float x1, float x2) {
                 if (n0 + r < N) {
                     ko[(int64_t)(n0 + r) * HD + c] = x1;
                     vo[vt_at(r, c)] = from_f<T>(x2);
@@ -513,12 +508,10 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
     } else {
         // in = RMS(x0) * (1 + m1) + m0, m = SiLU(c) @ w_mod[0..1]
         __syncthreads(); // statistics and SiLU(c) of every row
-        gemm_stage<T, true, SPLIT, PP>(
+        gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
             C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0], (int64_t)nkS * 64,
             opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1], (int64_t)nkS * 64,
-            [&](int nb, int v, float x1, float x2) {
-                const int c = nb * 32 + acc32_col(lane);
-                const int r = acc32_row(v, lane);
+            [&](int r, int c, float x1, float x2) {
                 const float rm = x0(r, c) * st[r * 4 + 1];
                 put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + x2) + x1);
             });
@@ -526,12 +519,10 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         for (int pass = 0; pass < 2; ++pass) {
             const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
-            gemm_stage<T, true, SPLIT, PP>(
+            gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
                 HD / 32, opQ, opQl, L.ldC, nkC, p.pk + off1, (int64_t)nkC * 64,
                 opQ, opQl, L.ldC, nkC, p.pk + off2, (int64_t)nkC * 64,
-                [&](int nb, int v, float x1, float x2) {
-                    const int c = nb * 32 + acc32_col(lane);
-                    const int r = acc32_row(v, lane);
+                [&](int r, int c, float x1, float x2) {
                     hb[r * L.hp + c] = x1;
                     const int nn = n0 + r;
                     if (nn < N) {
