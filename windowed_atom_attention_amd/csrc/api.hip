@@ -167,7 +167,7 @@ struct Mat {
     const void *src;
     int64_t ld;
     int kd, n;
-    bool post; // read by the post kernel (else by the projection kernels)
+    bool tile; // read by the 32-row tile kernels (prep, post), not k_token_proj
 };
 
 void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
@@ -185,19 +185,19 @@ void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
     off->ff_gate = off->ff_up = off->ff_out = off->w_pool = off->w_token = -1;
     if (style == ATOM_ATTN_AF3) {
         for (int j = 0; j < 3; ++j) {
-            mats->push_back({&off->w_scale[j], at(par ? par->w_scale : nullptr, (int64_t)j * S * C), C, S, C, j == 2});
-            mats->push_back({&off->w_shift[j], at(par ? par->w_shift : nullptr, (int64_t)j * S * C), C, S, C, j == 2});
+            mats->push_back({&off->w_scale[j], at(par ? par->w_scale : nullptr, (int64_t)j * S * C), C, S, C, true});
+            mats->push_back({&off->w_shift[j], at(par ? par->w_shift : nullptr, (int64_t)j * S * C), C, S, C, true});
         }
         for (int j = 0; j < 2; ++j)
             mats->push_back({&off->w_rg[j], at(par ? par->w_residual_gate : nullptr, (int64_t)j * S * C), C, S, C, true});
     } else {
         for (int j = 0; j < 6; ++j)
-            mats->push_back({&off->w_mod[j], at(par ? par->w_mod : nullptr, (int64_t)j * C), 6 * C, S, C, j >= 2});
+            mats->push_back({&off->w_mod[j], at(par ? par->w_mod : nullptr, (int64_t)j * C), 6 * C, S, C, true});
     }
-    mats->push_back({&off->w_q, par ? par->w_q : nullptr, HD, C, HD, false});
-    mats->push_back({&off->w_k, par ? par->w_k : nullptr, HD, C, HD, false});
-    mats->push_back({&off->w_v, par ? par->w_v : nullptr, HD, C, HD, false});
-    mats->push_back({&off->w_vg, par ? par->w_value_gate : nullptr, HD, C, HD, false});
+    mats->push_back({&off->w_q, par ? par->w_q : nullptr, HD, C, HD, true});
+    mats->push_back({&off->w_k, par ? par->w_k : nullptr, HD, C, HD, true});
+    mats->push_back({&off->w_v, par ? par->w_v : nullptr, HD, C, HD, true});
+    mats->push_back({&off->w_vg, par ? par->w_value_gate : nullptr, HD, C, HD, true});
     mats->push_back({&off->w_ao, par ? par->w_attention_out : nullptr, C, HD, C, true});
     mats->push_back({&off->ff_gate, par ? par->w_ff_gate : nullptr, M, C, M, true});
     mats->push_back({&off->ff_up, par ? par->w_ff_up : nullptr, M, C, M, true});
@@ -332,16 +332,17 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     PackedOffsets off;
     std::vector<Mat> mats;
     list_mats(d, style, stage, esz, par, &off, &mats);
-    // post with eight waves (32x16 strips) when its grid has at most one
-    // tile per CU; its matrices are then packed in the strip layout
+    // prep and post with eight waves (32x16 strips) when their grid has at
+    // most one tile per CU; their matrices are then packed in the strip
+    // layout
     const int64_t ntile = (d->B * d->A + 31) / 32;
-    const bool post8 = ntile <= device_cus();
+    const bool nw8 = ntile <= device_cus();
     PackArgs pa;
     std::memset(&pa, 0, sizeof(pa));
     pa.njobs = (int)mats.size();
     for (size_t i = 0; i < mats.size(); ++i)
         pa.job[i] = PackJob{mats[i].src, mats[i].ld, mats[i].kd, mats[i].n, *mats[i].off,
-                            post8 && mats[i].post ? 1 : 0};
+                            nw8 && mats[i].tile ? 1 : 0};
     pa.total = L.pack_units;
     pa.out = (uint4 *)(ws + L.packed);
 
@@ -370,7 +371,7 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.token_output = out->token_output; a.position_update = out->position_update;
     a.status = out->status;
     a.pair_scale = par->pair_scale; a.w_pair = par->w_pair;
-    a.post_nw8 = post8 ? 1 : 0;
+    a.nw8 = nw8 ? 1 : 0;
     a.pbias = af3 && prep_hosts_pair_bias(a.d, dt, st, sg) ? (float *)(ws + L.pbias) : nullptr;
 
     SlotArgs sa;

@@ -114,6 +114,10 @@ __device__ __forceinline__ float sum16(float v) {
     v += dpp_f(v, 0x140);
     return v;
 }
+// Row sum over the TPR threads of a tile row (aligned lane groups of 8 or 16).
+template <int TPR> __device__ __forceinline__ float row_sum(float x) {
+    return TPR == 16 ? sum16(x) : sum8(x);
+}
 __device__ __forceinline__ float max16(float v) {
     v = fmaxf(v, dpp_f(v, 0xB1));
     v = fmaxf(v, dpp_f(v, 0x4E));

@@ -54,9 +54,12 @@ struct BlockArgs {
     float *pool_sum;
     int *pool_int;
     // post kernel: stream the whole transition width in one pass (set by
-    // its launcher); eight waves with 32x16 output strips (its matrices are
-    // then packed in the strip layout)
-    int post_wide, post_nw8;
+    // its launcher)
+    int post_wide;
+    // grid of at most one tile per CU: the projection and post kernels run
+    // eight waves per workgroup with 32x16 output strips, and their
+    // matrices are packed in the strip layout
+    int nw8;
     // AF3 pair bias computed by extra workgroups of the projection kernel
     // (when its tiles leave most of the GPU idle): pbias[slot][4] fp32, the
     // bias of heads 0..3 of every slot (b, a, k); null when the slot kernel

@@ -72,11 +72,6 @@ size_t post_lds_bytes(const Dims &d, int dtype, int style) {
     return post_layout(d, dtype ? 2 : 4, style, 0).total;
 }
 
-// Row sum over the TPR threads of a tile row (aligned lane groups of 8 or 16).
-template <int TPR> __device__ __forceinline__ float row_sum(float x) {
-    return TPR == 16 ? sum16(x) : sum8(x);
-}
-
 // NW waves (4: 32x32 output blocks, several workgroups per CU; 8: 32x16
 // strips, two waves per SIMD for grids of at most one tile per CU), TPR =
 // 64*NW/32 threads per tile row.
@@ -505,7 +500,7 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
     b.post_wide = grid <= device_cus() && post_layout(a.d, esz, style, 1).total <= kMaxLds;
     const size_t lds = post_layout(a.d, esz, style, b.post_wide).total;
     const void *fn = nullptr;
-#define WAA_PICK(T, ST, SG) fn = a.post_nw8 ? (const void *)k_post<T, ST, SG, 8> : (const void *)k_post<T, ST, SG, 4>
+#define WAA_PICK(T, ST, SG) fn = a.nw8 ? (const void *)k_post<T, ST, SG, 8> : (const void *)k_post<T, ST, SG, 4>
     if (dtype == 0) {
         if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(float, 0, 0); else WAA_PICK(float, 0, 1); }
         else { if (stage == STAGE_ENCODER) WAA_PICK(float, 1, 0); else WAA_PICK(float, 1, 1); }
@@ -516,7 +511,7 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
 #undef WAA_PICK
     allow_lds(fn, lds);
     void *args[] = {(void *)&b};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(a.post_nw8 ? 512 : 256), args, lds, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(a.nw8 ? 512 : 256), args, lds, s);
     if (e != hipSuccess)
         return e;
     return hipGetLastError();

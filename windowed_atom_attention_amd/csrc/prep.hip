@@ -19,6 +19,8 @@
 //   The kernel also zero-fills token_output (encoder) and the status word,
 //   so that the pool kernel only writes non-empty tokens.
 // k_masks: the usable/allowed masks alone.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -175,7 +177,7 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
                 ss = fmaf(x[e + half], x[e + half], ss);
             }
         }
-        ss = sum8(ss);
+        ss = row_sum<TPR>(ss);
         const float rs = rsqrtf(ss * invD + p.eps);
         if (!ok)
             continue;
@@ -201,10 +203,10 @@ constexpr int prep_wgs() {
 // Pair-bias workgroup (AF3, extra workgroups of k_prep placed on compute
 // units its tiles leave idle): the bias of heads 0..3 of every slot of
 // [B*A*K], one pair row of NV 16-byte vectors per slot. Workgroup w of
-// nw takes chunks w, w + nw, ... of 256*RB consecutive slots (RB rows per
-// thread in flight at once, at most LIM vectors: a register budget). Slot
-// kernels that read pbias skip the pair rows.
-template <typename T, int NV, int LIM>
+// nw takes chunks w, w + nw, ... of NT*RB consecutive slots (NT threads, RB
+// rows per thread in flight at once, at most LIM vectors: a register
+// budget). Slot kernels that read pbias skip the pair rows.
+template <typename T, int NV, int LIM, int NT>
 __device__ __forceinline__ void pair_bias_wg(const BlockArgs &p, int w, int nw, unsigned char *smem) {
     constexpr int E = 16 / sizeof(T), VV = NV * E;
     constexpr int RB0 = LIM / NV < 8 ? LIM / NV : 8;
@@ -217,15 +219,15 @@ __device__ __forceinline__ void pair_bias_wg(const BlockArgs &p, int w, int nw, 
     __syncthreads();
     const float4 wsum = pair_wsum(wpart);
     const int64_t total = (int64_t)p.d.B * p.d.A * p.d.K;
-    const int64_t nchunk = (total + 256 * RB - 1) / (256 * RB);
+    const int64_t nchunk = (total + NT * RB - 1) / (NT * RB);
     const T *pair = reinterpret_cast<const T *>(p.pair);
     float4 *out = reinterpret_cast<float4 *>(p.pbias);
     for (int64_t c = w; c < nchunk; c += nw) {
-        const int64_t s0 = c * 256 * RB + threadIdx.x;
+        const int64_t s0 = c * NT * RB + threadIdx.x;
         uint4 rows[RB][NV];
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
-            const int64_t sl = min(s0 + (int64_t)i * 256, total - 1);
+            const int64_t sl = min(s0 + (int64_t)i * NT, total - 1);
 #pragma unroll
             for (int pt = 0; pt < NV; ++pt)
                 rows[i][pt] = *reinterpret_cast<const uint4 *>(pair + sl * VV + pt * E);
@@ -245,7 +247,7 @@ __device__ __forceinline__ void pair_bias_wg(const BlockArgs &p, int w, int nw, 
             pair_bias_rows<T, NV, CG>(grp, reinterpret_cast<const float4 *>(w4), wsum, p.eps, bb);
 #pragma unroll
             for (int i = 0; i < CG; ++i) {
-                const int64_t sl = s0 + (int64_t)(j + i) * 256;
+                const int64_t sl = s0 + (int64_t)(j + i) * NT;
                 if (sl < total)
                     out[sl] = make_float4(bb[i][0], bb[i][1], bb[i][2], bb[i][3]);
             }
@@ -253,14 +255,19 @@ __device__ __forceinline__ void pair_bias_wg(const BlockArgs &p, int w, int nw, 
     }
 }
 
-// 256 threads: four waves, TPR = 8 threads per tile row. Workgroups past
-// the tiles (AF3, pbias set) compute the pair bias.
-template <typename T, int STYLE, int STAGE>
-__global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(BlockArgs p) {
+// NW waves (4: 32x32 output blocks, several workgroups per CU; 8: 32x16
+// strips, two waves per SIMD, for grids of at most one tile per CU), TPR =
+// 64*NW/32 threads per tile row. Workgroups past the tiles (AF3, pbias set)
+// compute the pair bias.
+template <typename T, int STYLE, int STAGE, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>())) void k_prep(BlockArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int NT = 256, TPR = NT / 32;
+    constexpr int NT = 64 * NW, TPR = NT / 32;
+    using G = typename std::conditional<NW == 8, Blk16<T>, Blk32<T>>::type;
+    constexpr int BW = G::BW;
+    constexpr int WGS = NW == 8 ? 1 : prep_wgs<T, STYLE, STAGE>(); // workgroups per CU
     // GEMM pipeline depth: 2 where three workgroups share a CU (registers)
-    constexpr int PP = (prep_wgs<T, STYLE, STAGE>() == 3) ? 2 : 4;
+    constexpr int PP = WGS == 3 ? 2 : 4;
     const Dims d = p.d;
     const int N = d.B * d.A, C = d.C, S = d.S, HD = d.H * d.D;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -276,18 +283,18 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         const int w = blockIdx.x - ntile, nw = gridDim.x - ntile;
         // pair rows of up to 32 bytes (bf16) or 64 bytes (fp32); wider
         // bf16 rows keep the bias in the slot kernel (registers)
-        constexpr int LIM = prep_wgs<T, STYLE, STAGE>() == 3 ? 16 : 32;
+        constexpr int LIM = WGS == 3 ? 16 : 32;
         const int nv = d.V * (int)sizeof(T) / 16;
         if constexpr (sizeof(T) == 2) {
             if (nv == 1)
-                pair_bias_wg<T, 1, LIM>(p, w, nw, smem);
+                pair_bias_wg<T, 1, LIM, NT>(p, w, nw, smem);
             else
-                pair_bias_wg<T, 2, LIM>(p, w, nw, smem);
+                pair_bias_wg<T, 2, LIM, NT>(p, w, nw, smem);
         } else {
             if (nv == 2)
-                pair_bias_wg<T, 2, LIM>(p, w, nw, smem);
+                pair_bias_wg<T, 2, LIM, NT>(p, w, nw, smem);
             else
-                pair_bias_wg<T, 4, LIM>(p, w, nw, smem);
+                pair_bias_wg<T, 4, LIM, NT>(p, w, nw, smem);
         }
         return;
     }
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
     // entries of the tiles (written above by the same thread)
     {
         if (STYLE == STYLE_AF3) {
-            const float mean = sum8(xsum) / (float)C;
+            const float mean = row_sum<TPR>(xsum) / (float)C;
             float q = 0.0f;
             for (int vi = sub; vi < nvC; vi += TPR)
 #pragma unroll
@@ -411,8 +418,8 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
                     const float t = x0(row, vi * E + e) - mean;
                     q += t * t;
                 }
-            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
-            const float mc = sum8(csum) / (float)S;
+            const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
+            const float mc = row_sum<TPR>(csum) / (float)S;
             float q2 = 0.0f;
             for (int vi = sub; vi < nvS; vi += TPR)
 #pragma unroll
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
                     const float t = to_f(crs[row * L.ldS + vi * E + e]) - mc;
                     q2 += t * t;
                 }
-            const float rc = 1.0f / sqrtf(sum8(q2) / (float)S + p.eps);
+            const float rc = 1.0f / sqrtf(row_sum<TPR>(q2) / (float)S + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = mean; st[row * 4 + 1] = rstd;
                 st[row * 4 + 2] = mc;   st[row * 4 + 3] = rc;
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
                     const float t = x0(row, vi * E + e);
                     q += t * t;
                 }
-            const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
+            const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
                 st[row * 4 + 1] = rstd;
@@ -441,7 +448,7 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         }
     }
 
-    const int nkS = S / Mma32<T>::KC, nkC = C / Mma32<T>::KC;
+    const int nkS = S / G::KC, nkC = C / G::KC;
     // Q/K/V/G projections. Q and K (the logit operands) are stored in fp32,
     // V and G in the storage dtype.
     float *qo = reinterpret_cast<float *>(p.q);
@@ -468,8 +475,8 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
                              (to_f(crs[row * L.ldS + c]) - mc) * rc * to_f(cscale[j * S + c]));
         };
         auto adaln = [&](int j) {
-            gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
-                C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
+            gemm_stage<G, T, true, SPLIT, PP>(
+                C / BW, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
                 opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j], (int64_t)nkS * 64,
                 [&](int r, int c, float x1, float x2) {
                     const float ln = (x0(r, c) - st[r * 4 + 0]) * st[r * 4 + 1];
@@ -482,8 +489,8 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         __syncthreads();
         adaln(0);
         __syncthreads();
-        gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
-            HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q, (int64_t)nkC * 64,
+        gemm_stage<G, T, true, SPLIT, PP>(
+            HD / BW, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg, (int64_t)nkC * 64,
             [&](int r, int c, float x1, float x2) {
                 const int nn = n0 + r;
@@ -496,8 +503,8 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         __syncthreads();
         adaln(1);
         __syncthreads();
-        gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
-            HD / 32, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
+        gemm_stage<G, T, true, SPLIT, PP>(
+            HD / BW, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_v, (int64_t)nkC * 64,
             [&](int r, int c, float x1, float x2) {
                 if (n0 + r < N) {
@@ -508,8 +515,8 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
     } else {
         // in = RMS(x0) * (1 + m1) + m0, m = SiLU(c) @ w_mod[0..1]
         __syncthreads(); // statistics and SiLU(c) of every row
-        gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
-            C / 32, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0], (int64_t)nkS * 64,
+        gemm_stage<G, T, true, SPLIT, PP>(
+            C / BW, opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[0], (int64_t)nkS * 64,
             opA, opAl, L.ldS, nkS, p.pk + p.off.w_mod[1], (int64_t)nkS * 64,
             [&](int r, int c, float x1, float x2) {
                 const float rm = x0(r, c) * st[r * 4 + 1];
@@ -519,8 +526,8 @@ __global__ __launch_bounds__(256, (prep_wgs<T, STYLE, STAGE>())) void k_prep(Blo
         for (int pass = 0; pass < 2; ++pass) {
             const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
-            gemm_stage<Blk32<T>, T, true, SPLIT, PP>(
-                HD / 32, opQ, opQl, L.ldC, nkC, p.pk + off1, (int64_t)nkC * 64,
+            gemm_stage<G, T, true, SPLIT, PP>(
+                HD / BW, opQ, opQl, L.ldC, nkC, p.pk + off1, (int64_t)nkC * 64,
                 opQ, opQl, L.ldC, nkC, p.pk + off2, (int64_t)nkC * 64,
                 [&](int r, int c, float x1, float x2) {
                     hb[r * L.hp + c] = x1;
@@ -558,7 +565,7 @@ hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
     const int grid = (N + 31) / 32 + (a.pbias != nullptr ? pair_bias_wgs(a.d) : 0);
     const size_t lds = prep_lds_bytes(a.d, dtype, style, stage);
     const void *fn = nullptr;
-#define WAA_PICK(T, ST, SG) fn = (const void *)k_prep<T, ST, SG>
+#define WAA_PICK(T, ST, SG) fn = a.nw8 ? (const void *)k_prep<T, ST, SG, 8> : (const void *)k_prep<T, ST, SG, 4>
     if (dtype == 0) {
         if (style == STYLE_AF3) { if (stage == STAGE_ENCODER) WAA_PICK(float, 0, 0); else WAA_PICK(float, 0, 1); }
         else { if (stage == STAGE_ENCODER) WAA_PICK(float, 1, 0); else WAA_PICK(float, 1, 1); }
@@ -569,7 +576,7 @@ hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
 #undef WAA_PICK
     allow_lds(fn, lds);
     void *args[] = {(void *)&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(a.nw8 ? 512 : 256), args, lds, s);
     if (e != hipSuccess)
         return e;
     return hipGetLastError();
