@@ -415,23 +415,38 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
             __syncthreads(); // score tiles (and the tags) written
             if (hg == 0 && c == 0 && nch == 1) {
                 lose_any = 0;
+                // all tag reads first (unconditional, in range), then the
+                // tests: one LDS wait instead of one per slot
+                int tv[SPL];
+#pragma unroll
+                for (int i = 0; i < SPL; ++i)
+                    tv[i] = tag[q * kRMAX + (rel[i] >= 0 ? rel[i] - jal : 0)];
 #pragma unroll
                 for (int i = 0; i < SPL; ++i) {
-                    win[i] = rel[i] >= 0 && tag[q * kRMAX + rel[i] - jal] == k0 + i;
+                    win[i] = rel[i] >= 0 && tv[i] == k0 + i;
                     lose_any |= (rel[i] >= 0 && !win[i]) ? 1 : 0;
                 }
             }
+            // logits of the slots in this chunk: every tile read issued
+            // unconditionally (clamped into the row), then added where the
+            // slot is allowed, in the chunk and its head exists
+            {
+                float sv[kHG][SPL];
 #pragma unroll
-            for (int hh = 0; hh < kHG; ++hh) {
-                if (hg + hh >= H)
-                    break;
-                const float *sh = tile + (hh * kQB + q) * L.sp;
+                for (int hh = 0; hh < kHG; ++hh) {
+                    const float *sh = tile + (hh * kQB + q) * L.sp;
 #pragma unroll
-                for (int i = 0; i < SPL; ++i) {
-                    const int r = rel[i] - c0;
-                    if (rel[i] >= 0 && r >= 0 && r < rows)
-                        lg[i][hh] = fmaf(sh[r], scale, lg[i][hh]);
+                    for (int i = 0; i < SPL; ++i)
+                        sv[hh][i] = sh[min(max(rel[i] - c0, 0), kRMAX - 1)];
                 }
+#pragma unroll
+                for (int hh = 0; hh < kHG; ++hh)
+#pragma unroll
+                    for (int i = 0; i < SPL; ++i) {
+                        const int r = rel[i] - c0;
+                        if (hg + hh < H && rel[i] >= 0 && r >= 0 && r < rows)
+                            lg[i][hh] = fmaf(sv[hh][i], scale, lg[i][hh]);
+                    }
             }
             // score tiles read; the next chunk or P may reuse them
             if (hg == 0 && c == nch - 1)
