@@ -83,10 +83,6 @@ struct SlotArgs {
     // (then pair, pair_scale and w_pair are not read); null otherwise
     const float *pbias;
     void *attention, *o;
-    // key_index / window_mask rows may be read as 16-byte vectors: K is a
-    // multiple of the slots per thread and both bases are 16-byte aligned
-    // (set by the launcher)
-    int vec_rows;
 };
 
 // One matrix to pack: src[r*ld + c] for r < kd, c < n (storage dtype).

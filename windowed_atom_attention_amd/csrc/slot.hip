@@ -22,8 +22,6 @@ int slot_supported(const Dims &d, int dtype, int style) {
 hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) {
     SlotArgs a = a0;
     const int spl = slot_spl(a.K);
-    a.vec_rows = a.K % spl == 0 && ((uintptr_t)a.key_index & 15) == 0 &&
-                 ((uintptr_t)a.window_mask & 15) == 0;
     const Dims d{a.B, a.A, 1, a.K, 32, 32, a.H, a.D, a.V, 32, 32};
     const size_t lds = slot_lds_bytes(d, dtype, style);
     const void *fn;

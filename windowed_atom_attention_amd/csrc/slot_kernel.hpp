@@ -13,8 +13,11 @@
 // o[a, h] = sum_k w_k V[j_k, h].
 //
 // How:
-//  * Each thread owns SPL consecutive slots of one query. It loads their key
-//    ids and window bits (16-byte vectors where rows allow), gathers the key
+//  * Each thread owns SPL slots of one query, strided by 16 (thread j of a
+//    query has slots j, j+16, ...), so that the 16 threads of a query touch
+//    consecutive slots: coalesced key-id, window, pair and attention rows,
+//    and distinct LDS banks for the tile and tag cells of windowed key
+//    lists. It loads their key ids and window bits, gathers the key
 //    usability of the slots that can be allowed and, for a usable query,
 //    the pair rows of all its slots. The pair bias of every slot and head is
 //    formed in registers from one pass over the row: with d = x - x[0]
@@ -116,7 +119,9 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     const bool qin = a < A;
     const int64_t bA = (int64_t)b * A;
     const int64_t nrow = bA + (qin ? a : 0);
-    const int k0 = j16 * SPL;
+    // slot i of the thread is key slot j16 + 16*i of the query: for every i
+    // the 16 threads of a query touch 16 consecutive slots (coalesced rows,
+    // conflict-free tile and tag cells for windowed key lists)
     const SlotLayout L = slot_layout(H, VV, STYLE);
     float *wpr = reinterpret_cast<float *>(smem + L.o_wpr);
     float *tile = reinterpret_cast<float *>(smem + L.o_t);
@@ -131,16 +136,15 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     // first group is in flight from the start, each later group while the
     // previous one is reduced. Rows past the end of a ragged key list
     // re-read the last row; rows of unusable queries are loaded but unused.
-    const bool full = qin && k0 + SPL <= K; // every slot of the thread exists
-    const int nsl = !qin ? 0 : (full ? SPL : (K > k0 ? K - k0 : 0));
+    const int nsl = !qin || K <= j16 ? 0 : min(SPL, (K - j16 + 15) / 16); // slots that exist
     constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : (NV * (int)sizeof(T) <= 8 ? 2 : 1));
     constexpr int NG = SPL / GS;
     uint4 pbuf[2][GS][NVB];
-    const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + k0) * VV;
+    const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + j16) * VV;
     auto load_group = [&](uint4 (&dst)[GS][NVB], int g0) {
 #pragma unroll
         for (int ii = 0; ii < GS; ++ii) {
-            const T *src = prow + min(g0 + ii, nsl - 1) * VV;
+            const T *src = prow + (int64_t)min(g0 + ii, nsl - 1) * 16 * VV;
 #pragma unroll
             for (int pt = 0; pt < NV; ++pt)
                 dst[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
@@ -152,45 +156,25 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     // re-read the last one)
     float4 pbv[PRE ? SPL : 1];
     if (PRE && nsl > 0) {
-        const float4 *pbr = reinterpret_cast<const float4 *>(p.pbias) + nrow * K + k0;
+        const float4 *pbr = reinterpret_cast<const float4 *>(p.pbias) + nrow * K + j16;
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-            pbv[i] = pbr[min(i, nsl - 1)];
+            pbv[i] = pbr[min(i, nsl - 1) * 16];
     }
 
-    // ---- key ids and window bits of this thread's slots
+    // ---- key ids and window bits of this thread's slots (loads clamped
+    // into the row; slots past its end are marked missing)
     int64_t kid[SPL];
     bool wmv[SPL];
-    if (SPL >= 8 && p.vec_rows && full) {
-        const int64_t off = nrow * K + k0;
 #pragma unroll
-        for (int i = 0; i + 2 <= SPL; i += 2) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p.key_index + off + i);
-            kid[i] = (int64_t)(((uint64_t)v.y << 32) | v.x);
-            kid[i + 1] = (int64_t)(((uint64_t)v.w << 32) | v.z);
-        }
-        uint32_t wb[SPL / 4 > 0 ? SPL / 4 : 1] = {};
-        if constexpr (SPL == 8) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(p.window_mask + off);
-            wb[0] = w.x;
-            wb[1] = w.y;
-        } else if constexpr (SPL == 16) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(p.window_mask + off);
-            wb[0] = w.x; wb[1] = w.y; wb[2] = w.z; wb[3] = w.w;
-        }
-#pragma unroll
-        for (int i = 0; i < SPL; ++i)
-            wmv[i] = ((wb[i / 4] >> (8 * (i % 4))) & 0xffu) != 0;
-    } else {
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-            const int k = k0 + i;
+    for (int i = 0; i < SPL; ++i) {
+        const int k = j16 + 16 * i;
+        const int64_t off = nrow * K + min(k, K - 1);
+        kid[i] = p.key_index[off];
+        wmv[i] = p.window_mask[off] != 0;
+        if (!qin || k >= K) {
             kid[i] = -1;
             wmv[i] = false;
-            if (qin && k < K) {
-                kid[i] = p.key_index[nrow * K + k];
-                wmv[i] = p.window_mask[nrow * K + k] != 0;
-            }
         }
     }
     const bool qok = qin && p.usable[nrow];
@@ -269,33 +253,14 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     __syncthreads();
     const int jhi = s_hi;
 
-    // whole-vector attention stores when rows and slot groups are 16-byte
-    // multiples (attention rows then start 16-byte aligned)
-    constexpr bool kVecAtt = (SPL * (int)sizeof(T)) % 16 == 0;
-    const bool vec_att = kVecAtt && (K % SPL) == 0 && ((uintptr_t)att & 15) == 0;
     auto store_att = [&](int h, const float *w) {
-        if (!qin || k0 >= K) // K % SPL == 0 on the vector path: k0 < K means k0 + SPL <= K
+        if (!qin)
             return;
         T *arow = att + (((int64_t)b * H + h) * A + a) * K;
-        if (kVecAtt && vec_att) {
 #pragma unroll
-            for (int i = 0; i + E <= SPL; i += E) {
-                uint4 v4;
-                if constexpr (sizeof(T) == 2) {
-                    v4 = make_uint4(pack_bf16x2(w[i], w[i + 1]), pack_bf16x2(w[i + 2], w[i + 3]),
-                                    pack_bf16x2(w[i + 4], w[i + 5]), pack_bf16x2(w[i + 6], w[i + 7]));
-                } else {
-                    v4 = make_uint4(__float_as_uint(w[i]), __float_as_uint(w[i + 1]),
-                                    __float_as_uint(w[i + 2]), __float_as_uint(w[i + 3]));
-                }
-                *reinterpret_cast<uint4 *>(arow + k0 + i) = v4;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < SPL; ++i)
-                if (k0 + i < K)
-                    arow[k0 + i] = from_f<T>(w[i]);
-        }
+        for (int i = 0; i < SPL; ++i)
+            if (j16 + 16 * i < K)
+                arow[j16 + 16 * i] = from_f<T>(w[i]);
     };
 
     if (jhi < 0) {
@@ -334,7 +299,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
             if (rel[i] >= 0)
-                tag[q * kRMAX + rel[i] - jal] = k0 + i;
+                tag[q * kRMAX + rel[i] - jal] = j16 + 16 * i;
     }
 
     // V operands (B of P V) of the band chunk starting at key row c0, k
@@ -423,7 +388,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                     tv[i] = tag[q * kRMAX + (rel[i] >= 0 ? rel[i] - jal : 0)];
 #pragma unroll
                 for (int i = 0; i < SPL; ++i) {
-                    win[i] = rel[i] >= 0 && tv[i] == k0 + i;
+                    win[i] = rel[i] >= 0 && tv[i] == j16 + 16 * i;
                     lose_any |= (rel[i] >= 0 && !win[i]) ? 1 : 0;
                 }
             }
