@@ -460,6 +460,26 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
     auto vt_at = [&](int r, int c) -> int64_t {
         return ((int64_t)rb[32 + r] * HD + c) * vtp + rb[r];
     };
+    // V rows r .. r+3 (r a multiple of 4) of channel c into the transposed
+    // copy: one 4-element vector store when the four atoms are consecutive
+    // there (A a multiple of 4: same batch, aligned), else element by element
+    const bool vt_vec = d.A % 4 == 0;
+    auto store_v4 = [&](int r, int c, float v0, float v1, float v2, float v3) {
+        if (vt_vec && n0 + r + 3 < N) {
+            T *dst = vo + vt_at(r, c);
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            } else {
+                *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+            }
+        } else {
+            const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + r + j < N)
+                    vo[vt_at(r + j, c)] = from_f<T>(v[j]);
+        }
+    };
     if (STYLE == STYLE_AF3) {
         // A_j(x0) = LN(x0) * sigmoid(a_j @ w_scale[j] + b_scale[j]) + a_j @ w_shift[j]
         // with a_j = LN(c) * cond_scale[j]; A_0 feeds Q and G, A_1 K and V.
@@ -503,13 +523,19 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         __syncthreads();
         adaln(1);
         __syncthreads();
-        gemm_stage<G, T, true, SPLIT, PP>(
+        gemm_stage_blk<G, T, true, SPLIT, PP>(
             HD / BW, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_k, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_v, (int64_t)nkC * 64,
-            [&](int r, int c, float x1, float x2) {
-                if (n0 + r < N) {
-                    ko[(int64_t)(n0 + r) * HD + c] = x1;
-                    vo[vt_at(r, c)] = from_f<T>(x2);
+            [&](int nb, const typename G::Acc &x1, const typename G::Acc &x2) {
+                const int c = nb * BW + G::col(lane);
+#pragma unroll
+                for (int i = 0; i < G::NE; i += 4) {
+                    const int r = G::row(i, lane);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (n0 + r + j < N)
+                            ko[(int64_t)(n0 + r + j) * HD + c] = G::at(x1, i + j);
+                    store_v4(r, c, G::at(x2, i), G::at(x2, i + 1), G::at(x2, i + 2), G::at(x2, i + 3));
                 }
             });
     } else {
@@ -526,17 +552,22 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         for (int pass = 0; pass < 2; ++pass) {
             const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
-            gemm_stage<G, T, true, SPLIT, PP>(
+            gemm_stage_blk<G, T, true, SPLIT, PP>(
                 HD / BW, opQ, opQl, L.ldC, nkC, p.pk + off1, (int64_t)nkC * 64,
                 opQ, opQl, L.ldC, nkC, p.pk + off2, (int64_t)nkC * 64,
-                [&](int r, int c, float x1, float x2) {
-                    hb[r * L.hp + c] = x1;
-                    const int nn = n0 + r;
-                    if (nn < N) {
-                        if (pass == 0)
-                            go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(x2));
-                        else
-                            vo[vt_at(r, c)] = from_f<T>(x2);
+                [&](int nb, const typename G::Acc &x1, const typename G::Acc &x2) {
+                    const int c = nb * BW + G::col(lane);
+#pragma unroll
+                    for (int i = 0; i < G::NE; i += 4) {
+                        const int r = G::row(i, lane);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            hb[(r + j) * L.hp + c] = G::at(x1, i + j);
+                            if (pass == 0 && n0 + r + j < N)
+                                go[(int64_t)(n0 + r + j) * HD + c] = from_f<T>(sigmoid_f(G::at(x2, i + j)));
+                        }
+                        if (pass == 1)
+                            store_v4(r, c, G::at(x2, i), G::at(x2, i + 1), G::at(x2, i + 2), G::at(x2, i + 3));
                     }
                 });
             __syncthreads();

@@ -511,13 +511,15 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
             __syncthreads();
         }
         if (hv) {
+            // the block's rows of o from one base (32-bit offsets inside)
+            T *ob = og + (bA + a0) * HD + hw * DK + acc16_col(lane);
 #pragma unroll
             for (int t = 0; t < NDB; ++t) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int aq = a0 + acc16_row(v, lane);
-                    if (aq < A)
-                        og[(bA + aq) * HD + hw * DK + t * 16 + acc16_col(lane)] = from_f<T>(oacc[t][v]);
+                    const int r = acc16_row(v, lane);
+                    if (a0 + r < A)
+                        ob[r * HD + t * 16] = from_f<T>(oacc[t][v]);
                 }
             }
         }
