@@ -21,7 +21,16 @@ int slot_supported(const Dims &d, int dtype, int style) {
 
 hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) {
     SlotArgs a = a0;
-    const int spl = slot_spl(a.K);
+    // threads per query: 32 (the 512-thread form) for the AF3
+    // precomputed-bias variant, which runs only on small grids, and for
+    // ESMFold2 grids of at most two blocks per CU; 16 otherwise
+    const int nblk = a.B * ((a.A + kQB - 1) / kQB);
+    int tq;
+    if (style == STYLE_AF3)
+        tq = a.pbias != nullptr ? 32 : 16;
+    else
+        tq = nblk <= 2 * device_cus() ? 32 : 16;
+    const int spl = slot_spl(a.K, tq);
     const Dims d{a.B, a.A, 1, a.K, 32, 32, a.H, a.D, a.V, 32, 32};
     const size_t lds = slot_lds_bytes(d, dtype, style);
     const void *fn;
@@ -31,14 +40,14 @@ hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) 
         const int nv = a.V * (dtype ? 2 : 4) / 16;
         fn = dtype == 0 ? pick_slot_af3_f32(spl, a.D, nv) : pick_slot_af3_bf16(spl, a.D, nv);
     } else {
-        fn = pick_slot_esm(dtype, spl, a.D);
+        fn = pick_slot_esm(dtype, spl, a.D, tq);
     }
     if (fn == nullptr)
         return hipErrorInvalidValue;
     allow_lds(fn, lds);
     const int grid = a.B * ((a.A + kQB - 1) / kQB);
     void *args[] = {(void *)&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), args, lds, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kQB * tq), args, lds, s);
     if (e != hipSuccess)
         return e;
     return hipGetLastError();

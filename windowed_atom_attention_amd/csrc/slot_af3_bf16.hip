@@ -6,10 +6,10 @@ namespace waa {
 
 const void *pick_slot_af3_bf16(int spl, int D, int nv) {
     switch (nv) {
-    case 1: return pick_slot_sd<bf16_t, STYLE_AF3, 1>(spl, D);
-    case 2: return pick_slot_sd<bf16_t, STYLE_AF3, 2>(spl, D);
-    case 3: return pick_slot_sd<bf16_t, STYLE_AF3, 3>(spl, D);
-    case 4: return pick_slot_sd<bf16_t, STYLE_AF3, 4>(spl, D);
+    case 1: return pick_slot_sd<bf16_t, STYLE_AF3, 1, 16>(spl, D);
+    case 2: return pick_slot_sd<bf16_t, STYLE_AF3, 2, 16>(spl, D);
+    case 3: return pick_slot_sd<bf16_t, STYLE_AF3, 3, 16>(spl, D);
+    case 4: return pick_slot_sd<bf16_t, STYLE_AF3, 4, 16>(spl, D);
     default: return nullptr;
     }
 }

@@ -6,8 +6,8 @@ namespace waa {
 
 const void *pick_slot_af3_f32(int spl, int D, int nv) {
     switch (nv) {
-    case 2: return pick_slot_sd<float, STYLE_AF3, 2>(spl, D);
-    case 4: return pick_slot_sd<float, STYLE_AF3, 4>(spl, D);
+    case 2: return pick_slot_sd<float, STYLE_AF3, 2, 16>(spl, D);
+    case 4: return pick_slot_sd<float, STYLE_AF3, 4, 16>(spl, D);
     default: return nullptr;
     }
 }

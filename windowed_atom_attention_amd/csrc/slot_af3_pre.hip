@@ -5,8 +5,8 @@
 namespace waa {
 
 const void *pick_slot_af3_pre(int dtype, int spl, int D) {
-    return dtype == 0 ? pick_slot_sd<float, STYLE_AF3, 0>(spl, D)
-                      : pick_slot_sd<bf16_t, STYLE_AF3, 0>(spl, D);
+    return dtype == 0 ? pick_slot_sd<float, STYLE_AF3, 0, 32>(spl, D)
+                      : pick_slot_sd<bf16_t, STYLE_AF3, 0, 32>(spl, D);
 }
 
 } // namespace waa

@@ -75,7 +75,10 @@ __host__ __device__ inline SlotLayout slot_layout(int H, int V, int style) {
     return L;
 }
 
-__host__ __device__ inline int slot_spl(int K) { return K <= 16 ? 1 : (K <= 128 ? 8 : 16); }
+// Slots per thread for K and TQ threads per query (16 or 32).
+__host__ __device__ inline int slot_spl(int K, int tq) {
+    return tq == 32 ? (K <= 32 ? 1 : (K <= 128 ? 4 : 8)) : (K <= 16 ? 1 : (K <= 128 ? 8 : 16));
+}
 
 // P operand (probabilities, fp32 in LDS) as a 16-byte chunk of T.
 template <typename T>
@@ -93,8 +96,13 @@ template <> __device__ __forceinline__ uint4 p_chunk<bf16_t>(const float *src) {
 // NV: 16-byte vectors per AF3 pair row (V = NV * 16 / sizeof(T)), or 0
 // when the AF3 pair bias comes precomputed (p.pbias); 1 for ESMFold2, which
 // has no pair input.
-template <typename T, int STYLE, int SPL, int DK, int NV>
-__global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
+// TQ: threads per query (16: 256-thread workgroups, one wave per head,
+// three workgroups per CU; 32: 512-thread workgroups, two waves per head
+// splitting the score blocks and the output channels, half the slots and
+// registers per thread, two workgroups per CU -- for grids of at most about
+// two blocks per CU, where more waves per block shorten its latency chain).
+template <typename T, int STYLE, int SPL, int DK, int NV, int TQ>
+__global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void k_slot(SlotArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_lo, s_hi;
     constexpr int KC = Mma16<T>::KC, QU = Mma16<T>::QUARTER;
@@ -106,21 +114,25 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     constexpr int NKQ = DK / 16;                     // fp32 k chunks of Q.K
     constexpr int NDB = DK / 16;                     // 16-wide output blocks of o
     constexpr int NVC = kRMAX / KC;                  // P V k chunks of a full band chunk
-    constexpr int VG = NVC < 8 / NDB ? NVC : (8 / NDB > 0 ? 8 / NDB : 1); // V chunks per load batch (<= 8 vectors)
+    constexpr int NDBW0 = (DK / 16) / ((kQB * TQ) / 64 / kHG) > 0 ? (DK / 16) / ((kQB * TQ) / 64 / kHG) : 1;
+    constexpr int VG = NVC < 8 / NDBW0 ? NVC : (8 / NDBW0 > 0 ? 8 / NDBW0 : 1); // V chunks per load batch (<= 8 vectors)
     constexpr int CBG = DK <= 32 ? 4 : (DK == 64 ? 2 : 1); // score blocks per load batch
     const int A = p.A, K = p.K, H = p.H, HD = H * DK;
     const int nqb = (A + kQB - 1) / kQB;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int b = wg / nqb, a0 = (wg % nqb) * kQB;
+    constexpr int NT = kQB * TQ, NSUB = NT / 64 / kHG; // threads; waves per head
+    constexpr int NDBW = NDB / NSUB > 0 ? NDB / NSUB : 1;  // output blocks of o per wave
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int q = tid >> 4, j16 = tid & 15;
+    const int q = tid / TQ, jq = tid % TQ;
+    const int hsl = wave % kHG, hsub = wave / kHG; // head slot and sub-wave of this wave
     const int g = lane >> 4, l16 = lane & 15;
     const int a = a0 + q;
     const bool qin = a < A;
     const int64_t bA = (int64_t)b * A;
     const int64_t nrow = bA + (qin ? a : 0);
-    // slot i of the thread is key slot j16 + 16*i of the query: for every i
-    // the 16 threads of a query touch 16 consecutive slots (coalesced rows,
+    // slot i of the thread is key slot jq + TQ*i of the query: for every i
+    // the TQ threads of a query touch consecutive slots (coalesced rows,
     // conflict-free tile and tag cells for windowed key lists)
     const SlotLayout L = slot_layout(H, VV, STYLE);
     float *wpr = reinterpret_cast<float *>(smem + L.o_wpr);
@@ -136,15 +148,15 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     // first group is in flight from the start, each later group while the
     // previous one is reduced. Rows past the end of a ragged key list
     // re-read the last row; rows of unusable queries are loaded but unused.
-    const int nsl = !qin || K <= j16 ? 0 : min(SPL, (K - j16 + 15) / 16); // slots that exist
+    const int nsl = !qin || K <= jq ? 0 : min(SPL, (K - jq + TQ - 1) / TQ); // slots that exist
     constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : (NV * (int)sizeof(T) <= 8 ? 2 : 1));
     constexpr int NG = SPL / GS;
     uint4 pbuf[2][GS][NVB];
-    const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + j16) * VV;
+    const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + jq) * VV;
     auto load_group = [&](uint4 (&dst)[GS][NVB], int g0) {
 #pragma unroll
         for (int ii = 0; ii < GS; ++ii) {
-            const T *src = prow + (int64_t)min(g0 + ii, nsl - 1) * 16 * VV;
+            const T *src = prow + (int64_t)min(g0 + ii, nsl - 1) * TQ * VV;
 #pragma unroll
             for (int pt = 0; pt < NV; ++pt)
                 dst[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
@@ -156,10 +168,10 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     // re-read the last one)
     float4 pbv[PRE ? SPL : 1];
     if (PRE && nsl > 0) {
-        const float4 *pbr = reinterpret_cast<const float4 *>(p.pbias) + nrow * K + j16;
+        const float4 *pbr = reinterpret_cast<const float4 *>(p.pbias) + nrow * K + jq;
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-            pbv[i] = pbr[min(i, nsl - 1) * 16];
+            pbv[i] = pbr[min(i, nsl - 1) * TQ];
     }
 
     // ---- key ids and window bits of this thread's slots (loads clamped
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     bool wmv[SPL];
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
-        const int k = j16 + 16 * i;
+        const int k = jq + TQ * i;
         const int64_t off = nrow * K + min(k, K - 1);
         kid[i] = p.key_index[off];
         wmv[i] = p.window_mask[off] != 0;
@@ -259,8 +271,8 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
         T *arow = att + (((int64_t)b * H + h) * A + a) * K;
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-            if (j16 + 16 * i < K)
-                arow[j16 + 16 * i] = from_f<T>(w[i]);
+            if (jq + TQ * i < K)
+                arow[jq + TQ * i] = from_f<T>(w[i]);
     };
 
     if (jhi < 0) {
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
         for (int h = 0; h < H; ++h)
             store_att(h, zw);
         if (qin)
-            for (int c = j16; c < HD; c += 16)
+            for (int c = jq; c < HD; c += TQ)
                 og[nrow * HD + c] = from_f<T>(0.0f);
         return;
     }
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     const int span = jhi + 1 - jal;
     const int nch = (span + kRMAX - 1) / kRMAX;
     const float scale = p.inv_sqrt_d;
-    float *twave = tile + wave * kQB * L.sp; // this wave's head tile
+    float *twave = tile + hsl * kQB * L.sp; // this wave's head tile
     // Unique writer of each probability cell (query, key row): every
     // allowed slot writes its slot index into the tag tile and the one
     // whose index survives writes the cell with a plain store; the others
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
             if (rel[i] >= 0)
-                tag[q * kRMAX + rel[i] - jal] = j16 + 16 * i;
+                tag[q * kRMAX + rel[i] - jal] = jq + TQ * i;
     }
 
     // V operands (B of P V) of the band chunk starting at key row c0, k
@@ -308,19 +320,19 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
     // Chunks past the last re-read it; rows past the batch's last atom are
     // the zero padding of the transposed rows (at most 31 past A). All VG
     // chunks are in flight together.
-    auto load_v = [&](uint4 (&dst)[VG][NDB], int c0, int kc0, int nkc, int hw) {
+    auto load_v = [&](uint4 (&dst)[VG][NDBW], int c0, int kc0, int nkc, int hw, int t0) {
         const int hc = min(hw, H - 1);
         const T *vrow = vtg + ((int64_t)b * HD + hc * DK) * vtp;
 #pragma unroll
         for (int j = 0; j < VG; ++j) {
             const int r = c0 + min(kc0 + j, nkc - 1) * KC + g * QU;
 #pragma unroll
-            for (int t = 0; t < NDB; ++t)
-                dst[j][t] = *reinterpret_cast<const uint4 *>(vrow + (int64_t)(t * 16 + l16) * vtp + r);
+            for (int t = 0; t < NDBW; ++t)
+                dst[j][t] = *reinterpret_cast<const uint4 *>(vrow + (int64_t)((t0 + t) * 16 + l16) * vtp + r);
         }
     };
     for (int hg = 0; hg < H; hg += kHG) {
-        const int hw = hg + wave; // this wave's head in the S and P V products
+        const int hw = hg + hsl; // this wave's head in the S and P V products
         const bool hv = hw < H;
         // Q fragments (A operand of S): query row l16, fp32
         uint4 qf[NKQ];
@@ -349,7 +361,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
             const int rows = min(kRMAX, jhi + 1 - c0);
             const int ncb = (rows + 15) / 16;
             if (hv) {
-                for (int cb0 = 0; cb0 < ncb; cb0 += CBG) {
+                for (int cb0 = hsub * CBG; cb0 < ncb; cb0 += NSUB * CBG) {
                     f32x4_t acc[CBG];
                     uint4 kb[CBG][NKQ];
 #pragma unroll
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                     tv[i] = tag[q * kRMAX + (rel[i] >= 0 ? rel[i] - jal : 0)];
 #pragma unroll
                 for (int i = 0; i < SPL; ++i) {
-                    win[i] = rel[i] >= 0 && tv[i] == j16 + 16 * i;
+                    win[i] = rel[i] >= 0 && tv[i] == jq + TQ * i;
                     lose_any |= (rel[i] >= 0 && !win[i]) ? 1 : 0;
                 }
             }
@@ -420,10 +432,10 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                 __syncthreads();
         }
         // the tiles become the (zeroed) probability tiles
-        for (int i = tid; i < kHG * kQB * L.sp / 4; i += 256)
+        for (int i = tid; i < kHG * kQB * L.sp / 4; i += NT)
             reinterpret_cast<float4 *>(tile)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-        // masked softmax per head over the row: 16 lanes per query
+        // masked softmax per head over the row: TQ lanes per query
 #pragma unroll
         for (int hh = 0; hh < kHG; ++hh) {
             if (hg + hh >= H)
@@ -433,7 +445,7 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
             for (int i = 0; i < SPL; ++i)
                 if (rel[i] >= 0)
                     m = fmaxf(m, lg[i][hh]);
-            m = max16(m);
+            m = TQ == 32 ? fmaxf(max16(m), __shfl_xor(max16(m), 16)) : max16(m);
             float w[SPL];
             float sum = 0.0f;
 #pragma unroll
@@ -442,6 +454,8 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                 sum += w[i];
             }
             sum = sum16(sum);
+            if (TQ == 32)
+                sum += __shfl_xor(sum, 16);
             const float inv = sum > 0.0f ? __builtin_amdgcn_rcpf(sum) : 0.0f;
 #pragma unroll
             for (int i = 0; i < SPL; ++i) {
@@ -453,9 +467,12 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
         __syncthreads(); // probability tiles zero
 
         // o = P V per head; P scattered by key id (repeats add up)
-        f32x4_t oacc[NDB];
+        // this wave's output blocks of o: t0 .. t0 + NDBW - 1 (none past NDB)
+        const int t0 = hsub * NDBW;
+        const bool pv = hv && t0 < NDB;
+        f32x4_t oacc[NDBW];
 #pragma unroll
-        for (int t = 0; t < NDB; ++t)
+        for (int t = 0; t < NDBW; ++t)
             oacc[t] = zero4();
         for (int c = 0; c < nch; ++c) {
             const int c0 = jal + c * kRMAX;
@@ -489,32 +506,36 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
                 }
             }
             __syncthreads();
-            if (hv) {
+            if (pv) {
                 const float *prow = twave + l16 * L.sp + g * QU;
                 for (int kc0 = 0; kc0 < nkc; kc0 += VG) {
-                    uint4 vb[VG][NDB];
-                    load_v(vb, c0, kc0, nkc, hw);
+                    uint4 vb[VG][NDBW];
+                    load_v(vb, c0, kc0, nkc, hw, t0);
 #pragma unroll
                     for (int j = 0; j < VG; ++j) {
                         if (kc0 + j < nkc) {
                             const uint4 av = p_chunk<T>(prow + (kc0 + j) * KC);
 #pragma unroll
-                            for (int t = 0; t < NDB; ++t)
+                            for (int t = 0; t < NDBW; ++t)
                                 Mma16<T>::mma(oacc[t], av, vb[j][t]);
                         }
                     }
                 }
-                // leave this wave's P tile zero for the next chunk / head group
-                for (int i = lane; i < kQB * L.sp / 4; i += 64)
-                    reinterpret_cast<float4 *>(twave)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            __syncthreads();
+            if (c + 1 < nch || hg + kHG < H)
+                __syncthreads(); // P read: the next chunk or head group may rewrite the tiles
+            if (c + 1 < nch) {
+                // the next chunk's probability tiles start from zero
+                for (int i = tid; i < kHG * kQB * L.sp / 4; i += NT)
+                    reinterpret_cast<float4 *>(tile)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                __syncthreads();
+            }
         }
-        if (hv) {
+        if (pv) {
             // the block's rows of o from one base (32-bit offsets inside)
-            T *ob = og + (bA + a0) * HD + hw * DK + acc16_col(lane);
+            T *ob = og + (bA + a0) * HD + hw * DK + t0 * 16 + acc16_col(lane);
 #pragma unroll
-            for (int t = 0; t < NDB; ++t) {
+            for (int t = 0; t < NDBW; ++t) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int r = acc16_row(v, lane);
@@ -530,34 +551,43 @@ __global__ __launch_bounds__(256, SPL >= 16 ? 2 : 3) void k_slot(SlotArgs p) {
 // width and pair vectors per row (defined in the instantiating units).
 const void *pick_slot_af3_f32(int spl, int D, int nv);
 const void *pick_slot_af3_bf16(int spl, int D, int nv);
-const void *pick_slot_esm(int dtype, int spl, int D);
+const void *pick_slot_esm(int dtype, int spl, int D, int tq);
 const void *pick_slot_af3_pre(int dtype, int spl, int D);
 
-template <typename T, int STYLE, int NV>
-const void *pick_slot_sd(int spl, int D) {
+template <typename T, int STYLE, int NV, int TQ, int S1, int S2, int S3>
+const void *pick_slot_tq(int spl, int D) {
     switch (spl) {
-    case 1:
+    case S1:
         switch (D) {
-        case 16: return (const void *)k_slot<T, STYLE, 1, 16, NV>;
-        case 32: return (const void *)k_slot<T, STYLE, 1, 32, NV>;
-        case 64: return (const void *)k_slot<T, STYLE, 1, 64, NV>;
-        default: return (const void *)k_slot<T, STYLE, 1, 128, NV>;
+        case 16: return (const void *)k_slot<T, STYLE, S1, 16, NV, TQ>;
+        case 32: return (const void *)k_slot<T, STYLE, S1, 32, NV, TQ>;
+        case 64: return (const void *)k_slot<T, STYLE, S1, 64, NV, TQ>;
+        default: return (const void *)k_slot<T, STYLE, S1, 128, NV, TQ>;
         }
-    case 8:
+    case S2:
         switch (D) {
-        case 16: return (const void *)k_slot<T, STYLE, 8, 16, NV>;
-        case 32: return (const void *)k_slot<T, STYLE, 8, 32, NV>;
-        case 64: return (const void *)k_slot<T, STYLE, 8, 64, NV>;
-        default: return (const void *)k_slot<T, STYLE, 8, 128, NV>;
+        case 16: return (const void *)k_slot<T, STYLE, S2, 16, NV, TQ>;
+        case 32: return (const void *)k_slot<T, STYLE, S2, 32, NV, TQ>;
+        case 64: return (const void *)k_slot<T, STYLE, S2, 64, NV, TQ>;
+        default: return (const void *)k_slot<T, STYLE, S2, 128, NV, TQ>;
         }
     default:
         switch (D) {
-        case 16: return (const void *)k_slot<T, STYLE, 16, 16, NV>;
-        case 32: return (const void *)k_slot<T, STYLE, 16, 32, NV>;
-        case 64: return (const void *)k_slot<T, STYLE, 16, 64, NV>;
-        default: return (const void *)k_slot<T, STYLE, 16, 128, NV>;
+        case 16: return (const void *)k_slot<T, STYLE, S3, 16, NV, TQ>;
+        case 32: return (const void *)k_slot<T, STYLE, S3, 32, NV, TQ>;
+        case 64: return (const void *)k_slot<T, STYLE, S3, 64, NV, TQ>;
+        default: return (const void *)k_slot<T, STYLE, S3, 128, NV, TQ>;
         }
     }
+}
+
+// Kernel for slots per thread spl (slot_spl(K, TQ)) and head width D.
+template <typename T, int STYLE, int NV, int TQ>
+const void *pick_slot_sd(int spl, int D) {
+    if constexpr (TQ == 32)
+        return pick_slot_tq<T, STYLE, NV, 32, 1, 4, 8>(spl, D);
+    else
+        return pick_slot_tq<T, STYLE, NV, 16, 1, 8, 16>(spl, D);
 }
 
 } // namespace waa
