@@ -109,9 +109,17 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t
 //  x0 in the storage type (exact for an encoder: x0 is the atom row; a bf16
 //  decoder keeps the rest of the fp32 sum atom + token projection in a
 //  second tile); row statistics, usability, atom/batch index per row; the
-//  raw condition (AF3: LN(c) * cond_scale[j] is built twice); the A operand
+//  raw condition (AF3 but the bf16 decoder: LN(c) * cond_scale[j] is built
+//  twice); the A operand
 //  tile (hi + lo in bf16), which ESMFold2 reuses as the fp32 staging tile
 //  of its Q/K projections; the Q/K/V/G input tile (hi + lo in bf16).
+// AF3 keeps the raw condition tile except in the bf16 decoder, whose x0
+// needs a second tile: there the condition rows are read again from global
+// memory (L2) where needed, so that three workgroups fit a CU.
+__host__ __device__ constexpr bool prep_keeps_c(int esz, int style, int stage) {
+    return style == STYLE_AF3 && !(esz == 2 && stage == STAGE_DECODER);
+}
+
 __host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int style, int stage) {
     PrepLayout L;
     const bool split = esz == 2;
@@ -128,7 +136,7 @@ __host__ __device__ inline PrepLayout prep_layout(const Dims &d, int esz, int st
     L.o_us = o; o += 32;
     L.o_rb = o; o += 64 * 4; // per row: atom index within its batch, then batch
     L.o_cr = o;
-    if (style == STYLE_AF3)
+    if (prep_keeps_c(esz, style, stage))
         o += tS;
     L.o_opA = L.o_hb = o;
     L.o_opAl = o + tS;
@@ -193,11 +201,10 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
     }
 }
 
-// Workgroups per CU the LDS layout allows: three for bf16 except the AF3
-// decoder (whose x0 needs a hi + lo pair), two otherwise.
+// Workgroups per CU the LDS layout allows: three for bf16, two for fp32.
 template <typename T, int STYLE, int STAGE>
 constexpr int prep_wgs() {
-    return sizeof(T) == 2 && !(STYLE == STYLE_AF3 && STAGE == STAGE_DECODER) ? 3 : 2;
+    return sizeof(T) == 2 ? 3 : 2;
 }
 
 // Pair-bias workgroup (AF3, extra workgroups of k_prep placed on compute
@@ -278,6 +285,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
     constexpr int E = 16 / sizeof(T);
     constexpr bool SPLIT = sizeof(T) == 2;
     constexpr bool XLO = SPLIT && STAGE == STAGE_DECODER; // x0 kept as hi + lo
+    constexpr bool KEEPC = prep_keeps_c(sizeof(T), STYLE, STAGE); // raw condition tile
     const int ntile = (N + 31) / 32;
     if (STYLE == STYLE_AF3 && (int)blockIdx.x >= ntile) {
         const int w = blockIdx.x - ntile, nw = gridDim.x - ntile;
@@ -401,11 +409,19 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
                     if (STYLE == STYLE_ESM) // A operand of the modulation: SiLU(c)
                         put_split<T>(opA, opAl, row * L.ldS + vi * E + e, silu_f(cv[e]));
                 }
-                if (STYLE == STYLE_AF3)
+                if (KEEPC)
                     *reinterpret_cast<uint4 *>(crs + row * L.ldS + vi * E) = cvv;
             }
         }
     }
+    // 16 bytes vi of this row's sanitised condition: from the tile, or read
+    // again (L2) where the tile is not kept
+    auto c_vec = [&](int vi) -> uint4 {
+        if constexpr (KEEPC)
+            return *reinterpret_cast<const uint4 *>(crs + row * L.ldS + vi * E);
+        else
+            return u ? *reinterpret_cast<const uint4 *>(cr + vi * E) : make_uint4(0, 0, 0, 0);
+    };
     // row statistics of x0 (and of c for AF3), each thread over its own
     // entries of the tiles (written above by the same thread)
     {
@@ -421,12 +437,15 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
             const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             const float mc = row_sum<TPR>(csum) / (float)S;
             float q2 = 0.0f;
-            for (int vi = sub; vi < nvS; vi += TPR)
+            for (int vi = sub; vi < nvS; vi += TPR) {
+                float cv[E];
+                unpack16<T>(c_vec(vi), cv);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float t = to_f(crs[row * L.ldS + vi * E + e]) - mc;
+                    const float t = cv[e] - mc;
                     q2 += t * t;
                 }
+            }
             const float rc = 1.0f / sqrtf(row_sum<TPR>(q2) / (float)S + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = mean; st[row * 4 + 1] = rstd;
@@ -490,9 +509,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         const T *bq = reinterpret_cast<const T *>(p.b_q);
         auto build_a = [&](int j) {
             const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
-            for (int c = sub; c < S; c += TPR)
-                put_split<T>(opA, opAl, row * L.ldS + c,
-                             (to_f(crs[row * L.ldS + c]) - mc) * rc * to_f(cscale[j * S + c]));
+            for (int vi = sub; vi < nvS; vi += TPR) {
+                float cv[E], sc[E];
+                unpack16<T>(c_vec(vi), cv);
+                unpack16<T>(*reinterpret_cast<const uint4 *>(cscale + j * S + vi * E), sc);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    put_split<T>(opA, opAl, row * L.ldS + vi * E + e, (cv[e] - mc) * rc * sc[e]);
+            }
         };
         auto adaln = [&](int j) {
             gemm_stage<G, T, true, SPLIT, PP>(
