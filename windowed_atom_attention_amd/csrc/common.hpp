@@ -316,13 +316,12 @@ __device__ __forceinline__ f32x4_t zero4() {
 // zero), and partial column sums wpart[2][4] (lanes of one head reduced
 // per wave; V <= 32). Every thread of the (>= 128-thread) block calls it.
 template <typename T>
-__device__ __forceinline__ void pair_weights(const T *ps, const T *wp, int V, int H, float *w4,
-                                             float *wpart) {
+__device__ __forceinline__ void pair_weights_put(T sv, T wv, int V, int H, float *w4,
+                                                 float *wpart) {
     const int i = threadIdx.x;
     float w = 0.0f;
     if (i < V * 4) {
-        const int v = i / 4, h = i % 4;
-        w = h < H ? to_f(ps[v]) * to_f(wp[v * H + h]) : 0.0f;
+        w = i % 4 < H ? to_f(sv) * to_f(wv) : 0.0f;
         w4[i] = w;
     }
     if (i < 128) { // waves 0 and 1 (whole waves): sum over the lanes of head i % 4
@@ -334,6 +333,25 @@ __device__ __forceinline__ void pair_weights(const T *ps, const T *wp, int V, in
             wpart[(i >> 6) * 4 + (i & 3)] = w;
     }
 }
+// The two factors of this thread's weight, loaded unconditionally (indices
+// clamped; the values of threads past V * 4 are not used), so that a
+// kernel can issue them early and store them later with pair_weights_put.
+template <typename T>
+__device__ __forceinline__ void pair_weights_load(const T *ps, const T *wp, int V, int H, T &sv,
+                                                  T &wv) {
+    const int i = threadIdx.x;
+    const int v = min(i / 4, V - 1), h = min(i % 4, H - 1);
+    sv = ps[v];
+    wv = wp[v * H + h];
+}
+template <typename T>
+__device__ __forceinline__ void pair_weights(const T *ps, const T *wp, int V, int H, float *w4,
+                                             float *wpart) {
+    T sv, wv;
+    pair_weights_load<T>(ps, wp, V, H, sv, wv);
+    pair_weights_put<T>(sv, wv, V, H, w4, wpart);
+}
+
 // Column sums of the weights (after a barrier that follows pair_weights).
 __device__ __forceinline__ float4 pair_wsum(const float *wpart) {
     const float4 a = reinterpret_cast<const float4 *>(wpart)[0];
@@ -400,6 +418,19 @@ __device__ __forceinline__ void zero_vt_pad(T *vt, int B, int HD, int A, int wg,
     for (int64_t i = wg; i < (int64_t)B * HD; i += nwg)
         for (int e = threadIdx.x; e < w; e += blockDim.x)
             vt[i * pitch + A + e] = (T)0;
+}
+
+// Load / store of a V at a 32-bit byte offset from a base pointer. With a
+// base that is uniform over the wave this is the scalar-base addressing form
+// (64-bit base in scalar registers, 32-bit offset per lane): no 64-bit
+// address arithmetic and one vector register per address.
+template <typename V>
+__device__ __forceinline__ V ld_off(const void *base, uint32_t bytes) {
+    return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + bytes);
+}
+template <typename V>
+__device__ __forceinline__ void st_off(void *base, uint32_t bytes, V v) {
+    *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + bytes) = v;
 }
 
 // Map the hardware dispatch order (round-robin over the 8 XCDs of MI355X)

@@ -131,6 +131,10 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
     const bool qin = a < A;
     const int64_t bA = (int64_t)b * A;
     const int64_t nrow = bA + (qin ? a : 0);
+    // addresses: 64-bit bases uniform over the workgroup (scalar registers)
+    // plus 32-bit per-thread offsets
+    const int64_t row0 = bA + a0;          // first query row of the block
+    const uint32_t qr = qin ? (uint32_t)q : 0u; // this thread's row in the block (clamped)
     // slot i of the thread is key slot jq + TQ*i of the query: for every i
     // the TQ threads of a query touch consecutive slots (coalesced rows,
     // conflict-free tile and tag cells for windowed key lists)
@@ -144,59 +148,76 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
     T *att = reinterpret_cast<T *>(p.attention);
     T *og = reinterpret_cast<T *>(p.o);
 
-    // ---- AF3 pair rows of this thread's slots, in groups of GS slots: the
-    // first group is in flight from the start, each later group while the
-    // previous one is reduced. Rows past the end of a ragged key list
-    // re-read the last row; rows of unusable queries are loaded but unused.
-    const int nsl = !qin || K <= jq ? 0 : min(SPL, (K - jq + TQ - 1) / TQ); // slots that exist
-    constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : (NV * (int)sizeof(T) <= 8 ? 2 : 1));
-    constexpr int NG = SPL / GS;
-    uint4 pbuf[2][GS][NVB];
-    const T *prow = reinterpret_cast<const T *>(p.pair) + (nrow * K + jq) * VV;
-    auto load_group = [&](uint4 (&dst)[GS][NVB], int g0) {
-#pragma unroll
-        for (int ii = 0; ii < GS; ++ii) {
-            const T *src = prow + (int64_t)min(g0 + ii, nsl - 1) * TQ * VV;
-#pragma unroll
-            for (int pt = 0; pt < NV; ++pt)
-                dst[ii][pt] = *reinterpret_cast<const uint4 *>(src + pt * E);
-        }
-    };
-    if (FUSED && nsl > 0)
-        load_group(pbuf[0], 0);
-    // precomputed pair bias of the thread's slots (slots past a ragged end
-    // re-read the last one)
-    float4 pbv[PRE ? SPL : 1];
-    if (PRE && nsl > 0) {
-        const float4 *pbr = reinterpret_cast<const float4 *>(p.pbias) + nrow * K + jq;
-#pragma unroll
-        for (int i = 0; i < SPL; ++i)
-            pbv[i] = pbr[min(i, nsl - 1) * TQ];
-    }
-
+    // AF3 pair weight factors (first: the wait for them covers nothing else)
+    T psv{}, wpv{};
+    if (FUSED)
+        pair_weights_load<T>(reinterpret_cast<const T *>(p.pair_scale),
+                             reinterpret_cast<const T *>(p.w_pair), VV, H, psv, wpv);
     // ---- key ids and window bits of this thread's slots (loads clamped
-    // into the row; slots past its end are marked missing)
+    // into the row; slots past its end are marked missing), and the
+    // query's usability, unconditionally. Issued before the pair rows:
+    // loads return in order, so the key-id chain (ids, then the key
+    // usability gather) does not wait for the pair rows.
+    const uint8_t uq = ld_off<uint8_t>(p.usable + row0, qr);
     int64_t kid[SPL];
     bool wmv[SPL];
+    const int64_t *kib = p.key_index + row0 * K;
+    const uint8_t *wmb = p.window_mask + row0 * K;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
         const int k = jq + TQ * i;
-        const int64_t off = nrow * K + min(k, K - 1);
-        kid[i] = p.key_index[off];
-        wmv[i] = p.window_mask[off] != 0;
+        const uint32_t off = qr * (uint32_t)K + (uint32_t)min(k, K - 1);
+        kid[i] = ld_off<int64_t>(kib, off * 8u);
+        wmv[i] = ld_off<uint8_t>(wmb, off) != 0;
         if (!qin || k >= K) {
             kid[i] = -1;
             wmv[i] = false;
         }
     }
-    const bool qok = qin && p.usable[nrow];
+    // ---- AF3 pair rows of this thread's slots, in groups of GS slots: the
+    // first group (both, when there are two) is in flight from the start,
+    // each later group while the previous one is reduced. Loads are issued
+    // unconditionally (a load in a branch makes every later wait cover it):
+    // rows past the end of a ragged key list re-read the last row, threads
+    // without slots read the query's last row, rows of unusable queries are
+    // loaded but unused.
+    const int nsl = !qin || K <= jq ? 0 : min(SPL, (K - jq + TQ - 1) / TQ); // slots that exist
+    constexpr int GS = SPL < 4 ? SPL : (NV <= 2 ? 4 : (NV * (int)sizeof(T) <= 8 ? 2 : 1));
+    constexpr int NG = SPL / GS;
+    uint4 pbuf[2][GS][NVB];
+    const int slast = max(nsl, 1) - 1;
+    const T *pairb = reinterpret_cast<const T *>(p.pair) + row0 * K * VV;
+    const uint32_t prow = (qr * (uint32_t)K + (uint32_t)min(jq, K - 1)) * VV;
+    auto load_group = [&](uint4 (&dst)[GS][NVB], int g0) {
+#pragma unroll
+        for (int ii = 0; ii < GS; ++ii) {
+            const uint32_t src = prow + (uint32_t)(min(g0 + ii, slast) * TQ * VV);
+#pragma unroll
+            for (int pt = 0; pt < NV; ++pt)
+                dst[ii][pt] = ld_off<uint4>(pairb, (src + pt * E) * (uint32_t)sizeof(T));
+        }
+    };
+    // (two groups take the registers of the double buffer)
+    if (FUSED) {
+        load_group(pbuf[0], 0);
+        if (NG == 2)
+            load_group(pbuf[1], GS);
+    }
+    // precomputed pair bias of the thread's slots (clamped as the rows)
+    float4 pbv[PRE ? SPL : 1];
+    if (PRE) {
+        const float4 *pbb = reinterpret_cast<const float4 *>(p.pbias) + row0 * K;
+        const uint32_t pbr = qr * (uint32_t)K + (uint32_t)min(jq, K - 1);
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            pbv[i] = ld_off<float4>(pbb, (pbr + (uint32_t)(min(i, slast) * TQ)) * 16u);
+    }
+
+    const bool qok = qin && uq != 0;
     if (tid == 0) {
         s_lo = INT_MAX;
         s_hi = -1;
     }
-    if (FUSED)
-        pair_weights<T>(reinterpret_cast<const T *>(p.pair_scale),
-                        reinterpret_cast<const T *>(p.w_pair), VV, H, wpr, wpr + VV * 4);
     bool cand[SPL];
     uint8_t uj[SPL];
 #pragma unroll
@@ -206,10 +227,14 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
         cand[i] = qok && wmv[i] && j >= 0 && j < A && (p.radius < 0 || dist <= p.radius);
         uj[i] = 0;
     }
+    // key usability of every slot, loaded unconditionally (ids clamped into
+    // the batch) so that all SPL loads are in flight together; used (with
+    // cand) only once the pair bias is formed
 #pragma unroll
     for (int i = 0; i < SPL; ++i)
-        if (cand[i])
-            uj[i] = p.usable[bA + kid[i]];
+        uj[i] = ld_off<uint8_t>(p.usable + bA, (uint32_t)min(max(kid[i], (int64_t)0), (int64_t)A - 1));
+    if (FUSED)
+        pair_weights_put<T>(psv, wpv, VV, H, wpr, wpr + VV * 4);
 
     // ---- AF3 pair bias per slot and head (H <= 4), in registers
     float beta[SPL][kHG];
@@ -224,7 +249,7 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
         const float4 ws = pair_wsum(wpr + VV * 4);
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-            if (gi + 1 < NG)
+            if (NG > 2 && gi + 1 < NG)
                 load_group(pbuf[(gi + 1) & 1], (gi + 1) * GS);
             if (!qok)
                 continue;
@@ -268,11 +293,13 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
     auto store_att = [&](int h, const float *w) {
         if (!qin)
             return;
-        T *arow = att + (((int64_t)b * H + h) * A + a) * K;
+        // one per-thread offset; the slot's stride goes into the (uniform) base
+        T *ab = att + (((int64_t)b * H + h) * A + a0) * K;
+        const uint32_t ao = (uint32_t)(q * K + jq) * (uint32_t)sizeof(T);
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
             if (jq + TQ * i < K)
-                arow[jq + TQ * i] = from_f<T>(w[i]);
+                st_off<T>(ab + TQ * i, ao, from_f<T>(w[i]));
     };
 
     if (jhi < 0) {
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
             const int r = c0 + min(kc0 + j, nkc - 1) * KC + g * QU;
 #pragma unroll
             for (int t = 0; t < NDBW; ++t)
-                dst[j][t] = *reinterpret_cast<const uint4 *>(vrow + (int64_t)((t0 + t) * 16 + l16) * vtp + r);
+                dst[j][t] = ld_off<uint4>(vrow, (uint32_t)(((t0 + t) * 16 + l16) * vtp + r) * (uint32_t)sizeof(T));
         }
     };
     for (int hg = 0; hg < H; hg += kHG) {
@@ -342,7 +369,7 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
             for (int kc = 0; kc < NKQ; ++kc) {
                 qf[kc] = make_uint4(0, 0, 0, 0);
                 if (hv && aq < A)
-                    qf[kc] = *reinterpret_cast<const uint4 *>(qg + (bA + aq) * HD + hw * DK + kc * 16 + g * 4);
+                    qf[kc] = ld_off<uint4>(qg + row0 * HD, (uint32_t)(l16 * HD + hw * DK + kc * 16 + g * 4) * 4u);
             }
         }
         // lg: the pair bias until a slot's logit is added to it (each slot
@@ -372,8 +399,8 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
                         for (int kc = 0; kc < NKQ; ++kc) {
                             kb[t][kc] = make_uint4(0, 0, 0, 0);
                             if (r < rows)
-                                kb[t][kc] = *reinterpret_cast<const uint4 *>(
-                                    kg + (bA + c0 + r) * HD + hw * DK + kc * 16 + g * 4);
+                                kb[t][kc] = ld_off<uint4>(kg + (bA + c0) * HD,
+                                                          (uint32_t)(r * HD + hw * DK + kc * 16 + g * 4) * 4u);
                         }
                     }
 #pragma unroll
