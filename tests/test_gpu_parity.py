@@ -43,6 +43,9 @@ SMALL = [
     ("0", dict(A=600)),
     ("0", dict(A=450, K=40, style="esmfold2", dtype=torch.bfloat16)),
     ("0", dict(A=300, K=200, dtype=torch.bfloat16, stage="decoder")),
+    # bf16 rows that are not whole 16-byte vectors (attention stored per value)
+    ("0", dict(A=200, K=45, dtype=torch.bfloat16)),
+    ("0", dict(A=200, K=21, style="esmfold2", dtype=torch.bfloat16)),
     # every pair-row width the slot kernel specialises on (AF3 bf16: 8, 16,
     # 24, 32 channels; fp32: 8, 16), and wider heads
     ("0", dict(A=200, V=24, K=64, dtype=torch.bfloat16)),

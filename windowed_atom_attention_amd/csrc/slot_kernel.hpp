@@ -290,11 +290,36 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
     __syncthreads();
     const int jhi = s_hi;
 
+    // Attention rows of one head. For bf16 rows of whole 16-byte vectors
+    // (one fitting the query's 512-byte row of the tag tile, which is free
+    // by the time the weights exist) the values pass through that row so
+    // that each thread writes 16-byte vectors instead of 2-byte values: the
+    // row belongs to this wave's query, and the LDS accesses of one wave
+    // take effect in order, so no barrier is needed (compiler barriers keep
+    // the order of the accesses). fp32 values are stored directly.
+    constexpr int SROW = kRMAX * 4 / (int)sizeof(T); // staging row, elements
+    const bool vec_att = sizeof(T) == 2 && (K * (int)sizeof(T)) % 16 == 0 && K <= SROW &&
+                         (reinterpret_cast<uintptr_t>(p.attention) & 15) == 0;
+    T *stg = reinterpret_cast<T *>(smem + L.o_tag) + q * SROW;
     auto store_att = [&](int h, const float *w) {
+        T *ab = att + (((int64_t)b * H + h) * A + a0) * K;
+        if (vec_att) {
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < SPL; ++i)
+                if (jq + TQ * i < K)
+                    stg[jq + TQ * i] = from_f<T>(w[i]);
+            __asm__ volatile("" ::: "memory");
+            if (qin)
+                for (int c = jq * E; c < K; c += TQ * E)
+                    st_off<uint4>(ab, (uint32_t)(q * K + c) * (uint32_t)sizeof(T),
+                                  *reinterpret_cast<const uint4 *>(stg + c));
+            __asm__ volatile("" ::: "memory");
+            return;
+        }
         if (!qin)
             return;
         // one per-thread offset; the slot's stride goes into the (uniform) base
-        T *ab = att + (((int64_t)b * H + h) * A + a0) * K;
         const uint32_t ao = (uint32_t)(q * K + jq) * (uint32_t)sizeof(T);
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
