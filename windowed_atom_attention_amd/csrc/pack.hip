@@ -19,31 +19,41 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
     // argument block), then of this thread's unit (a job spans at least 128
     // units, so at most a step or two further)
     const int64_t u0 = (int64_t)blockIdx.x * 256;
+    // the block's first job: how many later jobs start at or before u0 (job
+    // offsets ascend); independent scalar loads rather than a dependent chain
     int j = 0;
-    while (j + 1 < a.njobs && u0 >= a.job[j + 1].dst)
-        ++j;
+#pragma unroll
+    for (int k = 1; k < kMaxPackJobs; ++k)
+        j += (k < a.njobs && u0 >= a.job[k].dst) ? 1 : 0;
     const int64_t u = u0 + threadIdx.x;
     if (u >= a.total)
         return;
-    while (j + 1 < a.njobs && u >= a.job[j + 1].dst)
-        ++j;
-    const PackJob &jb = a.job[j];
-    const int64_t local = u - jb.dst;
+    // a job spans at least 128 units, so a block's lanes lie in job j, j+1
+    // or j+2: uniform loads of the three, then a per-lane choice
+    const int j1 = min(j + 1, kMaxPackJobs - 1), j2 = min(j + 2, kMaxPackJobs - 1);
+    const bool in1 = j + 1 < a.njobs && u >= a.job[j1].dst;
+    const bool in2 = j + 2 < a.njobs && u >= a.job[j2].dst;
+    const PackJob &ja = a.job[j], &jb1 = a.job[j1], &jb2 = a.job[j2];
+    const int64_t dst = in2 ? jb2.dst : (in1 ? jb1.dst : ja.dst);
+    const int64_t ld = in2 ? jb2.ld : (in1 ? jb1.ld : ja.ld);
+    const int kd = in2 ? jb2.kd : (in1 ? jb1.kd : ja.kd);
+    const int strip = in2 ? jb2.strip : (in1 ? jb1.strip : ja.strip);
+    const T *src = reinterpret_cast<const T *>(in2 ? jb2.src : (in1 ? jb1.src : ja.src));
+    const int64_t local = u - dst;
     const int lane = (int)(local & 63);
     const int64_t rest = local >> 6;
-    const int KC = jb.strip ? Mma16<T>::KC : Mma32<T>::KC;
-    const int nkc = jb.kd / KC;
+    const int KC = strip ? Mma16<T>::KC : Mma32<T>::KC;
+    const int nkc = kd / KC;
     const int kc = (int)(rest % nkc);
     const int nb = (int)(rest / nkc);
-    const T *src = reinterpret_cast<const T *>(jb.src);
-    const int col = jb.strip ? nb * 16 + (lane & 15) : nb * 32 + (lane & 31);
-    const int row0 = kc * KC + (jb.strip ? (lane >> 4) * Mma16<T>::QUARTER
-                                         : (lane >> 5) * Mma32<T>::HALF);
+    const int col = strip ? nb * 16 + (lane & 15) : nb * 32 + (lane & 31);
+    const int row0 = kc * KC + (strip ? (lane >> 4) * Mma16<T>::QUARTER
+                                      : (lane >> 5) * Mma32<T>::HALF);
     constexpr int E = 16 / sizeof(T);
     T vals[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        vals[e] = src[(int64_t)(row0 + e) * jb.ld + col];
+        vals[e] = src[(int64_t)(row0 + e) * ld + col];
     uint4 out;
     __builtin_memcpy(&out, vals, 16);
     a.out[u] = out;
