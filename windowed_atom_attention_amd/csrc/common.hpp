@@ -63,6 +63,19 @@ __device__ __forceinline__ void unpack16(uint4 v, float *out) {
     }
 }
 
+// 16/sizeof(T) floats -> 16 bytes of storage-type values (round to nearest
+// even for bf16).
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float *in) {
+    if constexpr (sizeof(T) == 4) {
+        return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                          __float_as_uint(in[3]));
+    } else {
+        return make_uint4(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                          pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
+    }
+}
+
 // Logistic function from e = exp(-|z|) in (0, 1]: 1/(1+e) for z >= 0 and
 // e/(1+e) below, so a very negative argument keeps its tiny (down to
 // subnormal) value instead of 1 - 1. exp2f keeps subnormal results (the

@@ -131,6 +131,13 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
         const int nvC = C / E, nvS = S / E, nvH = HD / E;
         const int nvmax = nvC > nvS ? (nvC > nvH ? nvC : nvH) : (nvS > nvH ? nvS : nvH);
         constexpr int RV = sizeof(T) == 2 ? 2 : 4; // vectors per array and thread in one round
+        // AF3 with the condition row in one round: its values stay in
+        // registers for the statistics and LN(c) * cond_scale[2] (no LDS
+        // re-read), and the cond_scale[2] vectors load with the rows
+        const T *cscale2 = reinterpret_cast<const T *>(p.cond_scale) + 2 * S;
+        const bool keepc = STYLE == STYLE_AF3 && nvS <= RV * TPR;
+        float ck[RV][E];
+        uint4 vs[RV];
         float csum = 0.0f;
         for (int base = sub; base < nvmax; base += RV * TPR) {
             uint4 va[RV], vc[RV], vo[RV], vg[RV];
@@ -142,6 +149,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
                 vc[j] = *reinterpret_cast<const uint4 *>(cr + min(vi, nvS - 1) * E);
                 vo[j] = *reinterpret_cast<const uint4 *>(orow + min(vi, nvH - 1) * E);
                 vg[j] = *reinterpret_cast<const uint4 *>(grow + min(vi, nvH - 1) * E);
+                if (STYLE == STYLE_AF3)
+                    vs[j] = *reinterpret_cast<const uint4 *>(cscale2 + min(vi, nvS - 1) * E);
                 const uint4 z = make_uint4(0, 0, 0, 0);
                 if (!u) {
                     va[j] = z;
@@ -172,18 +181,23 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
                             xv[e] += vt[j][e];
                     }
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        xs[row * L.xp + vi * E + e] = xv[e];
+                    for (int e = 0; e < E; e += 4)
+                        *reinterpret_cast<float4 *>(xs + row * L.xp + vi * E + e) =
+                            make_float4(xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
                 }
                 if (vi < nvS) {
                     float cv[E];
                     unpack16<T>(vc[j], cv);
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        opC[row * L.ldS + vi * E + e] =
-                            STYLE == STYLE_AF3 ? from_f<T>(cv[e]) : from_f<T>(silu_f(cv[e]));
                         csum += cv[e];
+                        ck[j][e] = cv[e];
+                        if (STYLE != STYLE_AF3)
+                            cv[e] = silu_f(cv[e]);
                     }
+                    // (AF3: the raw condition, already in the storage type)
+                    *reinterpret_cast<uint4 *>(opC + row * L.ldS + vi * E) =
+                        STYLE == STYLE_AF3 ? vc[j] : pack16<T>(cv);
                 }
                 if (vi < nvH) {
                     float ov[E], gv[E];
@@ -191,7 +205,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
                     unpack16<T>(vg[j], gv);
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        opU[row * L.ldHD + vi * E + e] = from_f<T>(ov[e] * gv[e]);
+                        ov[e] *= gv[e];
+                    *reinterpret_cast<uint4 *>(opU + row * L.ldHD + vi * E) = pack16<T>(ov);
                 }
             }
         }
@@ -199,6 +214,30 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
             // c_2 = LN(c) * cond_scale[2], each thread on its own entries of
             // opC (written above by the same thread: no barrier needed)
             const float mc = row_sum<TPR>(csum) / (float)S;
+            if (keepc) {
+                float q = 0.0f;
+#pragma unroll
+                for (int j = 0; j < RV; ++j)
+                    if (sub + j * TPR < nvS)
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const float t = ck[j][e] - mc;
+                            q += t * t;
+                        }
+                const float rc = 1.0f / sqrtf(row_sum<TPR>(q) / (float)S + p.eps);
+#pragma unroll
+                for (int j = 0; j < RV; ++j) {
+                    const int vi = sub + j * TPR;
+                    if (vi < nvS) {
+                        float sc[E];
+                        unpack16<T>(vs[j], sc);
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            sc[e] *= (ck[j][e] - mc) * rc;
+                        *reinterpret_cast<uint4 *>(opC2 + row * L.ldS + vi * E) = pack16<T>(sc);
+                    }
+                }
+            } else {
             float q = 0.0f;
             for (int vi = sub; vi < nvS; vi += TPR)
 #pragma unroll
@@ -216,6 +255,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
                     const int c = vi * E + e;
                     opC2[row * L.ldS + c] = from_f<T>((to_f(opC[row * L.ldS + c]) - mc) * rc * sc[e]);
                 }
+            }
             }
         }
     }
