@@ -104,13 +104,18 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
     T *opZ = reinterpret_cast<T *>(smem + L.o_opZ);
     T *opH = reinterpret_cast<T *>(smem + L.o_opH);
 
-    const bool u = inb && p.usable[n];
+    // the row's usability and token, loaded unconditionally (row 0 past
+    // the end) so that the row loads below go out without waiting for them
+    const int64_t nc = inb ? n : 0;
+    const uint8_t usv = p.usable[nc];
+    const int64_t tkr = p.atom_to_token[nc];
+    const bool u = inb && usv;
     const int b = inb ? n / d.A : 0;
     int *rkey = reinterpret_cast<int *>(smem + L.o_key);
     if (sub == 0) {
         us[row] = u;
         if (STAGE == STAGE_ENCODER)
-            rkey[row] = u ? b * d.T + (int)p.atom_to_token[n] : -1;
+            rkey[row] = u ? b * d.T + (int)tkr : -1;
     }
     {
         // entry state (as the prep kernel builds it), condition (raw for the
@@ -119,14 +124,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
         // rows are converted into LDS
         // rows past the end read row 0 (loads are unconditional; the values
         // of unusable or missing rows are replaced by zeros after the load)
-        const int64_t nc = inb ? n : 0;
         const T *ar = reinterpret_cast<const T *>(p.atom) + nc * C;
         const T *cr = reinterpret_cast<const T *>(p.condition) + nc * S;
         const T *orow = reinterpret_cast<const T *>(p.o) + nc * HD;
         const T *grow = reinterpret_cast<const T *>(p.g) + nc * HD;
-        int64_t tk = 0;
-        if (STAGE == STAGE_DECODER && u)
-            tk = p.atom_to_token[n];
+        // (a usable atom's token is in range; others read token 0, unused)
+        const int64_t tk = tkr >= 0 && tkr < d.T ? tkr : 0;
         const float *tp = p.tokproj + ((int64_t)b * d.T + tk) * C;
         const int nvC = C / E, nvS = S / E, nvH = HD / E;
         const int nvmax = nvC > nvS ? (nvC > nvH ? nvC : nvH) : (nvS > nvH ? nvS : nvH);

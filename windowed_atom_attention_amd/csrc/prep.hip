@@ -338,10 +338,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         return v;
     };
 
-    // Row loads first (unconditional, rows past the end read row 0; values
-    // of unusable atoms are replaced by zeros: selected, never multiplied),
-    // while the usability of the row is resolved.
+    // Loads first, all unconditional (rows past the end read row 0; values
+    // of unusable atoms are replaced by zeros: selected, never multiplied):
+    // the atom's token and validity, the atom and condition rows, then the
+    // token's validity and (decoder) its projection row at the clamped
+    // token index. Two dependent steps, with the rows in flight meanwhile.
     const int64_t nc = inb ? n : 0;
+    const int64_t tk = p.atom_to_token[nc];
+    const uint8_t vld = p.valid[nc];
     const T *ar = reinterpret_cast<const T *>(p.atom) + nc * C;
     const T *cr = reinterpret_cast<const T *>(p.condition) + nc * S;
     const int nvC = C / E, nvS = S / E, nvmax = nvC > nvS ? nvC : nvS;
@@ -354,12 +358,19 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         vc[j] = *reinterpret_cast<const uint4 *>(cr + min(vi, nvS - 1) * E);
     }
     const int b = inb ? n / d.A : 0;
-    int64_t tk = 0;
-    bool u = false;
-    if (inb) {
-        tk = p.atom_to_token[n];
-        u = p.valid[n] && tk >= 0 && tk < d.T && p.token_valid[(int64_t)b * d.T + tk];
+    const int64_t tkc = tk >= 0 && tk < d.T ? tk : 0;
+    const uint8_t tvl = p.token_valid[(int64_t)b * d.T + tkc];
+    const float *tp = p.tokproj + ((int64_t)b * d.T + tkc) * C;
+    float4 tpv[STAGE == STAGE_DECODER ? RV * E / 4 : 1]; // first round's projection values
+    if (STAGE == STAGE_DECODER) {
+#pragma unroll
+        for (int j = 0; j < RV; ++j)
+#pragma unroll
+            for (int t = 0; t < E / 4; ++t)
+                tpv[j * (E / 4) + t] =
+                    *reinterpret_cast<const float4 *>(tp + min(sub + j * TPR, nvC - 1) * E + 4 * t);
     }
+    const bool u = inb && vld && tk >= 0 && tk < d.T && tvl;
     if (sub == 0) {
         us[row] = u;
         rb[row] = inb ? n - b * d.A : 0; // atom index within its batch
@@ -367,7 +378,6 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         if (inb)
             p.usable[n] = u;
     }
-    const float *tp = p.tokproj + ((int64_t)b * d.T + (u ? tk : 0)) * C;
     float xsum = 0.0f, csum = 0.0f;
     for (int base = sub; base < nvmax; base += RV * TPR) {
         if (base != sub) { // later rounds (wide C or S)
@@ -386,8 +396,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
                 unpack16<T>(va[j], xv);
                 if (STAGE == STAGE_DECODER) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        xv[e] += tp[vi * E + e];
+                    for (int t = 0; t < E / 4; ++t) {
+                        const float4 f = base == sub ? tpv[j * (E / 4) + t]
+                                                     : *reinterpret_cast<const float4 *>(tp + vi * E + 4 * t);
+                        xv[4 * t + 0] += f.x; xv[4 * t + 1] += f.y;
+                        xv[4 * t + 2] += f.z; xv[4 * t + 3] += f.w;
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
@@ -419,9 +433,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
     auto c_vec = [&](int vi) -> uint4 {
         if constexpr (KEEPC)
             return *reinterpret_cast<const uint4 *>(crs + row * L.ldS + vi * E);
-        else
-            return u ? *reinterpret_cast<const uint4 *>(cr + vi * E) : make_uint4(0, 0, 0, 0);
+        else { // unconditional load, then the selection (a load in a branch waits alone)
+            const uint4 v = *reinterpret_cast<const uint4 *>(cr + vi * E);
+            return u ? v : make_uint4(0, 0, 0, 0);
+        }
     };
+    const bool c1 = nvS <= RV * TPR; // the condition row took one round: vc holds it
     // row statistics of x0 (and of c for AF3), each thread over its own
     // entries of the tiles (written above by the same thread)
     {
@@ -437,13 +454,27 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
             const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             const float mc = row_sum<TPR>(csum) / (float)S;
             float q2 = 0.0f;
-            for (int vi = sub; vi < nvS; vi += TPR) {
-                float cv[E];
-                unpack16<T>(c_vec(vi), cv);
+            if (c1) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float t = cv[e] - mc;
-                    q2 += t * t;
+                for (int j = 0; j < RV; ++j)
+                    if (sub + j * TPR < nvS) {
+                        float cv[E];
+                        unpack16<T>(u ? vc[j] : make_uint4(0, 0, 0, 0), cv);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const float t = cv[e] - mc;
+                            q2 += t * t;
+                        }
+                    }
+            } else {
+                for (int vi = sub; vi < nvS; vi += TPR) {
+                    float cv[E];
+                    unpack16<T>(c_vec(vi), cv);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float t = cv[e] - mc;
+                        q2 += t * t;
+                    }
                 }
             }
             const float rc = 1.0f / sqrtf(row_sum<TPR>(q2) / (float)S + p.eps);
@@ -509,6 +540,28 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         const T *bq = reinterpret_cast<const T *>(p.b_q);
         auto build_a = [&](int j) {
             const float mc = st[row * 4 + 2], rc = st[row * 4 + 3];
+            if (c1) { // one round: every load issued before any is used
+                uint4 cvv[RV], scv[RV];
+#pragma unroll
+                for (int jj = 0; jj < RV; ++jj) {
+                    const int vi = min(sub + jj * TPR, nvS - 1);
+                    cvv[jj] = c_vec(vi);
+                    scv[jj] = *reinterpret_cast<const uint4 *>(cscale + j * S + vi * E);
+                }
+#pragma unroll
+                for (int jj = 0; jj < RV; ++jj) {
+                    const int vi = sub + jj * TPR;
+                    if (vi < nvS) {
+                        float cv[E], sc[E];
+                        unpack16<T>(cvv[jj], cv);
+                        unpack16<T>(scv[jj], sc);
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            put_split<T>(opA, opAl, row * L.ldS + vi * E + e, (cv[e] - mc) * rc * sc[e]);
+                    }
+                }
+                return;
+            }
             for (int vi = sub; vi < nvS; vi += TPR) {
                 float cv[E], sc[E];
                 unpack16<T>(c_vec(vi), cv);
