@@ -606,6 +606,28 @@ __device__ __forceinline__ void gemm_stage(int nblocks, const T *A1, const T *A1
     }
 }
 
+// gemm_stage whose epilogue also receives a per-column value v = colv(c)
+// (a bias or scale entry), read before the block's products so that its
+// load overlaps them instead of waiting in the epilogue:
+// epi(r, c, x1, x2, v).
+template <typename L, typename T, bool DUAL, bool SPLIT, int P = 4, typename Col, typename Epi>
+__device__ __forceinline__ void gemm_stage_cv(int nblocks, const T *A1, const T *A1lo, int lda1,
+                                              int nk1, const uint4 *B1, int64_t bs1,
+                                              const T *A2, const T *A2lo, int lda2, int nk2,
+                                              const uint4 *B2, int64_t bs2, Col &&colv, Epi &&epi) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int nb = wave; nb < nblocks; nb += L::NW) {
+        const int c0 = nb * L::BW + L::col(lane);
+        const float cv = colv(c0);
+        typename L::Acc a1 = L::zero(), a2 = L::zero();
+        L::template pipe<DUAL, SPLIT, P>(a1, A1, A1lo, lda1, nk1, B1 + nb * bs1,
+                                         a2, A2, A2lo, lda2, nk2, DUAL ? B2 + nb * bs2 : B1);
+#pragma unroll
+        for (int i = 0; i < L::NE; ++i)
+            epi(L::row(i, lane), c0, L::at(a1, i), DUAL ? L::at(a2, i) : 0.0f, cv);
+    }
+}
+
 // gemm_stage with a block epilogue: epi_blk(nb, a1, a2) receives the whole
 // accumulators of block nb (for epilogues that group elements, e.g. runs of
 // consecutive rows: elements 4m .. 4m+3 of a lane are rows L::row(4m) + 0..3

@@ -271,11 +271,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
     {
         const T *brg = reinterpret_cast<const T *>(p.b_rg);
         const int64_t offg = STYLE == STYLE_AF3 ? p.off.w_rg[0] : p.off.w_mod[2];
-        gemm_stage<G, T, true, false, PP>(
+        gemm_stage_cv<G, T, true, false, PP>(
             C / BW, opU, nullptr, L.ldHD, nkHD, p.pk + p.off.w_ao, (int64_t)nkHD * 64,
             opC, nullptr, L.ldS, nkS, p.pk + offg, (int64_t)nkS * 64,
-            [&](int r, int c, float x1, float x2) {
-                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(x2 + to_f(brg[c])) : x2;
+            [&](int c) { return STYLE == STYLE_AF3 ? to_f(brg[c]) : 0.0f; },
+            [&](int r, int c, float x1, float x2, float bg) {
+                const float gate = STYLE == STYLE_AF3 ? sigmoid_f(x2 + bg) : x2;
                 xs[r * L.xp + c] += gate * x1;
             });
     }
@@ -316,14 +317,15 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
         const T *opz = STYLE == STYLE_AF3 ? opC2 : opC;
         const int64_t o1 = STYLE == STYLE_AF3 ? p.off.w_scale[2] : p.off.w_mod[3];
         const int64_t o2 = STYLE == STYLE_AF3 ? p.off.w_shift[2] : p.off.w_mod[4];
-        gemm_stage<G, T, true, false, PP>(
+        gemm_stage_cv<G, T, true, false, PP>(
             C / BW, opz, nullptr, L.ldS, nkS, p.pk + o1, (int64_t)nkS * 64,
             opz, nullptr, L.ldS, nkS, p.pk + o2, (int64_t)nkS * 64,
-            [&](int r, int c, float x1, float x2) {
+            [&](int c) { return STYLE == STYLE_AF3 ? to_f(bsc[2 * C + c]) : 0.0f; },
+            [&](int r, int c, float x1, float x2, float bs) {
                 const float xn = (xs[r * L.xp + c] - st[r * 4 + 0]) * st[r * 4 + 1];
                 float z;
                 if (STYLE == STYLE_AF3)
-                    z = xn * sigmoid_f(x1 + to_f(bsc[2 * C + c])) + x2;
+                    z = xn * sigmoid_f(x1 + bs) + x2;
                 else
                     z = xn * (1.0f + x2) + x1;
                 opZ[r * L.ldC + c] = from_f<T>(z);
@@ -344,6 +346,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
         for (int cg = 0; cg < C / BW; cg += NW) {
             const int nb = cg + wave;
             const bool own = nb < C / BW;
+            // the gate bias of this lane's column, loaded before the products
+            const float bias =
+                STYLE == STYLE_AF3 ? to_f(brg[C + min(nb, C / BW - 1) * BW + G::col(lane)]) : 0.0f;
             Acc acc = G::zero(), ga = G::zero();
             for (int m0 = 0; m0 < M; m0 += MCW) {
                 const int mc = M - m0 < MCW ? M - m0 : MCW;
@@ -372,7 +377,6 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
             }
             if (own) {
                 const int c = nb * BW + G::col(lane);
-                const float bias = STYLE == STYLE_AF3 ? to_f(brg[C + c]) : 0.0f;
 #pragma unroll
                 for (int i = 0; i < G::NE; ++i) {
                     const int r = G::row(i, lane);
@@ -513,13 +517,32 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
         const T *rb = reinterpret_cast<const T *>(p.readout_bias);
         const T *wr = reinterpret_cast<const T *>(p.w_readout);
         float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f;
-        for (int c = sub; c < C; c += TPR) {
-            float z = (xr[c] - mean) * rstd * to_f(rs[c]);
-            if (STYLE == STYLE_ESM)
-                z += to_f(rb[c]);
-            acc0 += z * to_f(wr[c * 3 + 0]);
-            acc1 += z * to_f(wr[c * 3 + 1]);
-            acc2 += z * to_f(wr[c * 3 + 2]);
+        // RU columns per step, their parameter loads issued together
+        // (clamped) before any is used: one L2 wait per step
+        constexpr int RU = 8;
+        for (int c0 = sub; c0 < C; c0 += RU * TPR) {
+            T rsv[RU], rbv[RU], w0[RU], w1[RU], w2[RU];
+#pragma unroll
+            for (int k = 0; k < RU; ++k) {
+                const int c = min(c0 + k * TPR, C - 1);
+                rsv[k] = rs[c];
+                rbv[k] = STYLE == STYLE_ESM ? rb[c] : T{};
+                w0[k] = wr[c * 3 + 0];
+                w1[k] = wr[c * 3 + 1];
+                w2[k] = wr[c * 3 + 2];
+            }
+#pragma unroll
+            for (int k = 0; k < RU; ++k) {
+                const int c = c0 + k * TPR;
+                if (c < C) {
+                    float z = (xr[c] - mean) * rstd * to_f(rsv[k]);
+                    if (STYLE == STYLE_ESM)
+                        z += to_f(rbv[k]);
+                    acc0 += z * to_f(w0[k]);
+                    acc1 += z * to_f(w1[k]);
+                    acc2 += z * to_f(w2[k]);
+                }
+            }
         }
         acc0 = row_sum<TPR>(acc0);
         acc1 = row_sum<TPR>(acc1);

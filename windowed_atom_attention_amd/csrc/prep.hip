@@ -175,6 +175,20 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
     const T *cs = reinterpret_cast<const T *>(p.rope_cos) + (int64_t)(ok ? n : 0) * D;
     const T *sn = reinterpret_cast<const T *>(p.rope_sin) + (int64_t)(ok ? n : 0) * D;
     const float invD = 1.0f / (float)D;
+    // this thread's rotary factors (the same for every head) when it has at
+    // most PPM pairs: loaded once, all together (clamped), before the first
+    // use; wider heads read them per head
+    constexpr int PPM = 2;
+    const bool few = pp <= PPM;
+    float cv[PPM][2], sv[PPM][2];
+#pragma unroll
+    for (int i = 0; i < PPM; ++i) {
+        const int e = min(sub * pp + min(i, pp - 1), half - 1);
+        cv[i][0] = to_f(cs[e]);
+        cv[i][1] = to_f(cs[e + half]);
+        sv[i][0] = to_f(sn[e]);
+        sv[i][1] = to_f(sn[e + half]);
+    }
     for (int h = 0; h < d.H; ++h) {
         const float *x = hb + row * hp + h * D;
         float ss = 0.0f;
@@ -190,6 +204,18 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
         if (!ok)
             continue;
         float *out = dst + (int64_t)n * HD + h * D;
+        if (few) {
+#pragma unroll
+            for (int i = 0; i < PPM; ++i) {
+                const int e = sub * pp + i;
+                if (i < pp && e < half) {
+                    const float y1 = x[e] * rs, y2 = x[e + half] * rs;
+                    out[e] = y1 * cv[i][0] - y2 * sv[i][0];
+                    out[e + half] = y2 * cv[i][1] + y1 * sv[i][1];
+                }
+            }
+            continue;
+        }
         for (int i = 0; i < pp; ++i) {
             const int e = sub * pp + i;
             if (e >= half)
@@ -572,13 +598,13 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
             }
         };
         auto adaln = [&](int j) {
-            gemm_stage<G, T, true, SPLIT, PP>(
+            gemm_stage_cv<G, T, true, SPLIT, PP>(
                 C / BW, opA, opAl, L.ldS, nkS, p.pk + p.off.w_scale[j], (int64_t)nkS * 64,
                 opA, opAl, L.ldS, nkS, p.pk + p.off.w_shift[j], (int64_t)nkS * 64,
-                [&](int r, int c, float x1, float x2) {
+                [&](int c) { return to_f(bscale[j * C + c]); },
+                [&](int r, int c, float x1, float x2, float bs) {
                     const float ln = (x0(r, c) - st[r * 4 + 0]) * st[r * 4 + 1];
-                    put_split<T>(opQ, opQl, r * L.ldC + c,
-                                 ln * sigmoid_f(x1 + to_f(bscale[j * C + c])) + x2);
+                    put_split<T>(opQ, opQl, r * L.ldC + c, ln * sigmoid_f(x1 + bs) + x2);
                 });
         };
         __syncthreads(); // statistics of every row
@@ -586,13 +612,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         __syncthreads();
         adaln(0);
         __syncthreads();
-        gemm_stage<G, T, true, SPLIT, PP>(
+        gemm_stage_cv<G, T, true, SPLIT, PP>(
             HD / BW, opQ, opQl, L.ldC, nkC, p.pk + p.off.w_q, (int64_t)nkC * 64,
             opQ, opQl, L.ldC, nkC, p.pk + p.off.w_vg, (int64_t)nkC * 64,
-            [&](int r, int c, float x1, float x2) {
+            [&](int c) { return to_f(bq[c]); },
+            [&](int r, int c, float x1, float x2, float bqc) {
                 const int nn = n0 + r;
                 if (nn < N) {
-                    qo[(int64_t)nn * HD + c] = x1 + to_f(bq[c]);
+                    qo[(int64_t)nn * HD + c] = x1 + bqc;
                     go[(int64_t)nn * HD + c] = from_f<T>(sigmoid_f(x2));
                 }
             });
