@@ -163,9 +163,39 @@ size_t prep_lds_bytes(const Dims &d, int dtype, int style, int stage) {
 //   y = x * rsqrt(mean(x^2) + eps),
 //   out[e] = y[e] cos[e] - y[e+D/2] sin[e],
 //   out[e+D/2] = y[e+D/2] cos[e+D/2] + y[e] sin[e+D/2].
+// Rotary factors of one row for a thread with at most 2 of the head's
+// (e, e + D/2) pairs: cos and sin of both members, loaded together.
+struct RopeRow {
+    float c[2][2], s[2][2];
+};
+template <typename T, int TPR>
+__device__ __forceinline__ RopeRow rope_row(const BlockArgs &p, int n0) {
+    const Dims d = p.d;
+    const int N = d.B * d.A, D = d.D, half = d.D / 2;
+    const int pp = (half + TPR - 1) / TPR;
+    const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+    // the tile's first row as a uniform base, 32-bit offsets; clamped
+    const T *csb = reinterpret_cast<const T *>(p.rope_cos) + (int64_t)n0 * D;
+    const T *snb = reinterpret_cast<const T *>(p.rope_sin) + (int64_t)n0 * D;
+    const uint32_t ro = (uint32_t)((n0 + row < N ? row : 0) * D);
+    RopeRow rr;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t e = (uint32_t)max(min(sub * pp + min(i, pp - 1), half - 1), 0);
+        rr.c[i][0] = to_f(ld_off<T>(csb, (ro + e) * (uint32_t)sizeof(T)));
+        rr.c[i][1] = to_f(ld_off<T>(csb, (ro + e + half) * (uint32_t)sizeof(T)));
+        rr.s[i][0] = to_f(ld_off<T>(snb, (ro + e) * (uint32_t)sizeof(T)));
+        rr.s[i][1] = to_f(ld_off<T>(snb, (ro + e + half) * (uint32_t)sizeof(T)));
+    }
+    return rr;
+}
+
+// Per-head RMS norm and rotary embedding of the 32 rows in hb (fp32, pitch
+// hp) into dst (fp32 [N][HD]); rr holds the row's factors when a thread
+// has at most 2 pairs (D <= 4 * TPR), wider heads read them per head.
 template <typename T, int TPR>
 __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
-                                int n0, float *dst) {
+                                int n0, float *dst, const RopeRow &rr) {
     const Dims d = p.d;
     const int N = d.B * d.A, HD = d.H * d.D, D = d.D, half = d.D / 2;
     const int pp = (half + TPR - 1) / TPR; // pairs per thread
@@ -175,20 +205,8 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
     const T *cs = reinterpret_cast<const T *>(p.rope_cos) + (int64_t)(ok ? n : 0) * D;
     const T *sn = reinterpret_cast<const T *>(p.rope_sin) + (int64_t)(ok ? n : 0) * D;
     const float invD = 1.0f / (float)D;
-    // this thread's rotary factors (the same for every head) when it has at
-    // most PPM pairs: loaded once, all together (clamped), before the first
-    // use; wider heads read them per head
     constexpr int PPM = 2;
     const bool few = pp <= PPM;
-    float cv[PPM][2], sv[PPM][2];
-#pragma unroll
-    for (int i = 0; i < PPM; ++i) {
-        const int e = min(sub * pp + min(i, pp - 1), half - 1);
-        cv[i][0] = to_f(cs[e]);
-        cv[i][1] = to_f(cs[e + half]);
-        sv[i][0] = to_f(sn[e]);
-        sv[i][1] = to_f(sn[e + half]);
-    }
     for (int h = 0; h < d.H; ++h) {
         const float *x = hb + row * hp + h * D;
         float ss = 0.0f;
@@ -210,8 +228,8 @@ __device__ void head_rms_rotary(const BlockArgs &p, const float *hb, int hp,
                 const int e = sub * pp + i;
                 if (i < pp && e < half) {
                     const float y1 = x[e] * rs, y2 = x[e + half] * rs;
-                    out[e] = y1 * cv[i][0] - y2 * sv[i][0];
-                    out[e + half] = y2 * cv[i][1] + y1 * sv[i][1];
+                    out[e] = y1 * rr.c[i][0] - y2 * rr.s[i][0];
+                    out[e + half] = y2 * rr.c[i][1] + y1 * rr.s[i][1];
                 }
             }
             continue;
@@ -653,6 +671,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
                 put_split<T>(opQ, opQl, r * L.ldC + c, rm * (1.0f + x2) + x1);
             });
         __syncthreads(); // the A tile becomes the projection staging tile hb
+        const RopeRow rr = rope_row<T, TPR>(p, n0); // in flight during the projections
         for (int pass = 0; pass < 2; ++pass) {
             const int64_t off1 = pass == 0 ? p.off.w_q : p.off.w_k;
             const int64_t off2 = pass == 0 ? p.off.w_vg : p.off.w_v;
@@ -675,7 +694,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
                     }
                 });
             __syncthreads();
-            head_rms_rotary<T, TPR>(p, hb, L.hp, n0, pass == 0 ? qo : ko);
+            head_rms_rotary<T, TPR>(p, hb, L.hp, n0, pass == 0 ? qo : ko, rr);
             __syncthreads();
         }
     }
