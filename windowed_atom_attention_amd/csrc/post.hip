@@ -597,40 +597,79 @@ __global__ __launch_bounds__(256) void k_pool_fix(BlockArgs p) {
     const int t = blockIdx.x, ntile = gridDim.x, U = p.d.U, tid = threadIdx.x;
     const int *ri = p.pool_int;
     const float *rs = p.pool_sum;
-    const int nseg = ri[t * 8];
+    // Everything the common case needs is loaded at once, before any of it
+    // is used: this tile's record and both segment sums, the previous
+    // tile's record, the next tile's record and first-segment sums (indices
+    // clamped; a token rarely spans more than two tiles, the loops below
+    // cover the rest).
+    const int tp = t > 0 ? t - 1 : 0, tn = t + 1 < ntile ? t + 1 : t;
+    int rec[8], prv[8], nxt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        rec[k] = ri[t * 8 + k];
+        prv[k] = ri[tp * 8 + k];
+        nxt[k] = ri[tn * 8 + k];
+    }
+    float s0[2], s1[2], n0[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int col = min(tid + 256 * i, U - 1);
+        s0[i] = rs[((int64_t)t * 2 + 0) * U + col];
+        s1[i] = rs[((int64_t)t * 2 + 1) * U + col];
+        n0[i] = rs[(int64_t)tn * 2 * U + col];
+    }
+    const int nseg = rec[0];
     if (nseg == 0)
         return;
-    int u = t - 1;
-    while (u >= 0 && ri[u * 8] == 0)
-        --u;
-    const int prev_last = u < 0 ? -1 : (ri[u * 8] == 1 ? ri[u * 8 + 1] : ri[u * 8 + 3]);
-    const int fkey = ri[t * 8 + 1];
+    int prev_last = -1;
+    if (t > 0) {
+        if (prv[0] != 0) {
+            prev_last = prv[0] == 1 ? prv[1] : prv[3];
+        } else {
+            int u = t - 2;
+            while (u >= 0 && ri[u * 8] == 0)
+                --u;
+            prev_last = u < 0 ? -1 : (ri[u * 8] == 1 ? ri[u * 8 + 1] : ri[u * 8 + 3]);
+        }
+    }
+    const int fkey = rec[1];
     if (prev_last > fkey && tid == 0 && p.status != nullptr)
         p.status[0] = 1;
     T *tout = reinterpret_cast<T *>(p.token_output);
     for (int which = 0; which < 2; ++which) {
         int key, cnt;
         bool may_continue;
+        float acc[2];
         if (which == 0) {
             if (prev_last == fkey)
                 continue;
             key = fkey;
-            cnt = ri[t * 8 + 2];
+            cnt = rec[2];
             may_continue = nseg == 1;
+            acc[0] = s0[0];
+            acc[1] = s0[1];
         } else {
             if (nseg < 2)
                 continue;
-            key = ri[t * 8 + 3];
-            cnt = ri[t * 8 + 4];
+            key = rec[3];
+            cnt = rec[4];
             may_continue = true;
+            acc[0] = s1[0];
+            acc[1] = s1[1];
         }
-        float acc[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int col = tid + 256 * i;
-            acc[i] = col < U ? rs[((int64_t)t * 2 + which) * U + col] : 0.0f;
+        int v = t + 1;
+        if (may_continue && v < ntile && nxt[0] != 0) { // the next tile, from the loads above
+            if (nxt[1] != key) {
+                may_continue = false;
+            } else {
+                cnt += nxt[2];
+                acc[0] += n0[0];
+                acc[1] += n0[1];
+                may_continue = nxt[0] == 1;
+                ++v;
+            }
         }
-        for (int v = t + 1; may_continue && v < ntile; ++v) {
+        for (; may_continue && v < ntile; ++v) {
             const int ns = ri[v * 8];
             if (ns == 0)
                 continue;
