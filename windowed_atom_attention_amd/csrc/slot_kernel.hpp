@@ -319,8 +319,13 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
         }
         if (!qin)
             return;
-        // one per-thread offset; the slot's stride goes into the (uniform) base
-        const uint32_t ao = (uint32_t)(q * K + jq) * (uint32_t)sizeof(T);
+        // one per-thread offset; the slot's stride goes into the (uniform)
+        // base. The offset is opaque here, so the compiler forms each address
+        // at its store (scalar base + offset) instead of keeping 64-bit
+        // addresses of every head and slot live across the block, which
+        // spilled them.
+        uint32_t ao = (uint32_t)(q * K + jq) * (uint32_t)sizeof(T);
+        __asm__ volatile("" : "+v"(ao));
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
             if (jq + TQ * i < K)
@@ -584,15 +589,18 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
             }
         }
         if (pv) {
-            // the block's rows of o from one base (32-bit offsets inside)
-            T *ob = og + (bA + a0) * HD + hw * DK + t0 * 16 + acc16_col(lane);
+            // the block's rows of o: a uniform base and one opaque 32-bit
+            // lane offset (formed here, not hoisted and kept per element)
+            T *ob = og + (bA + a0) * HD + hw * DK + t0 * 16;
+            uint32_t oo = (uint32_t)(acc16_row(0, lane) * HD + acc16_col(lane)) * (uint32_t)sizeof(T);
+            __asm__ volatile("" : "+v"(oo));
 #pragma unroll
             for (int t = 0; t < NDBW; ++t) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int r = acc16_row(v, lane);
                     if (a0 + r < A)
-                        ob[r * HD + t * 16] = from_f<T>(oacc[t][v]);
+                        st_off<T>(ob + v * HD + t * 16, oo, from_f<T>(oacc[t][v]));
                 }
             }
         }
