@@ -31,13 +31,21 @@ namespace waa {
 template <typename T>
 __device__ __forceinline__ void copy_row(T *dst, const T *src, int n, bool ok,
                                          int sub) {
-    constexpr int E = 16 / sizeof(T);
+    // groups of 8 vectors per thread, all loads of a group issued
+    // (unconditionally, clamped into the row) before any is stored; rows
+    // that are not ok are stored as zeros
+    constexpr int E = 16 / sizeof(T), RG = 8;
     const int nv = n / E;
-    for (int vi = sub; vi < nv; vi += 8) {
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (ok)
-            val = *reinterpret_cast<const uint4 *>(src + vi * E);
-        *reinterpret_cast<uint4 *>(dst + vi * E) = val;
+    for (int v0 = sub; v0 < nv; v0 += 8 * RG) {
+        uint4 val[RG];
+#pragma unroll
+        for (int j = 0; j < RG; ++j)
+            val[j] = *reinterpret_cast<const uint4 *>(src + min(v0 + 8 * j, nv - 1) * E);
+#pragma unroll
+        for (int j = 0; j < RG; ++j)
+            if (v0 + 8 * j < nv)
+                *reinterpret_cast<uint4 *>(dst + (v0 + 8 * j) * E) =
+                    ok ? val[j] : make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -55,15 +63,18 @@ __global__ __launch_bounds__(256) void k_token_proj(BlockArgs p) {
     T *opA = reinterpret_cast<T *>(smem);
     {
         const int r = r0 + row;
-        const bool ok = r < rows && p.token_valid[r];
-        copy_row<T>(opA + row * ldU, reinterpret_cast<const T *>(p.token) + (int64_t)r * d.U,
+        const int rc = r < rows ? r : 0; // rows past the end read row 0
+        const uint8_t tv = p.token_valid[rc];
+        const bool ok = r < rows && tv;
+        copy_row<T>(opA + row * ldU, reinterpret_cast<const T *>(p.token) + (int64_t)rc * d.U,
                     d.U, ok, sub);
     }
     __syncthreads();
     const int nkc = d.U / Mma32<T>::KC;
     for (int nb = wave; nb < d.C / 32; nb += 4) {
         f32x16_t acc = zero16();
-        gemm1<T>(acc, opA, nullptr, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64);
+        // (8 chunks in flight: this kernel's grid is small and its registers are free)
+        gemm1<T, false, 8>(acc, opA, nullptr, ldU, nkc, p.pk + p.off.w_token + (int64_t)nb * nkc * 64);
         const int c = nb * 32 + acc32_col(lane);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
