@@ -1,7 +1,8 @@
 // slot_kernel.hpp -- masked slot attention, one block of 16 query atoms per
-// workgroup (4 waves, 16 threads per query). Included by the translation
-// units that instantiate it (slot_af3_f32.hip, slot_af3_bf16.hip,
-// slot_esm.hip); the launcher lives in slot.hip.
+// workgroup (4 waves and 16 threads per query, or 8 waves and 32 threads per
+// query). Included by the translation units that instantiate it
+// (slot_af3_f32.hip, slot_af3_bf16.hip, slot_af3_pre.hip, slot_esm.hip);
+// the launcher lives in slot.hip.
 //
 // What it computes ("windowed_atom_attention", Required behavior; the AF3
 // and ESMFold2 encoder pages): a slot (a, k) with key id j is allowed iff
@@ -13,13 +14,14 @@
 // o[a, h] = sum_k w_k V[j_k, h].
 //
 // How:
-//  * Each thread owns SPL slots of one query, strided by 16 (thread j of a
-//    query has slots j, j+16, ...), so that the 16 threads of a query touch
-//    consecutive slots: coalesced key-id, window, pair and attention rows,
-//    and distinct LDS banks for the tile and tag cells of windowed key
-//    lists. It loads their key ids and window bits, gathers the key
-//    usability of the slots that can be allowed and, for a usable query,
-//    the pair rows of all its slots. The pair bias of every slot and head is
+//  * Each thread owns SPL slots of one query, strided by the threads per
+//    query (thread j of a query has slots j, j+16, ... in the 16-thread
+//    form), so that the threads of a query touch consecutive slots:
+//    coalesced key-id, window, pair and attention rows, and distinct LDS
+//    banks for the tile and tag cells of windowed key lists. It loads their
+//    key ids and window bits, the pair rows of all its slots (or their
+//    precomputed bias) and then gathers the key usability of every slot,
+//    all unconditionally. The pair bias of every slot and head is
 //    formed in registers from one pass over the row: with d = x - x[0]
 //    (shifted data keeps the variance well conditioned),
 //      LN(x) . w_h = rstd * (sum_v d_v w_vh - mean(d) * sum_v w_vh),
