@@ -310,6 +310,112 @@ def test_esm_gates_and_transition():
     np.testing.assert_allclose(r["hidden"][0], hid.numpy(), rtol=0, atol=1e-12)
 
 
+# ------------- residual gates on the raw condition, stage-2 norm, rotary
+# "windowed_atom_attention", Required behavior: the AF3 residual gates
+# contract the RAW condition (no LayerNorm); the transition's adaptive norm is
+# stage j = 2 with its own cond_scale/w_scale/b_scale/w_shift; the rotary
+# step uses the supplied full-width rope_cos/rope_sin as they are.
+
+def _af3_transition_ref(w, x1, c, u):
+    """hidden from x1 with torch's layer_norm/silu/matmul: z = A_2(x1) with
+    c_2 = LN(c) * cond_scale[2], then the SwiGLU transition and its gate
+    sigmoid(c @ w_residual_gate[1] + b_residual_gate[1])."""
+    p = w.parameters
+    C, S = x1.shape[-1], c.shape[-1]
+    c2 = F.layer_norm(c, (S,), eps=w.eps) * p["cond_scale"][2]
+    z = (F.layer_norm(x1, (C,), eps=w.eps) *
+         torch.sigmoid(c2 @ p["w_scale"][2] + p["b_scale"][2]) + c2 @ p["w_shift"][2])
+    t = (F.silu(z @ p["w_ff_gate"]) * (z @ p["w_ff_up"])) @ p["w_ff_out"]
+    g_tr = torch.sigmoid(c @ p["w_residual_gate"][1] + p["b_residual_gate"][1])
+    return torch.where(u[:, None], x1 + g_tr * t, torch.zeros((), dtype=F64))
+
+
+def test_af3_residual_gates_use_raw_condition_closed_form():
+    """Condition rows that are constant per atom (kappa_a * 1) have LN(c) = 0
+    exactly, so every adaptive norm reduces to LN(x) * sigmoid(b_scale[j]),
+    while the raw-condition gates are sigmoid(kappa_a * colsum(w_rg[j]) +
+    b_rg[j]). A gate fed LN(c) would give sigmoid(b_rg[j]) instead."""
+    w = _tiny(A=24, K=8, seed=31)
+    p = w.parameters
+    A, S = w.dims["A"], w.dims["S"]
+    kappa = (torch.arange(A, dtype=F64) % 7 - 3.0) * 0.75  # exact binary values
+    w.activations["condition"] = kappa.view(1, A, 1).expand(1, A, S).clone()
+    p["w_residual_gate"].mul_(3.0)  # gates well away from 1/2
+    r = oracle.block(**w.kwargs(), intermediates=True)
+    u = torch.from_numpy(_usable_rows(r))
+    ka = torch.where(u, kappa, torch.zeros((), dtype=F64))  # sanitised
+    x0, o, g = _t(r["x0"])[0], _t(r["o"])[0], _t(r["g"])[0]
+    C = x0.shape[-1]
+    lnx0 = F.layer_norm(x0, (C,), eps=w.eps)
+    for j, name in ((0, "q_in"), (1, "kv_in")):
+        np.testing.assert_allclose(r[name][0], (lnx0 * torch.sigmoid(p["b_scale"][j])).numpy(),
+                                   rtol=0, atol=1e-12, err_msg=name)
+    g_att = torch.sigmoid(ka[:, None] * p["w_residual_gate"][0].sum(0) + p["b_residual_gate"][0])
+    g_tr = torch.sigmoid(ka[:, None] * p["w_residual_gate"][1].sum(0) + p["b_residual_gate"][1])
+    x1 = x0 + g_att * ((o * g) @ p["w_attention_out"])
+    np.testing.assert_allclose(r["x1"][0], x1.numpy(), rtol=0, atol=1e-12)
+    z = F.layer_norm(x1, (C,), eps=w.eps) * torch.sigmoid(p["b_scale"][2])
+    t = (F.silu(z @ p["w_ff_gate"]) * (z @ p["w_ff_up"])) @ p["w_ff_out"]
+    hid = torch.where(u[:, None], x1 + g_tr * t, torch.zeros((), dtype=F64))
+    np.testing.assert_allclose(r["hidden"][0], hid.numpy(), rtol=0, atol=1e-12)
+    # the raw and the normalised reading really differ on this input
+    assert float((g_att - torch.sigmoid(p["b_residual_gate"][0])).abs().max()) > 0.1
+
+
+def test_af3_gates_and_stage2_norm_random_condition():
+    """Random condition rows with non-zero mean and a non-unit spread, and
+    every conditioning weight non-zero (cond_scale[2] included, stage-2
+    matrices unlike stage 1's): x1 = x0 + sigmoid(c @ w_rg[0] + b_rg[0]) * u
+    and hidden = x1 + g_tr * SwiGLU(A_2(x1)), with torch layer_norm/silu."""
+    w = _tiny(A=24, K=8, seed=32)
+    p = w.parameters
+    w.activations["condition"].mul_(2.5).add_(1.5)
+    p["w_residual_gate"].mul_(3.0)
+    p["cond_scale"][2].mul_(2.0)
+    p["w_scale"][2].mul_(4.0)
+    p["w_shift"][2].mul_(4.0)
+    r = oracle.block(**w.kwargs(), intermediates=True)
+    u = torch.from_numpy(_usable_rows(r))
+    c = torch.where(u[:, None], w.activations["condition"][0], torch.zeros((), dtype=F64))
+    x0, o, g = _t(r["x0"])[0], _t(r["o"])[0], _t(r["g"])[0]
+    g_att = torch.sigmoid(c @ p["w_residual_gate"][0] + p["b_residual_gate"][0])
+    x1 = x0 + g_att * ((o * g) @ p["w_attention_out"])
+    np.testing.assert_allclose(r["x1"][0], x1.numpy(), rtol=0, atol=1e-12)
+    hid = _af3_transition_ref(w, x1, c, u)
+    np.testing.assert_allclose(r["hidden"][0], hid.numpy(), rtol=0, atol=1e-12)
+
+
+def test_esm_rotary_uses_full_width_tables():
+    """Tables whose halves differ. (a) cos = [1..1, 0..0], sin = [0..0, 1..1]
+    turn a head vector y = [y1, y2] into [y1, y1] (closed form); a rotary
+    that read only the first half would return y unchanged. (b) Independent
+    random halves against q * cos + cat(-q2, q1) * sin."""
+    for case in "ab":
+        w = _tiny(style="esmfold2", A=20, K=8, seed=33, rope="distinct")
+        H, D = w.dims["H"], w.dims["D"]
+        A = w.dims["A"]
+        h = D // 2
+        if case == "a":
+            one, zero = torch.ones(1, A, h, dtype=F64), torch.zeros(1, A, h, dtype=F64)
+            w.activations["rope_cos"] = torch.cat([one, zero], -1)
+            w.activations["rope_sin"] = torch.cat([zero, one], -1)
+        cos = w.activations["rope_cos"][0]
+        sin = w.activations["rope_sin"][0]
+        if case == "b":
+            assert not torch.equal(cos[:, :h], cos[:, h:])
+        r = oracle.block(**w.kwargs(), intermediates=True)
+        qin = _t(r["q_in"])[0]
+        for name, wm in (("q", w.parameters["w_q"]), ("k", w.parameters["w_k"])):
+            y = F.rms_norm((qin @ wm).view(-1, H, D), (D,), eps=w.eps)
+            if case == "a":
+                ref = torch.cat([y[..., :h], y[..., :h]], -1)
+            else:
+                rot = torch.cat([-y[..., h:], y[..., :h]], -1)
+                ref = y * cos[:, None, :] + rot * sin[:, None, :]
+            np.testing.assert_allclose(r[name][0], ref.reshape(-1, H * D).numpy(),
+                                       rtol=0, atol=1e-12, err_msg=case + name)
+
+
 # ------------------------------------------------------ stage boundaries
 
 @pytest.mark.parametrize("style", ["af3", "esmfold2"])

@@ -11,7 +11,9 @@ worked examples, so these synthetic inputs stand in for real molecules):
   ``w_mod`` ~ N(0, 0.02); activations (atom, condition, pair, token) ~ N(0, 1);
 * draws are fp32, rounded to bf16 (round-to-nearest-even) for bf16 workloads;
 * rotary tables: angles ~ U(0, 2*pi) over D/2 frequencies, duplicated to the
-  full width as [cos, cos] / [sin, sin];
+  full width as [cos, cos] / [sin, sin]; with ``rope="distinct"`` the two
+  halves come from independent angle draws, so a kernel that reads only one
+  half of the supplied tables gives a different result;
 * the window table W(32, K): a 32-query block starting at atom 32*floor(a/32)
   sees K consecutive atom ids centred on it, key_index[a, k] =
   32*floor(a/32) - (K-32)/2 + k; ids outside [0, A) stay in place and are
@@ -155,10 +157,13 @@ def make_workload(name: str, seed: Optional[int] = None, A: Optional[int] = None
                   K: Optional[int] = None, dtype: Optional[torch.dtype] = None,
                   style: Optional[str] = None, stage: Optional[str] = None,
                   radius: Optional[int] = None, eps: float = 1e-5,
-                  **widths: int) -> Workload:
+                  rope: str = "same", **widths: int) -> Workload:
     """Draw the named workload (optionally resized: A/B/T/K overrides keep the
     recipe, so a small instance spans a few tiles and a ragged tail; `widths`
-    may override C, S, V, H, D, M, U)."""
+    may override C, S, V, H, D, M, U). `rope` ("same" or "distinct") picks
+    the rotary-table recipe of ESMFold2 workloads."""
+    if rope not in ("same", "distinct"):
+        raise ValueError("rope must be 'same' or 'distinct'")
     r = dict(CONFIGS[name])
     for k, v in widths.items():
         if k not in ("C", "S", "V", "H", "D", "M", "U"):
@@ -276,8 +281,11 @@ def make_workload(name: str, seed: Optional[int] = None, A: Optional[int] = None
         acts["pair"] = pair
     else:
         theta = torch.rand((Bn, An, D // 2), generator=g, dtype=f32) * (2 * math.pi)
-        acts["rope_cos"] = torch.cat([theta.cos(), theta.cos()], dim=-1)
-        acts["rope_sin"] = torch.cat([theta.sin(), theta.sin()], dim=-1)
+        theta2 = theta
+        if rope == "distinct":
+            theta2 = torch.rand((Bn, An, D // 2), generator=g, dtype=f32) * (2 * math.pi)
+        acts["rope_cos"] = torch.cat([theta.cos(), theta2.cos()], dim=-1)
+        acts["rope_sin"] = torch.cat([theta.sin(), theta2.sin()], dim=-1)
     if stage_ == "decoder":
         tok = randn(Bn, Tn, U)
         tok = torch.where(token_valid[..., None], tok, torch.full_like(tok, math.nan))
