@@ -65,8 +65,9 @@ enum { ATOM_ATTN_ENCODER = 0, ATOM_ATTN_DECODER = 1 };
  * U token width (encoder output width, decoder input width).
  * Supported set of the kernels: C, S, H*D, M, U multiples of 32 and at most
  * 512; D one of 16, 32, 64, 128; K <= 256; AF3: V a multiple of 8
- * with V*sizeof(dtype) <= 64 bytes, H <= 8, and H <= 4 when K > 128.
- * Float pointers and the workspace must be 16-byte aligned. */
+ * with V*sizeof(dtype) <= 64 bytes and H <= 4; D*(A+39)*sizeof(dtype) <
+ * 2^31 (the slot kernel's 32-bit offsets into one head's transposed value
+ * rows). Float pointers and the workspace must be 16-byte aligned. */
 typedef struct {
     int64_t B, A, T, K, C, S, H, D, V, M, U;
 } atom_attn_dims;
@@ -122,43 +123,65 @@ typedef struct {
 int atom_attn_workspace_bytes(const atom_attn_dims *dims, int style,
                               int stage, int dtype, size_t *bytes);
 
-/* Encoder stage of the block (token_output = exact per-token mean of
- * ReLU(hidden @ w_pool) over usable assigned atoms; empty tokens 0).
+/* Encoder stage of the block. Defined by "windowed_atom_attention -- Local
+ * atom attention, encoder pooling and decoder skip/readout", Required
+ * behavior (stage 'encoder': the encoder starts from the sanitised atom
+ * features; token_output is the exact per-token mean of ReLU(hidden @
+ * w_pool) over usable assigned atoms, empty tokens 0), and by the pages
+ * "AlphaFold 3 Atom Attention Encoder" and "ESMFold 2 Atom Attention
+ * Encoder" (Required behavior, Worked example) for the two styles.
  * eps > 0 is the stabiliser inside every LayerNorm / RMS root (used in
  * fp32); radius >= 0 additionally requires |key id - query id| <= radius,
- * radius == -1 disables that index window. */
+ * radius == -1 disables that index window.
+ * Outputs: hidden, attention, token_output (position_update unused).
+ * Errors: the status codes above, all detected before any launch. */
 int atom_attn_encoder(const atom_attn_dims *dims, int style, int dtype,
                       const atom_attn_inputs *in, const atom_attn_params *par,
                       double eps, int64_t radius, atom_attn_outputs *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Decoder stage (entry state atom + gather(token @ w_token, atom_to_token);
- * position_update = masked (LN(hidden) * readout_scale [+ readout_bias])
- * @ w_readout, a coordinate update). Same arguments as the encoder. */
+/* Decoder stage. Defined by "windowed_atom_attention -- Local atom
+ * attention, encoder pooling and decoder skip/readout", Required behavior
+ * (stage 'decoder', the default there: entry state atom (skip) +
+ * gather(token @ w_token, atom_to_token), bias-free, zero for unusable
+ * atoms; position_update = (LN(hidden) * readout_scale [+ readout_bias for
+ * ESMFold2]) @ w_readout, masked to zero, a coordinate update).
+ * Same arguments as the encoder; outputs hidden, attention,
+ * position_update (token_output unused). */
 int atom_attn_decoder(const atom_attn_dims *dims, int style, int dtype,
                       const atom_attn_inputs *in, const atom_attn_params *par,
                       double eps, int64_t radius, atom_attn_outputs *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Masks alone, as the block uses them ("windowed_atom_attention", Required
- * behavior): usable [B,A] = valid and 0 <= atom_to_token < T and that
- * token valid; allowed [B,A,K] = key id in [0,A), query and key usable,
- * window_mask, and the radius window. Uses dims B, A, T, K only. */
+ * behavior: the usability, slot-permission and radius bullets; the pooling
+ * bullet for the counts): usable [B,A] = valid and 0 <= atom_to_token < T
+ * and that token valid; allowed [B,A,K] = key id in [0,A), query and key
+ * usable, window_mask, and the radius window; token_count [B,T] (int32) =
+ * number of usable atoms assigned to each token, the denominator of the
+ * encoder's token mean. Any of the three outputs may be NULL (not all).
+ * Uses dims B, A, T, K and the inputs valid, token_valid, window_mask,
+ * atom_to_token, key_index only. Errors: EINVAL for a bad argument,
+ * EUNSUPPORTED for A > 2^30 or B*T >= 2^31. */
 int atom_attn_masks(const atom_attn_dims *dims, const atom_attn_inputs *in,
                     int64_t radius, uint8_t *usable, uint8_t *allowed,
-                    void *stream);
+                    int32_t *token_count, void *stream);
 
-/* The slot-attention step alone, on caller-supplied per-atom rows q, k, v
- * [B,A,H*D] (head-major; for ESMFold2 already RMS-normalised and rotated)
- * and usable [B,A]. q and k are fp32 whatever `dtype` is (the block keeps
- * the logit operands in fp32); v, pair, pair_scale, w_pair, attention and
- * o use `dtype`. Computes logits q.k/sqrt(D) (+ AF3 pair bias
- * (LN(pair) * pair_scale) @ w_pair), the softmax over the allowed slots
- * with exact-zero empty rows, attention [B,H,A,K] and o [B,A,H*D] = sum of
- * weights times v rows -- with the same kernel as the full block, after a
- * copy of v into the transposed layout that kernel reads (in `workspace`,
- * atom_attn_slot_workspace_bytes() bytes). Uses dims B, A, K, H, D, V; eps
- * is used by the pair LayerNorm. */
+/* The slot-attention step alone ("windowed_atom_attention", Required
+ * behavior: the slot-permission, radius, pair-bias and attention-logit
+ * bullets), on caller-supplied per-atom rows q, k, v [B,A,H*D] (head-major;
+ * for ESMFold2 already RMS-normalised and rotated) and usable [B,A]. q and k
+ * are fp32 whatever `dtype` is (the block keeps the logit operands in
+ * fp32); v, pair, pair_scale, w_pair, attention and o use `dtype`. Computes
+ * logits q.k/sqrt(D) (+ AF3 pair bias (LN(pair) * pair_scale) @ w_pair),
+ * the softmax over the allowed slots with exact-zero empty rows, attention
+ * [B,H,A,K] and o [B,A,H*D] = sum of weights times v rows -- with the same
+ * kernel as the full block, after a copy of v into the transposed layout
+ * that kernel reads (in `workspace`, atom_attn_slot_workspace_bytes()
+ * bytes; rows of unusable atoms are copied as zeros, so their payload may
+ * be NaN/Inf). Uses dims B, A, K, H, D, V; eps is used by the pair
+ * LayerNorm. Errors: as the block, EUNSUPPORTED outside the slot kernel's
+ * supported set. */
 int atom_attn_slot_workspace_bytes(const atom_attn_dims *dims, int dtype,
                                    size_t *bytes);
 int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,

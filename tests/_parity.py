@@ -1,9 +1,17 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
-Tolerance (floating point): |gpu - oracle| <= rtol * (|oracle| + rms(oracle))
-elementwise, rms over the whole compared tensor; rtol = 1e-4 for fp32
-storage, 2e-2 for bf16 storage with fp32 arithmetic. Masks, indices and
-every exact-zero the pages require are compared bit-exactly."""
+Tolerances (floating point), rtol = 1e-4 for fp32 storage, 2e-2 for bf16
+storage with fp32 arithmetic:
+* attention weights: |gpu - oracle| <= rtol * |oracle| + 1e-30 elementwise.
+  The weights are non-negative softmax terms whose relative error is the
+  logit error plus one storage rounding, so no tensor-wide floor is needed
+  (the 1e-30 only admits results that underflow to subnormals);
+* outputs formed by sums with cancellation (hidden, o, token_output,
+  position_update): |gpu - oracle| <= rtol * (|oracle| + rms(oracle)), rms
+  over the whole compared tensor, so that an entry that cancels to near
+  zero is judged on the scale of its tensor.
+Masks, indices and every exact-zero the pages require are compared
+bit-exactly."""
 import numpy as np
 import torch
 
@@ -36,6 +44,29 @@ def assert_close(name, got, ref, rtol, where=None):
             "%s: %d/%d elements out of tolerance (rtol=%g, rms=%.3g); worst at %s: "
             "gpu=%.8g oracle=%.8g" % (name, int(bad.sum()), bad.size, rtol, rms,
                                      tuple(int(x) for x in i), got[i], ref[i]))
+
+
+def assert_close_rel(name, got, ref, rtol, where=None, floor=1e-30):
+    """Elementwise relative check for non-negative outputs (attention)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if where is not None:
+        got, ref = got[where], ref[where]
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    if ref.size == 0:
+        return
+    assert np.all(np.isfinite(got)), "%s: non-finite GPU values" % name
+    tol = rtol * np.abs(ref) + floor
+    err = np.abs(got - ref)
+    bad = err > tol
+    worst = float(np.max(err / tol))
+    print("%s: max err/tol %.3g (elementwise relative, rtol=%g)" % (name, worst, rtol))
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / tol), err.shape)
+        raise AssertionError(
+            "%s: %d/%d elements out of tolerance (rtol=%g, elementwise relative); "
+            "worst at %s: gpu=%.8g oracle=%.8g" % (name, int(bad.sum()), bad.size, rtol,
+                                                  tuple(int(x) for x in i), got[i], ref[i]))
 
 
 def run_gpu(w, **kw):
@@ -77,9 +108,9 @@ def compare_block(w, gpu, ref, rows=None, tokens=None):
     att = np64(gpu["attention"])
     if rows is not None:
         m = np.broadcast_to(rows[:, None, :, None], att.shape)
-        assert_close("attention", att, ref["attention"], rtol, m)
+        assert_close_rel("attention", att, ref["attention"], rtol, m)
     else:
-        assert_close("attention", att, ref["attention"], rtol)
+        assert_close_rel("attention", att, ref["attention"], rtol)
     if "token_output" in gpu:
         assert_close("token_output", np64(gpu["token_output"]), ref["token_output"],
                      rtol, tokens)

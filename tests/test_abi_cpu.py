@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.EXPORTS)
-    assert lib.atom_attn_version() == 3
+    assert lib.atom_attn_version() == 4
 
 
 def test_pair_bias_split_query():
@@ -84,6 +84,28 @@ def test_workspace_query_status_codes():
     assert _ws(_dims(), stage=N.DECODER)[1] > _ws(_dims())[1]
 
 
+def test_shapes_whose_32bit_value_offsets_would_overflow_are_rejected():
+    """The slot kernel reads one head's transposed value rows through a
+    32-bit byte offset of up to D * (A rounded up to 8, + 32) * sizeof(dtype):
+    shapes where that reaches 2^31 are outside the supported set, for the
+    block and for the standalone slot step."""
+    big = dict(H=1, D=128, K=1, T=8)
+    # fp32: 128 * 4 * pitch >= 2^31 once pitch >= 4194304
+    assert _ws(_dims(A=4_194_304 - 40, **big))[0] == N.OK
+    assert _ws(_dims(A=4_194_304, **big))[0] == N.EUNSUPPORTED
+    # bf16 halves the bytes per value
+    assert _ws(_dims(A=4_194_304, **big), dtype=N.BF16)[0] == N.OK
+    assert _ws(_dims(A=8_388_608, **big), dtype=N.BF16)[0] == N.EUNSUPPORTED
+    lib = N.lib()
+    fake = 4096  # aligned, never dereferenced: rejected before any launch
+    for A, dt, rc in ((4_194_304, N.F32, N.EUNSUPPORTED), (8_388_608, N.BF16, N.EUNSUPPORTED)):
+        nd = N.Dims(**_dims(A=A, **big))
+        got = lib.atom_attn_slot_attention(ctypes.byref(nd), N.ESMFOLD2, dt, 1e-5, -1,
+                                           fake, fake, fake, fake, fake, fake, None, None,
+                                           None, fake, fake, fake, 1 << 40, None)
+        assert got == rc, (A, dt, got)
+
+
 def test_workspace_sizes_of_all_workloads():
     for name in ("0", "1", "2", "3", "4a", "4b"):
         w = make_workload(name, A=64 if name != "0" else None)
@@ -105,7 +127,15 @@ def test_block_rejects_bad_arguments_before_any_launch():
                       ctypes.byref(npar), eps, radius, ctypes.byref(nout), None,
                       0, None) == N.EINVAL
         assert fn(None, N.AF3, N.F32, None, None, 1e-5, -1, None, None, 0, None) == N.EINVAL
-    assert lib.atom_attn_masks(ctypes.byref(nd), None, -1, None, None, None) == N.EINVAL
+    assert lib.atom_attn_masks(ctypes.byref(nd), None, -1, None, None, None, None) == N.EINVAL
+    # inputs present but no output requested
+    fake = 4096  # never dereferenced: the call is rejected on the host
+    nin_m = N.Inputs(valid=fake, token_valid=fake, window_mask=fake, atom_to_token=fake,
+                     key_index=fake)
+    assert lib.atom_attn_masks(ctypes.byref(nd), ctypes.byref(nin_m), -1, None, None, None,
+                               None) == N.EINVAL
+    assert lib.atom_attn_masks(ctypes.byref(nd), ctypes.byref(nin_m), -2, fake, fake, fake,
+                               None) == N.EINVAL
     assert lib.atom_attn_slot_attention(ctypes.byref(nd), N.AF3, N.F32, 1e-5, -1,
                                         None, None, None, None, None, None, None,
                                         None, None, None, None, None, 0, None) == N.EINVAL

@@ -16,7 +16,8 @@ import pytest
 import torch
 
 import oracle
-from _parity import RTOL, assert_close, compare_block, exact_zero_checks, np64, run_gpu
+from _parity import (RTOL, assert_close, assert_close_rel, compare_block, exact_zero_checks,
+                     np64, run_gpu)
 from windowed_atom_attention_amd import masks as gpu_masks
 from windowed_atom_attention_amd import slot_attention as gpu_slot_attention
 from windowed_atom_attention_amd import windowed_atom_attention, workspace_bytes
@@ -57,6 +58,10 @@ SMALL = [
     # form (small grids take the 8-wave form that splits k over wave pairs)
     ("0", dict(B=30, A=300)),
     ("0", dict(B=30, A=300, style="esmfold2", stage="decoder", dtype=torch.bfloat16)),
+    # rotary tables whose two halves differ (the full-width tables are used
+    # as supplied)
+    ("2", dict(A=300, rope="distinct")),
+    ("4b", dict(A=400, rope="distinct", dtype=torch.float32, stage="decoder")),
 ]
 
 
@@ -76,14 +81,22 @@ def test_block_small_matches_oracle(case):
     compare_block(w, gpu, ref)
 
 
-@pytest.mark.parametrize("name", ["0", "2", "4a", "4b"])
+@pytest.mark.parametrize("name", ["0", "2", "3", "4a", "4b"])
 def test_masks_bit_exact(name):
-    w = make_workload(name, A=None if name == "0" else 700)
+    w = make_workload(name, A=None if name == "0" else 700, B=2 if name == "3" else None)
     g = w.to("cuda")
-    us, al = gpu_masks(g.masks, g.structure, w.dims["T"], w.radius)
+    us, al, cnt = gpu_masks(g.masks, g.structure, w.dims["T"], w.radius)
     ref = oracle.block(**w.kwargs(), intermediates=True)
     assert np.array_equal(us.cpu().numpy(), ref["usable"].astype(bool))
     assert np.array_equal(al.cpu().numpy(), ref["allowed"].astype(bool))
+    # usable atoms per token, counted on the host from the oracle's mask
+    B, T = w.dims["B"], w.dims["T"]
+    exp = np.zeros((B, T), np.int64)
+    a2t = w.structure["atom_to_token"].numpy()
+    u = ref["usable"].astype(bool)
+    for b in range(B):
+        np.add.at(exp[b], a2t[b][u[b]], 1)
+    assert np.array_equal(cnt.cpu().numpy().astype(np.int64), exp)
 
 
 @pytest.mark.parametrize("style", ["af3", "esmfold2"])
@@ -96,6 +109,11 @@ def test_slot_attention_step(style, dtype):
     gen = torch.Generator().manual_seed(17)
     q, k, v = (torch.randn((B, A, HD), generator=gen).to(dtype) for _ in range(3))
     usable = torch.from_numpy(ref_masks["usable"]).bool()
+    # payloads of unusable atoms are junk (NaN and +-Inf) and must not leak
+    bad = ~usable
+    junk = torch.tensor([float("nan"), float("inf"), -float("inf")], dtype=dtype)
+    for t in (q, k, v):
+        t[bad] = junk[torch.arange(int(bad.sum())) % 3][:, None].expand(-1, HD)
     kw = dict(eps=w.eps, style=style, radius=w.radius)
     pair = pair_scale = w_pair = None
     if style == "af3":
@@ -113,8 +131,10 @@ def test_slot_attention_step(style, dtype):
     al = ref["allowed"].astype(bool)
     attn = np64(att)
     assert np.all(attn[np.broadcast_to(~al[:, None], attn.shape)] == 0.0)
-    assert_close("attention", attn, ref["attention"], rtol)
+    assert_close_rel("attention", attn, ref["attention"], rtol)
+    assert np.all(np.isfinite(np64(o)))
     assert_close("o", np64(o), ref["o"], rtol)
+    assert np.all(np64(o)[~ref_masks["usable"].astype(bool)] == 0.0)
 
 
 # ------------------------------------------------------- full size, sampled
@@ -152,7 +172,7 @@ def test_block_full_size_sampled(name):
     tol = 1e-4 if w.dtype == torch.float32 else 3e-2
     assert bool(((rs - 1).abs() < tol).logical_or(rs == 0).all())
     g = w.to("cuda")
-    us, al = gpu_masks(g.masks, g.structure, w.dims["T"], w.radius)
+    us, al, _ = gpu_masks(g.masks, g.structure, w.dims["T"], w.radius)
     empty = ~al.any(-1)  # rows without allowed slots: exactly zero
     assert bool((rs.transpose(0, 1)[:, empty] == 0).all())
     assert bool((gpu["hidden"][~us] == 0).all())

@@ -77,7 +77,7 @@ def lib():
                  _vp, szt, _vp]
         L.atom_attn_encoder.argtypes = block
         L.atom_attn_decoder.argtypes = block
-        L.atom_attn_masks.argtypes = [P(Dims), P(Inputs), i64, _vp, _vp, _vp]
+        L.atom_attn_masks.argtypes = [P(Dims), P(Inputs), i64, _vp, _vp, _vp, _vp]
         L.atom_attn_slot_attention.argtypes = [P(Dims), i32, i32, dbl, i64, _vp,
                                                _vp, _vp, _vp, _vp, _vp, _vp,
                                                _vp, _vp, _vp, _vp, _vp, szt, _vp]

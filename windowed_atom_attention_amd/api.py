@@ -273,7 +273,8 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
 
 
 def masks(masks: dict, structure: dict, T: int, radius: int = -1):
-    """usable [B,A] and allowed [B,A,K] (torch.bool) computed on the GPU."""
+    """usable [B,A] and allowed [B,A,K] (torch.bool) and token_count [B,T]
+    (torch.int32, usable atoms per token) computed on the GPU."""
     valid = _mask(masks["valid"])
     tv = _mask(masks["token_valid"])
     wm = _mask(masks["window_mask"])
@@ -283,6 +284,7 @@ def masks(masks: dict, structure: dict, T: int, radius: int = -1):
     dev = ki.device
     usable = torch.empty((B, A), dtype=torch.uint8, device=dev)
     allowed = torch.empty((B, A, K), dtype=torch.uint8, device=dev)
+    count = torch.empty((B, int(T)), dtype=torch.int32, device=dev)
     nd = N.Dims(B=B, A=A, T=int(T), K=K, C=1, S=1, H=1, D=1, V=1, M=1, U=1)
     nin = N.Inputs(valid=valid.data_ptr(), token_valid=tv.data_ptr(),
                    window_mask=wm.data_ptr(), atom_to_token=a2t.data_ptr(),
@@ -290,10 +292,10 @@ def masks(masks: dict, structure: dict, T: int, radius: int = -1):
     with torch.cuda.device(dev):
         rc = N.lib().atom_attn_masks(ctypes.byref(nd), ctypes.byref(nin), int(radius),
                                      usable.data_ptr(), allowed.data_ptr(),
-                                     _stream_handle(dev))
+                                     count.data_ptr(), _stream_handle(dev))
     N.check(rc, "atom_attn_masks")
     torch.cuda.current_stream(dev).synchronize()
-    return usable.bool(), allowed.bool()
+    return usable.bool(), allowed.bool(), count
 
 
 def slot_attention(q, k, v, usable, key_index, window_mask, heads: int,

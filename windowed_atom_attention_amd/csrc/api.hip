@@ -16,7 +16,7 @@ using namespace waa;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 // ------------------------------------------------------------ profiler
 
@@ -126,6 +126,14 @@ bool eps_valid(double eps, int dtype) {
 
 bool mult32_le(int64_t x, int64_t cap) { return x % 32 == 0 && x <= cap; }
 
+// The slot kernel addresses one head's rows of the transposed V copy with
+// a 32-bit byte offset from the head's base: D rows of vt_pitch(A) values.
+bool vt_offsets_fit(int64_t A, int64_t D, int esz) {
+    if (A > ((int64_t)1 << 30))
+        return false;
+    return D * (int64_t)vt_pitch((int)A) * esz < ((int64_t)1 << 31);
+}
+
 // The kernels' supported set; returns ATOM_ATTN_OK or EUNSUPPORTED.
 int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
     const int64_t HD = d->H * d->D;
@@ -136,7 +144,8 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
         return ATOM_ATTN_EUNSUPPORTED;
     if (d->B * d->A > (int64_t)1 << 30 || d->B * d->T > (int64_t)1 << 30 ||
         d->B * d->A * d->K > ((int64_t)1 << 31) - 1 ||
-        d->B * d->H * d->A * d->K > ((int64_t)1 << 31) - 1)
+        d->B * d->H * d->A * d->K > ((int64_t)1 << 31) - 1 ||
+        !vt_offsets_fit(d->A, d->D, dtype == ATOM_ATTN_BF16 ? 2 : 4))
         return ATOM_ATTN_EUNSUPPORTED;
     const Dims dd{(int)d->B, (int)d->A, (int)d->T, (int)d->K, (int)d->C, (int)d->S,
                   (int)d->H, (int)d->D, (int)d->V, (int)d->M, (int)d->U};
@@ -170,9 +179,20 @@ struct Mat {
     bool tile; // read by the 32-row tile kernels (prep, post), not k_token_proj
 };
 
+// The matrices of one call (at most kMaxPackJobs), held in place so that a
+// call makes no heap allocation.
+struct MatList {
+    Mat m[kMaxPackJobs];
+    int n = 0;
+    void push_back(const Mat &x) { m[n++] = x; }
+    Mat *begin() { return m; }
+    Mat *end() { return m + n; }
+    size_t size() const { return (size_t)n; }
+    Mat &operator[](size_t i) { return m[i]; }
+};
+
 void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
-               const atom_attn_params *par, PackedOffsets *off,
-               std::vector<Mat> *mats) {
+               const atom_attn_params *par, PackedOffsets *off, MatList *mats) {
     const int C = (int)d->C, S = (int)d->S, HD = (int)(d->H * d->D), M = (int)d->M,
               U = (int)d->U;
     auto at = [&](const void *base, int64_t elems) -> const void * {
@@ -216,7 +236,7 @@ void list_mats(const atom_attn_dims *d, int style, int stage, int esz,
 Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
     const int esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
     PackedOffsets off;
-    std::vector<Mat> mats;
+    MatList mats;
     list_mats(d, style, stage, esz, nullptr, &off, &mats);
     int64_t units = 0;
     for (auto &m : mats)
@@ -330,7 +350,7 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     hipStream_t s = (hipStream_t)stream;
 
     PackedOffsets off;
-    std::vector<Mat> mats;
+    MatList mats;
     list_mats(d, style, stage, esz, par, &off, &mats);
     // prep and post with eight waves (32x16 strips) when their grid has at
     // most one tile per CU; their matrices are then packed in the strip
@@ -423,8 +443,8 @@ const char *atom_attn_error_string(int code) {
     case ATOM_ATTN_EUNSUPPORTED:
         return "shape outside the supported set (C, S, H*D, M, U multiples of 32 "
                "and <= 512; D one of 16, 32, 64, 128; K <= 256; AF3: V a "
-               "multiple of 8 with V*sizeof(dtype) <= 64, H <= 8, and H <= 4 "
-               "when K > 128)";
+               "multiple of 8 with V*sizeof(dtype) <= 64, H <= 4; "
+               "D*(A+39)*sizeof(dtype) < 2^31)";
     default:
         return "unknown status";
     }
@@ -481,19 +501,20 @@ int atom_attn_decoder(const atom_attn_dims *dims, int style, int dtype,
 
 int atom_attn_masks(const atom_attn_dims *dims, const atom_attn_inputs *in,
                     int64_t radius, uint8_t *usable, uint8_t *allowed,
-                    void *stream) {
+                    int32_t *token_count, void *stream) {
     if (!dims || dims->B < 1 || dims->A < 1 || dims->T < 1 || dims->K < 1 || !in ||
         radius < -1 || !in->valid || !in->token_valid || !in->window_mask ||
-        !in->atom_to_token || !in->key_index || (!usable && !allowed))
+        !in->atom_to_token || !in->key_index || (!usable && !allowed && !token_count))
         return ATOM_ATTN_EINVAL;
-    if (dims->B * dims->A * dims->K > ((int64_t)1 << 40))
+    if (dims->B * dims->A * dims->K > ((int64_t)1 << 40) ||
+        dims->A > ((int64_t)1 << 30) || dims->B * dims->T > ((int64_t)1 << 31) - 1)
         return ATOM_ATTN_EUNSUPPORTED;
     const Dims d{(int)dims->B, (int)dims->A, (int)dims->T, (int)dims->K, 1, 1, 1, 1, 1, 1, 1};
     hipStream_t s = (hipStream_t)stream;
     return timed(KN_MASKS, s, [&] {
         return launch_masks(d, in->valid, in->token_valid, in->window_mask,
                             in->atom_to_token, in->key_index, radius, usable,
-                            allowed, s);
+                            allowed, token_count, s);
     });
 }
 
@@ -542,7 +563,8 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
     const int dt = dtype == ATOM_ATTN_BF16 ? 1 : 0;
     const int st = style == ATOM_ATTN_AF3 ? STYLE_AF3 : STYLE_ESM;
     if (!slot_supported(d, dt, st) || dims->B * dims->A > ((int64_t)1 << 30) ||
-        dims->B * dims->H * dims->A * dims->K > ((int64_t)1 << 31) - 1)
+        dims->B * dims->H * dims->A * dims->K > ((int64_t)1 << 31) - 1 ||
+        !vt_offsets_fit(dims->A, dims->D, dt ? 2 : 4))
         return ATOM_ATTN_EUNSUPPORTED;
     size_t need_ws = 0;
     atom_attn_slot_workspace_bytes(dims, dtype, &need_ws);
@@ -559,7 +581,7 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
     sa.pair = pair; sa.pair_scale = pair_scale; sa.w_pair = w_pair;
     sa.attention = attention; sa.o = o;
     hipStream_t s = (hipStream_t)stream;
-    if (launch_vt(v, workspace, d.B, d.A, (int)HD, dt, s) != hipSuccess)
+    if (launch_vt(v, usable, workspace, d.B, d.A, (int)HD, dt, s) != hipSuccess)
         return ATOM_ATTN_ELAUNCH;
     return timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); });
 }

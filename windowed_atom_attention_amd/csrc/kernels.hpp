@@ -121,13 +121,13 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
                        hipStream_t s);
 hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s);
 hipError_t launch_slot(const SlotArgs &a, int dtype, int style, hipStream_t s);
-hipError_t launch_vt(const void *v, void *vt, int B, int A, int HD, int dtype,
-                     hipStream_t s);
+hipError_t launch_vt(const void *v, const uint8_t *usable, void *vt, int B, int A,
+                     int HD, int dtype, hipStream_t s);
 hipError_t launch_masks(const Dims &d, const uint8_t *valid,
                         const uint8_t *token_valid, const uint8_t *window_mask,
                         const int64_t *atom_to_token, const int64_t *key_index,
                         int64_t radius, uint8_t *usable, uint8_t *allowed,
-                        hipStream_t s);
+                        int32_t *token_count, hipStream_t s);
 
 // LDS bytes each kernel needs for these sizes (host-side shape checks).
 size_t prep_lds_bytes(const Dims &d, int dtype, int style, int stage);

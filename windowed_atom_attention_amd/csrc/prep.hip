@@ -749,21 +749,36 @@ hipError_t launch_prep(const BlockArgs &a, int dtype, int style, int stage,
 
 // --------------------------------------------------------------- masks
 
+// x[0 .. n) = value (a kernel rather than a memset, so that a captured
+// graph replays it like any other launch)
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t *x, int64_t n, int32_t value) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        x[i] = value;
+}
+
 __global__ __launch_bounds__(256) void k_masks(Dims d, const uint8_t *valid,
                                                const uint8_t *token_valid,
                                                const uint8_t *window_mask,
                                                const int64_t *a2t,
                                                const int64_t *key_index,
                                                int64_t radius, uint8_t *usable,
-                                               uint8_t *allowed) {
+                                               uint8_t *allowed, int32_t *token_count) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t N = (int64_t)d.B * d.A;
     auto usable_of = [&](int64_t m) -> bool {
         const int64_t t = a2t[m];
         return valid[m] && t >= 0 && t < d.T && token_valid[(m / d.A) * d.T + t];
     };
-    if (i < N && usable)
-        usable[i] = usable_of(i);
+    if (i < N) {
+        const bool u = usable_of(i);
+        if (usable)
+            usable[i] = u;
+        // usable atoms per token: integer additions, so the count does not
+        // depend on their order
+        if (token_count && u)
+            atomicAdd(&token_count[(i / d.A) * d.T + a2t[i]], 1);
+    }
     if (i < N * d.K && allowed) {
         const int64_t n = i / d.K;
         const int64_t a = n % d.A, b = n / d.A;
@@ -780,12 +795,20 @@ hipError_t launch_masks(const Dims &d, const uint8_t *valid,
                         const uint8_t *token_valid, const uint8_t *window_mask,
                         const int64_t *atom_to_token, const int64_t *key_index,
                         int64_t radius, uint8_t *usable, uint8_t *allowed,
-                        hipStream_t s) {
+                        int32_t *token_count, hipStream_t s) {
+    if (token_count) {
+        const int64_t nt = (int64_t)d.B * d.T;
+        hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s,
+                           token_count, nt, 0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     const int64_t work = (int64_t)d.B * d.A * d.K;
     const int64_t grid = (work + 255) / 256;
     hipLaunchKernelGGL(k_masks, dim3((unsigned)grid), dim3(256), 0, s, d, valid,
                        token_valid, window_mask, atom_to_token, key_index,
-                       radius, usable, allowed);
+                       radius, usable, allowed, token_count);
     return hipGetLastError();
 }
 

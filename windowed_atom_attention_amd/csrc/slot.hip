@@ -54,10 +54,13 @@ hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) 
 }
 
 // Transposed copy of v ([B][A][HD] -> [B][HD][vt_pitch(A)], zero padding
-// included), for the standalone slot-attention entry point.
+// included), for the standalone slot-attention entry point. Rows of
+// unusable atoms are stored as zeros: the slot kernel multiplies whole key
+// bands of V by probabilities that are zero off the allowed slots, so a
+// NaN/Inf payload left in such a row would reach o as 0 * NaN.
 template <typename T>
-__global__ __launch_bounds__(256) void k_vt(const T *v, T *vt, int B, int A, int HD,
-                                            int pitch) {
+__global__ __launch_bounds__(256) void k_vt(const T *v, const uint8_t *usable, T *vt,
+                                            int B, int A, int HD, int pitch) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t per = (int64_t)A * HD;
     if (i >= per * B)
@@ -65,22 +68,23 @@ __global__ __launch_bounds__(256) void k_vt(const T *v, T *vt, int B, int A, int
     const int64_t b = i / per;
     const int64_t r = i - b * per;
     const int aa = (int)(r / HD), c = (int)(r - (int64_t)aa * HD);
-    vt[(b * HD + c) * pitch + aa] = v[i];
+    const T x = v[i];
+    vt[(b * HD + c) * pitch + aa] = usable[b * A + aa] ? x : (T)0;
     if (i < (int64_t)B * HD) // row i of the transposed copy: its zero padding
         for (int e = A; e < pitch; ++e)
             vt[i * pitch + e] = (T)0;
 }
 
-hipError_t launch_vt(const void *v, void *vt, int B, int A, int HD, int dtype,
-                     hipStream_t s) {
+hipError_t launch_vt(const void *v, const uint8_t *usable, void *vt, int B, int A,
+                     int HD, int dtype, hipStream_t s) {
     const int64_t total = (int64_t)A * HD * B;
     const int64_t grid = (total + 255) / 256;
     if (dtype == 0)
         hipLaunchKernelGGL(k_vt<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const float *)v, (float *)vt, B, A, HD, vt_pitch(A));
+                           (const float *)v, usable, (float *)vt, B, A, HD, vt_pitch(A));
     else
         hipLaunchKernelGGL(k_vt<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const bf16_t *)v, (bf16_t *)vt, B, A, HD, vt_pitch(A));
+                           (const bf16_t *)v, usable, (bf16_t *)vt, B, A, HD, vt_pitch(A));
     return hipGetLastError();
 }
 
