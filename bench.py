@@ -12,9 +12,13 @@ second timed region of the same K steps runs with the library's profiling
 mode on: HIP events recorded around each launch on the stream it launches
 on give every kernel's average duration (the roofline figures).
 
-Prints ONE JSON line: metric entries/s (B*A*H*K per second), plus
-atoms/s, the roofline of the dominant kernel and the fp64 oracle's rate on
-the host cores.
+Prints ONE JSON line: metric entries/s (B*A*H*K per second) of the
+headline workload (--config, default config 1, the AF3 encoder in fp32),
+plus atoms/s, every kernel's duration and roofline fraction, the roofline of
+the dominant kernel, the fp64 oracle's rate on the host cores (all threads
+and one thread, with the CPU model), and under "configs" the same figures
+for the other full-size workloads (--also, default 2, 3, 4a, 4b) timed in
+the same run.
 """
 from __future__ import annotations
 
@@ -185,10 +189,21 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
     print(json.dumps({k: v["bytes_per_launch"] for k, v in db.items()}))
 
 
-def cpu_baseline(name, seconds=12.0):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(name, seconds=12.0, seconds_1t=4.0):
     """The fp64 oracle, as it stands, on the host cores: repeated whole-block
     runs of the same workload (sampled atoms for workloads too large to run
-    whole within the budget)."""
+    whole within the budget), with every host thread the oracle uses and
+    then with one thread on a smaller sample."""
     import numpy as np
     import torch
     import oracle
@@ -198,76 +213,72 @@ def cpu_baseline(name, seconds=12.0):
     d = w.dims
     entries_per_atom = d["H"] * d["K"]
     nthreads = oracle.threads(0)
-    # one probe run on a bounded sample decides how much fits the budget
-    sel = None
-    if d["B"] * d["A"] > 8192:
+
+    def sample(n_per_batch):
+        if d["B"] * d["A"] <= n_per_batch:
+            return None
         g = np.random.default_rng(0)
         sel = np.zeros((d["B"], d["A"]), bool)
+        n = min(n_per_batch, d["A"])
         for b in range(d["B"]):
-            start = int(g.integers(0, d["A"] - 1024))
-            sel[b, start:start + 1024] = True
-        sel = torch.from_numpy(sel)
-    t0 = time.perf_counter()
-    r = oracle.block(**w.kwargs(), select=sel)
-    dt = time.perf_counter() - t0
-    atoms = int(r["done_atom"].sum()) if sel is not None else d["B"] * d["A"]
-    reps = max(1, min(50, int(seconds / max(dt, 1e-3))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.block(**w.kwargs(), select=sel)
-    dt = (time.perf_counter() - t0) / reps
-    sample = ("%d whole-block run(s) of workload %s" % (reps, name) if sel is None else
-              "%d run(s) of workload %s restricted to %d atoms (1024 consecutive query "
-              "atoms per batch, their keys and tokens)" % (reps, name, atoms))
+            start = int(g.integers(0, d["A"] - n + 1))
+            sel[b, start:start + n] = True
+        return torch.from_numpy(sel)
+
+    def rate(sel, nt, budget):
+        # one probe run decides how many repetitions fit the budget
+        t0 = time.perf_counter()
+        r = oracle.block(**w.kwargs(), select=sel, nthreads=nt)
+        dt = time.perf_counter() - t0
+        atoms = int(r["done_atom"].sum()) if sel is not None else d["B"] * d["A"]
+        reps = max(1, min(50, int(budget / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.block(**w.kwargs(), select=sel, nthreads=nt)
+        dt = (time.perf_counter() - t0) / reps
+        return atoms, reps, dt
+
+    sel = sample(1024) if d["B"] * d["A"] > 8192 else None
+    atoms, reps, dt = rate(sel, 0, seconds)
+    desc = ("%d whole-block run(s) of workload %s" % (reps, name) if sel is None else
+            "%d run(s) of workload %s restricted to %d atoms (1024 consecutive query "
+            "atoms per batch, their keys and tokens)" % (reps, name, atoms))
+    sel1 = sample(256)
+    atoms1, reps1, dt1 = rate(sel1, 1, seconds_1t)
     return {"value": atoms * entries_per_atom / dt, "unit": "entries/s",
-            "cores": nthreads, "kind": "oracle", "sample": sample,
-            "atoms_per_s": atoms / dt}
+            "cores": nthreads, "kind": "oracle", "sample": desc,
+            "atoms_per_s": atoms / dt, "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "one_thread": {"value": atoms1 * entries_per_atom / dt1, "unit": "entries/s",
+                           "cores": 1, "atoms_per_s": atoms1 / dt1,
+                           "sample": "%d run(s) of workload %s restricted to %d atoms "
+                                     "(256 consecutive query atoms per batch, their keys "
+                                     "and tokens)" % (reps1, name, atoms1)}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="1",
-                    help="workload: 0, 1, 2, 3, 4a, 4b (default 1)")
-    ap.add_argument("--cache-bytes", type=float, default=768e6,
-                    help="input copies are added until they exceed this")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of HIP graphs that capture one step each")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="run only the counter-calibration copy kernel")
-    ap.add_argument("--traffic-summary", nargs=4,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="write profiles/traffic.json entries for --config from "
-                         "rocprofv3 --pmc output directories (no GPU work)")
-    args = ap.parse_args()
-    if args.traffic_summary:
-        traffic_summary(args.config, *args.traffic_summary)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
-        sys.exit(2)
+NAMES = {"0": "tiny AF3 encoder fp32", "1": "AF3 encoder fp32",
+         "2": "ESMFold2 encoder bf16 radius 48", "3": "AF3 decoder bf16",
+         "4a": "large mixed AF3 encoder bf16",
+         "4b": "large mixed ESMFold2 encoder bf16 radius 64"}
 
-    if args.copy_probe:
-        copy_probe()
-        return
 
+def measure(config, steps, warmup, cache_bytes, graph=False):
+    """Time `steps` block calls of workload `config` on cuda:0 (inputs
+    resident in HBM, cycled over enough copies to defeat the Infinity Cache)
+    and return throughput, per-kernel durations and the dominant kernel's
+    roofline."""
     import torch
     from windowed_atom_attention_amd import (pair_bias_split, profile_enable, profile_read,
                                              windowed_atom_attention, workspace_bytes)
     from windowed_atom_attention_amd.workloads import make_workload
 
     dev = torch.device("cuda:0")
-    w = make_workload(args.config)
+    w = make_workload(config)
     d = w.dims
     g = w.to(dev)
     in_bytes = sum(t.numel() * t.element_size() for grp in
                    (g.activations, g.masks, g.structure) for t in grp.values())
-    copies = max(1, math.ceil(args.cache_bytes / max(in_bytes, 1)))
+    copies = max(1, math.ceil(cache_bytes / max(in_bytes, 1)))
     sets = [g]
     for _ in range(copies - 1):
         sets.append(dataclasses.replace(
@@ -296,7 +307,7 @@ def main():
             profile_read()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step(i, instrumented)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -304,9 +315,9 @@ def main():
         profile_enable(False)
         return t1 - t0, kt
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         eager(i)
-    if args.graph:
+    if graph:
         # one captured step per input copy (the library makes no allocation,
         # host synchronisation or memset inside a call)
         torch.cuda.synchronize()
@@ -322,9 +333,6 @@ def main():
     # of the same steps (the events add a little time between kernels)
     elapsed, _ = timed(False)
     elapsed_ev, kt = timed(True)
-    ms_step = elapsed * 1e3 / args.steps
-    entries = w.entries
-    value = entries * args.steps / elapsed
     dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     work = kernel_work(w, pair_bias_split(w.dims, w.style, w.stage, w.dtype))
     per_kernel = {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in kt.items()}
@@ -338,7 +346,7 @@ def main():
         roof = {"bound": "mfma", "achieved": amount / avg_s / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = _traffic(dom, args.config)
+    roof["traffic"] = _traffic(dom, config)
     roof["kernel"] = dom
     roof["work_per_launch"] = amount
     for k, v in per_kernel.items():
@@ -350,31 +358,93 @@ def main():
             else:
                 v["TFLOP_per_s"] = a / (v["avg_us"] * 1e-6) / 1e12
                 v["frac_mfma"] = v["TFLOP_per_s"] / MFMA_PEAK_TFLOPS[dtype]
+            v["traffic"] = _traffic(k, config)
+    res = {
+        "workload": "%s (config %s): B=%d A=%d T=%d K=%d C=%d S=%d H=%d D=%d V=%d M=%d "
+                    "U=%d, %s, radius %d" % (NAMES[config], config, d["B"], d["A"], d["T"],
+                                            d["K"], d["C"], d["S"], d["H"], d["D"], d["V"],
+                                            d["M"], d["U"], w.stage, w.radius),
+        "style": w.style, "stage": w.stage, "dtype": dtype,
+        "entries_per_step": w.entries, "atoms_per_step": w.atoms, "input_copies": copies,
+        "steps": steps, "ms_per_step": elapsed * 1e3 / steps,
+        "ms_per_step_instrumented": elapsed_ev * 1e3 / steps,
+        "entries_per_s": w.entries * steps / elapsed,
+        "atoms_per_s": w.atoms * steps / elapsed,
+        "kernels": per_kernel, "roofline": roof,
+    }
+    del sets, ws, out, graphs, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="1",
+                    help="workload of the headline line: 0, 1, 2, 3, 4a, 4b (default 1)")
+    ap.add_argument("--also", default="2,3,4a,4b",
+                    help="further workloads timed in the same run and reported under "
+                         "'configs' (comma separated; empty for none)")
+    ap.add_argument("--also-steps", type=int, default=50)
+    ap.add_argument("--cache-bytes", type=float, default=768e6,
+                    help="input copies are added until they exceed this")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of HIP graphs that capture one step each")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only the counter-calibration copy kernel")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic.json entries for --config from "
+                         "rocprofv3 --pmc output directories (no GPU work)")
+    args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.config, *args.traffic_summary)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    head = measure(args.config, args.steps, args.warmup, args.cache_bytes, args.graph)
+    print("bench: config %s %.4f ms/step" % (args.config, head["ms_per_step"]),
+          file=sys.stderr, flush=True)
+    others = {}
+    for c in [x for x in args.also.split(",") if x and x != args.config]:
+        r = measure(c, args.also_steps, min(args.warmup, 5), args.cache_bytes, args.graph)
+        others[c] = {k: r[k] for k in ("workload", "dtype", "ms_per_step", "entries_per_s",
+                                       "atoms_per_s", "kernels", "roofline", "steps")}
+        print("bench: config %s %.4f ms/step" % (c, r["ms_per_step"]), file=sys.stderr,
+              flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.config)
 
-    names = {"0": "tiny AF3 encoder fp32", "1": "AF3 encoder fp32",
-             "2": "ESMFold2 encoder bf16 radius 48", "3": "AF3 decoder bf16",
-             "4a": "large mixed AF3 encoder bf16", "4b": "large mixed ESMFold2 encoder bf16 radius 64"}
     line = {
         "metric": "atom-slot attention entries/sec (B*A*H*K) per block, 1xMI355X",
-        "value": value, "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step,
-        "ms_per_step_instrumented": elapsed_ev * 1e3 / args.steps, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-        "config": {"workload": "%s (config %s): B=%d A=%d T=%d K=%d C=%d S=%d H=%d D=%d "
-                               "V=%d M=%d U=%d, %s, radius %d" % (
-                                   names[args.config], args.config, d["B"], d["A"], d["T"],
-                                   d["K"], d["C"], d["S"], d["H"], d["D"], d["V"], d["M"],
-                                   d["U"], w.stage, w.radius),
-                   "style": w.style, "stage": w.stage, "entries_per_step": entries,
-                   "atoms_per_step": w.atoms, "input_copies": copies},
-        "atoms_per_s": w.atoms * args.steps / elapsed,
-        "kernels": per_kernel,
-        "roofline": roof,
+        "value": head["entries_per_s"], "unit": "entries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "ms_per_step_instrumented": head["ms_per_step_instrumented"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic",
+        "config": {"workload": head["workload"], "style": head["style"],
+                   "stage": head["stage"], "entries_per_step": head["entries_per_step"],
+                   "atoms_per_step": head["atoms_per_step"],
+                   "input_copies": head["input_copies"]},
+        "atoms_per_s": head["atoms_per_s"],
+        "kernels": head["kernels"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "configs": others,
     }
     print(json.dumps(line))
 
