@@ -54,6 +54,9 @@ extern "C" {
 #define ATOM_ATTN_ELAUNCH (-4)      /* the HIP runtime refused a launch */
 #define ATOM_ATTN_EUNSUPPORTED (-5) /* shape outside the kernels' supported
                                        set (see atom_attn_error_string) */
+#define ATOM_ATTN_ESCRATCH (-6)     /* atom_attn_block_noalloc: the sizes
+                                       need more scratch than its static
+                                       buffer holds */
 
 enum { ATOM_ATTN_AF3 = 0, ATOM_ATTN_ESMFOLD2 = 1 };
 enum { ATOM_ATTN_F32 = 0, ATOM_ATTN_BF16 = 1 };
@@ -192,6 +195,26 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
                              const void *pair_scale, const void *w_pair,
                              void *attention, void *o, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the block
+ * call of atom_attn_encoder (stage ATOM_ATTN_ENCODER) or atom_attn_decoder
+ * (stage ATOM_ATTN_DECODER) with the same arguments, results and status
+ * codes, minus the workspace. Its scratch memory is a static array inside
+ * the library, atom_attn_noalloc_max_bytes() bytes (64 MiB) per device,
+ * which each GPU the library runs on holds from its first such call until
+ * the process ends. The call allocates and frees nothing. Sizes whose
+ * atom_attn_workspace_bytes() exceeds that maximum are rejected with
+ * ATOM_ATTN_ESCRATCH before anything is enqueued. Every call on a device
+ * shares that device's array (nothing in it is assumed to start at zero):
+ * calls that may overlap on one GPU -- on different streams, or from
+ * different host threads -- race and must be serialised by the caller. */
+size_t atom_attn_noalloc_max_bytes(void);
+int atom_attn_block_noalloc(const atom_attn_dims *dims, int style, int stage,
+                            int dtype, const atom_attn_inputs *in,
+                            const atom_attn_params *par, double eps,
+                            int64_t radius, atom_attn_outputs *out,
+                            void *stream);
 
 /* Where a block call with these sizes computes the AF3 pair bias on the
  * current device (host-only, no GPU work; the compute-unit count of the

@@ -8,7 +8,7 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libatomattn.so")
 
-OK, EINVAL, EODD_HEAD, EWORKSPACE, ELAUNCH, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EODD_HEAD, EWORKSPACE, ELAUNCH, EUNSUPPORTED, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 AF3, ESMFOLD2 = 0, 1
 F32, BF16 = 0, 1
 ENCODER, DECODER = 0, 1
@@ -48,7 +48,8 @@ EXPORTS = ("atom_attn_workspace_bytes", "atom_attn_encoder",
            "atom_attn_decoder", "atom_attn_masks", "atom_attn_slot_attention",
            "atom_attn_slot_workspace_bytes", "atom_attn_pair_bias_split",
            "atom_attn_error_string", "atom_attn_version",
-           "atom_attn_profile_enable", "atom_attn_profile_read")
+           "atom_attn_profile_enable", "atom_attn_profile_read",
+           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -77,6 +78,10 @@ def lib():
                  _vp, szt, _vp]
         L.atom_attn_encoder.argtypes = block
         L.atom_attn_decoder.argtypes = block
+        L.atom_attn_block_noalloc.argtypes = [P(Dims), i32, i32, i32, P(Inputs), P(Params),
+                                              dbl, i64, P(Outputs), _vp]
+        L.atom_attn_noalloc_max_bytes.argtypes = []
+        L.atom_attn_noalloc_max_bytes.restype = szt
         L.atom_attn_masks.argtypes = [P(Dims), P(Inputs), i64, _vp, _vp, _vp, _vp]
         L.atom_attn_slot_attention.argtypes = [P(Dims), i32, i32, dbl, i64, _vp,
                                                _vp, _vp, _vp, _vp, _vp, _vp,
@@ -92,7 +97,9 @@ def lib():
                      "atom_attn_decoder", "atom_attn_masks",
                      "atom_attn_slot_attention", "atom_attn_slot_workspace_bytes",
                      "atom_attn_pair_bias_split", "atom_attn_version",
-                     "atom_attn_profile_enable", "atom_attn_profile_read"):
+                     "atom_attn_block_noalloc",
+                     "atom_attn_profile_enable", "atom_attn_profile_read",
+           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes"):
             getattr(L, name).restype = i32
         _lib = L
         return L

@@ -138,6 +138,11 @@ def workspace_bytes(dims: Dict[str, int], style: str, stage: str, dtype: torch.d
     return int(out.value)
 
 
+def noalloc_max_bytes() -> int:
+    """Size of the static per-device scratch of atom_attn_block_noalloc."""
+    return int(N.lib().atom_attn_noalloc_max_bytes())
+
+
 def pair_bias_split(dims: Dict[str, int], style: str, stage: str, dtype: torch.dtype) -> bool:
     """True when a block call with these sizes computes the AF3 pair bias in
     extra workgroups of the projection kernel (on compute units its tiles
@@ -156,8 +161,8 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
                             style: str = "af3", stage: str = "decoder",
                             radius: int = -1, *, workspace: Optional[torch.Tensor] = None,
                             status: Optional[torch.Tensor] = None,
-                            out: Optional[Dict[str, torch.Tensor]] = None
-                            ) -> Dict[str, torch.Tensor]:
+                            out: Optional[Dict[str, torch.Tensor]] = None,
+                            noalloc: bool = False) -> Dict[str, torch.Tensor]:
     """One windowed atom-attention block on the GPU.
 
     Returns {"hidden" [B,A,C], "attention" [B,H,A,K]} plus "token_output"
@@ -165,7 +170,9 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
     float dtype (float32 or bfloat16). `workspace` (uint8, at least
     workspace_bytes(...) bytes), `status` (int32 [1]) and preallocated
     `out` tensors are optional; the call is asynchronous on the current
-    stream."""
+    stream. With `noalloc=True` the call goes to atom_attn_block_noalloc,
+    whose scratch is the library's static per-device buffer (no workspace;
+    with `out` given and contiguous inputs nothing is allocated)."""
     if style not in _STYLES:
         raise ValueError("style must be 'af3' or 'esmfold2', got %r" % (style,))
     if stage not in _STAGES:
@@ -251,12 +258,25 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
             raise ValueError("status must be an int32 device tensor with >= 1 element")
         nout.status = status.data_ptr()
 
+    nd = N.Dims(**{k: int(v) for k, v in d.items()})
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc calls take no workspace")
+        with torch.cuda.device(dev):
+            rc = N.lib().atom_attn_block_noalloc(
+                ctypes.byref(nd), _STYLES[style], _STAGES[stage], _FLOAT_DTYPES[dtype],
+                ctypes.byref(nin), ctypes.byref(npar), float(eps), int(radius),
+                ctypes.byref(nout), _stream_handle(dev))
+        N.check(rc, "atom_attn_block_noalloc")
+        del keep
+        names_out = ["hidden", "attention",
+                     "token_output" if stage == "encoder" else "position_update"]
+        return {k: res[k] for k in names_out}
     need = workspace_bytes(d, style, stage, dtype)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
         raise ValueError("workspace needs %d bytes on %s" % (need, dev))
-    nd = N.Dims(**{k: int(v) for k, v in d.items()})
     fn = N.lib().atom_attn_encoder if stage == "encoder" else N.lib().atom_attn_decoder
     with torch.cuda.device(dev):
         rc = fn(ctypes.byref(nd), _STYLES[style], _FLOAT_DTYPES[dtype],

@@ -423,6 +423,22 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
 
 } // namespace
 
+namespace waa {
+// Entry points for the scratch-free block call (noalloc.hip): the same
+// checks and launch sequence as atom_attn_encoder/decoder.
+int block_call(const atom_attn_dims *d, int style, int stage, int dtype,
+               const atom_attn_inputs *in, const atom_attn_params *par, double eps,
+               int64_t radius, atom_attn_outputs *out, void *workspace,
+               size_t ws_bytes, void *stream) {
+    return run_block(d, style, stage, dtype, in, par, eps, radius, out, workspace,
+                     ws_bytes, stream);
+}
+int block_workspace_bytes(const atom_attn_dims *d, int style, int stage, int dtype,
+                          size_t *bytes) {
+    return atom_attn_workspace_bytes(d, style, stage, dtype, bytes);
+}
+} // namespace waa
+
 extern "C" {
 
 int atom_attn_version(void) { return kAbiVersion; }
@@ -440,6 +456,10 @@ const char *atom_attn_error_string(int code) {
         return "workspace missing, misaligned or smaller than atom_attn_workspace_bytes()";
     case ATOM_ATTN_ELAUNCH:
         return "the HIP runtime refused a kernel launch";
+    case ATOM_ATTN_ESCRATCH:
+        return "these sizes need more scratch than the library's static per-device "
+               "buffer holds (atom_attn_block_noalloc; see "
+               "atom_attn_noalloc_max_bytes)";
     case ATOM_ATTN_EUNSUPPORTED:
         return "shape outside the supported set (C, S, H*D, M, U multiples of 32 "
                "and <= 512; D one of 16, 32, 64, 128; K <= 256; AF3: V a "
