@@ -109,6 +109,11 @@ typedef struct {
         *w_attention_out;
     const void *w_ff_gate, *w_ff_up, *w_ff_out;
     const void *w_pool, *w_token, *readout_scale, *readout_bias, *w_readout;
+    /* Optional: the weight matrices packed beforehand by
+     * atom_attn_pack_params for calls with the same C, S, H*D, M, U, style,
+     * stage and dtype (NULL = pack them in the call, into the workspace).
+     * The other parameter pointers above are still required and read. */
+    const void *packed;
 } atom_attn_params;
 
 /* Outputs: hidden [B,A,C], attention [B,H,A,K], token_output [B,T,U]
@@ -215,6 +220,23 @@ int atom_attn_block_noalloc(const atom_attn_dims *dims, int style, int stage,
                             const atom_attn_params *par, double eps,
                             int64_t radius, atom_attn_outputs *out,
                             void *stream);
+
+/* Weight packing ahead of time (not a step of the method: the block
+ * reorders its weight matrices into the matrix cores' operand order, and a
+ * caller that keeps one parameter set across calls can do that once).
+ * atom_attn_packed_bytes gives the size of the packed copy of the matrices
+ * a call with these sizes reads (host-only); atom_attn_pack_params writes it
+ * into `packed` (device, 16-byte aligned, caller-owned) on `stream`, for
+ * every grid size: both operand layouts the projection kernels use. Pass
+ * it as atom_attn_params.packed to block calls with the same C, S, H*D, M,
+ * U, style, stage and dtype; it stays valid until the caller changes the
+ * matrices. Errors as atom_attn_workspace_bytes, EINVAL for a missing or
+ * misaligned matrix, EWORKSPACE for a missing or small `packed`. */
+int atom_attn_packed_bytes(const atom_attn_dims *dims, int style, int stage,
+                           int dtype, size_t *bytes);
+int atom_attn_pack_params(const atom_attn_dims *dims, int style, int stage,
+                          int dtype, const atom_attn_params *par, void *packed,
+                          size_t packed_bytes, void *stream);
 
 /* Where a block call with these sizes computes the AF3 pair bias on the
  * current device (host-only, no GPU work; the compute-unit count of the

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.EXPORTS)
-    assert lib.atom_attn_version() == 4
+    assert lib.atom_attn_version() == 5
 
 
 def test_pair_bias_split_query():
@@ -104,6 +104,38 @@ def test_shapes_whose_32bit_value_offsets_would_overflow_are_rejected():
                                            fake, fake, fake, fake, fake, fake, None, None,
                                            None, fake, fake, fake, 1 << 40, None)
         assert got == rc, (A, dt, got)
+
+
+def test_pack_params_status_codes():
+    lib = N.lib()
+    nd = N.Dims(**_dims())
+    n = ctypes.c_size_t(0)
+    assert lib.atom_attn_packed_bytes(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32,
+                                      ctypes.byref(n)) == N.OK
+    # both operand layouts of every matrix: 2 * (8 AF3 conditioning matrices
+    # [S,C] + 4 [C,HD] + [HD,C] + 2 [C,M] + [M,C] + w_pool [C,U]) * 4 bytes
+    d = _dims()
+    C, S, HD, M, U = d["C"], d["S"], d["H"] * d["D"], d["M"], d["U"]
+    elems = 8 * S * C + 4 * C * HD + HD * C + 2 * C * M + M * C + C * U
+    assert n.value == 2 * elems * 4
+    assert lib.atom_attn_packed_bytes(ctypes.byref(nd), N.AF3, N.ENCODER, 9,
+                                      ctypes.byref(n)) == N.EINVAL
+    fake = 4096  # never dereferenced: rejected on the host
+    par = N.Params()
+    assert lib.atom_attn_pack_params(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32,
+                                     ctypes.byref(par), fake, 1 << 30, None) == N.EINVAL
+    full = N.Params(**{k: fake for k in N.PARAM_NAMES if k != "packed"})
+    assert lib.atom_attn_pack_params(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32,
+                                     ctypes.byref(full), None, 1 << 30, None) == N.EWORKSPACE
+    assert lib.atom_attn_pack_params(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32,
+                                     ctypes.byref(full), fake, 16, None) == N.EWORKSPACE
+    # a misaligned prepacked buffer is rejected by the block call
+    nin = N.Inputs(**{k: fake for k, _ in N.Inputs._fields_})
+    nout = N.Outputs(hidden=fake, attention=fake, token_output=fake)
+    full.packed = fake + 8
+    assert lib.atom_attn_encoder(ctypes.byref(nd), N.AF3, N.F32, ctypes.byref(nin),
+                                 ctypes.byref(full), 1e-5, -1, ctypes.byref(nout), fake,
+                                 1 << 40, None) == N.EINVAL
 
 
 def test_workspace_sizes_of_all_workloads():

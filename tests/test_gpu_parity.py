@@ -11,6 +11,8 @@ the same seeded inputs.
   determinism), the subnormal sigmoid tail and the pooling precondition
   status word.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -20,7 +22,7 @@ from _parity import (RTOL, assert_close, assert_close_rel, compare_block, exact_
                      np64, run_gpu)
 from windowed_atom_attention_amd import masks as gpu_masks
 from windowed_atom_attention_amd import slot_attention as gpu_slot_attention
-from windowed_atom_attention_amd import windowed_atom_attention, workspace_bytes
+from windowed_atom_attention_amd import pack_params, windowed_atom_attention, workspace_bytes
 from windowed_atom_attention_amd.workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -135,6 +137,41 @@ def test_slot_attention_step(style, dtype):
     assert np.all(np.isfinite(np64(o)))
     assert_close("o", np64(o), ref["o"], rtol)
     assert np.all(np64(o)[~ref_masks["usable"].astype(bool)] == 0.0)
+
+
+PREPACKED = [
+    ("1", dict(A=700)),                     # one tile per CU at most: strip layout
+    ("0", dict(B=30, A=300)),               # more tiles than CUs: 32-column blocks
+    ("3", dict(B=2, A=600)),                # decoder: w_token stays in block layout
+    ("4b", dict(A=900, stage="decoder")),
+    ("2", dict(A=400, dtype=torch.float32)),
+]
+
+
+@pytest.mark.parametrize("case", PREPACKED, ids=[_id(c) for c in PREPACKED])
+def test_prepacked_weights_equal_per_call_packing(case):
+    """Weights packed once (atom_attn_pack_params) give the same bits as the
+    call that packs them itself, for both projection-kernel forms; one
+    packed buffer serves calls of different grid sizes."""
+    name, kw = case
+    w = make_workload(name, **kw)
+    print("prepacked", _id(case), w.dims, flush=True)
+    g = w.to("cuda")
+    ref = windowed_atom_attention(**g.kwargs())
+    pk = pack_params(g.parameters, w.dims, w.style, w.stage)
+    got = windowed_atom_attention(**g.kwargs(), packed=pk)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k].view(torch.uint8), ref[k].view(torch.uint8)), k
+    # the same packed weights on a smaller grid of the same widths
+    w2 = make_workload(name, **dict(kw, A=max(64, kw.get("A", 64) // 3), B=1))
+    g2 = w2.to("cuda")
+    g2 = dataclasses.replace(g2, parameters=g.parameters)
+    ref2 = windowed_atom_attention(**g2.kwargs())
+    got2 = windowed_atom_attention(**g2.kwargs(), packed=pk)
+    torch.cuda.synchronize()
+    for k in ref2:
+        assert torch.equal(got2[k].view(torch.uint8), ref2[k].view(torch.uint8)), k
 
 
 # ------------------------------------------------------- full size, sampled

@@ -32,7 +32,7 @@ PARAM_NAMES = ("cond_scale", "w_scale", "b_scale", "w_shift",
                "w_k", "w_v", "pair_scale", "w_pair", "w_value_gate",
                "w_attention_out", "w_ff_gate", "w_ff_up", "w_ff_out",
                "w_pool", "w_token", "readout_scale", "readout_bias",
-               "w_readout")
+               "w_readout", "packed")
 
 
 class Params(ctypes.Structure):
@@ -49,7 +49,8 @@ EXPORTS = ("atom_attn_workspace_bytes", "atom_attn_encoder",
            "atom_attn_slot_workspace_bytes", "atom_attn_pair_bias_split",
            "atom_attn_error_string", "atom_attn_version",
            "atom_attn_profile_enable", "atom_attn_profile_read",
-           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes")
+           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes",
+           "atom_attn_packed_bytes", "atom_attn_pack_params")
 
 _lock = threading.Lock()
 _lib = None
@@ -82,6 +83,8 @@ def lib():
                                               dbl, i64, P(Outputs), _vp]
         L.atom_attn_noalloc_max_bytes.argtypes = []
         L.atom_attn_noalloc_max_bytes.restype = szt
+        L.atom_attn_packed_bytes.argtypes = [P(Dims), i32, i32, i32, P(szt)]
+        L.atom_attn_pack_params.argtypes = [P(Dims), i32, i32, i32, P(Params), _vp, szt, _vp]
         L.atom_attn_masks.argtypes = [P(Dims), P(Inputs), i64, _vp, _vp, _vp, _vp]
         L.atom_attn_slot_attention.argtypes = [P(Dims), i32, i32, dbl, i64, _vp,
                                                _vp, _vp, _vp, _vp, _vp, _vp,
@@ -97,9 +100,11 @@ def lib():
                      "atom_attn_decoder", "atom_attn_masks",
                      "atom_attn_slot_attention", "atom_attn_slot_workspace_bytes",
                      "atom_attn_pair_bias_split", "atom_attn_version",
-                     "atom_attn_block_noalloc",
+                     "atom_attn_block_noalloc", "atom_attn_packed_bytes",
+                     "atom_attn_pack_params",
                      "atom_attn_profile_enable", "atom_attn_profile_read",
-           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes"):
+           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes",
+           "atom_attn_packed_bytes", "atom_attn_pack_params"):
             getattr(L, name).restype = i32
         _lib = L
         return L

@@ -138,6 +138,40 @@ def workspace_bytes(dims: Dict[str, int], style: str, stage: str, dtype: torch.d
     return int(out.value)
 
 
+def packed_bytes(dims: Dict[str, int], style: str, stage: str, dtype: torch.dtype) -> int:
+    """Bytes of the packed weight matrices of calls with these sizes."""
+    nd = N.Dims(**{k: int(v) for k, v in dims.items()})
+    out = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_packed_bytes(ctypes.byref(nd), _STYLES[style], _STAGES[stage],
+                                           _FLOAT_DTYPES[dtype], ctypes.byref(out)),
+            "atom_attn_packed_bytes")
+    return int(out.value)
+
+
+def pack_params(parameters: dict, dims: Dict[str, int], style: str, stage: str) -> torch.Tensor:
+    """Pack the weight matrices once (atom_attn_pack_params), for block calls
+    with the same widths, style, stage and dtype: pass the result as
+    `packed=` to windowed_atom_attention. Asynchronous on the current
+    stream; keep `parameters` unchanged while the result is in use."""
+    dtype = parameters["w_q"].dtype
+    dev = parameters["w_q"].device
+    if dtype not in _FLOAT_DTYPES or dev.type != "cuda":
+        raise ValueError("parameters must be float32/bfloat16 GPU tensors")
+    names = list(_PARAMS_COMMON) + list(_PARAMS_STYLE[style])
+    names += ["w_pool"] if stage == "encoder" else ["w_token"]
+    keep = {k: _prep(parameters[k], dtype) for k in names}
+    npar = N.Params(**{k: _dev_ptr(v) for k, v in keep.items()})
+    nd = N.Dims(**{k: int(v) for k, v in dims.items()})
+    nbytes = packed_bytes(dims, style, stage, dtype)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_pack_params(ctypes.byref(nd), _STYLES[style], _STAGES[stage],
+                                           _FLOAT_DTYPES[dtype], ctypes.byref(npar),
+                                           out.data_ptr(), nbytes, _stream_handle(dev))
+    N.check(rc, "atom_attn_pack_params")
+    return out
+
+
 def noalloc_max_bytes() -> int:
     """Size of the static per-device scratch of atom_attn_block_noalloc."""
     return int(N.lib().atom_attn_noalloc_max_bytes())
@@ -162,7 +196,8 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
                             radius: int = -1, *, workspace: Optional[torch.Tensor] = None,
                             status: Optional[torch.Tensor] = None,
                             out: Optional[Dict[str, torch.Tensor]] = None,
-                            noalloc: bool = False) -> Dict[str, torch.Tensor]:
+                            noalloc: bool = False,
+                            packed: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """One windowed atom-attention block on the GPU.
 
     Returns {"hidden" [B,A,C], "attention" [B,H,A,K]} plus "token_output"
@@ -172,7 +207,9 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
     `out` tensors are optional; the call is asynchronous on the current
     stream. With `noalloc=True` the call goes to atom_attn_block_noalloc,
     whose scratch is the library's static per-device buffer (no workspace;
-    with `out` given and contiguous inputs nothing is allocated)."""
+    with `out` given and contiguous inputs nothing is allocated). `packed`
+    is the result of pack_params(...) for these parameters: the call then
+    skips packing the weight matrices."""
     if style not in _STYLES:
         raise ValueError("style must be 'af3' or 'esmfold2', got %r" % (style,))
     if stage not in _STAGES:
@@ -234,6 +271,13 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
         atom_to_token=_dev_ptr(ix(structure["atom_to_token"])),
         key_index=_dev_ptr(ix(structure["key_index"])))
     npar = N.Params(**{k: _dev_ptr(v) for k, v in pars.items()})
+    if packed is not None:
+        need_p = packed_bytes(d, style, stage, dtype)
+        if (packed.dtype != torch.uint8 or packed.device != dev or not packed.is_contiguous()
+                or packed.numel() < need_p or packed.data_ptr() % 16 != 0):
+            raise ValueError("packed must be the uint8 device tensor pack_params returns "
+                             "(%d bytes)" % need_p)
+        npar.packed = packed.data_ptr()
 
     B, A, T, K, C, H, U = (d[k] for k in "B A T K C H U".split())
     res = dict(out) if out is not None else {}

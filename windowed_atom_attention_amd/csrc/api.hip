@@ -16,7 +16,7 @@ using namespace waa;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 // ------------------------------------------------------------ profiler
 
@@ -289,6 +289,26 @@ int check_common(const atom_attn_dims *d, int style, int stage, int dtype) {
     return ATOM_ATTN_OK;
 }
 
+// The weight matrices a style/stage needs are present and 16-byte aligned.
+bool matrices_present(const atom_attn_params *par, int style, int stage) {
+    const void *common[] = {par->w_q, par->w_k, par->w_v, par->w_value_gate,
+                            par->w_attention_out, par->w_ff_gate, par->w_ff_up,
+                            par->w_ff_out,
+                            stage == ATOM_ATTN_ENCODER ? par->w_pool : par->w_token};
+    for (const void *p : common)
+        if (!p || !aligned16(p))
+            return false;
+    if (style == ATOM_ATTN_AF3) {
+        const void *af[] = {par->w_scale, par->w_shift, par->w_residual_gate};
+        for (const void *p : af)
+            if (!p || !aligned16(p))
+                return false;
+    } else if (!par->w_mod || !aligned16(par->w_mod)) {
+        return false;
+    }
+    return true;
+}
+
 int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
               const atom_attn_inputs *in, const atom_attn_params *par,
               double eps, int64_t radius, atom_attn_outputs *out,
@@ -341,6 +361,11 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     const Layout L = layout_of(d, style, stage, dtype);
     if (!workspace || !aligned16(workspace) || ws_bytes < L.total)
         return ATOM_ATTN_EWORKSPACE;
+    // weights packed beforehand by atom_attn_pack_params: both layouts, the
+    // 32-column blocks first, then the 16-column strips
+    const bool prepacked = par->packed != nullptr;
+    if (prepacked && !aligned16(par->packed))
+        return ATOM_ATTN_EINVAL;
 
     const int esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
     const int dt = dtype == ATOM_ATTN_BF16 ? 1 : 0;
@@ -380,7 +405,8 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.b_rg = par->b_residual_gate; a.b_q = par->b_q;
     a.readout_scale = par->readout_scale; a.readout_bias = par->readout_bias;
     a.w_readout = par->w_readout;
-    a.pk = (const uint4 *)(ws + L.packed);
+    a.pk = prepacked ? (const uint4 *)par->packed + (nw8 ? L.pack_units : 0)
+                     : (const uint4 *)(ws + L.packed);
     a.off = off;
     a.q = ws + L.q; a.k = ws + L.k; a.v = ws + L.v; a.g = ws + L.g; a.o = ws + L.o;
     a.usable = (uint8_t *)(ws + L.usable);
@@ -406,7 +432,8 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.pbias = a.pbias;
     sa.attention = out->attention; sa.o = a.o;
 
-    if ((rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)
+    if (!prepacked &&
+        (rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)
         return rc;
     if (!enc && (rc = timed(KN_TOKEN, s, [&] { return launch_token_proj(a, dt, s); })) != ATOM_ATTN_OK)
         return rc;
@@ -481,6 +508,55 @@ int atom_attn_workspace_bytes(const atom_attn_dims *dims, int style, int stage,
     if (rc != ATOM_ATTN_OK)
         return rc;
     *bytes = layout_of(dims, style, stage, dtype).total;
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_packed_bytes(const atom_attn_dims *dims, int style, int stage, int dtype,
+                           size_t *bytes) {
+    int rc = check_common(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!bytes)
+        return ATOM_ATTN_EINVAL;
+    rc = shape_supported(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    *bytes = (size_t)layout_of(dims, style, stage, dtype).pack_units * 16 * 2;
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_pack_params(const atom_attn_dims *dims, int style, int stage, int dtype,
+                          const atom_attn_params *par, void *packed, size_t packed_bytes,
+                          void *stream) {
+    int rc = check_common(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!par || !matrices_present(par, style, stage))
+        return ATOM_ATTN_EINVAL;
+    rc = shape_supported(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    const Layout L = layout_of(dims, style, stage, dtype);
+    if (!packed || !aligned16(packed) || packed_bytes < (size_t)L.pack_units * 32)
+        return ATOM_ATTN_EWORKSPACE;
+    const int esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
+    const int dt = dtype == ATOM_ATTN_BF16 ? 1 : 0;
+    PackedOffsets off;
+    MatList mats;
+    list_mats(dims, style, stage, esz, par, &off, &mats);
+    hipStream_t s = (hipStream_t)stream;
+    for (int strips = 0; strips < 2; ++strips) {
+        PackArgs pa;
+        std::memset(&pa, 0, sizeof(pa));
+        pa.njobs = (int)mats.size();
+        for (size_t i = 0; i < mats.size(); ++i)
+            pa.job[i] = PackJob{mats[i].src, mats[i].ld, mats[i].kd, mats[i].n, *mats[i].off,
+                                strips && mats[i].tile ? 1 : 0};
+        pa.total = L.pack_units;
+        pa.out = (uint4 *)packed + (strips ? L.pack_units : 0);
+        if ((rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)
+            return rc;
+    }
     return ATOM_ATTN_OK;
 }
 
