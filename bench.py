@@ -20,7 +20,9 @@ plus atoms/s, every kernel's duration and roofline fraction, the roofline of
 the dominant kernel, the fp64 oracle's rate on the host cores (all threads
 and one thread, with the CPU model), and under "configs" the same figures
 for the other full-size workloads (--also, default 2, 3, 4a, 4b) timed in
-the same run.
+the same run, and under "ops" the per-kernel durations and roofline
+fractions of the other operators (single-to-pair features, tied pair row
+attention, the device window table).
 """
 from __future__ import annotations
 
@@ -384,6 +386,120 @@ def measure(config, steps, warmup, cache_bytes, graph=False, pack_per_call=False
     return res
 
 
+def _time_op(call, nbuf, steps, warmup):
+    """Average wall time per call (uninstrumented, between device
+    synchronisations) and per-kernel HIP-event durations of `call(i)`,
+    cycling over `nbuf` output buffers."""
+    import torch
+    from windowed_atom_attention_amd import profile_enable, profile_read
+    for i in range(warmup):
+        call(i % nbuf)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i % nbuf)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    profile_enable(True)
+    profile_read()
+    for i in range(steps):
+        call(i % nbuf)
+    torch.cuda.synchronize()
+    kt = profile_read()
+    profile_enable(False)
+    return wall, {k: {"avg_us": 1e3 * ms / n, "launches": n} for k, (ms, n) in kt.items()}
+
+
+def _roof(v, bound, amount, dtype):
+    sec = v["avg_us"] * 1e-6
+    if bound == "hbm":
+        v["GB_per_s"] = amount / sec / 1e9
+        v["frac_hbm"] = v["GB_per_s"] / HBM_PEAK_GBS
+    else:
+        v["TFLOP_per_s"] = amount / sec / 1e12
+        v["frac_mfma"] = v["TFLOP_per_s"] / MFMA_PEAK_TFLOPS[dtype]
+    v["work_per_launch"] = amount
+
+
+def measure_ops(steps=50, warmup=5, cache_bytes=768e6):
+    """The other operators at their benchmark sizes: single-to-pair features
+    (ESMFold-like trunk: B=1, N=512, C=1024, H=64, D=128, bf16) and the
+    device window table (the decoder workload's [4,12288,128], int64 and
+    int32). Outputs cycle over enough buffers to exceed the Infinity Cache."""
+    import torch
+    from windowed_atom_attention_amd import single_to_pair, window_table
+    from windowed_atom_attention_amd.workloads import make_s2p_workload
+
+    res = {}
+    acts, par, masks, on = make_s2p_workload()
+    B, Ntok, C = acts["x"].shape
+    H2, D = par["weight"].shape[-1], par["out_weight"].shape[-1]
+    cu = lambda d: {k: v.cuda() for k, v in d.items()}
+    a, p_, m = cu(acts), cu(par), cu(masks)
+    e = 2
+    per = B * Ntok * Ntok * (H2 + D) * e
+    nbuf = max(2, math.ceil(cache_bytes / per))
+    outs = [(torch.empty((B, Ntok, Ntok, H2), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((B, Ntok, Ntok, D), dtype=torch.bfloat16, device="cuda"))
+            for _ in range(nbuf)]
+    wall, kt = _time_op(lambda i: single_to_pair(a, p_, m, output_norm=on, out=outs[i]),
+                        nbuf, steps, warmup)
+    # algorithmic bytes: the two output tensors written once, the q|k rows
+    # (fp32) read once, the mask; the token kernel: x, its weight and q|k
+    pair_bytes = per + B * Ntok * H2 * 4 + B * Ntok
+    tok_bytes = B * Ntok * C * e + C * H2 * e + B * Ntok * H2 * 4 + B * Ntok
+    _roof(kt["s2p_pair"], "hbm", pair_bytes, "bf16")
+    _roof(kt["s2p_token"], "hbm", tok_bytes, "bf16")
+    kt["s2p_pair"]["flops_per_launch"] = B * Ntok * Ntok * H2 * D * 2
+    res["single_to_pair"] = {
+        "workload": "B=%d N=%d C=%d H=%d D=%d bf16, output_norm %s, %d%% absent tokens" % (
+            B, Ntok, C, H2 // 2, D, on, 5),
+        "ms_per_call": wall * 1e3, "pairs_per_s": B * Ntok * Ntok / wall,
+        "kernels": kt, "output_buffers": nbuf}
+    del outs
+    from windowed_atom_attention_amd import tied_row_attention, tied_workspace_bytes
+    from windowed_atom_attention_amd.workloads import make_tied_workload
+    acts, par = make_tied_workload()
+    B, L, _, C = acts["features"].shape
+    CB, H = acts["bias_features"].shape[-1], par["w_bias"].shape[-1]
+    HD = par["w_q"].shape[-1]
+    a, p_ = cu(acts), cu(par)
+    ws = torch.empty(tied_workspace_bytes(B, L, C, CB, H, HD // H, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    per = B * L * L * C * 2
+    nbuf = max(2, math.ceil(cache_bytes / per))
+    outs = [torch.empty((B, L, L, C), dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+    wall, kt = _time_op(lambda i: tied_row_attention(a, p_, out=outs[i], workspace=ws), nbuf,
+                        steps, warmup)
+    # algorithmic work per kernel: flops of its matrix products (the bf16
+    # path forms some of them from hi + lo pairs; counted once here)
+    LL = B * L * L
+    flops = {"tied_proj": LL * 2 * C * 4 * HD, "tied_logits": B * H * L * L * L * (HD // H) * 2,
+             "tied_out": B * H * L * L * L * (HD // H) * 2 + LL * 2 * HD * C}
+    for k, f in flops.items():
+        _roof(kt[k], "mfma", f, "bf16")
+    _roof(kt["tied_softmax"], "hbm", B * H * L * L * (4 + 4 + 2), "bf16")
+    _roof(kt["tied_bias"], "hbm", LL * CB * 2 + B * H * L * L * 4, "bf16")
+    res["tied_row_attention"] = {
+        "workload": "B=%d L=%d C=%d CB=%d H=%d D=%d bf16" % (B, L, C, CB, H, HD // H),
+        "ms_per_call": wall * 1e3, "pair_entries_per_s": LL / wall, "kernels": kt,
+        "flops_per_call": sum(flops.values())}
+    del outs, ws
+    Bw, Aw, Kw = 4, 12288, 128
+    for dt, esz in ((torch.int64, 8), (torch.int32, 4)):
+        nb = max(2, math.ceil(cache_bytes / (Bw * Aw * Kw * esz)))
+        bufs = [torch.empty((Bw, Aw, Kw), dtype=dt, device="cuda") for _ in range(nb)]
+        wall, kt = _time_op(lambda i: window_table(Bw, Aw, Kw, dtype=dt, out=bufs[i]), nb,
+                            steps, warmup)
+        _roof(kt["window"], "hbm", Bw * Aw * Kw * esz, "bf16")
+        res["window_table_%s" % ("int64" if esz == 8 else "int32")] = {
+            "workload": "B=%d A=%d K=%d, blocks of 32 queries" % (Bw, Aw, Kw),
+            "ms_per_call": wall * 1e3, "ids_per_s": Bw * Aw * Kw / wall, "kernels": kt}
+        del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +511,10 @@ def main():
                     help="further workloads timed in the same run and reported under "
                          "'configs' (comma separated; empty for none)")
     ap.add_argument("--also-steps", type=int, default=50)
+    ap.add_argument("--no-ops", action="store_true",
+                    help="skip the other operators (single-to-pair, tied attention, window table)")
+    ap.add_argument("--only-ops", action="store_true",
+                    help="time only the other operators (for profiler runs); prints their record")
     ap.add_argument("--cache-bytes", type=float, default=768e6,
                     help="input copies are added until they exceed this")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -423,6 +543,9 @@ def main():
         copy_probe()
         return
 
+    if args.only_ops:
+        print(json.dumps({"ops": measure_ops(args.steps, args.warmup)}))
+        return
     head = measure(args.config, args.steps, args.warmup, args.cache_bytes, args.graph,
                    args.pack_per_call)
     print("bench: config %s %.4f ms/step" % (args.config, head["ms_per_step"]),
@@ -435,6 +558,8 @@ def main():
                                        "atoms_per_s", "kernels", "roofline", "steps")}
         print("bench: config %s %.4f ms/step" % (c, r["ms_per_step"]), file=sys.stderr,
               flush=True)
+
+    ops = None if args.no_ops else measure_ops(args.also_steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -457,6 +582,7 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "configs": others,
+        "ops": ops,
     }
     print(json.dumps(line))
 

@@ -221,6 +221,89 @@ int atom_attn_block_noalloc(const atom_attn_dims *dims, int style, int stage,
                             int64_t radius, atom_attn_outputs *out,
                             void *stream);
 
+/* The windowed slot table on the device (the layout of local windows the
+ * block's key_index input describes; "windowed_atom_attention", Required
+ * behavior, takes key ids as supplied data, this builds such data): for
+ * every batch and query atom a, key_index[b,a,k] = q0 - (K-block)/2 + k with
+ * q0 = block*floor(a/block), i.e. each block of `block` consecutive queries
+ * sees the K consecutive ids centred on it. Ids outside [0, A) and, for
+ * radius >= 0, ids with |id - a| > radius are written as -1 (missing slots
+ * either way, so a block call gives the same results with or without
+ * them). Writes [B,A,K] ids of index_bytes = 8 (int64, the block's
+ * key_index type) or 4 (int32) into caller-owned device memory on
+ * `stream`. Errors: EINVAL for a size < 1, radius < -1, an index size
+ * other than 4 or 8 or a NULL output; EUNSUPPORTED for A > 2^29 or
+ * B*A*K >= 2^31. */
+int atom_attn_window_table(int64_t B, int64_t A, int64_t K, int64_t block,
+                           int64_t radius, int index_bytes, void *key_index,
+                           void *stream);
+
+/* Single-to-pair features ("ESMFold Single-to-Pair Features", Required
+ * behavior and Worked example). Tokens x [B,N,C] with presence mask [B,N]
+ * (one byte, 0 = absent; absent payloads may be NaN/Inf and are never read
+ * into arithmetic): y = (LN(x) * norm_scale + norm_bias) @ weight + bias
+ * (population LayerNorm, eps inside the root; weight [C,2H] stored
+ * [in][out], bias [2H], norm_scale/norm_bias [C]); q = y[:H], k = y[H:];
+ * pair_features[b,i,j] = [k_i * q_j, q_j - k_i] ([B,N,N,2H]);
+ * output[b,i,j] = pair_features[b,i,j] @ out_weight + out_bias
+ * (out_weight [2H,D], out_bias [D]), then, if output_norm, LN(.) *
+ * output_scale + output_bias ([D] each, may be NULL otherwise); both
+ * outputs are zero unless tokens i and j are both present. Float tensors
+ * share `dtype` (arithmetic fp32; for bf16 the features are rounded to
+ * bf16 once and the output is computed from those rounded values). Output
+ * pointers 16-byte aligned. Supported: H in {32, 64} (and 128 for bf16),
+ * D in {64, 128, 256}, C <= 4096, B*N <= 2^24. Workspace: fp32 q|k rows,
+ * atom_attn_single_to_pair_workspace_bytes() bytes. Errors: EINVAL,
+ * EWORKSPACE, EUNSUPPORTED, ELAUNCH as for the block. */
+typedef struct {
+    int64_t B, N, C, H, D;
+} atom_attn_s2p_dims;
+int atom_attn_single_to_pair_workspace_bytes(const atom_attn_s2p_dims *dims,
+                                             int dtype, size_t *bytes);
+int atom_attn_single_to_pair(const atom_attn_s2p_dims *dims, int dtype,
+                             double eps, int output_norm, const void *x,
+                             const uint8_t *mask, const void *weight,
+                             const void *bias, const void *norm_scale,
+                             const void *norm_bias, const void *out_weight,
+                             const void *out_bias, const void *output_scale,
+                             const void *output_bias, void *pair_features,
+                             void *output, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Tied pair row attention ("Tied Pair Row Attention", Required behavior
+ * and Worked example). features [B,L,L,C] and bias_features [B,L,L,CB]
+ * (a pair grid and its bias features); both pair axes are exchanged first
+ * and the update's axes exchanged back, so that for output position (a, c)
+ *   A[h][i][j] = softmax_j( sum_{s,d} q(F[i][s])[h,d] k(F[j][s])[h,d]
+ *                           / sqrt(L*D) + beta_h(Fb[j][i]) )
+ *   out[a][c] = (g(F[a][c]) * sum_j A[h][c][j] v(F[j][a])) @ w_out + b_out
+ * with F normalised by affine population LayerNorm (norm_scale, norm_bias
+ * [C]; eps inside the root), q, k, v = . @ w_q, w_k, w_v and the value gate
+ * g = sigmoid(. @ w_gate) (all [C,H*D], bias-free), beta_h = (LN(Fb) *
+ * bias_norm_scale + bias_norm_bias) @ w_bias[:, h] (w_bias [CB,H]), w_out
+ * [H*D,C], b_out [C]. The update is written to `output` [B,L,L,C]; no
+ * residual is added. Float tensors share `dtype` (arithmetic fp32; bf16
+ * keeps q, k, v, the gate and the attention weights in bf16 between
+ * kernels). Supported: D = 32, H <= 8, C a multiple of 32 <= 256,
+ * CB <= 1024, L <= 1024, B*L*L <= 2^26; features and output 16-byte
+ * aligned. Workspace: atom_attn_tied_row_attention_workspace_bytes(). */
+typedef struct {
+    int64_t B, L, C, CB, H, D;
+} atom_attn_tied_dims;
+int atom_attn_tied_row_attention_workspace_bytes(const atom_attn_tied_dims *dims,
+                                                 int dtype, size_t *bytes);
+int atom_attn_tied_row_attention(const atom_attn_tied_dims *dims, int dtype,
+                                 double eps, const void *features,
+                                 const void *bias_features,
+                                 const void *norm_scale, const void *norm_bias,
+                                 const void *bias_norm_scale,
+                                 const void *bias_norm_bias, const void *w_q,
+                                 const void *w_k, const void *w_v,
+                                 const void *w_bias, const void *w_gate,
+                                 const void *w_out, const void *b_out,
+                                 void *output, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 /* Weight packing ahead of time (not a step of the method: the block
  * reorders its weight matrices into the matrix cores' operand order, and a
  * caller that keeps one parameter set across calls can do that once).

@@ -38,6 +38,8 @@ def assert_close(name, got, ref, rtol, where=None):
     tol = rtol * (np.abs(ref) + rms)
     err = np.abs(got - ref)
     bad = err > tol
+    print("%s: max err/tol %.3g (rtol=%g, rms floor %.3g)" % (
+        name, float(np.max(err / np.maximum(tol, 1e-300))), rtol, rms))
     if bad.any():
         i = np.unravel_index(np.argmax(err / np.maximum(tol, 1e-300)), err.shape)
         raise AssertionError(

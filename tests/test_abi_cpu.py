@@ -138,6 +138,19 @@ def test_pack_params_status_codes():
                                  1 << 40, None) == N.EINVAL
 
 
+def test_window_table_status_codes():
+    lib = N.lib()
+    fake = 4096  # never dereferenced: rejected on the host
+    assert lib.atom_attn_window_table(1, 10, 4, 2, -1, 8, None, None) == N.EINVAL
+    assert lib.atom_attn_window_table(0, 10, 4, 2, -1, 8, fake, None) == N.EINVAL
+    assert lib.atom_attn_window_table(1, 10, 4, 0, -1, 8, fake, None) == N.EINVAL
+    assert lib.atom_attn_window_table(1, 10, 4, 2, -2, 8, fake, None) == N.EINVAL
+    assert lib.atom_attn_window_table(1, 10, 4, 2, -1, 2, fake, None) == N.EINVAL
+    assert lib.atom_attn_window_table(1, 1 << 31, 4, 2, -1, 8, fake, None) == N.EUNSUPPORTED
+    assert lib.atom_attn_window_table(1 << 12, 1 << 12, 1 << 8, 32, -1, 8, fake,
+                                      None) == N.EUNSUPPORTED
+
+
 def test_workspace_sizes_of_all_workloads():
     for name in ("0", "1", "2", "3", "4a", "4b"):
         w = make_workload(name, A=64 if name != "0" else None)

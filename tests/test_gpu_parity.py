@@ -401,3 +401,187 @@ def test_pooling_tokens_across_tiles(dtype):
     ref = oracle.block(**w.kwargs(), intermediates=True)
     assert_close("token_output", np64(out["token_output"]), ref["token_output"], RTOL[dtype])
     exact_zero_checks(w, {k: v for k, v in out.items()}, ref["usable"], ref["allowed"])
+
+
+# ------------------------------------------------- device window table
+
+@pytest.mark.parametrize("B,A,K,block,radius", [
+    (1, 300, 128, 32, -1), (2, 1000, 128, 32, 48), (1, 97, 21, 8, 5),   # ragged rows
+    (3, 50, 8, 16, 0), (1, 40, 5, 8, -1),                              # K < block, odd difference
+    (4, 12288, 128, 32, -1),                                            # decoder workload size
+])
+def test_window_table_bit_exact(B, A, K, block, radius):
+    from oracle import pair_ops
+    from windowed_atom_attention_amd import window_table
+    print("window", B, A, K, block, radius, flush=True)
+    exp = pair_ops.window_table(B, A, K, block=block, radius=radius)
+    for dt in (torch.int64, torch.int32):
+        got = window_table(B, A, K, block=block, radius=radius, dtype=dt)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().astype(np.int64), exp), dt
+
+
+def test_block_with_device_window_table_matches_host_table():
+    """The block gives the same bits with the device-built table (missing
+    ids written as -1, radius folded in) as with the generator's table."""
+    from windowed_atom_attention_amd import window_table
+    from windowed_atom_attention_amd.workloads import window_table as host_table
+    w = make_workload("4b", A=700)
+    w.structure["key_index"] = host_table(1, 700, 128)
+    g = w.to("cuda")
+    ref = windowed_atom_attention(**g.kwargs())
+    g.structure["key_index"] = window_table(1, 700, 128, radius=w.radius)
+    got = windowed_atom_attention(**g.kwargs())
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k].view(torch.uint8), ref[k].view(torch.uint8)), k
+
+
+# ---------------------------------------------------- single-to-pair features
+
+S2P_CASES = [
+    dict(B=1, N=70, C=96, H=32, D=64, dtype=torch.float32, output_norm=False),
+    dict(B=2, N=45, C=64, H=64, D=128, dtype=torch.float32, output_norm=True),
+    dict(B=1, N=100, C=1024, H=64, D=128, dtype=torch.bfloat16, output_norm=False),
+    dict(B=2, N=33, C=200, H=128, D=256, dtype=torch.bfloat16, output_norm=True),
+    dict(B=1, N=64, C=128, H=32, D=128, dtype=torch.bfloat16, output_norm=True),
+]
+
+
+def _s2p_case_id(c):
+    return "B%(B)d-N%(N)d-C%(C)d-H%(H)d-D%(D)d-" % c + ("bf16" if c["dtype"] == torch.bfloat16 else "f32") + \
+        ("-norm" if c["output_norm"] else "")
+
+
+def _s2p_check(acts, par, masks, on, pf, out, rows=None):
+    from oracle import pair_ops
+    rtol = RTOL[acts["x"].dtype]
+    ref_pf, ref_out = pair_ops.single_to_pair(
+        acts["x"], masks["mask"], par["weight"], par["bias"], par["norm_scale"],
+        par["norm_bias"], par["out_weight"], par["out_bias"], eps=1e-5, output_norm=on,
+        output_scale=par["output_scale"], output_bias=par["output_bias"], rows=rows)
+    gpf, gout = np64(pf), np64(out)
+    if rows is not None:
+        gpf, gout = gpf[:, rows], gout[:, rows]
+    m = masks["mask"].numpy()
+    I = np.arange(m.shape[1]) if rows is None else rows
+    both = m[:, I, None] & m[:, None, :]
+    assert np.all(gpf[~both] == 0.0) and np.all(gout[~both] == 0.0)
+    assert_close("pair_features", gpf, ref_pf, rtol)
+    assert_close("output", gout, ref_out, rtol)
+
+
+@pytest.mark.parametrize("case", S2P_CASES, ids=[_s2p_case_id(c) for c in S2P_CASES])
+def test_single_to_pair_matches_oracle(case):
+    from windowed_atom_attention_amd import single_to_pair
+    from windowed_atom_attention_amd.workloads import make_s2p_workload
+    c = dict(case)
+    print("s2p", _s2p_case_id(c), flush=True)
+    acts, par, masks, on = make_s2p_workload(**c, seed=11)
+    cu = lambda d: {k: v.cuda() for k, v in d.items()}
+    pf, out = single_to_pair(cu(acts), cu(par), cu(masks), output_norm=on)
+    torch.cuda.synchronize()
+    _s2p_check(acts, par, masks, on, pf, out)
+
+
+def test_single_to_pair_full_size_sampled_rows():
+    """The benchmarked size (B=1, N=512, C=1024, H=64, D=128, bf16) on
+    sampled query rows the oracle computes alone, both output modes."""
+    from windowed_atom_attention_amd import single_to_pair
+    from windowed_atom_attention_amd.workloads import make_s2p_workload
+    rows = np.array([0, 1, 31, 32, 255, 256, 480, 510, 511])
+    for on in (False, True):
+        acts, par, masks, _ = make_s2p_workload(output_norm=on)
+        cu = lambda d: {k: v.cuda() for k, v in d.items()}
+        pf, out = single_to_pair(cu(acts), cu(par), cu(masks), output_norm=on)
+        torch.cuda.synchronize()
+        assert torch.isfinite(pf.float()).all() and torch.isfinite(out.float()).all()
+        _s2p_check(acts, par, masks, on, pf, out, rows=rows)
+
+
+# ------------------------------------------------- tied pair row attention
+
+TIED_CASES = [
+    dict(B=1, L=37, C=64, CB=16, H=2, D=32, dtype=torch.float32),     # ragged grid
+    dict(B=2, L=64, C=128, CB=32, H=4, D=32, dtype=torch.float32),
+    dict(B=1, L=100, C=32, CB=8, H=1, D=32, dtype=torch.bfloat16),
+    dict(B=2, L=45, C=96, CB=40, H=3, D=32, dtype=torch.bfloat16),
+    dict(B=1, L=70, C=256, CB=128, H=8, D=32, dtype=torch.bfloat16),
+    dict(B=1, L=1, C=32, CB=4, H=1, D=32, dtype=torch.float32),       # one residue
+]
+
+
+def _tied_id(c):
+    return "B%(B)d-L%(L)d-C%(C)d-CB%(CB)d-H%(H)d" % c + ("-bf16" if c["dtype"] == torch.bfloat16 else "-f32")
+
+
+def _tied_check(acts, par, got, rtol):
+    from oracle import pair_ops
+    ref = pair_ops.tied_row_attention(
+        acts["features"], acts["bias_features"], par["norm_scale"], par["norm_bias"],
+        par["bias_norm_scale"], par["bias_norm_bias"], par["w_q"], par["w_k"], par["w_v"],
+        par["w_bias"], par["w_gate"], par["w_out"], par["b_out"], eps=1e-5)
+    g = np64(got)
+    assert np.all(np.isfinite(g))
+    assert_close("tied update", g, ref, rtol)
+
+
+@pytest.mark.parametrize("case", TIED_CASES, ids=[_tied_id(c) for c in TIED_CASES])
+def test_tied_row_attention_matches_oracle(case):
+    from windowed_atom_attention_amd import tied_row_attention
+    from windowed_atom_attention_amd.workloads import make_tied_workload
+    print("tied", _tied_id(case), flush=True)
+    acts, par = make_tied_workload(**case, seed=12)
+    cu = lambda d: {k: v.cuda() for k, v in d.items()}
+    got = tied_row_attention(cu(acts), cu(par))
+    torch.cuda.synchronize()
+    _tied_check(acts, par, got, RTOL[case["dtype"]])
+
+
+def test_tied_row_attention_worked_example_on_gpu():
+    """The page's worked example (fp32, L=2, C=2 padded to the kernel's
+    supported widths with zero channels and weights) gives its closed form."""
+    import json
+    import math
+    import os
+    from windowed_atom_attention_amd import tied_row_attention
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "tied_pair_row_attention_worked_example.json")))
+    p_ = 1.0 / (1.0 + math.exp(-math.sqrt(2.0)))
+    # C = 2 channels -> 32 (zero-padded channels change LayerNorm statistics,
+    # so the padding carries the mean and spread of the two real ones: the
+    # two-channel vectors [-1, 1] / [1, -1] become 16 copies of each value)
+    f = torch.tensor(g["features"], dtype=torch.float32)                 # [1,2,2,2]
+    feat = f.repeat_interleave(16, dim=-1)                               # [1,2,2,32]
+    bfeat = torch.tensor(g["bias_features"], dtype=torch.float32).repeat_interleave(2, dim=-1)
+    C, CB = 32, 4
+    w = torch.zeros(C, 32)
+    w[:16, 0] = -1.0 / 16
+    w[16:, 0] = 1.0 / 16            # -mean of first half + mean of second half = (-x0 + x1) of the example
+    par = {"norm_scale": torch.ones(C), "norm_bias": torch.zeros(C),
+           "bias_norm_scale": torch.ones(CB), "bias_norm_bias": torch.zeros(CB),
+           # the head is 32 wide here (logits scaled by 1/sqrt(2*32) instead of
+           # 1/sqrt(2)): q and k carry a factor 32**0.25 each, v none
+           "w_q": w * 32 ** 0.25, "w_k": w * 32 ** 0.25, "w_v": w.clone(),
+           "w_bias": torch.zeros(CB, 1),
+           "w_gate": torch.zeros(C, 32), "w_out": torch.zeros(32, C), "b_out": torch.zeros(C)}
+    par["w_out"][0, 0], par["w_out"][0, 1] = 2.0, 4.0
+    par["b_out"][0], par["b_out"][1] = 1.0, -1.0
+    cu = lambda d: {k: v.cuda().contiguous() for k, v in d.items()}
+    out = tied_row_attention(cu({"features": feat, "bias_features": bfeat}), cu(par),
+                             eps=g["eps"])
+    torch.cuda.synchronize()
+    got = out[0, :, :, :2].double().cpu().numpy()
+    exp = np.array([[[2, 1], [2, 1]], [[2 - 2 * p_, 1 - 4 * p_], [2 * p_, 4 * p_ - 3]]])
+    np.testing.assert_allclose(got, exp, rtol=1e-5, atol=1e-5)
+
+
+def test_tied_row_attention_full_size():
+    """The benchmarked size (B=1, L=256, C=128, CB=128, H=4, D=32, bf16)."""
+    from windowed_atom_attention_amd import tied_row_attention
+    from windowed_atom_attention_amd.workloads import make_tied_workload
+    acts, par = make_tied_workload()
+    cu = lambda d: {k: v.cuda() for k, v in d.items()}
+    got = tied_row_attention(cu(acts), cu(par))
+    torch.cuda.synchronize()
+    _tied_check(acts, par, got, RTOL[torch.bfloat16])

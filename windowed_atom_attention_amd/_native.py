@@ -39,6 +39,14 @@ class Params(ctypes.Structure):
     _fields_ = [(n, _vp) for n in PARAM_NAMES]
 
 
+class S2PDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in "B N C H D".split()]
+
+
+class TiedDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in "B L C CB H D".split()]
+
+
 class Outputs(ctypes.Structure):
     _fields_ = [("hidden", _vp), ("attention", _vp), ("token_output", _vp),
                 ("position_update", _vp), ("status", _vp)]
@@ -50,7 +58,9 @@ EXPORTS = ("atom_attn_workspace_bytes", "atom_attn_encoder",
            "atom_attn_error_string", "atom_attn_version",
            "atom_attn_profile_enable", "atom_attn_profile_read",
            "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes",
-           "atom_attn_packed_bytes", "atom_attn_pack_params")
+           "atom_attn_packed_bytes", "atom_attn_pack_params", "atom_attn_window_table",
+           "atom_attn_single_to_pair_workspace_bytes", "atom_attn_single_to_pair",
+           "atom_attn_tied_row_attention_workspace_bytes", "atom_attn_tied_row_attention")
 
 _lock = threading.Lock()
 _lib = None
@@ -85,6 +95,11 @@ def lib():
         L.atom_attn_noalloc_max_bytes.restype = szt
         L.atom_attn_packed_bytes.argtypes = [P(Dims), i32, i32, i32, P(szt)]
         L.atom_attn_pack_params.argtypes = [P(Dims), i32, i32, i32, P(Params), _vp, szt, _vp]
+        L.atom_attn_window_table.argtypes = [i64, i64, i64, i64, i64, i32, _vp, _vp]
+        L.atom_attn_single_to_pair_workspace_bytes.argtypes = [P(S2PDims), i32, P(szt)]
+        L.atom_attn_single_to_pair.argtypes = [P(S2PDims), i32, dbl, i32] + [_vp] * 13 + [szt, _vp]
+        L.atom_attn_tied_row_attention_workspace_bytes.argtypes = [P(TiedDims), i32, P(szt)]
+        L.atom_attn_tied_row_attention.argtypes = [P(TiedDims), i32, dbl] + [_vp] * 15 + [szt, _vp]
         L.atom_attn_masks.argtypes = [P(Dims), P(Inputs), i64, _vp, _vp, _vp, _vp]
         L.atom_attn_slot_attention.argtypes = [P(Dims), i32, i32, dbl, i64, _vp,
                                                _vp, _vp, _vp, _vp, _vp, _vp,
@@ -101,10 +116,15 @@ def lib():
                      "atom_attn_slot_attention", "atom_attn_slot_workspace_bytes",
                      "atom_attn_pair_bias_split", "atom_attn_version",
                      "atom_attn_block_noalloc", "atom_attn_packed_bytes",
-                     "atom_attn_pack_params",
+                     "atom_attn_pack_params", "atom_attn_window_table",
+                     "atom_attn_single_to_pair_workspace_bytes", "atom_attn_single_to_pair",
+                     "atom_attn_tied_row_attention_workspace_bytes",
+                     "atom_attn_tied_row_attention",
                      "atom_attn_profile_enable", "atom_attn_profile_read",
            "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes",
-           "atom_attn_packed_bytes", "atom_attn_pack_params"):
+           "atom_attn_packed_bytes", "atom_attn_pack_params", "atom_attn_window_table",
+           "atom_attn_single_to_pair_workspace_bytes", "atom_attn_single_to_pair",
+           "atom_attn_tied_row_attention_workspace_bytes", "atom_attn_tied_row_attention"):
             getattr(L, name).restype = i32
         _lib = L
         return L

@@ -172,6 +172,138 @@ def pack_params(parameters: dict, dims: Dict[str, int], style: str, stage: str) 
     return out
 
 
+def window_table(B: int, A: int, K: int, block: int = 32, radius: int = -1,
+                 dtype: torch.dtype = torch.int64, device="cuda", out=None) -> torch.Tensor:
+    """Windowed key ids [B,A,K] built on the GPU (atom_attn_window_table):
+    each block of `block` queries sees K consecutive ids centred on it;
+    out-of-range and out-of-radius ids are -1. `out` may supply the
+    (contiguous) result tensor."""
+    if dtype not in (torch.int64, torch.int32):
+        raise TypeError("dtype must be torch.int64 or torch.int32")
+    if out is None:
+        out = torch.empty((int(B), int(A), int(K)), dtype=dtype, device=device)
+    elif (tuple(out.shape) != (int(B), int(A), int(K)) or out.dtype != dtype
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous %s tensor of shape [B,A,K]" % dtype)
+    dev = out.device
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_window_table(int(B), int(A), int(K), int(block), int(radius),
+                                            out.element_size(), out.data_ptr(),
+                                            _stream_handle(dev))
+    N.check(rc, "atom_attn_window_table")
+    return out
+
+
+_S2P_PARAMS = ("weight", "bias", "norm_scale", "norm_bias", "out_weight", "out_bias")
+
+
+def single_to_pair(activations: dict, parameters: dict, masks: dict, eps: float = 1e-05,
+                   output_norm: bool = False, *, out=None):
+    """Single-to-pair features on the GPU (atom_attn_single_to_pair), with the
+    page's signature: activations {"x" [B,N,C]}, masks {"mask" [B,N] bool},
+    parameters {weight [C,2H], bias [2H], norm_scale, norm_bias [C],
+    out_weight [2H,D], out_bias [D], and output_scale/output_bias [D] when
+    output_norm}. Returns (pair_features [B,N,N,2H], output [B,N,N,D]);
+    `out` may supply those two tensors (contiguous, same dtype)."""
+    x = activations["x"]
+    dtype, dev = x.dtype, x.device
+    if dtype not in _FLOAT_DTYPES or dev.type != "cuda":
+        raise ValueError("x must be a float32/bfloat16 GPU tensor")
+    B, Ntok, C = x.shape
+    H2 = parameters["weight"].shape[-1]
+    D = parameters["out_weight"].shape[-1]
+    names = list(_S2P_PARAMS) + (["output_scale", "output_bias"] if output_norm else [])
+    keep = [_prep(x, dtype), _mask(masks["mask"])]
+    pp = {k: _prep(parameters[k], dtype) for k in names}
+    for k, v in pp.items():
+        if v.device != dev:
+            raise ValueError("all tensors must share one device")
+    nd = N.S2PDims(B=B, N=Ntok, C=C, H=H2 // 2, D=D)
+    need = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_single_to_pair_workspace_bytes(ctypes.byref(nd),
+                                                             _FLOAT_DTYPES[dtype],
+                                                             ctypes.byref(need)),
+            "atom_attn_single_to_pair_workspace_bytes")
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    if out is None:
+        pf = torch.empty((B, Ntok, Ntok, H2), dtype=dtype, device=dev)
+        out = torch.empty((B, Ntok, Ntok, D), dtype=dtype, device=dev)
+    else:
+        pf, out = out
+        for t, shp in ((pf, (B, Ntok, Ntok, H2)), (out, (B, Ntok, Ntok, D))):
+            if tuple(t.shape) != shp or t.dtype != dtype or not t.is_contiguous():
+                raise ValueError("out tensors must be contiguous %s of shape %s" % (dtype, shp))
+    g = lambda k: _dev_ptr(pp.get(k))
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_single_to_pair(
+            ctypes.byref(nd), _FLOAT_DTYPES[dtype], float(eps), 1 if output_norm else 0,
+            keep[0].data_ptr(), keep[1].data_ptr(), g("weight"), g("bias"), g("norm_scale"),
+            g("norm_bias"), g("out_weight"), g("out_bias"), g("output_scale"),
+            g("output_bias"), pf.data_ptr(), out.data_ptr(), ws.data_ptr(), int(need.value),
+            _stream_handle(dev))
+    N.check(rc, "atom_attn_single_to_pair")
+    del keep, pp
+    return pf, out
+
+
+_TIED_PARAMS = ("norm_scale", "norm_bias", "bias_norm_scale", "bias_norm_bias", "w_q", "w_k",
+                "w_v", "w_bias", "w_gate", "w_out", "b_out")
+
+
+def tied_row_attention(activations: dict, parameters: dict, eps: float = 1e-05, *, out=None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Tied pair row attention on the GPU (atom_attn_tied_row_attention),
+    with the page's signature: activations {"features" [B,L,L,C],
+    "bias_features" [B,L,L,CB]}, parameters {norm_scale, norm_bias [C],
+    bias_norm_scale, bias_norm_bias [CB], w_q, w_k, w_v, w_gate [C,H*D],
+    w_bias [CB,H], w_out [H*D,C], b_out [C]}. Returns the update [B,L,L,C]
+    (no residual added)."""
+    f = activations["features"]
+    dtype, dev = f.dtype, f.device
+    if dtype not in _FLOAT_DTYPES or dev.type != "cuda":
+        raise ValueError("features must be a float32/bfloat16 GPU tensor")
+    B, L, L2, C = f.shape
+    if L2 != L:
+        raise ValueError("features must be a square pair grid [B,L,L,C]")
+    fb = _prep(activations["bias_features"], dtype)
+    CB = fb.shape[-1]
+    H = parameters["w_bias"].shape[-1]
+    HD = parameters["w_q"].shape[-1]
+    keep = [_prep(f, dtype), fb]
+    pp = {k: _prep(parameters[k], dtype) for k in _TIED_PARAMS}
+    nd = N.TiedDims(B=B, L=L, C=C, CB=CB, H=H, D=HD // H)
+    need = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_tied_row_attention_workspace_bytes(
+        ctypes.byref(nd), _FLOAT_DTYPES[dtype], ctypes.byref(need)),
+        "atom_attn_tied_row_attention_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need.value:
+        raise ValueError("workspace needs %d bytes" % need.value)
+    if out is None:
+        out = torch.empty((B, L, L, C), dtype=dtype, device=dev)
+    elif tuple(out.shape) != (B, L, L, C) or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous %s tensor [B,L,L,C]" % dtype)
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_tied_row_attention(
+            ctypes.byref(nd), _FLOAT_DTYPES[dtype], float(eps), keep[0].data_ptr(),
+            keep[1].data_ptr(), *[pp[k].data_ptr() for k in _TIED_PARAMS], out.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(dev))
+    N.check(rc, "atom_attn_tied_row_attention")
+    del keep, pp
+    return out
+
+
+def tied_workspace_bytes(B, L, C, CB, H, D, dtype) -> int:
+    nd = N.TiedDims(B=B, L=L, C=C, CB=CB, H=H, D=D)
+    need = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_tied_row_attention_workspace_bytes(
+        ctypes.byref(nd), _FLOAT_DTYPES[dtype], ctypes.byref(need)),
+        "atom_attn_tied_row_attention_workspace_bytes")
+    return int(need.value)
+
+
 def noalloc_max_bytes() -> int:
     """Size of the static per-device scratch of atom_attn_block_noalloc."""
     return int(N.lib().atom_attn_noalloc_max_bytes())

@@ -29,8 +29,10 @@ struct Profiler {
     std::vector<ProfRec> recs;
     std::vector<hipEvent_t> pool;
     const char *names[16] = {"pack", "token_proj", "prep", "slot_attention",
-                             "post", "pool", "masks"};
-    int nnames = 7;
+                             "post", "pool", "masks", "s2p_token", "s2p_pair",
+                             "window", "tied_bias", "tied_proj", "tied_logits",
+                             "tied_softmax", "tied_out"};
+    int nnames = 15;
 };
 Profiler g_prof;
 
@@ -79,6 +81,7 @@ hipEvent_t prof_event() {
 }
 
 enum { KN_PACK = 0, KN_TOKEN = 1, KN_PREP = 2, KN_SLOT = 3, KN_POST = 4, KN_POOL = 5, KN_MASKS = 6 };
+static_assert(KN_MASKS + 1 == waa::KN_S2P_TOK, "profiler ids of the other operators follow");
 
 // Run one launcher, bracketed by events when profiling is on.
 template <typename F> int timed(int kernel, hipStream_t s, F launch) {
@@ -96,6 +99,30 @@ template <typename F> int timed(int kernel, hipStream_t s, F launch) {
     }
     return err == hipSuccess ? ATOM_ATTN_OK : ATOM_ATTN_ELAUNCH;
 }
+
+} // namespace
+
+namespace waa {
+ProfSpan prof_begin(int kernel, hipStream_t s) {
+    ProfSpan sp;
+    sp.kernel = kernel;
+    if (g_prof.on) {
+        sp.e0 = prof_event();
+        sp.e1 = prof_event();
+        if (sp.e0 && sp.e1)
+            (void)hipEventRecord(sp.e0, s);
+    }
+    return sp;
+}
+void prof_end(const ProfSpan &sp, hipStream_t s) {
+    if (g_prof.on && sp.e0 && sp.e1) {
+        (void)hipEventRecord(sp.e1, s);
+        g_prof.recs.push_back({sp.kernel, sp.e0, sp.e1});
+    }
+}
+} // namespace waa
+
+namespace {
 
 // ------------------------------------------------------------ checks
 

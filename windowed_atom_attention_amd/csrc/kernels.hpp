@@ -85,6 +85,38 @@ struct SlotArgs {
     void *attention, *o;
 };
 
+// Kernel timing with HIP events for the library's profiling mode (a no-op
+// unless atom_attn_profile_enable is on): prof_begin before a launch and
+// prof_end after it, on the launch stream. Ids past the block's kernels:
+enum { KN_S2P_TOK = 7, KN_S2P_PAIR = 8, KN_WINDOW = 9, KN_TIED_BIAS = 10, KN_TIED_PROJ = 11,
+       KN_TIED_LOGITS = 12, KN_TIED_SOFTMAX = 13, KN_TIED_OUT = 14 };
+struct ProfSpan {
+    int kernel = -1;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+};
+ProfSpan prof_begin(int kernel, hipStream_t s);
+void prof_end(const ProfSpan &sp, hipStream_t s);
+
+// Single-to-pair features (pair_s2p.hip): tokens x [B,N,C], mask [B,N];
+// weight [C,2H], bias [2H], norm_scale/norm_bias [C], out_weight [2H,D],
+// out_bias [D], output_scale/output_bias [D]; outputs pair_features
+// [B,N,N,2H], output [B,N,N,D]; qk: workspace, fp32 [B,N,2H] (q then k).
+struct S2PArgs {
+    int B, N, C, H, D;
+    float eps;
+    const void *x;
+    const uint8_t *mask;
+    const void *weight, *bias, *norm_scale, *norm_bias, *out_weight, *out_bias,
+        *output_scale, *output_bias;
+    float *qk;
+    const uint4 *wo_packed; // workspace: out_weight in MFMA B-fragment order
+    void *pair_features, *output;
+};
+hipError_t launch_s2p(const S2PArgs &a, int dtype, int output_norm, hipStream_t s);
+int s2p_supported(int64_t C, int64_t H, int64_t D, int dtype);
+size_t s2p_tok_lds(int C);
+size_t s2p_pair_lds(int H, int D);
+
 // One matrix to pack: src[r*ld + c] for r < kd, c < n (storage dtype).
 struct PackJob {
     const void *src;

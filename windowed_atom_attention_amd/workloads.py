@@ -29,7 +29,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make_workload", "window_table"]
+__all__ = ["Workload", "CONFIGS", "make_workload", "window_table", "make_s2p_workload",
+           "make_tied_workload"]
 
 
 @dataclasses.dataclass
@@ -336,3 +337,57 @@ def make_workload(name: str, seed: Optional[int] = None, A: Optional[int] = None
     return Workload(name=name, style=style_, stage=stage_, dtype=dt, eps=eps,
                     radius=r["radius"], dims=dims, activations=acts,
                     parameters=p, masks=masks, structure=structure)
+
+
+def make_s2p_workload(B: int = 1, N: int = 512, C: int = 1024, H: int = 64, D: int = 128,
+                      dtype: torch.dtype = torch.bfloat16, seed: int = 7,
+                      absent: float = 0.05, output_norm: bool = False):
+    """Inputs of the single-to-pair operator (the pages give no workload; the
+    default sizes are an ESMFold-like trunk: 1024-wide token states, q and k
+    of width 64, a 128-wide pair head, 512 tokens). x ~ N(0, 1), matrices
+    ~ N(0, 1/sqrt(fan_in)), biases ~ N(0, 0.1), norm scales ~ 1 + N(0, 0.1);
+    a fraction `absent` of tokens is absent with NaN payloads. Returns
+    (activations, parameters, masks, output_norm) for the page's signature."""
+    g = torch.Generator().manual_seed(seed)
+    f32 = torch.float32
+
+    def randn(*shape, std=1.0, mean=0.0):
+        return torch.randn(shape, generator=g, dtype=f32) * std + mean
+
+    x = randn(B, N, C)
+    mask = torch.rand((B, N), generator=g) >= absent
+    x = torch.where(mask[..., None], x, torch.full_like(x, math.nan))
+    p = {"weight": randn(C, 2 * H, std=1.0 / math.sqrt(C)), "bias": randn(2 * H, std=0.1),
+         "norm_scale": randn(C, std=0.1, mean=1.0), "norm_bias": randn(C, std=0.1),
+         "out_weight": randn(2 * H, D, std=1.0 / math.sqrt(2 * H)), "out_bias": randn(D, std=0.1),
+         "output_scale": randn(D, std=0.1, mean=1.0), "output_bias": randn(D, std=0.1)}
+    acts = {"x": x.to(dtype).contiguous()}
+    p = {k: v.to(dtype).contiguous() for k, v in p.items()}
+    return acts, p, {"mask": mask.contiguous()}, output_norm
+
+
+def make_tied_workload(B: int = 1, L: int = 256, C: int = 128, CB: int = 128, H: int = 4,
+                       D: int = 32, dtype: torch.dtype = torch.bfloat16, seed: int = 9):
+    """Inputs of tied pair row attention (the pages give no workload; the
+    default sizes are a pair stack of a 256-residue crop: 128 pair channels,
+    4 heads of width 32, 128-wide bias features). features and
+    bias_features ~ N(0, 1); matrices ~ N(0, 1/sqrt(fan_in)); norm scales
+    ~ 1 + N(0, 0.1), shifts and b_out ~ N(0, 0.1). Returns (activations,
+    parameters) for the page's signature."""
+    g = torch.Generator().manual_seed(seed)
+    f32 = torch.float32
+
+    def randn(*shape, std=1.0, mean=0.0):
+        return torch.randn(shape, generator=g, dtype=f32) * std + mean
+
+    HD = H * D
+    acts = {"features": randn(B, L, L, C), "bias_features": randn(B, L, L, CB)}
+    p = {"norm_scale": randn(C, std=0.1, mean=1.0), "norm_bias": randn(C, std=0.1),
+         "bias_norm_scale": randn(CB, std=0.1, mean=1.0), "bias_norm_bias": randn(CB, std=0.1),
+         "w_q": randn(C, HD, std=C ** -0.5), "w_k": randn(C, HD, std=C ** -0.5),
+         "w_v": randn(C, HD, std=C ** -0.5), "w_bias": randn(CB, H, std=CB ** -0.5),
+         "w_gate": randn(C, HD, std=C ** -0.5), "w_out": randn(HD, C, std=HD ** -0.5),
+         "b_out": randn(C, std=0.1)}
+    acts = {k: v.to(dtype).contiguous() for k, v in acts.items()}
+    p = {k: v.to(dtype).contiguous() for k, v in p.items()}
+    return acts, p
