@@ -251,7 +251,7 @@ int atom_attn_window_table(int64_t B, int64_t A, int64_t K, int64_t block,
  * outputs are zero unless tokens i and j are both present. Float tensors
  * share `dtype` (arithmetic fp32; for bf16 the features are rounded to
  * bf16 once and the output is computed from those rounded values). Output
- * pointers 16-byte aligned. Supported: H in {32, 64} (and 128 for bf16),
+ * pointers and `weight` 16-byte aligned. Supported: H in {32, 64} (and 128 for bf16),
  * D in {64, 128, 256}, C <= 4096, B*N <= 2^24. Workspace: fp32 q|k rows,
  * atom_attn_single_to_pair_workspace_bytes() bytes. Errors: EINVAL,
  * EWORKSPACE, EUNSUPPORTED, ELAUNCH as for the block. */

@@ -81,33 +81,45 @@ __global__ __launch_bounds__(256) void k_s2p_tok(S2PArgs p) {
         xs[e] = (xs[e] - st[2 * r]) * st[2 * r + 1] * to_f(ns[c]) + to_f(nb[c]);
     }
     __syncthreads();
-    // projection: thread -> (column o, part of the C range); the kTT rows
-    // share each weight load; 8 weights of a column are loaded together
-    const T *w = reinterpret_cast<const T *>(p.weight);
-    const int P = 256 / H2;                          // parts (2H <= 256)
-    const int o = tid % H2, part = tid / H2;
+    // projection: thread -> (group of E consecutive output columns, one of
+    // P parts of the C range). One 16-byte weight load feeds kTT x E FMAs;
+    // eight loads are in flight at a time; the parts reduce through LDS.
+    constexpr int E = 16 / sizeof(T);
+    const int ng = H2 / E, P = 256 / ng;             // ng divides 256 (2H a power of 2)
+    const int og = tid % ng, part = tid / ng;
     const int clo = part * C / P, chi = (part + 1) * C / P;
-    float acc[kTT];
+    const T *w = reinterpret_cast<const T *>(p.weight) + og * E;
+    float acc[kTT][E];
 #pragma unroll
     for (int rr = 0; rr < kTT; ++rr)
-        acc[rr] = 0.0f;
-    if (part < P) {
-        for (int c = clo; c < chi; c += 8) {
-            float wv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                wv[u] = to_f(w[(int64_t)min(c + u, chi - 1) * H2 + o]);
+        for (int e = 0; e < E; ++e)
+            acc[rr][e] = 0.0f;
+    for (int c = clo; c < chi; c += 8) {
+        uint4 wv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (c + u < chi)
+        for (int u = 0; u < 8; ++u)
+            wv[u] = *reinterpret_cast<const uint4 *>(w + (int64_t)min(c + u, chi - 1) * H2);
 #pragma unroll
-                    for (int rr = 0; rr < kTT; ++rr)
-                        acc[rr] = fmaf(xs[rr * C + c + u], wv[u], acc[rr]);
+        for (int u = 0; u < 8; ++u) {
+            if (c + u < chi) {
+                float wf[E];
+                unpack16<T>(wv[u], wf);
+#pragma unroll
+                for (int rr = 0; rr < kTT; ++rr) {
+                    const float xv = xs[rr * C + c + u];
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        acc[rr][e] = fmaf(xv, wf[e], acc[rr][e]);
+                }
+            }
         }
-#pragma unroll
-        for (int rr = 0; rr < kTT; ++rr)
-            red[(part * kTT + rr) * H2 + o] = acc[rr];
     }
+#pragma unroll
+    for (int rr = 0; rr < kTT; ++rr)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            red[(part * kTT + rr) * H2 + og * E + e] = acc[rr][e];
     __syncthreads();
     const T *bias = reinterpret_cast<const T *>(p.bias);
     for (int idx = tid; idx < kTT * H2; idx += 256) {
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
 
 } // namespace
 
-size_t s2p_tok_lds(int C) { return (size_t)kTT * C * 4 + kTT * 2 * 4 + (size_t)256 * kTT * 4; }
+size_t s2p_tok_lds(int C) { return (size_t)kTT * C * 4 + kTT * 2 * 4 + (size_t)256 * 8 * kTT * 4; }
 size_t s2p_pair_lds(int H, int D) {
     return ((size_t)H + 32 * (size_t)(D + 4) + (size_t)(D / 32) * 32) * 4;
 }
@@ -394,7 +406,7 @@ int atom_attn_single_to_pair(const atom_attn_s2p_dims *dims, int dtype, double e
     if (!(eps > 0.0) || !(fe > 0.0f) || !std::isfinite(fe) || !x || !mask || !weight ||
         !bias || !norm_scale || !norm_bias || !out_weight || !out_bias ||
         (output_norm && (!output_scale || !output_bias)) || !pair_features || !output ||
-        !al16(pair_features) || !al16(output))
+        !al16(pair_features) || !al16(output) || !al16(weight))
         return ATOM_ATTN_EINVAL;
     size_t need = 0;
     atom_attn_single_to_pair_workspace_bytes(dims, dtype, &need);

@@ -14,7 +14,7 @@
 //
 // Kernels (all on the caller's stream, workspace laid out by tied_layout):
 //  k_pack (pack.hip)  w_q, w_k, w_v, w_gate, w_out into MFMA B-fragment order
-//  k_tied_bias        beta, one thread per (b, i, j), fp32
+//  k_tied_bias        beta, eight threads per (b, i, j), fp32
 //  k_tied_proj        one workgroup per 32 entries F[j0..j0+31][kcol] of a
 //                     grid column: affine LayerNorm (fp32) into an LDS
 //                     operand tile, then q|k and v|gate on MFMA (32x32
@@ -25,9 +25,11 @@
 //                     later products read operands contiguous along their
 //                     reduction index. Entries outside the L x L grid (the
 //                     grid is padded to Lp = L rounded up to 32) are zeros.
-//  k_tied_logits      one workgroup per (b, h, 32 rows i, 32 columns j):
-//                     S = Qh Kh^T over the Lp*D reduction (split over the 4
-//                     waves, summed in LDS), scaled by 1/sqrt(L*D)
+//  k_tied_logits      kKS workgroups per (b, h, 32 rows i, 32 columns j):
+//                     S = Qh Kh^T over the Lp*D reduction (split over the
+//                     kKS workgroups and their 4 waves; the waves' parts are
+//                     summed in LDS, each workgroup writes its partial tile),
+//                     scaled by 1/sqrt(L*D); the softmax adds the partials
 // bf16 storage keeps five roundings in a chain (LayerNorm output, q/k/v/g,
 // the weights, the gated U, the output), enough to reach the 2e-2 bound on
 // large grids; so the LayerNorm output and the gated U go into the matrix
@@ -54,6 +56,7 @@ constexpr int kTD = 32;  // head width
 
 __host__ __device__ inline size_t tal16(size_t x) { return (x + 15) & ~(size_t)15; }
 constexpr int kNA = 4;   // anchors per workgroup of k_tied_out
+constexpr int kKS = 4;   // workgroups sharing one logit tile's reduction
 
 struct TiedArgs {
     int B, L, Lp, C, Cb, H;
@@ -70,40 +73,53 @@ struct TiedArgs {
 };
 
 // ---------------------------------------------------------------- bias
+// 8 threads per (b, i, j) entry, each a strided eighth of the Cb channels;
+// the row statistics and the H head sums reduce over the 8 lanes.
 template <typename T>
 __global__ __launch_bounds__(256) void k_tied_bias(TiedArgs p) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+    const int sub = threadIdx.x & 7;
     const int64_t LL = (int64_t)p.L * p.L;
-    if (t >= (int64_t)p.B * LL)
-        return;
-    const int64_t b = t / LL;
-    const int i = (int)((t - b * LL) / p.L), j = (int)(t - b * LL - (int64_t)i * p.L);
+    const bool live = t < (int64_t)p.B * LL;          // uniform over the 8 lanes of an entry
+    const int64_t tc = live ? t : 0;
+    const int64_t b = tc / LL;
+    const int i = (int)((tc - b * LL) / p.L), j = (int)(tc - b * LL - (int64_t)i * p.L);
     // exchanged axes: the bias of (query i, key j) comes from Fb[j][i]
     const T *row = reinterpret_cast<const T *>(p.fb) + ((b * p.L + j) * p.L + i) * p.Cb;
     const T *sc = reinterpret_cast<const T *>(p.bns);
     const T *sh = reinterpret_cast<const T *>(p.bnb);
     const T *wb = reinterpret_cast<const T *>(p.w_bias);
+    const int Cb = p.Cb;
     float s = 0.0f;
-    for (int c = 0; c < p.Cb; ++c)
+    for (int c = sub; c < Cb; c += 8)
         s += to_f(row[c]);
-    const float mean = s / (float)p.Cb;
+    const float mean = sum8(s) / (float)Cb;
     float q = 0.0f;
-    for (int c = 0; c < p.Cb; ++c) {
+    for (int c = sub; c < Cb; c += 8) {
         const float d = to_f(row[c]) - mean;
         q += d * d;
     }
-    const float rstd = 1.0f / sqrtf(q / (float)p.Cb + p.eps);
+    const float rstd = 1.0f / sqrtf(sum8(q) / (float)Cb + p.eps);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < p.Cb; ++c) {
+    for (int c = sub; c < Cb; c += 8) {
         const float xn = (to_f(row[c]) - mean) * rstd * to_f(sc[c]) + to_f(sh[c]);
 #pragma unroll
         for (int h = 0; h < 8; ++h)
             if (h < p.H)
                 acc[h] = fmaf(xn, to_f(wb[c * p.H + h]), acc[h]);
     }
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+        acc[h] = sum8(acc[h]);
     const int64_t LpLp = (int64_t)p.Lp * p.Lp;
-    for (int h = 0; h < p.H; ++h)
-        p.beta[(b * p.H + h) * LpLp + (int64_t)i * p.Lp + j] = acc[h];
+    if (live && sub < p.H) {
+        float v = acc[0];
+#pragma unroll
+        for (int h = 1; h < 8; ++h)
+            if (sub == h)
+                v = acc[h];
+        p.beta[(b * p.H + sub) * LpLp + (int64_t)i * p.Lp + j] = v;
+    }
 }
 
 // ---------------------------------------------------------- projections
@@ -240,6 +256,7 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = Lp / 32;
     int64_t t = blockIdx.x;
+    const int ks = (int)(t % kKS); t /= kKS;
     const int jb = (int)(t % nb); t /= nb;
     const int ib = (int)(t % nb); t /= nb;
     const int h = (int)(t % H);
@@ -247,8 +264,9 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
     const int64_t K = (int64_t)Lp * kTD;
     const T *qa = reinterpret_cast<const T *>(p.qh) + ((b * H + h) * Lp + ib * 32 + (lane & 31)) * K;
     const T *kb = reinterpret_cast<const T *>(p.kh) + ((b * H + h) * Lp + jb * 32 + (lane & 31)) * K;
-    const int nkc = (int)(K / KC), per = nkc / 4;     // chunks per wave (Lp*D/KC is a multiple of 4)
-    const int c0 = wave * per;
+    // chunks per wave: Lp*D/KC is a multiple of 4*kKS (Lp a multiple of 32)
+    const int nkc = (int)(K / KC), per = nkc / (4 * kKS);
+    const int c0 = (ks * 4 + wave) * per;
     const int hoff = (lane >> 5) * HALF;
     f32x16_t acc = zero16();
     constexpr int U = 4;
@@ -292,7 +310,9 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
     for (int e = 0; e < 16; ++e)
         red[wave][acc32_row(e, lane)][lane & 31] = acc[e];
     __syncthreads();
-    float *srow = p.s + ((b * H + h) * (int64_t)Lp + ib * 32) * Lp + jb * 32;
+    // partial tile ks of the logits: S[ks][b][h][i][j]
+    float *srow = p.s + (int64_t)ks * p.B * H * Lp * Lp + ((b * H + h) * (int64_t)Lp + ib * 32) * Lp +
+                  jb * 32;
     for (int idx = tid; idx < 32 * 32; idx += 256) {
         const int rr = idx >> 5, cc = idx & 31;
         srow[(int64_t)rr * Lp + cc] =
@@ -317,13 +337,21 @@ __global__ __launch_bounds__(256) void k_tied_softmax(TiedArgs p) {
         return;
     }
     const float *srow = p.s + rowid * Lp;
+    const int64_t pstride = (int64_t)p.B * p.H * Lp * Lp;  // between partial logit tiles
     const float *brow = p.beta + rowid * Lp;
     float v[16];
     float m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int j = lane + 64 * u;
-        v[u] = j < L ? srow[j] + brow[j] : -INFINITY;
+        float x = -INFINITY;
+        if (j < L) {
+            x = brow[j];
+#pragma unroll
+            for (int k = 0; k < kKS; ++k)
+                x += srow[k * pstride + j];
+        }
+        v[u] = x;
         m = fmaxf(m, v[u]);
     }
     m = group_max<64>(m);
@@ -451,7 +479,7 @@ TiedLayout tied_layout(int64_t B, int64_t L, int64_t C, int64_t H, int esz) {
     Lo.g = o; o = up256t(o + big);
     Lo.amat = o; o = up256t(o + (size_t)(B * H * Lp * Lp) * esz);
     Lo.beta = o; o = up256t(o + (size_t)(B * H * Lp * Lp) * 4);
-    Lo.s = o; o = up256t(o + (size_t)(B * H * Lp * Lp) * 4);
+    Lo.s = o; o = up256t(o + (size_t)kKS * (B * H * Lp * Lp) * 4);
     Lo.total = o;
     return Lo;
 }
@@ -559,12 +587,12 @@ int atom_attn_tied_row_attention(const atom_attn_tied_dims *d, int dtype, double
     const int64_t nb32 = Lp / 32;
     const bool ok =
         go(KN_TIED_BIAS, dt ? (const void *)k_tied_bias<bf16_t> : (const void *)k_tied_bias<float>,
-           (a.B * (int64_t)a.L * a.L + 255) / 256, 0) &&
+           (a.B * (int64_t)a.L * a.L * 8 + 255) / 256, 0) &&
         go(KN_TIED_PROJ, dt ? (const void *)k_tied_proj<bf16_t> : (const void *)k_tied_proj<float>,
            a.B * Lp * nb32, tied_proj_lds(C, esz)) &&
         go(KN_TIED_LOGITS,
            dt ? (const void *)k_tied_logits<bf16_t> : (const void *)k_tied_logits<float>,
-           a.B * (int64_t)a.H * nb32 * nb32, 0) &&
+           a.B * (int64_t)a.H * nb32 * nb32 * kKS, 0) &&
         go(KN_TIED_SOFTMAX,
            dt ? (const void *)k_tied_softmax<bf16_t> : (const void *)k_tied_softmax<float>,
            (a.B * (int64_t)a.H * Lp + 3) / 4, 0) &&
