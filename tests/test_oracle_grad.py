@@ -1,0 +1,187 @@
+"""Pins of the fp64 gradient oracle (oracle/block_grad.py).
+
+The gradient oracle differentiates a torch restatement of the block. Both
+halves are pinned to something outside that file:
+  * its forward equals the C oracle (oracle.c, pinned by test_oracle_pins /
+    test_oracle_invariants) value by value;
+  * every gradient tensor, sampled entry by entry, equals the central finite
+    difference of the C oracle's forward, (L(x+h) - L(x-h)) / 2h, where L is
+    the scalar <outputs, upstream gradients>. That is the definition of the
+    derivative applied to an independent implementation, so a dropped term,
+    wrong sign or index anywhere in the chain fails here.
+The slot-attention step is pinned the same way against the C slot step, with
+key tables that repeat keys within a row and across rows ("windowed_atom_
+attention", Required behavior: repeated selection accumulates gradients).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import block_grad
+from windowed_atom_attention_amd.workloads import make_workload
+
+CASES = [("af3", "encoder", -1), ("af3", "decoder", 5),
+         ("esmfold2", "encoder", 6), ("esmfold2", "decoder", -1)]
+
+
+def _workload(style, stage, radius):
+    wl = make_workload("0", style=style, stage=stage, radius=radius, dtype=torch.float32,
+                       rope="distinct")
+    return wl
+
+
+def _upstream(wl, seed=11):
+    g = torch.Generator().manual_seed(seed)
+    d = wl.dims
+    B, A, T, C, H, K, U = (d[k] for k in "B A T C H K U".split())
+    up = {"hidden": torch.randn((B, A, C), generator=g, dtype=torch.float64),
+          "attention": torch.randn((B, H, A, K), generator=g, dtype=torch.float64)}
+    if wl.stage == "encoder":
+        up["token_output"] = torch.randn((B, T, U), generator=g, dtype=torch.float64)
+    else:
+        up["position_update"] = torch.randn((B, A, 3), generator=g, dtype=torch.float64)
+    return up
+
+
+def _c_loss(wl, acts, params, up):
+    res = oracle.block(acts, params, wl.masks, wl.structure, eps=wl.eps, style=wl.style,
+                       stage=wl.stage, radius=wl.radius, nthreads=1)
+    return sum(float((torch.from_numpy(res[k]) * v).sum()) for k, v in up.items())
+
+
+@pytest.mark.parametrize("style,stage,radius", CASES)
+def test_grad_oracle_forward_equals_c_oracle(style, stage, radius):
+    wl = _workload(style, stage, radius)
+    f64 = lambda d: {k: v.to(torch.float64) for k, v in d.items()}
+    out = block_grad.block_forward(f64(wl.activations), f64(wl.parameters), wl.masks,
+                                   wl.structure, eps=wl.eps, style=style, stage=stage,
+                                   radius=radius)
+    ref = oracle.block(wl.activations, wl.parameters, wl.masks, wl.structure, eps=wl.eps,
+                       style=style, stage=stage, radius=radius, nthreads=1)
+    for k, v in out.items():
+        r = torch.from_numpy(ref[k])
+        assert v.shape == r.shape, k
+        err = (v.detach() - r).abs().max().item()
+        assert err <= 1e-12 * (1.0 + r.abs().max().item()), (k, err)
+
+
+def _sample_entries(x, n, g):
+    flat = x.reshape(-1)
+    fin = torch.nonzero(torch.isfinite(flat)).reshape(-1)
+    pick = fin[torch.randperm(len(fin), generator=g)[:n]]
+    return pick.tolist()
+
+
+@pytest.mark.parametrize("style,stage,radius", CASES)
+def test_grad_oracle_matches_finite_differences(style, stage, radius):
+    wl = _workload(style, stage, radius)
+    up = _upstream(wl)
+    _, din, dpar = block_grad.block_backward(wl.activations, wl.parameters, wl.masks,
+                                             wl.structure, up, eps=wl.eps, style=style,
+                                             stage=stage, radius=radius)
+    acts = {k: v.to(torch.float64).clone() for k, v in wl.activations.items()}
+    params = {k: v.to(torch.float64).clone() for k, v in wl.parameters.items()}
+    g = torch.Generator().manual_seed(5)
+    checked = 0
+    for kind, grads, store in (("in", din, acts), ("par", dpar, params)):
+        for name, grad in grads.items():
+            base = store[name]
+            rms = grad.pow(2).mean().sqrt().item()
+            for idx in _sample_entries(base, 4, g):
+                flat = base.view(-1)
+                x = flat[idx].item()
+                h = 1e-6 * max(1.0, abs(x))
+                flat[idx] = x + h
+                lp = _c_loss(wl, acts, params, up)
+                flat[idx] = x - h
+                lm = _c_loss(wl, acts, params, up)
+                flat[idx] = x
+                fd = (lp - lm) / (2 * h)
+                ad = grad.reshape(-1)[idx].item()
+                assert abs(fd - ad) <= 1e-6 * (abs(ad) + rms) + 1e-8, (kind, name, idx, fd, ad)
+                checked += 1
+    assert checked >= 40
+
+
+def test_grad_oracle_unusable_payloads_get_zero_gradient():
+    wl = _workload("af3", "encoder", -1)
+    up = _upstream(wl)
+    _, din, dpar = block_grad.block_backward(wl.activations, wl.parameters, wl.masks,
+                                             wl.structure, up, eps=wl.eps, style="af3",
+                                             stage="encoder", radius=-1)
+    bad = ~wl.masks["valid"]
+    assert bad.any()
+    assert (din["atom"][bad] == 0).all() and (din["condition"][bad] == 0).all()
+    assert (din["pair"][bad] == 0).all()
+    for k, v in list(din.items()) + list(dpar.items()):
+        assert torch.isfinite(v).all(), k
+
+
+def _slot_case(style, seed=3):
+    g = torch.Generator().manual_seed(seed)
+    B, A, K, H, D, V = 2, 9, 6, 2, 4, 5
+    q = torch.randn((B, A, H * D), generator=g, dtype=torch.float64)
+    k = torch.randn((B, A, H * D), generator=g, dtype=torch.float64)
+    v = torch.randn((B, A, H * D), generator=g, dtype=torch.float64)
+    usable = torch.ones((B, A), dtype=torch.bool)
+    usable[0, 4] = False
+    # rows that repeat a key within the row and across rows, plus missing ids
+    ki = torch.randint(0, A, (B, A, K), generator=g)
+    ki[:, :, 0] = 2
+    ki[:, :, 1] = 2
+    ki[0, 3, 2] = -1
+    ki[1, 5, 3] = A
+    wm = torch.rand((B, A, K), generator=g) < 0.85
+    d_att = torch.randn((B, H, A, K), generator=g, dtype=torch.float64)
+    d_o = torch.randn((B, A, H * D), generator=g, dtype=torch.float64)
+    extra = {}
+    if style == "af3":
+        extra = dict(pair=torch.randn((B, A, K, V), generator=g, dtype=torch.float64),
+                     pair_scale=1 + 0.1 * torch.randn((V,), generator=g, dtype=torch.float64),
+                     w_pair=0.5 * torch.randn((V, H), generator=g, dtype=torch.float64))
+    return q, k, v, usable, ki, wm, d_att, d_o, extra, H
+
+
+@pytest.mark.parametrize("style", ["af3", "esmfold2"])
+def test_slot_grad_oracle_matches_finite_differences(style):
+    q, k, v, usable, ki, wm, d_att, d_o, extra, H = _slot_case(style)
+    radius = 5 if style == "esmfold2" else -1
+    res = block_grad.slot_backward(q, k, v, usable, ki, wm, d_att, d_o, style=style,
+                                   radius=radius, heads=H, **extra)
+    # forward equals the C slot step
+    ref = oracle.slot_attention(q, k, v, usable, ki, wm, style=style, radius=radius,
+                                heads=H, nthreads=1, **extra)
+    assert np.abs(res["attention"].numpy() - ref["attention"]).max() < 1e-13
+    assert np.abs(res["o"].numpy() - ref["o"]).max() < 1e-13
+
+    def loss(q_, k_, v_, ex):
+        r = oracle.slot_attention(q_, k_, v_, usable, ki, wm, style=style, radius=radius,
+                                  heads=H, nthreads=1, **ex)
+        return float((torch.from_numpy(r["o"]) * d_o).sum() +
+                     (torch.from_numpy(r["attention"]) * d_att).sum())
+
+    tensors = {"dq": q, "dk": k, "dv": v}
+    if style == "af3":
+        tensors.update(d_pair=extra["pair"], d_pair_scale=extra["pair_scale"],
+                       d_w_pair=extra["w_pair"])
+    for gname, base in tensors.items():
+        grad = res[gname]
+        for idx in range(base.numel()):
+            flat = base.view(-1)
+            x = flat[idx].item()
+            h = 1e-6
+            flat[idx] = x + h
+            lp = loss(q, k, v, extra)
+            flat[idx] = x - h
+            lm = loss(q, k, v, extra)
+            flat[idx] = x
+            fd = (lp - lm) / (2 * h)
+            ad = grad.reshape(-1)[idx].item()
+            assert abs(fd - ad) <= 1e-6 * (abs(ad) + 1.0), (gname, idx, fd, ad)
+    # key 2 of batch 0 is selected twice by every usable row: its gradient is
+    # the sum over all those selections (nonzero), while the unusable atom 4
+    # receives nothing as a key or as a query
+    assert res["dk"][0, 2].abs().sum() > 0
+    assert (res["dq"][0, 4] == 0).all() and (res["dk"][0, 4] == 0).all()
+    assert (res["dv"][0, 4] == 0).all()
