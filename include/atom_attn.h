@@ -201,6 +201,85 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
                              void *attention, void *o, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- backward
+ * Gradients of the block ("windowed_atom_attention", Required behavior: the
+ * block's steps, and the rule that a key atom selected by several slots --
+ * of one query or of many -- receives the sum of the gradients of all those
+ * selections; "AlphaFold 3 Atom Attention Encoder" / "ESMFold 2 Atom
+ * Attention Encoder", Starter code: outputs are graded on values, shapes and
+ * gradients). For upstream gradients g_hidden, g_attention, g_token_output
+ * (encoder) or g_position_update (decoder), the call writes the derivative
+ * of sum <output, g> with respect to every float input and parameter.
+ *
+ * All gradient buffers (upstream and written) are fp32, row-major, in the
+ * shapes of the tensors they belong to, whatever `dtype` the inputs use;
+ * every write overwrites (nothing is accumulated into caller buffers).
+ * Upstream: hidden [B,A,C] (NULL = zero), attention [B,H,A,K], token_output
+ * [B,T,U], position_update [B,A,3] (each NULL = zero). Written gradients:
+ * any pointer may be NULL (not computed). Entries of unusable atoms, of
+ * slots that are not allowed and of invalid tokens get exact zeros: their
+ * payloads never enter the arithmetic. rope_cos / rope_sin receive the sum
+ * over heads of Q's and K's rotary terms (ESMFold2).
+ *
+ * The call recomputes the forward in fp32 from the inputs (its own kernels;
+ * results may differ from the forward call's in the last bits), then runs
+ * the chain rule on the device. Sums over atoms (parameter gradients) and
+ * over selections of a key (key and value rows) are taken in a fixed order
+ * with no floating-point atomics, so repeated calls give identical bits --
+ * except that a key atom selected by more than 2048 slots sums them in the
+ * order the reverse index was filled.
+ *
+ * Supported set: K <= 512; H <= 8; D one of 8, 16, 32, 64; H*D <= 256;
+ * AF3: V <= 16 and H <= 4; C, S, M, U <= 4096; B*A < 2^30;
+ * B*A*K*max(H, V) < 2^31. Otherwise EUNSUPPORTED. Status codes as the block
+ * call; workspace (256-byte aligned) of atom_attn_backward_workspace_bytes()
+ * bytes. Asynchronous on `stream`. */
+typedef struct {
+    const float *hidden, *attention, *token_output, *position_update;
+} atom_attn_grad_outputs;
+typedef struct {
+    float *atom, *condition, *pair, *token, *rope_cos, *rope_sin;
+} atom_attn_input_grads;
+typedef struct {
+    float *cond_scale, *w_scale, *b_scale, *w_shift, *w_residual_gate,
+        *b_residual_gate;
+    float *w_mod;
+    float *w_q, *b_q, *w_k, *w_v, *pair_scale, *w_pair, *w_value_gate,
+        *w_attention_out;
+    float *w_ff_gate, *w_ff_up, *w_ff_out;
+    float *w_pool, *w_token, *readout_scale, *readout_bias, *w_readout;
+} atom_attn_param_grads;
+int atom_attn_backward_workspace_bytes(const atom_attn_dims *dims, int style,
+                                       int stage, int dtype, size_t *bytes);
+int atom_attn_backward(const atom_attn_dims *dims, int style, int stage,
+                       int dtype, const atom_attn_inputs *in,
+                       const atom_attn_params *par, double eps, int64_t radius,
+                       const atom_attn_grad_outputs *grad_out,
+                       atom_attn_input_grads *grad_in,
+                       atom_attn_param_grads *grad_par, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Gradients of the slot-attention step alone ("windowed_atom_attention",
+ * Required behavior: the slot-permission, radius, pair-bias, logit and
+ * repeated-selection bullets), in fp32: q, k, v [B,A,H*D] fp32 (16-byte
+ * aligned), usable [B,A], key_index / window_mask [B,A,K]; AF3 pair
+ * [B,A,K,V], pair_scale [V], w_pair [V,H] in `dtype`. Upstream d_o
+ * [B,A,H*D] and d_attention [B,H,A,K] (NULL = zero), fp32. Writes dq, dk,
+ * dv [B,A,H*D] and, AF3, d_pair [B,A,K,V], d_pair_scale [V], d_w_pair [V,H]
+ * (each NULL = not computed); attention [B,H,A,K] and o [B,A,H*D] receive
+ * the recomputed fp32 forward when not NULL. Supported set and ordering of
+ * sums as atom_attn_backward (dims T, C, S, M, U are not read). */
+int atom_attn_slot_backward_workspace_bytes(const atom_attn_dims *dims,
+                                            int style, size_t *bytes);
+int atom_attn_slot_attention_backward(
+    const atom_attn_dims *dims, int style, int dtype, double eps,
+    int64_t radius, const uint8_t *usable, const float *q, const float *k,
+    const float *v, const int64_t *key_index, const uint8_t *window_mask,
+    const void *pair, const void *pair_scale, const void *w_pair,
+    const float *d_attention, const float *d_o, float *attention, float *o,
+    float *dq, float *dk, float *dv, float *d_pair, float *d_pair_scale,
+    float *d_w_pair, void *workspace, size_t workspace_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the block
  * call of atom_attn_encoder (stage ATOM_ATTN_ENCODER) or atom_attn_decoder

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.EXPORTS)
-    assert lib.atom_attn_version() == 5
+    assert lib.atom_attn_version() == 6
 
 
 def test_pair_bias_split_query():
@@ -201,3 +201,90 @@ def test_python_binding_argument_checks():
     bad.structure["key_index"] = bad.structure["key_index"][..., :5]
     with pytest.raises(ValueError):
         windowed_atom_attention(**bad.kwargs())
+
+
+def _bws(d, style=N.AF3, stage=N.ENCODER, dtype=N.F32):
+    nd = N.Dims(**d)
+    out = ctypes.c_size_t(0)
+    rc = N.lib().atom_attn_backward_workspace_bytes(ctypes.byref(nd), style, stage, dtype,
+                                                    ctypes.byref(out))
+    return rc, out.value
+
+
+def test_backward_workspace_query_status_codes():
+    rc, n = _bws(_dims())
+    assert rc == N.OK and n > 0
+    assert _bws(_dims(A=0))[0] == N.EINVAL
+    assert _bws(_dims(), style=5)[0] == N.EINVAL
+    assert _bws(_dims(), stage=2)[0] == N.EINVAL
+    assert _bws(_dims(), dtype=9)[0] == N.EINVAL
+    assert _bws(_dims(H=4, D=7), style=N.ESMFOLD2)[0] == N.EODD_HEAD
+    assert _bws(_dims(D=128, H=2))[0] == N.EUNSUPPORTED     # head width outside 8..64
+    assert _bws(_dims(D=12))[0] == N.EUNSUPPORTED
+    assert _bws(_dims(K=513))[0] == N.EUNSUPPORTED
+    assert _bws(_dims(H=5, D=16))[0] == N.EUNSUPPORTED      # AF3 pair gradients: H <= 4
+    assert _bws(_dims(H=5, D=16), style=N.ESMFOLD2)[0] == N.OK
+    assert _bws(_dims(V=17))[0] == N.EUNSUPPORTED
+    assert _bws(_dims(V=17), style=N.ESMFOLD2)[0] == N.OK   # no pair there
+    # dense widths need not be multiples of 32 here
+    assert _bws(_dims(C=48, S=40, M=72, U=20))[0] == N.OK
+    # decoder keeps the token projection and its reverse index
+    assert _bws(_dims(), stage=N.DECODER)[1] > 0
+    for name in ("1", "3", "4a", "4b"):
+        w = make_workload(name, A=64)
+        st = N.AF3 if w.style == "af3" else N.ESMFOLD2
+        sg = N.ENCODER if w.stage == "encoder" else N.DECODER
+        assert _bws(w.dims, st, sg, N.BF16)[0] == N.OK
+
+
+def test_backward_rejects_bad_arguments_before_any_launch():
+    lib = N.lib()
+    fake = 4096  # never dereferenced: every case fails its checks first
+    nd = N.Dims(**_dims())
+    ins = N.Inputs()
+    par = N.Params()
+    gout = N.GradOutputs()
+    # missing inputs / parameters
+    rc = lib.atom_attn_backward(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32, ctypes.byref(ins),
+                                ctypes.byref(par), 1e-5, -1, ctypes.byref(gout), None, None,
+                                fake, 1 << 40, None)
+    assert rc == N.EINVAL
+    for name in N.Inputs._fields_:
+        setattr(ins, name[0], fake)
+    for name in N.Params._fields_:
+        if name[0] != "packed":
+            setattr(par, name[0], fake)
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        rc = lib.atom_attn_backward(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32,
+                                    ctypes.byref(ins), ctypes.byref(par), eps, -1,
+                                    ctypes.byref(gout), None, None, fake, 1 << 40, None)
+        assert rc == N.EINVAL, eps
+    rc = lib.atom_attn_backward(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32, ctypes.byref(ins),
+                                ctypes.byref(par), 1e-5, -2, ctypes.byref(gout), None, None,
+                                fake, 1 << 40, None)
+    assert rc == N.EINVAL
+    # workspace missing, misaligned or short
+    for ws, nbytes in ((None, 1 << 40), (fake + 16, 1 << 40), (fake, 16)):
+        rc = lib.atom_attn_backward(ctypes.byref(nd), N.AF3, N.ENCODER, N.F32,
+                                    ctypes.byref(ins), ctypes.byref(par), 1e-5, -1,
+                                    ctypes.byref(gout), None, None, ws, nbytes, None)
+        assert rc == N.EWORKSPACE, (ws, nbytes)
+    # the slot step: NULL gradient buffers, unsupported head width
+    out = ctypes.c_size_t(0)
+    assert lib.atom_attn_slot_backward_workspace_bytes(ctypes.byref(nd), N.AF3,
+                                                       ctypes.byref(out)) == N.OK
+    # usable, q, k, v, key_index, window_mask; pair, pair_scale, w_pair;
+    # d_attention, d_o; attention, o; dq (NULL), dk, dv; d_pair, d_pair_scale,
+    # d_w_pair; workspace, bytes, stream
+    args = [fake] * 6 + [None, None, None, fake, fake, None, None, None, fake, fake, None,
+                         None, None, fake, 1 << 40, None]
+    rc = lib.atom_attn_slot_attention_backward(ctypes.byref(nd), N.ESMFOLD2, N.F32, 1e-5, -1,
+                                               *args)
+    assert rc == N.EINVAL
+    rc = lib.atom_attn_slot_attention_backward(ctypes.byref(nd), N.AF3, N.F32, 1e-5, -1,
+                                               *args)
+    assert rc == N.EINVAL                                    # AF3 needs the pair inputs
+    bad = N.Dims(**_dims(D=128))
+    rc = lib.atom_attn_slot_attention_backward(ctypes.byref(bad), N.ESMFOLD2, N.F32, 1e-5, -1,
+                                               *args)
+    assert rc == N.EUNSUPPORTED

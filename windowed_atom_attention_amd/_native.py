@@ -52,6 +52,21 @@ class Outputs(ctypes.Structure):
                 ("position_update", _vp), ("status", _vp)]
 
 
+class GradOutputs(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("hidden", "attention", "token_output", "position_update")]
+
+
+INPUT_GRAD_NAMES = ("atom", "condition", "pair", "token", "rope_cos", "rope_sin")
+
+
+class InputGrads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in INPUT_GRAD_NAMES]
+
+
+class ParamGrads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in PARAM_NAMES if n != "packed"]
+
+
 EXPORTS = ("atom_attn_workspace_bytes", "atom_attn_encoder",
            "atom_attn_decoder", "atom_attn_masks", "atom_attn_slot_attention",
            "atom_attn_slot_workspace_bytes", "atom_attn_pair_bias_split",
@@ -60,7 +75,9 @@ EXPORTS = ("atom_attn_workspace_bytes", "atom_attn_encoder",
            "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes",
            "atom_attn_packed_bytes", "atom_attn_pack_params", "atom_attn_window_table",
            "atom_attn_single_to_pair_workspace_bytes", "atom_attn_single_to_pair",
-           "atom_attn_tied_row_attention_workspace_bytes", "atom_attn_tied_row_attention")
+           "atom_attn_tied_row_attention_workspace_bytes", "atom_attn_tied_row_attention",
+           "atom_attn_backward_workspace_bytes", "atom_attn_backward",
+           "atom_attn_slot_backward_workspace_bytes", "atom_attn_slot_attention_backward")
 
 _lock = threading.Lock()
 _lib = None
@@ -106,6 +123,13 @@ def lib():
                                                _vp, _vp, _vp, _vp, _vp, szt, _vp]
         L.atom_attn_slot_workspace_bytes.argtypes = [P(Dims), i32, P(szt)]
         L.atom_attn_pair_bias_split.argtypes = [P(Dims), i32, i32, i32, P(i32)]
+        L.atom_attn_backward_workspace_bytes.argtypes = [P(Dims), i32, i32, i32, P(szt)]
+        L.atom_attn_backward.argtypes = [P(Dims), i32, i32, i32, P(Inputs), P(Params), dbl, i64,
+                                         P(GradOutputs), P(InputGrads), P(ParamGrads), _vp,
+                                         szt, _vp]
+        L.atom_attn_slot_backward_workspace_bytes.argtypes = [P(Dims), i32, P(szt)]
+        L.atom_attn_slot_attention_backward.argtypes = [P(Dims), i32, i32, dbl, i64] + \
+            [_vp] * 20 + [szt, _vp]
         L.atom_attn_error_string.argtypes = [i32]
         L.atom_attn_error_string.restype = ctypes.c_char_p
         L.atom_attn_version.argtypes = []
@@ -120,11 +144,10 @@ def lib():
                      "atom_attn_single_to_pair_workspace_bytes", "atom_attn_single_to_pair",
                      "atom_attn_tied_row_attention_workspace_bytes",
                      "atom_attn_tied_row_attention",
-                     "atom_attn_profile_enable", "atom_attn_profile_read",
-           "atom_attn_block_noalloc", "atom_attn_noalloc_max_bytes",
-           "atom_attn_packed_bytes", "atom_attn_pack_params", "atom_attn_window_table",
-           "atom_attn_single_to_pair_workspace_bytes", "atom_attn_single_to_pair",
-           "atom_attn_tied_row_attention_workspace_bytes", "atom_attn_tied_row_attention"):
+                     "atom_attn_backward_workspace_bytes", "atom_attn_backward",
+                     "atom_attn_slot_backward_workspace_bytes",
+                     "atom_attn_slot_attention_backward",
+                     "atom_attn_profile_enable", "atom_attn_profile_read"):
             getattr(L, name).restype = i32
         _lib = L
         return L

@@ -322,26 +322,9 @@ def pair_bias_split(dims: Dict[str, int], style: str, stage: str, dtype: torch.d
     return bool(out.value)
 
 
-def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
-                            structure: dict, eps: float = 1e-05,
-                            style: str = "af3", stage: str = "decoder",
-                            radius: int = -1, *, workspace: Optional[torch.Tensor] = None,
-                            status: Optional[torch.Tensor] = None,
-                            out: Optional[Dict[str, torch.Tensor]] = None,
-                            noalloc: bool = False,
-                            packed: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
-    """One windowed atom-attention block on the GPU.
-
-    Returns {"hidden" [B,A,C], "attention" [B,H,A,K]} plus "token_output"
-    [B,T,U] (encoder) or "position_update" [B,A,3] (decoder), in the input
-    float dtype (float32 or bfloat16). `workspace` (uint8, at least
-    workspace_bytes(...) bytes), `status` (int32 [1]) and preallocated
-    `out` tensors are optional; the call is asynchronous on the current
-    stream. With `noalloc=True` the call goes to atom_attn_block_noalloc,
-    whose scratch is the library's static per-device buffer (no workspace;
-    with `out` given and contiguous inputs nothing is allocated). `packed`
-    is the result of pack_params(...) for these parameters: the call then
-    skips packing the weight matrices."""
+def _marshal(activations, parameters, masks, structure, style, stage, radius):
+    """Checked, contiguous device copies/views of the block's inputs and
+    their C structs: (dims, dtype, device, Inputs, Params, keep-alive list)."""
     if style not in _STYLES:
         raise ValueError("style must be 'af3' or 'esmfold2', got %r" % (style,))
     if stage not in _STAGES:
@@ -403,6 +386,31 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
         atom_to_token=_dev_ptr(ix(structure["atom_to_token"])),
         key_index=_dev_ptr(ix(structure["key_index"])))
     npar = N.Params(**{k: _dev_ptr(v) for k, v in pars.items()})
+    return d, dtype, dev, nin, npar, keep
+
+
+def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
+                            structure: dict, eps: float = 1e-05,
+                            style: str = "af3", stage: str = "decoder",
+                            radius: int = -1, *, workspace: Optional[torch.Tensor] = None,
+                            status: Optional[torch.Tensor] = None,
+                            out: Optional[Dict[str, torch.Tensor]] = None,
+                            noalloc: bool = False,
+                            packed: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """One windowed atom-attention block on the GPU.
+
+    Returns {"hidden" [B,A,C], "attention" [B,H,A,K]} plus "token_output"
+    [B,T,U] (encoder) or "position_update" [B,A,3] (decoder), in the input
+    float dtype (float32 or bfloat16). `workspace` (uint8, at least
+    workspace_bytes(...) bytes), `status` (int32 [1]) and preallocated
+    `out` tensors are optional; the call is asynchronous on the current
+    stream. With `noalloc=True` the call goes to atom_attn_block_noalloc,
+    whose scratch is the library's static per-device buffer (no workspace;
+    with `out` given and contiguous inputs nothing is allocated). `packed`
+    is the result of pack_params(...) for these parameters: the call then
+    skips packing the weight matrices."""
+    d, dtype, dev, nin, npar, keep = _marshal(activations, parameters, masks, structure, style,
+                                              stage, radius)
     if packed is not None:
         need_p = packed_bytes(d, style, stage, dtype)
         if (packed.dtype != torch.uint8 or packed.device != dev or not packed.is_contiguous()
@@ -466,6 +474,138 @@ def windowed_atom_attention(activations: dict, parameters: dict, masks: dict,
     del keep
     names_out = ["hidden", "attention", "token_output" if stage == "encoder" else "position_update"]
     return {k: res[k] for k in names_out}
+
+
+def backward_workspace_bytes(dims: Dict[str, int], style: str, stage: str,
+                             dtype: torch.dtype) -> int:
+    """Bytes of device workspace one block_backward call needs."""
+    nd = N.Dims(**{k: int(v) for k, v in dims.items()})
+    need = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_backward_workspace_bytes(
+        ctypes.byref(nd), _STYLES[style], _STAGES[stage], _FLOAT_DTYPES[dtype],
+        ctypes.byref(need)), "atom_attn_backward_workspace_bytes")
+    return int(need.value)
+
+
+def block_backward(activations: dict, parameters: dict, masks: dict, structure: dict,
+                   grad_outputs: dict, eps: float = 1e-05, style: str = "af3",
+                   stage: str = "decoder", radius: int = -1, *,
+                   workspace: Optional[torch.Tensor] = None, inputs: Optional[tuple] = None,
+                   params: Optional[tuple] = None):
+    """Gradients of the block on the GPU (atom_attn_backward).
+
+    grad_outputs: upstream gradients by output name ("hidden", "attention",
+    "token_output" / "position_update"; a missing one is zero), any float
+    dtype (passed as fp32). Returns (input_grads, param_grads): dicts of
+    fp32 tensors for every float input of the style/stage and every
+    parameter it reads, or only those named in `inputs` / `params`.
+    Asynchronous on the current stream."""
+    d, dtype, dev, nin, npar, keep = _marshal(activations, parameters, masks, structure,
+                                              style, stage, radius)
+    B, A, T, K, C, H, D, U, V = (d[k] for k in "B A T K C H D U V".split())
+    up_shapes = {"hidden": (B, A, C), "attention": (B, H, A, K)}
+    if stage == "encoder":
+        up_shapes["token_output"] = (B, T, U)
+    else:
+        up_shapes["position_update"] = (B, A, 3)
+    gout = N.GradOutputs()
+    for name, g in grad_outputs.items():
+        if name not in up_shapes:
+            raise ValueError("no output %r for stage %r" % (name, stage))
+        if g is None:
+            continue
+        if tuple(g.shape) != up_shapes[name] or g.device != dev:
+            raise ValueError("grad_outputs[%r] must have shape %s on %s"
+                             % (name, up_shapes[name], dev))
+        g = _prep(g.float())
+        keep.append(g)
+        setattr(gout, name, g.data_ptr())
+
+    in_names = list(_ACT_BY_STYLE[style]) + (["token"] if stage == "decoder" else [])
+    par_names = [k for k in N.PARAM_NAMES if k != "packed" and getattr(npar, k)]
+    if inputs is not None:
+        in_names = [k for k in in_names if k in inputs]
+    if params is not None:
+        par_names = [k for k in par_names if k in params]
+    din = {k: torch.empty(activations[k].shape, dtype=torch.float32, device=dev)
+           for k in in_names}
+    dpar = {k: torch.empty(parameters[k].shape, dtype=torch.float32, device=dev)
+            for k in par_names}
+    gin = N.InputGrads(**{k: v.data_ptr() for k, v in din.items()})
+    gpar = N.ParamGrads(**{k: v.data_ptr() for k, v in dpar.items()})
+    need = backward_workspace_bytes(d, style, stage, dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif (workspace.numel() * workspace.element_size() < need or workspace.device != dev
+          or workspace.data_ptr() % 256 != 0):
+        raise ValueError("workspace needs %d bytes (256-byte aligned) on %s" % (need, dev))
+    nd = N.Dims(**{k: int(v) for k, v in d.items()})
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_backward(
+            ctypes.byref(nd), _STYLES[style], _STAGES[stage], _FLOAT_DTYPES[dtype],
+            ctypes.byref(nin), ctypes.byref(npar), float(eps), int(radius),
+            ctypes.byref(gout), ctypes.byref(gin), ctypes.byref(gpar), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    N.check(rc, "atom_attn_backward")
+    del keep
+    return din, dpar
+
+
+def slot_attention_backward(q, k, v, usable, key_index, window_mask, d_o, heads: int,
+                            d_attention=None, eps: float = 1e-5, style: str = "af3",
+                            radius: int = -1, pair=None, pair_scale=None, w_pair=None):
+    """Gradients of the slot-attention step alone (fp32 q, k, v [B,A,H*D];
+    AF3 pair [B,A,K,V] with pair_scale [V] and w_pair [V,H] in one float
+    dtype). Returns a dict with dq, dk, dv (and d_pair, d_pair_scale,
+    d_w_pair for AF3) plus the recomputed attention [B,H,A,K] and o, all
+    fp32."""
+    q, k, v = (_prep(x.float()) for x in (q, k, v))
+    B, A, HD = q.shape
+    K = key_index.shape[-1]
+    H = int(heads)
+    D = HD // H
+    dev = q.device
+    us = _prep(usable.to(torch.uint8))
+    ki = _prep(key_index, torch.int64)
+    wm = _mask(window_mask)
+    g_o = _prep(d_o.float())
+    g_a = _prep(d_attention.float()) if d_attention is not None else None
+    keep = [q, k, v, us, ki, wm, g_o, g_a]
+    V, dtype = 1, torch.float32
+    ptrs = [None, None, None]
+    if style == "af3":
+        dtype = pair.dtype
+        pair, pair_scale, w_pair = (_prep(x, dtype) for x in (pair, pair_scale, w_pair))
+        keep += [pair, pair_scale, w_pair]
+        V = pair.shape[-1]
+        ptrs = [pair.data_ptr(), pair_scale.data_ptr(), w_pair.data_ptr()]
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"attention": torch.empty((B, H, A, K), **f32), "o": torch.empty((B, A, HD), **f32),
+           "dq": torch.empty((B, A, HD), **f32), "dk": torch.empty((B, A, HD), **f32),
+           "dv": torch.empty((B, A, HD), **f32)}
+    if style == "af3":
+        res.update(d_pair=torch.empty((B, A, K, V), **f32),
+                   d_pair_scale=torch.empty((V,), **f32), d_w_pair=torch.empty((V, H), **f32))
+    nd = N.Dims(B=B, A=A, T=1, K=K, C=1, S=1, H=H, D=D, V=V, M=1, U=1)
+    need = ctypes.c_size_t(0)
+    N.check(N.lib().atom_attn_slot_backward_workspace_bytes(ctypes.byref(nd), _STYLES[style],
+                                                            ctypes.byref(need)),
+            "atom_attn_slot_backward_workspace_bytes")
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    p = lambda name: res[name].data_ptr() if name in res else None
+    with torch.cuda.device(dev):
+        rc = N.lib().atom_attn_slot_attention_backward(
+            ctypes.byref(nd), _STYLES[style], _FLOAT_DTYPES[dtype], float(eps), int(radius),
+            us.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), ki.data_ptr(),
+            wm.data_ptr(), ptrs[0], ptrs[1], ptrs[2],
+            g_a.data_ptr() if g_a is not None else None, g_o.data_ptr(),
+            p("attention"), p("o"), p("dq"), p("dk"), p("dv"), p("d_pair"),
+            p("d_pair_scale"), p("d_w_pair"), ws.data_ptr(), int(need.value),
+            _stream_handle(dev))
+    N.check(rc, "atom_attn_slot_attention_backward")
+    torch.cuda.current_stream(dev).synchronize()
+    del keep
+    return res
 
 
 def masks(masks: dict, structure: dict, T: int, radius: int = -1):

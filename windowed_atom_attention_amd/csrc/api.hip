@@ -16,7 +16,7 @@ using namespace waa;
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 // ------------------------------------------------------------ profiler
 
@@ -28,11 +28,12 @@ struct Profiler {
     bool on = false;
     std::vector<ProfRec> recs;
     std::vector<hipEvent_t> pool;
-    const char *names[16] = {"pack", "token_proj", "prep", "slot_attention",
+    const char *names[32] = {"pack", "token_proj", "prep", "slot_attention",
                              "post", "pool", "masks", "s2p_token", "s2p_pair",
                              "window", "tied_bias", "tied_proj", "tied_logits",
-                             "tied_softmax", "tied_out"};
-    int nnames = 15;
+                             "tied_softmax", "tied_out", "bwd_recompute", "bwd_slot_fwd",
+                             "bwd_slot_q", "bwd_slot_kv", "bwd_chain"};
+    int nnames = 20;
 };
 Profiler g_prof;
 
@@ -716,8 +717,8 @@ int atom_attn_profile_enable(int on) {
 
 int atom_attn_profile_read(const char **names, double *total_ms, int64_t *launches,
                            int max) {
-    double tot[16] = {0};
-    int64_t cnt[16] = {0};
+    double tot[32] = {0};
+    int64_t cnt[32] = {0};
     for (auto &r : g_prof.recs) {
         if (hipEventSynchronize(r.stop) != hipSuccess)
             return ATOM_ATTN_ELAUNCH;

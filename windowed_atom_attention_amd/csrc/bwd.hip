@@ -1,0 +1,675 @@
+// bwd.hip -- the C ABI of the backward pass (declared in include/atom_attn.h):
+// atom_attn_backward, the gradients of every float input and parameter of
+// the block, and atom_attn_slot_attention_backward, the slot step alone.
+// Host code only: the forward intermediates the chain rule needs are
+// recomputed in fp32 from the inputs, then the chain rule runs from the
+// outputs back to the inputs, every step in the kernels of bwd_dense.hip
+// and bwd_slot.hip.
+//
+// Pages: "windowed_atom_attention" (Required behavior: the block, and the
+// repeated-selection rule for gradients), "AlphaFold 3 Atom Attention
+// Encoder" and "ESMFold 2 Atom Attention Encoder" (Required behavior; their
+// Starter code grades gradients).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/atom_attn.h"
+#include "bwd.hpp"
+#include "kernels.hpp"
+
+using namespace waa;
+using namespace waa::bwd;
+
+namespace {
+
+struct Arena {
+    char *base;
+    size_t off = 0;
+    template <typename T> T *get(size_t n) {
+        off = (off + 255) & ~(size_t)255;
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += std::max<size_t>(n, 1) * sizeof(T);
+        return p;
+    }
+};
+
+bool eps_ok(double eps) {
+    return eps > 0.0 && std::isfinite(eps) && (float)eps > 0.0f && std::isfinite((float)eps);
+}
+
+// Shapes the backward kernels handle (the dense kernels take any sizes).
+int bwd_shape_ok(const atom_attn_dims *d, int style) {
+    if (!slot_bwd_supported((int)d->K, (int)d->H, (int)d->D, (int)d->V,
+                            style == ATOM_ATTN_AF3 ? STYLE_AF3 : STYLE_ESM))
+        return ATOM_ATTN_EUNSUPPORTED;
+    const int64_t N = d->B * d->A;
+    if (N >= ((int64_t)1 << 30) || N * d->K * std::max<int64_t>(d->H, d->V) >= ((int64_t)1 << 31) ||
+        d->B * d->T >= ((int64_t)1 << 30))
+        return ATOM_ATTN_EUNSUPPORTED;
+    const int64_t widths[] = {d->C, d->S, d->M, d->U};
+    for (int64_t x : widths)
+        if (x > 4096)
+            return ATOM_ATTN_EUNSUPPORTED;
+    return ATOM_ATTN_OK;
+}
+
+// Every buffer of one backward call, carved from the workspace.
+struct Bufs {
+    // fp32 parameters
+    float *cs, *ws, *bs, *wsh, *wrg, *brg, *wmod, *wq, *bq, *wk, *wv, *ps, *wp, *wvg, *wao;
+    float *ffg, *ffu, *ffo, *wpool, *wtok, *rs, *rb, *wro;
+    // masks
+    uint8_t *usable, *allowed;
+    int32_t *tcount;
+    // recomputed forward
+    float *tok, *tokproj, *x0, *c, *ch, *rc, *cj, *sig[3], *mu[3], *gr[2], *mods, *sc;
+    float *xh0, *r0, *qin, *kvin, *qraw, *kraw, *rcos, *rsin, *q, *k, *v, *g, *P, *o;
+    int32_t *kid;
+    float *og, *uu, *x1, *xh1, *r1, *z, *fa, *fb, *hh, *tr, *hid, *proj, *xhh, *rh, *lnh;
+    // backward
+    float *dh, *dx2, *dtr, *dgT, *dhh, *da, *dbb, *dz, *dx1, *gt, *du, *dgA, *dog, *dO, *dGp;
+    float *dS, *dq, *dk, *dv, *dqin, *dkvin, *dx0, *dzs[3], *dzg[2], *dcj, *dch, *dc, *dmods,
+        *ds, *dpu, *dln, *dtp, *dP, *pwp, *part;
+    int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list;
+};
+
+void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
+    std::memset(&b, 0, sizeof(b));
+    const size_t B = d->B, A = d->A, T = d->T, K = d->K, C = d->C, S = d->S, H = d->H,
+                 D = d->D, V = d->V, M = d->M, U = d->U;
+    const size_t N = B * A, E = N * K, HD = H * D, BT = B * T;
+    const bool af3 = style == ATOM_ATTN_AF3, dec = stage == ATOM_ATTN_DECODER;
+    auto f = [&](size_t n) { return ar.get<float>(n); };
+    if (af3) {
+        b.cs = f(3 * S); b.ws = f(3 * S * C); b.bs = f(3 * C); b.wsh = f(3 * S * C);
+        b.wrg = f(2 * S * C); b.brg = f(2 * C); b.bq = f(HD); b.ps = f(V); b.wp = f(V * H);
+    } else {
+        b.wmod = f(S * 6 * C);
+    }
+    b.wq = f(C * HD); b.wk = f(C * HD); b.wv = f(C * HD); b.wvg = f(C * HD); b.wao = f(HD * C);
+    b.ffg = f(C * M); b.ffu = f(C * M); b.ffo = f(M * C);
+    if (dec) {
+        b.wtok = f(U * C); b.rs = f(C); b.rb = f(C); b.wro = f(C * 3);
+    } else {
+        b.wpool = f(C * U);
+    }
+    b.usable = ar.get<uint8_t>(N);
+    b.allowed = ar.get<uint8_t>(E);
+    b.tcount = ar.get<int32_t>(BT);
+    if (dec) {
+        b.tok = f(BT * U); b.tokproj = f(BT * C);
+    }
+    b.x0 = f(N * C); b.c = f(N * S); b.xh0 = f(N * C); b.r0 = f(N); b.qin = f(N * C);
+    if (af3) {
+        b.ch = f(N * S); b.rc = f(N); b.cj = f(N * S);
+        for (int j = 0; j < 3; ++j) { b.sig[j] = f(N * C); b.mu[j] = f(N * C); }
+        for (int j = 0; j < 2; ++j) b.gr[j] = f(N * C);
+        b.kvin = f(N * C);
+    } else {
+        b.mods = f(N * 6 * C); b.sc = f(N * S); b.kvin = b.qin;
+        b.qraw = f(N * HD); b.kraw = f(N * HD); b.rcos = f(N * D); b.rsin = f(N * D);
+    }
+    b.q = f(N * HD); b.k = f(N * HD); b.v = f(N * HD); b.g = f(N * HD);
+    b.P = f(E * H); b.o = f(N * HD); b.kid = ar.get<int32_t>(E);
+    b.og = f(N * HD); b.uu = f(N * C); b.x1 = f(N * C); b.xh1 = f(N * C); b.r1 = f(N);
+    b.z = f(N * C); b.fa = f(N * M); b.fb = f(N * M); b.hh = f(N * M); b.tr = f(N * C);
+    b.hid = f(N * C);
+    if (dec) {
+        b.xhh = f(N * C); b.rh = f(N); b.lnh = f(N * C);
+    } else {
+        b.proj = f(N * U);
+    }
+    b.dh = f(N * C); b.dx2 = f(N * C); b.dtr = f(N * C); b.dgT = f(N * C);
+    b.dhh = f(N * M); b.da = f(N * M); b.dbb = f(N * M); b.dz = f(N * C); b.dx1 = f(N * C);
+    b.gt = f(N * C); b.du = f(N * C); b.dgA = f(N * C); b.dog = f(N * HD); b.dO = f(N * HD);
+    b.dGp = f(N * HD); b.dS = f(E * H); b.dq = f(N * HD); b.dk = f(N * HD); b.dv = f(N * HD);
+    b.dqin = f(N * C); b.dkvin = f(N * C); b.dx0 = f(N * C); b.dc = f(N * S);
+    if (af3) {
+        for (int j = 0; j < 3; ++j) b.dzs[j] = f(N * C);
+        for (int j = 0; j < 2; ++j) b.dzg[j] = f(N * C);
+        b.dcj = f(N * S); b.dch = f(N * S);
+    } else {
+        b.dmods = f(N * 6 * C); b.ds = f(N * S);
+    }
+    if (dec) {
+        b.dpu = f(N * 3); b.dln = f(N * C); b.dtp = f(BT * C);
+        b.tkey = ar.get<int32_t>(N); b.tcnt = ar.get<int32_t>(BT);
+        b.toff = ar.get<int32_t>(BT + 1); b.tlist = ar.get<int32_t>(N);
+    } else {
+        b.dP = f(N * U);
+    }
+    b.cnt = ar.get<int32_t>(N); b.off = ar.get<int32_t>(N + 1); b.list = ar.get<int32_t>(E);
+    b.pwp = f(slot_bwd_partial_floats((int64_t)N, (int)V, (int)H));
+    b.part = f(kGemmPartialFloats);
+}
+
+// Sequenced launches that stop at the first failure.
+struct Run {
+    hipStream_t s;
+    float *part;
+    hipError_t err = hipSuccess;
+    void ok(hipError_t e) {
+        if (err == hipSuccess && e != hipSuccess)
+            err = e;
+    }
+    // C (+)= A @ B, A [M,K], B [K,N]
+    void mm(int M, int N, int K, Mat A, Mat B, float *C, int64_t ldc, float beta = 0.0f,
+            const float *bias = nullptr) {
+        if (err == hipSuccess)
+            ok(gemm(M, N, K, A, B, View{C, ldc}, beta, bias, part, kGemmPartialFloats, s));
+    }
+    void e(EwOp op, int rows, int W, float *o, int64_t ldo, const float *a, int64_t lda,
+           const float *b = nullptr, int64_t ldb = 0, const float *c = nullptr, int64_t ldc = 0,
+           const float *vec = nullptr, const uint8_t *mask = nullptr, int acc = 0) {
+        if (err == hipSuccess)
+            ok(ew(op, rows, W, View{o, ldo}, view(a, lda), view(b, ldb), view(c, ldc), vec, mask,
+                  acc, s));
+    }
+    void cs(int rows, int W, const float *X, int64_t ldx, const float *Y, int64_t ldy, float *out) {
+        if (err == hipSuccess && out)
+            ok(colsum(rows, W, view(X, ldx), view(Y, ldy), out, 0.0f, part, kGemmPartialFloats, s));
+    }
+    void norm(int mode, int rows, int W, float eps, const float *x, float *xh, float *r) {
+        if (err == hipSuccess)
+            ok(norm_rows(mode, rows, W, eps, view(x, W), view(xh, W), r, s));
+    }
+    void norm_bwd(int mode, int rows, int W, const float *xh, const float *r, const float *g,
+                  float *o, int acc) {
+        if (err == hipSuccess)
+            ok(norm_rows_bwd(mode, rows, W, view(xh, W), r, view(g, W), view(o, W), acc, s));
+    }
+    void cvt(const void *src, int dtype, int64_t n, float *dst) {
+        if (err == hipSuccess && src)
+            ok(to_f32(src, dtype, 1, (int)n, n, dst, nullptr, s));
+    }
+};
+
+int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
+                 const atom_attn_inputs *in, const atom_attn_params *par, float eps,
+                 int64_t radius, const atom_attn_grad_outputs *gout, atom_attn_input_grads *gin,
+                 atom_attn_param_grads *gpar, void *workspace, hipStream_t s) {
+    Arena ar{(char *)workspace};
+    Bufs b;
+    carve(ar, d, style, stage, b);
+    const int B = (int)d->B, A = (int)d->A, T = (int)d->T, K = (int)d->K, C = (int)d->C,
+              S = (int)d->S, H = (int)d->H, D = (int)d->D, V = (int)d->V, M = (int)d->M,
+              U = (int)d->U;
+    const int N = B * A, HD = H * D, BT = B * T;
+    const bool af3 = style == ATOM_ATTN_AF3, dec = stage == ATOM_ATTN_DECODER;
+    const int nm = af3 ? 0 : 1; // row normalisation: LayerNorm (AF3) / RMS (ESMFold2)
+    const int C6 = 6 * C;
+    Run r{s, b.part};
+
+    // ---------------------------------------------------------- recompute
+    ProfSpan sp = prof_begin(KN_BWD_RECOMPUTE, s);
+    if (af3) {
+        r.cvt(par->cond_scale, dtype, 3 * S, b.cs);
+        r.cvt(par->w_scale, dtype, 3 * (int64_t)S * C, b.ws);
+        r.cvt(par->b_scale, dtype, 3 * C, b.bs);
+        r.cvt(par->w_shift, dtype, 3 * (int64_t)S * C, b.wsh);
+        r.cvt(par->w_residual_gate, dtype, 2 * (int64_t)S * C, b.wrg);
+        r.cvt(par->b_residual_gate, dtype, 2 * C, b.brg);
+        r.cvt(par->b_q, dtype, HD, b.bq);
+        r.cvt(par->pair_scale, dtype, V, b.ps);
+        r.cvt(par->w_pair, dtype, (int64_t)V * H, b.wp);
+    } else {
+        r.cvt(par->w_mod, dtype, (int64_t)S * C6, b.wmod);
+    }
+    r.cvt(par->w_q, dtype, (int64_t)C * HD, b.wq);
+    r.cvt(par->w_k, dtype, (int64_t)C * HD, b.wk);
+    r.cvt(par->w_v, dtype, (int64_t)C * HD, b.wv);
+    r.cvt(par->w_value_gate, dtype, (int64_t)C * HD, b.wvg);
+    r.cvt(par->w_attention_out, dtype, (int64_t)HD * C, b.wao);
+    r.cvt(par->w_ff_gate, dtype, (int64_t)C * M, b.ffg);
+    r.cvt(par->w_ff_up, dtype, (int64_t)C * M, b.ffu);
+    r.cvt(par->w_ff_out, dtype, (int64_t)M * C, b.ffo);
+    if (dec) {
+        r.cvt(par->w_token, dtype, (int64_t)U * C, b.wtok);
+        r.cvt(par->readout_scale, dtype, C, b.rs);
+        if (!af3)
+            r.cvt(par->readout_bias, dtype, C, b.rb);
+        r.cvt(par->w_readout, dtype, (int64_t)C * 3, b.wro);
+    } else {
+        r.cvt(par->w_pool, dtype, (int64_t)C * U, b.wpool);
+    }
+    const Dims dd{B, A, T, K, C, S, H, D, V, M, U};
+    r.ok(launch_masks(dd, in->valid, in->token_valid, in->window_mask, in->atom_to_token,
+                      in->key_index, radius, b.usable, b.allowed, b.tcount, s));
+    if (dec) {
+        // token rows of invalid tokens never reach a usable atom: zeros
+        if (r.err == hipSuccess)
+            r.ok(to_f32(in->token, dtype, BT, U, U, b.tok, in->token_valid, s));
+        r.mm(BT, C, U, mat(b.tok, U), mat(b.wtok, C), b.tokproj, C);
+    }
+    if (r.err == hipSuccess)
+        r.ok(sanitize(B, A, T, C, S, dtype, in->atom, in->condition, b.usable, in->atom_to_token,
+                      dec ? b.tokproj : nullptr, b.x0, b.c, s));
+    // conditioning
+    if (af3) {
+        r.norm(0, N, S, eps, b.c, b.ch, b.rc);
+        for (int j = 0; j < 3; ++j) {
+            r.e(EW_MUL_VEC, N, S, b.cj, S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + j * S);
+            r.mm(N, C, S, mat(b.cj, S), mat(b.ws + (size_t)j * S * C, C), b.sig[j], C);
+            r.e(EW_SIGMOID_VEC, N, C, b.sig[j], C, b.sig[j], C, nullptr, 0, nullptr, 0, b.bs + j * C);
+            r.mm(N, C, S, mat(b.cj, S), mat(b.wsh + (size_t)j * S * C, C), b.mu[j], C);
+        }
+        for (int j = 0; j < 2; ++j) {
+            r.mm(N, C, S, mat(b.c, S), mat(b.wrg + (size_t)j * S * C, C), b.gr[j], C);
+            r.e(EW_SIGMOID_VEC, N, C, b.gr[j], C, b.gr[j], C, nullptr, 0, nullptr, 0, b.brg + j * C);
+        }
+    } else {
+        r.e(EW_SILU, N, S, b.sc, S, b.c, S);
+        r.mm(N, C6, S, mat(b.sc, S), mat(b.wmod, C6), b.mods, C6);
+    }
+    const float *gA = af3 ? b.gr[0] : b.mods + 2 * C;
+    const float *gT = af3 ? b.gr[1] : b.mods + 5 * C;
+    const int64_t ldg = af3 ? C : C6;
+    // modulated norms
+    r.norm(nm, N, C, eps, b.x0, b.xh0, b.r0);
+    if (af3) {
+        r.e(EW_AFFINE, N, C, b.qin, C, b.xh0, C, b.sig[0], C, b.mu[0], C);
+        r.e(EW_AFFINE, N, C, b.kvin, C, b.xh0, C, b.sig[1], C, b.mu[1], C);
+    } else {
+        r.e(EW_AFFINE1, N, C, b.qin, C, b.xh0, C, b.mods + C, C6, b.mods, C6);
+    }
+    // projections
+    float *qdst = af3 ? b.q : b.qraw;
+    float *kdst = af3 ? b.k : b.kraw;
+    r.mm(N, HD, C, mat(b.qin, C), mat(b.wq, HD), qdst, HD, 0.0f, af3 ? b.bq : nullptr);
+    r.mm(N, HD, C, mat(b.kvin, C), mat(b.wk, HD), kdst, HD);
+    r.mm(N, HD, C, mat(b.kvin, C), mat(b.wv, HD), b.v, HD);
+    r.mm(N, HD, C, mat(b.qin, C), mat(b.wvg, HD), b.g, HD);
+    r.e(EW_SIGMOID, N, HD, b.g, HD, b.g, HD);
+    float *dcos = gin ? gin->rope_cos : nullptr, *dsin = gin ? gin->rope_sin : nullptr;
+    const float *cs_f = nullptr, *sn_f = nullptr;
+    if (!af3) {
+        float *ct = b.rcos, *st = b.rsin; // rotary tables in fp32
+        if (r.err == hipSuccess) {
+            r.ok(to_f32(in->rope_cos, dtype, N, D, D, ct, nullptr, s));
+            r.ok(to_f32(in->rope_sin, dtype, N, D, D, st, nullptr, s));
+        }
+        cs_f = ct;
+        sn_f = st;
+        if (r.err == hipSuccess)
+            r.ok(head_rope(N, H, D, eps, b.qraw, b.kraw, ct, st, b.q, b.k, s));
+    }
+    prof_end(sp, s);
+    // slot attention with its weights kept
+    SlotBwdArgs sa{};
+    sa.B = B; sa.A = A; sa.K = K; sa.H = H; sa.D = D; sa.V = V;
+    sa.eps = eps; sa.radius = radius; sa.pair_dtype = dtype;
+    sa.usable = b.usable; sa.window_mask = in->window_mask; sa.key_index = in->key_index;
+    sa.q = b.q; sa.k = b.k; sa.v = b.v; sa.pair = af3 ? in->pair : nullptr;
+    sa.ps = b.ps; sa.wp = b.wp; sa.P = b.P; sa.o = b.o; sa.kid = b.kid;
+    sa.d_att = gout->attention; sa.d_o = b.dO; sa.dS = b.dS;
+    sa.dq = b.dq; sa.dk = b.dk; sa.dv = b.dv; sa.d_pair = (af3 && gin) ? gin->pair : nullptr;
+    sa.pw_partial = b.pwp; sa.count = b.cnt; sa.offset = b.off; sa.list = b.list;
+    if (r.err == hipSuccess) {
+        sp = prof_begin(KN_BWD_SLOT_FWD, s);
+        r.ok(slot_fwd(sa, af3 ? STYLE_AF3 : STYLE_ESM, s));
+        prof_end(sp, s);
+    }
+    sp = prof_begin(KN_BWD_RECOMPUTE, s);
+    r.e(EW_MUL, N, HD, b.og, HD, b.o, HD, b.g, HD);
+    r.mm(N, C, HD, mat(b.og, HD), mat(b.wao, C), b.uu, C);
+    r.e(EW_RESID, N, C, b.x1, C, b.x0, C, gA, ldg, b.uu, C);
+    r.norm(nm, N, C, eps, b.x1, b.xh1, b.r1);
+    if (af3)
+        r.e(EW_AFFINE, N, C, b.z, C, b.xh1, C, b.sig[2], C, b.mu[2], C);
+    else
+        r.e(EW_AFFINE1, N, C, b.z, C, b.xh1, C, b.mods + 4 * C, C6, b.mods + 3 * C, C6);
+    r.mm(N, M, C, mat(b.z, C), mat(b.ffg, M), b.fa, M);
+    r.mm(N, M, C, mat(b.z, C), mat(b.ffu, M), b.fb, M);
+    r.e(EW_SWIGLU, N, M, b.hh, M, b.fa, M, b.fb, M);
+    r.mm(N, C, M, mat(b.hh, M), mat(b.ffo, C), b.tr, C);
+    r.e(EW_RESID_MASK, N, C, b.hid, C, b.x1, C, gT, ldg, b.tr, C, nullptr, b.usable);
+    if (dec) {
+        r.norm(0, N, C, eps, b.hid, b.xhh, b.rh);
+        r.e(EW_MUL_VEC, N, C, b.lnh, C, b.xhh, C, nullptr, 0, nullptr, 0, b.rs);
+        if (!af3)
+            r.e(EW_ADD_VEC, N, C, b.lnh, C, b.lnh, C, nullptr, 0, nullptr, 0, b.rb);
+    } else {
+        r.mm(N, U, C, mat(b.hid, C), mat(b.wpool, U), b.proj, U);
+    }
+    prof_end(sp, s);
+
+    // ------------------------------------------------------------ chain rule
+    sp = prof_begin(KN_BWD_CHAIN, s);
+    if (gout->hidden)
+        r.e(EW_COPY, N, C, b.dh, C, gout->hidden, C);
+    else
+        r.e(EW_ZERO, N, C, b.dh, C, nullptr, 0);
+    if (!dec) {
+        float *dwpool = gpar ? gpar->w_pool : nullptr;
+        if (gout->token_output) {
+            if (r.err == hipSuccess)
+                r.ok(pool_bwd(B, A, T, U, b.usable, in->atom_to_token, b.tcount,
+                              gout->token_output, b.proj, b.dP, s));
+            r.mm(N, C, U, mat(b.dP, U), mat_t(b.wpool, U), b.dh, C, 1.0f);
+            if (dwpool)
+                r.mm(C, U, N, mat_t(b.hid, C), mat(b.dP, U), dwpool, U);
+        } else if (dwpool) {
+            r.e(EW_ZERO, C, U, dwpool, U, nullptr, 0);
+        }
+    } else {
+        float *dwro = gpar ? gpar->w_readout : nullptr;
+        float *drs = gpar ? gpar->readout_scale : nullptr;
+        float *drb = (gpar && !af3) ? gpar->readout_bias : nullptr;
+        if (gout->position_update) {
+            r.e(EW_MASK, N, 3, b.dpu, 3, gout->position_update, 3, nullptr, 0, nullptr, 0, nullptr,
+                b.usable);
+            if (dwro)
+                r.mm(C, 3, N, mat_t(b.lnh, C), mat(b.dpu, 3), dwro, 3);
+            r.mm(N, C, 3, mat(b.dpu, 3), mat_t(b.wro, 3), b.dln, C);
+            r.cs(N, C, b.dln, C, b.xhh, C, drs);
+            r.cs(N, C, b.dln, C, nullptr, 0, drb);
+            r.e(EW_MUL_VEC, N, C, b.gt, C, b.dln, C, nullptr, 0, nullptr, 0, b.rs);
+            r.norm_bwd(0, N, C, b.xhh, b.rh, b.gt, b.dh, 1);
+        } else {
+            if (dwro)
+                r.e(EW_ZERO, C, 3, dwro, 3, nullptr, 0);
+            if (drs)
+                r.e(EW_ZERO, 1, C, drs, C, nullptr, 0);
+            if (drb)
+                r.e(EW_ZERO, 1, C, drb, C, nullptr, 0);
+        }
+    }
+    // hidden = usable ? x1 + gT * tr : 0
+    r.e(EW_MASK, N, C, b.dx2, C, b.dh, C, nullptr, 0, nullptr, 0, nullptr, b.usable);
+    r.e(EW_MUL, N, C, b.dtr, C, b.dx2, C, gT, ldg);
+    r.e(EW_MUL, N, C, b.dgT, C, b.dx2, C, b.tr, C);
+    // transition
+    r.mm(N, M, C, mat(b.dtr, C), mat_t(b.ffo, C), b.dhh, M);
+    if (gpar && gpar->w_ff_out)
+        r.mm(M, C, N, mat_t(b.hh, M), mat(b.dtr, C), gpar->w_ff_out, C);
+    r.e(EW_DSWIGLU_A, N, M, b.da, M, b.dhh, M, b.fa, M, b.fb, M);
+    r.e(EW_DSWIGLU_B, N, M, b.dbb, M, b.dhh, M, b.fa, M);
+    r.mm(N, C, M, mat(b.da, M), mat_t(b.ffg, M), b.dz, C);
+    r.mm(N, C, M, mat(b.dbb, M), mat_t(b.ffu, M), b.dz, C, 1.0f);
+    if (gpar && gpar->w_ff_gate)
+        r.mm(C, M, N, mat_t(b.z, C), mat(b.da, M), gpar->w_ff_gate, M);
+    if (gpar && gpar->w_ff_up)
+        r.mm(C, M, N, mat_t(b.z, C), mat(b.dbb, M), gpar->w_ff_up, M);
+    // transition norm
+    r.e(EW_COPY, N, C, b.dx1, C, b.dx2, C);
+    if (af3) {
+        r.e(EW_MUL, N, C, b.gt, C, b.dz, C, b.sig[2], C);
+        r.norm_bwd(0, N, C, b.xh1, b.r1, b.gt, b.dx1, 1);
+        r.e(EW_DGATE, N, C, b.dzs[2], C, b.dz, C, b.xh1, C, b.sig[2], C);
+    } else {
+        r.e(EW_MUL1, N, C, b.gt, C, b.dz, C, b.mods + 4 * C, C6);
+        r.norm_bwd(1, N, C, b.xh1, b.r1, b.gt, b.dx1, 1);
+        r.e(EW_MUL, N, C, b.dmods + 4 * C, C6, b.dz, C, b.xh1, C);
+        r.e(EW_COPY, N, C, b.dmods + 3 * C, C6, b.dz, C);
+    }
+    // x1 = x0 + gA * u
+    r.e(EW_MUL, N, C, b.du, C, b.dx1, C, gA, ldg);
+    r.e(EW_MUL, N, C, b.dgA, C, b.dx1, C, b.uu, C);
+    if (af3) {
+        r.e(EW_DSIG, N, C, b.dzg[0], C, b.dgA, C, b.gr[0], C);
+        r.e(EW_DSIG, N, C, b.dzg[1], C, b.dgT, C, b.gr[1], C);
+    } else {
+        r.e(EW_COPY, N, C, b.dmods + 2 * C, C6, b.dgA, C);
+        r.e(EW_COPY, N, C, b.dmods + 5 * C, C6, b.dgT, C);
+    }
+    // output projection and value gate
+    r.mm(N, HD, C, mat(b.du, C), mat_t(b.wao, C), b.dog, HD);
+    if (gpar && gpar->w_attention_out)
+        r.mm(HD, C, N, mat_t(b.og, HD), mat(b.du, C), gpar->w_attention_out, C);
+    r.e(EW_MUL, N, HD, b.dO, HD, b.dog, HD, b.g, HD);
+    r.e(EW_DGATE, N, HD, b.dGp, HD, b.dog, HD, b.o, HD, b.g, HD);
+    prof_end(sp, s);
+    // slot attention
+    if (r.err == hipSuccess)
+        r.ok(slot_bwd(sa, af3 ? STYLE_AF3 : STYLE_ESM, gpar ? gpar->pair_scale : nullptr,
+                      gpar ? gpar->w_pair : nullptr, s));
+    sp = prof_begin(KN_BWD_CHAIN, s);
+    if (!af3 && r.err == hipSuccess)
+        r.ok(head_rope_bwd(N, H, D, eps, b.qraw, b.kraw, cs_f, sn_f, b.dq, b.dk, dcos, dsin, s));
+    // projections
+    r.mm(N, C, HD, mat(b.dq, HD), mat_t(b.wq, HD), b.dqin, C);
+    r.mm(N, C, HD, mat(b.dGp, HD), mat_t(b.wvg, HD), b.dqin, C, 1.0f);
+    r.mm(N, C, HD, mat(b.dk, HD), mat_t(b.wk, HD), b.dkvin, C);
+    r.mm(N, C, HD, mat(b.dv, HD), mat_t(b.wv, HD), b.dkvin, C, 1.0f);
+    if (gpar) {
+        if (gpar->w_q)
+            r.mm(C, HD, N, mat_t(b.qin, C), mat(b.dq, HD), gpar->w_q, HD);
+        if (af3)
+            r.cs(N, HD, b.dq, HD, nullptr, 0, gpar->b_q);
+        if (gpar->w_value_gate)
+            r.mm(C, HD, N, mat_t(b.qin, C), mat(b.dGp, HD), gpar->w_value_gate, HD);
+        if (gpar->w_k)
+            r.mm(C, HD, N, mat_t(b.kvin, C), mat(b.dk, HD), gpar->w_k, HD);
+        if (gpar->w_v)
+            r.mm(C, HD, N, mat_t(b.kvin, C), mat(b.dv, HD), gpar->w_v, HD);
+    }
+    // modulated norms
+    r.e(EW_COPY, N, C, b.dx0, C, b.dx1, C);
+    if (af3) {
+        r.e(EW_MUL, N, C, b.gt, C, b.dqin, C, b.sig[0], C);
+        r.e(EW_MUL, N, C, b.gt, C, b.dkvin, C, b.sig[1], C, nullptr, 0, nullptr, nullptr, 1);
+        r.norm_bwd(0, N, C, b.xh0, b.r0, b.gt, b.dx0, 1);
+        r.e(EW_DGATE, N, C, b.dzs[0], C, b.dqin, C, b.xh0, C, b.sig[0], C);
+        r.e(EW_DGATE, N, C, b.dzs[1], C, b.dkvin, C, b.xh0, C, b.sig[1], C);
+    } else {
+        // q_in and kv_in are one tensor: their gradients add
+        r.e(EW_ADD, N, C, b.dqin, C, b.dqin, C, b.dkvin, C);
+        r.e(EW_MUL1, N, C, b.gt, C, b.dqin, C, b.mods + C, C6);
+        r.norm_bwd(1, N, C, b.xh0, b.r0, b.gt, b.dx0, 1);
+        r.e(EW_MUL, N, C, b.dmods + C, C6, b.dqin, C, b.xh0, C);
+        r.e(EW_COPY, N, C, b.dmods, C6, b.dqin, C);
+    }
+    // conditioning
+    if (af3) {
+        const float *dmu[3] = {b.dqin, b.dkvin, b.dz};
+        for (int j = 0; j < 3; ++j) {
+            r.e(EW_MUL_VEC, N, S, b.cj, S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + j * S);
+            if (gpar && gpar->w_scale)
+                r.mm(S, C, N, mat_t(b.cj, S), mat(b.dzs[j], C), gpar->w_scale + (size_t)j * S * C, C);
+            if (gpar && gpar->w_shift)
+                r.mm(S, C, N, mat_t(b.cj, S), mat(dmu[j], C), gpar->w_shift + (size_t)j * S * C, C);
+            if (gpar && gpar->b_scale)
+                r.cs(N, C, b.dzs[j], C, nullptr, 0, gpar->b_scale + j * C);
+            r.mm(N, S, C, mat(b.dzs[j], C), mat_t(b.ws + (size_t)j * S * C, C), b.dcj, S);
+            r.mm(N, S, C, mat(dmu[j], C), mat_t(b.wsh + (size_t)j * S * C, C), b.dcj, S, 1.0f);
+            if (gpar && gpar->cond_scale)
+                r.cs(N, S, b.dcj, S, b.ch, S, gpar->cond_scale + j * S);
+            r.e(EW_MUL_VEC, N, S, b.dch, S, b.dcj, S, nullptr, 0, nullptr, 0, b.cs + j * S, nullptr,
+                j > 0 ? 1 : 0);
+        }
+        r.norm_bwd(0, N, S, b.ch, b.rc, b.dch, b.dc, 0);
+        for (int j = 0; j < 2; ++j) {
+            if (gpar && gpar->w_residual_gate)
+                r.mm(S, C, N, mat_t(b.c, S), mat(b.dzg[j], C),
+                     gpar->w_residual_gate + (size_t)j * S * C, C);
+            if (gpar && gpar->b_residual_gate)
+                r.cs(N, C, b.dzg[j], C, nullptr, 0, gpar->b_residual_gate + j * C);
+            r.mm(N, S, C, mat(b.dzg[j], C), mat_t(b.wrg + (size_t)j * S * C, C), b.dc, S, 1.0f);
+        }
+    } else {
+        if (gpar && gpar->w_mod)
+            r.mm(S, C6, N, mat_t(b.sc, S), mat(b.dmods, C6), gpar->w_mod, C6);
+        r.mm(N, S, C6, mat(b.dmods, C6), mat_t(b.wmod, C6), b.ds, S);
+        r.e(EW_DSILU, N, S, b.dc, S, b.ds, S, b.c, S);
+    }
+    if (gin && gin->condition)
+        r.e(EW_MASK, N, S, gin->condition, S, b.dc, S, nullptr, 0, nullptr, 0, nullptr, b.usable);
+    if (gin && gin->atom)
+        r.e(EW_MASK, N, C, gin->atom, C, b.dx0, C, nullptr, 0, nullptr, 0, nullptr, b.usable);
+    if (dec && ((gin && gin->token) || (gpar && gpar->w_token))) {
+        if (r.err == hipSuccess)
+            r.ok(token_keys(B, A, T, b.usable, in->atom_to_token, b.tkey, s));
+        if (r.err == hipSuccess)
+            r.ok(reverse_index(b.tkey, N, BT, b.tcnt, b.toff, b.tlist, s));
+        if (r.err == hipSuccess)
+            r.ok(segment_sum(BT, C, b.toff, b.tlist, b.dx0, b.dtp, s));
+        if (gin && gin->token)
+            r.mm(BT, U, C, mat(b.dtp, C), mat_t(b.wtok, C), gin->token, U);
+        if (gpar && gpar->w_token)
+            r.mm(U, C, BT, mat_t(b.tok, U), mat(b.dtp, C), gpar->w_token, C);
+    }
+    prof_end(sp, s);
+    return r.err == hipSuccess ? ATOM_ATTN_OK : ATOM_ATTN_ELAUNCH;
+}
+
+int check_backward(const atom_attn_dims *d, int style, int stage, int dtype) {
+    if (!d || d->B < 1 || d->A < 1 || d->T < 1 || d->K < 1 || d->C < 1 || d->S < 1 ||
+        d->H < 1 || d->D < 1 || d->V < 1 || d->M < 1 || d->U < 1)
+        return ATOM_ATTN_EINVAL;
+    if ((style != ATOM_ATTN_AF3 && style != ATOM_ATTN_ESMFOLD2) ||
+        (stage != ATOM_ATTN_ENCODER && stage != ATOM_ATTN_DECODER) ||
+        (dtype != ATOM_ATTN_F32 && dtype != ATOM_ATTN_BF16))
+        return ATOM_ATTN_EINVAL;
+    if (style == ATOM_ATTN_ESMFOLD2 && d->D % 2 != 0)
+        return ATOM_ATTN_EODD_HEAD;
+    return bwd_shape_ok(d, style);
+}
+
+size_t backward_bytes(const atom_attn_dims *d, int style, int stage) {
+    Arena ar{nullptr};
+    Bufs b;
+    carve(ar, d, style, stage, b);
+    return ar.off + 256;
+}
+
+} // namespace
+
+extern "C" {
+
+int atom_attn_backward_workspace_bytes(const atom_attn_dims *dims, int style, int stage,
+                                       int dtype, size_t *bytes) {
+    const int rc = check_backward(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!bytes)
+        return ATOM_ATTN_EINVAL;
+    *bytes = backward_bytes(dims, style, stage);
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_backward(const atom_attn_dims *dims, int style, int stage, int dtype,
+                       const atom_attn_inputs *in, const atom_attn_params *par, double eps,
+                       int64_t radius, const atom_attn_grad_outputs *grad_out,
+                       atom_attn_input_grads *grad_in, atom_attn_param_grads *grad_par,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_backward(dims, style, stage, dtype);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    if (!in || !par || !grad_out || !eps_ok(eps) || radius < -1)
+        return ATOM_ATTN_EINVAL;
+    const bool af3 = style == ATOM_ATTN_AF3, dec = stage == ATOM_ATTN_DECODER;
+    if (!in->atom || !in->condition || !in->valid || !in->token_valid || !in->window_mask ||
+        !in->atom_to_token || !in->key_index)
+        return ATOM_ATTN_EINVAL;
+    if (af3 && (!in->pair || !par->cond_scale || !par->w_scale || !par->b_scale ||
+                !par->w_shift || !par->w_residual_gate || !par->b_residual_gate || !par->b_q ||
+                !par->pair_scale || !par->w_pair))
+        return ATOM_ATTN_EINVAL;
+    if (!af3 && (!in->rope_cos || !in->rope_sin || !par->w_mod))
+        return ATOM_ATTN_EINVAL;
+    if (!par->w_q || !par->w_k || !par->w_v || !par->w_value_gate || !par->w_attention_out ||
+        !par->w_ff_gate || !par->w_ff_up || !par->w_ff_out)
+        return ATOM_ATTN_EINVAL;
+    if (dec && (!in->token || !par->w_token || !par->readout_scale || !par->w_readout ||
+                (!af3 && !par->readout_bias)))
+        return ATOM_ATTN_EINVAL;
+    if (!dec && !par->w_pool)
+        return ATOM_ATTN_EINVAL;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+        workspace_bytes < backward_bytes(dims, style, stage))
+        return ATOM_ATTN_EWORKSPACE;
+    return run_backward(dims, style, stage, dtype, in, par, (float)eps, radius, grad_out, grad_in,
+                        grad_par, workspace, (hipStream_t)stream);
+}
+
+int atom_attn_slot_backward_workspace_bytes(const atom_attn_dims *dims, int style,
+                                            size_t *bytes) {
+    if (!dims || !bytes || dims->B < 1 || dims->A < 1 || dims->K < 1 || dims->H < 1 ||
+        dims->D < 1 || dims->V < 1 || (style != ATOM_ATTN_AF3 && style != ATOM_ATTN_ESMFOLD2))
+        return ATOM_ATTN_EINVAL;
+    const int rc = bwd_shape_ok(dims, style);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    const size_t N = dims->B * dims->A, E = N * dims->K, HD = dims->H * dims->D;
+    Arena ar{nullptr};
+    ar.get<float>(E * dims->H);                   // weights
+    ar.get<float>(N * HD);                        // o
+    ar.get<float>(E * dims->H);                   // logit gradients
+    ar.get<int32_t>(E);                           // slot -> key
+    ar.get<int32_t>(N);                           // reverse index
+    ar.get<int32_t>(N + 1);
+    ar.get<int32_t>(E);
+    ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
+    ar.get<float>(dims->V);                       // pair parameters in fp32
+    ar.get<float>(dims->V * dims->H);
+    *bytes = ar.off + 256;
+    return ATOM_ATTN_OK;
+}
+
+int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int dtype,
+                                      double eps, int64_t radius, const uint8_t *usable,
+                                      const float *q, const float *k, const float *v,
+                                      const int64_t *key_index, const uint8_t *window_mask,
+                                      const void *pair, const void *pair_scale,
+                                      const void *w_pair, const float *d_attention,
+                                      const float *d_o, float *attention, float *o, float *dq,
+                                      float *dk, float *dv, float *d_pair, float *d_pair_scale,
+                                      float *d_w_pair, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+    size_t need = 0;
+    int rc = atom_attn_slot_backward_workspace_bytes(dims, style, &need);
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    const bool af3 = style == ATOM_ATTN_AF3;
+    if ((dtype != ATOM_ATTN_F32 && dtype != ATOM_ATTN_BF16) || !eps_ok(eps) || radius < -1 ||
+        !usable || !q || !k || !v || !key_index || !window_mask || !d_o || !dq || !dk || !dv)
+        return ATOM_ATTN_EINVAL;
+    if (af3 && (!pair || !pair_scale || !w_pair))
+        return ATOM_ATTN_EINVAL;
+    const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v;
+    if (al & 15u)
+        return ATOM_ATTN_EINVAL;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need)
+        return ATOM_ATTN_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t N = dims->B * dims->A, E = N * dims->K, HD = dims->H * dims->D;
+    Arena ar{(char *)workspace};
+    float *P = ar.get<float>(E * dims->H);
+    float *ob = ar.get<float>(N * HD);
+    float *dS = ar.get<float>(E * dims->H);
+    int32_t *kid = ar.get<int32_t>(E);
+    int32_t *cnt = ar.get<int32_t>(N);
+    int32_t *off = ar.get<int32_t>(N + 1);
+    int32_t *list = ar.get<int32_t>(E);
+    float *pwp = ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
+    float *psf = ar.get<float>(dims->V);              // pair parameters in fp32
+    float *wpf = ar.get<float>(dims->V * dims->H);
+    hipError_t e = hipSuccess;
+    SlotBwdArgs sa{};
+    sa.B = (int)dims->B; sa.A = (int)dims->A; sa.K = (int)dims->K; sa.H = (int)dims->H;
+    sa.D = (int)dims->D; sa.V = (int)dims->V; sa.eps = (float)eps; sa.radius = radius;
+    sa.pair_dtype = dtype; sa.usable = usable; sa.window_mask = window_mask;
+    sa.key_index = key_index; sa.q = q; sa.k = k; sa.v = v; sa.pair = af3 ? pair : nullptr;
+    sa.ps = psf; sa.wp = wpf; sa.P = attention ? attention : P; sa.o = o ? o : ob;
+    sa.kid = kid; sa.d_att = d_attention; sa.d_o = d_o; sa.dS = dS; sa.dq = dq; sa.dk = dk;
+    sa.dv = dv; sa.d_pair = af3 ? d_pair : nullptr; sa.pw_partial = pwp; sa.count = cnt;
+    sa.offset = off; sa.list = list;
+    if (af3) {
+        e = to_f32(pair_scale, dtype, 1, (int)dims->V, dims->V, psf, nullptr, s);
+        if (e == hipSuccess)
+            e = to_f32(w_pair, dtype, 1, (int)(dims->V * dims->H), dims->V * dims->H, wpf,
+                       nullptr, s);
+    }
+    if (e == hipSuccess) {
+        ProfSpan sp = prof_begin(KN_BWD_SLOT_FWD, s);
+        e = slot_fwd(sa, af3 ? STYLE_AF3 : STYLE_ESM, s);
+        prof_end(sp, s);
+    }
+    if (e == hipSuccess)
+        e = slot_bwd(sa, af3 ? STYLE_AF3 : STYLE_ESM, af3 ? d_pair_scale : nullptr,
+                     af3 ? d_w_pair : nullptr, s);
+    return e == hipSuccess ? ATOM_ATTN_OK : ATOM_ATTN_ELAUNCH;
+}
+
+} // extern "C"

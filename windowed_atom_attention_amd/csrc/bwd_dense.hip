@@ -1,0 +1,718 @@
+// bwd_dense.hip -- the dense and row kernels of the block's backward pass:
+// an fp32 matrix-core product for any operand strides, column sums, the
+// elementwise steps of the chain rule, row normalisation and its backward,
+// the ESMFold2 head RMS + rotary and its backward, sanitising, the pooling
+// backward, and the reverse index that turns "entry -> key" maps into
+// per-key lists without floating-point atomics.
+#include <algorithm>
+
+#include "bwd.hpp"
+#include "common.hpp"
+
+namespace waa {
+namespace bwd {
+
+namespace {
+
+// ------------------------------------------------------------------ product
+
+struct GemmK {
+    const float *A;
+    int64_t ars, acs;
+    const float *B;
+    int64_t brs, bcs;
+    float *C;
+    int64_t ldc;
+    const float *bias;
+    float beta;
+    int M, N, K, kchunk;
+    float *partial; // split mode: partial[z][M][N], no beta / bias
+};
+
+// 64x64 output tile per workgroup, four waves of 32x32 (v_mfma_f32_32x32x2_f32),
+// 16-deep k steps staged through LDS with the next step prefetched into
+// registers. Tile loads follow whichever operand axis is contiguous.
+__global__ __launch_bounds__(256) void k_gemm(GemmK g) {
+    __shared__ float As[16][68];
+    __shared__ float Bs[16][68];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int kb = blockIdx.z * g.kchunk;
+    const int ke = min(g.K, kb + g.kchunk);
+    const bool a_k = g.acs == 1;
+    const bool b_n = g.bcs == 1;
+    float ra[4], rb[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int m, k;
+            if (a_k) {
+                m = t >> 2;
+                k = (t & 3) * 4 + i;
+            } else {
+                k = t >> 4;
+                m = (t & 15) * 4 + i;
+            }
+            const int gm = m0 + m, gk = k0 + k;
+            ra[i] = (gm < g.M && gk < ke) ? g.A[(int64_t)gm * g.ars + (int64_t)gk * g.acs] : 0.0f;
+            int n, kk;
+            if (b_n) {
+                kk = t >> 4;
+                n = (t & 15) * 4 + i;
+            } else {
+                n = t >> 2;
+                kk = (t & 3) * 4 + i;
+            }
+            const int gn = n0 + n, gk2 = k0 + kk;
+            rb[i] = (gn < g.N && gk2 < ke) ? g.B[(int64_t)gk2 * g.brs + (int64_t)gn * g.bcs] : 0.0f;
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (a_k)
+                As[(t & 3) * 4 + i][t >> 2] = ra[i];
+            else
+                As[t >> 4][(t & 15) * 4 + i] = ra[i];
+            if (b_n)
+                Bs[t >> 4][(t & 15) * 4 + i] = rb[i];
+            else
+                Bs[(t & 3) * 4 + i][t >> 2] = rb[i];
+        }
+    };
+    f32x16_t acc = zero16();
+    const int wm = (w & 1) * 32, wn = (w >> 1) * 32;
+    const int half = lane >> 5, l32 = lane & 31;
+    if (kb < ke)
+        load(kb);
+    for (int k0 = kb; k0 < ke; k0 += 16) {
+        __syncthreads();
+        store();
+        __syncthreads();
+        if (k0 + 16 < ke)
+            load(k0 + 16);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const float a = As[kk * 2 + half][wm + l32];
+            const float b = Bs[kk * 2 + half][wn + l32];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+        }
+    }
+    const int c = n0 + wn + l32;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm + acc32_row(v, lane);
+        if (r >= g.M || c >= g.N)
+            continue;
+        if (g.partial) {
+            g.partial[((int64_t)blockIdx.z * g.M + r) * g.N + c] = acc[v];
+        } else {
+            float x = acc[v];
+            if (g.bias)
+                x += g.bias[c];
+            float *dst = g.C + (int64_t)r * g.ldc + c;
+            *dst = g.beta != 0.0f ? *dst + x : x;
+        }
+    }
+}
+
+// C = beta*C + bias + sum over splits, in split order.
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmK g, int splits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t MN = (int64_t)g.M * g.N;
+    if (i >= MN)
+        return;
+    const int r = (int)(i / g.N), c = (int)(i - (int64_t)r * g.N);
+    float x = 0.0f;
+    for (int z = 0; z < splits; ++z)
+        x += g.partial[(int64_t)z * MN + i];
+    if (g.bias)
+        x += g.bias[c];
+    float *dst = g.C + (int64_t)r * g.ldc + c;
+    *dst = g.beta != 0.0f ? *dst + x : x;
+}
+
+// ------------------------------------------------------------- column sums
+
+__global__ __launch_bounds__(256) void k_colsum(int rows, int W, const float *X, int64_t ldx,
+                                                const float *Y, int64_t ldy, float *partial,
+                                                int rows_per) {
+    __shared__ float red[4][64];
+    const int t = threadIdx.x, grp = t >> 6;
+    const int col = blockIdx.x * 64 + (t & 63);
+    const int r0 = blockIdx.y * rows_per, r1 = min(rows, r0 + rows_per);
+    float acc = 0.0f;
+    if (col < W)
+        for (int r = r0 + grp; r < r1; r += 4) {
+            float x = X[(int64_t)r * ldx + col];
+            if (Y)
+                x *= Y[(int64_t)r * ldy + col];
+            acc += x;
+        }
+    red[grp][t & 63] = acc;
+    __syncthreads();
+    if (grp == 0 && col < W)
+        partial[(int64_t)blockIdx.y * W + col] =
+            ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+}
+
+__global__ __launch_bounds__(256) void k_colsum_reduce(int W, int splits, const float *partial,
+                                                       float *out, float beta) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= W)
+        return;
+    float x = 0.0f;
+    for (int z = 0; z < splits; ++z)
+        x += partial[(int64_t)z * W + col];
+    out[col] = beta != 0.0f ? out[col] + x : x;
+}
+
+// ------------------------------------------------------------- elementwise
+
+__device__ __forceinline__ float dsilu_f(float z) {
+    const float s = sigmoid_f(z);
+    return s * (1.0f + z * (1.0f - s));
+}
+
+struct EwK {
+    int op, rows, W, acc;
+    float *o;
+    int64_t ldo;
+    const float *a, *b, *c;
+    int64_t lda, ldb, ldc;
+    const float *vec;
+    const uint8_t *mask;
+};
+
+__global__ __launch_bounds__(256) void k_ew(EwK e) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)e.rows * e.W)
+        return;
+    const int r = (int)(i / e.W), col = (int)(i - (int64_t)r * e.W);
+    const float a = e.a ? e.a[(int64_t)r * e.lda + col] : 0.0f;
+    const float b = e.b ? e.b[(int64_t)r * e.ldb + col] : 0.0f;
+    const float c = e.c ? e.c[(int64_t)r * e.ldc + col] : 0.0f;
+    const float vc = e.vec ? e.vec[col] : 0.0f;
+    const bool m = e.mask ? e.mask[r] != 0 : true;
+    float x;
+    switch (e.op) {
+    case EW_COPY: x = a; break;
+    case EW_ADD: x = a + b; break;
+    case EW_MUL: x = a * b; break;
+    case EW_MUL_VEC: x = a * vc; break;
+    case EW_AFFINE: x = a * b + c; break;
+    case EW_AFFINE1: x = a * (1.0f + b) + c; break;
+    case EW_MUL1: x = a * (1.0f + b); break;
+    case EW_SIGMOID: x = sigmoid_f(a); break;
+    case EW_SIGMOID_VEC: x = sigmoid_f(a + vc); break;
+    case EW_SILU: x = silu_f(a); break;
+    case EW_SWIGLU: x = silu_f(a) * b; break;
+    case EW_RESID: x = a + b * c; break;
+    case EW_RESID_MASK: x = m ? a + b * c : 0.0f; break;
+    case EW_MASK: x = m ? a : 0.0f; break;
+    case EW_DSIG: x = a * b * (1.0f - b); break;
+    case EW_DGATE: x = a * b * c * (1.0f - c); break;
+    case EW_DSWIGLU_A: x = a * c * dsilu_f(b); break;
+    case EW_DSWIGLU_B: x = a * silu_f(b); break;
+    case EW_DSILU: x = a * dsilu_f(b); break;
+    case EW_ADD_VEC: x = a + vc; break;
+    case EW_ZERO: x = 0.0f; break;
+    default: x = 0.0f; break;
+    }
+    float *dst = e.o + (int64_t)r * e.ldo + col;
+    *dst = e.acc ? *dst + x : x;
+}
+
+// --------------------------------------------------------- normalisation
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+__global__ __launch_bounds__(256) void k_norm_rows(int mode, int rows, int W, float eps,
+                                                   const float *x, int64_t ldx, float *xh,
+                                                   int64_t ldh, float *rstd) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const float *xr = x + (int64_t)row * ldx;
+    float mean = 0.0f;
+    if (mode == 0) {
+        float s = 0.0f;
+        for (int i = lane; i < W; i += 64)
+            s += xr[i];
+        mean = wave_sum(s) / (float)W;
+    }
+    float q = 0.0f;
+    for (int i = lane; i < W; i += 64) {
+        const float d = xr[i] - mean;
+        q += d * d;
+    }
+    const float r = 1.0f / sqrtf(wave_sum(q) / (float)W + eps);
+    float *hr = xh + (int64_t)row * ldh;
+    for (int i = lane; i < W; i += 64)
+        hr[i] = (xr[i] - mean) * r;
+    if (lane == 0)
+        rstd[row] = r;
+}
+
+__global__ __launch_bounds__(256) void k_norm_rows_bwd(int mode, int rows, int W,
+                                                       const float *xh, int64_t ldh,
+                                                       const float *rstd, const float *g,
+                                                       int64_t ldg, float *o, int64_t ldo,
+                                                       int acc) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const float *hr = xh + (int64_t)row * ldh;
+    const float *gr = g + (int64_t)row * ldg;
+    float sg = 0.0f, sgx = 0.0f;
+    for (int i = lane; i < W; i += 64) {
+        sg += gr[i];
+        sgx += gr[i] * hr[i];
+    }
+    const float mg = mode == 0 ? wave_sum(sg) / (float)W : 0.0f;
+    const float mgx = wave_sum(sgx) / (float)W;
+    const float r = rstd[row];
+    float *orow = o + (int64_t)row * ldo;
+    for (int i = lane; i < W; i += 64) {
+        const float d = r * (gr[i] - mg - hr[i] * mgx);
+        orow[i] = acc ? orow[i] + d : d;
+    }
+}
+
+// ------------------------------------------------------------ conversions
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_to_f32(const T *src, int64_t rows, int W, int64_t lds,
+                                                float *dst, const uint8_t *mask) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * W)
+        return;
+    const int64_t r = i / W;
+    const int col = (int)(i - r * W);
+    dst[i] = (!mask || mask[r]) ? to_f(src[r * lds + col]) : 0.0f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_sanitize_x(int B, int A, int T_, int C, const T *atom,
+                                                    const uint8_t *usable, const int64_t *a2t,
+                                                    const float *tokproj, float *x0) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)B * A * C)
+        return;
+    const int64_t n = i / C;
+    const int col = (int)(i - n * C);
+    float x = 0.0f;
+    if (usable[n]) {
+        x = to_f(atom[i]);
+        if (tokproj) {
+            const int64_t b = n / A;
+            x += tokproj[(b * T_ + a2t[n]) * C + col];
+        }
+    }
+    x0[i] = x;
+}
+
+// ------------------------------------------------------ head RMS + rotary
+
+// One thread per (row, channel i of a head); the D threads of a row's head
+// are an aligned lane group, so head sums and the rotary partner i ^ D/2
+// are lane exchanges.
+template <int D>
+__global__ __launch_bounds__(256) void k_head_rope(int rows, int H, float eps, const float *qraw,
+                                                   const float *kraw, const float *cs,
+                                                   const float *sn, float *q, float *k) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = t / D;
+    const int i = (int)(t % D);
+    const bool live = row < rows;
+    const int64_t rr = live ? row : 0;
+    const float c = cs[rr * D + i], s = sn[rr * D + i];
+    const int HD = H * D;
+    for (int which = 0; which < 2; ++which) {
+        const float *src = which ? kraw : qraw;
+        float *dst = which ? k : q;
+        for (int h = 0; h < H; ++h) {
+            const float x = src[rr * HD + h * D + i];
+            const float r = 1.0f / sqrtf(group_sum<D>(x * x) / (float)D + eps);
+            const float y = x * r;
+            const float yp = __shfl_xor(y, D / 2, D);
+            const float rot = i < D / 2 ? -yp : yp;
+            if (live)
+                dst[rr * HD + h * D + i] = y * c + rot * s;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_head_rope_bwd(int rows, int H, float eps,
+                                                       const float *qraw, const float *kraw,
+                                                       const float *cs, const float *sn,
+                                                       float *dq, float *dk, float *dcos,
+                                                       float *dsin) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = t / D;
+    const int i = (int)(t % D);
+    const bool live = row < rows;
+    const int64_t rr = live ? row : 0;
+    const float c = cs[rr * D + i], s = sn[rr * D + i];
+    const int HD = H * D;
+    float gc = 0.0f, gs = 0.0f;
+    for (int which = 0; which < 2; ++which) {
+        const float *src = which ? kraw : qraw;
+        float *g = which ? dk : dq;
+        for (int h = 0; h < H; ++h) {
+            const int64_t at = rr * HD + h * D + i;
+            const float x = src[at];
+            const float r = 1.0f / sqrtf(group_sum<D>(x * x) / (float)D + eps);
+            const float y = x * r;
+            const float yp = __shfl_xor(y, D / 2, D);
+            const float rot = i < D / 2 ? -yp : yp;
+            const float go = live ? g[at] : 0.0f;
+            gc += go * y;
+            gs += go * rot;
+            // through the rotation: dy = cos*go + R^T (sin*go)
+            const float zp = __shfl_xor(s * go, D / 2, D);
+            const float dy = c * go + (i < D / 2 ? zp : -zp);
+            // through the RMS: dx = r * (dy - y * mean(dy * y))
+            const float m = group_sum<D>(dy * y) / (float)D;
+            if (live)
+                g[at] = r * (dy - y * m);
+        }
+    }
+    if (live) {
+        if (dcos)
+            dcos[rr * D + i] = gc;
+        if (dsin)
+            dsin[rr * D + i] = gs;
+    }
+}
+
+// ------------------------------------------------------------ pooling
+
+__global__ __launch_bounds__(256) void k_pool_bwd(int B, int A, int T_, int U,
+                                                  const uint8_t *usable, const int64_t *a2t,
+                                                  const int32_t *count, const float *dto,
+                                                  const float *proj, float *dp) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)B * A * U)
+        return;
+    const int64_t n = i / U;
+    const int col = (int)(i - n * U);
+    float x = 0.0f;
+    if (usable[n] && proj[i] > 0.0f) {
+        const int64_t tok = (n / A) * T_ + a2t[n];
+        x = dto[tok * U + col] / (float)count[tok];
+    }
+    dp[i] = x;
+}
+
+__global__ __launch_bounds__(256) void k_token_keys(int B, int A, int T_, const uint8_t *usable,
+                                                    const int64_t *a2t, int32_t *key_of) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= (int64_t)B * A)
+        return;
+    key_of[n] = usable[n] ? (int32_t)((n / A) * T_ + a2t[n]) : -1;
+}
+
+// ------------------------------------------------------- reverse index
+
+__global__ __launch_bounds__(256) void k_fill_int(int32_t *p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_ri_count(const int32_t *key_of, int64_t n,
+                                                  int32_t *count) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const int k = key_of[i];
+    if (k >= 0)
+        atomicAdd(&count[k], 1);
+}
+
+// Exclusive scan of count into offset[0..nkeys], one workgroup: each thread
+// sums a contiguous chunk, the chunk totals are scanned in LDS.
+__global__ __launch_bounds__(1024) void k_ri_scan(const int32_t *count, int nkeys,
+                                                  int32_t *offset) {
+    __shared__ int32_t sh[1024];
+    const int t = threadIdx.x;
+    const int chunk = (nkeys + 1023) / 1024;
+    const int beg = min(nkeys, t * chunk), end = min(nkeys, beg + chunk);
+    int32_t s = 0;
+    for (int i = beg; i < end; ++i)
+        s += count[i];
+    sh[t] = s;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = t >= off ? sh[t - off] : 0;
+        __syncthreads();
+        sh[t] += v;
+        __syncthreads();
+    }
+    int32_t run = sh[t] - s;
+    for (int i = beg; i < end; ++i) {
+        offset[i] = run;
+        run += count[i];
+    }
+    if (t == 1023)
+        offset[nkeys] = sh[1023];
+}
+
+__global__ __launch_bounds__(256) void k_ri_fill(const int32_t *key_of, int64_t n,
+                                                 const int32_t *offset, int32_t *cursor,
+                                                 int32_t *list) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const int k = key_of[i];
+    if (k >= 0)
+        list[offset[k] + atomicAdd(&cursor[k], 1)] = (int32_t)i;
+}
+
+// Sort every list of at most kSortCap entries ascending, one wave per key:
+// an entry's place is the number of smaller entries in its list (entries
+// are distinct), counted over lane exchanges (<= 64) or an LDS copy.
+__global__ __launch_bounds__(256) void k_ri_sort(const int32_t *offset, int nkeys,
+                                                 int32_t *list) {
+    __shared__ int32_t sh[4][kSortCap];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int key = blockIdx.x * 4 + w;
+    int o = 0, L = 0;
+    if (key < nkeys) {
+        o = offset[key];
+        L = offset[key + 1] - o;
+    }
+    const bool small = L > 1 && L <= 64;
+    const bool mid = L > 64 && L <= kSortCap;
+    if (small) {
+        const int32_t x = lane < L ? list[o + lane] : 0x7fffffff;
+        int rank = 0;
+        for (int m = 0; m < L; ++m)
+            rank += __shfl(x, m) < x ? 1 : 0;
+        if (lane < L)
+            list[o + rank] = x;
+    }
+    if (mid)
+        for (int i = lane; i < L; i += 64)
+            sh[w][i] = list[o + i];
+    __syncthreads();
+    if (mid)
+        for (int i = lane; i < L; i += 64) {
+            const int32_t x = sh[w][i];
+            int rank = 0;
+            for (int m = 0; m < L; ++m)
+                rank += sh[w][m] < x ? 1 : 0;
+            list[o + rank] = x;
+        }
+}
+
+__global__ __launch_bounds__(256) void k_segment_sum(int nkeys, int W, const int32_t *offset,
+                                                     const int32_t *list, const float *X,
+                                                     float *out) {
+    const int lane = threadIdx.x & 63;
+    const int key = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (key >= nkeys)
+        return;
+    const int b = offset[key], e = offset[key + 1];
+    for (int c0 = 0; c0 < W; c0 += 64) {
+        const int col = c0 + lane;
+        float acc = 0.0f;
+        if (col < W)
+            for (int i = b; i < e; ++i)
+                acc += X[(int64_t)list[i] * W + col];
+        if (col < W)
+            out[(int64_t)key * W + col] = acc;
+    }
+}
+
+inline unsigned nblk(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+} // namespace
+
+hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const float *bias,
+                float *partial, size_t cap, hipStream_t s) {
+    if (M <= 0 || N <= 0)
+        return hipSuccess;
+    GemmK g{A.p, A.rs, A.cs, B.p, B.rs, B.cs, C.p, C.ld, bias, beta, M, N, K, 0, nullptr};
+    if (K <= 0) {
+        // an empty product: C = beta*C + bias
+        g.partial = nullptr;
+        g.kchunk = 16;
+        hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), 1), dim3(256), 0, s, g);
+        return hipGetLastError();
+    }
+    const int64_t tiles = (int64_t)nblk(M, 64) * nblk(N, 64);
+    int64_t splits = 1;
+    if (partial && tiles < 512 && K > 256) {
+        splits = std::min<int64_t>((512 + tiles - 1) / tiles, (K + 255) / 256);
+        splits = std::min<int64_t>(splits, (int64_t)(cap / ((size_t)M * N)));
+        if (splits < 2)
+            splits = 1;
+    }
+    int64_t kchunk = (K + splits - 1) / splits;
+    kchunk = (kchunk + 15) / 16 * 16;
+    splits = (K + kchunk - 1) / kchunk;
+    g.kchunk = (int)kchunk;
+    if (splits > 1) {
+        g.partial = partial;
+        hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), (unsigned)splits), dim3(256),
+                           0, s, g);
+        hipLaunchKernelGGL(k_gemm_reduce, dim3(nblk((int64_t)M * N, 256)), dim3(256), 0, s, g,
+                           (int)splits);
+    } else {
+        hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), 1), dim3(256), 0, s, g);
+    }
+    return hipGetLastError();
+}
+
+hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, float *partial,
+                  size_t cap, hipStream_t s) {
+    if (W <= 0)
+        return hipSuccess;
+    int64_t splits = std::max<int64_t>(1, std::min<int64_t>((rows + 255) / 256, 1024));
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (int64_t)(cap / (size_t)W)));
+    const int rows_per = (int)((rows + splits - 1) / splits);
+    splits = rows > 0 ? (rows + rows_per - 1) / rows_per : 1;
+    hipLaunchKernelGGL(k_colsum, dim3(nblk(W, 64), (unsigned)splits), dim3(256), 0, s, rows, W,
+                       (const float *)X.p, X.ld, (const float *)Y.p, Y.ld, partial,
+                       std::max(rows_per, 1));
+    hipLaunchKernelGGL(k_colsum_reduce, dim3(nblk(W, 256)), dim3(256), 0, s, W, (int)splits,
+                       (const float *)partial, out, beta);
+    return hipGetLastError();
+}
+
+hipError_t ew(EwOp op, int rows, int W, View o, View a, View b, View c, const float *vec,
+              const uint8_t *mask, int acc, hipStream_t s) {
+    const int64_t n = (int64_t)rows * W;
+    if (n <= 0)
+        return hipSuccess;
+    EwK e{(int)op, rows, W, acc, o.p, o.ld, a.p, b.p, c.p, a.ld, b.ld, c.ld, vec, mask};
+    hipLaunchKernelGGL(k_ew, dim3(nblk(n, 256)), dim3(256), 0, s, e);
+    return hipGetLastError();
+}
+
+hipError_t norm_rows(int mode, int rows, int W, float eps, View x, View xhat, float *rstd,
+                     hipStream_t s) {
+    if (rows <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_norm_rows, dim3(nblk(rows, 4)), dim3(256), 0, s, mode, rows, W, eps,
+                       (const float *)x.p, x.ld, xhat.p, xhat.ld, rstd);
+    return hipGetLastError();
+}
+
+hipError_t norm_rows_bwd(int mode, int rows, int W, View xhat, const float *rstd, View g,
+                         View o, int acc, hipStream_t s) {
+    if (rows <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_norm_rows_bwd, dim3(nblk(rows, 4)), dim3(256), 0, s, mode, rows, W,
+                       (const float *)xhat.p, xhat.ld, rstd, (const float *)g.p, g.ld, o.p,
+                       o.ld, acc);
+    return hipGetLastError();
+}
+
+hipError_t to_f32(const void *src, int dtype, int64_t rows, int W, int64_t lds, float *dst,
+                  const uint8_t *mask, hipStream_t s) {
+    const int64_t n = rows * W;
+    if (n <= 0)
+        return hipSuccess;
+    if (dtype == 1)
+        hipLaunchKernelGGL(k_to_f32<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, s,
+                           (const bf16_t *)src, rows, W, lds, dst, mask);
+    else
+        hipLaunchKernelGGL(k_to_f32<float>, dim3(nblk(n, 256)), dim3(256), 0, s,
+                           (const float *)src, rows, W, lds, dst, mask);
+    return hipGetLastError();
+}
+
+hipError_t head_rope(int rows, int H, int D, float eps, const float *qraw, const float *kraw,
+                     const float *cs, const float *sn, float *q, float *k, hipStream_t s) {
+    const dim3 grid(nblk((int64_t)rows * D, 256));
+    switch (D) {
+    case 8: hipLaunchKernelGGL(k_head_rope<8>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, q, k); break;
+    case 16: hipLaunchKernelGGL(k_head_rope<16>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, q, k); break;
+    case 32: hipLaunchKernelGGL(k_head_rope<32>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, q, k); break;
+    case 64: hipLaunchKernelGGL(k_head_rope<64>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, q, k); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t head_rope_bwd(int rows, int H, int D, float eps, const float *qraw,
+                         const float *kraw, const float *cs, const float *sn, float *dq,
+                         float *dk, float *dcos, float *dsin, hipStream_t s) {
+    const dim3 grid(nblk((int64_t)rows * D, 256));
+    switch (D) {
+    case 8: hipLaunchKernelGGL(k_head_rope_bwd<8>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, dq, dk, dcos, dsin); break;
+    case 16: hipLaunchKernelGGL(k_head_rope_bwd<16>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, dq, dk, dcos, dsin); break;
+    case 32: hipLaunchKernelGGL(k_head_rope_bwd<32>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, dq, dk, dcos, dsin); break;
+    case 64: hipLaunchKernelGGL(k_head_rope_bwd<64>, grid, dim3(256), 0, s, rows, H, eps, qraw, kraw, cs, sn, dq, dk, dcos, dsin); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t sanitize(int B, int A, int T, int C, int S, int dtype, const void *atom,
+                    const void *cond, const uint8_t *usable, const int64_t *a2t,
+                    const float *tokproj, float *x0, float *c, hipStream_t s) {
+    const int64_t n = (int64_t)B * A * C;
+    if (dtype == 1)
+        hipLaunchKernelGGL(k_sanitize_x<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, s, B, A, T, C,
+                           (const bf16_t *)atom, usable, a2t, tokproj, x0);
+    else
+        hipLaunchKernelGGL(k_sanitize_x<float>, dim3(nblk(n, 256)), dim3(256), 0, s, B, A, T, C,
+                           (const float *)atom, usable, a2t, tokproj, x0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return to_f32(cond, dtype, (int64_t)B * A, S, S, c, usable, s);
+}
+
+hipError_t pool_bwd(int B, int A, int T, int U, const uint8_t *usable, const int64_t *a2t,
+                    const int32_t *count, const float *dto, const float *proj, float *dp,
+                    hipStream_t s) {
+    const int64_t n = (int64_t)B * A * U;
+    hipLaunchKernelGGL(k_pool_bwd, dim3(nblk(n, 256)), dim3(256), 0, s, B, A, T, U, usable, a2t,
+                       count, dto, proj, dp);
+    return hipGetLastError();
+}
+
+hipError_t token_keys(int B, int A, int T, const uint8_t *usable, const int64_t *a2t,
+                      int32_t *key_of, hipStream_t s) {
+    hipLaunchKernelGGL(k_token_keys, dim3(nblk((int64_t)B * A, 256)), dim3(256), 0, s, B, A, T,
+                       usable, a2t, key_of);
+    return hipGetLastError();
+}
+
+hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *count,
+                         int32_t *offset, int32_t *list, hipStream_t s) {
+    hipLaunchKernelGGL(k_fill_int, dim3(nblk(nkeys, 256)), dim3(256), 0, s, count,
+                       (int64_t)nkeys, 0);
+    if (n > 0)
+        hipLaunchKernelGGL(k_ri_count, dim3(nblk(n, 256)), dim3(256), 0, s, key_of, n, count);
+    hipLaunchKernelGGL(k_ri_scan, dim3(1), dim3(1024), 0, s, (const int32_t *)count, nkeys,
+                       offset);
+    hipLaunchKernelGGL(k_fill_int, dim3(nblk(nkeys, 256)), dim3(256), 0, s, count,
+                       (int64_t)nkeys, 0);
+    if (n > 0)
+        hipLaunchKernelGGL(k_ri_fill, dim3(nblk(n, 256)), dim3(256), 0, s, key_of, n,
+                           (const int32_t *)offset, count, list);
+    hipLaunchKernelGGL(k_ri_sort, dim3(nblk(nkeys, 4)), dim3(256), 0, s,
+                       (const int32_t *)offset, nkeys, list);
+    return hipGetLastError();
+}
+
+hipError_t segment_sum(int nkeys, int W, const int32_t *offset, const int32_t *list,
+                       const float *X, float *out, hipStream_t s) {
+    if (nkeys <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_segment_sum, dim3(nblk(nkeys, 4)), dim3(256), 0, s, nkeys, W, offset,
+                       list, X, out);
+    return hipGetLastError();
+}
+
+} // namespace bwd
+} // namespace waa

@@ -1,0 +1,467 @@
+// bwd_slot.hip -- the slot-attention step of the backward pass
+// ("windowed_atom_attention", Required behavior: masked softmax over each
+// query's allowed slots of Q.K/sqrt(D) (+ the AF3 pair bias), o = sum of
+// weights times the selected V rows; a key chosen by several slots, of one
+// query or of many, receives the sum of their gradients).
+//
+// Forward (fp32, weights kept): one wave per query atom. The wave marks its
+// allowed slots, computes the AF3 pair bias of each, then per head the
+// logits (lane = slot), the masked softmax (wave reductions) and o (lane =
+// channel, lane groups over slots).
+//
+// Backward, query side (one wave per query atom), per head h:
+//   dW_s = dA_s + dO_h . V[key_s]_h,   dS_s = P_s (dW_s - sum_t P_t dW_t),
+//   dQ_h = sum_s dS_s K[key_s]_h / sqrt(D);
+// AF3: dS_s is also the gradient of the slot's pair bias, which flows back
+// through LN(pair) * pair_scale @ w_pair to the pair row, pair_scale and
+// w_pair (per-workgroup partial sums, reduced in a fixed order).
+// Backward, key side: the reverse index of the slot -> key map (per key,
+// its (query, slot) entries in ascending order) lets one wave per key sum
+//   dK_j = sum dS Q_query / sqrt(D),  dV_j = sum P dO_query
+// over every selection of key j, with no floating-point atomics.
+#include "bwd.hpp"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace waa {
+namespace bwd {
+
+namespace {
+
+constexpr int kMaxK = 512, kMaxH = 8, kMaxHD = 256;
+constexpr int kPairV = 16, kPairH = 4; // AF3 pair-bias gradient bounds
+
+struct SK {
+    SlotBwdArgs a;
+    float inv_sqrt_d;
+};
+
+// LDS floats per wave: key ids [K], per-slot values [K*H], one head's slot
+// values [K], one query row [HD].
+__host__ __device__ inline int wave_floats(int K, int H, int HD) { return K + K * H + K + HD; }
+
+template <typename TP>
+__device__ __forceinline__ void load_pair_row(const TP *pair, int64_t row, int V, float *x) {
+#pragma unroll
+    for (int v = 0; v < kPairV; ++v)
+        x[v] = v < V ? to_f(pair[row * V + v]) : 0.0f;
+}
+
+// LN of a pair row (population, eps in the root): xhat and 1/sqrt(var+eps).
+__device__ __forceinline__ float pair_ln(float *x, int V, float eps) {
+    float m = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kPairV; ++v)
+        m += v < V ? x[v] : 0.0f;
+    m /= (float)V;
+    float q = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kPairV; ++v) {
+        const float d = v < V ? x[v] - m : 0.0f;
+        q += d * d;
+    }
+    const float r = 1.0f / sqrtf(q / (float)V + eps);
+#pragma unroll
+    for (int v = 0; v < kPairV; ++v)
+        x[v] = v < V ? (x[v] - m) * r : 0.0f;
+    return r;
+}
+
+template <typename TP, bool AF3>
+__global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
+    extern __shared__ float smem[];
+    const SlotBwdArgs &a = p.a;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int K = a.K, H = a.H, D = a.D, HD = H * D;
+    float *base = smem + w * wave_floats(K, H, HD);
+    int *skid = reinterpret_cast<int *>(base);
+    float *sbeta = base + K;
+    float *sP = sbeta + K * H;
+    float *sq = sP + K;
+    const int64_t N = (int64_t)a.B * a.A;
+    const int64_t n = (int64_t)blockIdx.x * 4 + w;
+    const bool live = n < N;
+    const int64_t nn = live ? n : 0;
+    const int64_t b = nn / a.A, qa = nn - b * a.A;
+    const bool qu = live && a.usable[nn];
+
+    for (int s = lane; s < K; s += 64) {
+        const int64_t e = nn * K + s;
+        const int64_t j = a.key_index[e];
+        bool ok = qu && j >= 0 && j < a.A && a.window_mask[e];
+        if (ok)
+            ok = a.usable[b * a.A + j] && (a.radius < 0 || (j > qa ? j - qa : qa - j) <= a.radius);
+        const int id = ok ? (int)(b * a.A + j) : -1;
+        skid[s] = id;
+        if (live)
+            a.kid[e] = id;
+        if constexpr (AF3) {
+            float x[kPairV];
+            if (ok) {
+                load_pair_row(reinterpret_cast<const TP *>(a.pair), e, a.V, x);
+                pair_ln(x, a.V, a.eps);
+            }
+            for (int h = 0; h < H; ++h) {
+                float acc = 0.0f;
+                if (ok)
+#pragma unroll
+                    for (int v = 0; v < kPairV; ++v)
+                        if (v < a.V)
+                            acc += x[v] * a.ps[v] * a.wp[v * H + h];
+                sbeta[s * H + h] = acc;
+            }
+        }
+    }
+    for (int i = lane; i < HD; i += 64)
+        sq[i] = a.q[nn * HD + i];
+    __syncthreads();
+
+    const int G = 64 / D, grp = lane / D, dd = lane - grp * D;
+    for (int h = 0; h < H; ++h) {
+        float l[kMaxK / 64];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < kMaxK / 64; ++c) {
+            const int s = lane + 64 * c;
+            l[c] = -INFINITY;
+            if (s < K && skid[s] >= 0) {
+                const float4 *kr = reinterpret_cast<const float4 *>(a.k + (int64_t)skid[s] * HD + h * D);
+                float dot = 0.0f;
+                for (int d4 = 0; d4 < D / 4; ++d4) {
+                    const float4 kv = kr[d4];
+                    const float *qv = sq + h * D + d4 * 4;
+                    dot += qv[0] * kv.x + qv[1] * kv.y + qv[2] * kv.z + qv[3] * kv.w;
+                }
+                l[c] = dot * p.inv_sqrt_d + (AF3 ? sbeta[s * H + h] : 0.0f);
+                mx = fmaxf(mx, l[c]);
+            }
+        }
+        mx = group_max<64>(mx);
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxK / 64; ++c) {
+            const int s = lane + 64 * c;
+            if (s < K && skid[s] >= 0) {
+                l[c] = expf(l[c] - mx);
+                sum += l[c];
+            }
+        }
+        sum = group_sum<64>(sum);
+        const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxK / 64; ++c) {
+            const int s = lane + 64 * c;
+            if (s < K) {
+                const float pw = skid[s] >= 0 ? l[c] * inv : 0.0f;
+                sP[s] = pw;
+                if (live)
+                    a.P[((b * H + h) * a.A + qa) * K + s] = pw;
+            }
+        }
+        __syncthreads();
+        float acc = 0.0f;
+        for (int s = grp; s < K; s += G) {
+            const float pw = sP[s];
+            if (pw != 0.0f)
+                acc += pw * a.v[(int64_t)skid[s] * HD + h * D + dd];
+        }
+        for (int off = D; off < 64; off <<= 1)
+            acc += __shfl_xor(acc, off);
+        if (live && grp == 0)
+            a.o[nn * HD + h * D + dd] = acc;
+        __syncthreads();
+    }
+}
+
+template <typename TP, bool AF3>
+__global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
+    extern __shared__ float smem[];
+    __shared__ float wred[4][kPairV + kPairV * kPairH];
+    const SlotBwdArgs &a = p.a;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int K = a.K, H = a.H, D = a.D, HD = H * D;
+    float *base = smem + w * wave_floats(K, H, HD);
+    int *skid = reinterpret_cast<int *>(base);
+    float *sdl = base + K;
+    float *sP = sdl + K * H;
+    float *sdo = sP + K;
+    const int64_t N = (int64_t)a.B * a.A;
+    const int64_t n = (int64_t)blockIdx.x * 4 + w;
+    const bool live = n < N;
+    const int64_t nn = live ? n : 0;
+    const int64_t b = nn / a.A, qa = nn - b * a.A;
+
+    for (int s = lane; s < K; s += 64)
+        skid[s] = live ? a.kid[nn * K + s] : -1;
+    for (int i = lane; i < HD; i += 64)
+        sdo[i] = a.d_o[nn * HD + i];
+    __syncthreads();
+
+    const int G = 64 / D, grp = lane / D, dd = lane - grp * D;
+    for (int h = 0; h < H; ++h) {
+        const int64_t rowbase = ((b * H + h) * a.A + qa) * K;
+        float pw[kMaxK / 64], dw[kMaxK / 64];
+        float dsum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxK / 64; ++c) {
+            const int s = lane + 64 * c;
+            pw[c] = 0.0f;
+            dw[c] = 0.0f;
+            if (s < K && skid[s] >= 0) {
+                pw[c] = a.P[rowbase + s];
+                float x = a.d_att ? a.d_att[rowbase + s] : 0.0f;
+                if (pw[c] != 0.0f) {
+                    const float4 *vr = reinterpret_cast<const float4 *>(a.v + (int64_t)skid[s] * HD + h * D);
+                    for (int d4 = 0; d4 < D / 4; ++d4) {
+                        const float4 vv = vr[d4];
+                        const float *ov = sdo + h * D + d4 * 4;
+                        x += ov[0] * vv.x + ov[1] * vv.y + ov[2] * vv.z + ov[3] * vv.w;
+                    }
+                }
+                dw[c] = x;
+                dsum += pw[c] * x;
+            }
+        }
+        dsum = group_sum<64>(dsum);
+#pragma unroll
+        for (int c = 0; c < kMaxK / 64; ++c) {
+            const int s = lane + 64 * c;
+            if (s < K) {
+                const float dl = pw[c] * (dw[c] - dsum);
+                sP[s] = dl;
+                sdl[s * H + h] = dl;
+                if (live)
+                    a.dS[rowbase + s] = dl;
+            }
+        }
+        __syncthreads();
+        float acc = 0.0f;
+        for (int s = grp; s < K; s += G) {
+            const float dl = sP[s];
+            if (dl != 0.0f)
+                acc += dl * a.k[(int64_t)skid[s] * HD + h * D + dd];
+        }
+        for (int off = D; off < 64; off <<= 1)
+            acc += __shfl_xor(acc, off);
+        if (live && grp == 0)
+            a.dq[nn * HD + h * D + dd] = acc * p.inv_sqrt_d;
+        __syncthreads();
+    }
+
+    if constexpr (AF3) {
+        // pair bias: beta_h = sum_v xhat_v ps_v wp[v][h]
+        const int V = a.V;
+        float gps[kPairV], gwp[kPairV * kPairH];
+#pragma unroll
+        for (int i = 0; i < kPairV; ++i)
+            gps[i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPairV * kPairH; ++i)
+            gwp[i] = 0.0f;
+        for (int s = lane; s < K; s += 64) {
+            const int64_t e = nn * K + s;
+            if (skid[s] >= 0) {
+                float x[kPairV];
+                load_pair_row(reinterpret_cast<const TP *>(a.pair), e, V, x);
+                const float r = pair_ln(x, V, a.eps);
+                float db[kPairH];
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    db[h] = h < H ? sdl[s * H + h] : 0.0f;
+                float y[kPairV];
+                float my = 0.0f, myx = 0.0f;
+#pragma unroll
+                for (int v = 0; v < kPairV; ++v) {
+                    float dpn = 0.0f;
+#pragma unroll
+                    for (int h = 0; h < kPairH; ++h)
+                        if (v < V && h < H)
+                            dpn += db[h] * a.wp[v * H + h];
+                    gps[v] += dpn * x[v];
+                    const float psv = v < V ? a.ps[v] : 0.0f;
+#pragma unroll
+                    for (int h = 0; h < kPairH; ++h)
+                        gwp[v * kPairH + h] += x[v] * psv * db[h];
+                    y[v] = dpn * psv;
+                    my += y[v];
+                    myx += y[v] * x[v];
+                }
+                if (a.d_pair) {
+                    my /= (float)V;
+                    myx /= (float)V;
+                    for (int v = 0; v < V; ++v)
+                        a.d_pair[e * V + v] = r * (y[v] - my - x[v] * myx);
+                }
+            } else if (a.d_pair && live) {
+                for (int v = 0; v < V; ++v)
+                    a.d_pair[e * V + v] = 0.0f;
+            }
+        }
+        // wave sums, then the workgroup's four waves in order
+#pragma unroll
+        for (int i = 0; i < kPairV; ++i) {
+            const float t = group_sum<64>(gps[i]);
+            if (lane == 0)
+                wred[w][i] = t;
+        }
+#pragma unroll
+        for (int i = 0; i < kPairV * kPairH; ++i) {
+            const float t = group_sum<64>(gwp[i]);
+            if (lane == 0)
+                wred[w][kPairV + i] = t;
+        }
+        __syncthreads();
+        constexpr int W = kPairV + kPairV * kPairH;
+        for (int i = threadIdx.x; i < W; i += 256)
+            a.pw_partial[(int64_t)blockIdx.x * W + i] =
+                ((wred[0][i] + wred[1][i]) + wred[2][i]) + wred[3][i];
+    }
+}
+
+// One wave per key atom: its list of (query, slot) entries in order.
+__global__ __launch_bounds__(256) void k_slot_bwd_kv(SK p) {
+    const SlotBwdArgs &a = p.a;
+    const int lane = threadIdx.x & 63;
+    const int64_t N = (int64_t)a.B * a.A;
+    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= N)
+        return;
+    const int K = a.K, H = a.H, D = a.D, HD = H * D;
+    float ak[kMaxHD / 64], av[kMaxHD / 64];
+#pragma unroll
+    for (int i = 0; i < kMaxHD / 64; ++i) {
+        ak[i] = 0.0f;
+        av[i] = 0.0f;
+    }
+    const int beg = a.offset[j], end = a.offset[j + 1];
+    for (int it = beg; it < end; ++it) {
+        const int64_t e = a.list[it];
+        const int64_t n = e / K, s = e - n * K;
+        const int64_t b = n / a.A, qa = n - b * a.A;
+#pragma unroll
+        for (int i = 0; i < kMaxHD / 64; ++i) {
+            const int c = lane + 64 * i;
+            if (c < HD) {
+                const int h = c / D;
+                const int64_t at = ((b * H + h) * a.A + qa) * K + s;
+                ak[i] += a.dS[at] * a.q[n * HD + c];
+                av[i] += a.P[at] * a.d_o[n * HD + c];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxHD / 64; ++i) {
+        const int c = lane + 64 * i;
+        if (c < HD) {
+            a.dk[j * HD + c] = ak[i] * p.inv_sqrt_d;
+            a.dv[j * HD + c] = av[i];
+        }
+    }
+}
+
+inline unsigned nblk(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+template <typename Fn> void set_lds(Fn fn, size_t bytes) {
+    allow_lds(reinterpret_cast<const void *>(fn), bytes);
+}
+
+} // namespace
+
+int slot_bwd_supported(int K, int H, int D, int V, int style) {
+    if (K < 1 || K > kMaxK || H < 1 || H > kMaxH)
+        return 0;
+    if (D != 8 && D != 16 && D != 32 && D != 64)
+        return 0;
+    if (H * D > kMaxHD)
+        return 0;
+    if (style == STYLE_AF3 && (V < 1 || V > kPairV || H > kPairH))
+        return 0;
+    return 1;
+}
+
+size_t slot_bwd_partial_floats(int64_t rows, int V, int H) {
+    (void)V;
+    (void)H;
+    return 2 * (size_t)nblk(rows, 4) * (kPairV + kPairV * kPairH);
+}
+
+hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s) {
+    const int64_t N = (int64_t)a.B * a.A;
+    if (N <= 0)
+        return hipSuccess;
+    SK p{a, 1.0f / sqrtf((float)a.D)};
+    const size_t lds = 4 * sizeof(float) * (size_t)wave_floats(a.K, a.H, a.H * a.D);
+    const dim3 grid(nblk(N, 4));
+    if (style == STYLE_AF3) {
+        if (a.pair_dtype == 1) {
+            set_lds(k_slot_fwd<bf16_t, true>, lds);
+            hipLaunchKernelGGL((k_slot_fwd<bf16_t, true>), grid, dim3(256), lds, s, p);
+        } else {
+            set_lds(k_slot_fwd<float, true>, lds);
+            hipLaunchKernelGGL((k_slot_fwd<float, true>), grid, dim3(256), lds, s, p);
+        }
+    } else {
+        set_lds(k_slot_fwd<float, false>, lds);
+        hipLaunchKernelGGL((k_slot_fwd<float, false>), grid, dim3(256), lds, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float *d_w_pair,
+                    hipStream_t s) {
+    const int64_t N = (int64_t)a.B * a.A;
+    if (N <= 0)
+        return hipSuccess;
+    SK p{a, 1.0f / sqrtf((float)a.D)};
+    const size_t lds = 4 * sizeof(float) * (size_t)wave_floats(a.K, a.H, a.H * a.D);
+    const dim3 grid(nblk(N, 4));
+    ProfSpan sp = prof_begin(KN_BWD_SLOT_Q, s);
+    if (style == STYLE_AF3) {
+        if (a.pair_dtype == 1) {
+            set_lds(k_slot_bwd_q<bf16_t, true>, lds);
+            hipLaunchKernelGGL((k_slot_bwd_q<bf16_t, true>), grid, dim3(256), lds, s, p);
+        } else {
+            set_lds(k_slot_bwd_q<float, true>, lds);
+            hipLaunchKernelGGL((k_slot_bwd_q<float, true>), grid, dim3(256), lds, s, p);
+        }
+    } else {
+        set_lds(k_slot_bwd_q<float, false>, lds);
+        hipLaunchKernelGGL((k_slot_bwd_q<float, false>), grid, dim3(256), lds, s, p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    prof_end(sp, s);
+    if (style == STYLE_AF3 && (d_pair_scale || d_w_pair)) {
+        // sum the per-workgroup partials in workgroup order
+        constexpr int W = kPairV + kPairV * kPairH;
+        const int rows = (int)grid.x;
+        float *tmp = a.pw_partial + (size_t)rows * W; // room for colsum partials
+        const size_t cap = (size_t)rows * W;
+        if (d_pair_scale) {
+            e = colsum(rows, a.V, view(a.pw_partial, W), View{nullptr, 0}, d_pair_scale, 0.0f,
+                       tmp, cap, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        if (d_w_pair) {
+            // gradient of w_pair [V][H] from the [V][kPairH] block of the partials
+            for (int v = 0; v < a.V; ++v) {
+                e = colsum(rows, a.H, view(a.pw_partial + kPairV + v * kPairH, W),
+                           View{nullptr, 0}, d_w_pair + v * a.H, 0.0f, tmp, cap, s);
+                if (e != hipSuccess)
+                    return e;
+            }
+        }
+    }
+    sp = prof_begin(KN_BWD_SLOT_KV, s);
+    e = reverse_index(a.kid, N * a.K, (int)N, a.count, a.offset, a.list, s);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_slot_bwd_kv, grid, dim3(256), 0, s, p);
+    prof_end(sp, s);
+    return hipGetLastError();
+}
+
+} // namespace bwd
+} // namespace waa

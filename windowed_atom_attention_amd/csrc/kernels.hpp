@@ -89,7 +89,11 @@ struct SlotArgs {
 // unless atom_attn_profile_enable is on): prof_begin before a launch and
 // prof_end after it, on the launch stream. Ids past the block's kernels:
 enum { KN_S2P_TOK = 7, KN_S2P_PAIR = 8, KN_WINDOW = 9, KN_TIED_BIAS = 10, KN_TIED_PROJ = 11,
-       KN_TIED_LOGITS = 12, KN_TIED_SOFTMAX = 13, KN_TIED_OUT = 14 };
+       KN_TIED_LOGITS = 12, KN_TIED_SOFTMAX = 13, KN_TIED_OUT = 14,
+       // backward pass: forward recomputation, its slot step, the slot
+       // backward (query side, reverse index + key side), the dense chain
+       KN_BWD_RECOMPUTE = 15, KN_BWD_SLOT_FWD = 16, KN_BWD_SLOT_Q = 17, KN_BWD_SLOT_KV = 18,
+       KN_BWD_CHAIN = 19 };
 struct ProfSpan {
     int kernel = -1;
     hipEvent_t e0 = nullptr, e1 = nullptr;
