@@ -500,6 +500,80 @@ def measure_ops(steps=50, warmup=5, cache_bytes=768e6):
     return res
 
 
+def _dense_flops(d, style, stage):
+    """Flops of the block's dense products for one call (forward)."""
+    N = d["B"] * d["A"]
+    C, S, HD, M, U = d["C"], d["S"], d["H"] * d["D"], d["M"], d["U"]
+    per = 2 * C * HD * 4 + 2 * HD * C + 2 * C * M * 2 + 2 * M * C
+    per += 2 * S * C * 8 if style == "af3" else 2 * S * 6 * C
+    per += 2 * C * U if stage == "encoder" else 2 * C * 3
+    tok = 2 * d["B"] * d["T"] * U * C if stage == "decoder" else 0
+    return N * per + tok
+
+
+def measure_backward(names=("1", "4a"), steps=20, warmup=3):
+    """The backward pass (atom_attn_backward) on whole workloads: wall time per
+    call with every upstream gradient given, and the per-phase HIP-event
+    spans with their rooflines: the forward recomputation and the chain
+    rule's dense products against the fp32 matrix-core peak (they run in
+    fp32 whatever the storage), the slot-step kernels against HBM."""
+    import torch
+    from windowed_atom_attention_amd import backward_workspace_bytes, block_backward
+    from windowed_atom_attention_amd.workloads import make_workload
+    res = {}
+    for name in names:
+        w = make_workload(name).to("cuda")
+        d = w.dims
+        B, A, T, K, C, H, D, U, V = (d[k] for k in "B A T K C H D U V".split())
+        g = torch.Generator(device="cuda").manual_seed(0)
+        up = {"hidden": torch.randn((B, A, C), generator=g, device="cuda"),
+              "attention": torch.randn((B, H, A, K), generator=g, device="cuda")}
+        if w.stage == "encoder":
+            up["token_output"] = torch.randn((B, T, U), generator=g, device="cuda")
+        else:
+            up["position_update"] = torch.randn((B, A, 3), generator=g, device="cuda")
+        ws = torch.empty(backward_workspace_bytes(d, w.style, w.stage, w.dtype),
+                         dtype=torch.uint8, device="cuda")
+        call = lambda i: block_backward(w.activations, w.parameters, w.masks, w.structure, up,
+                                        eps=w.eps, style=w.style, stage=w.stage,
+                                        radius=w.radius, workspace=ws)
+        wall, kt = _time_op(call, 1, steps, warmup)
+        N, E, HD = B * A, B * A * K, H * D
+        e = 2 if w.dtype == torch.bfloat16 else 4
+        pair = E * V * e if w.style == "af3" else 0
+        dpair = E * V * 4 if w.style == "af3" else 0
+        f32 = 4
+        work = {
+            # Q, K, V rows, key ids, window mask, usable, pair rows; weights,
+            # o, slot -> key map written
+            "bwd_slot_fwd": ("hbm", 3 * N * HD * f32 + 9 * E + N + pair + E * H * f32 +
+                             N * HD * f32 + 4 * E),
+            # weights, upstream weights, d_o, K and V rows, slot -> key map,
+            # pair rows read; logit gradients, dq, d_pair written
+            "bwd_slot_q": ("hbm", 2 * E * H * f32 + 3 * N * HD * f32 + 4 * E + pair +
+                           E * H * f32 + N * HD * f32 + dpair),
+            # reverse index (map read twice, list written and read), weights
+            # and logit gradients, Q and d_o rows read; dk, dv written
+            "bwd_slot_kv": ("hbm", 16 * E + 2 * E * H * f32 + 4 * N * HD * f32),
+            "bwd_recompute": ("mfma", _dense_flops(d, w.style, w.stage)),
+            "bwd_chain": ("mfma", 2 * _dense_flops(d, w.style, w.stage)),
+        }
+        for k, (bound, amount) in work.items():
+            if k in kt:
+                _roof(kt[k], bound, amount, "f32")
+        res[name] = {"workload": "%s (config %s), B=%d A=%d K=%d, every upstream gradient"
+                                 % (NAMES[name], name, B, A, K),
+                     "storage_dtype": str(w.dtype).replace("torch.", ""), "compute_dtype": "f32",
+                     "ms_per_call": wall * 1e3, "atoms_per_s": N / wall,
+                     "entries_per_s": N * H * K / wall, "kernels": kt, "steps": steps,
+                     "workspace_bytes": ws.numel()}
+        print("bench: backward %s %.3f ms/call" % (name, wall * 1e3), file=sys.stderr,
+              flush=True)
+        del ws, w, up
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -515,6 +589,11 @@ def main():
                     help="skip the other operators (single-to-pair, tied attention, window table)")
     ap.add_argument("--only-ops", action="store_true",
                     help="time only the other operators (for profiler runs); prints their record")
+    ap.add_argument("--backward", default="1,4a",
+                    help="workloads whose backward pass is timed and reported under "
+                         "'backward' (comma separated; empty for none)")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only the backward pass of --backward (for profiler runs)")
     ap.add_argument("--cache-bytes", type=float, default=768e6,
                     help="input copies are added until they exceed this")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -546,6 +625,10 @@ def main():
     if args.only_ops:
         print(json.dumps({"ops": measure_ops(args.steps, args.warmup)}))
         return
+    bwd_names = [x for x in args.backward.split(",") if x]
+    if args.only_backward:
+        print(json.dumps({"backward": measure_backward(bwd_names, args.steps, args.warmup)}))
+        return
     head = measure(args.config, args.steps, args.warmup, args.cache_bytes, args.graph,
                    args.pack_per_call)
     print("bench: config %s %.4f ms/step" % (args.config, head["ms_per_step"]),
@@ -560,6 +643,7 @@ def main():
               flush=True)
 
     ops = None if args.no_ops else measure_ops(args.also_steps)
+    bwd = measure_backward(bwd_names, 20, 3) if bwd_names else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -583,6 +667,7 @@ def main():
         "cpu_baseline": cpu,
         "configs": others,
         "ops": ops,
+        "backward": bwd,
     }
     print(json.dumps(line))
 
