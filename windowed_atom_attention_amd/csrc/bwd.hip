@@ -147,7 +147,7 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
 // Sequenced launches that stop at the first failure.
 struct Run {
     hipStream_t s;
-    float *part;
+    Scratch sc;
     hipError_t err = hipSuccess;
     void ok(hipError_t e) {
         if (err == hipSuccess && e != hipSuccess)
@@ -157,7 +157,7 @@ struct Run {
     void mm(int M, int N, int K, Mat A, Mat B, float *C, int64_t ldc, float beta = 0.0f,
             const float *bias = nullptr) {
         if (err == hipSuccess)
-            ok(gemm(M, N, K, A, B, View{C, ldc}, beta, bias, part, kGemmPartialFloats, s));
+            ok(gemm(M, N, K, A, B, View{C, ldc}, beta, bias, sc, s));
     }
     void e(EwOp op, int rows, int W, float *o, int64_t ldo, const float *a, int64_t lda,
            const float *b = nullptr, int64_t ldb = 0, const float *c = nullptr, int64_t ldc = 0,
@@ -168,7 +168,7 @@ struct Run {
     }
     void cs(int rows, int W, const float *X, int64_t ldx, const float *Y, int64_t ldy, float *out) {
         if (err == hipSuccess && out)
-            ok(colsum(rows, W, view(X, ldx), view(Y, ldy), out, 0.0f, part, kGemmPartialFloats, s));
+            ok(colsum(rows, W, view(X, ldx), view(Y, ldy), out, 0.0f, sc, s));
     }
     void norm(int mode, int rows, int W, float eps, const float *x, float *xh, float *r) {
         if (err == hipSuccess)
@@ -199,39 +199,48 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     const bool af3 = style == ATOM_ATTN_AF3, dec = stage == ATOM_ATTN_DECODER;
     const int nm = af3 ? 0 : 1; // row normalisation: LayerNorm (AF3) / RMS (ESMFold2)
     const int C6 = 6 * C;
-    Run r{s, b.part};
+    Run r{s, Scratch{b.part, kGemmPartialFloats}};
 
     // ---------------------------------------------------------- recompute
     ProfSpan sp = prof_begin(KN_BWD_RECOMPUTE, s);
+    // parameters in fp32: used in place when stored as fp32, else widened
+    auto prm = [&](const void *src, int64_t n, float *&dst) {
+        if (!src)
+            return;
+        if (dtype == ATOM_ATTN_F32)
+            dst = const_cast<float *>(static_cast<const float *>(src));
+        else
+            r.cvt(src, dtype, n, dst);
+    };
     if (af3) {
-        r.cvt(par->cond_scale, dtype, 3 * S, b.cs);
-        r.cvt(par->w_scale, dtype, 3 * (int64_t)S * C, b.ws);
-        r.cvt(par->b_scale, dtype, 3 * C, b.bs);
-        r.cvt(par->w_shift, dtype, 3 * (int64_t)S * C, b.wsh);
-        r.cvt(par->w_residual_gate, dtype, 2 * (int64_t)S * C, b.wrg);
-        r.cvt(par->b_residual_gate, dtype, 2 * C, b.brg);
-        r.cvt(par->b_q, dtype, HD, b.bq);
-        r.cvt(par->pair_scale, dtype, V, b.ps);
-        r.cvt(par->w_pair, dtype, (int64_t)V * H, b.wp);
+        prm(par->cond_scale, 3 * S, b.cs);
+        prm(par->w_scale, 3 * (int64_t)S * C, b.ws);
+        prm(par->b_scale, 3 * C, b.bs);
+        prm(par->w_shift, 3 * (int64_t)S * C, b.wsh);
+        prm(par->w_residual_gate, 2 * (int64_t)S * C, b.wrg);
+        prm(par->b_residual_gate, 2 * C, b.brg);
+        prm(par->b_q, HD, b.bq);
+        prm(par->pair_scale, V, b.ps);
+        prm(par->w_pair, (int64_t)V * H, b.wp);
     } else {
-        r.cvt(par->w_mod, dtype, (int64_t)S * C6, b.wmod);
+        prm(par->w_mod, (int64_t)S * C6, b.wmod);
     }
-    r.cvt(par->w_q, dtype, (int64_t)C * HD, b.wq);
-    r.cvt(par->w_k, dtype, (int64_t)C * HD, b.wk);
-    r.cvt(par->w_v, dtype, (int64_t)C * HD, b.wv);
-    r.cvt(par->w_value_gate, dtype, (int64_t)C * HD, b.wvg);
-    r.cvt(par->w_attention_out, dtype, (int64_t)HD * C, b.wao);
-    r.cvt(par->w_ff_gate, dtype, (int64_t)C * M, b.ffg);
-    r.cvt(par->w_ff_up, dtype, (int64_t)C * M, b.ffu);
-    r.cvt(par->w_ff_out, dtype, (int64_t)M * C, b.ffo);
+    prm(par->w_q, (int64_t)C * HD, b.wq);
+    prm(par->w_k, (int64_t)C * HD, b.wk);
+    prm(par->w_v, (int64_t)C * HD, b.wv);
+    prm(par->w_value_gate, (int64_t)C * HD, b.wvg);
+    prm(par->w_attention_out, (int64_t)HD * C, b.wao);
+    prm(par->w_ff_gate, (int64_t)C * M, b.ffg);
+    prm(par->w_ff_up, (int64_t)C * M, b.ffu);
+    prm(par->w_ff_out, (int64_t)M * C, b.ffo);
     if (dec) {
-        r.cvt(par->w_token, dtype, (int64_t)U * C, b.wtok);
-        r.cvt(par->readout_scale, dtype, C, b.rs);
+        prm(par->w_token, (int64_t)U * C, b.wtok);
+        prm(par->readout_scale, C, b.rs);
         if (!af3)
-            r.cvt(par->readout_bias, dtype, C, b.rb);
-        r.cvt(par->w_readout, dtype, (int64_t)C * 3, b.wro);
+            prm(par->readout_bias, C, b.rb);
+        prm(par->w_readout, (int64_t)C * 3, b.wro);
     } else {
-        r.cvt(par->w_pool, dtype, (int64_t)C * U, b.wpool);
+        prm(par->w_pool, (int64_t)C * U, b.wpool);
     }
     const Dims dd{B, A, T, K, C, S, H, D, V, M, U};
     r.ok(launch_masks(dd, in->valid, in->token_valid, in->window_mask, in->atom_to_token,
@@ -305,6 +314,7 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.d_att = gout->attention; sa.d_o = b.dO; sa.dS = b.dS;
     sa.dq = b.dq; sa.dk = b.dk; sa.dv = b.dv; sa.d_pair = (af3 && gin) ? gin->pair : nullptr;
     sa.pw_partial = b.pwp; sa.count = b.cnt; sa.offset = b.off; sa.list = b.list;
+    sa.sc = r.sc;
     if (r.err == hipSuccess) {
         sp = prof_begin(KN_BWD_SLOT_FWD, s);
         r.ok(slot_fwd(sa, af3 ? STYLE_AF3 : STYLE_ESM, s));
@@ -603,6 +613,7 @@ int atom_attn_slot_backward_workspace_bytes(const atom_attn_dims *dims, int styl
     ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
     ar.get<float>(dims->V);                       // pair parameters in fp32
     ar.get<float>(dims->V * dims->H);
+    ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H)); // sums
     *bytes = ar.off + 256;
     return ATOM_ATTN_OK;
 }
@@ -645,6 +656,9 @@ int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int
     float *pwp = ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
     float *psf = ar.get<float>(dims->V);              // pair parameters in fp32
     float *wpf = ar.get<float>(dims->V * dims->H);
+    const size_t pcap = slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H);
+    float *cpart = ar.get<float>(pcap);
+    const Scratch sc{cpart, pcap};
     hipError_t e = hipSuccess;
     SlotBwdArgs sa{};
     sa.B = (int)dims->B; sa.A = (int)dims->A; sa.K = (int)dims->K; sa.H = (int)dims->H;
@@ -654,8 +668,8 @@ int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int
     sa.ps = psf; sa.wp = wpf; sa.P = attention ? attention : P; sa.o = o ? o : ob;
     sa.kid = kid; sa.d_att = d_attention; sa.d_o = d_o; sa.dS = dS; sa.dq = dq; sa.dk = dk;
     sa.dv = dv; sa.d_pair = af3 ? d_pair : nullptr; sa.pw_partial = pwp; sa.count = cnt;
-    sa.offset = off; sa.list = list;
-    if (af3) {
+    sa.offset = off; sa.list = list; sa.sc = sc;
+    if (af3 && e == hipSuccess) {
         e = to_f32(pair_scale, dtype, 1, (int)dims->V, dims->V, psf, nullptr, s);
         if (e == hipSuccess)
             e = to_f32(w_pair, dtype, 1, (int)(dims->V * dims->H), dims->V * dims->H, wpf,

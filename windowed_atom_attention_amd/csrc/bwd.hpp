@@ -31,17 +31,23 @@ struct Mat {
 inline Mat mat(const float *p, int64_t ld) { return Mat{p, ld, 1}; }
 inline Mat mat_t(const float *p, int64_t ld) { return Mat{p, 1, ld}; }
 
-// C[M, N] = beta * C + A[M, K] B[K, N] (+ bias[N]); beta is 0 or 1. Long
-// reductions are split over workgroups into `partial` (floats, `cap`
-// available) and summed in a fixed order, so results are deterministic.
-hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const float *bias,
-                float *partial, size_t cap, hipStream_t s);
-// Floats of partial sums any gemm call of the backward pass may use.
+// Scratch of the products and column sums: `partial` (cap floats) for
+// split reductions.
+struct Scratch {
+    float *partial;
+    size_t cap;
+};
 constexpr size_t kGemmPartialFloats = (size_t)8 << 20;
 
+// C[M, N] = beta * C + A[M, K] B[K, N] (+ bias[N]); beta is 0 or 1. Long
+// reductions are split over workgroups and summed in a fixed order, so
+// results are deterministic.
+hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const float *bias,
+                Scratch sc, hipStream_t s);
+
 // out[c] = beta * out[c] + sum_r X[r, c] (* Y[r, c] when Y.p), c < W.
-hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, float *partial,
-                  size_t cap, hipStream_t s);
+hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scratch sc,
+                  hipStream_t s);
 
 // Elementwise operations over rows x W (o = op, or o += op when acc).
 enum EwOp {
@@ -147,6 +153,7 @@ struct SlotBwdArgs {
     float *d_pair;            // [B,A,K,V] or null
     float *pw_partial;        // per-workgroup sums for d_pair_scale / d_w_pair
     int32_t *count, *offset, *list;
+    Scratch sc;               // column-sum scratch
 };
 int slot_bwd_supported(int K, int H, int D, int V, int style);
 hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s);

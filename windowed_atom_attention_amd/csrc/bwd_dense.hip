@@ -25,59 +25,108 @@ struct GemmK {
     int64_t ldc;
     const float *bias;
     float beta;
-    int M, N, K, kchunk;
-    float *partial; // split mode: partial[z][M][N], no beta / bias
+    int M, N, K, kchunk, splits;
+    int avec, bvec;  // 16-byte loads along the operand's contiguous axis
+    float *partial;  // split mode: partial[z][M][N]
 };
 
-// 64x64 output tile per workgroup, four waves of 32x32 (v_mfma_f32_32x32x2_f32),
-// 16-deep k steps staged through LDS with the next step prefetched into
-// registers. Tile loads follow whichever operand axis is contiguous.
+constexpr int kKS = 32; // k depth of one LDS stage
+
+// Eight consecutive elements of a row (stride 1) starting at `idx` of a
+// length-`lim` axis: two 16-byte loads when allowed and whole, else
+// guarded scalar loads.
+__device__ __forceinline__ void load8(const float *p, int idx, int lim, bool vec, float *r) {
+    if (vec && idx + 7 < lim) {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = idx + i < lim ? p[i] : 0.0f;
+    }
+}
+
+// 64x64 output tile per workgroup, four waves of 32x32 (v_mfma_f32_32x32x2_f32).
+// k advances in 32-deep stages staged through LDS; the next stage's operand
+// tiles are loaded into registers while the current one is multiplied.
+// Each thread moves 8 consecutive elements of an operand's contiguous axis.
+// Split k: every workgroup writes its partial tile; k_gemm_reduce sums
+// them in split order.
 __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
-    __shared__ float As[16][68];
-    __shared__ float Bs[16][68];
+    __shared__ float As[kKS][68];
+    __shared__ float Bs[kKS][68];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
     const int kb = blockIdx.z * g.kchunk;
     const int ke = min(g.K, kb + g.kchunk);
     const bool a_k = g.acs == 1;
     const bool b_n = g.bcs == 1;
-    float ra[4], rb[4];
+    float ra[8], rb[8];
     auto load = [&](int k0) {
+        if (a_k) {
+            // row m, 8 consecutive k
+            const int m = t >> 2, kq = (t & 3) * 8;
+            const int gm = m0 + m, gk = k0 + kq;
+            if (gm < g.M)
+                load8(g.A + (int64_t)gm * g.ars + gk, gk, ke, g.avec, ra);
+            else
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int m, k;
-            if (a_k) {
-                m = t >> 2;
-                k = (t & 3) * 4 + i;
+                for (int i = 0; i < 8; ++i) ra[i] = 0.0f;
+        } else {
+            // column k, 8 consecutive m (stride ars)
+            const int k = t >> 3, mq = (t & 7) * 8;
+            const int gk = k0 + k, gm = m0 + mq;
+            if (gk < ke) {
+                if (g.ars == 1)
+                    load8(g.A + (int64_t)gk * g.acs + gm, gm, g.M, g.avec, ra);
+                else
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        ra[i] = gm + i < g.M ? g.A[(int64_t)(gm + i) * g.ars + (int64_t)gk * g.acs] : 0.0f;
             } else {
-                k = t >> 4;
-                m = (t & 15) * 4 + i;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ra[i] = 0.0f;
             }
-            const int gm = m0 + m, gk = k0 + k;
-            ra[i] = (gm < g.M && gk < ke) ? g.A[(int64_t)gm * g.ars + (int64_t)gk * g.acs] : 0.0f;
-            int n, kk;
-            if (b_n) {
-                kk = t >> 4;
-                n = (t & 15) * 4 + i;
+        }
+        if (b_n) {
+            // row k, 8 consecutive n
+            const int k = t >> 3, nq = (t & 7) * 8;
+            const int gk = k0 + k, gn = n0 + nq;
+            if (gk < ke)
+                load8(g.B + (int64_t)gk * g.brs + gn, gn, g.N, g.bvec, rb);
+            else
+#pragma unroll
+                for (int i = 0; i < 8; ++i) rb[i] = 0.0f;
+        } else {
+            // column n, 8 consecutive k (stride brs)
+            const int n = t >> 2, kq = (t & 3) * 8;
+            const int gn = n0 + n, gk = k0 + kq;
+            if (gn < g.N) {
+                if (g.brs == 1)
+                    load8(g.B + (int64_t)gn * g.bcs + gk, gk, ke, g.bvec, rb);
+                else
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        rb[i] = gk + i < ke ? g.B[(int64_t)(gk + i) * g.brs + (int64_t)gn * g.bcs] : 0.0f;
             } else {
-                n = t >> 2;
-                kk = (t & 3) * 4 + i;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) rb[i] = 0.0f;
             }
-            const int gn = n0 + n, gk2 = k0 + kk;
-            rb[i] = (gn < g.N && gk2 < ke) ? g.B[(int64_t)gk2 * g.brs + (int64_t)gn * g.bcs] : 0.0f;
         }
     };
     auto store = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             if (a_k)
-                As[(t & 3) * 4 + i][t >> 2] = ra[i];
+                As[(t & 3) * 8 + i][t >> 2] = ra[i];
             else
-                As[t >> 4][(t & 15) * 4 + i] = ra[i];
+                As[t >> 3][(t & 7) * 8 + i] = ra[i];
             if (b_n)
-                Bs[t >> 4][(t & 15) * 4 + i] = rb[i];
+                Bs[t >> 3][(t & 7) * 8 + i] = rb[i];
             else
-                Bs[(t & 3) * 4 + i][t >> 2] = rb[i];
+                Bs[(t & 3) * 8 + i][t >> 2] = rb[i];
         }
     };
     f32x16_t acc = zero16();
@@ -85,46 +134,54 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
     const int half = lane >> 5, l32 = lane & 31;
     if (kb < ke)
         load(kb);
-    for (int k0 = kb; k0 < ke; k0 += 16) {
+    for (int k0 = kb; k0 < ke; k0 += kKS) {
         __syncthreads();
         store();
         __syncthreads();
-        if (k0 + 16 < ke)
-            load(k0 + 16);
+        if (k0 + kKS < ke)
+            load(k0 + kKS);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
+        for (int kk = 0; kk < kKS / 2; ++kk) {
             const float a = As[kk * 2 + half][wm + l32];
             const float b = Bs[kk * 2 + half][wn + l32];
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
     }
     const int c = n0 + wn + l32;
+    if (g.splits == 1) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm + acc32_row(v, lane);
-        if (r >= g.M || c >= g.N)
-            continue;
-        if (g.partial) {
-            g.partial[((int64_t)blockIdx.z * g.M + r) * g.N + c] = acc[v];
-        } else {
+        for (int v = 0; v < 16; ++v) {
+            const int r = m0 + wm + acc32_row(v, lane);
+            if (r >= g.M || c >= g.N)
+                continue;
             float x = acc[v];
             if (g.bias)
                 x += g.bias[c];
             float *dst = g.C + (int64_t)r * g.ldc + c;
             *dst = g.beta != 0.0f ? *dst + x : x;
         }
+        return;
+    }
+    const int64_t MN = (int64_t)g.M * g.N;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm + acc32_row(v, lane);
+        if (r < g.M && c < g.N)
+            g.partial[(int64_t)blockIdx.z * MN + (int64_t)r * g.N + c] = acc[v];
     }
 }
 
-// C = beta*C + bias + sum over splits, in split order.
-__global__ __launch_bounds__(256) void k_gemm_reduce(GemmK g, int splits) {
+// C = beta*C + bias + sum over splits, in split order (a kernel of its own:
+// the partial tiles of other workgroups become visible at the launch
+// boundary, with no device-wide fence inside a kernel).
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmK g) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t MN = (int64_t)g.M * g.N;
     if (i >= MN)
         return;
     const int r = (int)(i / g.N), c = (int)(i - (int64_t)r * g.N);
     float x = 0.0f;
-    for (int z = 0; z < splits; ++z)
+    for (int z = 0; z < g.splits; ++z)
         x += g.partial[(int64_t)z * MN + i];
     if (g.bias)
         x += g.bias[c];
@@ -534,54 +591,51 @@ inline unsigned nblk(int64_t n, int per) { return (unsigned)((n + per - 1) / per
 } // namespace
 
 hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const float *bias,
-                float *partial, size_t cap, hipStream_t s) {
+                Scratch sc, hipStream_t s) {
     if (M <= 0 || N <= 0)
         return hipSuccess;
-    GemmK g{A.p, A.rs, A.cs, B.p, B.rs, B.cs, C.p, C.ld, bias, beta, M, N, K, 0, nullptr};
-    if (K <= 0) {
-        // an empty product: C = beta*C + bias
-        g.partial = nullptr;
-        g.kchunk = 16;
-        hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), 1), dim3(256), 0, s, g);
-        return hipGetLastError();
-    }
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+    GemmK g{A.p, A.rs, A.cs, B.p, B.rs, B.cs, C.p, C.ld, bias, beta, M, N, K, 0, 1, 0, 0,
+            nullptr};
+    // 16-byte loads: contiguous axis stride 1, base and the other stride
+    // 16-byte aligned
+    g.avec = al16(A.p) && ((A.cs == 1 && A.rs % 4 == 0) || (A.rs == 1 && A.cs % 4 == 0));
+    g.bvec = al16(B.p) && ((B.cs == 1 && B.rs % 4 == 0) || (B.rs == 1 && B.cs % 4 == 0));
     const int64_t tiles = (int64_t)nblk(M, 64) * nblk(N, 64);
+    // split only long reductions (parameter gradients over every atom)
     int64_t splits = 1;
-    if (partial && tiles < 512 && K > 256) {
-        splits = std::min<int64_t>((512 + tiles - 1) / tiles, (K + 255) / 256);
-        splits = std::min<int64_t>(splits, (int64_t)(cap / ((size_t)M * N)));
+    if (sc.partial && tiles < 256 && K >= 1024) {
+        splits = std::min<int64_t>((512 + tiles - 1) / tiles, K / 256);
+        splits = std::min<int64_t>(splits, (int64_t)(sc.cap / ((size_t)M * N)));
         if (splits < 2)
             splits = 1;
     }
-    int64_t kchunk = (K + splits - 1) / splits;
-    kchunk = (kchunk + 15) / 16 * 16;
-    splits = (K + kchunk - 1) / kchunk;
+    int64_t kchunk = std::max<int64_t>(1, (K + splits - 1) / splits);
+    kchunk = (kchunk + kKS - 1) / kKS * kKS;
+    splits = K > 0 ? (K + kchunk - 1) / kchunk : 1;
     g.kchunk = (int)kchunk;
-    if (splits > 1) {
-        g.partial = partial;
-        hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), (unsigned)splits), dim3(256),
-                           0, s, g);
-        hipLaunchKernelGGL(k_gemm_reduce, dim3(nblk((int64_t)M * N, 256)), dim3(256), 0, s, g,
-                           (int)splits);
-    } else {
-        hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), 1), dim3(256), 0, s, g);
-    }
+    g.splits = (int)splits;
+    if (splits > 1)
+        g.partial = sc.partial;
+    hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), (unsigned)splits), dim3(256), 0,
+                       s, g);
+    if (splits > 1)
+        hipLaunchKernelGGL(k_gemm_reduce, dim3(nblk((int64_t)M * N, 256)), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
-hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, float *partial,
-                  size_t cap, hipStream_t s) {
+hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scratch sc,
+                  hipStream_t s) {
     if (W <= 0)
         return hipSuccess;
-    int64_t splits = std::max<int64_t>(1, std::min<int64_t>((rows + 255) / 256, 1024));
-    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (int64_t)(cap / (size_t)W)));
-    const int rows_per = (int)((rows + splits - 1) / splits);
+    int64_t splits = std::max<int64_t>(1, std::min<int64_t>((rows + 127) / 128, 1024));
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (int64_t)(sc.cap / (size_t)W)));
+    const int rows_per = std::max(1, (int)((rows + splits - 1) / splits));
     splits = rows > 0 ? (rows + rows_per - 1) / rows_per : 1;
     hipLaunchKernelGGL(k_colsum, dim3(nblk(W, 64), (unsigned)splits), dim3(256), 0, s, rows, W,
-                       (const float *)X.p, X.ld, (const float *)Y.p, Y.ld, partial,
-                       std::max(rows_per, 1));
+                       (const float *)X.p, X.ld, (const float *)Y.p, Y.ld, sc.partial, rows_per);
     hipLaunchKernelGGL(k_colsum_reduce, dim3(nblk(W, 256)), dim3(256), 0, s, W, (int)splits,
-                       (const float *)partial, out, beta);
+                       (const float *)sc.partial, out, beta);
     return hipGetLastError();
 }
 

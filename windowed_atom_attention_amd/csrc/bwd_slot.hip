@@ -67,12 +67,68 @@ __device__ __forceinline__ float pair_ln(float *x, int V, float eps) {
     return r;
 }
 
-template <typename TP, bool AF3>
+// sum over slots s (in order within each lane group) of w[s] times the
+// D channels at rows[kid[s] * HD + off ..]: lane group g = lane / (D/4)
+// takes slots g, g + 256/D, ...; its lanes hold one float4 of channels each
+// and issue four slots' loads before using them. The groups' partial sums
+// are added by lane exchanges; every lane returns its float4 of the total
+// (channels 4 * (lane % (D/4)) ..).
+template <int D>
+__device__ __forceinline__ float4 slot_rowsum(const float *w, const int *kid, int K,
+                                              const float *rows, int HD, int off, int lane) {
+    constexpr int L4 = D / 4, SP = 64 / L4;
+    const int g = lane / L4, q = lane - g * L4;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s0 = 0; s0 < K; s0 += 4 * SP) {
+        float4 r[4];
+        float ww[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + u * SP + g;
+            ww[u] = s < K ? w[s] : 0.0f;
+            r[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (ww[u] != 0.0f)
+                r[u] = *reinterpret_cast<const float4 *>(rows + (int64_t)kid[s] * HD + off + q * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc.x += ww[u] * r[u].x;
+            acc.y += ww[u] * r[u].y;
+            acc.z += ww[u] * r[u].z;
+            acc.w += ww[u] * r[u].w;
+        }
+    }
+#pragma unroll
+    for (int o = L4; o < 64; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o);
+        acc.y += __shfl_xor(acc.y, o);
+        acc.z += __shfl_xor(acc.z, o);
+        acc.w += __shfl_xor(acc.w, o);
+    }
+    return acc;
+}
+
+// dot of the D channels at row[0..D) (global, 16-byte aligned) with v[0..D)
+// (LDS), all loads issued first.
+template <int D>
+__device__ __forceinline__ float row_dot(const float *row, const float *v) {
+    float4 r[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+        r[i] = reinterpret_cast<const float4 *>(row)[i];
+    float x = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+        x += v[4 * i] * r[i].x + v[4 * i + 1] * r[i].y + v[4 * i + 2] * r[i].z + v[4 * i + 3] * r[i].w;
+    return x;
+}
+
+template <typename TP, bool AF3, int D>
 __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
     extern __shared__ float smem[];
     const SlotBwdArgs &a = p.a;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int K = a.K, H = a.H, D = a.D, HD = H * D;
+    const int K = a.K, H = a.H, HD = H * D;
     float *base = smem + w * wave_floats(K, H, HD);
     int *skid = reinterpret_cast<int *>(base);
     float *sbeta = base + K;
@@ -116,7 +172,6 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
         sq[i] = a.q[nn * HD + i];
     __syncthreads();
 
-    const int G = 64 / D, grp = lane / D, dd = lane - grp * D;
     for (int h = 0; h < H; ++h) {
         float l[kMaxK / 64];
         float mx = -INFINITY;
@@ -125,13 +180,7 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
             const int s = lane + 64 * c;
             l[c] = -INFINITY;
             if (s < K && skid[s] >= 0) {
-                const float4 *kr = reinterpret_cast<const float4 *>(a.k + (int64_t)skid[s] * HD + h * D);
-                float dot = 0.0f;
-                for (int d4 = 0; d4 < D / 4; ++d4) {
-                    const float4 kv = kr[d4];
-                    const float *qv = sq + h * D + d4 * 4;
-                    dot += qv[0] * kv.x + qv[1] * kv.y + qv[2] * kv.z + qv[3] * kv.w;
-                }
+                const float dot = row_dot<D>(a.k + (int64_t)skid[s] * HD + h * D, sq + h * D);
                 l[c] = dot * p.inv_sqrt_d + (AF3 ? sbeta[s * H + h] : 0.0f);
                 mx = fmaxf(mx, l[c]);
             }
@@ -159,27 +208,20 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
             }
         }
         __syncthreads();
-        float acc = 0.0f;
-        for (int s = grp; s < K; s += G) {
-            const float pw = sP[s];
-            if (pw != 0.0f)
-                acc += pw * a.v[(int64_t)skid[s] * HD + h * D + dd];
-        }
-        for (int off = D; off < 64; off <<= 1)
-            acc += __shfl_xor(acc, off);
-        if (live && grp == 0)
-            a.o[nn * HD + h * D + dd] = acc;
+        const float4 acc = slot_rowsum<D>(sP, skid, K, a.v, HD, h * D, lane);
+        if (live && lane < D / 4)
+            *reinterpret_cast<float4 *>(a.o + nn * HD + h * D + lane * 4) = acc;
         __syncthreads();
     }
 }
 
-template <typename TP, bool AF3>
+template <typename TP, bool AF3, int D>
 __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     extern __shared__ float smem[];
     __shared__ float wred[4][kPairV + kPairV * kPairH];
     const SlotBwdArgs &a = p.a;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int K = a.K, H = a.H, D = a.D, HD = H * D;
+    const int K = a.K, H = a.H, HD = H * D;
     float *base = smem + w * wave_floats(K, H, HD);
     int *skid = reinterpret_cast<int *>(base);
     float *sdl = base + K;
@@ -197,7 +239,6 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
         sdo[i] = a.d_o[nn * HD + i];
     __syncthreads();
 
-    const int G = 64 / D, grp = lane / D, dd = lane - grp * D;
     for (int h = 0; h < H; ++h) {
         const int64_t rowbase = ((b * H + h) * a.A + qa) * K;
         float pw[kMaxK / 64], dw[kMaxK / 64];
@@ -210,14 +251,8 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
             if (s < K && skid[s] >= 0) {
                 pw[c] = a.P[rowbase + s];
                 float x = a.d_att ? a.d_att[rowbase + s] : 0.0f;
-                if (pw[c] != 0.0f) {
-                    const float4 *vr = reinterpret_cast<const float4 *>(a.v + (int64_t)skid[s] * HD + h * D);
-                    for (int d4 = 0; d4 < D / 4; ++d4) {
-                        const float4 vv = vr[d4];
-                        const float *ov = sdo + h * D + d4 * 4;
-                        x += ov[0] * vv.x + ov[1] * vv.y + ov[2] * vv.z + ov[3] * vv.w;
-                    }
-                }
+                if (pw[c] != 0.0f)
+                    x += row_dot<D>(a.v + (int64_t)skid[s] * HD + h * D, sdo + h * D);
                 dw[c] = x;
                 dsum += pw[c] * x;
             }
@@ -235,16 +270,14 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
             }
         }
         __syncthreads();
-        float acc = 0.0f;
-        for (int s = grp; s < K; s += G) {
-            const float dl = sP[s];
-            if (dl != 0.0f)
-                acc += dl * a.k[(int64_t)skid[s] * HD + h * D + dd];
+        float4 acc = slot_rowsum<D>(sP, skid, K, a.k, HD, h * D, lane);
+        if (live && lane < D / 4) {
+            acc.x *= p.inv_sqrt_d;
+            acc.y *= p.inv_sqrt_d;
+            acc.z *= p.inv_sqrt_d;
+            acc.w *= p.inv_sqrt_d;
+            *reinterpret_cast<float4 *>(a.dq + nn * HD + h * D + lane * 4) = acc;
         }
-        for (int off = D; off < 64; off <<= 1)
-            acc += __shfl_xor(acc, off);
-        if (live && grp == 0)
-            a.dq[nn * HD + h * D + dd] = acc * p.inv_sqrt_d;
         __syncthreads();
     }
 
@@ -318,7 +351,11 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     }
 }
 
-// One wave per key atom: its list of (query, slot) entries in order.
+// One wave per key atom, over its list of (query, slot) entries in order.
+// A lane holds one float4 of the H*D channels (all in one head); the wave
+// takes EPP = 64 / (HD/4) entries per pass (one per lane group) and four
+// passes' loads are issued before they are used. The groups' sums are
+// added in group order at the end.
 __global__ __launch_bounds__(256) void k_slot_bwd_kv(SK p) {
     const SlotBwdArgs &a = p.a;
     const int lane = threadIdx.x & 63;
@@ -327,35 +364,56 @@ __global__ __launch_bounds__(256) void k_slot_bwd_kv(SK p) {
     if (j >= N)
         return;
     const int K = a.K, H = a.H, D = a.D, HD = H * D;
-    float ak[kMaxHD / 64], av[kMaxHD / 64];
-#pragma unroll
-    for (int i = 0; i < kMaxHD / 64; ++i) {
-        ak[i] = 0.0f;
-        av[i] = 0.0f;
-    }
+    const int LPE = HD / 4, EPP = 64 / LPE;
+    const int g = lane / LPE, q = lane - g * LPE;
+    const bool act = g < EPP;
+    const int h = (q * 4) / D;
+    float4 ak = make_float4(0.0f, 0.0f, 0.0f, 0.0f), av = ak;
     const int beg = a.offset[j], end = a.offset[j + 1];
-    for (int it = beg; it < end; ++it) {
-        const int64_t e = a.list[it];
-        const int64_t n = e / K, s = e - n * K;
-        const int64_t b = n / a.A, qa = n - b * a.A;
+    for (int base = beg; base < end; base += 64) {
+        const int cnt = min(64, end - base);
+        const int le = lane < cnt ? a.list[base + lane] : 0;
+        for (int u0 = 0; u0 < cnt; u0 += 4 * EPP) {
+            float4 rq[4], ro[4];
+            float ws[4], wp[4];
 #pragma unroll
-        for (int i = 0; i < kMaxHD / 64; ++i) {
-            const int c = lane + 64 * i;
-            if (c < HD) {
-                const int h = c / D;
-                const int64_t at = ((b * H + h) * a.A + qa) * K + s;
-                ak[i] += a.dS[at] * a.q[n * HD + c];
-                av[i] += a.P[at] * a.d_o[n * HD + c];
+            for (int u = 0; u < 4; ++u) {
+                const int idx = u0 + u * EPP + g;
+                const int64_t e = __shfl(le, idx < 64 ? idx : 0);
+                ws[u] = wp[u] = 0.0f;
+                rq[u] = ro[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (act && idx < cnt) {
+                    const int64_t n = e / K, s = e - n * K;
+                    const int64_t b = n / a.A, qa = n - b * a.A;
+                    const int64_t at = ((b * H + h) * a.A + qa) * K + s;
+                    ws[u] = a.dS[at];
+                    wp[u] = a.P[at];
+                    rq[u] = *reinterpret_cast<const float4 *>(a.q + n * HD + q * 4);
+                    ro[u] = *reinterpret_cast<const float4 *>(a.d_o + n * HD + q * 4);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ak.x += ws[u] * rq[u].x; ak.y += ws[u] * rq[u].y;
+                ak.z += ws[u] * rq[u].z; ak.w += ws[u] * rq[u].w;
+                av.x += wp[u] * ro[u].x; av.y += wp[u] * ro[u].y;
+                av.z += wp[u] * ro[u].z; av.w += wp[u] * ro[u].w;
             }
         }
     }
-#pragma unroll
-    for (int i = 0; i < kMaxHD / 64; ++i) {
-        const int c = lane + 64 * i;
-        if (c < HD) {
-            a.dk[j * HD + c] = ak[i] * p.inv_sqrt_d;
-            a.dv[j * HD + c] = av[i];
-        }
+    // groups' sums in group order, into the lanes of group 0
+    float4 tk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), tv = tk;
+    for (int gg = 0; gg < EPP; ++gg) {
+        const int src = gg * LPE + q;
+        tk.x += __shfl(ak.x, src); tk.y += __shfl(ak.y, src);
+        tk.z += __shfl(ak.z, src); tk.w += __shfl(ak.w, src);
+        tv.x += __shfl(av.x, src); tv.y += __shfl(av.y, src);
+        tv.z += __shfl(av.z, src); tv.w += __shfl(av.w, src);
+    }
+    if (g == 0) {
+        tk.x *= p.inv_sqrt_d; tk.y *= p.inv_sqrt_d; tk.z *= p.inv_sqrt_d; tk.w *= p.inv_sqrt_d;
+        *reinterpret_cast<float4 *>(a.dk + j * HD + q * 4) = tk;
+        *reinterpret_cast<float4 *>(a.dv + j * HD + q * 4) = tv;
     }
 }
 
@@ -382,7 +440,39 @@ int slot_bwd_supported(int K, int H, int D, int V, int style) {
 size_t slot_bwd_partial_floats(int64_t rows, int V, int H) {
     (void)V;
     (void)H;
-    return 2 * (size_t)nblk(rows, 4) * (kPairV + kPairV * kPairH);
+    return (size_t)nblk(rows, 4) * (kPairV + kPairV * kPairH) + 256;
+}
+
+template <int D>
+void launch_fwd(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
+    if (style == STYLE_AF3) {
+        if (p.a.pair_dtype == 1) {
+            set_lds(k_slot_fwd<bf16_t, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_fwd<bf16_t, true, D>), grid, dim3(256), lds, s, p);
+        } else {
+            set_lds(k_slot_fwd<float, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_fwd<float, true, D>), grid, dim3(256), lds, s, p);
+        }
+    } else {
+        set_lds(k_slot_fwd<float, false, D>, lds);
+        hipLaunchKernelGGL((k_slot_fwd<float, false, D>), grid, dim3(256), lds, s, p);
+    }
+}
+
+template <int D>
+void launch_bwd_q(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
+    if (style == STYLE_AF3) {
+        if (p.a.pair_dtype == 1) {
+            set_lds(k_slot_bwd_q<bf16_t, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_bwd_q<bf16_t, true, D>), grid, dim3(256), lds, s, p);
+        } else {
+            set_lds(k_slot_bwd_q<float, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_bwd_q<float, true, D>), grid, dim3(256), lds, s, p);
+        }
+    } else {
+        set_lds(k_slot_bwd_q<float, false, D>, lds);
+        hipLaunchKernelGGL((k_slot_bwd_q<float, false, D>), grid, dim3(256), lds, s, p);
+    }
 }
 
 hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s) {
@@ -392,17 +482,12 @@ hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s) {
     SK p{a, 1.0f / sqrtf((float)a.D)};
     const size_t lds = 4 * sizeof(float) * (size_t)wave_floats(a.K, a.H, a.H * a.D);
     const dim3 grid(nblk(N, 4));
-    if (style == STYLE_AF3) {
-        if (a.pair_dtype == 1) {
-            set_lds(k_slot_fwd<bf16_t, true>, lds);
-            hipLaunchKernelGGL((k_slot_fwd<bf16_t, true>), grid, dim3(256), lds, s, p);
-        } else {
-            set_lds(k_slot_fwd<float, true>, lds);
-            hipLaunchKernelGGL((k_slot_fwd<float, true>), grid, dim3(256), lds, s, p);
-        }
-    } else {
-        set_lds(k_slot_fwd<float, false>, lds);
-        hipLaunchKernelGGL((k_slot_fwd<float, false>), grid, dim3(256), lds, s, p);
+    switch (a.D) {
+    case 8: launch_fwd<8>(p, style, lds, grid, s); break;
+    case 16: launch_fwd<16>(p, style, lds, grid, s); break;
+    case 32: launch_fwd<32>(p, style, lds, grid, s); break;
+    case 64: launch_fwd<64>(p, style, lds, grid, s); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -416,43 +501,32 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
     const size_t lds = 4 * sizeof(float) * (size_t)wave_floats(a.K, a.H, a.H * a.D);
     const dim3 grid(nblk(N, 4));
     ProfSpan sp = prof_begin(KN_BWD_SLOT_Q, s);
-    if (style == STYLE_AF3) {
-        if (a.pair_dtype == 1) {
-            set_lds(k_slot_bwd_q<bf16_t, true>, lds);
-            hipLaunchKernelGGL((k_slot_bwd_q<bf16_t, true>), grid, dim3(256), lds, s, p);
-        } else {
-            set_lds(k_slot_bwd_q<float, true>, lds);
-            hipLaunchKernelGGL((k_slot_bwd_q<float, true>), grid, dim3(256), lds, s, p);
-        }
-    } else {
-        set_lds(k_slot_bwd_q<float, false>, lds);
-        hipLaunchKernelGGL((k_slot_bwd_q<float, false>), grid, dim3(256), lds, s, p);
+    switch (a.D) {
+    case 8: launch_bwd_q<8>(p, style, lds, grid, s); break;
+    case 16: launch_bwd_q<16>(p, style, lds, grid, s); break;
+    case 32: launch_bwd_q<32>(p, style, lds, grid, s); break;
+    case 64: launch_bwd_q<64>(p, style, lds, grid, s); break;
+    default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     prof_end(sp, s);
     if (style == STYLE_AF3 && (d_pair_scale || d_w_pair)) {
-        // sum the per-workgroup partials in workgroup order
+        // sum the per-workgroup partials in workgroup order, then pick the
+        // [V] and [V][H] blocks out of the padded record
         constexpr int W = kPairV + kPairV * kPairH;
         const int rows = (int)grid.x;
-        float *tmp = a.pw_partial + (size_t)rows * W; // room for colsum partials
-        const size_t cap = (size_t)rows * W;
-        if (d_pair_scale) {
-            e = colsum(rows, a.V, view(a.pw_partial, W), View{nullptr, 0}, d_pair_scale, 0.0f,
-                       tmp, cap, s);
-            if (e != hipSuccess)
-                return e;
-        }
-        if (d_w_pair) {
-            // gradient of w_pair [V][H] from the [V][kPairH] block of the partials
-            for (int v = 0; v < a.V; ++v) {
-                e = colsum(rows, a.H, view(a.pw_partial + kPairV + v * kPairH, W),
-                           View{nullptr, 0}, d_w_pair + v * a.H, 0.0f, tmp, cap, s);
-                if (e != hipSuccess)
-                    return e;
-            }
-        }
+        float *sums = a.pw_partial + (size_t)rows * W;
+        e = colsum(rows, W, view(a.pw_partial, W), View{nullptr, 0}, sums, 0.0f, a.sc, s);
+        if (e == hipSuccess && d_pair_scale)
+            e = ew(EW_COPY, 1, a.V, View{d_pair_scale, a.V}, view(sums, kPairV), View{nullptr, 0},
+                   View{nullptr, 0}, nullptr, nullptr, 0, s);
+        if (e == hipSuccess && d_w_pair)
+            e = ew(EW_COPY, a.V, a.H, View{d_w_pair, a.H}, view(sums + kPairV, kPairH),
+                   View{nullptr, 0}, View{nullptr, 0}, nullptr, nullptr, 0, s);
+        if (e != hipSuccess)
+            return e;
     }
     sp = prof_begin(KN_BWD_SLOT_KV, s);
     e = reverse_index(a.kid, N * a.K, (int)N, a.count, a.offset, a.list, s);
