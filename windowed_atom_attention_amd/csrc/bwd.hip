@@ -13,6 +13,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <unordered_map>
 
 #include "../../include/atom_attn.h"
 #include "bwd.hpp"
@@ -63,14 +65,14 @@ struct Bufs {
     uint8_t *usable, *allowed;
     int32_t *tcount;
     // recomputed forward
-    float *tok, *tokproj, *x0, *c, *ch, *rc, *cj, *sig[3], *mu[3], *gr[2], *mods, *sc;
+    float *tok, *tokproj, *x0, *c, *ch, *rc, *cj[3], *sig[3], *mu[3], *gr[2], *mods, *sc;
     float *xh0, *r0, *qin, *kvin, *qraw, *kraw, *rcos, *rsin, *q, *k, *v, *g, *P, *o;
     int32_t *kid;
     float *og, *uu, *x1, *xh1, *r1, *z, *fa, *fb, *hh, *tr, *hid, *proj, *xhh, *rh, *lnh;
     // backward
     float *dh, *dx2, *dtr, *dgT, *dhh, *da, *dbb, *dz, *dx1, *gt, *du, *dgA, *dog, *dO, *dGp;
-    float *dS, *dq, *dk, *dv, *dqin, *dkvin, *dx0, *dzs[3], *dzg[2], *dcj, *dch, *dc, *dmods,
-        *ds, *dpu, *dln, *dtp, *dP, *pwp, *part;
+    float *dS, *dq, *dk, *dv, *dqin, *dkvin, *dx0, *dzs[3], *dzg[2], *dcj[3], *dch, *dc, *dmods,
+        *ds, *dpu, *dln, *dtp, *dP, *pwp, *part, *part2;
     int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list;
 };
 
@@ -102,7 +104,8 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
     }
     b.x0 = f(N * C); b.c = f(N * S); b.xh0 = f(N * C); b.r0 = f(N); b.qin = f(N * C);
     if (af3) {
-        b.ch = f(N * S); b.rc = f(N); b.cj = f(N * S);
+        b.ch = f(N * S); b.rc = f(N);
+        for (int j = 0; j < 3; ++j) b.cj[j] = f(N * S);
         for (int j = 0; j < 3; ++j) { b.sig[j] = f(N * C); b.mu[j] = f(N * C); }
         for (int j = 0; j < 2; ++j) b.gr[j] = f(N * C);
         b.kvin = f(N * C);
@@ -128,7 +131,8 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
     if (af3) {
         for (int j = 0; j < 3; ++j) b.dzs[j] = f(N * C);
         for (int j = 0; j < 2; ++j) b.dzg[j] = f(N * C);
-        b.dcj = f(N * S); b.dch = f(N * S);
+        for (int j = 0; j < 3; ++j) b.dcj[j] = f(N * S);
+        b.dch = f(N * S);
     } else {
         b.dmods = f(N * 6 * C); b.ds = f(N * S);
     }
@@ -142,13 +146,69 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
     b.cnt = ar.get<int32_t>(N); b.off = ar.get<int32_t>(N + 1); b.list = ar.get<int32_t>(E);
     b.pwp = f(slot_bwd_partial_floats((int64_t)N, (int)V, (int)H));
     b.part = f(kGemmPartialFloats);
+    b.part2 = f(kGemmPartialFloats);
+}
+
+// A second stream per device for the parameter gradients: every product
+// or column sum whose result is a parameter gradient is a leaf of the
+// chain rule (nothing downstream reads it), so it can run beside the main
+// chain. Default priority; fork and join through events.
+struct Side {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex enqueue; // one backward call at a time enqueues on a device
+};
+Side *side_stream() {
+    static std::mutex mu;
+    static std::unordered_map<int, Side *> per_dev;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    Side *&x = per_dev[dev];
+    if (!x) {
+        Side *n = new Side();
+        if (hipStreamCreateWithFlags(&n->s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&n->fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&n->join, hipEventDisableTiming) != hipSuccess)
+            return nullptr; // (leaked on failure; the call then stays on one stream)
+        x = n;
+    }
+    return x;
 }
 
 // Sequenced launches that stop at the first failure.
 struct Run {
     hipStream_t s;
     Scratch sc;
+    Side *side = nullptr; // null: leaves run on the main stream
+    Scratch sc2{};
     hipError_t err = hipSuccess;
+    // make the side stream wait for everything enqueued on the main stream
+    void fork() {
+        if (side && err == hipSuccess) {
+            ok(hipEventRecord(side->fork, s));
+            ok(hipStreamWaitEvent(side->s, side->fork, 0));
+        }
+    }
+    void join() {
+        if (side) {
+            ok(hipEventRecord(side->join, side->s));
+            ok(hipStreamWaitEvent(s, side->join, 0));
+        }
+    }
+    // a parameter-gradient product / column sum (after a fork)
+    void leaf_mm(int M, int N, int K, Mat A, Mat B, float *C, int64_t ldc) {
+        if (err == hipSuccess && C)
+            ok(gemm(M, N, K, A, B, View{C, ldc}, 0.0f, nullptr, side ? sc2 : sc,
+                    side ? side->s : s));
+    }
+    void leaf_cs(int rows, int W, const float *X, int64_t ldx, const float *Y, int64_t ldy,
+                 float *out) {
+        if (err == hipSuccess && out)
+            ok(colsum(rows, W, view(X, ldx), view(Y, ldy), out, 0.0f, side ? sc2 : sc,
+                      side ? side->s : s));
+    }
     void ok(hipError_t e) {
         if (err == hipSuccess && e != hipSuccess)
             err = e;
@@ -200,6 +260,13 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     const int nm = af3 ? 0 : 1; // row normalisation: LayerNorm (AF3) / RMS (ESMFold2)
     const int C6 = 6 * C;
     Run r{s, Scratch{b.part, kGemmPartialFloats}};
+    Side *side = side_stream();
+    std::unique_lock<std::mutex> lk;
+    if (side) {
+        lk = std::unique_lock<std::mutex>(side->enqueue);
+        r.side = side;
+        r.sc2 = Scratch{b.part2, kGemmPartialFloats};
+    }
 
     // ---------------------------------------------------------- recompute
     ProfSpan sp = prof_begin(KN_BWD_RECOMPUTE, s);
@@ -258,10 +325,10 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     if (af3) {
         r.norm(0, N, S, eps, b.c, b.ch, b.rc);
         for (int j = 0; j < 3; ++j) {
-            r.e(EW_MUL_VEC, N, S, b.cj, S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + j * S);
-            r.mm(N, C, S, mat(b.cj, S), mat(b.ws + (size_t)j * S * C, C), b.sig[j], C);
+            r.e(EW_MUL_VEC, N, S, b.cj[j], S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + j * S);
+            r.mm(N, C, S, mat(b.cj[j], S), mat(b.ws + (size_t)j * S * C, C), b.sig[j], C);
             r.e(EW_SIGMOID_VEC, N, C, b.sig[j], C, b.sig[j], C, nullptr, 0, nullptr, 0, b.bs + j * C);
-            r.mm(N, C, S, mat(b.cj, S), mat(b.wsh + (size_t)j * S * C, C), b.mu[j], C);
+            r.mm(N, C, S, mat(b.cj[j], S), mat(b.wsh + (size_t)j * S * C, C), b.mu[j], C);
         }
         for (int j = 0; j < 2; ++j) {
             r.mm(N, C, S, mat(b.c, S), mat(b.wrg + (size_t)j * S * C, C), b.gr[j], C);
@@ -356,9 +423,9 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
             if (r.err == hipSuccess)
                 r.ok(pool_bwd(B, A, T, U, b.usable, in->atom_to_token, b.tcount,
                               gout->token_output, b.proj, b.dP, s));
+            r.fork();
+            r.leaf_mm(C, U, N, mat_t(b.hid, C), mat(b.dP, U), dwpool, U);
             r.mm(N, C, U, mat(b.dP, U), mat_t(b.wpool, U), b.dh, C, 1.0f);
-            if (dwpool)
-                r.mm(C, U, N, mat_t(b.hid, C), mat(b.dP, U), dwpool, U);
         } else if (dwpool) {
             r.e(EW_ZERO, C, U, dwpool, U, nullptr, 0);
         }
@@ -369,11 +436,11 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
         if (gout->position_update) {
             r.e(EW_MASK, N, 3, b.dpu, 3, gout->position_update, 3, nullptr, 0, nullptr, 0, nullptr,
                 b.usable);
-            if (dwro)
-                r.mm(C, 3, N, mat_t(b.lnh, C), mat(b.dpu, 3), dwro, 3);
             r.mm(N, C, 3, mat(b.dpu, 3), mat_t(b.wro, 3), b.dln, C);
-            r.cs(N, C, b.dln, C, b.xhh, C, drs);
-            r.cs(N, C, b.dln, C, nullptr, 0, drb);
+            r.fork();
+            r.leaf_mm(C, 3, N, mat_t(b.lnh, C), mat(b.dpu, 3), dwro, 3);
+            r.leaf_cs(N, C, b.dln, C, b.xhh, C, drs);
+            r.leaf_cs(N, C, b.dln, C, nullptr, 0, drb);
             r.e(EW_MUL_VEC, N, C, b.gt, C, b.dln, C, nullptr, 0, nullptr, 0, b.rs);
             r.norm_bwd(0, N, C, b.xhh, b.rh, b.gt, b.dh, 1);
         } else {
@@ -390,17 +457,16 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     r.e(EW_MUL, N, C, b.dtr, C, b.dx2, C, gT, ldg);
     r.e(EW_MUL, N, C, b.dgT, C, b.dx2, C, b.tr, C);
     // transition
+    r.fork();
+    r.leaf_mm(M, C, N, mat_t(b.hh, M), mat(b.dtr, C), gpar ? gpar->w_ff_out : nullptr, C);
     r.mm(N, M, C, mat(b.dtr, C), mat_t(b.ffo, C), b.dhh, M);
-    if (gpar && gpar->w_ff_out)
-        r.mm(M, C, N, mat_t(b.hh, M), mat(b.dtr, C), gpar->w_ff_out, C);
     r.e(EW_DSWIGLU_A, N, M, b.da, M, b.dhh, M, b.fa, M, b.fb, M);
     r.e(EW_DSWIGLU_B, N, M, b.dbb, M, b.dhh, M, b.fa, M);
+    r.fork();
+    r.leaf_mm(C, M, N, mat_t(b.z, C), mat(b.da, M), gpar ? gpar->w_ff_gate : nullptr, M);
+    r.leaf_mm(C, M, N, mat_t(b.z, C), mat(b.dbb, M), gpar ? gpar->w_ff_up : nullptr, M);
     r.mm(N, C, M, mat(b.da, M), mat_t(b.ffg, M), b.dz, C);
     r.mm(N, C, M, mat(b.dbb, M), mat_t(b.ffu, M), b.dz, C, 1.0f);
-    if (gpar && gpar->w_ff_gate)
-        r.mm(C, M, N, mat_t(b.z, C), mat(b.da, M), gpar->w_ff_gate, M);
-    if (gpar && gpar->w_ff_up)
-        r.mm(C, M, N, mat_t(b.z, C), mat(b.dbb, M), gpar->w_ff_up, M);
     // transition norm
     r.e(EW_COPY, N, C, b.dx1, C, b.dx2, C);
     if (af3) {
@@ -424,9 +490,9 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
         r.e(EW_COPY, N, C, b.dmods + 5 * C, C6, b.dgT, C);
     }
     // output projection and value gate
+    r.fork();
+    r.leaf_mm(HD, C, N, mat_t(b.og, HD), mat(b.du, C), gpar ? gpar->w_attention_out : nullptr, C);
     r.mm(N, HD, C, mat(b.du, C), mat_t(b.wao, C), b.dog, HD);
-    if (gpar && gpar->w_attention_out)
-        r.mm(HD, C, N, mat_t(b.og, HD), mat(b.du, C), gpar->w_attention_out, C);
     r.e(EW_MUL, N, HD, b.dO, HD, b.dog, HD, b.g, HD);
     r.e(EW_DGATE, N, HD, b.dGp, HD, b.dog, HD, b.o, HD, b.g, HD);
     prof_end(sp, s);
@@ -438,22 +504,19 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     if (!af3 && r.err == hipSuccess)
         r.ok(head_rope_bwd(N, H, D, eps, b.qraw, b.kraw, cs_f, sn_f, b.dq, b.dk, dcos, dsin, s));
     // projections
+    if (gpar) {
+        r.fork();
+        r.leaf_mm(C, HD, N, mat_t(b.qin, C), mat(b.dq, HD), gpar->w_q, HD);
+        if (af3)
+            r.leaf_cs(N, HD, b.dq, HD, nullptr, 0, gpar->b_q);
+        r.leaf_mm(C, HD, N, mat_t(b.qin, C), mat(b.dGp, HD), gpar->w_value_gate, HD);
+        r.leaf_mm(C, HD, N, mat_t(b.kvin, C), mat(b.dk, HD), gpar->w_k, HD);
+        r.leaf_mm(C, HD, N, mat_t(b.kvin, C), mat(b.dv, HD), gpar->w_v, HD);
+    }
     r.mm(N, C, HD, mat(b.dq, HD), mat_t(b.wq, HD), b.dqin, C);
     r.mm(N, C, HD, mat(b.dGp, HD), mat_t(b.wvg, HD), b.dqin, C, 1.0f);
     r.mm(N, C, HD, mat(b.dk, HD), mat_t(b.wk, HD), b.dkvin, C);
     r.mm(N, C, HD, mat(b.dv, HD), mat_t(b.wv, HD), b.dkvin, C, 1.0f);
-    if (gpar) {
-        if (gpar->w_q)
-            r.mm(C, HD, N, mat_t(b.qin, C), mat(b.dq, HD), gpar->w_q, HD);
-        if (af3)
-            r.cs(N, HD, b.dq, HD, nullptr, 0, gpar->b_q);
-        if (gpar->w_value_gate)
-            r.mm(C, HD, N, mat_t(b.qin, C), mat(b.dGp, HD), gpar->w_value_gate, HD);
-        if (gpar->w_k)
-            r.mm(C, HD, N, mat_t(b.kvin, C), mat(b.dk, HD), gpar->w_k, HD);
-        if (gpar->w_v)
-            r.mm(C, HD, N, mat_t(b.kvin, C), mat(b.dv, HD), gpar->w_v, HD);
-    }
     // modulated norms
     r.e(EW_COPY, N, C, b.dx0, C, b.dx1, C);
     if (af3) {
@@ -473,33 +536,42 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     // conditioning
     if (af3) {
         const float *dmu[3] = {b.dqin, b.dkvin, b.dz};
+        if (gpar) {
+            r.fork();
+            for (int j = 0; j < 3; ++j) {
+                r.leaf_mm(S, C, N, mat_t(b.cj[j], S), mat(b.dzs[j], C),
+                          gpar->w_scale ? gpar->w_scale + (size_t)j * S * C : nullptr, C);
+                r.leaf_mm(S, C, N, mat_t(b.cj[j], S), mat(dmu[j], C),
+                          gpar->w_shift ? gpar->w_shift + (size_t)j * S * C : nullptr, C);
+                r.leaf_cs(N, C, b.dzs[j], C, nullptr, 0,
+                          gpar->b_scale ? gpar->b_scale + j * C : nullptr);
+            }
+            for (int j = 0; j < 2; ++j) {
+                r.leaf_mm(S, C, N, mat_t(b.c, S), mat(b.dzg[j], C),
+                          gpar->w_residual_gate ? gpar->w_residual_gate + (size_t)j * S * C : nullptr, C);
+                r.leaf_cs(N, C, b.dzg[j], C, nullptr, 0,
+                          gpar->b_residual_gate ? gpar->b_residual_gate + j * C : nullptr);
+            }
+        }
         for (int j = 0; j < 3; ++j) {
-            r.e(EW_MUL_VEC, N, S, b.cj, S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + j * S);
-            if (gpar && gpar->w_scale)
-                r.mm(S, C, N, mat_t(b.cj, S), mat(b.dzs[j], C), gpar->w_scale + (size_t)j * S * C, C);
-            if (gpar && gpar->w_shift)
-                r.mm(S, C, N, mat_t(b.cj, S), mat(dmu[j], C), gpar->w_shift + (size_t)j * S * C, C);
-            if (gpar && gpar->b_scale)
-                r.cs(N, C, b.dzs[j], C, nullptr, 0, gpar->b_scale + j * C);
-            r.mm(N, S, C, mat(b.dzs[j], C), mat_t(b.ws + (size_t)j * S * C, C), b.dcj, S);
-            r.mm(N, S, C, mat(dmu[j], C), mat_t(b.wsh + (size_t)j * S * C, C), b.dcj, S, 1.0f);
-            if (gpar && gpar->cond_scale)
-                r.cs(N, S, b.dcj, S, b.ch, S, gpar->cond_scale + j * S);
-            r.e(EW_MUL_VEC, N, S, b.dch, S, b.dcj, S, nullptr, 0, nullptr, 0, b.cs + j * S, nullptr,
+            r.mm(N, S, C, mat(b.dzs[j], C), mat_t(b.ws + (size_t)j * S * C, C), b.dcj[j], S);
+            r.mm(N, S, C, mat(dmu[j], C), mat_t(b.wsh + (size_t)j * S * C, C), b.dcj[j], S, 1.0f);
+            r.e(EW_MUL_VEC, N, S, b.dch, S, b.dcj[j], S, nullptr, 0, nullptr, 0, b.cs + j * S, nullptr,
                 j > 0 ? 1 : 0);
         }
-        r.norm_bwd(0, N, S, b.ch, b.rc, b.dch, b.dc, 0);
-        for (int j = 0; j < 2; ++j) {
-            if (gpar && gpar->w_residual_gate)
-                r.mm(S, C, N, mat_t(b.c, S), mat(b.dzg[j], C),
-                     gpar->w_residual_gate + (size_t)j * S * C, C);
-            if (gpar && gpar->b_residual_gate)
-                r.cs(N, C, b.dzg[j], C, nullptr, 0, gpar->b_residual_gate + j * C);
-            r.mm(N, S, C, mat(b.dzg[j], C), mat_t(b.wrg + (size_t)j * S * C, C), b.dc, S, 1.0f);
+        if (gpar && gpar->cond_scale) {
+            r.fork();
+            for (int j = 0; j < 3; ++j)
+                r.leaf_cs(N, S, b.dcj[j], S, b.ch, S, gpar->cond_scale + j * S);
         }
+        r.norm_bwd(0, N, S, b.ch, b.rc, b.dch, b.dc, 0);
+        for (int j = 0; j < 2; ++j)
+            r.mm(N, S, C, mat(b.dzg[j], C), mat_t(b.wrg + (size_t)j * S * C, C), b.dc, S, 1.0f);
     } else {
-        if (gpar && gpar->w_mod)
-            r.mm(S, C6, N, mat_t(b.sc, S), mat(b.dmods, C6), gpar->w_mod, C6);
+        if (gpar && gpar->w_mod) {
+            r.fork();
+            r.leaf_mm(S, C6, N, mat_t(b.sc, S), mat(b.dmods, C6), gpar->w_mod, C6);
+        }
         r.mm(N, S, C6, mat(b.dmods, C6), mat_t(b.wmod, C6), b.ds, S);
         r.e(EW_DSILU, N, S, b.dc, S, b.ds, S, b.c, S);
     }
@@ -514,11 +586,14 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
             r.ok(reverse_index(b.tkey, N, BT, b.tcnt, b.toff, b.tlist, s));
         if (r.err == hipSuccess)
             r.ok(segment_sum(BT, C, b.toff, b.tlist, b.dx0, b.dtp, s));
+        if (gpar && gpar->w_token) {
+            r.fork();
+            r.leaf_mm(U, C, BT, mat_t(b.tok, U), mat(b.dtp, C), gpar->w_token, C);
+        }
         if (gin && gin->token)
             r.mm(BT, U, C, mat(b.dtp, C), mat_t(b.wtok, C), gin->token, U);
-        if (gpar && gpar->w_token)
-            r.mm(U, C, BT, mat_t(b.tok, U), mat(b.dtp, C), gpar->w_token, C);
     }
+    r.join();
     prof_end(sp, s);
     return r.err == hipSuccess ? ATOM_ATTN_OK : ATOM_ATTN_ELAUNCH;
 }
