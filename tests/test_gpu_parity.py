@@ -64,6 +64,14 @@ SMALL = [
     # as supplied)
     ("2", dict(A=300, rope="distinct")),
     ("4b", dict(A=400, rope="distinct", dtype=torch.float32, stage="decoder")),
+    # scattered key ids over thousands of atoms: query blocks whose key band
+    # spans more than eight 128-row chunks are computed by the gather kernel
+    ("0", dict(A=2000, K=64)),
+    ("0", dict(A=1500, K=48, style="esmfold2", dtype=torch.bfloat16, stage="decoder")),
+    ("0", dict(A=2500, K=40, dtype=torch.bfloat16)),   # AF3 pair bias precomputed
+    ("0", dict(A=9000, K=24, dtype=torch.bfloat16)),   # AF3 pair bias from the pair rows
+    ("0", dict(A=2000, K=32, H=2, D=128, V=16, dtype=torch.bfloat16)),
+    ("0", dict(A=2100, K=20, style="esmfold2", H=8, D=16)),
 ]
 
 
@@ -585,3 +593,49 @@ def test_tied_row_attention_full_size():
     got = tied_row_attention(cu(acts), cu(par))
     torch.cuda.synchronize()
     _tied_check(acts, par, got, RTOL[torch.bfloat16])
+
+
+def test_mixed_local_and_scattered_key_tables():
+    """One call whose first atoms use local windows (slot kernel) and whose
+    later atoms select keys anywhere in the batch (gather kernel)."""
+    w = make_workload("1", A=3000)
+    ki = w.structure["key_index"].clone()
+    g = torch.Generator().manual_seed(3)
+    ki[:, 1504:] = torch.randint(-1, 3000, ki[:, 1504:].shape, generator=g)
+    w.structure["key_index"] = ki
+    gpu = run_gpu(w)
+    ref = oracle.block(**w.kwargs(), intermediates=True)
+    exact_zero_checks(w, gpu, ref["usable"], ref["allowed"])
+    compare_block(w, gpu, ref)
+
+
+@pytest.mark.parametrize("style", ["af3", "esmfold2"])
+def test_slot_attention_step_scattered_keys(style):
+    w = make_workload("4a" if style == "af3" else "4b", A=2000, dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(8)
+    ki = torch.randint(-2, 2002, w.structure["key_index"].shape, generator=g)
+    ki[:, :, 1] = ki[:, :, 0]
+    ref_masks = oracle.block(**w.kwargs(), intermediates=True)
+    B, A, H = w.dims["B"], w.dims["A"], w.dims["H"]
+    HD = H * w.dims["D"]
+    q, k, v = (torch.randn((B, A, HD), generator=g).to(torch.bfloat16) for _ in range(3))
+    usable = torch.from_numpy(ref_masks["usable"]).bool()
+    pair = pair_scale = w_pair = None
+    if style == "af3":
+        # the recipe's NaN rows sit on its own missing slots; with the new
+        # ids some of those slots are allowed, so give every row a value
+        pair = torch.nan_to_num(w.activations["pair"], nan=0.5)
+        pair_scale, w_pair = w.parameters["pair_scale"], w.parameters["w_pair"]
+    kw = dict(eps=w.eps, style=style, radius=-1)
+    ref = oracle.slot_attention(q, k, v, usable, ki, w.masks["window_mask"], heads=H,
+                                pair=pair, pair_scale=pair_scale, w_pair=w_pair, **kw)
+    cu = lambda t: None if t is None else t.cuda()
+    att, o = gpu_slot_attention(cu(q), cu(k), cu(v), cu(usable), cu(ki),
+                                cu(w.masks["window_mask"]), heads=H, pair=cu(pair),
+                                pair_scale=cu(pair_scale), w_pair=cu(w_pair), **kw)
+    rtol = RTOL[torch.bfloat16]
+    al = ref["allowed"].astype(bool)
+    attn = np64(att)
+    assert np.all(attn[np.broadcast_to(~al[:, None], attn.shape)] == 0.0)
+    assert_close_rel("attention", attn, ref["attention"], rtol)
+    assert_close("o", np64(o), ref["o"], rtol)

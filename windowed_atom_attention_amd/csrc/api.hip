@@ -32,8 +32,8 @@ struct Profiler {
                              "post", "pool", "masks", "s2p_token", "s2p_pair",
                              "window", "tied_bias", "tied_proj", "tied_logits",
                              "tied_softmax", "tied_out", "bwd_recompute", "bwd_slot_fwd",
-                             "bwd_slot_q", "bwd_slot_kv", "bwd_chain"};
-    int nnames = 20;
+                             "bwd_slot_q", "bwd_slot_kv", "bwd_chain", "slot_gather"};
+    int nnames = 21;
 };
 Profiler g_prof;
 
@@ -192,7 +192,7 @@ int shape_supported(const atom_attn_dims *d, int style, int stage, int dtype) {
 // ------------------------------------------------------------ workspace
 
 struct Layout {
-    size_t packed, q, k, v, g, o, usable, tokproj, pool_sum, pool_int, pbias, total;
+    size_t packed, q, k, v, g, o, usable, tokproj, pool_sum, pool_int, pbias, vrows, wide, total;
     int64_t pack_units;
 };
 
@@ -299,6 +299,9 @@ Layout layout_of(const atom_attn_dims *d, int style, int stage, int dtype) {
     L.pbias = o;
     if (style == ATOM_ATTN_AF3)
         o = up256(o + N * (size_t)d->K * 16);
+    // row-major V and the queue of wide query blocks (slot gather path)
+    L.vrows = o; o = up256(o + N * rowb);
+    L.wide = o; o = up256(o + 4 * ((size_t)d->B * ((d->A + 15) / 16) + 1));
     L.total = o;
     return L;
 }
@@ -447,6 +450,8 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.pair_scale = par->pair_scale; a.w_pair = par->w_pair;
     a.nw8 = nw8 ? 1 : 0;
     a.pbias = af3 && prep_hosts_pair_bias(a.d, dt, st, sg) ? (float *)(ws + L.pbias) : nullptr;
+    a.vrows = ws + L.vrows;
+    a.wide = (int *)(ws + L.wide);
 
     SlotArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -459,6 +464,7 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.pair = in->pair; sa.pair_scale = par->pair_scale; sa.w_pair = par->w_pair;
     sa.pbias = a.pbias;
     sa.attention = out->attention; sa.o = a.o;
+    sa.wide = a.wide; sa.vrows = a.vrows;
 
     if (!prepacked &&
         (rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)
@@ -468,6 +474,9 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     if ((rc = timed(KN_PREP, s, [&] { return launch_prep(a, dt, st, sg, s); })) != ATOM_ATTN_OK)
         return rc;
     if ((rc = timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); })) != ATOM_ATTN_OK)
+        return rc;
+    if ((rc = timed(KN_SLOT_GATHER, s, [&] { return launch_slot_gather(sa, dt, st, s); })) !=
+        ATOM_ATTN_OK)
         return rc;
     if ((rc = timed(KN_POST, s, [&] { return launch_post(a, dt, st, sg, s); })) != ATOM_ATTN_OK)
         return rc;
@@ -648,7 +657,9 @@ int atom_attn_slot_workspace_bytes(const atom_attn_dims *dims, int dtype,
         (dtype != ATOM_ATTN_F32 && dtype != ATOM_ATTN_BF16))
         return ATOM_ATTN_EINVAL;
     const size_t esz = dtype == ATOM_ATTN_BF16 ? 2 : 4;
-    *bytes = up256((size_t)(dims->B * dims->H * dims->D) * vt_pitch((int)dims->A) * esz);
+    // transposed v, then the queue of wide query blocks
+    *bytes = up256((size_t)(dims->B * dims->H * dims->D) * vt_pitch((int)dims->A) * esz) +
+             up256(4 * ((size_t)dims->B * ((dims->A + 15) / 16) + 1));
     return ATOM_ATTN_OK;
 }
 
@@ -704,10 +715,17 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
     sa.q = q; sa.k = k; sa.v = workspace;
     sa.pair = pair; sa.pair_scale = pair_scale; sa.w_pair = w_pair;
     sa.attention = attention; sa.o = o;
+    const size_t vt_bytes = up256((size_t)(dims->B * dims->H * dims->D) * vt_pitch((int)dims->A) *
+                                  (dt ? 2 : 4));
+    sa.wide = (int *)((char *)workspace + vt_bytes);
+    sa.vrows = v; // the caller's rows serve the gather path
     hipStream_t s = (hipStream_t)stream;
-    if (launch_vt(v, usable, workspace, d.B, d.A, (int)HD, dt, s) != hipSuccess)
+    if (launch_vt(v, usable, workspace, d.B, d.A, (int)HD, dt, sa.wide, s) != hipSuccess)
         return ATOM_ATTN_ELAUNCH;
-    return timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); });
+    const int rc = timed(KN_SLOT, s, [&] { return launch_slot(sa, dt, st, s); });
+    if (rc != ATOM_ATTN_OK)
+        return rc;
+    return timed(KN_SLOT_GATHER, s, [&] { return launch_slot_gather(sa, dt, st, s); });
 }
 
 int atom_attn_profile_enable(int on) {

@@ -66,6 +66,10 @@ struct BlockArgs {
     // computes it from the pair rows itself
     const void *pair_scale, *w_pair;
     float *pbias;
+    // row-major copy of V ([B*A][H*D], storage dtype) for the slot step's
+    // gather path, and that path's queue (wide[0] = count, set to 0 here)
+    void *vrows;
+    int *wide;
     // outputs
     void *hidden, *attention, *token_output, *position_update;
     int32_t *status;
@@ -83,7 +87,14 @@ struct SlotArgs {
     // (then pair, pair_scale and w_pair are not read); null otherwise
     const float *pbias;
     void *attention, *o;
+    // query blocks whose key band spans more than kWideChunks chunks are
+    // queued here (wide[0] = count, zeroed before the slot kernel; wide[1..]
+    // = block ids) and computed by k_slot_gather from the row-major V copy
+    // vrows; null: every block stays in the slot kernel
+    int *wide;
+    const void *vrows;
 };
+constexpr int kWideChunks = 8;
 
 // Kernel timing with HIP events for the library's profiling mode (a no-op
 // unless atom_attn_profile_enable is on): prof_begin before a launch and
@@ -93,7 +104,7 @@ enum { KN_S2P_TOK = 7, KN_S2P_PAIR = 8, KN_WINDOW = 9, KN_TIED_BIAS = 10, KN_TIE
        // backward pass: forward recomputation, its slot step, the slot
        // backward (query side, reverse index + key side), the dense chain
        KN_BWD_RECOMPUTE = 15, KN_BWD_SLOT_FWD = 16, KN_BWD_SLOT_Q = 17, KN_BWD_SLOT_KV = 18,
-       KN_BWD_CHAIN = 19 };
+       KN_BWD_CHAIN = 19, KN_SLOT_GATHER = 20 };
 struct ProfSpan {
     int kernel = -1;
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -157,8 +168,13 @@ hipError_t launch_post(const BlockArgs &a, int dtype, int style, int stage,
                        hipStream_t s);
 hipError_t launch_pool(const BlockArgs &a, int dtype, hipStream_t s);
 hipError_t launch_slot(const SlotArgs &a, int dtype, int style, hipStream_t s);
+// the queued wide blocks of the last launch_slot (exits at once when none)
+hipError_t launch_slot_gather(const SlotArgs &a, int dtype, int style, hipStream_t s);
+size_t slot_gather_lds_bytes(int K, int H, int D);
+// transposed copy of v for the standalone slot step; also sets wide[0] = 0
+// when wide is not null
 hipError_t launch_vt(const void *v, const uint8_t *usable, void *vt, int B, int A,
-                     int HD, int dtype, hipStream_t s);
+                     int HD, int dtype, int *wide, hipStream_t s);
 hipError_t launch_masks(const Dims &d, const uint8_t *valid,
                         const uint8_t *token_valid, const uint8_t *window_mask,
                         const int64_t *atom_to_token, const int64_t *key_index,

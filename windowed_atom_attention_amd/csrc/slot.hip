@@ -60,8 +60,10 @@ hipError_t launch_slot(const SlotArgs &a0, int dtype, int style, hipStream_t s) 
 // NaN/Inf payload left in such a row would reach o as 0 * NaN.
 template <typename T>
 __global__ __launch_bounds__(256) void k_vt(const T *v, const uint8_t *usable, T *vt,
-                                            int B, int A, int HD, int pitch) {
+                                            int B, int A, int HD, int pitch, int *wide) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i == 0 && wide)
+        wide[0] = 0;
     const int64_t per = (int64_t)A * HD;
     if (i >= per * B)
         return;
@@ -76,15 +78,15 @@ __global__ __launch_bounds__(256) void k_vt(const T *v, const uint8_t *usable, T
 }
 
 hipError_t launch_vt(const void *v, const uint8_t *usable, void *vt, int B, int A,
-                     int HD, int dtype, hipStream_t s) {
+                     int HD, int dtype, int *wide, hipStream_t s) {
     const int64_t total = (int64_t)A * HD * B;
     const int64_t grid = (total + 255) / 256;
     if (dtype == 0)
         hipLaunchKernelGGL(k_vt<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const float *)v, usable, (float *)vt, B, A, HD, vt_pitch(A));
+                           (const float *)v, usable, (float *)vt, B, A, HD, vt_pitch(A), wide);
     else
         hipLaunchKernelGGL(k_vt<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const bf16_t *)v, usable, (bf16_t *)vt, B, A, HD, vt_pitch(A));
+                           (const bf16_t *)v, usable, (bf16_t *)vt, B, A, HD, vt_pitch(A), wide);
     return hipGetLastError();
 }
 

@@ -351,6 +351,13 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
     const int jal = s_lo & ~7; // band start, aligned for the transposed V rows
     const int span = jhi + 1 - jal;
     const int nch = (span + kRMAX - 1) / kRMAX;
+    if (p.wide && nch > kWideChunks) {
+        // scattered key ids: the band grows with their spread, not with K;
+        // the gather kernel takes this block
+        if (tid == 0)
+            p.wide[1 + atomicAdd(p.wide, 1)] = wg;
+        return;
+    }
     const float scale = p.inv_sqrt_d;
     float *twave = tile + hsl * kQB * L.sp; // this wave's head tile
     // Unique writer of each probability cell (query, key row): every
