@@ -450,7 +450,6 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     a.pair_scale = par->pair_scale; a.w_pair = par->w_pair;
     a.nw8 = nw8 ? 1 : 0;
     a.pbias = af3 && prep_hosts_pair_bias(a.d, dt, st, sg) ? (float *)(ws + L.pbias) : nullptr;
-    a.vrows = ws + L.vrows;
     a.wide = (int *)(ws + L.wide);
 
     SlotArgs sa;
@@ -464,7 +463,7 @@ int run_block(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.pair = in->pair; sa.pair_scale = par->pair_scale; sa.w_pair = par->w_pair;
     sa.pbias = a.pbias;
     sa.attention = out->attention; sa.o = a.o;
-    sa.wide = a.wide; sa.vrows = a.vrows;
+    sa.wide = a.wide; sa.vrows = ws + L.vrows; sa.vrows_out = ws + L.vrows;
 
     if (!prepacked &&
         (rc = timed(KN_PACK, s, [&] { return launch_pack(pa, dt, s); })) != ATOM_ATTN_OK)

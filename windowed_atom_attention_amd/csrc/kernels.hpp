@@ -66,9 +66,8 @@ struct BlockArgs {
     // computes it from the pair rows itself
     const void *pair_scale, *w_pair;
     float *pbias;
-    // row-major copy of V ([B*A][H*D], storage dtype) for the slot step's
-    // gather path, and that path's queue (wide[0] = count, set to 0 here)
-    void *vrows;
+    // the slot step's queue of wide query blocks (wide[0] = count, set to 0
+    // by the projection kernel)
     int *wide;
     // outputs
     void *hidden, *attention, *token_output, *position_update;
@@ -89,10 +88,13 @@ struct SlotArgs {
     void *attention, *o;
     // query blocks whose key band spans more than kWideChunks chunks are
     // queued here (wide[0] = count, zeroed before the slot kernel; wide[1..]
-    // = block ids) and computed by k_slot_gather from the row-major V copy
-    // vrows; null: every block stays in the slot kernel
+    // = block ids) and computed by k_slot_gather from row-major V rows
+    // vrows; null: every block stays in the slot kernel. vrows_out (may be
+    // null): the slot kernel writes each block's 16 V rows there, row-major,
+    // from the transposed copy (vrows then points to the same buffer).
     int *wide;
     const void *vrows;
+    void *vrows_out;
 };
 constexpr int kWideChunks = 8;
 

@@ -571,16 +571,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
     // copy: one 4-element vector store when the four atoms are consecutive
     // there (A a multiple of 4: same batch, aligned), else element by element
     const bool vt_vec = d.A % 4 == 0;
-    T *vrow = reinterpret_cast<T *>(p.vrows);
     auto store_v4 = [&](int r, int c, float v0, float v1, float v2, float v3) {
-        if (vrow) {
-            // row-major copy for the slot step's gather path
-            const float v[4] = {v0, v1, v2, v3};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (n0 + r + j < N)
-                    vrow[(int64_t)(n0 + r + j) * HD + c] = from_f<T>(v[j]);
-        }
         if (vt_vec && n0 + r + 3 < N) {
             T *dst = vo + vt_at(r, c);
             if constexpr (sizeof(T) == 2) {

@@ -176,6 +176,24 @@ __global__ __launch_bounds__(kQB * TQ, TQ == 32 ? 4 : (SPL >= 16 ? 2 : 3)) void 
             wmv[i] = false;
         }
     }
+    // ---- row-major copy of this block's V rows (for the gather path of
+    // other blocks): one 16-byte vector of one channel's consecutive atoms
+    // from the transposed copy per thread, stored element by element; the
+    // stores need no wait and overlap the loads below
+    if (p.vrows_out) {
+        constexpr int CH = kQB / E; // 16-byte vectors per channel
+        T *vrw = reinterpret_cast<T *>(p.vrows_out);
+        for (int t = tid; t < HD * CH; t += NT) {
+            const int c = t / CH, q0 = (t - c * CH) * E;
+            const uint4 vv = ld_off<uint4>(vtg + ((int64_t)b * HD + c) * vtp,
+                                           (uint32_t)(a0 + q0) * (uint32_t)sizeof(T));
+            const T *ve = reinterpret_cast<const T *>(&vv);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (a0 + q0 + e < A)
+                    vrw[(row0 + q0 + e) * HD + c] = ve[e];
+        }
+    }
     // ---- AF3 pair rows of this thread's slots, in groups of GS slots: the
     // first group (both, when there are two) is in flight from the start,
     // each later group while the previous one is reduced. Loads are issued
