@@ -43,6 +43,35 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}  # dense matrix peaks
 
 
+def wide_block_fraction(w):
+    """Fraction of 16-query blocks whose allowed key ids span more than eight
+    128-row chunks (from the 8-aligned band start), i.e. the blocks the slot
+    kernel hands to the gather kernel."""
+    import torch
+    ki = w.structure["key_index"]
+    B, A, K = ki.shape
+    T = w.masks["token_valid"].shape[-1]
+    a2t = w.structure["atom_to_token"]
+    usable = w.masks["valid"] & (a2t >= 0) & (a2t < T) & torch.gather(
+        w.masks["token_valid"], 1, a2t.clamp(0, T - 1))
+    jc = ki.clamp(0, A - 1)
+    uk = torch.gather(usable, 1, jc.reshape(B, A * K)).reshape(B, A, K)
+    ok = usable[..., None] & (ki >= 0) & (ki < A) & uk & w.masks["window_mask"]
+    if w.radius >= 0:
+        ok &= (jc - torch.arange(A)[None, :, None]).abs() <= w.radius
+    nqb = (A + 15) // 16
+    pad = nqb * 16 - A
+    big = torch.iinfo(torch.int64).max
+    lo = torch.where(ok, ki, torch.full_like(ki, big)).amin(-1)
+    hi = torch.where(ok, ki, torch.full_like(ki, -1)).amax(-1)
+    lo = torch.nn.functional.pad(lo, (0, pad), value=big).reshape(B, nqb, 16).amin(-1)
+    hi = torch.nn.functional.pad(hi, (0, pad), value=-1).reshape(B, nqb, 16).amax(-1)
+    has = hi >= 0
+    span = hi + 1 - (lo.clamp(max=A) & ~7)
+    nch = (span + 127) // 128
+    return float(((nch > 8) & has).sum()) / float(B * nqb)
+
+
 def kernel_work(w, split=False):
     """Algorithmic work per launch of each kernel: ('hbm', bytes) for the
     bandwidth-bound slot attention, ('mfma', flops) for the projections.
@@ -64,8 +93,15 @@ def kernel_work(w, split=False):
     else:
         prep = N * 2 * (2 * S * C + 4 * C * HD)
         post = N * 2 * (HD * C + S * C + 2 * S * C + 2 * C * M + M * C + S * C)
-    work = {"slot_attention": ("hbm", slot_bytes), "prep": ("mfma", prep),
+    # query blocks of 16 whose key band exceeds eight 128-row chunks take the
+    # gather kernel, where every slot reads its key's K row (fp32) and V row
+    wide = wide_block_fraction(w)
+    gather_bytes = (N * HD * 4 + E * HD * (4 + e) + 8 * E + E + N + pair
+                    + E * H * e + N * HD * e)
+    work = {"slot_attention": ("hbm", slot_bytes * (1.0 - wide)), "prep": ("mfma", prep),
             "post": ("mfma", post)}
+    if wide > 0:
+        work["slot_gather"] = ("hbm", gather_bytes * wide)
     if w.stage == "encoder":
         # the pooled projection runs inside post; the pool kernel only joins
         # tokens that cross 32-row tiles (reads the tile records, writes at
@@ -263,7 +299,9 @@ def cpu_baseline(name, seconds=12.0, seconds_1t=4.0):
 NAMES = {"0": "tiny AF3 encoder fp32", "1": "AF3 encoder fp32",
          "2": "ESMFold2 encoder bf16 radius 48", "3": "AF3 decoder bf16",
          "4a": "large mixed AF3 encoder bf16",
-         "4b": "large mixed ESMFold2 encoder bf16 radius 64"}
+         "4b": "large mixed ESMFold2 encoder bf16 radius 64",
+         "1r": "AF3 encoder fp32, scattered key ids",
+         "4r": "large AF3 encoder bf16, scattered key ids"}
 
 
 def measure(config, steps, warmup, cache_bytes, graph=False, pack_per_call=False):
@@ -581,7 +619,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="1",
                     help="workload of the headline line: 0, 1, 2, 3, 4a, 4b (default 1)")
-    ap.add_argument("--also", default="2,3,4a,4b",
+    ap.add_argument("--also", default="2,3,4a,4b,1r,4r",
                     help="further workloads timed in the same run and reported under "
                          "'configs' (comma separated; empty for none)")
     ap.add_argument("--also-steps", type=int, default=50)

@@ -100,6 +100,15 @@ CONFIGS = {
                A=24576, T=2048, K=128, C=128, S=128, V=16, H=4, D=32, M=256,
                U=384, radius=64, tokens="even", slots="window_miss10_dup5",
                bad="mixed8", seed=5),
+    # scattered key tables (ids uniform over the batch, 2 missing per row,
+    # window_mask Bernoulli(0.9)) at the sizes of workloads 1 and 4a
+    "1r": dict(style="af3", stage="encoder", dtype=torch.float32, B=1, A=4608,
+               T=384, K=128, C=128, S=128, V=16, H=4, D=32, M=256, U=384,
+               radius=-1, tokens="even", slots="random", bad="inf5", seed=11),
+    "4r": dict(style="af3", stage="encoder", dtype=torch.bfloat16, B=1,
+               A=24576, T=2048, K=128, C=128, S=128, V=16, H=4, D=32, M=256,
+               U=384, radius=-1, tokens="even", slots="random", bad="mixed8",
+               seed=14),
 }
 
 
