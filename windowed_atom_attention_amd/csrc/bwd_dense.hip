@@ -171,18 +171,26 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
     }
 }
 
-// C = beta*C + bias + sum over splits, in split order (a kernel of its own:
-// the partial tiles of other workgroups become visible at the launch
-// boundary, with no device-wide fence inside a kernel).
+// C = beta*C + bias + sum over splits (a kernel of its own: the partial
+// tiles of other workgroups become visible at the launch boundary, with no
+// device-wide fence inside a kernel). Eight lanes per output element: lane
+// l of the group sums splits l, l+8, ... in order, then the eight sums are
+// added by a fixed butterfly -- the same order on every call.
 __global__ __launch_bounds__(256) void k_gemm_reduce(GemmK g) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+    const int sub = threadIdx.x & 7;
     const int64_t MN = (int64_t)g.M * g.N;
-    if (i >= MN)
+    const bool live = i < MN;
+    float x = 0.0f;
+    if (live)
+        for (int z = sub; z < g.splits; z += 8)
+            x += g.partial[(int64_t)z * MN + i];
+    x += __shfl_xor(x, 1, 8);
+    x += __shfl_xor(x, 2, 8);
+    x += __shfl_xor(x, 4, 8);
+    if (!live || sub != 0)
         return;
     const int r = (int)(i / g.N), c = (int)(i - (int64_t)r * g.N);
-    float x = 0.0f;
-    for (int z = 0; z < g.splits; ++z)
-        x += g.partial[(int64_t)z * MN + i];
     if (g.bias)
         x += g.bias[c];
     float *dst = g.C + (int64_t)r * g.ldc + c;
@@ -213,15 +221,19 @@ __global__ __launch_bounds__(256) void k_colsum(int rows, int W, const float *X,
             ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
 }
 
+// One wave per column: lane l sums splits l, l+64, ... in order, then a
+// fixed butterfly adds the lanes.
 __global__ __launch_bounds__(256) void k_colsum_reduce(int W, int splits, const float *partial,
                                                        float *out, float beta) {
-    const int col = blockIdx.x * 256 + threadIdx.x;
+    const int col = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (col >= W)
         return;
     float x = 0.0f;
-    for (int z = 0; z < splits; ++z)
+    for (int z = lane; z < splits; z += 64)
         x += partial[(int64_t)z * W + col];
-    out[col] = beta != 0.0f ? out[col] + x : x;
+    x = group_sum<64>(x);
+    if (lane == 0)
+        out[col] = beta != 0.0f ? out[col] + x : x;
 }
 
 // ------------------------------------------------------------- elementwise
@@ -620,7 +632,7 @@ hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const flo
     hipLaunchKernelGGL(k_gemm, dim3(nblk(N, 64), nblk(M, 64), (unsigned)splits), dim3(256), 0,
                        s, g);
     if (splits > 1)
-        hipLaunchKernelGGL(k_gemm_reduce, dim3(nblk((int64_t)M * N, 256)), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(k_gemm_reduce, dim3(nblk((int64_t)M * N * 8, 256)), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
@@ -634,7 +646,7 @@ hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scrat
     splits = rows > 0 ? (rows + rows_per - 1) / rows_per : 1;
     hipLaunchKernelGGL(k_colsum, dim3(nblk(W, 64), (unsigned)splits), dim3(256), 0, s, rows, W,
                        (const float *)X.p, X.ld, (const float *)Y.p, Y.ld, sc.partial, rows_per);
-    hipLaunchKernelGGL(k_colsum_reduce, dim3(nblk(W, 256)), dim3(256), 0, s, W, (int)splits,
+    hipLaunchKernelGGL(k_colsum_reduce, dim3(nblk(W, 4)), dim3(256), 0, s, W, (int)splits,
                        (const float *)sc.partial, out, beta);
     return hipGetLastError();
 }
