@@ -117,7 +117,8 @@ def kernel_work(w, split=False):
 def _source_sha(kernel):
     files = {"slot_attention": ["slot.hip", "slot_kernel.hpp"], "prep": ["prep.hip"],
              "post": ["post.hip"], "pool": ["post.hip"], "token_proj": ["prep.hip"],
-             "pack": ["pack.hip"], "vt": ["slot.hip"], "masks": ["prep.hip"]}
+             "pack": ["pack.hip"], "vt": ["slot.hip"], "masks": ["prep.hip"],
+             "slot_gather": ["slot_gather.hip"]}
     h = hashlib.sha256()
     for f in files.get(kernel, []) + ["common.hpp", "kernels.hpp"]:
         p = os.path.join(ROOT, "windowed_atom_attention_amd", "csrc", f)
@@ -145,13 +146,14 @@ def _traffic(kernel, workload):
 # names the library's own profiler gives them.
 KERNEL_SYMBOLS = {"k_slot": "slot_attention", "k_prep": "prep", "k_post": "post",
                   "k_pool_fix": "pool", "k_pack": "pack", "k_token_proj": "token_proj",
-                  "k_vt": "vt", "k_masks": "masks"}
+                  "k_vt": "vt", "k_masks": "masks", "k_slot_gather": "slot_gather"}
 
 
 def kernel_of(symbol):
     """Library kernel name of a trace symbol (demangled or mangled), else None."""
     import re
-    m = re.search(r"k_(slot|prep|post|pool_fix|pack|token_proj|vt|masks)(?![a-z_])", symbol)
+    m = re.search(r"k_(slot_gather|slot|prep|post|pool_fix|pack|token_proj|vt|masks)(?![a-z_])",
+                  symbol)
     return KERNEL_SYMBOLS["k_" + m.group(1)] if m else None
 
 
