@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <unordered_map>
 
@@ -70,7 +71,7 @@ struct Bufs {
     int32_t *kid;
     float *og, *uu, *x1, *xh1, *r1, *z, *fa, *fb, *hh, *tr, *hid, *proj, *xhh, *rh, *lnh;
     // backward
-    float *dh, *dx2, *dtr, *dgT, *dhh, *da, *dbb, *dz, *dx1, *gt, *du, *dgA, *dog, *dO, *dGp;
+    float *dh, *dx2, *dtr, *dhh, *da, *dbb, *dz, *dx1, *gt, *du, *dog, *dO, *dGp;
     float *dS, *dq, *dk, *dv, *dqin, *dkvin, *dx0, *dzs[3], *dzg[2], *dcj[3], *dch, *dc, *dmods,
         *ds, *dpu, *dln, *dtp, *dP, *pwp, *part, *part2;
     int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list;
@@ -123,9 +124,9 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
     } else {
         b.proj = f(N * U);
     }
-    b.dh = f(N * C); b.dx2 = f(N * C); b.dtr = f(N * C); b.dgT = f(N * C);
+    b.dh = f(N * C); b.dx2 = f(N * C); b.dtr = f(N * C);
     b.dhh = f(N * M); b.da = f(N * M); b.dbb = f(N * M); b.dz = f(N * C); b.dx1 = f(N * C);
-    b.gt = f(N * C); b.du = f(N * C); b.dgA = f(N * C); b.dog = f(N * HD); b.dO = f(N * HD);
+    b.gt = f(N * C); b.du = f(N * C); b.dog = f(N * HD); b.dO = f(N * HD);
     b.dGp = f(N * HD); b.dS = f(E * H); b.dq = f(N * HD); b.dk = f(N * HD); b.dv = f(N * HD);
     b.dqin = f(N * C); b.dkvin = f(N * C); b.dx0 = f(N * C); b.dc = f(N * S);
     if (af3) {
@@ -226,6 +227,17 @@ struct Run {
             ok(ew(op, rows, W, View{o, ldo}, view(a, lda), view(b, ldb), view(c, ldc), vec, mask,
                   acc, s));
     }
+    // independent products / elementwise jobs in one launch each
+    void mmg(std::initializer_list<GemmJob> jobs) { mmg(jobs.begin(), (int)jobs.size()); }
+    void mmg(const GemmJob *jobs, int n) {
+        if (err == hipSuccess)
+            ok(gemm_group(jobs, n, s));
+    }
+    void eg(std::initializer_list<EwJob> jobs) { eg(jobs.begin(), (int)jobs.size()); }
+    void eg(const EwJob *jobs, int n) {
+        if (err == hipSuccess && n > 0)
+            ok(ew_group(jobs, n, s));
+    }
     void cs(int rows, int W, const float *X, int64_t ldx, const float *Y, int64_t ldy, float *out) {
         if (err == hipSuccess && out)
             ok(colsum(rows, W, view(X, ldx), view(Y, ldy), out, 0.0f, sc, s));
@@ -244,6 +256,29 @@ struct Run {
             ok(to_f32(src, dtype, 1, (int)n, n, dst, nullptr, s));
     }
 };
+
+// One product job: C (+)= sum of the segments' A B (+ bias), then epi.
+GemmJob gj(int M, int N, float *C, int64_t ldc, std::initializer_list<GemmSeg> segs,
+           const float *bias = nullptr, int epi = GEMM_NONE) {
+    GemmJob j{};
+    j.M = M;
+    j.N = N;
+    j.C = View{C, ldc};
+    j.beta = 0.0f;
+    j.bias = bias;
+    j.epi = epi;
+    for (const GemmSeg &x : segs)
+        j.seg[j.nseg++] = x;
+    return j;
+}
+GemmSeg sg(int K, Mat A, Mat B) { return GemmSeg{A, B, K}; }
+// One elementwise job (operands as for Run::e; d and vec2/vec3 set apart).
+EwJob ej(EwOp op, int rows, int W, float *o, int64_t ldo, const float *a, int64_t lda,
+         const float *b = nullptr, int64_t ldb = 0, const float *c = nullptr, int64_t ldc = 0,
+         const float *vec = nullptr, const uint8_t *mask = nullptr, int acc = 0) {
+    return EwJob{op, rows, W, View{o, ldo}, view(a, lda), view(b, ldb), view(c, ldc),
+                 View{nullptr, 0}, vec, nullptr, nullptr, mask, acc};
+}
 
 int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
                  const atom_attn_inputs *in, const atom_attn_params *par, float eps,
@@ -324,16 +359,21 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     // conditioning
     if (af3) {
         r.norm(0, N, S, eps, b.c, b.ch, b.rc);
+        r.eg({ej(EW_MUL_VEC, N, S, b.cj[0], S, b.ch, S, nullptr, 0, nullptr, 0, b.cs),
+              ej(EW_MUL_VEC, N, S, b.cj[1], S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + S),
+              ej(EW_MUL_VEC, N, S, b.cj[2], S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + 2 * S)});
+        // the eight conditioning products (sigmoid gates with their biases)
+        GemmJob js[kGroupJobs];
+        int nj = 0;
         for (int j = 0; j < 3; ++j) {
-            r.e(EW_MUL_VEC, N, S, b.cj[j], S, b.ch, S, nullptr, 0, nullptr, 0, b.cs + j * S);
-            r.mm(N, C, S, mat(b.cj[j], S), mat(b.ws + (size_t)j * S * C, C), b.sig[j], C);
-            r.e(EW_SIGMOID_VEC, N, C, b.sig[j], C, b.sig[j], C, nullptr, 0, nullptr, 0, b.bs + j * C);
-            r.mm(N, C, S, mat(b.cj[j], S), mat(b.wsh + (size_t)j * S * C, C), b.mu[j], C);
+            js[nj++] = gj(N, C, b.sig[j], C, {sg(S, mat(b.cj[j], S), mat(b.ws + (size_t)j * S * C, C))},
+                          b.bs + j * C, GEMM_SIGMOID);
+            js[nj++] = gj(N, C, b.mu[j], C, {sg(S, mat(b.cj[j], S), mat(b.wsh + (size_t)j * S * C, C))});
         }
-        for (int j = 0; j < 2; ++j) {
-            r.mm(N, C, S, mat(b.c, S), mat(b.wrg + (size_t)j * S * C, C), b.gr[j], C);
-            r.e(EW_SIGMOID_VEC, N, C, b.gr[j], C, b.gr[j], C, nullptr, 0, nullptr, 0, b.brg + j * C);
-        }
+        for (int j = 0; j < 2; ++j)
+            js[nj++] = gj(N, C, b.gr[j], C, {sg(S, mat(b.c, S), mat(b.wrg + (size_t)j * S * C, C))},
+                          b.brg + j * C, GEMM_SIGMOID);
+        r.mmg(js, nj);
     } else {
         r.e(EW_SILU, N, S, b.sc, S, b.c, S);
         r.mm(N, C6, S, mat(b.sc, S), mat(b.wmod, C6), b.mods, C6);
@@ -343,20 +383,18 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     const int64_t ldg = af3 ? C : C6;
     // modulated norms
     r.norm(nm, N, C, eps, b.x0, b.xh0, b.r0);
-    if (af3) {
-        r.e(EW_AFFINE, N, C, b.qin, C, b.xh0, C, b.sig[0], C, b.mu[0], C);
-        r.e(EW_AFFINE, N, C, b.kvin, C, b.xh0, C, b.sig[1], C, b.mu[1], C);
-    } else {
+    if (af3)
+        r.eg({ej(EW_AFFINE, N, C, b.qin, C, b.xh0, C, b.sig[0], C, b.mu[0], C),
+              ej(EW_AFFINE, N, C, b.kvin, C, b.xh0, C, b.sig[1], C, b.mu[1], C)});
+    else
         r.e(EW_AFFINE1, N, C, b.qin, C, b.xh0, C, b.mods + C, C6, b.mods, C6);
-    }
-    // projections
+    // projections (the value gate's sigmoid in the product's epilogue)
     float *qdst = af3 ? b.q : b.qraw;
     float *kdst = af3 ? b.k : b.kraw;
-    r.mm(N, HD, C, mat(b.qin, C), mat(b.wq, HD), qdst, HD, 0.0f, af3 ? b.bq : nullptr);
-    r.mm(N, HD, C, mat(b.kvin, C), mat(b.wk, HD), kdst, HD);
-    r.mm(N, HD, C, mat(b.kvin, C), mat(b.wv, HD), b.v, HD);
-    r.mm(N, HD, C, mat(b.qin, C), mat(b.wvg, HD), b.g, HD);
-    r.e(EW_SIGMOID, N, HD, b.g, HD, b.g, HD);
+    r.mmg({gj(N, HD, qdst, HD, {sg(C, mat(b.qin, C), mat(b.wq, HD))}, af3 ? b.bq : nullptr),
+           gj(N, HD, kdst, HD, {sg(C, mat(b.kvin, C), mat(b.wk, HD))}),
+           gj(N, HD, b.v, HD, {sg(C, mat(b.kvin, C), mat(b.wv, HD))}),
+           gj(N, HD, b.g, HD, {sg(C, mat(b.qin, C), mat(b.wvg, HD))}, nullptr, GEMM_SIGMOID)});
     float *dcos = gin ? gin->rope_cos : nullptr, *dsin = gin ? gin->rope_sin : nullptr;
     const float *cs_f = nullptr, *sn_f = nullptr;
     if (!af3) {
@@ -396,8 +434,8 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
         r.e(EW_AFFINE, N, C, b.z, C, b.xh1, C, b.sig[2], C, b.mu[2], C);
     else
         r.e(EW_AFFINE1, N, C, b.z, C, b.xh1, C, b.mods + 4 * C, C6, b.mods + 3 * C, C6);
-    r.mm(N, M, C, mat(b.z, C), mat(b.ffg, M), b.fa, M);
-    r.mm(N, M, C, mat(b.z, C), mat(b.ffu, M), b.fb, M);
+    r.mmg({gj(N, M, b.fa, M, {sg(C, mat(b.z, C), mat(b.ffg, M))}),
+           gj(N, M, b.fb, M, {sg(C, mat(b.z, C), mat(b.ffu, M))})});
     r.e(EW_SWIGLU, N, M, b.hh, M, b.fa, M, b.fb, M);
     r.mm(N, C, M, mat(b.hh, M), mat(b.ffo, C), b.tr, C);
     r.e(EW_RESID_MASK, N, C, b.hid, C, b.x1, C, gT, ldg, b.tr, C, nullptr, b.usable);
@@ -453,48 +491,45 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
         }
     }
     // hidden = usable ? x1 + gT * tr : 0
-    r.e(EW_MASK, N, C, b.dx2, C, b.dh, C, nullptr, 0, nullptr, 0, nullptr, b.usable);
-    r.e(EW_MUL, N, C, b.dtr, C, b.dx2, C, gT, ldg);
-    r.e(EW_MUL, N, C, b.dgT, C, b.dx2, C, b.tr, C);
+    // (the gate's gradient dh * tr goes straight into its pre-activation
+    // gradient: AF3 through the sigmoid, ESMFold2 into the modulation row)
+    r.eg({ej(EW_MASK, N, C, b.dx2, C, b.dh, C, nullptr, 0, nullptr, 0, nullptr, b.usable),
+          ej(EW_MUL, N, C, b.dtr, C, b.dh, C, gT, ldg, nullptr, 0, nullptr, b.usable),
+          af3 ? ej(EW_DGATE, N, C, b.dzg[1], C, b.dh, C, b.tr, C, b.gr[1], C, nullptr, b.usable)
+              : ej(EW_MUL, N, C, b.dmods + 5 * C, C6, b.dh, C, b.tr, C, nullptr, 0, nullptr,
+                   b.usable)});
     // transition
     r.fork();
     r.leaf_mm(M, C, N, mat_t(b.hh, M), mat(b.dtr, C), gpar ? gpar->w_ff_out : nullptr, C);
     r.mm(N, M, C, mat(b.dtr, C), mat_t(b.ffo, C), b.dhh, M);
-    r.e(EW_DSWIGLU_A, N, M, b.da, M, b.dhh, M, b.fa, M, b.fb, M);
-    r.e(EW_DSWIGLU_B, N, M, b.dbb, M, b.dhh, M, b.fa, M);
+    r.eg({ej(EW_DSWIGLU_A, N, M, b.da, M, b.dhh, M, b.fa, M, b.fb, M),
+          ej(EW_DSWIGLU_B, N, M, b.dbb, M, b.dhh, M, b.fa, M)});
     r.fork();
     r.leaf_mm(C, M, N, mat_t(b.z, C), mat(b.da, M), gpar ? gpar->w_ff_gate : nullptr, M);
     r.leaf_mm(C, M, N, mat_t(b.z, C), mat(b.dbb, M), gpar ? gpar->w_ff_up : nullptr, M);
-    r.mm(N, C, M, mat(b.da, M), mat_t(b.ffg, M), b.dz, C);
-    r.mm(N, C, M, mat(b.dbb, M), mat_t(b.ffu, M), b.dz, C, 1.0f);
+    r.mmg({gj(N, C, b.dz, C, {sg(M, mat(b.da, M), mat_t(b.ffg, M)), sg(M, mat(b.dbb, M), mat_t(b.ffu, M))})});
     // transition norm
-    r.e(EW_COPY, N, C, b.dx1, C, b.dx2, C);
     if (af3) {
-        r.e(EW_MUL, N, C, b.gt, C, b.dz, C, b.sig[2], C);
+        r.eg({ej(EW_COPY, N, C, b.dx1, C, b.dx2, C), ej(EW_MUL, N, C, b.gt, C, b.dz, C, b.sig[2], C),
+              ej(EW_DGATE, N, C, b.dzs[2], C, b.dz, C, b.xh1, C, b.sig[2], C)});
         r.norm_bwd(0, N, C, b.xh1, b.r1, b.gt, b.dx1, 1);
-        r.e(EW_DGATE, N, C, b.dzs[2], C, b.dz, C, b.xh1, C, b.sig[2], C);
     } else {
-        r.e(EW_MUL1, N, C, b.gt, C, b.dz, C, b.mods + 4 * C, C6);
+        r.eg({ej(EW_COPY, N, C, b.dx1, C, b.dx2, C),
+              ej(EW_MUL1, N, C, b.gt, C, b.dz, C, b.mods + 4 * C, C6),
+              ej(EW_MUL, N, C, b.dmods + 4 * C, C6, b.dz, C, b.xh1, C),
+              ej(EW_COPY, N, C, b.dmods + 3 * C, C6, b.dz, C)});
         r.norm_bwd(1, N, C, b.xh1, b.r1, b.gt, b.dx1, 1);
-        r.e(EW_MUL, N, C, b.dmods + 4 * C, C6, b.dz, C, b.xh1, C);
-        r.e(EW_COPY, N, C, b.dmods + 3 * C, C6, b.dz, C);
     }
     // x1 = x0 + gA * u
-    r.e(EW_MUL, N, C, b.du, C, b.dx1, C, gA, ldg);
-    r.e(EW_MUL, N, C, b.dgA, C, b.dx1, C, b.uu, C);
-    if (af3) {
-        r.e(EW_DSIG, N, C, b.dzg[0], C, b.dgA, C, b.gr[0], C);
-        r.e(EW_DSIG, N, C, b.dzg[1], C, b.dgT, C, b.gr[1], C);
-    } else {
-        r.e(EW_COPY, N, C, b.dmods + 2 * C, C6, b.dgA, C);
-        r.e(EW_COPY, N, C, b.dmods + 5 * C, C6, b.dgT, C);
-    }
+    r.eg({ej(EW_MUL, N, C, b.du, C, b.dx1, C, gA, ldg),
+          af3 ? ej(EW_DGATE, N, C, b.dzg[0], C, b.dx1, C, b.uu, C, b.gr[0], C)
+              : ej(EW_MUL, N, C, b.dmods + 2 * C, C6, b.dx1, C, b.uu, C)});
     // output projection and value gate
     r.fork();
     r.leaf_mm(HD, C, N, mat_t(b.og, HD), mat(b.du, C), gpar ? gpar->w_attention_out : nullptr, C);
     r.mm(N, HD, C, mat(b.du, C), mat_t(b.wao, C), b.dog, HD);
-    r.e(EW_MUL, N, HD, b.dO, HD, b.dog, HD, b.g, HD);
-    r.e(EW_DGATE, N, HD, b.dGp, HD, b.dog, HD, b.o, HD, b.g, HD);
+    r.eg({ej(EW_MUL, N, HD, b.dO, HD, b.dog, HD, b.g, HD),
+          ej(EW_DGATE, N, HD, b.dGp, HD, b.dog, HD, b.o, HD, b.g, HD)});
     prof_end(sp, s);
     // slot attention
     if (r.err == hipSuccess)
@@ -513,25 +548,25 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
         r.leaf_mm(C, HD, N, mat_t(b.kvin, C), mat(b.dk, HD), gpar->w_k, HD);
         r.leaf_mm(C, HD, N, mat_t(b.kvin, C), mat(b.dv, HD), gpar->w_v, HD);
     }
-    r.mm(N, C, HD, mat(b.dq, HD), mat_t(b.wq, HD), b.dqin, C);
-    r.mm(N, C, HD, mat(b.dGp, HD), mat_t(b.wvg, HD), b.dqin, C, 1.0f);
-    r.mm(N, C, HD, mat(b.dk, HD), mat_t(b.wk, HD), b.dkvin, C);
-    r.mm(N, C, HD, mat(b.dv, HD), mat_t(b.wv, HD), b.dkvin, C, 1.0f);
+    const GemmSeg sq = sg(HD, mat(b.dq, HD), mat_t(b.wq, HD)), sgp = sg(HD, mat(b.dGp, HD), mat_t(b.wvg, HD));
+    const GemmSeg sk = sg(HD, mat(b.dk, HD), mat_t(b.wk, HD)), sv = sg(HD, mat(b.dv, HD), mat_t(b.wv, HD));
     // modulated norms
-    r.e(EW_COPY, N, C, b.dx0, C, b.dx1, C);
     if (af3) {
-        r.e(EW_MUL, N, C, b.gt, C, b.dqin, C, b.sig[0], C);
-        r.e(EW_MUL, N, C, b.gt, C, b.dkvin, C, b.sig[1], C, nullptr, 0, nullptr, nullptr, 1);
+        r.mmg({gj(N, C, b.dqin, C, {sq, sgp}), gj(N, C, b.dkvin, C, {sk, sv})});
+        EwJob g2 = ej(EW_FMA2, N, C, b.gt, C, b.dqin, C, b.sig[0], C, b.dkvin, C);
+        g2.d = view(b.sig[1], C);
+        r.eg({ej(EW_COPY, N, C, b.dx0, C, b.dx1, C), g2,
+              ej(EW_DGATE, N, C, b.dzs[0], C, b.dqin, C, b.xh0, C, b.sig[0], C),
+              ej(EW_DGATE, N, C, b.dzs[1], C, b.dkvin, C, b.xh0, C, b.sig[1], C)});
         r.norm_bwd(0, N, C, b.xh0, b.r0, b.gt, b.dx0, 1);
-        r.e(EW_DGATE, N, C, b.dzs[0], C, b.dqin, C, b.xh0, C, b.sig[0], C);
-        r.e(EW_DGATE, N, C, b.dzs[1], C, b.dkvin, C, b.xh0, C, b.sig[1], C);
     } else {
-        // q_in and kv_in are one tensor: their gradients add
-        r.e(EW_ADD, N, C, b.dqin, C, b.dqin, C, b.dkvin, C);
-        r.e(EW_MUL1, N, C, b.gt, C, b.dqin, C, b.mods + C, C6);
+        // q_in and kv_in are one tensor: its gradient sums all four products
+        r.mmg({gj(N, C, b.dqin, C, {sq, sgp, sk, sv})});
+        r.eg({ej(EW_COPY, N, C, b.dx0, C, b.dx1, C),
+              ej(EW_MUL1, N, C, b.gt, C, b.dqin, C, b.mods + C, C6),
+              ej(EW_MUL, N, C, b.dmods + C, C6, b.dqin, C, b.xh0, C),
+              ej(EW_COPY, N, C, b.dmods, C6, b.dqin, C)});
         r.norm_bwd(1, N, C, b.xh0, b.r0, b.gt, b.dx0, 1);
-        r.e(EW_MUL, N, C, b.dmods + C, C6, b.dqin, C, b.xh0, C);
-        r.e(EW_COPY, N, C, b.dmods, C6, b.dqin, C);
     }
     // conditioning
     if (af3) {
@@ -553,20 +588,27 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
                           gpar->b_residual_gate ? gpar->b_residual_gate + j * C : nullptr);
             }
         }
-        for (int j = 0; j < 3; ++j) {
-            r.mm(N, S, C, mat(b.dzs[j], C), mat_t(b.ws + (size_t)j * S * C, C), b.dcj[j], S);
-            r.mm(N, S, C, mat(dmu[j], C), mat_t(b.wsh + (size_t)j * S * C, C), b.dcj[j], S, 1.0f);
-            r.e(EW_MUL_VEC, N, S, b.dch, S, b.dcj[j], S, nullptr, 0, nullptr, 0, b.cs + j * S, nullptr,
-                j > 0 ? 1 : 0);
-        }
+        // dc: the residual gates' part here, the conditioning norm's added below
+        GemmJob js[kGroupJobs];
+        int nj = 0;
+        for (int j = 0; j < 3; ++j)
+            js[nj++] = gj(N, S, b.dcj[j], S,
+                          {sg(C, mat(b.dzs[j], C), mat_t(b.ws + (size_t)j * S * C, C)),
+                           sg(C, mat(dmu[j], C), mat_t(b.wsh + (size_t)j * S * C, C))});
+        js[nj++] = gj(N, S, b.dc, S,
+                      {sg(C, mat(b.dzg[0], C), mat_t(b.wrg, C)),
+                       sg(C, mat(b.dzg[1], C), mat_t(b.wrg + (size_t)S * C, C))});
+        r.mmg(js, nj);
+        EwJob m3 = ej(EW_MUL_VEC3, N, S, b.dch, S, b.dcj[0], S, b.dcj[1], S, b.dcj[2], S, b.cs);
+        m3.vec2 = b.cs + S;
+        m3.vec3 = b.cs + 2 * S;
+        r.eg({m3});
         if (gpar && gpar->cond_scale) {
             r.fork();
             for (int j = 0; j < 3; ++j)
                 r.leaf_cs(N, S, b.dcj[j], S, b.ch, S, gpar->cond_scale + j * S);
         }
-        r.norm_bwd(0, N, S, b.ch, b.rc, b.dch, b.dc, 0);
-        for (int j = 0; j < 2; ++j)
-            r.mm(N, S, C, mat(b.dzg[j], C), mat_t(b.wrg + (size_t)j * S * C, C), b.dc, S, 1.0f);
+        r.norm_bwd(0, N, S, b.ch, b.rc, b.dch, b.dc, 1);
     } else {
         if (gpar && gpar->w_mod) {
             r.fork();
@@ -575,10 +617,17 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
         r.mm(N, S, C6, mat(b.dmods, C6), mat_t(b.wmod, C6), b.ds, S);
         r.e(EW_DSILU, N, S, b.dc, S, b.ds, S, b.c, S);
     }
-    if (gin && gin->condition)
-        r.e(EW_MASK, N, S, gin->condition, S, b.dc, S, nullptr, 0, nullptr, 0, nullptr, b.usable);
-    if (gin && gin->atom)
-        r.e(EW_MASK, N, C, gin->atom, C, b.dx0, C, nullptr, 0, nullptr, 0, nullptr, b.usable);
+    {
+        EwJob mk[2];
+        int nm2 = 0;
+        if (gin && gin->condition)
+            mk[nm2++] = ej(EW_MASK, N, S, gin->condition, S, b.dc, S, nullptr, 0, nullptr, 0, nullptr,
+                           b.usable);
+        if (gin && gin->atom)
+            mk[nm2++] = ej(EW_MASK, N, C, gin->atom, C, b.dx0, C, nullptr, 0, nullptr, 0, nullptr,
+                           b.usable);
+        r.eg(mk, nm2);
+    }
     if (dec && ((gin && gin->token) || (gpar && gpar->w_token))) {
         if (r.err == hipSuccess)
             r.ok(token_keys(B, A, T, b.usable, in->atom_to_token, b.tkey, s));

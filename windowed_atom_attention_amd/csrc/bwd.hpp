@@ -45,6 +45,28 @@ constexpr size_t kGemmPartialFloats = (size_t)8 << 20;
 hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const float *bias,
                 Scratch sc, hipStream_t s);
 
+// Independent products in one launch (no split k): job j computes
+//   C_j (+)= sum over its segments i of A_i[M, K_i] B_i[K_i, N] (+ bias[N]),
+// then applies its epilogue (GEMM_SIGMOID: sigmoid of the sum). Segments of
+// one job are accumulated in order; every output element is written by one
+// workgroup, so results do not depend on the grouping.
+constexpr int kGroupJobs = 8, kGroupSegs = 4;
+enum GemmEpi { GEMM_NONE, GEMM_SIGMOID };
+struct GemmSeg {
+    Mat A, B;
+    int K;
+};
+struct GemmJob {
+    int M, N;
+    int nseg;
+    GemmSeg seg[kGroupSegs];
+    View C;
+    float beta;
+    const float *bias;
+    int epi;
+};
+hipError_t gemm_group(const GemmJob *jobs, int n, hipStream_t s);
+
 // out[c] = beta * out[c] + sum_r X[r, c] (* Y[r, c] when Y.p), c < W.
 hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scratch sc,
                   hipStream_t s);
@@ -72,9 +94,22 @@ enum EwOp {
     EW_DSILU,       // a * silu'(b)
     EW_ADD_VEC,     // a + vec[c]
     EW_ZERO,        // 0
+    EW_FMA2,        // a * b + c * d
+    EW_MUL_VEC3,    // a * vec[c] + b * vec2[c] + c * vec3[c]
 };
+// A mask (one byte per row) zeroes the result of every row whose byte is 0.
 hipError_t ew(EwOp op, int rows, int W, View o, View a, View b, View c, const float *vec,
               const uint8_t *mask, int acc, hipStream_t s);
+// Independent elementwise jobs in one launch.
+struct EwJob {
+    EwOp op;
+    int rows, W;
+    View o, a, b, c, d;
+    const float *vec, *vec2, *vec3;
+    const uint8_t *mask;
+    int acc;
+};
+hipError_t ew_group(const EwJob *jobs, int n, hipStream_t s);
 
 // Row normalisation without affine terms (mode 0 LayerNorm, 1 RMS): xhat
 // and the row's 1/sqrt(var + eps) (resp. 1/sqrt(mean x^2 + eps)).

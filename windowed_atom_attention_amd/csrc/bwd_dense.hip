@@ -48,19 +48,27 @@ __device__ __forceinline__ void load8(const float *p, int idx, int lim, bool vec
     }
 }
 
-// 64x64 output tile per workgroup, four waves of 32x32 (v_mfma_f32_32x32x2_f32).
-// k advances in 32-deep stages staged through LDS; the next stage's operand
-// tiles are loaded into registers while the current one is multiplied.
-// Each thread moves 8 consecutive elements of an operand's contiguous axis.
-// Split k: every workgroup writes its partial tile; k_gemm_reduce sums
-// them in split order.
-__global__ __launch_bounds__(256) void k_gemm(GemmK g) {
-    __shared__ float As[kKS][68];
-    __shared__ float Bs[kKS][68];
+// One operand pair of a product: A [M, K] (element (m, k) at
+// A[m * ars + k * acs]), B [K, N] likewise.
+struct SegK {
+    const float *A;
+    int64_t ars, acs;
+    const float *B;
+    int64_t brs, bcs;
+    int K;
+    int avec, bvec; // 16-byte loads along the operand's contiguous axis
+};
+
+// 64x64 output tile per workgroup, four waves of 32x32 (v_mfma_f32_32x32x2_f32):
+// acc += A[m0.., kb..ke) B[kb..ke, n0..). k advances in 32-deep stages
+// staged through LDS; the next stage's operand tiles are loaded into
+// registers while the current one is multiplied. Each thread moves 8
+// consecutive elements of an operand's contiguous axis. Every stage starts
+// with a barrier, so consecutive calls may reuse As/Bs.
+__device__ __forceinline__ void tile_product(const SegK &g, int M, int N, int m0, int n0, int kb,
+                                             int ke, float (&As)[kKS][68], float (&Bs)[kKS][68],
+                                             f32x16_t &acc) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-    const int kb = blockIdx.z * g.kchunk;
-    const int ke = min(g.K, kb + g.kchunk);
     const bool a_k = g.acs == 1;
     const bool b_n = g.bcs == 1;
     float ra[8], rb[8];
@@ -69,7 +77,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
             // row m, 8 consecutive k
             const int m = t >> 2, kq = (t & 3) * 8;
             const int gm = m0 + m, gk = k0 + kq;
-            if (gm < g.M)
+            if (gm < M)
                 load8(g.A + (int64_t)gm * g.ars + gk, gk, ke, g.avec, ra);
             else
 #pragma unroll
@@ -80,11 +88,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
             const int gk = k0 + k, gm = m0 + mq;
             if (gk < ke) {
                 if (g.ars == 1)
-                    load8(g.A + (int64_t)gk * g.acs + gm, gm, g.M, g.avec, ra);
+                    load8(g.A + (int64_t)gk * g.acs + gm, gm, M, g.avec, ra);
                 else
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        ra[i] = gm + i < g.M ? g.A[(int64_t)(gm + i) * g.ars + (int64_t)gk * g.acs] : 0.0f;
+                        ra[i] = gm + i < M ? g.A[(int64_t)(gm + i) * g.ars + (int64_t)gk * g.acs] : 0.0f;
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ra[i] = 0.0f;
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
             const int k = t >> 3, nq = (t & 7) * 8;
             const int gk = k0 + k, gn = n0 + nq;
             if (gk < ke)
-                load8(g.B + (int64_t)gk * g.brs + gn, gn, g.N, g.bvec, rb);
+                load8(g.B + (int64_t)gk * g.brs + gn, gn, N, g.bvec, rb);
             else
 #pragma unroll
                 for (int i = 0; i < 8; ++i) rb[i] = 0.0f;
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
             // column n, 8 consecutive k (stride brs)
             const int n = t >> 2, kq = (t & 3) * 8;
             const int gn = n0 + n, gk = k0 + kq;
-            if (gn < g.N) {
+            if (gn < N) {
                 if (g.brs == 1)
                     load8(g.B + (int64_t)gn * g.bcs + gk, gk, ke, g.bvec, rb);
                 else
@@ -129,7 +137,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
                 Bs[(t & 3) * 8 + i][t >> 2] = rb[i];
         }
     };
-    f32x16_t acc = zero16();
     const int wm = (w & 1) * 32, wn = (w >> 1) * 32;
     const int half = lane >> 5, l32 = lane & 31;
     if (kb < ke)
@@ -147,7 +154,22 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
     }
-    const int c = n0 + wn + l32;
+}
+
+// Split k: every workgroup writes its partial tile; k_gemm_reduce sums
+// them in split order.
+__global__ __launch_bounds__(256) void k_gemm(GemmK g) {
+    __shared__ float As[kKS][68];
+    __shared__ float Bs[kKS][68];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int kb = blockIdx.z * g.kchunk;
+    const int ke = min(g.K, kb + g.kchunk);
+    const SegK sg{g.A, g.ars, g.acs, g.B, g.brs, g.bcs, g.K, g.avec, g.bvec};
+    f32x16_t acc = zero16();
+    tile_product(sg, g.M, g.N, m0, n0, kb, ke, As, Bs, acc);
+    const int wm = (w & 1) * 32, wn = (w >> 1) * 32;
+    const int c = n0 + wn + (lane & 31);
     if (g.splits == 1) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -168,6 +190,53 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
         const int r = m0 + wm + acc32_row(v, lane);
         if (r < g.M && c < g.N)
             g.partial[(int64_t)blockIdx.z * MN + (int64_t)r * g.N + c] = acc[v];
+    }
+}
+
+// Independent products in one launch: workgroups tile0[j] .. tile0[j+1]-1
+// take job j's 64x64 tiles (row-major over its tile grid).
+struct GemmJobK {
+    SegK seg[kGroupSegs];
+    int nseg, M, N, epi;
+    float *C;
+    int64_t ldc;
+    const float *bias;
+    float beta;
+    int tiles_n, tile0;
+};
+struct GemmGroupK {
+    GemmJobK job[kGroupJobs];
+    int n;
+};
+
+__global__ __launch_bounds__(256) void k_gemm_group(GemmGroupK G) {
+    __shared__ float As[kKS][68];
+    __shared__ float Bs[kKS][68];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int j = 0;
+    while (j + 1 < G.n && (int)blockIdx.x >= G.job[j + 1].tile0)
+        ++j;
+    const GemmJobK &g = G.job[j];
+    const int tl = (int)blockIdx.x - g.tile0;
+    const int m0 = (tl / g.tiles_n) * 64, n0 = (tl % g.tiles_n) * 64;
+    f32x16_t acc = zero16();
+    for (int i = 0; i < g.nseg; ++i)
+        tile_product(g.seg[i], g.M, g.N, m0, n0, 0, g.seg[i].K, As, Bs, acc);
+    const int wm = (w & 1) * 32, wn = (w >> 1) * 32;
+    const int c = n0 + wn + (lane & 31);
+    if (c >= g.N)
+        return;
+    const float bc = g.bias ? g.bias[c] : 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm + acc32_row(v, lane);
+        if (r >= g.M)
+            continue;
+        float x = acc[v] + bc;
+        if (g.epi == GEMM_SIGMOID)
+            x = sigmoid_f(x);
+        float *dst = g.C + (int64_t)r * g.ldc + c;
+        *dst = g.beta != 0.0f ? *dst + x : x;
     }
 }
 
@@ -247,20 +316,30 @@ struct EwK {
     int op, rows, W, acc;
     float *o;
     int64_t ldo;
-    const float *a, *b, *c;
-    int64_t lda, ldb, ldc;
-    const float *vec;
+    const float *a, *b, *c, *d;
+    int64_t lda, ldb, ldc, ldd;
+    const float *vec, *vec2, *vec3;
     const uint8_t *mask;
+    int blk0; // first workgroup of the job in a group launch
+};
+struct EwGroupK {
+    EwK job[kGroupJobs];
+    int n;
 };
 
-__global__ __launch_bounds__(256) void k_ew(EwK e) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void k_ew(EwGroupK G) {
+    int j = 0;
+    while (j + 1 < G.n && (int)blockIdx.x >= G.job[j + 1].blk0)
+        ++j;
+    const EwK &e = G.job[j];
+    const int64_t i = (int64_t)((int)blockIdx.x - e.blk0) * 256 + threadIdx.x;
     if (i >= (int64_t)e.rows * e.W)
         return;
     const int r = (int)(i / e.W), col = (int)(i - (int64_t)r * e.W);
     const float a = e.a ? e.a[(int64_t)r * e.lda + col] : 0.0f;
     const float b = e.b ? e.b[(int64_t)r * e.ldb + col] : 0.0f;
     const float c = e.c ? e.c[(int64_t)r * e.ldc + col] : 0.0f;
+    const float d = e.d ? e.d[(int64_t)r * e.ldd + col] : 0.0f;
     const float vc = e.vec ? e.vec[col] : 0.0f;
     const bool m = e.mask ? e.mask[r] != 0 : true;
     float x;
@@ -277,8 +356,8 @@ __global__ __launch_bounds__(256) void k_ew(EwK e) {
     case EW_SILU: x = silu_f(a); break;
     case EW_SWIGLU: x = silu_f(a) * b; break;
     case EW_RESID: x = a + b * c; break;
-    case EW_RESID_MASK: x = m ? a + b * c : 0.0f; break;
-    case EW_MASK: x = m ? a : 0.0f; break;
+    case EW_RESID_MASK: x = a + b * c; break;
+    case EW_MASK: x = a; break;
     case EW_DSIG: x = a * b * (1.0f - b); break;
     case EW_DGATE: x = a * b * c * (1.0f - c); break;
     case EW_DSWIGLU_A: x = a * c * dsilu_f(b); break;
@@ -286,8 +365,12 @@ __global__ __launch_bounds__(256) void k_ew(EwK e) {
     case EW_DSILU: x = a * dsilu_f(b); break;
     case EW_ADD_VEC: x = a + vc; break;
     case EW_ZERO: x = 0.0f; break;
+    case EW_FMA2: x = a * b + c * d; break;
+    case EW_MUL_VEC3: x = a * vc + b * e.vec2[col] + c * e.vec3[col]; break;
     default: x = 0.0f; break;
     }
+    if (!m)
+        x = 0.0f;
     float *dst = e.o + (int64_t)r * e.ldo + col;
     *dst = e.acc ? *dst + x : x;
 }
@@ -636,6 +719,47 @@ hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const flo
     return hipGetLastError();
 }
 
+hipError_t gemm_group(const GemmJob *jobs, int n, hipStream_t s) {
+    if (n < 1 || n > kGroupJobs)
+        return hipErrorInvalidValue;
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+    auto vec_ok = [&](const Mat &x) {
+        return al16(x.p) && ((x.cs == 1 && x.rs % 4 == 0) || (x.rs == 1 && x.cs % 4 == 0));
+    };
+    GemmGroupK G{};
+    int tiles = 0, m = 0;
+    for (int j = 0; j < n; ++j) {
+        const GemmJob &x = jobs[j];
+        if (x.M <= 0 || x.N <= 0)
+            continue;
+        if (x.nseg < 1 || x.nseg > kGroupSegs)
+            return hipErrorInvalidValue;
+        GemmJobK &k = G.job[m];
+        for (int i = 0; i < x.nseg; ++i) {
+            const GemmSeg &sg = x.seg[i];
+            k.seg[i] = SegK{sg.A.p, sg.A.rs, sg.A.cs, sg.B.p, sg.B.rs, sg.B.cs, sg.K,
+                            vec_ok(sg.A) ? 1 : 0, vec_ok(sg.B) ? 1 : 0};
+        }
+        k.nseg = x.nseg;
+        k.M = x.M;
+        k.N = x.N;
+        k.epi = x.epi;
+        k.C = x.C.p;
+        k.ldc = x.C.ld;
+        k.bias = x.bias;
+        k.beta = x.beta;
+        k.tiles_n = (int)nblk(x.N, 64);
+        k.tile0 = tiles;
+        tiles += (int)nblk(x.M, 64) * k.tiles_n;
+        ++m;
+    }
+    if (m == 0)
+        return hipSuccess;
+    G.n = m;
+    hipLaunchKernelGGL(k_gemm_group, dim3((unsigned)tiles), dim3(256), 0, s, G);
+    return hipGetLastError();
+}
+
 hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scratch sc,
                   hipStream_t s) {
     if (W <= 0)
@@ -651,14 +775,32 @@ hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scrat
     return hipGetLastError();
 }
 
+hipError_t ew_group(const EwJob *jobs, int n, hipStream_t s) {
+    if (n < 1 || n > kGroupJobs)
+        return hipErrorInvalidValue;
+    EwGroupK G{};
+    int blk = 0, m = 0;
+    for (int j = 0; j < n; ++j) {
+        const EwJob &x = jobs[j];
+        const int64_t cnt = (int64_t)x.rows * x.W;
+        if (cnt <= 0)
+            continue;
+        G.job[m] = EwK{(int)x.op, x.rows, x.W, x.acc, x.o.p, x.o.ld, x.a.p, x.b.p, x.c.p, x.d.p,
+                       x.a.ld, x.b.ld, x.c.ld, x.d.ld, x.vec, x.vec2, x.vec3, x.mask, blk};
+        blk += (int)nblk(cnt, 256);
+        ++m;
+    }
+    if (m == 0)
+        return hipSuccess;
+    G.n = m;
+    hipLaunchKernelGGL(k_ew, dim3((unsigned)blk), dim3(256), 0, s, G);
+    return hipGetLastError();
+}
+
 hipError_t ew(EwOp op, int rows, int W, View o, View a, View b, View c, const float *vec,
               const uint8_t *mask, int acc, hipStream_t s) {
-    const int64_t n = (int64_t)rows * W;
-    if (n <= 0)
-        return hipSuccess;
-    EwK e{(int)op, rows, W, acc, o.p, o.ld, a.p, b.p, c.p, a.ld, b.ld, c.ld, vec, mask};
-    hipLaunchKernelGGL(k_ew, dim3(nblk(n, 256)), dim3(256), 0, s, e);
-    return hipGetLastError();
+    EwJob j{op, rows, W, o, a, b, c, View{nullptr, 0}, vec, nullptr, nullptr, mask, acc};
+    return ew_group(&j, 1, s);
 }
 
 hipError_t norm_rows(int mode, int rows, int W, float eps, View x, View xhat, float *rstd,

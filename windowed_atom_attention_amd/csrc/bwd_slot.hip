@@ -40,30 +40,56 @@ struct SK {
 // values [K], one query row [HD].
 __host__ __device__ inline int wave_floats(int K, int H, int HD) { return K + K * H + K + HD; }
 
+// Channels 4 qv .. 4 qv + 3 of pair row `row` (zeros past V): one 8- or
+// 16-byte load when V is a multiple of 4, else element loads.
 template <typename TP>
-__device__ __forceinline__ void load_pair_row(const TP *pair, int64_t row, int V, float *x) {
+__device__ __forceinline__ void load_pair_piece(const TP *pair, int64_t row, int V, int qv,
+                                                float (&x)[4]) {
+    const TP *p = pair + row * V + 4 * qv;
+    if (V % 4 == 0) {
+        if (4 * qv < V) {
+            if constexpr (sizeof(TP) == 4) {
+                const float4 t = *reinterpret_cast<const float4 *>(p);
+                x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+            } else {
+                const uint2 t = *reinterpret_cast<const uint2 *>(p);
+                x[0] = __uint_as_float(t.x << 16);
+                x[1] = __uint_as_float(t.x & 0xffff0000u);
+                x[2] = __uint_as_float(t.y << 16);
+                x[3] = __uint_as_float(t.y & 0xffff0000u);
+            }
+        } else {
+            x[0] = x[1] = x[2] = x[3] = 0.0f;
+        }
+    } else {
 #pragma unroll
-    for (int v = 0; v < kPairV; ++v)
-        x[v] = v < V ? to_f(pair[row * V + v]) : 0.0f;
+        for (int i = 0; i < 4; ++i)
+            x[i] = 4 * qv + i < V ? to_f(p[i]) : 0.0f;
+    }
 }
 
-// LN of a pair row (population, eps in the root): xhat and 1/sqrt(var+eps).
-__device__ __forceinline__ float pair_ln(float *x, int V, float eps) {
-    float m = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kPairV; ++v)
-        m += v < V ? x[v] : 0.0f;
-    m /= (float)V;
+// sum over the four lanes of a slot (lanes 4 k .. 4 k + 3)
+__device__ __forceinline__ float sum4(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    return v;
+}
+
+// LN of a pair row held as four 4-channel pieces by the slot's four lanes
+// (x = 0 past V): xhat in place, returns 1/sqrt(var + eps).
+__device__ __forceinline__ float pair_ln4(float (&x)[4], int V, int qv, float eps) {
+    const float m = sum4(x[0] + x[1] + x[2] + x[3]) / (float)V;
     float q = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kPairV; ++v) {
-        const float d = v < V ? x[v] - m : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        const float d = 4 * qv + i < V ? x[i] - m : 0.0f;
+        x[i] = d;
         q += d * d;
     }
-    const float r = 1.0f / sqrtf(q / (float)V + eps);
+    const float r = 1.0f / sqrtf(sum4(q) / (float)V + eps);
 #pragma unroll
-    for (int v = 0; v < kPairV; ++v)
-        x[v] = v < V ? (x[v] - m) * r : 0.0f;
+    for (int i = 0; i < 4; ++i)
+        x[i] *= r;
     return r;
 }
 
@@ -123,6 +149,58 @@ __device__ __forceinline__ float row_dot(const float *row, const float *v) {
     return x;
 }
 
+// Slot ownership of the per-slot values (logits, weights, gradients):
+// slot s = 64 c + sl(lane) of chunk c, sl(lane) = (lane % (D/4)) * (256/D)
+// + lane / (D/4) -- the order in which group_dots produces the slots.
+template <int D> __device__ __forceinline__ int slot_of_lane(int lane) {
+    constexpr int L4 = D / 4, G = 64 / L4;
+    return (lane % L4) * G + lane / L4;
+}
+
+// Dots of v[0..D) (LDS) with the rows rows[kid[s] * HD + off ..] of slots s
+// of chunks c < NC (kid < 0: 0): lane groups of D/4 lanes read one row per
+// load (one 16-byte piece per lane, so a load instruction touches 256/D
+// rows, not one row per lane), four rows per group in flight; each group's
+// partial dots are added by lane exchanges and the lane that owns the slot
+// (slot_of_lane) keeps it in out[c].
+template <int D, int NC>
+__device__ __forceinline__ void group_dots(const float *v, const int *kid, int K,
+                                           const float *rows, int HD, int off, int lane,
+                                           float (&out)[NC]) {
+    constexpr int L4 = D / 4, G = 64 / L4;
+    const int g = lane / L4, q = lane - g * L4;
+    const float4 vv = reinterpret_cast<const float4 *>(v)[q];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        out[c] = 0.0f;
+        if (c * 64 >= K)
+            continue;
+#pragma unroll
+        for (int i0 = 0; i0 < L4; i0 += 4) {
+            float4 r[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = c * 64 + (i0 + u) * G + g;
+                const int id = (i0 + u < L4 && s < K) ? kid[s] : -1;
+                r[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (id >= 0)
+                    r[u] = *reinterpret_cast<const float4 *>(rows + (int64_t)id * HD + off + q * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (i0 + u >= L4)
+                    break;
+                float x = vv.x * r[u].x + vv.y * r[u].y + vv.z * r[u].z + vv.w * r[u].w;
+#pragma unroll
+                for (int o = 1; o < L4; o <<= 1)
+                    x += __shfl_xor(x, o);
+                if (q == i0 + u)
+                    out[c] = x;
+            }
+        }
+    }
+}
+
 template <typename TP, bool AF3, int D>
 __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
     extern __shared__ float smem[];
@@ -151,45 +229,67 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
         skid[s] = id;
         if (live)
             a.kid[e] = id;
-        if constexpr (AF3) {
-            float x[kPairV];
-            if (ok) {
-                load_pair_row(reinterpret_cast<const TP *>(a.pair), e, a.V, x);
-                pair_ln(x, a.V, a.eps);
-            }
-            for (int h = 0; h < H; ++h) {
-                float acc = 0.0f;
-                if (ok)
+    }
+    if constexpr (AF3) {
+        // pair bias (LN(pair row) * pair_scale) @ w_pair: four lanes per
+        // slot, lane quarter qv holding channels 4 qv .. 4 qv + 3 (16
+        // slots per pass, whole rows per load); lane qv writes head qv
+        const int V = a.V, qv = lane & 3, sg4 = lane >> 2;
+        float wv[4][kPairH];
 #pragma unroll
-                    for (int v = 0; v < kPairV; ++v)
-                        if (v < a.V)
-                            acc += x[v] * a.ps[v] * a.wp[v * H + h];
-                sbeta[s * H + h] = acc;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int v = 4 * qv + i;
+            const float ps = v < V ? a.ps[v] : 0.0f;
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                wv[i][h] = (v < V && h < H) ? ps * a.wp[v * H + h] : 0.0f;
+        }
+        for (int s0 = 0; s0 < K; s0 += 16) {
+            const int s = s0 + sg4;
+            const bool in = s < K;
+            const bool ok = in && skid[s] >= 0;
+            float x[4];
+            load_pair_piece(reinterpret_cast<const TP *>(a.pair), nn * K + (in ? s : 0), V, qv, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x[i] = ok ? x[i] : 0.0f; // rows of slots not allowed may hold junk
+            pair_ln4(x, V, qv, a.eps);
+            float bh[kPairH];
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                bh[h] = sum4(x[0] * wv[0][h] + x[1] * wv[1][h] + x[2] * wv[2][h] + x[3] * wv[3][h]);
+            float mine = bh[0];
+#pragma unroll
+            for (int h = 1; h < kPairH; ++h)
+                mine = qv == h ? bh[h] : mine;
+            if (in && qv < H)
+                sbeta[s * H + qv] = ok ? mine : 0.0f;
         }
     }
     for (int i = lane; i < HD; i += 64)
         sq[i] = a.q[nn * HD + i];
     __syncthreads();
 
+    const int sl = slot_of_lane<D>(lane);
     for (int h = 0; h < H; ++h) {
         float l[kMaxK / 64];
+        group_dots<D, kMaxK / 64>(sq + h * D, skid, K, a.k, HD, h * D, lane, l);
         float mx = -INFINITY;
 #pragma unroll
         for (int c = 0; c < kMaxK / 64; ++c) {
-            const int s = lane + 64 * c;
-            l[c] = -INFINITY;
+            const int s = sl + 64 * c;
             if (s < K && skid[s] >= 0) {
-                const float dot = row_dot<D>(a.k + (int64_t)skid[s] * HD + h * D, sq + h * D);
-                l[c] = dot * p.inv_sqrt_d + (AF3 ? sbeta[s * H + h] : 0.0f);
+                l[c] = l[c] * p.inv_sqrt_d + (AF3 ? sbeta[s * H + h] : 0.0f);
                 mx = fmaxf(mx, l[c]);
+            } else {
+                l[c] = -INFINITY;
             }
         }
         mx = group_max<64>(mx);
         float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < kMaxK / 64; ++c) {
-            const int s = lane + 64 * c;
+            const int s = sl + 64 * c;
             if (s < K && skid[s] >= 0) {
                 l[c] = expf(l[c] - mx);
                 sum += l[c];
@@ -199,7 +299,7 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
         const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
 #pragma unroll
         for (int c = 0; c < kMaxK / 64; ++c) {
-            const int s = lane + 64 * c;
+            const int s = sl + 64 * c;
             if (s < K) {
                 const float pw = skid[s] >= 0 ? l[c] * inv : 0.0f;
                 sP[s] = pw;
@@ -239,20 +339,20 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
         sdo[i] = a.d_o[nn * HD + i];
     __syncthreads();
 
+    const int sl = slot_of_lane<D>(lane);
     for (int h = 0; h < H; ++h) {
         const int64_t rowbase = ((b * H + h) * a.A + qa) * K;
-        float pw[kMaxK / 64], dw[kMaxK / 64];
+        float pw[kMaxK / 64], dw[kMaxK / 64], vd[kMaxK / 64];
+        group_dots<D, kMaxK / 64>(sdo + h * D, skid, K, a.v, HD, h * D, lane, vd);
         float dsum = 0.0f;
 #pragma unroll
         for (int c = 0; c < kMaxK / 64; ++c) {
-            const int s = lane + 64 * c;
+            const int s = sl + 64 * c;
             pw[c] = 0.0f;
             dw[c] = 0.0f;
             if (s < K && skid[s] >= 0) {
                 pw[c] = a.P[rowbase + s];
-                float x = a.d_att ? a.d_att[rowbase + s] : 0.0f;
-                if (pw[c] != 0.0f)
-                    x += row_dot<D>(a.v + (int64_t)skid[s] * HD + h * D, sdo + h * D);
+                const float x = (a.d_att ? a.d_att[rowbase + s] : 0.0f) + vd[c];
                 dw[c] = x;
                 dsum += pw[c] * x;
             }
@@ -260,7 +360,7 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
         dsum = group_sum<64>(dsum);
 #pragma unroll
         for (int c = 0; c < kMaxK / 64; ++c) {
-            const int s = lane + 64 * c;
+            const int s = sl + 64 * c;
             if (s < K) {
                 const float dl = pw[c] * (dw[c] - dsum);
                 sP[s] = dl;
@@ -282,67 +382,100 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     }
 
     if constexpr (AF3) {
-        // pair bias: beta_h = sum_v xhat_v ps_v wp[v][h]
-        const int V = a.V;
-        float gps[kPairV], gwp[kPairV * kPairH];
+        // pair bias beta_h = sum_v xhat_v ps_v wp[v][h]: its gradient dS
+        // flows to the pair row, pair_scale and w_pair. Four lanes per slot,
+        // lane quarter qv holding channels 4 qv .. 4 qv + 3 (16 slots per
+        // pass, whole rows per load and store).
+        const int V = a.V, qv = lane & 3, sg4 = lane >> 2;
+        float psv[4], wpv[4][kPairH];
 #pragma unroll
-        for (int i = 0; i < kPairV; ++i)
+        for (int i = 0; i < 4; ++i) {
+            const int v = 4 * qv + i;
+            psv[i] = v < V ? a.ps[v] : 0.0f;
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                wpv[i][h] = (v < V && h < H) ? a.wp[v * H + h] : 0.0f;
+        }
+        float gps[4], gwp[4][kPairH];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             gps[i] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPairV * kPairH; ++i)
-            gwp[i] = 0.0f;
-        for (int s = lane; s < K; s += 64) {
-            const int64_t e = nn * K + s;
-            if (skid[s] >= 0) {
-                float x[kPairV];
-                load_pair_row(reinterpret_cast<const TP *>(a.pair), e, V, x);
-                const float r = pair_ln(x, V, a.eps);
-                float db[kPairH];
+            for (int h = 0; h < kPairH; ++h)
+                gwp[i][h] = 0.0f;
+        }
+        for (int s0 = 0; s0 < K; s0 += 16) {
+            const int s = s0 + sg4;
+            const bool in = s < K;
+            const bool ok = in && skid[s] >= 0;
+            const int64_t e = nn * K + (in ? s : 0);
+            float x[4];
+            load_pair_piece(reinterpret_cast<const TP *>(a.pair), e, V, qv, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x[i] = ok ? x[i] : 0.0f; // rows of slots not allowed may hold junk
+            const float r = pair_ln4(x, V, qv, a.eps);
+            float db[kPairH];
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                db[h] = (ok && h < H) ? sdl[s * H + h] : 0.0f;
+            float y[4];
+            float my = 0.0f, myx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float dpn = 0.0f;
 #pragma unroll
                 for (int h = 0; h < kPairH; ++h)
-                    db[h] = h < H ? sdl[s * H + h] : 0.0f;
-                float y[kPairV];
-                float my = 0.0f, myx = 0.0f;
+                    dpn += db[h] * wpv[i][h];
+                gps[i] += dpn * x[i];
 #pragma unroll
-                for (int v = 0; v < kPairV; ++v) {
-                    float dpn = 0.0f;
+                for (int h = 0; h < kPairH; ++h)
+                    gwp[i][h] += x[i] * psv[i] * db[h];
+                y[i] = dpn * psv[i];
+                my += y[i];
+                myx += y[i] * x[i];
+            }
+            my = sum4(my) / (float)V;
+            myx = sum4(myx) / (float)V;
+            if (a.d_pair && live && in) {
+                float dp[4];
 #pragma unroll
-                    for (int h = 0; h < kPairH; ++h)
-                        if (v < V && h < H)
-                            dpn += db[h] * a.wp[v * H + h];
-                    gps[v] += dpn * x[v];
-                    const float psv = v < V ? a.ps[v] : 0.0f;
+                for (int i = 0; i < 4; ++i)
+                    dp[i] = ok ? r * (y[i] - my - x[i] * myx) : 0.0f;
+                float *dst = a.d_pair + e * V + 4 * qv;
+                if (V % 4 == 0) {
+                    if (4 * qv < V)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(dp[0], dp[1], dp[2], dp[3]);
+                } else {
 #pragma unroll
-                    for (int h = 0; h < kPairH; ++h)
-                        gwp[v * kPairH + h] += x[v] * psv * db[h];
-                    y[v] = dpn * psv;
-                    my += y[v];
-                    myx += y[v] * x[v];
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * qv + i < V)
+                            dst[i] = dp[i];
                 }
-                if (a.d_pair) {
-                    my /= (float)V;
-                    myx /= (float)V;
-                    for (int v = 0; v < V; ++v)
-                        a.d_pair[e * V + v] = r * (y[v] - my - x[v] * myx);
-                }
-            } else if (a.d_pair && live) {
-                for (int v = 0; v < V; ++v)
-                    a.d_pair[e * V + v] = 0.0f;
             }
         }
-        // wave sums, then the workgroup's four waves in order
+        // sums over the wave's 16 slot groups (lanes of one channel quarter)
 #pragma unroll
-        for (int i = 0; i < kPairV; ++i) {
-            const float t = group_sum<64>(gps[i]);
-            if (lane == 0)
-                wred[w][i] = t;
-        }
+        for (int o = 4; o < 64; o <<= 1) {
 #pragma unroll
-        for (int i = 0; i < kPairV * kPairH; ++i) {
-            const float t = group_sum<64>(gwp[i]);
-            if (lane == 0)
-                wred[w][kPairV + i] = t;
+            for (int i = 0; i < 4; ++i) {
+                gps[i] += __shfl_xor(gps[i], o);
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    gwp[i][h] += __shfl_xor(gwp[i][h], o);
+            }
         }
+        if (lane < 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = 4 * lane + i;
+                wred[w][v] = gps[i];
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    wred[w][kPairV + v * kPairH + h] = gwp[i][h];
+            }
+        }
+        // then the workgroup's four waves in order
         __syncthreads();
         constexpr int W = kPairV + kPairV * kPairH;
         for (int i = threadIdx.x; i < W; i += 256)
