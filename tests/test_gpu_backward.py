@@ -11,6 +11,14 @@ over every atom) carry relative errors near 1e-6, and the normalisation
 and softmax backward steps cancel at most a few digits more. Exact zeros
 the method fixes (unusable atoms, slots that are not allowed) are compared
 bit-exactly.
+
+The encoder pooling applies ReLU to each atom's pooled projection, whose
+derivative is undefined at 0. A projection within fp32 rounding of 0 can
+land on either side in the GPU's fp32 arithmetic and the oracle's fp64, and
+the two are then both valid but different gradients (the whole backward of
+that atom and its window changes). The upstream token gradient is therefore
+zeroed on each (token, channel) with an atom whose oracle projection lies
+within 1e-4 rms of the kink: no gradient depends on the side taken there.
 """
 import numpy as np
 import pytest
@@ -40,6 +48,30 @@ def _upstream(w, seed=21, which=("hidden", "attention", "pooled")):
             up["token_output"] = torch.randn((B, T, U), generator=g)
         else:
             up["position_update"] = torch.randn((B, A, 3), generator=g)
+    return up
+
+
+def _kink_safe(w, up):
+    """Zero d_token_output[b, t, u] where a usable atom of token t has its
+    oracle projection (hidden @ w_pool, fp64) within 1e-4 rms of the ReLU
+    kink."""
+    if w.stage != "encoder" or "token_output" not in up:
+        return up
+    f64 = lambda d: {k: v.to(torch.float64) for k, v in d.items()}
+    out = block_grad.block_forward(f64(w.activations), f64(w.parameters), w.masks, w.structure,
+                                   eps=w.eps, style=w.style, stage=w.stage, radius=w.radius)
+    proj = out["hidden"].detach() @ w.parameters["w_pool"].to(torch.float64)
+    a2t = w.structure["atom_to_token"]
+    T = w.dims["T"]
+    inr = (a2t >= 0) & (a2t < T)
+    usable = w.masks["valid"] & inr & torch.gather(w.masks["token_valid"], 1, a2t.clamp(0, T - 1))
+    rms = proj[usable].pow(2).mean().sqrt()
+    near = (proj.abs() <= 1e-4 * rms) & usable[..., None]
+    b, n, u = torch.nonzero(near, as_tuple=True)
+    t = a2t[b, n]
+    up = dict(up)
+    up["token_output"] = up["token_output"].clone()
+    up["token_output"][b, t, u] = 0.0
     return up
 
 
@@ -93,7 +125,7 @@ CASES = [
 def test_block_backward_matches_oracle(name, kw):
     w = make_workload(name, rope="distinct", **kw)
     print("case", name, kw, w.style, w.stage, w.dtype, flush=True)
-    up = _upstream(w)
+    up = _kink_safe(w, _upstream(w))
     _, ref_in, ref_par = block_grad.block_backward(w.activations, w.parameters, w.masks,
                                                    w.structure, up, eps=w.eps, style=w.style,
                                                    stage=w.stage, radius=w.radius)
@@ -121,7 +153,7 @@ def test_block_backward_partial_upstream_and_subsets():
 
 def test_block_backward_is_deterministic():
     w = make_workload("4a", A=700)
-    up = _upstream(w)
+    up = _kink_safe(w, _upstream(w))
     a_in, a_par = _gpu_backward(w, up)
     b_in, b_par = _gpu_backward(w, up)
     for k in a_in:
@@ -134,7 +166,7 @@ def test_block_backward_full_size_headline_workload():
     """The AF3 encoder fp32 workload at its full size (A=4608, K=128), every
     gradient against the oracle."""
     w = make_workload("1")
-    up = _upstream(w)
+    up = _kink_safe(w, _upstream(w))
     _, ref_in, ref_par = block_grad.block_backward(w.activations, w.parameters, w.masks,
                                                    w.structure, up, eps=w.eps, style=w.style,
                                                    stage=w.stage, radius=w.radius)
