@@ -73,8 +73,8 @@ struct Bufs {
     // backward
     float *dh, *dx2, *dtr, *dhh, *da, *dbb, *dz, *dx1, *gt, *du, *dog, *dO, *dGp;
     float *dS, *dq, *dk, *dv, *dqin, *dkvin, *dx0, *dzs[3], *dzg[2], *dcj[3], *dch, *dc, *dmods,
-        *ds, *dpu, *dln, *dtp, *dP, *pwp, *part, *part2;
-    int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list;
+        *ds, *dpu, *dln, *dtp, *dP, *pwp, *part, *part2, *Pk;
+    int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list, *inv;
 };
 
 void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
@@ -139,12 +139,13 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
     }
     if (dec) {
         b.dpu = f(N * 3); b.dln = f(N * C); b.dtp = f(BT * C);
-        b.tkey = ar.get<int32_t>(N); b.tcnt = ar.get<int32_t>(BT);
+        b.tkey = ar.get<int32_t>(N); b.tcnt = ar.get<int32_t>(reverse_index_count_ints(BT));
         b.toff = ar.get<int32_t>(BT + 1); b.tlist = ar.get<int32_t>(N);
     } else {
         b.dP = f(N * U);
     }
-    b.cnt = ar.get<int32_t>(N); b.off = ar.get<int32_t>(N + 1); b.list = ar.get<int32_t>(E);
+    b.cnt = ar.get<int32_t>(reverse_index_count_ints(N)); b.off = ar.get<int32_t>(N + 1);
+    b.list = ar.get<int32_t>(E); b.inv = ar.get<int32_t>(E); b.Pk = f(E * H);
     b.pwp = f(slot_bwd_partial_floats((int64_t)N, (int)V, (int)H));
     b.part = f(kGemmPartialFloats);
     b.part2 = f(kGemmPartialFloats);
@@ -419,6 +420,7 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.d_att = gout->attention; sa.d_o = b.dO; sa.dS = b.dS;
     sa.dq = b.dq; sa.dk = b.dk; sa.dv = b.dv; sa.d_pair = (af3 && gin) ? gin->pair : nullptr;
     sa.pw_partial = b.pwp; sa.count = b.cnt; sa.offset = b.off; sa.list = b.list;
+    sa.inv = b.inv; sa.Pk = b.Pk;
     sa.sc = r.sc;
     if (r.err == hipSuccess) {
         sp = prof_begin(KN_BWD_SLOT_FWD, s);
@@ -731,9 +733,11 @@ int atom_attn_slot_backward_workspace_bytes(const atom_attn_dims *dims, int styl
     ar.get<float>(N * HD);                        // o
     ar.get<float>(E * dims->H);                   // logit gradients
     ar.get<int32_t>(E);                           // slot -> key
-    ar.get<int32_t>(N);                           // reverse index
+    ar.get<int32_t>(reverse_index_count_ints(N)); // reverse index
     ar.get<int32_t>(N + 1);
     ar.get<int32_t>(E);
+    ar.get<int32_t>(E);                           // list position of each entry
+    ar.get<float>(E * dims->H);                   // key-major weights
     ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
     ar.get<float>(dims->V);                       // pair parameters in fp32
     ar.get<float>(dims->V * dims->H);
@@ -774,9 +778,11 @@ int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int
     float *ob = ar.get<float>(N * HD);
     float *dS = ar.get<float>(E * dims->H);
     int32_t *kid = ar.get<int32_t>(E);
-    int32_t *cnt = ar.get<int32_t>(N);
+    int32_t *cnt = ar.get<int32_t>(reverse_index_count_ints(N));
     int32_t *off = ar.get<int32_t>(N + 1);
     int32_t *list = ar.get<int32_t>(E);
+    int32_t *inv = ar.get<int32_t>(E);
+    float *Pk = ar.get<float>(E * dims->H);
     float *pwp = ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
     float *psf = ar.get<float>(dims->V);              // pair parameters in fp32
     float *wpf = ar.get<float>(dims->V * dims->H);
@@ -792,7 +798,7 @@ int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int
     sa.ps = psf; sa.wp = wpf; sa.P = attention ? attention : P; sa.o = o ? o : ob;
     sa.kid = kid; sa.d_att = d_attention; sa.d_o = d_o; sa.dS = dS; sa.dq = dq; sa.dk = dk;
     sa.dv = dv; sa.d_pair = af3 ? d_pair : nullptr; sa.pw_partial = pwp; sa.count = cnt;
-    sa.offset = off; sa.list = list; sa.sc = sc;
+    sa.offset = off; sa.list = list; sa.sc = sc; sa.inv = inv; sa.Pk = Pk;
     if (af3 && e == hipSuccess) {
         e = to_f32(pair_scale, dtype, 1, (int)dims->V, dims->V, psf, nullptr, s);
         if (e == hipSuccess)

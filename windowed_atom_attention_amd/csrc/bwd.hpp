@@ -151,10 +151,18 @@ hipError_t pool_bwd(int B, int A, int T, int U, const uint8_t *usable, const int
 // Reverse index: for entries e < n with key_of[e] >= 0, list holds the
 // entries of key k at offset[k] .. offset[k+1]-1, in ascending entry order
 // for every key with at most kSortCap entries (longer lists keep their fill
-// order). count/cursor: nkeys ints of scratch.
+// order).
+// count/cursor: nkeys ints plus the scan's tile totals
+// (reverse_index_count_ints(nkeys) ints in all).
 constexpr int kSortCap = 2048;
+inline int64_t reverse_index_count_ints(int64_t nkeys) { return nkeys + nkeys / 2048 + 2; }
 hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *count,
                          int32_t *offset, int32_t *list, hipStream_t s);
+
+// inv[e] = position of entry e in list (-1 for entries not listed), for
+// entries e < n.
+hipError_t reverse_index_inverse(const int32_t *offset, int nkeys, const int32_t *list,
+                                 int64_t n, int32_t *inv, hipStream_t s);
 
 // out[k, :] = sum over list entries e of key k (in list order) of X[e, :].
 hipError_t segment_sum(int nkeys, int W, const int32_t *offset, const int32_t *list,
@@ -183,7 +191,10 @@ struct SlotBwdArgs {
     int32_t *kid;
     // backward
     const float *d_att, *d_o; // d_att may be null
-    float *dS;                // [B,H,A,K]: gradient of the logits
+    // the logits' gradients and the weights in the key-major order of the
+    // reverse index: [list position][H]
+    float *dS, *Pk;
+    int32_t *inv;             // [B*A*K]: list position of each slot entry, or -1
     float *dq, *dk, *dv;      // [B*A, H*D]
     float *d_pair;            // [B,A,K,V] or null
     float *pw_partial;        // per-workgroup sums for d_pair_scale / d_w_pair
@@ -192,8 +203,8 @@ struct SlotBwdArgs {
 };
 int slot_bwd_supported(int K, int H, int D, int V, int style);
 hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s);
-// Query side: dS, dq, d_pair and the pair-parameter partial sums; then the
-// key side: dk, dv from the reverse index of kid.
+// The reverse index of kid; the query side: dS, dq, d_pair and the
+// pair-parameter partial sums; then the key side: dk, dv.
 hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float *d_w_pair,
                     hipStream_t s);
 // Floats of pair-parameter partial sums slot_bwd uses for B*A query rows.

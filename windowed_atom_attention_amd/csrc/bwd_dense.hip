@@ -586,32 +586,86 @@ __global__ __launch_bounds__(256) void k_ri_count(const int32_t *key_of, int64_t
         atomicAdd(&count[k], 1);
 }
 
-// Exclusive scan of count into offset[0..nkeys], one workgroup: each thread
-// sums a contiguous chunk, the chunk totals are scanned in LDS.
-__global__ __launch_bounds__(1024) void k_ri_scan(const int32_t *count, int nkeys,
-                                                  int32_t *offset) {
+// Exclusive scan of count into offset[0..nkeys] in three launches: each
+// workgroup scans a tile of kScanTile keys (8 consecutive per thread, wave
+// scans by lane exchanges) and writes the tile's total to bsum; one
+// workgroup scans the totals; then every offset gets its tile's prefix.
+constexpr int kScanTile = 2048;
+
+__global__ __launch_bounds__(256) void k_ri_scan_local(const int32_t *count, int nkeys,
+                                                       int32_t *offset, int32_t *bsum) {
+    __shared__ int32_t wsum[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kScanTile + t * 8;
+    int32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = base + i < nkeys ? count[base + i] : 0;
+    int32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int32_t c = v[i];
+        v[i] = tot;
+        tot += c;
+    }
+    int32_t x = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        wsum[w] = x;
+    __syncthreads();
+    int32_t pre = 0;
+    for (int ww = 0; ww < w; ++ww)
+        pre += wsum[ww];
+    const int32_t excl = pre + x - tot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (base + i < nkeys)
+            offset[base + i] = excl + v[i];
+    if (t == 0)
+        bsum[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// bsum[0..nb) -> exclusive prefix, bsum[nb] = total (one workgroup, chunks
+// of 1024 with a carried sum)
+__global__ __launch_bounds__(1024) void k_ri_scan_top(int32_t *bsum, int nb) {
     __shared__ int32_t sh[1024];
     const int t = threadIdx.x;
-    const int chunk = (nkeys + 1023) / 1024;
-    const int beg = min(nkeys, t * chunk), end = min(nkeys, beg + chunk);
-    int32_t s = 0;
-    for (int i = beg; i < end; ++i)
-        s += count[i];
-    sh[t] = s;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = t >= off ? sh[t - off] : 0;
+    int32_t carry = 0;
+    for (int c0 = 0; c0 < nb; c0 += 1024) {
+        const int i = c0 + t;
+        const int32_t v = i < nb ? bsum[i] : 0;
+        sh[t] = v;
         __syncthreads();
-        sh[t] += v;
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t y = t >= off ? sh[t - off] : 0;
+            __syncthreads();
+            sh[t] += y;
+            __syncthreads();
+        }
+        if (i < nb)
+            bsum[i] = carry + sh[t] - v;
+        carry += sh[1023];
         __syncthreads();
     }
-    int32_t run = sh[t] - s;
-    for (int i = beg; i < end; ++i) {
-        offset[i] = run;
-        run += count[i];
-    }
-    if (t == 1023)
-        offset[nkeys] = sh[1023];
+    if (t == 0)
+        bsum[nb] = carry;
+}
+
+// offset[i] += its tile's prefix; count[i] = 0 (the fill's cursor)
+__global__ __launch_bounds__(256) void k_ri_scan_add(int32_t *offset, int32_t *count, int nkeys,
+                                                     const int32_t *bsum, int nb) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i == 0)
+        offset[nkeys] = bsum[nb];
+    if (i >= nkeys)
+        return;
+    offset[i] += bsum[i / kScanTile];
+    count[i] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_ri_fill(const int32_t *key_of, int64_t n,
@@ -660,6 +714,15 @@ __global__ __launch_bounds__(256) void k_ri_sort(const int32_t *offset, int nkey
                 rank += sh[w][m] < x ? 1 : 0;
             list[o + rank] = x;
         }
+}
+
+// inv[list[p]] = p for every listed entry (inv pre-filled with -1)
+__global__ __launch_bounds__(256) void k_ri_inverse(const int32_t *offset, int nkeys,
+                                                    const int32_t *list, int32_t *inv) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= offset[nkeys])
+        return;
+    inv[list[p]] = (int32_t)p;
 }
 
 __global__ __launch_bounds__(256) void k_segment_sum(int nkeys, int W, const int32_t *offset,
@@ -901,15 +964,30 @@ hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *c
                        (int64_t)nkeys, 0);
     if (n > 0)
         hipLaunchKernelGGL(k_ri_count, dim3(nblk(n, 256)), dim3(256), 0, s, key_of, n, count);
-    hipLaunchKernelGGL(k_ri_scan, dim3(1), dim3(1024), 0, s, (const int32_t *)count, nkeys,
-                       offset);
-    hipLaunchKernelGGL(k_fill_int, dim3(nblk(nkeys, 256)), dim3(256), 0, s, count,
-                       (int64_t)nkeys, 0);
+    // tile totals after the nkeys counts (the caller sizes count with
+    // reverse_index_count_ints)
+    const int nb = (int)nblk(nkeys, kScanTile);
+    int32_t *bsum = count + nkeys;
+    if (nb > 0)
+        hipLaunchKernelGGL(k_ri_scan_local, dim3((unsigned)nb), dim3(256), 0, s,
+                           (const int32_t *)count, nkeys, offset, bsum);
+    hipLaunchKernelGGL(k_ri_scan_top, dim3(1), dim3(1024), 0, s, bsum, nb);
+    hipLaunchKernelGGL(k_ri_scan_add, dim3(nblk(nkeys + 1, 256)), dim3(256), 0, s, offset, count,
+                       nkeys, (const int32_t *)bsum, nb);
     if (n > 0)
         hipLaunchKernelGGL(k_ri_fill, dim3(nblk(n, 256)), dim3(256), 0, s, key_of, n,
                            (const int32_t *)offset, count, list);
     hipLaunchKernelGGL(k_ri_sort, dim3(nblk(nkeys, 4)), dim3(256), 0, s,
                        (const int32_t *)offset, nkeys, list);
+    return hipGetLastError();
+}
+
+hipError_t reverse_index_inverse(const int32_t *offset, int nkeys, const int32_t *list,
+                                 int64_t n, int32_t *inv, hipStream_t s) {
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_fill_int, dim3(nblk(n, 256)), dim3(256), 0, s, inv, n, -1);
+    hipLaunchKernelGGL(k_ri_inverse, dim3(nblk(n, 256)), dim3(256), 0, s, offset, nkeys, list, inv);
     return hipGetLastError();
 }
 

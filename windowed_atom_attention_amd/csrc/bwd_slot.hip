@@ -37,8 +37,9 @@ struct SK {
 };
 
 // LDS floats per wave: key ids [K], per-slot values [K*H], one head's slot
-// values [K], one query row [HD].
-__host__ __device__ inline int wave_floats(int K, int H, int HD) { return K + K * H + K + HD; }
+// values [K], one query row [HD], the weights of every head [K*H] (query
+// side of the backward).
+__host__ __device__ inline int wave_floats(int K, int H, int HD) { return K + K * H + K + HD + K * H; }
 
 // Channels 4 qv .. 4 qv + 3 of pair row `row` (zeros past V): one 8- or
 // 16-byte load when V is a multiple of 4, else element loads.
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     float *sdl = base + K;
     float *sP = sdl + K * H;
     float *sdo = sP + K;
+    float *spa = sdo + HD;
     const int64_t N = (int64_t)a.B * a.A;
     const int64_t n = (int64_t)blockIdx.x * 4 + w;
     const bool live = n < N;
@@ -352,6 +354,7 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
             dw[c] = 0.0f;
             if (s < K && skid[s] >= 0) {
                 pw[c] = a.P[rowbase + s];
+                spa[s * H + h] = pw[c];
                 const float x = (a.d_att ? a.d_att[rowbase + s] : 0.0f) + vd[c];
                 dw[c] = x;
                 dsum += pw[c] * x;
@@ -365,8 +368,6 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
                 const float dl = pw[c] * (dw[c] - dsum);
                 sP[s] = dl;
                 sdl[s * H + h] = dl;
-                if (live)
-                    a.dS[rowbase + s] = dl;
             }
         }
         __syncthreads();
@@ -379,6 +380,28 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
             *reinterpret_cast<float4 *>(a.dq + nn * HD + h * D + lane * 4) = acc;
         }
         __syncthreads();
+    }
+
+    // every head's dS and P of an allowed slot go to the slot's place in the
+    // reverse index (key-major), H values together
+    for (int s = lane; s < K; s += 64) {
+        const int pos = (live && skid[s] >= 0) ? a.inv[nn * K + s] : -1;
+        if (pos < 0)
+            continue;
+        float *dd = a.dS + (int64_t)pos * H;
+        float *pp = a.Pk + (int64_t)pos * H;
+        if (H % 4 == 0) { // 16-byte global stores (LDS read element-wise: K may be odd)
+            for (int h = 0; h < H; h += 4) {
+                const float *x = sdl + s * H + h, *y = spa + s * H + h;
+                *reinterpret_cast<float4 *>(dd + h) = make_float4(x[0], x[1], x[2], x[3]);
+                *reinterpret_cast<float4 *>(pp + h) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+        } else {
+            for (int h = 0; h < H; ++h) {
+                dd[h] = sdl[s * H + h];
+                pp[h] = spa[s * H + h];
+            }
+        }
     }
 
     if constexpr (AF3) {
@@ -516,11 +539,10 @@ __global__ __launch_bounds__(256) void k_slot_bwd_kv(SK p) {
                 ws[u] = wp[u] = 0.0f;
                 rq[u] = ro[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 if (act && idx < cnt) {
-                    const int64_t n = e / K, s = e - n * K;
-                    const int64_t b = n / a.A, qa = n - b * a.A;
-                    const int64_t at = ((b * H + h) * a.A + qa) * K + s;
+                    const int64_t n = e / K;
+                    const int64_t at = (int64_t)(base + idx) * H + h; // key-major
                     ws[u] = a.dS[at];
-                    wp[u] = a.P[at];
+                    wp[u] = a.Pk[at];
                     rq[u] = *reinterpret_cast<const float4 *>(a.q + n * HD + q * 4);
                     ro[u] = *reinterpret_cast<const float4 *>(a.d_o + n * HD + q * 4);
                 }
@@ -633,7 +655,17 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
     SK p{a, 1.0f / sqrtf((float)a.D)};
     const size_t lds = 4 * sizeof(float) * (size_t)wave_floats(a.K, a.H, a.H * a.D);
     const dim3 grid(nblk(N, 4));
-    ProfSpan sp = prof_begin(KN_BWD_SLOT_Q, s);
+    // reverse index of the slot -> key map and each entry's place in it
+    ProfSpan sp = prof_begin(KN_BWD_SLOT_KV, s);
+    {
+        hipError_t e0 = reverse_index(a.kid, N * a.K, (int)N, a.count, a.offset, a.list, s);
+        if (e0 == hipSuccess)
+            e0 = reverse_index_inverse(a.offset, (int)N, a.list, N * a.K, a.inv, s);
+        if (e0 != hipSuccess)
+            return e0;
+    }
+    prof_end(sp, s);
+    sp = prof_begin(KN_BWD_SLOT_Q, s);
     switch (a.D) {
     case 8: launch_bwd_q<8>(p, style, lds, grid, s); break;
     case 16: launch_bwd_q<16>(p, style, lds, grid, s); break;
@@ -662,9 +694,6 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
             return e;
     }
     sp = prof_begin(KN_BWD_SLOT_KV, s);
-    e = reverse_index(a.kid, N * a.K, (int)N, a.count, a.offset, a.list, s);
-    if (e != hipSuccess)
-        return e;
     hipLaunchKernelGGL(k_slot_bwd_kv, grid, dim3(256), 0, s, p);
     prof_end(sp, s);
     return hipGetLastError();
