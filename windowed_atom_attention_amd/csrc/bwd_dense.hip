@@ -321,11 +321,44 @@ struct EwK {
     const float *vec, *vec2, *vec3;
     const uint8_t *mask;
     int blk0; // first workgroup of the job in a group launch
+    int v4;   // four consecutive columns per thread (16-byte accesses)
 };
 struct EwGroupK {
     EwK job[kGroupJobs];
     int n;
 };
+
+__device__ __forceinline__ float ew_op(int op, float a, float b, float c, float d, float vc,
+                                       float vc2, float vc3) {
+    switch (op) {
+    case EW_COPY: return a;
+    case EW_ADD: return a + b;
+    case EW_MUL: return a * b;
+    case EW_MUL_VEC: return a * vc;
+    case EW_AFFINE: return a * b + c;
+    case EW_AFFINE1: return a * (1.0f + b) + c;
+    case EW_MUL1: return a * (1.0f + b);
+    case EW_SIGMOID: return sigmoid_f(a);
+    case EW_SIGMOID_VEC: return sigmoid_f(a + vc);
+    case EW_SILU: return silu_f(a);
+    case EW_SWIGLU: return silu_f(a) * b;
+    case EW_RESID: return a + b * c;
+    case EW_RESID_MASK: return a + b * c;
+    case EW_MASK: return a;
+    case EW_DSIG: return a * b * (1.0f - b);
+    case EW_DGATE: return a * b * c * (1.0f - c);
+    case EW_DSWIGLU_A: return a * c * dsilu_f(b);
+    case EW_DSWIGLU_B: return a * silu_f(b);
+    case EW_DSILU: return a * dsilu_f(b);
+    case EW_ADD_VEC: return a + vc;
+    case EW_ZERO: return 0.0f;
+    case EW_FMA2: return a * b + c * d;
+    case EW_MUL_VEC3: return a * vc + b * vc2 + c * vc3;
+    default: return 0.0f;
+    }
+}
+
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
 __global__ __launch_bounds__(256) void k_ew(EwGroupK G) {
     int j = 0;
@@ -333,6 +366,38 @@ __global__ __launch_bounds__(256) void k_ew(EwGroupK G) {
         ++j;
     const EwK &e = G.job[j];
     const int64_t i = (int64_t)((int)blockIdx.x - e.blk0) * 256 + threadIdx.x;
+    if (e.v4) {
+        const int W4 = e.W >> 2;
+        if (i >= (int64_t)e.rows * W4)
+            return;
+        const int r = (int)(i / W4), col = (int)(i - (int64_t)r * W4) * 4;
+        const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float4 a = e.a ? ld4(e.a + (int64_t)r * e.lda + col) : z;
+        const float4 b = e.b ? ld4(e.b + (int64_t)r * e.ldb + col) : z;
+        const float4 c = e.c ? ld4(e.c + (int64_t)r * e.ldc + col) : z;
+        const float4 d = e.d ? ld4(e.d + (int64_t)r * e.ldd + col) : z;
+        const float4 v1 = e.vec ? ld4(e.vec + col) : z;
+        const float4 v2 = e.vec2 ? ld4(e.vec2 + col) : z;
+        const float4 v3 = e.vec3 ? ld4(e.vec3 + col) : z;
+        const bool m = e.mask ? e.mask[r] != 0 : true;
+        float4 x;
+        x.x = ew_op(e.op, a.x, b.x, c.x, d.x, v1.x, v2.x, v3.x);
+        x.y = ew_op(e.op, a.y, b.y, c.y, d.y, v1.y, v2.y, v3.y);
+        x.z = ew_op(e.op, a.z, b.z, c.z, d.z, v1.z, v2.z, v3.z);
+        x.w = ew_op(e.op, a.w, b.w, c.w, d.w, v1.w, v2.w, v3.w);
+        if (!m)
+            x = z;
+        float4 *dst = reinterpret_cast<float4 *>(e.o + (int64_t)r * e.ldo + col);
+        if (e.acc) {
+            const float4 o = *dst;
+            x.x += o.x;
+            x.y += o.y;
+            x.z += o.z;
+            x.w += o.w;
+        }
+        *dst = x;
+        return;
+    }
     if (i >= (int64_t)e.rows * e.W)
         return;
     const int r = (int)(i / e.W), col = (int)(i - (int64_t)r * e.W);
@@ -341,34 +406,10 @@ __global__ __launch_bounds__(256) void k_ew(EwGroupK G) {
     const float c = e.c ? e.c[(int64_t)r * e.ldc + col] : 0.0f;
     const float d = e.d ? e.d[(int64_t)r * e.ldd + col] : 0.0f;
     const float vc = e.vec ? e.vec[col] : 0.0f;
+    const float vc2 = e.vec2 ? e.vec2[col] : 0.0f;
+    const float vc3 = e.vec3 ? e.vec3[col] : 0.0f;
     const bool m = e.mask ? e.mask[r] != 0 : true;
-    float x;
-    switch (e.op) {
-    case EW_COPY: x = a; break;
-    case EW_ADD: x = a + b; break;
-    case EW_MUL: x = a * b; break;
-    case EW_MUL_VEC: x = a * vc; break;
-    case EW_AFFINE: x = a * b + c; break;
-    case EW_AFFINE1: x = a * (1.0f + b) + c; break;
-    case EW_MUL1: x = a * (1.0f + b); break;
-    case EW_SIGMOID: x = sigmoid_f(a); break;
-    case EW_SIGMOID_VEC: x = sigmoid_f(a + vc); break;
-    case EW_SILU: x = silu_f(a); break;
-    case EW_SWIGLU: x = silu_f(a) * b; break;
-    case EW_RESID: x = a + b * c; break;
-    case EW_RESID_MASK: x = a + b * c; break;
-    case EW_MASK: x = a; break;
-    case EW_DSIG: x = a * b * (1.0f - b); break;
-    case EW_DGATE: x = a * b * c * (1.0f - c); break;
-    case EW_DSWIGLU_A: x = a * c * dsilu_f(b); break;
-    case EW_DSWIGLU_B: x = a * silu_f(b); break;
-    case EW_DSILU: x = a * dsilu_f(b); break;
-    case EW_ADD_VEC: x = a + vc; break;
-    case EW_ZERO: x = 0.0f; break;
-    case EW_FMA2: x = a * b + c * d; break;
-    case EW_MUL_VEC3: x = a * vc + b * e.vec2[col] + c * e.vec3[col]; break;
-    default: x = 0.0f; break;
-    }
+    float x = ew_op(e.op, a, b, c, d, vc, vc2, vc3);
     if (!m)
         x = 0.0f;
     float *dst = e.o + (int64_t)r * e.ldo + col;
@@ -848,9 +889,17 @@ hipError_t ew_group(const EwJob *jobs, int n, hipStream_t s) {
         const int64_t cnt = (int64_t)x.rows * x.W;
         if (cnt <= 0)
             continue;
+        // 16-byte accesses when every row of every operand starts aligned
+        auto ok4 = [](const float *p, int64_t ld) {
+            return !p || (((uintptr_t)p & 15u) == 0 && ld % 4 == 0);
+        };
+        auto okv = [](const float *p) { return !p || ((uintptr_t)p & 15u) == 0; };
+        const int v4 = (x.W % 4 == 0 && ok4(x.o.p, x.o.ld) && ok4(x.a.p, x.a.ld) &&
+                        ok4(x.b.p, x.b.ld) && ok4(x.c.p, x.c.ld) && ok4(x.d.p, x.d.ld) &&
+                        okv(x.vec) && okv(x.vec2) && okv(x.vec3)) ? 1 : 0;
         G.job[m] = EwK{(int)x.op, x.rows, x.W, x.acc, x.o.p, x.o.ld, x.a.p, x.b.p, x.c.p, x.d.p,
-                       x.a.ld, x.b.ld, x.c.ld, x.d.ld, x.vec, x.vec2, x.vec3, x.mask, blk};
-        blk += (int)nblk(cnt, 256);
+                       x.a.ld, x.b.ld, x.c.ld, x.d.ld, x.vec, x.vec2, x.vec3, x.mask, blk, v4};
+        blk += (int)nblk(v4 ? cnt / 4 : cnt, 256);
         ++m;
     }
     if (m == 0)
