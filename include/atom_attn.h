@@ -231,7 +231,8 @@ int atom_attn_slot_attention(const atom_attn_dims *dims, int style, int dtype,
  *
  * Supported set: K <= 512; H <= 8; D one of 8, 16, 32, 64; H*D <= 256;
  * AF3: V <= 16 and H <= 4; C, S, M, U <= 4096; B*A < 2^30;
- * B*A*K*max(H, V) < 2^31. Otherwise EUNSUPPORTED. Status codes as the block
+ * B*A*K*max(H, V) < 2^31; B*A*max(6C, S, M, U, H*D) <= 2^34. Otherwise
+ * EUNSUPPORTED. Status codes as the block
  * call; workspace (256-byte aligned) of atom_attn_backward_workspace_bytes()
  * bytes. Asynchronous on `stream`. */
 typedef struct {

@@ -226,6 +226,9 @@ def test_backward_workspace_query_status_codes():
     assert _bws(_dims(H=5, D=16), style=N.ESMFOLD2)[0] == N.OK
     assert _bws(_dims(V=17))[0] == N.EUNSUPPORTED
     assert _bws(_dims(V=17), style=N.ESMFOLD2)[0] == N.OK   # no pair there
+    # rows x widest intermediate (6C) above 2^34 elements
+    assert _bws(_dims(A=1 << 21, C=4096, K=8))[0] == N.EUNSUPPORTED
+    assert _bws(_dims(A=1 << 18, C=4096, K=8))[0] == N.OK
     # dense widths need not be multiples of 32 here
     assert _bws(_dims(C=48, S=40, M=72, U=20))[0] == N.OK
     # decoder keeps the token projection and its reverse index

@@ -54,6 +54,12 @@ int bwd_shape_ok(const atom_attn_dims *d, int style) {
     for (int64_t x : widths)
         if (x > 4096)
             return ATOM_ATTN_EUNSUPPORTED;
+    // every intermediate (rows x widest row, 6C for the ESMFold2 modulations)
+    // below 2^34 elements: the grouped launches count workgroups and tiles
+    // of up to eight such jobs in 32 bits
+    const int64_t wmax = std::max<int64_t>({6 * d->C, d->S, d->M, d->U, d->H * d->D});
+    if (N * wmax > ((int64_t)1 << 34))
+        return ATOM_ATTN_EUNSUPPORTED;
     return ATOM_ATTN_OK;
 }
 
