@@ -117,6 +117,8 @@ CASES = [
     ("0", dict(A=200, K=48, style="esmfold2", H=8, D=16)),
     ("0", dict(A=120, H=2, D=8, K=24, style="esmfold2", stage="decoder")),
     ("0", dict(A=100, C=48, S=40, M=72, U=20)),
+    # 768 query blocks of 16: the block form of the slot step's query side
+    ("4a", dict(A=12288)),
 ]
 
 
@@ -174,13 +176,22 @@ def test_block_backward_full_size_headline_workload():
     _compare(w, din, dpar, ref_in, ref_par)
 
 
-def _slot_inputs(style, B=2, A=70, K=24, H=2, D=16, V=8, seed=4, hub=None, dtype=torch.float32):
+def _slot_inputs(style, B=2, A=70, K=24, H=2, D=16, V=8, seed=4, hub=None, dtype=torch.float32,
+                 local=None):
     g = torch.Generator().manual_seed(seed)
     q = torch.randn((B, A, H * D), generator=g)
     k = torch.randn((B, A, H * D), generator=g)
     v = torch.randn((B, A, H * D), generator=g)
     usable = torch.rand((B, A), generator=g) < 0.9
     ki = torch.randint(-2, A + 2, (B, A, K), generator=g)
+    if local is not None:
+        # key ids within +-local of the query (a narrow band per 16-query
+        # block), except in every eighth block of queries, which keeps the
+        # scattered ids (a wide band)
+        a = torch.arange(A).view(1, A, 1)
+        near = (a + torch.randint(-local, local + 1, (B, A, K), generator=g)).clamp(-1, A)
+        far_block = ((torch.arange(A) // 16) % 8 == 3).view(1, A, 1)
+        ki = torch.where(far_block, ki, near)
     ki[:, :, 1] = ki[:, :, 0]                     # repeats within a row
     if hub is not None:
         ki[:, :, 2:2 + hub] = 5                   # one key selected by many slots
@@ -207,6 +218,11 @@ SLOT_CASES = [
     # and the LDS sort paths)
     ("esmfold2", dict(hub=20, A=120, K=30)),
     ("af3", dict(hub=3, A=200, K=16)),
+    # 768+ query blocks: the block form, with some blocks queued for the
+    # per-query kernel (scattered ids) and repeated keys
+    ("af3", dict(B=48, A=256, K=64, H=4, D=32, V=16, local=40)),
+    ("esmfold2", dict(B=48, A=260, K=48, H=4, D=16, local=30)),
+    ("af3", dict(B=24, A=520, K=128, H=2, D=64, V=8, local=56, dtype=torch.bfloat16)),
 ]
 
 

@@ -80,7 +80,7 @@ struct Bufs {
     float *dh, *dx2, *dtr, *dhh, *da, *dbb, *dz, *dx1, *gt, *du, *dog, *dO, *dGp;
     float *dS, *dq, *dk, *dv, *dqin, *dkvin, *dx0, *dzs[3], *dzg[2], *dcj[3], *dch, *dc, *dmods,
         *ds, *dpu, *dln, *dtp, *dP, *pwp, *part, *part2, *Pk;
-    int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list, *inv;
+    int32_t *tkey, *tcnt, *toff, *tlist, *cnt, *off, *list, *inv, *wide;
 };
 
 void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
@@ -152,7 +152,8 @@ void carve(Arena &ar, const atom_attn_dims *d, int style, int stage, Bufs &b) {
     }
     b.cnt = ar.get<int32_t>(reverse_index_count_ints(N)); b.off = ar.get<int32_t>(N + 1);
     b.list = ar.get<int32_t>(E); b.inv = ar.get<int32_t>(E); b.Pk = f(E * H);
-    b.pwp = f(slot_bwd_partial_floats((int64_t)N, (int)V, (int)H));
+    b.pwp = f(slot_bwd_partial_floats((int64_t)B, (int64_t)A, (int)V, (int)H));
+    b.wide = ar.get<int32_t>(slot_bwd_queue_ints((int64_t)B, (int64_t)A));
     b.part = f(kGemmPartialFloats);
     b.part2 = f(kGemmPartialFloats);
 }
@@ -426,7 +427,7 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
     sa.d_att = gout->attention; sa.d_o = b.dO; sa.dS = b.dS;
     sa.dq = b.dq; sa.dk = b.dk; sa.dv = b.dv; sa.d_pair = (af3 && gin) ? gin->pair : nullptr;
     sa.pw_partial = b.pwp; sa.count = b.cnt; sa.offset = b.off; sa.list = b.list;
-    sa.inv = b.inv; sa.Pk = b.Pk;
+    sa.inv = b.inv; sa.Pk = b.Pk; sa.wide = b.wide;
     sa.sc = r.sc;
     if (r.err == hipSuccess) {
         sp = prof_begin(KN_BWD_SLOT_FWD, s);
@@ -744,10 +745,11 @@ int atom_attn_slot_backward_workspace_bytes(const atom_attn_dims *dims, int styl
     ar.get<int32_t>(E);
     ar.get<int32_t>(E);                           // list position of each entry
     ar.get<float>(E * dims->H);                   // key-major weights
-    ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
+    ar.get<int32_t>(slot_bwd_queue_ints(dims->B, dims->A)); // wide blocks
+    ar.get<float>(slot_bwd_partial_floats(dims->B, dims->A, (int)dims->V, (int)dims->H));
     ar.get<float>(dims->V);                       // pair parameters in fp32
     ar.get<float>(dims->V * dims->H);
-    ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H)); // sums
+    ar.get<float>(slot_bwd_partial_floats(dims->B, dims->A, (int)dims->V, (int)dims->H)); // sums
     *bytes = ar.off + 256;
     return ATOM_ATTN_OK;
 }
@@ -789,10 +791,11 @@ int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int
     int32_t *list = ar.get<int32_t>(E);
     int32_t *inv = ar.get<int32_t>(E);
     float *Pk = ar.get<float>(E * dims->H);
-    float *pwp = ar.get<float>(slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H));
+    int32_t *wq = ar.get<int32_t>(slot_bwd_queue_ints(dims->B, dims->A));
+    float *pwp = ar.get<float>(slot_bwd_partial_floats(dims->B, dims->A, (int)dims->V, (int)dims->H));
     float *psf = ar.get<float>(dims->V);              // pair parameters in fp32
     float *wpf = ar.get<float>(dims->V * dims->H);
-    const size_t pcap = slot_bwd_partial_floats((int64_t)N, (int)dims->V, (int)dims->H);
+    const size_t pcap = slot_bwd_partial_floats(dims->B, dims->A, (int)dims->V, (int)dims->H);
     float *cpart = ar.get<float>(pcap);
     const Scratch sc{cpart, pcap};
     hipError_t e = hipSuccess;
@@ -804,7 +807,7 @@ int atom_attn_slot_attention_backward(const atom_attn_dims *dims, int style, int
     sa.ps = psf; sa.wp = wpf; sa.P = attention ? attention : P; sa.o = o ? o : ob;
     sa.kid = kid; sa.d_att = d_attention; sa.d_o = d_o; sa.dS = dS; sa.dq = dq; sa.dk = dk;
     sa.dv = dv; sa.d_pair = af3 ? d_pair : nullptr; sa.pw_partial = pwp; sa.count = cnt;
-    sa.offset = off; sa.list = list; sa.sc = sc; sa.inv = inv; sa.Pk = Pk;
+    sa.offset = off; sa.list = list; sa.sc = sc; sa.inv = inv; sa.Pk = Pk; sa.wide = wq;
     if (af3 && e == hipSuccess) {
         e = to_f32(pair_scale, dtype, 1, (int)dims->V, dims->V, psf, nullptr, s);
         if (e == hipSuccess)

@@ -111,6 +111,9 @@ struct EwJob {
 };
 hipError_t ew_group(const EwJob *jobs, int n, hipStream_t s);
 
+// p[0..n) = v
+hipError_t fill_int(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+
 // Row normalisation without affine terms (mode 0 LayerNorm, 1 RMS): xhat
 // and the row's 1/sqrt(var + eps) (resp. 1/sqrt(mean x^2 + eps)).
 hipError_t norm_rows(int mode, int rows, int W, float eps, View x, View xhat, float *rstd,
@@ -195,6 +198,9 @@ struct SlotBwdArgs {
     // reverse index: [list position][H]
     float *dS, *Pk;
     int32_t *inv;             // [B*A*K]: list position of each slot entry, or -1
+    int32_t *wide;            // queue of 16-query blocks with a wide key band
+                              // (count, then block ids; null: no block form)
+    int rec0;                 // first pair-parameter record of a launch
     float *dq, *dk, *dv;      // [B*A, H*D]
     float *d_pair;            // [B,A,K,V] or null
     float *pw_partial;        // per-workgroup sums for d_pair_scale / d_w_pair
@@ -207,8 +213,10 @@ hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s);
 // pair-parameter partial sums; then the key side: dk, dv.
 hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float *d_w_pair,
                     hipStream_t s);
-// Floats of pair-parameter partial sums slot_bwd uses for B*A query rows.
-size_t slot_bwd_partial_floats(int64_t rows, int V, int H);
+// Floats of pair-parameter partial sums slot_bwd uses for B batches of A
+// query rows, and the ints of its queue of wide blocks.
+size_t slot_bwd_partial_floats(int64_t B, int64_t A, int V, int H);
+int64_t slot_bwd_queue_ints(int64_t B, int64_t A);
 
 } // namespace bwd
 } // namespace waa

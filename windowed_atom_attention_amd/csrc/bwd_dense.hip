@@ -1031,6 +1031,13 @@ hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *c
     return hipGetLastError();
 }
 
+hipError_t fill_int(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_fill_int, dim3(nblk(n, 256)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
 hipError_t reverse_index_inverse(const int32_t *offset, int nkeys, const int32_t *list,
                                  int64_t n, int32_t *inv, hipStream_t s) {
     if (n <= 0)

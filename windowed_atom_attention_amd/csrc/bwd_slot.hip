@@ -330,8 +330,25 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     float *sdo = sP + K;
     float *spa = sdo + HD;
     const int64_t N = (int64_t)a.B * a.A;
-    const int64_t n = (int64_t)blockIdx.x * 4 + w;
-    const bool live = n < N;
+    int64_t n = (int64_t)blockIdx.x * 4 + w;
+    bool live = n < N;
+    const int rec = a.rec0 + (int)blockIdx.x; // pair-parameter partial record
+    if (a.wide) {
+        // queue mode: four workgroups per queued 16-query block
+        const int qi = (int)blockIdx.x >> 2;
+        if (qi >= a.wide[0]) {
+            if constexpr (AF3) {
+                constexpr int W = kPairV + kPairV * kPairH;
+                for (int i = threadIdx.x; i < W; i += 256)
+                    a.pw_partial[(int64_t)rec * W + i] = 0.0f;
+            }
+            return;
+        }
+        const int blk = a.wide[1 + qi], nqb = (a.A + 15) / 16;
+        const int qa0 = (blk % nqb) * 16 + ((int)blockIdx.x & 3) * 4 + w;
+        live = qa0 < a.A;
+        n = (int64_t)(blk / nqb) * a.A + qa0;
+    }
     const int64_t nn = live ? n : 0;
     const int64_t b = nn / a.A, qa = nn - b * a.A;
 
@@ -502,8 +519,322 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
         __syncthreads();
         constexpr int W = kPairV + kPairV * kPairH;
         for (int i = threadIdx.x; i < W; i += 256)
-            a.pw_partial[(int64_t)blockIdx.x * W + i] =
+            a.pw_partial[(int64_t)rec * W + i] =
                 ((wred[0][i] + wred[1][i]) + wred[2][i]) + wred[3][i];
+    }
+}
+
+// ---------------------------------------------------------------------
+// Block form of the query side (K <= 128, H <= 4, D >= 16): one workgroup
+// per block of 16 consecutive query atoms whose allowed key ids lie in a
+// band of at most kBandRows rows. The two products over the band run on
+// the matrix cores with each band row read once per block instead of once
+// per slot: G = dO_block . V_band^T (per head a 16 x band tile in LDS,
+// read by each slot at its key), then dS per slot (16 threads per query,
+// slot jq + 16 i), scattered by key into the tile (repeated keys add), and
+// dQ = dS_tile . K_band. Blocks with a wider band go to a queue that the
+// per-query kernel takes.
+constexpr int kBandRows = 128, kBandPitch = kBandRows + 4;
+constexpr int kBlockMinBlocks = 768; // grids from which the block form is used
+
+__host__ __device__ inline int block_lds_floats() { return kPairH * 16 * kBandPitch; }
+
+template <typename TP, bool AF3, int D>
+__global__ __launch_bounds__(256) void k_slot_bwd_qb(SK p) {
+    extern __shared__ __align__(16) float smem[];
+    __shared__ int s_lo, s_hi;
+    __shared__ float wred[4][kPairV + kPairV * kPairH];
+    constexpr int SPL = 8, NKC = D / 16, W = kPairV + kPairV * kPairH;
+    const SlotBwdArgs &a = p.a;
+    const int K = a.K, H = a.H, HD = H * D, A = a.A;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int q = tid >> 4, jq = tid & 15;    // query of the block, its thread
+    const int l16 = lane & 15, g4 = lane >> 4; // matrix-core lane coordinates
+    const int nqb = (A + 15) / 16;
+    const int b = (int)blockIdx.x / nqb, a0 = ((int)blockIdx.x - b * nqb) * 16;
+    const int64_t bA = (int64_t)b * A;
+    const bool live = a0 + q < A;
+    const int64_t n = bA + a0 + (live ? q : 0);
+    float *tile = smem; // [head][16][kBandPitch]
+
+    // allowed key ids of this thread's slots, relative to the batch
+    int rel[SPL];
+    int lo = INT_MAX, hi = -1;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int sl = jq + 16 * i;
+        rel[i] = -1;
+        if (live && sl < K) {
+            const int id = a.kid[n * K + sl];
+            rel[i] = id >= 0 ? (int)(id - bA) : -1;
+        }
+        if (rel[i] >= 0) {
+            lo = min(lo, rel[i]);
+            hi = max(hi, rel[i]);
+        }
+    }
+    if (tid == 0) {
+        s_lo = INT_MAX;
+        s_hi = -1;
+    }
+    __syncthreads();
+    lo = wave_min_i(lo);
+    hi = wave_max_i(hi);
+    if (lane == 0) {
+        atomicMin(&s_lo, lo);
+        atomicMax(&s_hi, hi);
+    }
+    __syncthreads();
+    const int bhi = s_hi, blo = bhi >= 0 ? s_lo : 0;
+    const bool any = bhi >= 0;
+    const int rows = any ? bhi + 1 - blo : 0;
+    if (rows > kBandRows) {
+        // scattered ids: the per-query kernel takes this block
+        if (tid == 0)
+            a.wide[1 + atomicAdd(a.wide, 1)] = (int)blockIdx.x;
+        if constexpr (AF3)
+            for (int i = tid; i < W; i += 256)
+                a.pw_partial[(int64_t)blockIdx.x * W + i] = 0.0f;
+        return;
+    }
+    const int ncb = (rows + 15) / 16;
+    const int hw = w; // this wave's head in the two products
+    const bool hv = hw < H && any;
+
+    // ---- G = dO . V_band^T: query l16, band row 16 cb + l16
+    if (hv) {
+        uint4 af[NKC];
+        const bool qin = a0 + l16 < A;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            af[kc] = make_uint4(0, 0, 0, 0);
+            if (qin)
+                af[kc] = *reinterpret_cast<const uint4 *>(a.d_o + (bA + a0 + l16) * HD + hw * D + kc * 16 + g4 * 4);
+        }
+        for (int cb0 = 0; cb0 < ncb; cb0 += 4) {
+            uint4 vb[4][NKC];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = (cb0 + t) * 16 + l16;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    vb[t][kc] = make_uint4(0, 0, 0, 0);
+                    if (r < rows)
+                        vb[t][kc] = *reinterpret_cast<const uint4 *>(a.v + (bA + blo + r) * HD + hw * D + kc * 16 + g4 * 4);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (cb0 + t >= ncb)
+                    break;
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+                    Mma16<float>::mma(acc, af[kc], vb[t][kc]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    tile[(hw * 16 + acc16_row(v, lane)) * kBandPitch + (cb0 + t) * 16 + acc16_col(lane)] = acc[v];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- dS per slot and head: dW = dA + G[key], dS = P (dW - sum P dW)
+    float dsv[SPL][kPairH], pv[SPL][kPairH];
+#pragma unroll
+    for (int h = 0; h < kPairH; ++h) {
+        float dsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            dsv[i][h] = 0.0f;
+            pv[i][h] = 0.0f;
+            if (h < H && rel[i] >= 0) {
+                const int64_t at = (((int64_t)b * H + h) * A + a0 + q) * K + jq + 16 * i;
+                const float P = a.P[at];
+                const float x = (a.d_att ? a.d_att[at] : 0.0f) + tile[(h * 16 + q) * kBandPitch + rel[i] - blo];
+                pv[i][h] = P;
+                dsv[i][h] = x;
+                dsum += P * x;
+            }
+        }
+        dsum = sum16(dsum);
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            dsv[i][h] = pv[i][h] * (dsv[i][h] - dsum);
+    }
+    __syncthreads(); // G read
+    for (int i = tid; i < block_lds_floats() / 4; i += 256)
+        reinterpret_cast<float4 *>(tile)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    __syncthreads();
+    // dS into the tile by key (a query's repeated keys add, in slot order)
+#pragma unroll
+    for (int h = 0; h < kPairH; ++h)
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            if (h < H && rel[i] >= 0)
+                atomicAdd(&tile[(h * 16 + q) * kBandPitch + rel[i] - blo], dsv[i][h]);
+    __syncthreads();
+
+    // ---- dQ = dS_tile . K_band / sqrt(D): query l16, channel 16 db + l16
+    if (hw < H) {
+        f32x4_t acc[NKC];
+#pragma unroll
+        for (int db = 0; db < NKC; ++db)
+            acc[db] = zero4();
+        for (int kc = 0; kc < ncb; ++kc) {
+            const uint4 av = *reinterpret_cast<const uint4 *>(tile + (hw * 16 + l16) * kBandPitch + kc * 16 + g4 * 4);
+            float kv[NKC][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = kc * 16 + g4 * 4 + t;
+#pragma unroll
+                for (int db = 0; db < NKC; ++db)
+                    kv[db][t] = r < rows ? a.k[(bA + blo + r) * HD + hw * D + db * 16 + l16] : 0.0f;
+            }
+#pragma unroll
+            for (int db = 0; db < NKC; ++db)
+                Mma16<float>::mma(acc[db], av, make_uint4(__float_as_uint(kv[db][0]), __float_as_uint(kv[db][1]),
+                                                          __float_as_uint(kv[db][2]), __float_as_uint(kv[db][3])));
+        }
+#pragma unroll
+        for (int db = 0; db < NKC; ++db)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = acc16_row(v, lane);
+                if (a0 + r < A)
+                    a.dq[(bA + a0 + r) * HD + hw * D + db * 16 + acc16_col(lane)] = acc[db][v] * p.inv_sqrt_d;
+            }
+    }
+
+    // ---- every head's dS and P of an allowed slot at its place in the
+    // reverse index (key-major)
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        if (rel[i] < 0)
+            continue;
+        const int pos = a.inv[n * K + jq + 16 * i];
+        float *dd = a.dS + (int64_t)pos * H;
+        float *pp = a.Pk + (int64_t)pos * H;
+        if (H == 4) {
+            *reinterpret_cast<float4 *>(dd) = make_float4(dsv[i][0], dsv[i][1], dsv[i][2], dsv[i][3]);
+            *reinterpret_cast<float4 *>(pp) = make_float4(pv[i][0], pv[i][1], pv[i][2], pv[i][3]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                if (h < H) {
+                    dd[h] = dsv[i][h];
+                    pp[h] = pv[i][h];
+                }
+        }
+    }
+
+    if constexpr (AF3) {
+        // pair-bias gradients as in the per-query kernel, over the block's
+        // 16 K slots: four lanes per slot (channel quarter qv), 64 slots per
+        // pass; the slots' dS from LDS
+        __syncthreads(); // dQ read the tile
+        float *sdl = smem; // [16][K][H]
+#pragma unroll
+        for (int h = 0; h < kPairH; ++h)
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+                const int sl = jq + 16 * i;
+                if (h < H && sl < K)
+                    sdl[(q * K + sl) * H + h] = dsv[i][h];
+            }
+        __syncthreads();
+        const int V = a.V, qv = lane & 3, sg4 = tid >> 2;
+        float psv[4], wpv[4][kPairH];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int v = 4 * qv + i;
+            psv[i] = v < V ? a.ps[v] : 0.0f;
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                wpv[i][h] = (v < V && h < H) ? a.wp[v * H + h] : 0.0f;
+        }
+        float gps[4], gwp[4][kPairH];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gps[i] = 0.0f;
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                gwp[i][h] = 0.0f;
+        }
+        for (int e0 = 0; e0 < 16 * K; e0 += 64) {
+            const int idx = e0 + sg4;
+            const int qq = idx / K, sl = idx - qq * K;
+            const bool in = idx < 16 * K && a0 + qq < A;
+            const int64_t e = (bA + a0 + (in ? qq : 0)) * K + (in ? sl : 0);
+            const bool ok = in && a.kid[e] >= 0;
+            float x[4];
+            load_pair_piece(reinterpret_cast<const TP *>(a.pair), e, V, qv, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x[i] = ok ? x[i] : 0.0f; // rows of slots not allowed may hold junk
+            const float r = pair_ln4(x, V, qv, a.eps);
+            float db[kPairH];
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h)
+                db[h] = (ok && h < H) ? sdl[(qq * K + sl) * H + h] : 0.0f;
+            float y[4];
+            float my = 0.0f, myx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float dpn = 0.0f;
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    dpn += db[h] * wpv[i][h];
+                gps[i] += dpn * x[i];
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    gwp[i][h] += x[i] * psv[i] * db[h];
+                y[i] = dpn * psv[i];
+                my += y[i];
+                myx += y[i] * x[i];
+            }
+            my = sum4(my) / (float)V;
+            myx = sum4(myx) / (float)V;
+            if (a.d_pair && in) {
+                float dp[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dp[i] = ok ? r * (y[i] - my - x[i] * myx) : 0.0f;
+                float *dst = a.d_pair + e * V + 4 * qv;
+                if (V % 4 == 0) {
+                    if (4 * qv < V)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(dp[0], dp[1], dp[2], dp[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * qv + i < V)
+                            dst[i] = dp[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 4; o < 64; o <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gps[i] += __shfl_xor(gps[i], o);
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    gwp[i][h] += __shfl_xor(gwp[i][h], o);
+            }
+        }
+        if (lane < 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = 4 * lane + i;
+                wred[w][v] = gps[i];
+#pragma unroll
+                for (int h = 0; h < kPairH; ++h)
+                    wred[w][kPairV + v * kPairH + h] = gwp[i][h];
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < W; i += 256)
+            a.pw_partial[(int64_t)blockIdx.x * W + i] = ((wred[0][i] + wred[1][i]) + wred[2][i]) + wred[3][i];
     }
 }
 
@@ -592,11 +923,17 @@ int slot_bwd_supported(int K, int H, int D, int V, int style) {
     return 1;
 }
 
-size_t slot_bwd_partial_floats(int64_t rows, int V, int H) {
+size_t slot_bwd_partial_floats(int64_t B, int64_t A, int V, int H) {
     (void)V;
     (void)H;
-    return (size_t)nblk(rows, 4) * (kPairV + kPairV * kPairH) + 256;
+    // the per-query kernel over every query (one record per 4 queries), or
+    // the block kernel (one per 16-query block) followed by the per-query
+    // kernel in queue mode (four per block)
+    const int64_t blocks = B * ((A + 15) / 16);
+    return (size_t)std::max<int64_t>(nblk(B * A, 4), 5 * blocks) * (kPairV + kPairV * kPairH) + 256;
 }
+
+int64_t slot_bwd_queue_ints(int64_t B, int64_t A) { return 1 + B * ((A + 15) / 16); }
 
 template <int D>
 void launch_fwd(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
@@ -611,6 +948,22 @@ void launch_fwd(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
     } else {
         set_lds(k_slot_fwd<float, false, D>, lds);
         hipLaunchKernelGGL((k_slot_fwd<float, false, D>), grid, dim3(256), lds, s, p);
+    }
+}
+
+template <int D>
+void launch_bwd_qb(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
+    if (style == STYLE_AF3) {
+        if (p.a.pair_dtype == 1) {
+            set_lds(k_slot_bwd_qb<bf16_t, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_bwd_qb<bf16_t, true, D>), grid, dim3(256), lds, s, p);
+        } else {
+            set_lds(k_slot_bwd_qb<float, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_bwd_qb<float, true, D>), grid, dim3(256), lds, s, p);
+        }
+    } else {
+        set_lds(k_slot_bwd_qb<float, false, D>, lds);
+        hipLaunchKernelGGL((k_slot_bwd_qb<float, false, D>), grid, dim3(256), lds, s, p);
     }
 }
 
@@ -666,11 +1019,39 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
     }
     prof_end(sp, s);
     sp = prof_begin(KN_BWD_SLOT_Q, s);
+    // block form where it applies (blocks with a wide key band are queued
+    // for the per-query kernel), else the per-query kernel over every query
+    const int nblocks = a.B * ((a.A + 15) / 16);
+    // (at fewer blocks than about three per CU the per-query kernel's finer
+    // grid is faster: config 1, 288 blocks, 74 against 107 us)
+    const bool block = a.K <= 128 && a.H <= kPairH && a.D >= 16 && a.wide &&
+                       nblocks >= kBlockMinBlocks;
+    int records = (int)grid.x;
+    SK pq = p;
+    pq.a.wide = nullptr;
+    pq.a.rec0 = 0;
+    dim3 gq = grid;
+    if (block) {
+        hipError_t e1 = fill_int(a.wide, 1, 0, s);
+        if (e1 != hipSuccess)
+            return e1;
+        const size_t blds = sizeof(float) * (size_t)block_lds_floats();
+        switch (a.D) {
+        case 16: launch_bwd_qb<16>(p, style, blds, dim3((unsigned)nblocks), s); break;
+        case 32: launch_bwd_qb<32>(p, style, blds, dim3((unsigned)nblocks), s); break;
+        case 64: launch_bwd_qb<64>(p, style, blds, dim3((unsigned)nblocks), s); break;
+        default: return hipErrorInvalidValue;
+        }
+        pq.a.wide = a.wide;
+        pq.a.rec0 = nblocks;
+        gq = dim3((unsigned)(4 * nblocks));
+        records = 5 * nblocks;
+    }
     switch (a.D) {
-    case 8: launch_bwd_q<8>(p, style, lds, grid, s); break;
-    case 16: launch_bwd_q<16>(p, style, lds, grid, s); break;
-    case 32: launch_bwd_q<32>(p, style, lds, grid, s); break;
-    case 64: launch_bwd_q<64>(p, style, lds, grid, s); break;
+    case 8: launch_bwd_q<8>(pq, style, lds, gq, s); break;
+    case 16: launch_bwd_q<16>(pq, style, lds, gq, s); break;
+    case 32: launch_bwd_q<32>(pq, style, lds, gq, s); break;
+    case 64: launch_bwd_q<64>(pq, style, lds, gq, s); break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -681,7 +1062,7 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
         // sum the per-workgroup partials in workgroup order, then pick the
         // [V] and [V][H] blocks out of the padded record
         constexpr int W = kPairV + kPairV * kPairH;
-        const int rows = (int)grid.x;
+        const int rows = records;
         float *sums = a.pw_partial + (size_t)rows * W;
         e = colsum(rows, W, view(a.pw_partial, W), View{nullptr, 0}, sums, 0.0f, a.sc, s);
         if (e == hipSuccess && d_pair_scale)
