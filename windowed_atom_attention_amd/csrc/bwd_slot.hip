@@ -214,8 +214,18 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
     float *sP = sbeta + K * H;
     float *sq = sP + K;
     const int64_t N = (int64_t)a.B * a.A;
-    const int64_t n = (int64_t)blockIdx.x * 4 + w;
-    const bool live = n < N;
+    int64_t n = (int64_t)blockIdx.x * 4 + w;
+    bool live = n < N;
+    if (a.wide) {
+        // queue mode: four workgroups per queued 16-query block
+        const int qi = (int)blockIdx.x >> 2;
+        if (qi >= a.wide[0])
+            return;
+        const int blk = a.wide[1 + qi], nqb = (a.A + 15) / 16;
+        const int qa0 = (blk % nqb) * 16 + ((int)blockIdx.x & 3) * 4 + w;
+        live = qa0 < a.A;
+        n = (int64_t)(blk / nqb) * a.A + qa0;
+    }
     const int64_t nn = live ? n : 0;
     const int64_t b = nn / a.A, qa = nn - b * a.A;
     const bool qu = live && a.usable[nn];
@@ -537,6 +547,12 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
 constexpr int kBandRows = 128, kBandPitch = kBandRows + 4;
 constexpr int kBlockMinBlocks = 768; // grids from which the block form is used
 
+// (at fewer blocks than about three per CU the per-query kernels' finer
+// grid is faster: config 1, 288 blocks, query side 74 against 107 us)
+inline bool block_form(const SlotBwdArgs &a, int nblocks) {
+    return a.K <= 128 && a.H <= kPairH && a.D >= 16 && a.wide && nblocks >= kBlockMinBlocks;
+}
+
 __host__ __device__ inline int block_lds_floats() { return kPairH * 16 * kBandPitch; }
 
 template <typename TP, bool AF3, int D>
@@ -838,6 +854,237 @@ __global__ __launch_bounds__(256) void k_slot_bwd_qb(SK p) {
     }
 }
 
+// Block form of the forward step (same conditions as the query side's):
+// per 16-query block, S = Q . K_band^T on the matrix cores into a per-head
+// tile, each thread's slots take their logits from it (plus the AF3 pair
+// bias of the slot's row), the masked softmax runs over the query's 16
+// threads, and o = P_tile . V_band, with P scattered by key (repeated keys
+// add). Blocks with a wide key band are queued for the per-query kernel.
+template <typename TP, bool AF3, int D>
+__global__ __launch_bounds__(256) void k_slot_fwd_b(SK p) {
+    extern __shared__ __align__(16) float smem[];
+    __shared__ int s_lo, s_hi;
+    __shared__ float sw[kPairV * kPairH]; // pair_scale[v] * w_pair[v][h]
+    constexpr int SPL = 8, NKC = D / 16;
+    const SlotBwdArgs &a = p.a;
+    const int K = a.K, H = a.H, HD = H * D, A = a.A;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int q = tid >> 4, jq = tid & 15;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int nqb = (A + 15) / 16;
+    const int b = (int)blockIdx.x / nqb, a0 = ((int)blockIdx.x - b * nqb) * 16;
+    const int64_t bA = (int64_t)b * A;
+    const bool live = a0 + q < A;
+    const int64_t n = bA + a0 + (live ? q : 0);
+    const bool qu = live && a.usable[n];
+    float *tile = smem; // [head][16][kBandPitch]
+
+    int rel[SPL];
+    int lo = INT_MAX, hi = -1;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int sl = jq + 16 * i;
+        rel[i] = -1;
+        if (live && sl < K) {
+            const int64_t e = n * K + sl;
+            const int64_t j = a.key_index[e];
+            bool ok = qu && j >= 0 && j < A && a.window_mask[e];
+            if (ok) {
+                const int64_t dq = j > a0 + q ? j - (a0 + q) : (a0 + q) - j;
+                ok = a.usable[bA + j] && (a.radius < 0 || dq <= a.radius);
+            }
+            rel[i] = ok ? (int)j : -1;
+            a.kid[e] = ok ? (int)(bA + j) : -1;
+        }
+        if (rel[i] >= 0) {
+            lo = min(lo, rel[i]);
+            hi = max(hi, rel[i]);
+        }
+    }
+    if (tid == 0) {
+        s_lo = INT_MAX;
+        s_hi = -1;
+    }
+    if (AF3 && tid < kPairV * kPairH) {
+        const int v = tid / kPairH, h = tid - v * kPairH;
+        sw[tid] = (v < a.V && h < H) ? a.ps[v] * a.wp[v * H + h] : 0.0f;
+    }
+    __syncthreads();
+    lo = wave_min_i(lo);
+    hi = wave_max_i(hi);
+    if (lane == 0) {
+        atomicMin(&s_lo, lo);
+        atomicMax(&s_hi, hi);
+    }
+    __syncthreads();
+    const int bhi = s_hi, blo = bhi >= 0 ? s_lo : 0;
+    const bool any = bhi >= 0;
+    const int rows = any ? bhi + 1 - blo : 0;
+    if (rows > kBandRows) {
+        if (tid == 0)
+            a.wide[1 + atomicAdd(a.wide, 1)] = (int)blockIdx.x;
+        return;
+    }
+    const int ncb = (rows + 15) / 16;
+    const int hw = w;
+
+    // pair bias of the thread's slots (whole rows, 16-byte pieces)
+    float lg[SPL][kPairH]; // the bias, then the logit, then the weight
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int h = 0; h < kPairH; ++h)
+            lg[i][h] = 0.0f;
+    if constexpr (AF3) {
+        const int V = a.V;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            if (rel[i] < 0)
+                continue;
+            const int64_t e = n * K + jq + 16 * i;
+            float x[kPairV];
+#pragma unroll
+            for (int qv = 0; qv < kPairV / 4; ++qv) {
+                float x4[4];
+                load_pair_piece(reinterpret_cast<const TP *>(a.pair), e, V, qv, x4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    x[4 * qv + t] = x4[t];
+            }
+            float m = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kPairV; ++v)
+                m += x[v];
+            m /= (float)V;
+            float var = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kPairV; ++v) {
+                const float d = v < V ? x[v] - m : 0.0f;
+                x[v] = d;
+                var += d * d;
+            }
+            const float r = 1.0f / sqrtf(var / (float)V + a.eps);
+#pragma unroll
+            for (int h = 0; h < kPairH; ++h) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int v = 0; v < kPairV; ++v)
+                    acc += x[v] * sw[v * kPairH + h];
+                lg[i][h] = acc * r;
+            }
+        }
+    }
+
+    // ---- S = Q . K_band^T: query l16, band row 16 cb + l16
+    if (hw < H && any) {
+        uint4 af[NKC];
+        const bool qin = a0 + l16 < A;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            af[kc] = make_uint4(0, 0, 0, 0);
+            if (qin)
+                af[kc] = *reinterpret_cast<const uint4 *>(a.q + (bA + a0 + l16) * HD + hw * D + kc * 16 + g4 * 4);
+        }
+        for (int cb0 = 0; cb0 < ncb; cb0 += 4) {
+            uint4 kb[4][NKC];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = (cb0 + t) * 16 + l16;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    kb[t][kc] = make_uint4(0, 0, 0, 0);
+                    if (r < rows)
+                        kb[t][kc] = *reinterpret_cast<const uint4 *>(a.k + (bA + blo + r) * HD + hw * D + kc * 16 + g4 * 4);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (cb0 + t >= ncb)
+                    break;
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+                    Mma16<float>::mma(acc, af[kc], kb[t][kc]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    tile[(hw * 16 + acc16_row(v, lane)) * kBandPitch + (cb0 + t) * 16 + acc16_col(lane)] = acc[v];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- masked softmax over the query's allowed slots
+#pragma unroll
+    for (int h = 0; h < kPairH; ++h) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            if (h < H && rel[i] >= 0) {
+                lg[i][h] += tile[(h * 16 + q) * kBandPitch + rel[i] - blo] * p.inv_sqrt_d;
+                mx = fmaxf(mx, lg[i][h]);
+            }
+        }
+        mx = max16(mx);
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            lg[i][h] = (h < H && rel[i] >= 0) ? expf(lg[i][h] - mx) : 0.0f;
+            sum += lg[i][h];
+        }
+        sum = sum16(sum);
+        const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            lg[i][h] *= inv;
+            const int sl = jq + 16 * i;
+            if (h < H && live && sl < K)
+                a.P[(((int64_t)b * H + h) * A + a0 + q) * K + sl] = lg[i][h];
+        }
+    }
+    __syncthreads(); // S read
+    for (int i = tid; i < block_lds_floats() / 4; i += 256)
+        reinterpret_cast<float4 *>(tile)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < kPairH; ++h)
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+            if (h < H && rel[i] >= 0)
+                atomicAdd(&tile[(h * 16 + q) * kBandPitch + rel[i] - blo], lg[i][h]);
+    __syncthreads();
+
+    // ---- o = P_tile . V_band: query l16, channel 16 db + l16
+    if (hw < H) {
+        f32x4_t acc[NKC];
+#pragma unroll
+        for (int db = 0; db < NKC; ++db)
+            acc[db] = zero4();
+        for (int kc = 0; kc < ncb; ++kc) {
+            const uint4 av = *reinterpret_cast<const uint4 *>(tile + (hw * 16 + l16) * kBandPitch + kc * 16 + g4 * 4);
+            float vv[NKC][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = kc * 16 + g4 * 4 + t;
+#pragma unroll
+                for (int db = 0; db < NKC; ++db)
+                    vv[db][t] = r < rows ? a.v[(bA + blo + r) * HD + hw * D + db * 16 + l16] : 0.0f;
+            }
+#pragma unroll
+            for (int db = 0; db < NKC; ++db)
+                Mma16<float>::mma(acc[db], av, make_uint4(__float_as_uint(vv[db][0]), __float_as_uint(vv[db][1]),
+                                                          __float_as_uint(vv[db][2]), __float_as_uint(vv[db][3])));
+        }
+#pragma unroll
+        for (int db = 0; db < NKC; ++db)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = acc16_row(v, lane);
+                if (a0 + r < A)
+                    a.o[(bA + a0 + r) * HD + hw * D + db * 16 + acc16_col(lane)] = acc[db][v];
+            }
+    }
+}
+
 // One wave per key atom, over its list of (query, slot) entries in order.
 // A lane holds one float4 of the H*D channels (all in one head); the wave
 // takes EPP = 64 / (HD/4) entries per pass (one per lane group) and four
@@ -952,6 +1199,22 @@ void launch_fwd(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
 }
 
 template <int D>
+void launch_fwd_b(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
+    if (style == STYLE_AF3) {
+        if (p.a.pair_dtype == 1) {
+            set_lds(k_slot_fwd_b<bf16_t, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_fwd_b<bf16_t, true, D>), grid, dim3(256), lds, s, p);
+        } else {
+            set_lds(k_slot_fwd_b<float, true, D>, lds);
+            hipLaunchKernelGGL((k_slot_fwd_b<float, true, D>), grid, dim3(256), lds, s, p);
+        }
+    } else {
+        set_lds(k_slot_fwd_b<float, false, D>, lds);
+        hipLaunchKernelGGL((k_slot_fwd_b<float, false, D>), grid, dim3(256), lds, s, p);
+    }
+}
+
+template <int D>
 void launch_bwd_qb(const SK &p, int style, size_t lds, dim3 grid, hipStream_t s) {
     if (style == STYLE_AF3) {
         if (p.a.pair_dtype == 1) {
@@ -989,12 +1252,31 @@ hipError_t slot_fwd(const SlotBwdArgs &a, int style, hipStream_t s) {
         return hipSuccess;
     SK p{a, 1.0f / sqrtf((float)a.D)};
     const size_t lds = 4 * sizeof(float) * (size_t)wave_floats(a.K, a.H, a.H * a.D);
-    const dim3 grid(nblk(N, 4));
+    dim3 grid(nblk(N, 4));
+    // block form where it applies (as the query side's), then the
+    // per-query kernel for the queued blocks; else the per-query kernel
+    const int nblocks = a.B * ((a.A + 15) / 16);
+    SK pq = p;
+    pq.a.wide = nullptr;
+    if (block_form(a, nblocks)) {
+        hipError_t e1 = fill_int(a.wide, 1, 0, s);
+        if (e1 != hipSuccess)
+            return e1;
+        const size_t blds = sizeof(float) * (size_t)block_lds_floats();
+        switch (a.D) {
+        case 16: launch_fwd_b<16>(p, style, blds, dim3((unsigned)nblocks), s); break;
+        case 32: launch_fwd_b<32>(p, style, blds, dim3((unsigned)nblocks), s); break;
+        case 64: launch_fwd_b<64>(p, style, blds, dim3((unsigned)nblocks), s); break;
+        default: return hipErrorInvalidValue;
+        }
+        pq.a.wide = a.wide;
+        grid = dim3((unsigned)(4 * nblocks));
+    }
     switch (a.D) {
-    case 8: launch_fwd<8>(p, style, lds, grid, s); break;
-    case 16: launch_fwd<16>(p, style, lds, grid, s); break;
-    case 32: launch_fwd<32>(p, style, lds, grid, s); break;
-    case 64: launch_fwd<64>(p, style, lds, grid, s); break;
+    case 8: launch_fwd<8>(pq, style, lds, grid, s); break;
+    case 16: launch_fwd<16>(pq, style, lds, grid, s); break;
+    case 32: launch_fwd<32>(pq, style, lds, grid, s); break;
+    case 64: launch_fwd<64>(pq, style, lds, grid, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1022,10 +1304,7 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
     // block form where it applies (blocks with a wide key band are queued
     // for the per-query kernel), else the per-query kernel over every query
     const int nblocks = a.B * ((a.A + 15) / 16);
-    // (at fewer blocks than about three per CU the per-query kernel's finer
-    // grid is faster: config 1, 288 blocks, 74 against 107 us)
-    const bool block = a.K <= 128 && a.H <= kPairH && a.D >= 16 && a.wide &&
-                       nblocks >= kBlockMinBlocks;
+    const bool block = block_form(a, nblocks);
     int records = (int)grid.x;
     SK pq = p;
     pq.a.wide = nullptr;
