@@ -213,11 +213,14 @@ __global__ __launch_bounds__(256) void k_gemm_group(GemmGroupK G) {
     __shared__ float As[kKS][68];
     __shared__ float Bs[kKS][68];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // consecutive tiles (the column tiles of one row block) on one XCD, so
+    // the second read of a row block's A comes from that XCD's L2
+    const int bid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
     int j = 0;
-    while (j + 1 < G.n && (int)blockIdx.x >= G.job[j + 1].tile0)
+    while (j + 1 < G.n && bid >= G.job[j + 1].tile0)
         ++j;
     const GemmJobK &g = G.job[j];
-    const int tl = (int)blockIdx.x - g.tile0;
+    const int tl = bid - g.tile0;
     const int m0 = (tl / g.tiles_n) * 64, n0 = (tl % g.tiles_n) * 64;
     f32x16_t acc = zero16();
     for (int i = 0; i < g.nseg; ++i)

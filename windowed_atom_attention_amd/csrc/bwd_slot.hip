@@ -214,7 +214,8 @@ __global__ __launch_bounds__(256) void k_slot_fwd(SK p) {
     float *sP = sbeta + K * H;
     float *sq = sP + K;
     const int64_t N = (int64_t)a.B * a.A;
-    int64_t n = (int64_t)blockIdx.x * 4 + w;
+    // neighbouring queries (which share key rows) on one XCD
+    int64_t n = (int64_t)xcd_remap((int)blockIdx.x, (int)gridDim.x) * 4 + w;
     bool live = n < N;
     if (a.wide) {
         // queue mode: four workgroups per queued 16-query block
@@ -340,7 +341,8 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     float *sdo = sP + K;
     float *spa = sdo + HD;
     const int64_t N = (int64_t)a.B * a.A;
-    int64_t n = (int64_t)blockIdx.x * 4 + w;
+    // neighbouring queries (which share key rows) on one XCD
+    int64_t n = (int64_t)xcd_remap((int)blockIdx.x, (int)gridDim.x) * 4 + w;
     bool live = n < N;
     const int rec = a.rec0 + (int)blockIdx.x; // pair-parameter partial record
     if (a.wide) {
@@ -567,7 +569,9 @@ __global__ __launch_bounds__(256) void k_slot_bwd_qb(SK p) {
     const int q = tid >> 4, jq = tid & 15;    // query of the block, its thread
     const int l16 = lane & 15, g4 = lane >> 4; // matrix-core lane coordinates
     const int nqb = (A + 15) / 16;
-    const int b = (int)blockIdx.x / nqb, a0 = ((int)blockIdx.x - b * nqb) * 16;
+    // neighbouring blocks (overlapping key bands) on one XCD
+    const int wg = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int b = wg / nqb, a0 = (wg - b * nqb) * 16;
     const int64_t bA = (int64_t)b * A;
     const bool live = a0 + q < A;
     const int64_t n = bA + a0 + (live ? q : 0);
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(256) void k_slot_bwd_qb(SK p) {
     if (rows > kBandRows) {
         // scattered ids: the per-query kernel takes this block
         if (tid == 0)
-            a.wide[1 + atomicAdd(a.wide, 1)] = (int)blockIdx.x;
+            a.wide[1 + atomicAdd(a.wide, 1)] = wg;
         if constexpr (AF3)
             for (int i = tid; i < W; i += 256)
                 a.pw_partial[(int64_t)blockIdx.x * W + i] = 0.0f;
@@ -872,7 +876,9 @@ __global__ __launch_bounds__(256) void k_slot_fwd_b(SK p) {
     const int q = tid >> 4, jq = tid & 15;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int nqb = (A + 15) / 16;
-    const int b = (int)blockIdx.x / nqb, a0 = ((int)blockIdx.x - b * nqb) * 16;
+    // neighbouring blocks (overlapping key bands) on one XCD
+    const int wg = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int b = wg / nqb, a0 = (wg - b * nqb) * 16;
     const int64_t bA = (int64_t)b * A;
     const bool live = a0 + q < A;
     const int64_t n = bA + a0 + (live ? q : 0);
@@ -922,7 +928,7 @@ __global__ __launch_bounds__(256) void k_slot_fwd_b(SK p) {
     const int rows = any ? bhi + 1 - blo : 0;
     if (rows > kBandRows) {
         if (tid == 0)
-            a.wide[1 + atomicAdd(a.wide, 1)] = (int)blockIdx.x;
+            a.wide[1 + atomicAdd(a.wide, 1)] = wg;
         return;
     }
     const int ncb = (rows + 15) / 16;
@@ -1094,7 +1100,8 @@ __global__ __launch_bounds__(256) void k_slot_bwd_kv(SK p) {
     const SlotBwdArgs &a = p.a;
     const int lane = threadIdx.x & 63;
     const int64_t N = (int64_t)a.B * a.A;
-    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // neighbouring keys (selected by the same queries) on one XCD
+    const int64_t j = (int64_t)xcd_remap((int)blockIdx.x, (int)gridDim.x) * 4 + (threadIdx.x >> 6);
     if (j >= N)
         return;
     const int K = a.K, H = a.H, D = a.D, HD = H * D;
