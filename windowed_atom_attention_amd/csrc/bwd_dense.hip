@@ -807,7 +807,7 @@ hipError_t gemm(int M, int N, int K, Mat A, Mat B, View C, float beta, const flo
     // split only long reductions (parameter gradients over every atom)
     int64_t splits = 1;
     if (sc.partial && tiles < 256 && K >= 1024) {
-        splits = std::min<int64_t>((512 + tiles - 1) / tiles, K / 256);
+        splits = std::min<int64_t>((512 + tiles - 1) / tiles, K / 128);
         splits = std::min<int64_t>(splits, (int64_t)(sc.cap / ((size_t)M * N)));
         if (splits < 2)
             splits = 1;
