@@ -262,3 +262,26 @@ def test_slot_backward_without_attention_gradient_and_repeat_bits():
     for n in ("dq", "dk", "dv", "d_pair", "d_pair_scale", "d_w_pair"):
         assert_close(n, np64(a[n]), ref[n].numpy(), RTOL)
         assert torch.equal(a[n], b[n]), n
+
+
+def test_block_form_is_deterministic():
+    """The block forms of the slot step (768+ query blocks) add each query's
+    weights and logit gradients into their LDS tiles in a fixed order:
+    repeated calls give identical bits, also with queued wide blocks."""
+    q, k, v, usable, ki, wm, d_att, d_o, extra, H = _slot_inputs(
+        "af3", B=48, A=256, K=64, H=4, D=32, V=16, local=40)
+    cu = lambda x: x.cuda()
+    args = (cu(q), cu(k), cu(v), cu(usable), cu(ki), cu(wm), cu(d_o), H)
+    ex = {n: cu(t) for n, t in extra.items()}
+    a = slot_attention_backward(*args, d_attention=cu(d_att), style="af3", **ex)
+    b = slot_attention_backward(*args, d_attention=cu(d_att), style="af3", **ex)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+    w = make_workload("4a", A=12288)
+    up = _upstream(w)
+    a_in, a_par = _gpu_backward(w, up)
+    b_in, b_par = _gpu_backward(w, up)
+    for kk in a_in:
+        assert torch.equal(a_in[kk], b_in[kk]), kk
+    for kk in a_par:
+        assert torch.equal(a_par[kk], b_par[kk]), kk

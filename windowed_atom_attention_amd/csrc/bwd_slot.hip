@@ -344,19 +344,17 @@ __global__ __launch_bounds__(256) void k_slot_bwd_q(SK p) {
     // neighbouring queries (which share key rows) on one XCD
     int64_t n = (int64_t)xcd_remap((int)blockIdx.x, (int)gridDim.x) * 4 + w;
     bool live = n < N;
-    const int rec = a.rec0 + (int)blockIdx.x; // pair-parameter partial record
+    // pair-parameter partial record: by workgroup, or in queue mode by the
+    // queued block's id (fixed places whatever the queue order; the block
+    // kernel zeroes the four records of every block it completes)
+    int rec = a.rec0 + (int)blockIdx.x;
     if (a.wide) {
         // queue mode: four workgroups per queued 16-query block
         const int qi = (int)blockIdx.x >> 2;
-        if (qi >= a.wide[0]) {
-            if constexpr (AF3) {
-                constexpr int W = kPairV + kPairV * kPairH;
-                for (int i = threadIdx.x; i < W; i += 256)
-                    a.pw_partial[(int64_t)rec * W + i] = 0.0f;
-            }
+        if (qi >= a.wide[0])
             return;
-        }
         const int blk = a.wide[1 + qi], nqb = (a.A + 15) / 16;
+        rec = a.rec0 + blk * 4 + ((int)blockIdx.x & 3);
         const int qa0 = (blk % nqb) * 16 + ((int)blockIdx.x & 3) * 4 + w;
         live = qa0 < a.A;
         n = (int64_t)(blk / nqb) * a.A + qa0;
@@ -614,7 +612,7 @@ __global__ __launch_bounds__(256) void k_slot_bwd_qb(SK p) {
             a.wide[1 + atomicAdd(a.wide, 1)] = wg;
         if constexpr (AF3)
             for (int i = tid; i < W; i += 256)
-                a.pw_partial[(int64_t)blockIdx.x * W + i] = 0.0f;
+                a.pw_partial[(int64_t)wg * W + i] = 0.0f;
         return;
     }
     const int ncb = (rows + 15) / 16;
@@ -854,7 +852,11 @@ __global__ __launch_bounds__(256) void k_slot_bwd_qb(SK p) {
         }
         __syncthreads();
         for (int i = tid; i < W; i += 256)
-            a.pw_partial[(int64_t)blockIdx.x * W + i] = ((wred[0][i] + wred[1][i]) + wred[2][i]) + wred[3][i];
+            a.pw_partial[(int64_t)wg * W + i] = ((wred[0][i] + wred[1][i]) + wred[2][i]) + wred[3][i];
+        // this block's four records of the queue-mode kernel stay zero
+        const int nblocks = a.B * nqb;
+        for (int i = tid; i < 4 * W; i += 256)
+            a.pw_partial[((int64_t)nblocks + 4 * wg) * W + i] = 0.0f;
     }
 }
 
