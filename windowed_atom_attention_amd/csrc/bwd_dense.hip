@@ -1,6 +1,8 @@
 // bwd_dense.hip -- the dense and row kernels of the block's backward pass:
-// an fp32 matrix-core product for any operand strides, column sums, the
-// elementwise steps of the chain rule, row normalisation and its backward,
+// an fp32 matrix-core product for any operand strides (split-k for long
+// reductions; grouped launches of independent products), column sums, the
+// elementwise steps of the chain rule (grouped launches, 16-byte accesses
+// where aligned), row normalisation and its backward,
 // the ESMFold2 head RMS + rotary and its backward, sanitising, the pooling
 // backward, and the reverse index that turns "entry -> key" maps into
 // per-key lists without floating-point atomics.

@@ -15,10 +15,19 @@
 // AF3: dS_s is also the gradient of the slot's pair bias, which flows back
 // through LN(pair) * pair_scale @ w_pair to the pair row, pair_scale and
 // w_pair (per-workgroup partial sums, reduced in a fixed order).
-// Backward, key side: the reverse index of the slot -> key map (per key,
-// its (query, slot) entries in ascending order) lets one wave per key sum
+// The query side writes each slot's dS and P (every head) at the slot's
+// place in the reverse index of the slot -> key map (per key, its (query,
+// slot) entries in ascending order), so that on the key side one wave per
+// key sums
 //   dK_j = sum dS Q_query / sqrt(D),  dV_j = sum P dO_query
-// over every selection of key j, with no floating-point atomics.
+// over every selection of key j reading them contiguously, with no
+// floating-point atomics in global memory.
+//
+// Block forms (large grids, K <= 128, H <= 4, D >= 16): the forward and the
+// query side per block of 16 queries whose allowed keys lie in a band of at
+// most 128 rows, with the band products (Q.K^T, P.V, dO.V^T, dS.K) on the
+// matrix cores and each band row read once per block; blocks with a wider
+// band are queued for the per-query kernels.
 #include "bwd.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
