@@ -193,30 +193,47 @@ struct Run {
     Side *side = nullptr; // null: leaves run on the main stream
     Scratch sc2{};
     hipError_t err = hipSuccess;
+    // parameter-gradient leaves queued since the last fork; they go out as
+    // grouped launches (leaf_group) when the next fork or the join comes.
+    // Their inputs stay valid until the join (the main chain never rewrites
+    // a buffer a leaf reads), so the deferral changes no value.
+    LeafJob pending[64];
+    int npend = 0;
+    void flush() {
+        for (int i = 0; i < npend && err == hipSuccess; i += kLeafJobs)
+            ok(leaf_group(pending + i, std::min(kLeafJobs, npend - i), side ? sc2 : sc,
+                          side ? side->s : s));
+        npend = 0;
+    }
     // make the side stream wait for everything enqueued on the main stream
     void fork() {
+        flush();
         if (side && err == hipSuccess) {
             ok(hipEventRecord(side->fork, s));
             ok(hipStreamWaitEvent(side->s, side->fork, 0));
         }
     }
     void join() {
+        flush();
         if (side) {
             ok(hipEventRecord(side->join, side->s));
             ok(hipStreamWaitEvent(s, side->join, 0));
         }
     }
+    void queue(const LeafJob &x) {
+        if (npend == 64)
+            flush();
+        pending[npend++] = x;
+    }
     // a parameter-gradient product / column sum (after a fork)
     void leaf_mm(int M, int N, int K, Mat A, Mat B, float *C, int64_t ldc) {
         if (err == hipSuccess && C)
-            ok(gemm(M, N, K, A, B, View{C, ldc}, 0.0f, nullptr, side ? sc2 : sc,
-                    side ? side->s : s));
+            queue(LeafJob{0, M, N, K, A, B, C, ldc});
     }
     void leaf_cs(int rows, int W, const float *X, int64_t ldx, const float *Y, int64_t ldy,
                  float *out) {
         if (err == hipSuccess && out)
-            ok(colsum(rows, W, view(X, ldx), view(Y, ldy), out, 0.0f, side ? sc2 : sc,
-                      side ? side->s : s));
+            queue(LeafJob{1, 1, W, rows, mat(X, ldx), Mat{Y, ldy, 1}, out, W});
     }
     void ok(hipError_t e) {
         if (err == hipSuccess && e != hipSuccess)

@@ -67,6 +67,21 @@ struct GemmJob {
 };
 hipError_t gemm_group(const GemmJob *jobs, int n, hipStream_t s);
 
+// Parameter-gradient leaves, up to kLeafJobs in two launches (split partial
+// sums, then their reduction in a fixed order; results overwrite `out`):
+//   kind 0: out[M][N] = A[M][K] B[K][N] (K the long axis, split);
+//   kind 1: out[c] = sum over K rows r of A[r][c] (* B[r][c] when B.p), c < N
+//           (A = mat(X, ldx), B = mat(Y, ldy) or a null pointer).
+constexpr int kLeafJobs = 8;
+struct LeafJob {
+    int kind;
+    int M, N, K;
+    Mat A, B;
+    float *out;
+    int64_t ldo;
+};
+hipError_t leaf_group(const LeafJob *jobs, int n, Scratch sc, hipStream_t s);
+
 // out[c] = beta * out[c] + sum_r X[r, c] (* Y[r, c] when Y.p), c < W.
 hipError_t colsum(int rows, int W, View X, View Y, float *out, float beta, Scratch sc,
                   hipStream_t s);

@@ -310,6 +310,98 @@ __global__ __launch_bounds__(256) void k_colsum_reduce(int W, int splits, const 
         out[col] = beta != 0.0f ? out[col] + x : x;
 }
 
+// --------------------------------------------------- parameter-gradient leaves
+
+// Up to kLeafJobs parameter-gradient leaves in two launches: split partial
+// sums, then their fixed-order reduction. A leaf is a product C = A B whose
+// long reduction axis K is split over workgroups (64x64 tiles, as k_gemm),
+// or a column sum out[c] = sum_r X[r, c] (* Y[r, c]) whose rows are split.
+struct LeafK {
+    int kind; // 0 product, 1 column sum
+    SegK seg; // product operands; column sum: A = X (ars = ld), B = Y or null (brs = ld)
+    int M, N, kchunk, splits, tiles_n, units;
+    float *out;
+    int64_t ldo;
+    float *partial; // [splits][M][N] (column sum: [splits][N])
+    int unit0, red0;
+};
+struct LeafGroupK {
+    LeafK job[kLeafJobs];
+    int n;
+};
+
+__global__ __launch_bounds__(256) void k_leaf_split(LeafGroupK G) {
+    __shared__ float As[kKS][68];
+    __shared__ float Bs[kKS][68];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int j = 0;
+    while (j + 1 < G.n && (int)blockIdx.x >= G.job[j + 1].unit0)
+        ++j;
+    const LeafK &g = G.job[j];
+    const int u = (int)blockIdx.x - g.unit0;
+    if (g.kind == 0) {
+        const int tiles = (g.units / g.splits);
+        const int z = u / tiles, tl = u - z * tiles;
+        const int m0 = (tl / g.tiles_n) * 64, n0 = (tl % g.tiles_n) * 64;
+        const int kb = z * g.kchunk, ke = min(g.seg.K, kb + g.kchunk);
+        f32x16_t acc = zero16();
+        tile_product(g.seg, g.M, g.N, m0, n0, kb, ke, As, Bs, acc);
+        const int wm = (w & 1) * 32, wn = (w >> 1) * 32;
+        const int c = n0 + wn + (lane & 31);
+        const int64_t MN = (int64_t)g.M * g.N;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = m0 + wm + acc32_row(v, lane);
+            if (r < g.M && c < g.N)
+                g.partial[(int64_t)z * MN + (int64_t)r * g.N + c] = acc[v];
+        }
+        return;
+    }
+    // column sum: 64 columns per workgroup, rows split in `splits` ranges
+    const int nb = (g.N + 63) / 64;
+    const int z = u / nb, cb = u - z * nb;
+    const int col = cb * 64 + lane;
+    const int rows = g.seg.K, per = g.kchunk;
+    const int r0 = z * per, r1 = min(rows, r0 + per);
+    float acc = 0.0f;
+    if (col < g.N)
+        for (int r = r0 + w; r < r1; r += 4) {
+            float x = g.seg.A[(int64_t)r * g.seg.ars + col];
+            if (g.seg.B)
+                x *= g.seg.B[(int64_t)r * g.seg.brs + col];
+            acc += x;
+        }
+    float *red = &As[0][0];
+    red[w * 64 + lane] = acc;
+    __syncthreads();
+    if (w == 0 && col < g.N)
+        g.partial[(int64_t)z * g.N + col] = ((red[lane] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
+}
+
+// 8 lanes per output element: lane l of the group sums splits l, l+8, ...
+// in order, then a fixed butterfly
+__global__ __launch_bounds__(256) void k_leaf_reduce(LeafGroupK G) {
+    int j = 0;
+    while (j + 1 < G.n && (int)blockIdx.x >= G.job[j + 1].red0)
+        ++j;
+    const LeafK &g = G.job[j];
+    const int64_t i = ((int64_t)((int)blockIdx.x - g.red0) * 256 + threadIdx.x) >> 3;
+    const int sub = threadIdx.x & 7;
+    const int64_t MN = (int64_t)g.M * g.N;
+    const bool live = i < MN;
+    float x = 0.0f;
+    if (live)
+        for (int z = sub; z < g.splits; z += 8)
+            x += g.partial[(int64_t)z * MN + i];
+    x += __shfl_xor(x, 1, 8);
+    x += __shfl_xor(x, 2, 8);
+    x += __shfl_xor(x, 4, 8);
+    if (!live || sub != 0)
+        return;
+    const int r = (int)(i / g.N), c = (int)(i - (int64_t)r * g.N);
+    g.out[(int64_t)r * g.ldo + c] = x;
+}
+
 // ------------------------------------------------------------- elementwise
 
 __device__ __forceinline__ float dsilu_f(float z) {
@@ -866,6 +958,85 @@ hipError_t gemm_group(const GemmJob *jobs, int n, hipStream_t s) {
         return hipSuccess;
     G.n = m;
     hipLaunchKernelGGL(k_gemm_group, dim3((unsigned)tiles), dim3(256), 0, s, G);
+    return hipGetLastError();
+}
+
+hipError_t leaf_group(const LeafJob *jobs, int n, Scratch sc, hipStream_t s) {
+    if (n < 1 || n > kLeafJobs)
+        return hipErrorInvalidValue;
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+    LeafGroupK G{};
+    // splits: about 512 workgroups per product (chunks of at least 128 rows)
+    // and rows / 128 (at most 1024) per column sum, scaled down together if
+    // the partial sums would not fit the scratch
+    int64_t want[kLeafJobs], outs[kLeafJobs], need = 0;
+    int m = 0;
+    for (int j = 0; j < n; ++j) {
+        const LeafJob &x = jobs[j];
+        if (!x.out || x.N <= 0 || (x.kind == 0 && x.M <= 0))
+            continue;
+        const int64_t K = x.K;
+        if (x.kind == 0) {
+            const int64_t tiles = (int64_t)nblk(x.M, 64) * nblk(x.N, 64);
+            want[m] = std::max<int64_t>(1, std::min<int64_t>((512 + tiles - 1) / tiles, K / 128));
+            outs[m] = (int64_t)x.M * x.N;
+        } else {
+            want[m] = std::max<int64_t>(1, std::min<int64_t>((K + 127) / 128, 1024));
+            outs[m] = x.N;
+        }
+        need += want[m] * outs[m];
+        G.job[m].kind = x.kind;
+        ++m;
+    }
+    if (m == 0)
+        return hipSuccess;
+    const double scale = need > (int64_t)sc.cap ? (double)sc.cap / (double)need : 1.0;
+    int units = 0, reds = 0, jj = 0;
+    size_t off = 0;
+    for (int j = 0; j < n; ++j) {
+        const LeafJob &x = jobs[j];
+        if (!x.out || x.N <= 0 || (x.kind == 0 && x.M <= 0))
+            continue;
+        LeafK &k = G.job[jj];
+        int64_t splits = std::max<int64_t>(1, (int64_t)(want[jj] * scale));
+        const int64_t K = x.K;
+        if (x.kind == 0) {
+            int64_t kchunk = (K + splits - 1) / splits;
+            kchunk = (kchunk + kKS - 1) / kKS * kKS;
+            splits = K > 0 ? (K + kchunk - 1) / kchunk : 1;
+            k.kchunk = (int)kchunk;
+            k.seg = SegK{x.A.p, x.A.rs, x.A.cs, x.B.p, x.B.rs, x.B.cs, (int)K,
+                         (al16(x.A.p) && ((x.A.cs == 1 && x.A.rs % 4 == 0) || (x.A.rs == 1 && x.A.cs % 4 == 0))) ? 1 : 0,
+                         (al16(x.B.p) && ((x.B.cs == 1 && x.B.rs % 4 == 0) || (x.B.rs == 1 && x.B.cs % 4 == 0))) ? 1 : 0};
+            k.M = x.M;
+            k.tiles_n = (int)nblk(x.N, 64);
+            k.units = (int)(nblk(x.M, 64) * k.tiles_n * splits);
+        } else {
+            const int64_t per = std::max<int64_t>(1, (K + splits - 1) / splits);
+            splits = K > 0 ? (K + per - 1) / per : 1;
+            k.kchunk = (int)per;
+            k.seg = SegK{x.A.p, x.A.rs, 1, x.B.p, x.B.rs, 1, (int)K, 0, 0};
+            k.M = 1;
+            k.tiles_n = 1;
+            k.units = (int)(nblk(x.N, 64) * splits);
+        }
+        k.N = x.N;
+        k.splits = (int)splits;
+        k.out = x.out;
+        k.ldo = x.ldo;
+        k.partial = sc.partial + off;
+        off += (size_t)splits * (size_t)k.M * (size_t)x.N;
+        if (off > sc.cap)
+            return hipErrorInvalidValue;
+        k.unit0 = units;
+        units += k.units;
+        k.red0 = reds;
+        reds += (int)nblk((int64_t)k.M * x.N * 8, 256);
+        ++jj;
+    }
+    G.n = jj;
+    hipLaunchKernelGGL(k_leaf_split, dim3((unsigned)units), dim3(256), 0, s, G);
+    hipLaunchKernelGGL(k_leaf_reduce, dim3((unsigned)reds), dim3(256), 0, s, G);
     return hipGetLastError();
 }
 
