@@ -174,13 +174,10 @@ hipError_t pool_bwd(int B, int A, int T, int U, const uint8_t *usable, const int
 // (reverse_index_count_ints(nkeys) ints in all).
 constexpr int kSortCap = 2048;
 inline int64_t reverse_index_count_ints(int64_t nkeys) { return nkeys + nkeys / 2048 + 2; }
+// With inv (n ints), inv[e] = the position of entry e in list, for every
+// listed entry (others are left as they were).
 hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *count,
-                         int32_t *offset, int32_t *list, hipStream_t s);
-
-// inv[e] = position of entry e in list (-1 for entries not listed), for
-// entries e < n.
-hipError_t reverse_index_inverse(const int32_t *offset, int nkeys, const int32_t *list,
-                                 int64_t n, int32_t *inv, hipStream_t s);
+                         int32_t *offset, int32_t *list, hipStream_t s, int32_t *inv = nullptr);
 
 // out[k, :] = sum over list entries e of key k (in list order) of X[e, :].
 hipError_t segment_sum(int nkeys, int W, const int32_t *offset, const int32_t *list,
@@ -212,7 +209,7 @@ struct SlotBwdArgs {
     // the logits' gradients and the weights in the key-major order of the
     // reverse index: [list position][H]
     float *dS, *Pk;
-    int32_t *inv;             // [B*A*K]: list position of each slot entry, or -1
+    int32_t *inv;             // [B*A*K]: list position of each allowed slot entry
     int32_t *wide;            // queue of 16-query blocks with a wide key band
                               // (count, then block ids; null: no block form)
     int rec0;                 // first pair-parameter record of a launch

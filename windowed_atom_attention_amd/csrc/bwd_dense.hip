@@ -819,9 +819,11 @@ __global__ __launch_bounds__(256) void k_ri_fill(const int32_t *key_of, int64_t 
 
 // Sort every list of at most kSortCap entries ascending, one wave per key:
 // an entry's place is the number of smaller entries in its list (entries
-// are distinct), counted over lane exchanges (<= 64) or an LDS copy.
+// are distinct), counted over lane exchanges (<= 64) or an LDS copy. With
+// inv, every listed entry's final place is also written there (lists of
+// one entry and lists longer than kSortCap keep their order).
 __global__ __launch_bounds__(256) void k_ri_sort(const int32_t *offset, int nkeys,
-                                                 int32_t *list) {
+                                                 int32_t *list, int32_t *inv) {
     __shared__ int32_t sh[4][kSortCap];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int key = blockIdx.x * 4 + w;
@@ -832,13 +834,19 @@ __global__ __launch_bounds__(256) void k_ri_sort(const int32_t *offset, int nkey
     }
     const bool small = L > 1 && L <= 64;
     const bool mid = L > 64 && L <= kSortCap;
+    if (inv && (L == 1 || L > kSortCap))
+        for (int i = lane; i < L; i += 64)
+            inv[list[o + i]] = o + i;
     if (small) {
         const int32_t x = lane < L ? list[o + lane] : 0x7fffffff;
         int rank = 0;
         for (int m = 0; m < L; ++m)
             rank += __shfl(x, m) < x ? 1 : 0;
-        if (lane < L)
+        if (lane < L) {
             list[o + rank] = x;
+            if (inv)
+                inv[x] = o + rank;
+        }
     }
     if (mid)
         for (int i = lane; i < L; i += 64)
@@ -851,16 +859,9 @@ __global__ __launch_bounds__(256) void k_ri_sort(const int32_t *offset, int nkey
             for (int m = 0; m < L; ++m)
                 rank += sh[w][m] < x ? 1 : 0;
             list[o + rank] = x;
+            if (inv)
+                inv[x] = o + rank;
         }
-}
-
-// inv[list[p]] = p for every listed entry (inv pre-filled with -1)
-__global__ __launch_bounds__(256) void k_ri_inverse(const int32_t *offset, int nkeys,
-                                                    const int32_t *list, int32_t *inv) {
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (p >= offset[nkeys])
-        return;
-    inv[list[p]] = (int32_t)p;
 }
 
 __global__ __launch_bounds__(256) void k_segment_sum(int nkeys, int W, const int32_t *offset,
@@ -1184,7 +1185,7 @@ hipError_t token_keys(int B, int A, int T, const uint8_t *usable, const int64_t 
 }
 
 hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *count,
-                         int32_t *offset, int32_t *list, hipStream_t s) {
+                         int32_t *offset, int32_t *list, hipStream_t s, int32_t *inv) {
     hipLaunchKernelGGL(k_fill_int, dim3(nblk(nkeys, 256)), dim3(256), 0, s, count,
                        (int64_t)nkeys, 0);
     if (n > 0)
@@ -1203,7 +1204,7 @@ hipError_t reverse_index(const int32_t *key_of, int64_t n, int nkeys, int32_t *c
         hipLaunchKernelGGL(k_ri_fill, dim3(nblk(n, 256)), dim3(256), 0, s, key_of, n,
                            (const int32_t *)offset, count, list);
     hipLaunchKernelGGL(k_ri_sort, dim3(nblk(nkeys, 4)), dim3(256), 0, s,
-                       (const int32_t *)offset, nkeys, list);
+                       (const int32_t *)offset, nkeys, list, inv);
     return hipGetLastError();
 }
 
@@ -1211,15 +1212,6 @@ hipError_t fill_int(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
     if (n <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(k_fill_int, dim3(nblk(n, 256)), dim3(256), 0, s, p, n, v);
-    return hipGetLastError();
-}
-
-hipError_t reverse_index_inverse(const int32_t *offset, int nkeys, const int32_t *list,
-                                 int64_t n, int32_t *inv, hipStream_t s) {
-    if (n <= 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(k_fill_int, dim3(nblk(n, 256)), dim3(256), 0, s, inv, n, -1);
-    hipLaunchKernelGGL(k_ri_inverse, dim3(nblk(n, 256)), dim3(256), 0, s, offset, nkeys, list, inv);
     return hipGetLastError();
 }
 

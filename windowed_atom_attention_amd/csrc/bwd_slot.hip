@@ -1311,9 +1311,8 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
     // reverse index of the slot -> key map and each entry's place in it
     ProfSpan sp = prof_begin(KN_BWD_SLOT_KV, s);
     {
-        hipError_t e0 = reverse_index(a.kid, N * a.K, (int)N, a.count, a.offset, a.list, s);
-        if (e0 == hipSuccess)
-            e0 = reverse_index_inverse(a.offset, (int)N, a.list, N * a.K, a.inv, s);
+        const hipError_t e0 =
+            reverse_index(a.kid, N * a.K, (int)N, a.count, a.offset, a.list, s, a.inv);
         if (e0 != hipSuccess)
             return e0;
     }
