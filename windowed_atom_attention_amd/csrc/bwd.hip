@@ -558,9 +558,20 @@ int run_backward(const atom_attn_dims *d, int style, int stage, int dtype,
           ej(EW_DGATE, N, HD, b.dGp, HD, b.dog, HD, b.o, HD, b.g, HD)});
     prof_end(sp, s);
     // slot attention
+    // with four heads the pair parameters' sums over the partial records are
+    // leaves on the side stream (the records' [V] and [V][4] blocks are the
+    // gradients' layouts); otherwise slot_bwd sums them itself
+    const bool pw_leaf = af3 && gpar && H == 4;
     if (r.err == hipSuccess)
-        r.ok(slot_bwd(sa, af3 ? STYLE_AF3 : STYLE_ESM, gpar ? gpar->pair_scale : nullptr,
-                      gpar ? gpar->w_pair : nullptr, s));
+        r.ok(slot_bwd(sa, af3 ? STYLE_AF3 : STYLE_ESM,
+                      (gpar && !pw_leaf) ? gpar->pair_scale : nullptr,
+                      (gpar && !pw_leaf) ? gpar->w_pair : nullptr, s));
+    if (pw_leaf && r.err == hipSuccess) {
+        const int rec = slot_bwd_records(sa);
+        r.fork();
+        r.leaf_cs(rec, V, b.pwp, kSlotPairRecord, nullptr, 0, gpar->pair_scale);
+        r.leaf_cs(rec, V * 4, b.pwp + 16, kSlotPairRecord, nullptr, 0, gpar->w_pair);
+    }
     sp = prof_begin(KN_BWD_CHAIN, s);
     if (!af3 && r.err == hipSuccess)
         r.ok(head_rope_bwd(N, H, D, eps, b.qraw, b.kraw, cs_f, sn_f, b.dq, b.dk, dcos, dsin, s));

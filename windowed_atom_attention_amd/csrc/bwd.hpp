@@ -229,6 +229,10 @@ hipError_t slot_bwd(const SlotBwdArgs &a, int style, float *d_pair_scale, float 
 // query rows, and the ints of its queue of wide blocks.
 size_t slot_bwd_partial_floats(int64_t B, int64_t A, int V, int H);
 int64_t slot_bwd_queue_ints(int64_t B, int64_t A);
+// Pair-parameter partial records slot_bwd writes (rows of
+// kSlotPairRecord floats: [16] pair_scale sums, then [16][4] w_pair sums).
+constexpr int kSlotPairRecord = 16 + 16 * 4;
+int slot_bwd_records(const SlotBwdArgs &a);
 
 } // namespace bwd
 } // namespace waa

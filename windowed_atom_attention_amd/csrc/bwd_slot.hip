@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kMaxK = 512, kMaxH = 8, kMaxHD = 256;
 constexpr int kPairV = 16, kPairH = 4; // AF3 pair-bias gradient bounds
+static_assert(kSlotPairRecord == kPairV + kPairV * kPairH, "record layout");
 
 struct SK {
     SlotBwdArgs a;
@@ -1186,6 +1187,11 @@ int slot_bwd_supported(int K, int H, int D, int V, int style) {
     if (style == STYLE_AF3 && (V < 1 || V > kPairV || H > kPairH))
         return 0;
     return 1;
+}
+
+int slot_bwd_records(const SlotBwdArgs &a) {
+    const int nblocks = a.B * ((a.A + 15) / 16);
+    return block_form(a, nblocks) ? 5 * nblocks : (int)nblk((int64_t)a.B * a.A, 4);
 }
 
 size_t slot_bwd_partial_floats(int64_t B, int64_t A, int V, int H) {
