@@ -160,6 +160,59 @@ def kernel_of(symbol):
 COPY_PROBE_BYTES = 1 << 30
 
 
+def measured_peaks(reps=10):
+    """Achievable ceilings on this GPU, beside the spec peaks: HBM from a
+    1 GiB device-to-device copy (bytes read + written per second), the
+    matrix cores from large square fp32 and bf16 products (torch.matmul,
+    TF32 off; 2 n^3 flops each). The rooflines report their fraction of
+    these as the secondary figure (the spec peak stays primary)."""
+    import torch
+    torch.backends.cuda.matmul.allow_tf32 = False
+    dev = torch.device("cuda:0")
+
+    def tavg(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+
+    n = 1 << 28  # fp32 elements: 1 GiB
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    t = tavg(lambda: dst.copy_(src))
+    out = {"hbm_copy_GBps": 2.0 * 4 * n / t / 1e9, "copy_bytes": 4 * n}
+    del src, dst
+    for name, dt, m in (("fp32", torch.float32, 8192), ("bf16", torch.bfloat16, 8192)):
+        a = torch.randn((m, m), device=dev).to(dt)
+        b = torch.randn((m, m), device=dev).to(dt)
+        t = tavg(lambda: torch.matmul(a, b))
+        out["%s_matmul_TFLOPs" % name] = 2.0 * m ** 3 / t / 1e12
+        del a, b
+    out["matmul_n"] = 8192
+    torch.cuda.empty_cache()
+    return out
+
+
+def _with_measured(roof, peaks, dtype):
+    """Add the fraction of the measured ceiling to a roofline record."""
+    if not peaks or not roof:
+        return roof
+    if roof["bound"] == "hbm":
+        ref = peaks["hbm_copy_GBps"]
+    else:
+        ref = peaks["fp32_matmul_TFLOPs" if dtype == "f32" else "bf16_matmul_TFLOPs"]
+    roof = dict(roof)
+    roof["peak_measured"] = ref
+    roof["frac_measured"] = roof["achieved"] / ref
+    return roof
+
+
 def copy_probe(reps=5):
     """A plain elementwise copy (y = -x, fp32) of COPY_PROBE_BYTES read and
     the same written, the calibration kernel for the HBM byte counters."""
@@ -636,7 +689,10 @@ def main():
                     help="time only the backward pass of --backward (for profiler runs)")
     ap.add_argument("--cache-bytes", type=float, default=768e6,
                     help="input copies are added until they exceed this")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU baseline and the measured ceilings (profiler runs)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured ceilings (copy and matrix-product microbenchmarks)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs that capture one step each")
     ap.add_argument("--pack-per-call", action="store_true",
@@ -685,6 +741,14 @@ def main():
     ops = None if args.no_ops else measure_ops(args.also_steps)
     bwd = measure_backward(bwd_names, 20, 3) if bwd_names else None
 
+    peaks = None if (args.no_peaks or args.no_cpu_baseline) else measured_peaks()
+    if peaks:
+        head["roofline"] = _with_measured(head["roofline"], peaks, head["dtype"])
+        for r in others.values():
+            r["roofline"] = _with_measured(r["roofline"], peaks, r["dtype"])
+        print("bench: measured ceilings %s" % json.dumps({k: round(v, 1) for k, v in peaks.items()}),
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.config)
@@ -704,6 +768,7 @@ def main():
         "atoms_per_s": head["atoms_per_s"],
         "kernels": head["kernels"],
         "roofline": head["roofline"],
+        "peaks_measured": peaks,
         "cpu_baseline": cpu,
         "configs": others,
         "ops": ops,
