@@ -11,10 +11,10 @@
 // k_s2p_tok: one workgroup per TT tokens: the rows in LDS (fp32), their
 //   population statistics, the affine norm and the projection (VALU, fp32),
 //   written as fp32 [B,N,2H] rows (q then k) to the workspace.
-// k_s2p_pair: one workgroup per query token i and TPW tiles of 32 key tokens
-//   j; NW = D/32 waves, wave w owns output columns 32w..32w+31. The A
+// k_s2p_pair: one workgroup per tile of 32 key tokens j and kIG query tokens
+//   i; NW = D/32 waves, wave w owns output columns 32w..32w+31. The A
 //   operand of the pair head is the pair-feature row itself, formed chunk by
-//   chunk in registers from q_j (fp32, L2) and k_i (fp32, LDS) and rounded
+//   chunk in registers from q_j (fp32, registers) and k_i (fp32, LDS) and rounded
 //   to the storage type -- exactly the values stored as pair_features, so
 //   output = stored features @ out_weight on the matrix cores (32x32 MFMA,
 //   fp32 accumulation). Each wave stores the feature chunks kc = w (mod NW);
@@ -32,31 +32,48 @@ namespace waa {
 namespace {
 
 constexpr int kTT = 4;   // tokens per workgroup of the token kernel
-constexpr int kTPW = 8;  // 32-pair tiles per workgroup of the pair kernel
+constexpr int kTokThreads = 1024;  // threads per workgroup of the token kernel
+constexpr int kIG = 8;   // query tokens per workgroup of the pair kernel
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_s2p_tok(S2PArgs p) {
+__global__ __launch_bounds__(kTokThreads) void k_s2p_tok(S2PArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NWV = kTokThreads / 64;
     const int C = p.C, H2 = 2 * p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * kTT;
     const int64_t ntok = (int64_t)p.B * p.N;
     float *xs = reinterpret_cast<float *>(smem);   // [kTT][C]
     float *st = xs + kTT * C;                       // [kTT][2] mean, rstd
-    float *red = st + 2 * kTT;                      // [P][kTT][2H] partial sums
+    float *red = st + 2 * kTT;                      // [NWV][kTT][2H] partial sums
     const T *x = reinterpret_cast<const T *>(p.x);
-    // rows in LDS (absent or missing tokens as zeros, never read)
-    for (int e = tid; e < kTT * C; e += 256) {
-        const int r = e / C, c = e - r * C;
-        const int64_t t = t0 + r;
-        float v = 0.0f;
-        if (t < ntok && p.mask[t])
-            v = to_f(x[t * C + c]);
-        xs[e] = v;
+    // rows in LDS: the row and presence loads of four elements are issued
+    // together from clamped indices, absent or missing tokens are selected to
+    // zeros (their payloads never enter arithmetic)
+    const int nel = kTT * C;
+    for (int e0 = tid; e0 < nel; e0 += 4 * kTokThreads) {
+        T v[4];
+        uint8_t m[4];
+        bool in[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = min(e0 + u * kTokThreads, nel - 1);
+            const int r = e / C;
+            const int64_t t = min(t0 + r, ntok - 1);
+            in[u] = t0 + r < ntok;
+            m[u] = p.mask[t];
+            v[u] = x[t * C + (e - r * C)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kTokThreads;
+            if (e < nel)
+                xs[e] = in[u] && m[u] != 0 ? to_f(v[u]) : 0.0f;
+        }
     }
     __syncthreads();
     // population mean and variance (two passes over LDS), one row per wave
-    for (int r = wave; r < kTT; r += 4) {
+    for (int r = wave; r < kTT; r += NWV) {
         float s = 0.0f;
         for (int c = lane; c < C; c += 64)
             s += xs[r * C + c];
@@ -76,18 +93,19 @@ __global__ __launch_bounds__(256) void k_s2p_tok(S2PArgs p) {
     __syncthreads();
     const T *ns = reinterpret_cast<const T *>(p.norm_scale);
     const T *nb = reinterpret_cast<const T *>(p.norm_bias);
-    for (int e = tid; e < kTT * C; e += 256) {
+    for (int e = tid; e < nel; e += kTokThreads) {
         const int r = e / C, c = e - r * C;
         xs[e] = (xs[e] - st[2 * r]) * st[2 * r + 1] * to_f(ns[c]) + to_f(nb[c]);
     }
     __syncthreads();
     // projection: thread -> (group of E consecutive output columns, one of
     // P parts of the C range). One 16-byte weight load feeds kTT x E FMAs;
-    // eight loads are in flight at a time; the parts reduce through LDS.
+    // eight loads are in flight at a time. The parts of a wave reduce with
+    // lane exchanges, the waves' partial sums through LDS in wave order.
     constexpr int E = 16 / sizeof(T);
-    const int ng = H2 / E, P = 256 / ng;             // ng divides 256 (2H a power of 2)
+    const int ng = H2 / E, P = kTokThreads / ng;   // ng divides 64 (2H a power of 2)
     const int og = tid % ng, part = tid / ng;
-    const int clo = part * C / P, chi = (part + 1) * C / P;
+    const int clo = (int)((int64_t)part * C / P), chi = (int)((int64_t)(part + 1) * C / P);
     const T *w = reinterpret_cast<const T *>(p.weight) + og * E;
     float acc[kTT][E];
 #pragma unroll
@@ -115,17 +133,25 @@ __global__ __launch_bounds__(256) void k_s2p_tok(S2PArgs p) {
             }
         }
     }
+    for (int o = ng; o < 64; o <<= 1)
 #pragma unroll
-    for (int rr = 0; rr < kTT; ++rr)
+        for (int rr = 0; rr < kTT; ++rr)
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            red[(part * kTT + rr) * H2 + og * E + e] = acc[rr][e];
+            for (int e = 0; e < E; ++e)
+                acc[rr][e] += __shfl_xor(acc[rr][e], o);
+    if (lane < ng)
+#pragma unroll
+        for (int rr = 0; rr < kTT; ++rr)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                red[(wave * kTT + rr) * H2 + og * E + e] = acc[rr][e];
     __syncthreads();
     const T *bias = reinterpret_cast<const T *>(p.bias);
-    for (int idx = tid; idx < kTT * H2; idx += 256) {
+    for (int idx = tid; idx < kTT * H2; idx += kTokThreads) {
         const int rr = idx / H2, oo = idx - rr * H2;
         float v = to_f(bias[oo]);
-        for (int q = 0; q < P; ++q)
+#pragma unroll
+        for (int q = 0; q < NWV; ++q)
             v += red[(q * kTT + rr) * H2 + oo];
         const int64_t t = t0 + rr;
         if (t < ntok)
@@ -133,11 +159,15 @@ __global__ __launch_bounds__(256) void k_s2p_tok(S2PArgs p) {
     }
 }
 
-// NW = D/32 waves, HH = H (q and k width). Each lane owns one row r = lane%32
-// of a 32-pair tile and the lane half hh = lane/32 of every A chunk: feature
-// indices kc*KC + hh*HALF + e. Chunks kc < H/KC are products k_i*q_j, the
-// rest differences q_j - k_i of the same q indices, so a lane keeps H/2
-// values of q_j in registers.
+// NW = D/32 waves, HH = H (q and k width). A workgroup owns one tile of 32
+// key tokens j and kIG query tokens i. Each lane owns one row r = lane%32 of
+// the tile and the lane half hh = lane/32 of every A chunk: feature indices
+// kc*KC + hh*HALF + e. Chunks kc < H/KC are products k_i*q_j, the rest
+// differences q_j - k_i of the same q indices, so a lane keeps H/2 values of
+// q_j in registers for the whole workgroup. Everything the loop over i reads
+// (q_j, the masks, k_i, the weight fragments) is loaded before it, so the
+// loop issues only stores and LDS traffic: a global load inside it would
+// make each tile wait for the stores issued before it.
 template <typename T, int HH, int NW, bool NORM>
 __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -146,32 +176,29 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
     const int N = p.N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ntile = (N + 31) / 32;
-    const int ngrp = (ntile + kTPW - 1) / kTPW;
-    const int64_t bi = blockIdx.x / ngrp;        // b * N + i
-    const int tg = blockIdx.x % ngrp;
-    const int64_t b = bi / N;
-    const int tlo = tg * kTPW, thi = min(ntile, tlo + kTPW);
+    const int nig = (N + kIG - 1) / kIG;
+    const int t = blockIdx.x % ntile;              // key tile
+    const int64_t bg = blockIdx.x / ntile;         // b * nig + query group
+    const int64_t b = bg / nig;
+    const int i0 = (int)(bg % nig) * kIG;
+    const int j0 = t * 32;
+    const int ni = min(kIG, N - i0);
     constexpr int SP = D + 4;                     // LDS row pitch of the output tile (fp32)
-    float *ki = reinterpret_cast<float *>(smem);  // [H] k_i
-    float *ot = ki + HH;                          // [32][SP] output tile
+    float *ki = reinterpret_cast<float *>(smem);  // [kIG][H] k_i
+    float *ot = ki + kIG * HH;                    // [32][SP] output tile
     float *red = ot + 32 * SP;                    // [NW][32] row partial sums
-    T *pf = reinterpret_cast<T *>(p.pair_features) + bi * (int64_t)N * H2;
-    T *out = reinterpret_cast<T *>(p.output) + bi * (int64_t)N * D;
-    constexpr int VPF = H2 / E, VPO = D / E;      // 16-byte vectors per row
-    if (p.mask[bi] == 0) {
-        // absent query token: its rows of both tensors are zeros
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        for (int t = tlo; t < thi; ++t) {
-            const int rows = min(32, N - t * 32);
-            for (int idx = tid; idx < rows * VPF; idx += 64 * NW)
-                reinterpret_cast<uint4 *>(pf + (int64_t)t * 32 * H2)[idx] = z;
-            for (int idx = tid; idx < rows * VPO; idx += 64 * NW)
-                reinterpret_cast<uint4 *>(out + (int64_t)t * 32 * D)[idx] = z;
-        }
-        return;
+    int *mi = reinterpret_cast<int *>(red + NW * 32);  // [kIG] query presence
+    int *mj = mi + kIG;                           // [32] key presence
+    const float *qk = p.qk + b * (int64_t)N * H2;
+    const uint8_t *mrow = p.mask + b * N;
+    for (int e = tid; e < kIG * HH; e += 64 * NW) {
+        const int ii = e / HH;
+        ki[e] = p.qk[(b * N + i0 + min(ii, ni - 1)) * H2 + HH + (e - ii * HH)];
     }
-    for (int e = tid; e < HH; e += 64 * NW)
-        ki[e] = p.qk[bi * H2 + HH + e];
+    if (tid < kIG)
+        mi[tid] = tid < ni ? mrow[i0 + tid] : 0;
+    if (tid < 32)
+        mj[tid] = j0 + tid < N ? mrow[j0 + tid] : 0;
     // B fragments of this wave's 32 output columns over all 2H feature rows,
     // from the packed copy of out_weight (one 16-byte load per chunk)
     const int col = wave * 32 + (lane & 31), hh = lane >> 5;
@@ -185,36 +212,36 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
         osc = to_f(reinterpret_cast<const T *>(p.output_scale)[col]);
         osh = to_f(reinterpret_cast<const T *>(p.output_bias)[col]);
     }
-    __syncthreads();
-    const float *qk = p.qk + b * (int64_t)N * H2;
-    const uint8_t *mrow = p.mask + b * N;
+    // this lane's q_j values (indices qc*KC + hh*HALF + e, qc < H/KC)
     const int r = lane & 31;
-    // this lane's q_j values (indices qc*KC + hh*HALF + e, qc < H/KC) of
-    // tile t, loaded one tile ahead
-    float4 qn[NQC][HALF / 4];
-    auto load_q = [&](int t) {
-        const int jr = min(t * 32 + r, N - 1);
+    const int jr = min(j0 + r, N - 1);            // clamped row of this lane
+    float qv[NQC][HALF];
 #pragma unroll
-        for (int qc = 0; qc < NQC; ++qc)
+    for (int qc = 0; qc < NQC; ++qc)
 #pragma unroll
-            for (int e = 0; e < HALF; e += 4)
-                qn[qc][e / 4] = *reinterpret_cast<const float4 *>(
-                    qk + (int64_t)jr * H2 + qc * KC + hh * HALF + e);
-    };
-    load_q(tlo);
-    for (int t = tlo; t < thi; ++t) {
-        const int j0 = t * 32;
-        const int jr = min(j0 + r, N - 1);            // clamped row of this lane
-        const bool live = j0 + r < N && mrow[jr] != 0;
-        float qv[NQC][HALF];
-#pragma unroll
-        for (int qc = 0; qc < NQC; ++qc)
-#pragma unroll
-            for (int e = 0; e < HALF; e += 4) {
-                const float4 f = qn[qc][e / 4];
-                qv[qc][e] = f.x; qv[qc][e + 1] = f.y; qv[qc][e + 2] = f.z; qv[qc][e + 3] = f.w;
-            }
-        load_q(min(t + 1, thi - 1));
+        for (int e = 0; e < HALF; e += 4) {
+            const float4 f = *reinterpret_cast<const float4 *>(
+                qk + (int64_t)jr * H2 + qc * KC + hh * HALF + e);
+            qv[qc][e] = f.x; qv[qc][e + 1] = f.y; qv[qc][e + 2] = f.z; qv[qc][e + 3] = f.w;
+        }
+    const bool jlive = j0 + r < N && mrow[jr] != 0;
+    __syncthreads();
+    constexpr int VPF = H2 / E, VPO = D / E;      // 16-byte vectors per row
+    const int rows = min(32, N - j0);
+    for (int ii = 0; ii < ni; ++ii) {
+        const int64_t bi = b * N + i0 + ii;
+        T *pf = reinterpret_cast<T *>(p.pair_features) + (bi * N + j0) * (int64_t)H2;
+        T *out = reinterpret_cast<T *>(p.output) + (bi * N + j0) * (int64_t)D;
+        if (mi[ii] == 0) {
+            // absent query token: its rows of both tensors are zeros
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            for (int idx = tid; idx < rows * VPF; idx += 64 * NW)
+                reinterpret_cast<uint4 *>(pf)[idx] = z;
+            for (int idx = tid; idx < rows * VPO; idx += 64 * NW)
+                reinterpret_cast<uint4 *>(out)[idx] = z;
+            continue;
+        }
+        const float *kis = ki + ii * HH;
         f32x16_t acc = zero16();
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
@@ -223,14 +250,14 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
             float f[HALF];
 #pragma unroll
             for (int e = 0; e < HALF; ++e)
-                f[e] = kc < NQC ? ki[m0 + e] * qv[qc][e] : qv[qc][e] - ki[m0 + e];
+                f[e] = kc < NQC ? kis[m0 + e] * qv[qc][e] : qv[qc][e] - kis[m0 + e];
             const uint4 a = pack16<T>(f);
             Mma32<T>::mma(acc, a, bfrag[kc]);
             // this wave stores feature chunks kc = wave (mod NW); absent
             // pairs are zeros
-            if (kc % NW == wave && j0 + r < N)
-                *reinterpret_cast<uint4 *>(pf + (int64_t)(j0 + r) * H2 + k0) =
-                    live ? a : make_uint4(0, 0, 0, 0);
+            if (kc % NW == wave && r < rows)
+                *reinterpret_cast<uint4 *>(pf + (int64_t)r * H2 + k0) =
+                    jlive ? a : make_uint4(0, 0, 0, 0);
         }
         // bias, then the optional LayerNorm over the D columns (rows are
         // split over the NW waves: sums over a wave's 32 lanes, then partial
@@ -281,14 +308,10 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
             ot[acc32_row(e, lane) * SP + col] = v[e];
         __syncthreads();
         // rows of the tile as 16-byte vectors; absent pairs as zeros
-        for (int idx = tid; idx < 32 * VPO; idx += 64 * NW) {
+        for (int idx = tid; idx < rows * VPO; idx += 64 * NW) {
             const int rr = idx / VPO, c0 = (idx - rr * VPO) * E;
-            const int j = j0 + rr;
-            if (j < N) {
-                const bool ok = mrow[j] != 0;
-                *reinterpret_cast<uint4 *>(out + (int64_t)j * D + c0) =
-                    ok ? pack16<T>(ot + rr * SP + c0) : make_uint4(0, 0, 0, 0);
-            }
+            *reinterpret_cast<uint4 *>(out + (int64_t)rr * D + c0) =
+                mj[rr] != 0 ? pack16<T>(ot + rr * SP + c0) : make_uint4(0, 0, 0, 0);
         }
         __syncthreads(); // the tile and the partial sums are rewritten next
     }
@@ -296,9 +319,12 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
 
 } // namespace
 
-size_t s2p_tok_lds(int C) { return (size_t)kTT * C * 4 + kTT * 2 * 4 + (size_t)256 * 8 * kTT * 4; }
+size_t s2p_tok_lds(int C, int H) {
+    return ((size_t)kTT * C + kTT * 2 + (size_t)(kTokThreads / 64) * kTT * 2 * H) * 4;
+}
 size_t s2p_pair_lds(int H, int D) {
-    return ((size_t)H + 32 * (size_t)(D + 4) + (size_t)(D / 32) * 32) * 4;
+    return ((size_t)kIG * H + 32 * (size_t)(D + 4) + (size_t)(D / 32) * 32) * 4 +
+           (size_t)(kIG + 32) * 4;
 }
 
 int s2p_supported(int64_t C, int64_t H, int64_t D, int dtype) {
@@ -329,20 +355,20 @@ hipError_t launch_s2p(const S2PArgs &a, int dtype, int output_norm, hipStream_t 
         if (e != hipSuccess)
             return e;
     }
-    const size_t lt = s2p_tok_lds(a.C);
+    const size_t lt = s2p_tok_lds(a.C, a.H);
     const void *ft = dtype ? (const void *)k_s2p_tok<bf16_t> : (const void *)k_s2p_tok<float>;
     allow_lds(ft, lt);
     S2PArgs pa = a;
     void *args[] = {(void *)&pa};
     ProfSpan sp = prof_begin(KN_S2P_TOK, s);
-    hipError_t e = hipLaunchKernel(ft, dim3((unsigned)((ntok + kTT - 1) / kTT)), dim3(256), args,
+    hipError_t e = hipLaunchKernel(ft, dim3((unsigned)((ntok + kTT - 1) / kTT)), dim3(kTokThreads), args,
                                    lt, s);
     prof_end(sp, s);
     if (e != hipSuccess)
         return e;
     const int nw = a.D / 32;
     const int ntile = (a.N + 31) / 32;
-    const int64_t grid = ntok * ((ntile + kTPW - 1) / kTPW);
+    const int64_t grid = (int64_t)a.B * ((a.N + kIG - 1) / kIG) * ntile;
     const void *fp;
     if (dtype)
         fp = a.H == 32 ? pick_s2p<bf16_t, 32>(nw, output_norm)
