@@ -572,7 +572,8 @@ def measure_ops(steps=50, warmup=5, cache_bytes=768e6):
     for k, f in flops.items():
         _roof(kt[k], "mfma", f, "bf16")
     _roof(kt["tied_softmax"], "hbm", B * H * L * L * (4 + 4 + 2), "bf16")
-    _roof(kt["tied_bias"], "hbm", LL * CB * 2 + B * H * L * L * 4, "bf16")
+    if "tied_bias" in kt:   # beta is formed inside k_tied_proj for most Cb
+        _roof(kt["tied_bias"], "hbm", LL * CB * 2 + B * H * L * L * 4, "bf16")
     res["tied_row_attention"] = {
         "workload": "B=%d L=%d C=%d CB=%d H=%d D=%d bf16" % (B, L, C, CB, H, HD // H),
         "ms_per_call": wall * 1e3, "pair_entries_per_s": LL / wall, "kernels": kt,

@@ -132,7 +132,7 @@ struct S2PArgs {
 hipError_t launch_s2p(const S2PArgs &a, int dtype, int output_norm, hipStream_t s);
 int s2p_supported(int64_t C, int64_t H, int64_t D, int dtype);
 size_t s2p_tok_lds(int C, int H);
-size_t s2p_pair_lds(int H, int D);
+size_t s2p_pair_lds(int H, int D, int esz);
 
 // One matrix to pack: src[r*ld + c] for r < kd, c < n (storage dtype).
 struct PackJob {

@@ -93,9 +93,23 @@ __global__ __launch_bounds__(kTokThreads) void k_s2p_tok(S2PArgs p) {
     __syncthreads();
     const T *ns = reinterpret_cast<const T *>(p.norm_scale);
     const T *nb = reinterpret_cast<const T *>(p.norm_bias);
-    for (int e = tid; e < nel; e += kTokThreads) {
-        const int r = e / C, c = e - r * C;
-        xs[e] = (xs[e] - st[2 * r]) * st[2 * r + 1] * to_f(ns[c]) + to_f(nb[c]);
+    for (int e0 = tid; e0 < nel; e0 += 4 * kTokThreads) {
+        T sv[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = min(e0 + u * kTokThreads, nel - 1);
+            const int c = e - (e / C) * C;
+            sv[u] = ns[c];
+            bv[u] = nb[c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kTokThreads;
+            if (e < nel) {
+                const int r = e / C;
+                xs[e] = (xs[e] - st[2 * r]) * st[2 * r + 1] * to_f(sv[u]) + to_f(bv[u]);
+            }
+        }
     }
     __syncthreads();
     // projection: thread -> (group of E consecutive output columns, one of
@@ -189,6 +203,8 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
     float *red = ot + 32 * SP;                    // [NW][32] row partial sums
     int *mi = reinterpret_cast<int *>(red + NW * 32);  // [kIG] query presence
     int *mj = mi + kIG;                           // [32] key presence
+    constexpr int FP = H2 + E;                    // LDS row pitch of the feature tile
+    T *ft = reinterpret_cast<T *>(mj + 32);       // [32][FP] feature tile
     const float *qk = p.qk + b * (int64_t)N * H2;
     const uint8_t *mrow = p.mask + b * N;
     for (int e = tid; e < kIG * HH; e += 64 * NW) {
@@ -253,11 +269,10 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
                 f[e] = kc < NQC ? kis[m0 + e] * qv[qc][e] : qv[qc][e] - kis[m0 + e];
             const uint4 a = pack16<T>(f);
             Mma32<T>::mma(acc, a, bfrag[kc]);
-            // this wave stores feature chunks kc = wave (mod NW); absent
-            // pairs are zeros
-            if (kc % NW == wave && r < rows)
-                *reinterpret_cast<uint4 *>(pf + (int64_t)r * H2 + k0) =
-                    jlive ? a : make_uint4(0, 0, 0, 0);
+            // this wave puts feature chunks kc = wave (mod NW) into the
+            // feature tile; absent pairs are zeros
+            if (kc % NW == wave)
+                *reinterpret_cast<uint4 *>(ft + r * FP + k0) = jlive ? a : make_uint4(0, 0, 0, 0);
         }
         // bias, then the optional LayerNorm over the D columns (rows are
         // split over the NW waves: sums over a wave's 32 lanes, then partial
@@ -307,7 +322,13 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
         for (int e = 0; e < 16; ++e)
             ot[acc32_row(e, lane) * SP + col] = v[e];
         __syncthreads();
-        // rows of the tile as 16-byte vectors; absent pairs as zeros
+        // both tiles leave as whole rows of 16-byte vectors; absent pairs
+        // as zeros
+        for (int idx = tid; idx < rows * VPF; idx += 64 * NW) {
+            const int rr = idx / VPF, c0 = (idx - rr * VPF) * E;
+            *reinterpret_cast<uint4 *>(pf + (int64_t)rr * H2 + c0) =
+                *reinterpret_cast<const uint4 *>(ft + rr * FP + c0);
+        }
         for (int idx = tid; idx < rows * VPO; idx += 64 * NW) {
             const int rr = idx / VPO, c0 = (idx - rr * VPO) * E;
             *reinterpret_cast<uint4 *>(out + (int64_t)rr * D + c0) =
@@ -322,9 +343,9 @@ __global__ __launch_bounds__(64 * NW) void k_s2p_pair(S2PArgs p) {
 size_t s2p_tok_lds(int C, int H) {
     return ((size_t)kTT * C + kTT * 2 + (size_t)(kTokThreads / 64) * kTT * 2 * H) * 4;
 }
-size_t s2p_pair_lds(int H, int D) {
+size_t s2p_pair_lds(int H, int D, int esz) {
     return ((size_t)kIG * H + 32 * (size_t)(D + 4) + (size_t)(D / 32) * 32) * 4 +
-           (size_t)(kIG + 32) * 4;
+           (size_t)(kIG + 32) * 4 + (size_t)32 * (2 * H + 16 / esz) * esz;
 }
 
 int s2p_supported(int64_t C, int64_t H, int64_t D, int dtype) {
@@ -376,7 +397,7 @@ hipError_t launch_s2p(const S2PArgs &a, int dtype, int output_norm, hipStream_t 
                                     : pick_s2p<bf16_t, 128>(nw, output_norm));
     else
         fp = a.H == 32 ? pick_s2p<float, 32>(nw, output_norm) : pick_s2p<float, 64>(nw, output_norm);
-    const size_t lp = s2p_pair_lds(a.H, a.D);
+    const size_t lp = s2p_pair_lds(a.H, a.D, dtype ? 2 : 4);
     allow_lds(fp, lp);
     sp = prof_begin(KN_S2P_PAIR, s);
     e = hipLaunchKernel(fp, dim3((unsigned)grid), dim3(64 * nw), args, lp, s);

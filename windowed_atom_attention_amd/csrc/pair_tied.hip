@@ -14,10 +14,14 @@
 //
 // Kernels (all on the caller's stream, workspace laid out by tied_layout):
 //  k_pack (pack.hip)  w_q, w_k, w_v, w_gate, w_out into MFMA B-fragment order
-//  k_tied_bias        beta, eight threads per (b, i, j), fp32
+//  k_tied_bias        beta, eight threads per (b, i, j), fp32 (only when Cb is
+//                     not a multiple of 8 or exceeds 256; else k_tied_proj
+//                     forms beta)
 //  k_tied_proj        one workgroup per 32 entries F[j0..j0+31][kcol] of a
 //                     grid column: affine LayerNorm (fp32) into an LDS
-//                     operand tile, then q|k and v|gate on MFMA (32x32
+//                     operand tile (and, for the bias, the LayerNorm of
+//                     Fb[j][kcol] times w_bias, written as beta[h][kcol][j]),
+//                     then q|k and v|gate on MFMA (32x32
 //                     blocks, one head per block since D = 32), stored as
 //                       Qh[h][row][col*D + d], Kh[h][row][col*D + d]
 //                       Vt[h][col*D + d][row], G[row][col][h*D + d]
@@ -70,7 +74,41 @@ struct TiedArgs {
     void *qlo, *klo;                  // bf16: the rest of q and k (q = qh + qlo), else null
     float *beta, *s;                  // fp32 [B][H][Lp][Lp]
     void *out;                        // [B,L,L,C]
+    int fuse_bias;                    // beta formed by k_tied_proj (Cb % 8 == 0, Cb <= 256)
+    int vec_f, vec_fb;                // rows of F / Fb read as 16-byte vectors
 };
+
+// Channels [0, per) of one eighth of a row (per <= 32) into x, zeros past per
+// and for rows that are not valid. The loads are issued together from
+// clamped offsets before any value is used: 16-byte vectors when vec (the
+// row part 16-byte aligned), else single elements.
+template <typename T>
+__device__ __forceinline__ void load_part(const T *row, int per, bool vec, bool valid,
+                                          float (&x)[32]) {
+    constexpr int E = 16 / sizeof(T);
+    if (vec) {
+        uint4 v[32 / E];
+#pragma unroll
+        for (int u = 0; u < 32 / E; ++u)
+            v[u] = *reinterpret_cast<const uint4 *>(row + min(u * E, per - E));
+#pragma unroll
+        for (int u = 0; u < 32 / E; ++u) {
+            float f[E];
+            unpack16<T>(v[u], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                x[u * E + e] = valid && u * E + e < per ? f[e] : 0.0f;
+        }
+    } else {
+        T v[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            v[e] = row[min(e, per - 1)];
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            x[e] = valid && e < per ? to_f(v[e]) : 0.0f;
+    }
+}
 
 // ---------------------------------------------------------------- bias
 // 8 threads per (b, i, j) entry, each a strided eighth of the Cb channels;
@@ -140,27 +178,47 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
     T *opAlo = opA + 32 * lda;                    // [32][lda] (bf16 only)
     float *stg = reinterpret_cast<float *>(smem + tal16((size_t)(SPLIT ? 2 : 1) * 32 * lda * sizeof(T)));
     float *ws = stg + wave * 32 * 33;             // this wave's 32x32 staging block
-    // rows: 8 threads per entry, each C/8 channels (C multiple of 32)
+    // LayerNorm parameters (and, when beta is formed here, the bias
+    // LayerNorm's and w_bias) into LDS; rows: 8 threads per entry, each an
+    // eighth of the channels, all loads issued before the first use
+    const int Cb = p.Cb;
+    const bool fb = p.fuse_bias != 0;
+    float *prm = stg + 4 * 32 * 33;               // ns, nb [C]; bns, bnb [Cb]; w_bias [Cb][H]
+    const int nprm = 2 * C + (fb ? Cb * (2 + H) : 0);
+    {
+        for (int e0 = tid; e0 < nprm; e0 += 4 * 256) {
+            T v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = min(e0 + u * 256, nprm - 1);
+                const void *src = e < C ? p.ns : e < 2 * C ? p.nb
+                                : e < 2 * C + Cb ? p.bns : e < 2 * C + 2 * Cb ? p.bnb : p.w_bias;
+                const int base = e < C ? 0 : e < 2 * C ? C
+                               : e < 2 * C + Cb ? 2 * C : e < 2 * C + 2 * Cb ? 2 * C + Cb : 2 * C + 2 * Cb;
+                v[u] = reinterpret_cast<const T *>(src)[e - base];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e0 + u * 256 < nprm)
+                    prm[e0 + u * 256] = to_f(v[u]);
+        }
+    }
     const int r = tid >> 3, sub = tid & 7;
     const int j = j0 + r;
     const bool valid = j < L && kcol < L;
+    const int64_t ent = (b * L + min(j, L - 1)) * L + min(kcol, L - 1);
+    float x[32], xb[32];
+    const int per = C / 8, perb = Cb / 8;
+    load_part<T>(reinterpret_cast<const T *>(p.f) + ent * C + sub * per, per, p.vec_f != 0, valid, x);
+    if (fb)
+        load_part<T>(reinterpret_cast<const T *>(p.fb) + ent * Cb + sub * perb, perb,
+                     p.vec_fb != 0, valid, xb);
+    __syncthreads();
     {
-        const T *row = reinterpret_cast<const T *>(p.f) +
-                       ((b * L + min(j, L - 1)) * L + min(kcol, L - 1)) * C;
-        const T *sc = reinterpret_cast<const T *>(p.ns);
-        const T *sh = reinterpret_cast<const T *>(p.nb);
-        // channels sub*per .. sub*per+per-1 (per = C/8 <= 32), held in
-        // registers under compile-time indices
-        float x[32];
-        const int per = C / 8;
         float s = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            x[e] = 0.0f;
-            if (e < per && valid)
-                x[e] = to_f(row[sub * per + e]);
+        for (int e = 0; e < 32; ++e)
             s += x[e];
-        }
         const float mean = sum8(s) / (float)C;
         float q = 0.0f;
 #pragma unroll
@@ -174,8 +232,48 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
             if (e < per) {
                 const int c = sub * per + e;
                 put_split<T>(opA, SPLIT ? opAlo : nullptr, r * lda + c,
-                             (x[e] - mean) * rstd * to_f(sc[c]) + to_f(sh[c]));
+                             (x[e] - mean) * rstd * prm[c] + prm[C + c]);
             }
+        }
+    }
+    if (fb) {
+        // beta[h][kcol][j] of this entry: the bias row is Fb[j][kcol], the
+        // entry (query kcol, key j) once both axes are exchanged
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            s += xb[e];
+        const float mean = sum8(s) / (float)Cb;
+        float q = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const float d = e < perb ? xb[e] - mean : 0.0f;
+            q += d * d;
+        }
+        const float rstd = 1.0f / sqrtf(sum8(q) / (float)Cb + p.eps);
+        const float *bsc = prm + 2 * C, *bsh = bsc + Cb, *wb = bsh + Cb;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            if (e < perb) {
+                const int c = sub * perb + e;
+                const float xn = (xb[e] - mean) * rstd * bsc[c] + bsh[c];
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    if (h < H)
+                        acc[h] = fmaf(xn, wb[c * H + h], acc[h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+            acc[h] = sum8(acc[h]);
+        if (valid && sub < H) {
+            float v = acc[0];
+#pragma unroll
+            for (int h = 1; h < 8; ++h)
+                if (sub == h)
+                    v = acc[h];
+            p.beta[((b * H + sub) * Lp + kcol) * (int64_t)Lp + j] = v;
         }
     }
     __syncthreads();
@@ -255,28 +353,34 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
     const int Lp = p.Lp, H = p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = Lp / 32;
-    int64_t t = blockIdx.x;
-    const int ks = (int)(t % kKS); t /= kKS;
+    // logical block order (b, h, ks, ib, jb), dealt to the XCDs in
+    // contiguous runs, so that the tiles reading one K range of one head's
+    // q and k rows share an L2
+    int64_t t = xcd_remap(blockIdx.x, gridDim.x);
     const int jb = (int)(t % nb); t /= nb;
     const int ib = (int)(t % nb); t /= nb;
+    const int ks = (int)(t % kKS); t /= kKS;
     const int h = (int)(t % H);
     const int64_t b = t / H;
     const int64_t K = (int64_t)Lp * kTD;
     const T *qa = reinterpret_cast<const T *>(p.qh) + ((b * H + h) * Lp + ib * 32 + (lane & 31)) * K;
     const T *kb = reinterpret_cast<const T *>(p.kh) + ((b * H + h) * Lp + jb * 32 + (lane & 31)) * K;
-    // chunks per wave: Lp*D/KC is a multiple of 4*kKS (Lp a multiple of 32)
+    // chunks per wave: Lp*D/KC is a multiple of 4*kKS*U (Lp a multiple of 32)
     const int nkc = (int)(K / KC), per = nkc / (4 * kKS);
     const int c0 = (ks * 4 + wave) * per;
     const int hoff = (lane >> 5) * HALF;
     f32x16_t acc = zero16();
+    // two register stages: the chunks of the next step are requested before
+    // the products of this one (clamped at the end, so every load is
+    // unconditional)
     constexpr int U = 4;
     if constexpr (sizeof(T) == 2) {
         // q.k = qh.kh + qh.klo + qlo.kh (the qlo.klo term is below the
         // rounding of the sum)
         const int64_t dl = reinterpret_cast<const T *>(p.qlo) - reinterpret_cast<const T *>(p.qh);
         const int64_t dk = reinterpret_cast<const T *>(p.klo) - reinterpret_cast<const T *>(p.kh);
-        for (int kc = 0; kc < per; kc += U) {
-            uint4 av[U], bv[U], al[U], bl[U];
+        uint4 av[U], bv[U], al[U], bl[U];
+        auto ld = [&](int kc) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t o = (int64_t)(c0 + kc + u) * KC + hoff;
@@ -285,25 +389,43 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
                 al[u] = *reinterpret_cast<const uint4 *>(qa + dl + o);
                 bl[u] = *reinterpret_cast<const uint4 *>(kb + dk + o);
             }
+        };
+        ld(0);
+        for (int kc = 0; kc < per; kc += U) {
+            uint4 ca[U], cb[U], cal[U], cbl[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                Mma32<T>::mma(acc, av[u], bv[u]);
-                Mma32<T>::mma(acc, av[u], bl[u]);
-                Mma32<T>::mma(acc, al[u], bv[u]);
+                ca[u] = av[u]; cb[u] = bv[u]; cal[u] = al[u]; cbl[u] = bl[u];
+            }
+            ld(min(kc + U, per - U));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                Mma32<T>::mma(acc, ca[u], cb[u]);
+                Mma32<T>::mma(acc, ca[u], cbl[u]);
+                Mma32<T>::mma(acc, cal[u], cb[u]);
             }
         }
     } else {
-        for (int kc = 0; kc < per; kc += U) {
-            uint4 av[U], bv[U];
+        uint4 av[U], bv[U];
+        auto ld = [&](int kc) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t o = (int64_t)(c0 + kc + u) * KC + hoff;
                 av[u] = *reinterpret_cast<const uint4 *>(qa + o);
                 bv[u] = *reinterpret_cast<const uint4 *>(kb + o);
             }
+        };
+        ld(0);
+        for (int kc = 0; kc < per; kc += U) {
+            uint4 ca[U], cb[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ca[u] = av[u]; cb[u] = bv[u];
+            }
+            ld(min(kc + U, per - U));
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                Mma32<T>::mma(acc, av[u], bv[u]);
+                Mma32<T>::mma(acc, ca[u], cb[u]);
         }
     }
 #pragma unroll
@@ -484,8 +606,10 @@ TiedLayout tied_layout(int64_t B, int64_t L, int64_t C, int64_t H, int esz) {
     return Lo;
 }
 
-static size_t tied_proj_lds(int64_t C, int esz) {
-    return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (C + 16 / esz) * esz) + (size_t)4 * 32 * 33 * 4;
+static bool tied_fuse_bias(int64_t Cb) { return Cb % 8 == 0 && Cb <= 256; }
+static size_t tied_proj_lds(int64_t C, int64_t Cb, int64_t H, int esz) {
+    return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (C + 16 / esz) * esz) + (size_t)4 * 32 * 33 * 4 +
+           (size_t)(2 * C + (tied_fuse_bias(Cb) ? Cb * (2 + H) : 0)) * 4;
 }
 static size_t tied_out_lds(int64_t C, int64_t H, int esz) {
     return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (H * kTD + 16 / esz) * esz) +
@@ -572,6 +696,9 @@ int atom_attn_tied_row_attention(const atom_attn_tied_dims *d, int dtype, double
     a.klo = esz == 2 ? ws + Lo.klo : nullptr;
     a.amat = ws + Lo.amat; a.beta = (float *)(ws + Lo.beta); a.s = (float *)(ws + Lo.s);
     a.out = output;
+    a.fuse_bias = tied_fuse_bias(d->CB) ? 1 : 0;
+    a.vec_f = (C / 8 * esz) % 16 == 0;
+    a.vec_fb = a.fuse_bias && (d->CB / 8 * esz) % 16 == 0 && ((uintptr_t)bias_features & 15) == 0;
     void *args[] = {(void *)&a};
     const int64_t Lp = a.Lp;
     hipError_t e = launch_pack(pa, dt, s);
@@ -586,10 +713,11 @@ int atom_attn_tied_row_attention(const atom_attn_tied_dims *d, int dtype, double
     };
     const int64_t nb32 = Lp / 32;
     const bool ok =
-        go(KN_TIED_BIAS, dt ? (const void *)k_tied_bias<bf16_t> : (const void *)k_tied_bias<float>,
-           (a.B * (int64_t)a.L * a.L * 8 + 255) / 256, 0) &&
+        (a.fuse_bias ||
+         go(KN_TIED_BIAS, dt ? (const void *)k_tied_bias<bf16_t> : (const void *)k_tied_bias<float>,
+            (a.B * (int64_t)a.L * a.L * 8 + 255) / 256, 0)) &&
         go(KN_TIED_PROJ, dt ? (const void *)k_tied_proj<bf16_t> : (const void *)k_tied_proj<float>,
-           a.B * Lp * nb32, tied_proj_lds(C, esz)) &&
+           a.B * Lp * nb32, tied_proj_lds(C, d->CB, d->H, esz)) &&
         go(KN_TIED_LOGITS,
            dt ? (const void *)k_tied_logits<bf16_t> : (const void *)k_tied_logits<float>,
            a.B * (int64_t)a.H * nb32 * nb32 * kKS, 0) &&
