@@ -78,6 +78,24 @@ struct TiedArgs {
     int vec_f, vec_fb;                // rows of F / Fb read as 16-byte vectors
 };
 
+// Operand-fragment order of the intermediates read by the matrix products
+// (q, k, their low parts, v, A). A [rows][Kd] matrix of matrix mat is stored
+// as 1 KB fragments, one per (row tile rt of 32 rows, k chunk kc of KC):
+// lane l = r + 32*hf holds k = kc*KC + hf*HALF + e of row rt*32 + r at
+// element offset (((mat*ntiles + rt)*nkc + kc)*64 + l)*HALF + e, i.e. exactly
+// the 16 bytes that lane passes to the 32x32 MFMA, so a wave's operand load
+// is one contiguous kilobyte. frag_base gives the offset of fragment (rt, 0);
+// ntiles*32 = rows (Lp for q, k, A; Lp anchors of 32 columns for v) and
+// nkc*KC = Kd, so every matrix holds Lp*Lp*32 or Lp*Lp elements as before.
+template <typename T>
+__device__ __forceinline__ int64_t frag_base(int64_t mat, int rt, int nkc, int ntiles) {
+    return ((mat * ntiles + rt) * (int64_t)nkc) * 64 * Mma32<T>::HALF;
+}
+
+__device__ __forceinline__ float f4_get(const float4 &f, int c) {
+    return c == 0 ? f.x : c == 1 ? f.y : c == 2 ? f.z : f.w;
+}
+
 // Channels [0, per) of one eighth of a row (per <= 32) into x, zeros past per
 // and for rows that are not valid. The loads are issued together from
 // clamped offsets before any value is used: 16-byte vectors when vec (the
@@ -277,7 +295,6 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
         }
     }
     __syncthreads();
-    const int64_t LpLp = (int64_t)Lp * Lp;
     T *qh = reinterpret_cast<T *>(p.qh), *kh = reinterpret_cast<T *>(p.kh);
     T *vt = reinterpret_cast<T *>(p.vt), *gg = reinterpret_cast<T *>(p.g);
     const int nkc = C / Mma32<T>::KC;
@@ -294,24 +311,37 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
         }
         __asm__ volatile("" ::: "memory");
         // (one wave's LDS accesses take effect in order)
-        for (int idx = lane; idx < 32 * 32 / E; idx += 64) {
-            const int a = idx / (32 / E), c0 = (idx % (32 / E)) * E;
-            float v[E];
-            if (which == 2) {
-                // Vt[h][kcol*D + d][row]: a = d, c0 = first row of the vector
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    v[e] = ws[(c0 + e) * 33 + a];
-                *reinterpret_cast<uint4 *>(vt + (b * H + h) * LpLp * kTD +
-                                           ((int64_t)kcol * kTD + a) * Lp + j0 + c0) = pack16<T>(v);
-            } else {
+        constexpr int KC = Mma32<T>::KC, HALF = Mma32<T>::HALF;   // HALF == E
+        if (which == 3) {
+            // G[row][col][h*D + d]: rows of the block, 16-byte vectors
+            for (int idx = lane; idx < 32 * 32 / E; idx += 64) {
+                const int a = idx / (32 / E), c0 = (idx % (32 / E)) * E;
+                float v[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     v[e] = ws[a * 33 + c0 + e];
+                *reinterpret_cast<uint4 *>(gg + ((b * Lp + j0 + a) * (int64_t)Lp + kcol) * HD +
+                                           h * kTD + c0) = pack16<T>(v);
+            }
+        } else {
+            // operand-fragment order (see frag_base): each step of 64 lanes
+            // writes one 1 KB fragment. q, k: A fragments of rows j0 + r
+            // (row tile j0/32), k index kcol*D + d; v: B fragments of anchor
+            // kcol, column d, k index j0 + r.
+            for (int idx = lane; idx < 32 * 32 / E; idx += 64) {
+                const int kcl = idx >> 6, ln = idx & 63;
+                const int rr = ln & 31, k0 = kcl * KC + (ln >> 5) * HALF;
+                float v[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v[e] = which == 2 ? ws[(k0 + e) * 33 + rr] : ws[rr * 33 + k0 + e];
                 const uint4 pv = pack16<T>(v);
-                const int64_t row = j0 + a;
-                const int64_t qo = ((b * H + h) * Lp + row) * (int64_t)Lp * kTD + (int64_t)kcol * kTD + c0;
-                if (which <= 1) {
+                if (which == 2) {
+                    *reinterpret_cast<uint4 *>(vt + frag_base<T>(b * H + h, kcol, Lp / KC, Lp) +
+                                               ((int64_t)(j0 / KC + kcl) * 64 + ln) * E) = pv;
+                } else {
+                    const int64_t qo = frag_base<T>(b * H + h, j0 / 32, Lp * kTD / KC, Lp / 32) +
+                                       ((int64_t)(kcol * (kTD / KC) + kcl) * 64 + ln) * E;
                     *reinterpret_cast<uint4 *>((which == 0 ? qh : kh) + qo) = pv;
                     if (SPLIT) {
                         // the remainder after rounding, so that hi + lo keeps
@@ -323,9 +353,7 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
                         *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(which == 0 ? p.qlo : p.klo) + qo) =
                             pack16<T>(lo);
                     }
-                } else
-                    *reinterpret_cast<uint4 *>(gg + ((b * Lp + row) * (int64_t)Lp + kcol) * HD +
-                                               h * kTD + c0) = pv;
+                }
             }
         }
         __asm__ volatile("" ::: "memory");
@@ -363,12 +391,13 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
     const int h = (int)(t % H);
     const int64_t b = t / H;
     const int64_t K = (int64_t)Lp * kTD;
-    const T *qa = reinterpret_cast<const T *>(p.qh) + ((b * H + h) * Lp + ib * 32 + (lane & 31)) * K;
-    const T *kb = reinterpret_cast<const T *>(p.kh) + ((b * H + h) * Lp + jb * 32 + (lane & 31)) * K;
     // chunks per wave: Lp*D/KC is a multiple of 4*kKS*U (Lp a multiple of 32)
     const int nkc = (int)(K / KC), per = nkc / (4 * kKS);
     const int c0 = (ks * 4 + wave) * per;
-    const int hoff = (lane >> 5) * HALF;
+    // q and k in operand-fragment order: chunk c of a row tile is the
+    // kilobyte at c*64*HALF, this lane's 16 bytes at lane*HALF
+    const T *qa = reinterpret_cast<const T *>(p.qh) + frag_base<T>(b * H + h, ib, nkc, nb) + lane * HALF;
+    const T *kb = reinterpret_cast<const T *>(p.kh) + frag_base<T>(b * H + h, jb, nkc, nb) + lane * HALF;
     f32x16_t acc = zero16();
     // two register stages: the chunks of the next step are requested before
     // the products of this one (clamped at the end, so every load is
@@ -383,7 +412,7 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
         auto ld = [&](int kc) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t o = (int64_t)(c0 + kc + u) * KC + hoff;
+                const int64_t o = (int64_t)(c0 + kc + u) * 64 * HALF;
                 av[u] = *reinterpret_cast<const uint4 *>(qa + o);
                 bv[u] = *reinterpret_cast<const uint4 *>(kb + o);
                 al[u] = *reinterpret_cast<const uint4 *>(qa + dl + o);
@@ -410,7 +439,7 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
         auto ld = [&](int kc) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t o = (int64_t)(c0 + kc + u) * KC + hoff;
+                const int64_t o = (int64_t)(c0 + kc + u) * 64 * HALF;
                 av[u] = *reinterpret_cast<const uint4 *>(qa + o);
                 bv[u] = *reinterpret_cast<const uint4 *>(kb + o);
             }
@@ -445,6 +474,7 @@ __global__ __launch_bounds__(256) void k_tied_logits(TiedArgs p) {
 // -------------------------------------------------------------- softmax
 template <typename T>
 __global__ __launch_bounds__(256) void k_tied_softmax(TiedArgs p) {
+    constexpr int KC = Mma32<T>::KC, HALF = Mma32<T>::HALF, NU = 16 / HALF;
     const int Lp = p.Lp, L = p.L;
     const int lane = threadIdx.x & 63;
     const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h)*Lp + i
@@ -452,45 +482,76 @@ __global__ __launch_bounds__(256) void k_tied_softmax(TiedArgs p) {
     if (rowid >= nrow)
         return;
     const int i = (int)(rowid % Lp);
-    T *arow = reinterpret_cast<T *>(p.amat) + rowid * Lp;
+    // A in operand-fragment order (row tile i/32, k index j): the HALF
+    // consecutive j of one step of this lane are one 16-byte piece
+    T *am = reinterpret_cast<T *>(p.amat) + frag_base<T>(rowid / Lp, i / 32, Lp / KC, Lp / 32);
+    auto put = [&](int jj, const float *v) {
+        const int kc = jj / KC, hf = (jj % KC) / HALF;
+        *reinterpret_cast<uint4 *>(am + ((int64_t)kc * 64 + (i & 31) + 32 * hf) * HALF) = pack16<T>(v);
+    };
+    float v[NU][HALF];
     if (i >= L) {
-        for (int j = lane; j < Lp; j += 64)
-            arow[j] = from_f<T>(0.0f);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int e = 0; e < HALF; ++e)
+                v[u][e] = 0.0f;
+            const int jj = (u * 64 + lane) * HALF;
+            if (jj < Lp)
+                put(jj, v[u]);
+        }
         return;
     }
     const float *srow = p.s + rowid * Lp;
     const int64_t pstride = (int64_t)p.B * p.H * Lp * Lp;  // between partial logit tiles
     const float *brow = p.beta + rowid * Lp;
-    float v[16];
-    float m = -INFINITY;
+    // this lane's j = (u*64 + lane)*HALF + e: loads of clamped offsets, all
+    // issued before the first use
+    float4 bq[NU][HALF / 4], sq[kKS][NU][HALF / 4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int j = lane + 64 * u;
-        float x = -INFINITY;
-        if (j < L) {
-            x = brow[j];
+    for (int u = 0; u < NU; ++u) {
+        const int jj = min((u * 64 + lane) * HALF, Lp - HALF);
+#pragma unroll
+        for (int q = 0; q < HALF / 4; ++q) {
+            bq[u][q] = *reinterpret_cast<const float4 *>(brow + jj + 4 * q);
 #pragma unroll
             for (int k = 0; k < kKS; ++k)
-                x += srow[k * pstride + j];
+                sq[k][u][q] = *reinterpret_cast<const float4 *>(srow + k * pstride + jj + 4 * q);
         }
-        v[u] = x;
-        m = fmaxf(m, v[u]);
     }
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int e = 0; e < HALF; ++e) {
+            const int j = (u * 64 + lane) * HALF + e;
+            float x = f4_get(bq[u][e / 4], e % 4);
+#pragma unroll
+            for (int k = 0; k < kKS; ++k)
+                x += f4_get(sq[k][u][e / 4], e % 4);
+            v[u][e] = j < L ? x : -INFINITY;
+            m = fmaxf(m, v[u][e]);
+        }
     m = group_max<64>(m);
     float sum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int j = lane + 64 * u;
-        v[u] = j < L ? expf(v[u] - m) : 0.0f;
-        sum += v[u];
-    }
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int e = 0; e < HALF; ++e) {
+            const int j = (u * 64 + lane) * HALF + e;
+            v[u][e] = j < L ? expf(v[u][e] - m) : 0.0f;
+            sum += v[u][e];
+        }
     sum = group_sum<64>(sum);
     const float inv = 1.0f / sum;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int j = lane + 64 * u;
-        if (j < Lp)
-            arow[j] = from_f<T>(v[u] * inv);
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+        for (int e = 0; e < HALF; ++e)
+            v[u][e] *= inv;
+        const int jj = (u * 64 + lane) * HALF;
+        if (jj < Lp)
+            put(jj, v[u]);
     }
 }
 
@@ -513,19 +574,20 @@ __global__ __launch_bounds__(256) void k_tied_out(TiedArgs p) {
     T *utlo = ut + 32 * ldu;                                              // [32][ldu] (bf16)
     float *ot = reinterpret_cast<float *>(smem + tal16((size_t)(SPLIT ? 2 : 1) * 32 * ldu * sizeof(T)));  // [32][C+4]
     const int ldo = C + 4;
-    const int64_t LpLp = (int64_t)Lp * Lp;
     const T *amat = reinterpret_cast<const T *>(p.amat);
     const T *vt = reinterpret_cast<const T *>(p.vt);
     const T *gg = reinterpret_cast<const T *>(p.g);
     const T *bo = reinterpret_cast<const T *>(p.b_out);
     T *out = reinterpret_cast<T *>(p.out);
     const int nkc = Lp / KC;
-    const int hoff = (lane >> 5) * HALF, r = lane & 31;
+    const int r = lane & 31;
     for (int a = ag * kNA; a < min(L, ag * kNA + kNA); ++a) {
         // U[i][a] of each head this wave takes, times the gate g(F[a][i])
         for (int h = wave; h < H; h += 4) {
-            const T *ar = amat + ((b * H + h) * Lp + i0 + r) * (int64_t)Lp + hoff;
-            const T *vr = vt + (b * H + h) * LpLp * kTD + ((int64_t)a * kTD + r) * Lp + hoff;
+            // A (row tile i0/32) and v (anchor a) in operand-fragment order:
+            // chunk k is the kilobyte at k*64*HALF
+            const T *ar = amat + frag_base<T>(b * H + h, i0 / 32, nkc, nib) + lane * HALF;
+            const T *vr = vt + frag_base<T>(b * H + h, a, nkc, Lp) + lane * HALF;
             f32x16_t acc = zero16();
             constexpr int U = 4;
             for (int kc = 0; kc < nkc; kc += U) {
@@ -533,8 +595,8 @@ __global__ __launch_bounds__(256) void k_tied_out(TiedArgs p) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int k = min(kc + u, nkc - 1);
-                    av[u] = *reinterpret_cast<const uint4 *>(ar + k * KC);
-                    bv[u] = *reinterpret_cast<const uint4 *>(vr + k * KC);
+                    av[u] = *reinterpret_cast<const uint4 *>(ar + (int64_t)k * 64 * HALF);
+                    bv[u] = *reinterpret_cast<const uint4 *>(vr + (int64_t)k * 64 * HALF);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u)
