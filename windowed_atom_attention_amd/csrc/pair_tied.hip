@@ -22,13 +22,14 @@
 //                     operand tile (and, for the bias, the LayerNorm of
 //                     Fb[j][kcol] times w_bias, written as beta[h][kcol][j]),
 //                     then q|k and v|gate on MFMA (32x32
-//                     blocks, one head per block since D = 32), stored as
-//                       Qh[h][row][col*D + d], Kh[h][row][col*D + d]
-//                       Vt[h][col*D + d][row], G[row][col][h*D + d]
-//                     (row, col: grid position of the entry), so that both
-//                     later products read operands contiguous along their
-//                     reduction index. Entries outside the L x L grid (the
-//                     grid is padded to Lp = L rounded up to 32) are zeros.
+//                     blocks, one head per block since D = 32). q and k
+//                     (rows: grid row, reduction index: grid column*D + d)
+//                     and v (rows: anchor*D + d, reduction index: key) are
+//                     stored in operand-fragment order (frag_base below),
+//                     G as G[row][col][h*D + d], so that each later product
+//                     loads a wave's operand as one contiguous kilobyte.
+//                     Entries outside the L x L grid (the grid is padded to
+//                     Lp = L rounded up to 32) are zeros.
 //  k_tied_logits      kKS workgroups per (b, h, 32 rows i, 32 columns j):
 //                     S = Qh Kh^T over the Lp*D reduction (split over the
 //                     kKS workgroups and their 4 waves; the waves' parts are
