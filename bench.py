@@ -459,6 +459,13 @@ def measure(config, steps, warmup, cache_bytes, graph=False, pack_per_call=False
                 v["TFLOP_per_s"] = a / (v["avg_us"] * 1e-6) / 1e12
                 v["frac_mfma"] = v["TFLOP_per_s"] / MFMA_PEAK_TFLOPS[dtype]
             v["traffic"] = _traffic(k, config)
+    # the slot step's rate on its own kernel time: entries (B*A*H*K) per
+    # second of the slot kernel (and of the gather kernel, which takes the
+    # blocks of scattered key ids)
+    slot_us = sum(per_kernel[k]["avg_us"] for k in ("slot_attention", "slot_gather")
+                  if k in per_kernel)
+    if slot_us > 0:
+        per_kernel["slot_attention"]["entries_per_s_slot_step"] = w.entries / (slot_us * 1e-6)
     res = {
         "workload": "%s (config %s): B=%d A=%d T=%d K=%d C=%d S=%d H=%d D=%d V=%d M=%d "
                     "U=%d, %s, radius %d" % (NAMES[config], config, d["B"], d["A"], d["T"],
