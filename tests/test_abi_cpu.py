@@ -201,6 +201,13 @@ def test_python_binding_argument_checks():
     bad.structure["key_index"] = bad.structure["key_index"][..., :5]
     with pytest.raises(ValueError):
         windowed_atom_attention(**bad.kwargs())
+    # zero-size inputs are rejected before anything else happens
+    empty = make_workload("0")
+    empty.structure["key_index"] = empty.structure["key_index"][..., :0]
+    empty.masks["window_mask"] = empty.masks["window_mask"][..., :0]
+    empty.activations["pair"] = empty.activations["pair"][:, :, :0]
+    with pytest.raises(ValueError, match="zero-size"):
+        windowed_atom_attention(**empty.kwargs())
 
 
 def _bws(d, style=N.AF3, stage=N.ENCODER, dtype=N.F32):

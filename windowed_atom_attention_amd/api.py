@@ -82,6 +82,9 @@ def dims_from(activations, parameters, masks, structure, style, stage) -> Dict[s
     D = HD // H
     U = parameters["w_pool"].shape[-1] if stage == "encoder" else activations["token"].shape[-1]
     d = dict(B=B, A=A, T=T, K=K, C=C, S=S, H=H, D=D, V=V, M=M, U=U)
+    if min(B, A, T, K) < 1:
+        raise ValueError("zero-size input: B, A, T and K must be >= 1 (got B=%d A=%d T=%d K=%d)"
+                         % (B, A, T, K))
     expect = {
         ("activations", "condition"): (B, A, S),
         ("masks", "valid"): (B, A), ("masks", "token_valid"): (B, T),
