@@ -199,10 +199,17 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
     float *ws = stg + wave * 32 * 33;             // this wave's 32x32 staging block
     // LayerNorm parameters (and, when beta is formed here, the bias
     // LayerNorm's and w_bias) into LDS; rows: 8 threads per entry, each an
-    // eighth of the channels, all loads issued before the first use
+    // eighth of the channels, all loads issued before the first use.
+    // Channel c of a vector sits at c + c / per (per = channels per thread),
+    // w_bias row c at (c + c / perb) * H: the 8 threads of an entry read
+    // channels per apart, and the padding puts them in 8 different LDS
+    // banks (unpadded, a stride of 16 or 64 floats sent all 8 to one bank).
     const int Cb = p.Cb;
     const bool fb = p.fuse_bias != 0;
-    float *prm = stg + 4 * 32 * 33;               // ns, nb [C]; bns, bnb [Cb]; w_bias [Cb][H]
+    const int per = C / 8, perb = Cb / 8;
+    float *prm = stg + 4 * 32 * 33;               // ns, nb [C + 8]; bns, bnb [Cb + 8]; w_bias [Cb + 8][H]
+    float *pns = prm, *pnb = prm + (C + 8);
+    float *pbs = prm + 2 * (C + 8), *pbh = pbs + (Cb + 8), *pwb = pbh + (Cb + 8);
     const int nprm = 2 * C + (fb ? Cb * (2 + H) : 0);
     {
         for (int e0 = tid; e0 < nprm; e0 += 4 * 256) {
@@ -217,9 +224,23 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
                 v[u] = reinterpret_cast<const T *>(src)[e - base];
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (e0 + u * 256 < nprm)
-                    prm[e0 + u * 256] = to_f(v[u]);
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * 256;
+                if (e >= nprm)
+                    continue;
+                float *dst;
+                if (e < 2 * C) {
+                    const int c = e < C ? e : e - C;
+                    dst = (e < C ? pns : pnb) + c + c / per;
+                } else if (e < 2 * C + 2 * Cb) {
+                    const int c = e < 2 * C + Cb ? e - 2 * C : e - 2 * C - Cb;
+                    dst = (e < 2 * C + Cb ? pbs : pbh) + c + c / perb;
+                } else {
+                    const int k = e - 2 * C - 2 * Cb, c = k / H;
+                    dst = pwb + (c + c / perb) * H + (k - c * H);
+                }
+                *dst = to_f(v[u]);
+            }
         }
     }
     const int r = tid >> 3, sub = tid & 7;
@@ -227,7 +248,6 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
     const bool valid = j < L && kcol < L;
     const int64_t ent = (b * L + min(j, L - 1)) * L + min(kcol, L - 1);
     float x[32], xb[32];
-    const int per = C / 8, perb = Cb / 8;
     load_part<T>(reinterpret_cast<const T *>(p.f) + ent * C + sub * per, per, p.vec_f != 0, valid, x);
     if (fb)
         load_part<T>(reinterpret_cast<const T *>(p.fb) + ent * Cb + sub * perb, perb,
@@ -246,12 +266,35 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
             q += d * d;
         }
         const float rstd = 1.0f / sqrtf(sum8(q) / (float)C + p.eps);
+        // (padded parameter index of channel sub * per + e: + sub)
+        if (per % E == 0) {
+            // whole 16-byte pieces of the row (16-byte aligned: the tile
+            // pitch and sub * per * sizeof(T) are multiples of 16 bytes)
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            if (e < per) {
-                const int c = sub * per + e;
-                put_split<T>(opA, SPLIT ? opAlo : nullptr, r * lda + c,
-                             (x[e] - mean) * rstd * prm[c] + prm[C + c]);
+            for (int u = 0; u < 32 / E; ++u) {
+                if (u * E < per) {
+                    float hv[E], lv[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int c = sub * per + u * E + e;
+                        const float v = (x[u * E + e] - mean) * rstd * pns[c + sub] + pnb[c + sub];
+                        hv[e] = v;
+                        lv[e] = v - to_f(from_f<T>(v));
+                    }
+                    const int off = r * lda + sub * per + u * E;
+                    *reinterpret_cast<uint4 *>(opA + off) = pack16<T>(hv);
+                    if (SPLIT)
+                        *reinterpret_cast<uint4 *>(opAlo + off) = pack16<T>(lv);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                if (e < per) {
+                    const int c = sub * per + e;
+                    put_split<T>(opA, SPLIT ? opAlo : nullptr, r * lda + c,
+                                 (x[e] - mean) * rstd * pns[c + sub] + pnb[c + sub]);
+                }
             }
         }
     }
@@ -270,17 +313,16 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
             q += d * d;
         }
         const float rstd = 1.0f / sqrtf(sum8(q) / (float)Cb + p.eps);
-        const float *bsc = prm + 2 * C, *bsh = bsc + Cb, *wb = bsh + Cb;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
             if (e < perb) {
-                const int c = sub * perb + e;
-                const float xn = (xb[e] - mean) * rstd * bsc[c] + bsh[c];
+                const int c = sub * perb + e + sub; // padded index
+                const float xn = (xb[e] - mean) * rstd * pbs[c] + pbh[c];
 #pragma unroll
                 for (int h = 0; h < 8; ++h)
                     if (h < H)
-                        acc[h] = fmaf(xn, wb[c * H + h], acc[h]);
+                        acc[h] = fmaf(xn, pwb[c * H + h], acc[h]);
             }
         }
 #pragma unroll
@@ -672,7 +714,7 @@ TiedLayout tied_layout(int64_t B, int64_t L, int64_t C, int64_t H, int esz) {
 static bool tied_fuse_bias(int64_t Cb) { return Cb % 8 == 0 && Cb <= 256; }
 static size_t tied_proj_lds(int64_t C, int64_t Cb, int64_t H, int esz) {
     return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (C + 16 / esz) * esz) + (size_t)4 * 32 * 33 * 4 +
-           (size_t)(2 * C + (tied_fuse_bias(Cb) ? Cb * (2 + H) : 0)) * 4;
+           (size_t)(2 * (C + 8) + (tied_fuse_bias(Cb) ? (Cb + 8) * (2 + H) : 0)) * 4;
 }
 static size_t tied_out_lds(int64_t C, int64_t H, int esz) {
     return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (H * kTD + 16 / esz) * esz) +
