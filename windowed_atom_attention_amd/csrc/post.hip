@@ -281,18 +281,27 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
             });
     }
     __syncthreads();
-    // statistics of the NEW state for the transition norm
+    // statistics of the NEW state for the transition norm: each thread reads
+    // 16-byte pieces of its row (channels 4*sub + 4*TPR*k ..), several
+    // reads in flight per loop step (single-float reads in a loop of
+    // runtime length had each waited for the previous one: 3.8 k cycles per
+    // workgroup on a 24576-atom bf16 workload)
     {
         const float *xr = xs + row * L.xp;
         if (STYLE == STYLE_AF3) {
             float s = 0.0f;
-            for (int c = sub; c < C; c += TPR)
-                s += xr[c];
+#pragma unroll 4
+            for (int c = 4 * sub; c < C; c += 4 * TPR) {
+                const float4 v = *reinterpret_cast<const float4 *>(xr + c);
+                s += (v.x + v.y) + (v.z + v.w);
+            }
             const float mean = row_sum<TPR>(s) / (float)C;
             float q = 0.0f;
-            for (int c = sub; c < C; c += TPR) {
-                const float t = xr[c] - mean;
-                q += t * t;
+#pragma unroll 4
+            for (int c = 4 * sub; c < C; c += 4 * TPR) {
+                const float4 v = *reinterpret_cast<const float4 *>(xr + c);
+                const float t0 = v.x - mean, t1 = v.y - mean, t2 = v.z - mean, t3 = v.w - mean;
+                q += (t0 * t0 + t1 * t1) + (t2 * t2 + t3 * t3);
             }
             const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             if (sub == 0) {
@@ -301,8 +310,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
             }
         } else {
             float q = 0.0f;
-            for (int c = sub; c < C; c += TPR)
-                q += xr[c] * xr[c];
+#pragma unroll 4
+            for (int c = 4 * sub; c < C; c += 4 * TPR) {
+                const float4 v = *reinterpret_cast<const float4 *>(xr + c);
+                q += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+            }
             const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
@@ -504,13 +516,18 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (sizeof(T) == 2 ? 3 : 2)) vo
     if (STAGE == STAGE_DECODER) {
         const float *xr = xs + row * L.xp;
         float s = 0.0f;
-        for (int c = sub; c < C; c += TPR)
-            s += xr[c];
+#pragma unroll 4
+        for (int c = 4 * sub; c < C; c += 4 * TPR) {
+            const float4 v = *reinterpret_cast<const float4 *>(xr + c);
+            s += (v.x + v.y) + (v.z + v.w);
+        }
         const float mean = row_sum<TPR>(s) / (float)C;
         float q = 0.0f;
-        for (int c = sub; c < C; c += TPR) {
-            const float t = xr[c] - mean;
-            q += t * t;
+#pragma unroll 4
+        for (int c = 4 * sub; c < C; c += 4 * TPR) {
+            const float4 v = *reinterpret_cast<const float4 *>(xr + c);
+            const float t0 = v.x - mean, t1 = v.y - mean, t2 = v.z - mean, t3 = v.w - mean;
+            q += (t0 * t0 + t1 * t1) + (t2 * t2 + t3 * t3);
         }
         const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
         const T *rs = reinterpret_cast<const T *>(p.readout_scale);

@@ -394,6 +394,18 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
             v += to_f(xl[r * L.ldC + c]);
         return v;
     };
+    // x0 of the 16-byte piece vi of row r (one LDS read per tile instead of
+    // one per element)
+    auto x0vec = [&](int r, int vi, float (&out)[E]) {
+        unpack16<T>(*reinterpret_cast<const uint4 *>(xh + r * L.ldC + vi * E), out);
+        if (XLO) {
+            float lo[E];
+            unpack16<T>(*reinterpret_cast<const uint4 *>(xl + r * L.ldC + vi * E), lo);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                out[e] += lo[e];
+        }
+    };
 
     // Loads first, all unconditional (rows past the end read row 0; values
     // of unusable atoms are replaced by zeros: selected, never multiplied):
@@ -502,12 +514,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
         if (STYLE == STYLE_AF3) {
             const float mean = row_sum<TPR>(xsum) / (float)C;
             float q = 0.0f;
-            for (int vi = sub; vi < nvC; vi += TPR)
+#pragma unroll 2
+            for (int vi = sub; vi < nvC; vi += TPR) {
+                float xv[E];
+                x0vec(row, vi, xv);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float t = x0(row, vi * E + e) - mean;
+                    const float t = xv[e] - mean;
                     q += t * t;
                 }
+            }
             const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             const float mc = row_sum<TPR>(csum) / (float)S;
             float q2 = 0.0f;
@@ -541,12 +557,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (prep_wgs<T, STYLE, STAGE>()
             }
         } else {
             float q = 0.0f;
-            for (int vi = sub; vi < nvC; vi += TPR)
+#pragma unroll 2
+            for (int vi = sub; vi < nvC; vi += TPR) {
+                float xv[E];
+                x0vec(row, vi, xv);
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float t = x0(row, vi * E + e);
-                    q += t * t;
-                }
+                for (int e = 0; e < E; ++e)
+                    q += xv[e] * xv[e];
+            }
             const float rstd = 1.0f / sqrtf(row_sum<TPR>(q) / (float)C + p.eps);
             if (sub == 0) {
                 st[row * 4 + 0] = 0.0f;
