@@ -515,6 +515,7 @@ TIED_CASES = [
     dict(B=1, L=100, C=32, CB=8, H=1, D=32, dtype=torch.bfloat16),
     dict(B=2, L=45, C=96, CB=40, H=3, D=32, dtype=torch.bfloat16),
     dict(B=1, L=70, C=256, CB=128, H=8, D=32, dtype=torch.bfloat16),
+    dict(B=1, L=40, C=64, CB=24, H=6, D=32, dtype=torch.float32),     # bias rows padded to 8 heads, any width
     dict(B=1, L=1, C=32, CB=4, H=1, D=32, dtype=torch.float32),       # one residue
 ]
 

@@ -47,6 +47,7 @@
 //                     LDS tile; the output projection on MFMA (w_out packed),
 //                     + b_out, rows out[b][k][i0..i0+31] as 16-byte vectors.
 #include <cmath>
+#include <type_traits>
 #include <cstring>
 
 #include "../../include/atom_attn.h"
@@ -180,7 +181,9 @@ __global__ __launch_bounds__(256) void k_tied_bias(TiedArgs p) {
 }
 
 // ---------------------------------------------------------- projections
-template <typename T>
+// PB: bias-row channels per thread fixed at compile time (16: bias width
+// 128), or 0 for any width.
+template <typename T, int PB>
 __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int E = 16 / sizeof(T);
@@ -206,11 +209,12 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
     // banks (unpadded, a stride of 16 or 64 floats sent all 8 to one bank).
     const int Cb = p.Cb;
     const bool fb = p.fuse_bias != 0;
-    const int per = C / 8, perb = Cb / 8;
-    float *prm = stg + 4 * 32 * 33;               // ns, nb [C + 8]; bns, bnb [Cb + 8]; w_bias [Cb + 8][H]
+    const int per = C / 8, perb = PB > 0 ? PB : Cb / 8;
+    const int HP = H <= 4 ? 4 : 8;                // w_bias rows padded to HP heads (zeros past H)
+    float *prm = stg + 4 * 32 * 33;               // ns, nb [C + 8]; bns, bnb [Cb + 8]; w_bias [Cb + 8][HP]
     float *pns = prm, *pnb = prm + (C + 8);
     float *pbs = prm + 2 * (C + 8), *pbh = pbs + (Cb + 8), *pwb = pbh + (Cb + 8);
-    const int nprm = 2 * C + (fb ? Cb * (2 + H) : 0);
+    const int nprm = 2 * C + (fb ? Cb * (2 + HP) : 0);
     {
         for (int e0 = tid; e0 < nprm; e0 += 4 * 256) {
             T v[4];
@@ -219,9 +223,14 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
                 const int e = min(e0 + u * 256, nprm - 1);
                 const void *src = e < C ? p.ns : e < 2 * C ? p.nb
                                 : e < 2 * C + Cb ? p.bns : e < 2 * C + 2 * Cb ? p.bnb : p.w_bias;
-                const int base = e < C ? 0 : e < 2 * C ? C
-                               : e < 2 * C + Cb ? 2 * C : e < 2 * C + 2 * Cb ? 2 * C + Cb : 2 * C + 2 * Cb;
-                v[u] = reinterpret_cast<const T *>(src)[e - base];
+                int idx;
+                if (e < 2 * C + 2 * Cb) {
+                    idx = e - (e < C ? 0 : e < 2 * C ? C : e < 2 * C + Cb ? 2 * C : 2 * C + Cb);
+                } else { // w_bias entry (c, h) of the padded rows; h >= H reads (c, H - 1), unused
+                    const int k = e - 2 * C - 2 * Cb, c = k / HP;
+                    idx = c * H + min(k - c * HP, H - 1);
+                }
+                v[u] = reinterpret_cast<const T *>(src)[idx];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -236,8 +245,10 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
                     const int c = e < 2 * C + Cb ? e - 2 * C : e - 2 * C - Cb;
                     dst = (e < 2 * C + Cb ? pbs : pbh) + c + c / perb;
                 } else {
-                    const int k = e - 2 * C - 2 * Cb, c = k / H;
-                    dst = pwb + (c + c / perb) * H + (k - c * H);
+                    const int k = e - 2 * C - 2 * Cb, c = k / HP, h = k - c * HP;
+                    dst = pwb + (c + c / perb) * HP + h;
+                    if (h >= H)
+                        v[u] = T{};
                 }
                 *dst = to_f(v[u]);
             }
@@ -314,17 +325,35 @@ __global__ __launch_bounds__(256) void k_tied_proj(TiedArgs p) {
         }
         const float rstd = 1.0f / sqrtf(sum8(q) / (float)Cb + p.eps);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // one or two 16-byte reads of the padded weight row per channel, no
+        // branch inside the channel loop (a fixed PB unrolls it whole)
+        auto bias_sum = [&](auto hp8) {
+            constexpr bool H8 = decltype(hp8)::value;
+            constexpr int NP = H8 ? 8 : 4;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            if (e < perb) {
-                const int c = sub * perb + e + sub; // padded index
-                const float xn = (xb[e] - mean) * rstd * pbs[c] + pbh[c];
-#pragma unroll
-                for (int h = 0; h < 8; ++h)
-                    if (h < H)
-                        acc[h] = fmaf(xn, pwb[c * H + h], acc[h]);
+            for (int e = 0; e < (PB > 0 ? PB : 32); ++e) {
+                if (PB > 0 || e < perb) {
+                    const int c = sub * perb + e + sub; // padded index
+                    const float xn = (xb[e] - mean) * rstd * pbs[c] + pbh[c];
+                    const float4 w0 = *reinterpret_cast<const float4 *>(pwb + c * NP);
+                    acc[0] = fmaf(xn, w0.x, acc[0]);
+                    acc[1] = fmaf(xn, w0.y, acc[1]);
+                    acc[2] = fmaf(xn, w0.z, acc[2]);
+                    acc[3] = fmaf(xn, w0.w, acc[3]);
+                    if (H8) {
+                        const float4 w1 = *reinterpret_cast<const float4 *>(pwb + c * NP + 4);
+                        acc[4] = fmaf(xn, w1.x, acc[4]);
+                        acc[5] = fmaf(xn, w1.y, acc[5]);
+                        acc[6] = fmaf(xn, w1.z, acc[6]);
+                        acc[7] = fmaf(xn, w1.w, acc[7]);
+                    }
+                }
             }
-        }
+        };
+        if (HP == 8)
+            bias_sum(std::true_type{});
+        else
+            bias_sum(std::false_type{});
 #pragma unroll
         for (int h = 0; h < 8; ++h)
             acc[h] = sum8(acc[h]);
@@ -714,7 +743,7 @@ TiedLayout tied_layout(int64_t B, int64_t L, int64_t C, int64_t H, int esz) {
 static bool tied_fuse_bias(int64_t Cb) { return Cb % 8 == 0 && Cb <= 256; }
 static size_t tied_proj_lds(int64_t C, int64_t Cb, int64_t H, int esz) {
     return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (C + 16 / esz) * esz) + (size_t)4 * 32 * 33 * 4 +
-           (size_t)(2 * (C + 8) + (tied_fuse_bias(Cb) ? (Cb + 8) * (2 + H) : 0)) * 4;
+           (size_t)(2 * (C + 8) + (tied_fuse_bias(Cb) ? (Cb + 8) * (2 + (H <= 4 ? 4 : 8)) : 0)) * 4;
 }
 static size_t tied_out_lds(int64_t C, int64_t H, int esz) {
     return tal16((size_t)(esz == 2 ? 2 : 1) * 32 * (H * kTD + 16 / esz) * esz) +
@@ -821,7 +850,10 @@ int atom_attn_tied_row_attention(const atom_attn_tied_dims *d, int dtype, double
         (a.fuse_bias ||
          go(KN_TIED_BIAS, dt ? (const void *)k_tied_bias<bf16_t> : (const void *)k_tied_bias<float>,
             (a.B * (int64_t)a.L * a.L * 8 + 255) / 256, 0)) &&
-        go(KN_TIED_PROJ, dt ? (const void *)k_tied_proj<bf16_t> : (const void *)k_tied_proj<float>,
+        go(KN_TIED_PROJ,
+           a.fuse_bias && d->CB == 128
+               ? (dt ? (const void *)k_tied_proj<bf16_t, 16> : (const void *)k_tied_proj<float, 16>)
+               : (dt ? (const void *)k_tied_proj<bf16_t, 0> : (const void *)k_tied_proj<float, 0>),
            a.B * Lp * nb32, tied_proj_lds(C, d->CB, d->H, esz)) &&
         go(KN_TIED_LOGITS,
            dt ? (const void *)k_tied_logits<bf16_t> : (const void *)k_tied_logits<float>,
