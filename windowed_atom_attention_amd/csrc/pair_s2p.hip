@@ -47,10 +47,24 @@ __global__ __launch_bounds__(kTokThreads) void k_s2p_tok(S2PArgs p) {
     float *st = xs + kTT * C;                       // [kTT][2] mean, rstd
     float *red = st + 2 * kTT;                      // [NWV][kTT][2H] partial sums
     const T *x = reinterpret_cast<const T *>(p.x);
+    const int nel = kTT * C;
+    // the norm parameters of this thread's elements e0 + u * kTokThreads (the
+    // first group: every later group repeats its channels when C divides
+    // the thread count, else they are read again below), requested first
+    const T *ns = reinterpret_cast<const T *>(p.norm_scale);
+    const T *nb = reinterpret_cast<const T *>(p.norm_bias);
+    const bool prm_once = kTokThreads % C == 0;
+    T sv0[4], bv0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = min(tid + u * kTokThreads, nel - 1);
+        const int c = e - (e / C) * C;
+        sv0[u] = ns[c];
+        bv0[u] = nb[c];
+    }
     // rows in LDS: the row and presence loads of four elements are issued
     // together from clamped indices, absent or missing tokens are selected to
     // zeros (their payloads never enter arithmetic)
-    const int nel = kTT * C;
     for (int e0 = tid; e0 < nel; e0 += 4 * kTokThreads) {
         T v[4];
         uint8_t m[4];
@@ -72,17 +86,23 @@ __global__ __launch_bounds__(kTokThreads) void k_s2p_tok(S2PArgs p) {
         }
     }
     __syncthreads();
-    // population mean and variance (two passes over LDS), one row per wave
+    // population mean and variance (two passes over LDS), one row per wave,
+    // 16-byte reads with several in flight (C is a multiple of 32)
     for (int r = wave; r < kTT; r += NWV) {
         float s = 0.0f;
-        for (int c = lane; c < C; c += 64)
-            s += xs[r * C + c];
+#pragma unroll 4
+        for (int c = 4 * lane; c < C; c += 256) {
+            const float4 v = *reinterpret_cast<const float4 *>(xs + r * C + c);
+            s += (v.x + v.y) + (v.z + v.w);
+        }
         s = group_sum<64>(s);
         const float mean = s / (float)C;
         float q = 0.0f;
-        for (int c = lane; c < C; c += 64) {
-            const float d = xs[r * C + c] - mean;
-            q += d * d;
+#pragma unroll 4
+        for (int c = 4 * lane; c < C; c += 256) {
+            const float4 v = *reinterpret_cast<const float4 *>(xs + r * C + c);
+            const float d0 = v.x - mean, d1 = v.y - mean, d2 = v.z - mean, d3 = v.w - mean;
+            q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
         }
         q = group_sum<64>(q);
         if (lane == 0) {
@@ -91,16 +111,21 @@ __global__ __launch_bounds__(kTokThreads) void k_s2p_tok(S2PArgs p) {
         }
     }
     __syncthreads();
-    const T *ns = reinterpret_cast<const T *>(p.norm_scale);
-    const T *nb = reinterpret_cast<const T *>(p.norm_bias);
     for (int e0 = tid; e0 < nel; e0 += 4 * kTokThreads) {
         T sv[4], bv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int e = min(e0 + u * kTokThreads, nel - 1);
-            const int c = e - (e / C) * C;
-            sv[u] = ns[c];
-            bv[u] = nb[c];
+            sv[u] = sv0[u];
+            bv[u] = bv0[u];
+        }
+        if (!prm_once || e0 != tid) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = min(e0 + u * kTokThreads, nel - 1);
+                const int c = e - (e / C) * C;
+                sv[u] = ns[c];
+                bv[u] = nb[c];
+            }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
